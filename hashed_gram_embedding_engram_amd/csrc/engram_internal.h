@@ -1,0 +1,49 @@
+// Internal declarations shared by the kernels and the C-ABI layer of libengram.
+// Not installed; the public interface is include/engram.h.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace engram {
+
+constexpr int kMaxNgram = 8;
+constexpr int kMaxHeads = 64;
+
+// Hash parameters passed by value as a kernel argument (1.6 KB, read through
+// the scalar cache).  magic[h] = floor(2^64 / mod[h]) drives a Barrett
+// reduction: for v < 2^63 and 2 <= p <= 2^62, q = umulhi(v, magic) is
+// floor(v / p) or one less, so v - q*p needs at most one correction.
+struct HashParams {
+    int64_t eos;
+    int64_t fill;
+    int64_t mult[kMaxNgram];
+    uint64_t mod[kMaxHeads];
+    uint64_t magic[kMaxHeads];
+    int64_t off[kMaxHeads];
+    int32_t ngram_size;
+    int32_t heads_per_ngram;
+};
+
+// 16-byte vector used for every bulk copy (one dwordx4 per lane).
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
+hipError_t launch_hash(const int64_t* tokens, int64_t batch, int64_t seq_len, int64_t seq_begin,
+                       int64_t seq_end, const HashParams& p, int64_t* rows_out, hipStream_t stream);
+
+hipError_t launch_gather(const void* table, int elem_bytes, int64_t row_begin, int64_t num_rows, int dim,
+                         const int64_t* rows, int64_t n, void* out, int64_t* status, hipStream_t stream);
+
+size_t scatter_workspace_bytes(int64_t n, int64_t num_rows, int dim);
+
+hipError_t launch_scatter_add(const int64_t* rows, int64_t n, const void* grad_out, int elem_bytes, int dim,
+                              int64_t row_begin, int64_t num_rows, float* grad_dense, int64_t* uniq_rows,
+                              float* uniq_grad, int64_t* num_uniq, void* workspace, int64_t* status,
+                              hipStream_t stream);
+
+// Sets *status = -1 on the stream (a kernel, not a memset, so the call can be
+// captured in a graph).
+hipError_t launch_status_init(int64_t* status, hipStream_t stream);
+
+}  // namespace engram

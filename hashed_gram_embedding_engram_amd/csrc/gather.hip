@@ -1,0 +1,126 @@
+// Owner-local row gather for gfx950: out[i] = table[rows[i] - row_begin].
+//
+// Engram API page ("nemo_automodel.components.models.qwen3_8_flash_next.engram"):
+// Qwen3_8_FlashNextOwnerShardedEmbedding (an owner looks up only its contiguous
+// rows) and Qwen3_8_FlashNextNGramEmbedding._lookup_ngram_ids (the H head rows of
+// a position, concatenated).  A row outside the owned range is never read: its
+// output is zero and the lowest such lookup index is reported through `status`
+// (_validate_received_ids raises instead of clamping).
+//
+// The copy is pure HBM traffic: one random table row read and one sequential
+// output row written per lookup.  A row is cut into 16-byte chunks (CPR chunks
+// per row).  One wave copies G consecutive lookups, G * CPR = 64 * PER_LANE
+// chunks, so each lane moves PER_LANE chunks with dwordx4 loads and stores:
+//   bf16 x 160 -> CPR = 20, G = 16 (one position's 16 heads, 5,120 B out per wave)
+//   fp32 x 160 -> CPR = 40, G = 8
+// Each store instruction covers 1 KB of contiguous output; each load
+// instruction reads 64 consecutive chunks of the wave's rows (every row is
+// fully read by consecutive lanes).  Output stores are non-temporal: the
+// output is not re-read by this kernel and should not evict table rows that
+// repeat (hot n-grams) from L2 and the Infinity Cache.
+#include "engram_internal.h"
+
+namespace engram {
+namespace {
+
+__device__ __forceinline__ void report_bad(int64_t* status, int64_t idx) {
+    if (status) atomicMin((unsigned long long*)status, (unsigned long long)idx);
+}
+
+template <int CPR, int G>
+__global__ __launch_bounds__(256) void gather_rows_kernel(const u32x4* __restrict__ table, int64_t row_begin,
+                                                          uint64_t num_rows, const int64_t* __restrict__ rows,
+                                                          int64_t n, u32x4* __restrict__ out,
+                                                          int64_t* __restrict__ status) {
+    constexpr int PER_LANE = CPR * G / 64;
+    static_assert(CPR * G % 64 == 0, "wave tile must be whole dwordx4 per lane");
+    const int lane = threadIdx.x & 63;
+    const int64_t wave = (int64_t)blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6);
+    const int64_t n0 = wave * G;
+    if (n0 >= n) return;
+
+    int64_t src[PER_LANE];
+#pragma unroll
+    for (int j = 0; j < PER_LANE; ++j) {
+        const int c = lane + 64 * j;
+        const int64_t i = n0 + c / CPR;
+        src[j] = -1;
+        if (i < n) {
+            const uint64_t local = (uint64_t)rows[i] - (uint64_t)row_begin;
+            if (local < num_rows) {
+                src[j] = (int64_t)local * CPR + c % CPR;
+            } else if (c % CPR == 0) {
+                report_bad(status, i);
+            }
+        }
+    }
+    u32x4 v[PER_LANE];
+#pragma unroll
+    for (int j = 0; j < PER_LANE; ++j) {
+        v[j] = (u32x4){0u, 0u, 0u, 0u};
+        if (src[j] >= 0) v[j] = table[src[j]];
+    }
+#pragma unroll
+    for (int j = 0; j < PER_LANE; ++j) {
+        const int c = lane + 64 * j;
+        if (n0 + c / CPR < n) __builtin_nontemporal_store(v[j], out + n0 * CPR + c);
+    }
+}
+
+// Any row size (multiple of 16 B, at most 64 chunks): one chunk per lane over
+// the flattened output.
+__global__ __launch_bounds__(256) void gather_rows_generic_kernel(const u32x4* __restrict__ table,
+                                                                  int64_t row_begin, uint64_t num_rows,
+                                                                  const int64_t* __restrict__ rows, int64_t n,
+                                                                  int cpr, u32x4* __restrict__ out,
+                                                                  int64_t* __restrict__ status) {
+    const int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (e >= n * cpr) return;
+    const int64_t i = e / cpr;
+    const int k = (int)(e - i * cpr);
+    const uint64_t local = (uint64_t)rows[i] - (uint64_t)row_begin;
+    u32x4 v = (u32x4){0u, 0u, 0u, 0u};
+    if (local < num_rows)
+        v = table[(int64_t)local * cpr + k];
+    else if (k == 0)
+        report_bad(status, i);
+    __builtin_nontemporal_store(v, out + e);
+}
+
+__global__ void status_init_kernel(int64_t* status) { *status = -1; }
+
+}  // namespace
+
+hipError_t launch_status_init(int64_t* status, hipStream_t stream) {
+    if (!status) return hipSuccess;
+    hipLaunchKernelGGL(status_init_kernel, dim3(1), dim3(1), 0, stream, status);
+    return hipGetLastError();
+}
+
+hipError_t launch_gather(const void* table, int elem_bytes, int64_t row_begin, int64_t num_rows, int dim,
+                         const int64_t* rows, int64_t n, void* out, int64_t* status, hipStream_t stream) {
+    hipError_t err = launch_status_init(status, stream);
+    if (err != hipSuccess || n == 0) return err;
+    const int cpr = dim * elem_bytes / 16;
+    const u32x4* t = (const u32x4*)table;
+    u32x4* o = (u32x4*)out;
+    const int block = 256, waves_per_block = block / 64;
+    if (cpr == 20) {
+        const int64_t waves = (n + 15) / 16;
+        const int64_t grid = (waves + waves_per_block - 1) / waves_per_block;
+        hipLaunchKernelGGL((gather_rows_kernel<20, 16>), dim3((unsigned)grid), dim3(block), 0, stream, t,
+                           row_begin, (uint64_t)num_rows, rows, n, o, status);
+    } else if (cpr == 40) {
+        const int64_t waves = (n + 7) / 8;
+        const int64_t grid = (waves + waves_per_block - 1) / waves_per_block;
+        hipLaunchKernelGGL((gather_rows_kernel<40, 8>), dim3((unsigned)grid), dim3(block), 0, stream, t,
+                           row_begin, (uint64_t)num_rows, rows, n, o, status);
+    } else {
+        const int64_t grid = (n * cpr + block - 1) / block;
+        hipLaunchKernelGGL(gather_rows_generic_kernel, dim3((unsigned)grid), dim3(block), 0, stream, t,
+                           row_begin, (uint64_t)num_rows, rows, n, cpr, o, status);
+    }
+    return hipGetLastError();
+}
+
+}  // namespace engram

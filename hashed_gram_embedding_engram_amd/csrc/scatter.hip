@@ -1,0 +1,611 @@
+// Owner-local gradient scatter-add for gfx950: the backward of the row gather.
+//
+// Engram API page ("nemo_automodel.components.models.qwen3_8_flash_next.engram"),
+// Qwen3_8_FlashNextOwnerShardedEmbedding: the backward route brings each
+// lookup's output gradient back to the row's owner, which alone accumulates
+// the row's gradient (also the model-coverage page "Qwen3.8-Flash-Next",
+// Validated Configuration).  For every distinct owned row r the result is
+// the sum of grad_out[i] over the lookups i of r.
+//
+// Hot rows (Zipf token streams repeat the same n-grams thousands of times)
+// must not serialise on atomics, and the sums must not depend on scheduling.
+// So the path sorts instead of atomically adding:
+//   1. keys     key = row - row_begin (or the sentinel num_rows for a row out
+//               of range), value = lookup index; per-tile histogram of the
+//               first digit in the same pass.
+//   2. sort     stable LSD radix sort of (key, index), 8-bit digits, as many
+//               passes as the bit length of num_rows needs (29 bits -> 4).
+//               Per pass: tile histograms, a per-digit scan over tiles, and a
+//               stable scatter that ranks digits inside each wave with ballots
+//               (no atomics) and writes each tile digit-grouped through LDS.
+//   3. runs     run starts per slice of S sorted entries and their prefix
+//               sum: the unique-row index of every run (compact output).
+//   4. reduce   one worker (CPR lanes, one 16-byte chunk of the row each)
+//               per slice walks its S entries in order, accumulating the
+//               gradient rows in fp64.  A run that ends inside the slice is
+//               written once; a run cut by a slice edge leaves an fp64 partial.
+//   5. fix-up   the slice where a cut run starts adds the partials of the
+//               following slices in slice order and writes the run.
+// Every step has a fixed order, so two calls give bit-identical results.
+#include "engram_internal.h"
+
+namespace engram {
+namespace {
+
+constexpr int kBlock = 256;                       // threads per block, 4 waves
+constexpr int kItems = 16;                        // keys per thread in a sort tile
+constexpr int kTile = kBlock * kItems;            // 4096 keys per sort tile
+constexpr int kWaveSpan = 64 * kItems;            // contiguous keys owned by one wave
+constexpr int kRadix = 256;
+constexpr uint32_t kSlice = 256;                  // sorted entries per reduce worker
+constexpr uint32_t kFlagHead = 1, kFlagWhole = 2, kFlagTail = 4;
+
+struct Layout {
+    size_t keys_a, keys_b, vals_a, vals_b, hist, digit_total, counters, slice_runs, slice_base, slice_flags,
+        carry_head, carry_tail, total;
+    int64_t num_tiles, num_slices;
+};
+
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+Layout make_layout(int64_t n, int dim) {
+    Layout L;
+    L.num_tiles = (n + kTile - 1) / kTile;
+    L.num_slices = (n + kSlice - 1) / kSlice;
+    size_t off = 0;
+    auto take = [&](size_t bytes) { size_t at = off; off = align256(off + bytes); return at; };
+    L.keys_a = take(4 * (size_t)n);
+    L.keys_b = take(4 * (size_t)n);
+    L.vals_a = take(4 * (size_t)n);
+    L.vals_b = take(4 * (size_t)n);
+    L.hist = take(4 * (size_t)kRadix * (size_t)L.num_tiles);
+    L.digit_total = take(4 * kRadix);
+    L.counters = take(16);
+    L.slice_runs = take(4 * (size_t)L.num_slices);
+    L.slice_base = take(4 * (size_t)L.num_slices);
+    L.slice_flags = take(4 * (size_t)L.num_slices);
+    L.carry_head = take(8 * (size_t)L.num_slices * (size_t)dim);
+    L.carry_tail = take(8 * (size_t)L.num_slices * (size_t)dim);
+    L.total = off;
+    return L;
+}
+
+__device__ __forceinline__ uint64_t lanemask_lt(int lane) { return (1ull << lane) - 1ull; }
+
+// Lanes of the wave whose 8-bit digit equals this lane's, among lanes with `live`.
+__device__ __forceinline__ uint64_t match_digit(uint32_t d, bool live) {
+    uint64_t m = __ballot(live);
+#pragma unroll
+    for (int b = 0; b < 8; ++b) {
+        const bool bit = (d >> b) & 1u;
+        const uint64_t bb = __ballot(bit);
+        m &= bit ? bb : ~bb;
+    }
+    return m;
+}
+
+// Exclusive prefix sum over the 256 threads of a block; *total gets the sum.
+__device__ __forceinline__ uint32_t block_exclusive_scan(uint32_t v, uint32_t* total, uint32_t* s_tmp) {
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    uint32_t x = v;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+        const uint32_t y = __shfl_up(x, o, 64);
+        if (lane >= o) x += y;
+    }
+    if (lane == 63) s_tmp[w] = x;
+    __syncthreads();
+    uint32_t wave_off = 0, tot = 0;
+#pragma unroll
+    for (int k = 0; k < kBlock / 64; ++k) {
+        const uint32_t t = s_tmp[k];
+        if (k < w) wave_off += t;
+        tot += t;
+    }
+    __syncthreads();
+    *total = tot;
+    return wave_off + x - v;
+}
+
+__device__ __forceinline__ void report_bad(int64_t* status, int64_t idx) {
+    if (status) atomicMin((unsigned long long*)status, (unsigned long long)idx);
+}
+
+__global__ void scatter_init_kernel(int64_t* status, uint32_t* counters, int64_t* num_uniq) {
+    if (status) *status = -1;
+    counters[0] = 0;  // number of in-range lookups
+    if (num_uniq) *num_uniq = 0;
+}
+
+// Tile histogram of one digit (per-wave ballot aggregation, one LDS add per
+// distinct digit per wave instead of one per key).
+__device__ __forceinline__ void tile_histogram_add(uint32_t* s_cnt, uint32_t digit, bool live, int lane) {
+    const uint64_t peers = match_digit(digit, live);
+    if (live && (peers & lanemask_lt(lane)) == 0) atomicAdd(&s_cnt[digit], (uint32_t)__popcll(peers));
+}
+
+// Step 1: keys, lookup indices, digit-0 tile histograms, in-range count.
+__global__ __launch_bounds__(kBlock) void keys_kernel(const int64_t* __restrict__ rows, uint32_t n,
+                                                      int64_t row_begin, uint64_t num_rows,
+                                                      uint32_t* __restrict__ keys, uint32_t* __restrict__ vals,
+                                                      uint32_t* __restrict__ hist, uint32_t num_tiles,
+                                                      int64_t* __restrict__ status, uint32_t* __restrict__ counters) {
+    __shared__ uint32_t s_cnt[kRadix];
+    __shared__ uint32_t s_valid;
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    s_cnt[tid] = 0;
+    if (tid == 0) s_valid = 0;
+    __syncthreads();
+    const uint32_t base = blockIdx.x * (uint32_t)kTile + (uint32_t)w * kWaveSpan;
+    const uint32_t sentinel = (uint32_t)num_rows;
+    uint32_t my_valid = 0;
+#pragma unroll 4
+    for (int it = 0; it < kItems; ++it) {
+        const uint32_t e = base + (uint32_t)it * 64 + (uint32_t)lane;
+        const bool live = e < n;
+        uint32_t key = sentinel;
+        if (live) {
+            const uint64_t local = (uint64_t)rows[e] - (uint64_t)row_begin;
+            if (local < num_rows) {
+                key = (uint32_t)local;
+                ++my_valid;
+            } else {
+                report_bad(status, e);
+            }
+            keys[e] = key;
+            vals[e] = e;
+        }
+        tile_histogram_add(s_cnt, key & 0xFFu, live, lane);
+    }
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) my_valid += __shfl_xor(my_valid, o, 64);
+    if (lane == 0 && my_valid) atomicAdd(&s_valid, my_valid);
+    __syncthreads();
+    hist[(size_t)tid * num_tiles + blockIdx.x] = s_cnt[tid];
+    if (tid == 0 && s_valid) atomicAdd(&counters[0], s_valid);
+}
+
+// Tile histograms of the digit at `shift` (passes after the first).
+__global__ __launch_bounds__(kBlock) void upsweep_kernel(const uint32_t* __restrict__ keys, uint32_t n, int shift,
+                                                         uint32_t* __restrict__ hist, uint32_t num_tiles) {
+    __shared__ uint32_t s_cnt[kRadix];
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    s_cnt[tid] = 0;
+    __syncthreads();
+    const uint32_t base = blockIdx.x * (uint32_t)kTile + (uint32_t)w * kWaveSpan;
+#pragma unroll 4
+    for (int it = 0; it < kItems; ++it) {
+        const uint32_t e = base + (uint32_t)it * 64 + (uint32_t)lane;
+        const bool live = e < n;
+        const uint32_t key = live ? keys[e] : 0u;
+        tile_histogram_add(s_cnt, (key >> shift) & 0xFFu, live, lane);
+    }
+    __syncthreads();
+    hist[(size_t)tid * num_tiles + blockIdx.x] = s_cnt[tid];
+}
+
+// hist[d][tile] -> exclusive prefix over tiles (in place); digit_total[d] = sum.
+__global__ __launch_bounds__(kBlock) void digit_scan_kernel(uint32_t* __restrict__ hist, uint32_t num_tiles,
+                                                            uint32_t* __restrict__ digit_total) {
+    __shared__ uint32_t s_tmp[kBlock / 64];
+    uint32_t* row = hist + (size_t)blockIdx.x * num_tiles;
+    uint32_t running = 0;
+    for (uint32_t b = 0; b < num_tiles; b += kBlock) {
+        const uint32_t i = b + threadIdx.x;
+        const uint32_t v = i < num_tiles ? row[i] : 0u;
+        uint32_t tot;
+        const uint32_t ex = block_exclusive_scan(v, &tot, s_tmp);
+        if (i < num_tiles) row[i] = running + ex;
+        running += tot;
+    }
+    if (threadIdx.x == 0) digit_total[blockIdx.x] = running;
+}
+
+// One stable scatter pass of the LSD radix sort.
+__global__ __launch_bounds__(kBlock) void downsweep_kernel(const uint32_t* __restrict__ keys_in,
+                                                           const uint32_t* __restrict__ vals_in,
+                                                           uint32_t* __restrict__ keys_out,
+                                                           uint32_t* __restrict__ vals_out, uint32_t n, int shift,
+                                                           const uint32_t* __restrict__ hist,
+                                                           const uint32_t* __restrict__ digit_total,
+                                                           uint32_t num_tiles) {
+    __shared__ uint32_t s_keys[kTile];
+    __shared__ uint32_t s_vals[kTile];
+    __shared__ uint32_t s_wave_cnt[kBlock / 64][kRadix];
+    __shared__ uint32_t s_digit_start[kRadix];
+    __shared__ uint32_t s_global[kRadix];
+    __shared__ uint32_t s_tmp[kBlock / 64];
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    for (int i = tid; i < (kBlock / 64) * kRadix; i += kBlock) (&s_wave_cnt[0][0])[i] = 0;
+    __syncthreads();
+
+    const uint32_t tile_base = blockIdx.x * (uint32_t)kTile;
+    const uint32_t base = tile_base + (uint32_t)w * kWaveSpan;
+    uint32_t key[kItems], val[kItems], rank[kItems];
+#pragma unroll
+    for (int it = 0; it < kItems; ++it) {
+        const uint32_t e = base + (uint32_t)it * 64 + (uint32_t)lane;
+        const bool live = e < n;
+        key[it] = live ? keys_in[e] : 0u;
+        val[it] = live ? vals_in[e] : 0u;
+    }
+    // Rank every key among the equal digits before it in this wave's span:
+    // items are visited in index order and the lowest lane of each digit group
+    // advances the wave's counter for that digit.
+#pragma unroll
+    for (int it = 0; it < kItems; ++it) {
+        const bool live = base + (uint32_t)it * 64 + (uint32_t)lane < n;
+        const uint32_t d = (key[it] >> shift) & 0xFFu;
+        const uint64_t peers = match_digit(d, live);
+        const uint32_t before = (uint32_t)__popcll(peers & lanemask_lt(lane));
+        uint32_t cnt = 0;
+        if (live) cnt = s_wave_cnt[w][d];
+        rank[it] = cnt + before;
+        if (live && before == 0) s_wave_cnt[w][d] = cnt + (uint32_t)__popcll(peers);
+    }
+    __syncthreads();
+    // Per digit: offsets of the waves inside the tile and the tile total.
+    {
+        const int d = tid;
+        uint32_t sum = 0;
+#pragma unroll
+        for (int k = 0; k < kBlock / 64; ++k) {
+            const uint32_t c = s_wave_cnt[k][d];
+            s_wave_cnt[k][d] = sum;
+            sum += c;
+        }
+        uint32_t tot;
+        const uint32_t start = block_exclusive_scan(sum, &tot, s_tmp);
+        s_digit_start[d] = start;
+        uint32_t tot2;
+        const uint32_t digit_base = block_exclusive_scan(digit_total[d], &tot2, s_tmp);
+        s_global[d] = digit_base + hist[(size_t)d * num_tiles + blockIdx.x];
+    }
+    __syncthreads();
+#pragma unroll
+    for (int it = 0; it < kItems; ++it) {
+        const bool live = base + (uint32_t)it * 64 + (uint32_t)lane < n;
+        if (live) {
+            const uint32_t d = (key[it] >> shift) & 0xFFu;
+            const uint32_t pos = s_digit_start[d] + s_wave_cnt[w][d] + rank[it];
+            s_keys[pos] = key[it];
+            s_vals[pos] = val[it];
+        }
+    }
+    __syncthreads();
+    const uint32_t count = min((uint32_t)kTile, n - tile_base);
+    for (uint32_t j = tid; j < count; j += kBlock) {
+        const uint32_t k = s_keys[j];
+        const uint32_t d = (k >> shift) & 0xFFu;
+        const uint32_t g = s_global[d] + (j - s_digit_start[d]);
+        if (g < n) {  // always true for a consistent histogram; keeps every store in bounds
+            keys_out[g] = k;
+            vals_out[g] = s_vals[j];
+        }
+    }
+}
+
+// Step 3a: number of runs that start in each slice of sorted in-range keys.
+__global__ __launch_bounds__(kBlock) void run_count_kernel(const uint32_t* __restrict__ keys,
+                                                           const uint32_t* __restrict__ counters,
+                                                           uint32_t* __restrict__ slice_runs) {
+    __shared__ uint32_t s_part[kBlock / 64];
+    const uint32_t nv = counters[0];
+    const uint32_t i = blockIdx.x * kSlice + threadIdx.x;
+    const bool start = i < nv && (i == 0 || keys[i] != keys[i - 1]);
+    const uint64_t b = __ballot(start);
+    if ((threadIdx.x & 63) == 0) s_part[threadIdx.x >> 6] = (uint32_t)__popcll(b);
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        uint32_t s = 0;
+        for (int k = 0; k < kBlock / 64; ++k) s += s_part[k];
+        slice_runs[blockIdx.x] = s;
+    }
+}
+
+// Step 3b: exclusive prefix of the slice run counts (one block); the total is
+// the number of distinct rows.
+__global__ __launch_bounds__(kBlock) void slice_scan_kernel(const uint32_t* __restrict__ slice_runs,
+                                                            uint32_t num_slices, uint32_t* __restrict__ slice_base,
+                                                            int64_t* __restrict__ num_uniq) {
+    __shared__ uint32_t s_tmp[kBlock / 64];
+    uint32_t running = 0;
+    for (uint32_t b = 0; b < num_slices; b += kBlock) {
+        const uint32_t i = b + threadIdx.x;
+        const uint32_t v = i < num_slices ? slice_runs[i] : 0u;
+        uint32_t tot;
+        const uint32_t ex = block_exclusive_scan(v, &tot, s_tmp);
+        if (i < num_slices) slice_base[i] = running + ex;
+        running += tot;
+    }
+    if (threadIdx.x == 0 && num_uniq) *num_uniq = running;
+}
+
+// 16 bytes of gradient -> EPC fp64 addends (bf16 = upper half of a binary32).
+template <bool BF16>
+__device__ __forceinline__ void accumulate(double* acc, u32x4 x) {
+    if (BF16) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            acc[2 * q] += (double)__uint_as_float(x[q] << 16);
+            acc[2 * q + 1] += (double)__uint_as_float(x[q] & 0xFFFF0000u);
+        }
+    } else {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) acc[q] += (double)__uint_as_float(x[q]);
+    }
+}
+
+template <int EPC>
+__device__ __forceinline__ void store_partial(double* dst, const double* acc) {
+#pragma unroll
+    for (int e = 0; e < EPC; e += 2) {
+        double __attribute__((ext_vector_type(2))) v;
+        v.x = acc[e];
+        v.y = acc[e + 1];
+        *(double __attribute__((ext_vector_type(2)))*)(dst + e) = v;
+    }
+}
+
+template <int EPC>
+__device__ __forceinline__ void add_partial(double* acc, const double* src) {
+#pragma unroll
+    for (int e = 0; e < EPC; e += 2) {
+        const double __attribute__((ext_vector_type(2))) v = *(const double __attribute__((ext_vector_type(2)))*)(src + e);
+        acc[e] += v.x;
+        acc[e + 1] += v.y;
+    }
+}
+
+// Final write of one run's chunk: dense RMW (fp64 add, one rounding) or compact.
+// The key < num_rows and u < n checks hold for every run of a correct sort;
+// they keep each store in bounds regardless.
+template <int EPC, bool DENSE>
+__device__ __forceinline__ void write_run(const double* acc, uint32_t key, uint32_t u, int c, int dim, uint32_t n,
+                                          uint32_t num_rows, int64_t row_begin, float* grad_dense,
+                                          int64_t* uniq_rows, float* uniq_grad) {
+    typedef float f32x4 __attribute__((ext_vector_type(4)));
+    if (DENSE ? key >= num_rows : u >= n) return;
+    if (DENSE) {
+        f32x4* g = (f32x4*)(grad_dense + (size_t)key * dim + c * EPC);
+#pragma unroll
+        for (int q = 0; q < EPC / 4; ++q) {
+            f32x4 old = g[q], nw;
+            nw.x = (float)((double)old.x + acc[4 * q]);
+            nw.y = (float)((double)old.y + acc[4 * q + 1]);
+            nw.z = (float)((double)old.z + acc[4 * q + 2]);
+            nw.w = (float)((double)old.w + acc[4 * q + 3]);
+            g[q] = nw;
+        }
+    } else {
+        if (c == 0) uniq_rows[u] = (int64_t)key + row_begin;
+        f32x4* g = (f32x4*)(uniq_grad + (size_t)u * dim + c * EPC);
+#pragma unroll
+        for (int q = 0; q < EPC / 4; ++q) {
+            f32x4 v;
+            v.x = (float)acc[4 * q];
+            v.y = (float)acc[4 * q + 1];
+            v.z = (float)acc[4 * q + 2];
+            v.w = (float)acc[4 * q + 3];
+            __builtin_nontemporal_store(v, g + q);
+        }
+    }
+}
+
+constexpr int kReduceBatch = 8;  // sorted entries whose gradient chunks are in flight per lane
+
+// Step 4.  Worker = CPR consecutive lanes (one 16-byte chunk of the row each);
+// 64 / CPR workers per wave (bf16 x 160: 3 workers of 20 lanes).  CPR_T == 0
+// takes the chunk count at run time.
+template <int CPR_T, bool BF16, bool DENSE>
+__global__ __launch_bounds__(kBlock) void segment_reduce_kernel(
+    const uint32_t* __restrict__ keys, const uint32_t* __restrict__ vals, const uint32_t* __restrict__ counters,
+    const u32x4* __restrict__ dy, uint32_t n, uint32_t num_rows, int cpr_rt, int dim, uint32_t num_slices,
+    const uint32_t* __restrict__ slice_base, int64_t row_begin, float* __restrict__ grad_dense,
+    int64_t* __restrict__ uniq_rows, float* __restrict__ uniq_grad, double* __restrict__ carry_head,
+    double* __restrict__ carry_tail, uint32_t* __restrict__ slice_flags) {
+    constexpr int EPC = BF16 ? 8 : 4;
+    const int cpr = CPR_T ? CPR_T : cpr_rt;
+    const int wpw = 64 / cpr;
+    const int lane = threadIdx.x & 63;
+    const int sub = lane / cpr;
+    const int c = lane - sub * cpr;
+    const int64_t wave = (int64_t)blockIdx.x * (kBlock / 64) + (threadIdx.x >> 6);
+    const int64_t j = wave * wpw + sub;
+    if (sub >= wpw || j >= num_slices) return;
+    const uint32_t nv = counters[0];
+    const uint32_t s0 = (uint32_t)j * kSlice;
+    if (s0 >= nv) {
+        if (c == 0) slice_flags[j] = 0;
+        return;
+    }
+    const uint32_t s1 = min(s0 + kSlice, nv);
+    bool head_open = s0 > 0 && keys[s0 - 1] == keys[s0];
+    uint32_t u = slice_base[j];
+    uint32_t flags = 0;
+    double acc[EPC];
+#pragma unroll
+    for (int e = 0; e < EPC; ++e) acc[e] = 0.0;
+
+    for (uint32_t i = s0; i < s1; i += kReduceBatch) {
+        uint32_t kk[kReduceBatch + 1], vv[kReduceBatch];
+        u32x4 x[kReduceBatch];
+#pragma unroll
+        for (int b = 0; b <= kReduceBatch; ++b) {
+            const uint32_t p = i + b;
+            kk[b] = p < nv ? keys[p] : 0xFFFFFFFFu;  // the entry after the batch decides its last run
+        }
+#pragma unroll
+        for (int b = 0; b < kReduceBatch; ++b) vv[b] = (i + b < s1) ? vals[i + b] : 0u;
+#pragma unroll
+        for (int b = 0; b < kReduceBatch; ++b) {
+            x[b] = (u32x4){0u, 0u, 0u, 0u};
+            if (i + b < s1 && vv[b] < n) x[b] = dy[(size_t)vv[b] * cpr + c];
+        }
+#pragma unroll
+        for (int b = 0; b < kReduceBatch; ++b) {
+            const uint32_t p = i + b;
+            if (p >= s1) break;
+            accumulate<BF16>(acc, x[b]);
+            const bool next_same = (p + 1 < nv) && kk[b + 1] == kk[b];
+            if (p + 1 < s1 && next_same) continue;
+            if (head_open) {
+                // first run of the slice, begun in an earlier slice
+                store_partial<EPC>(carry_head + (size_t)j * dim + c * EPC, acc);
+                flags |= kFlagHead | (next_same ? kFlagWhole : 0u);
+                head_open = false;
+            } else if (next_same) {
+                // begins here and runs on into the next slice
+                store_partial<EPC>(carry_tail + (size_t)j * dim + c * EPC, acc);
+                flags |= kFlagTail;
+                ++u;
+            } else {
+                write_run<EPC, DENSE>(acc, kk[b], u, c, dim, n, num_rows, row_begin, grad_dense, uniq_rows,
+                                      uniq_grad);
+                ++u;
+            }
+#pragma unroll
+            for (int e = 0; e < EPC; ++e) acc[e] = 0.0;
+        }
+    }
+    if (c == 0) slice_flags[j] = flags;
+}
+
+// Step 5: runs cut by slice edges, summed in slice order by the slice where
+// they begin.
+template <int CPR_T, bool BF16, bool DENSE>
+__global__ __launch_bounds__(kBlock) void carry_fixup_kernel(
+    const uint32_t* __restrict__ keys, uint32_t n, uint32_t num_rows, int cpr_rt, int dim, uint32_t num_slices,
+    const uint32_t* __restrict__ slice_runs, const uint32_t* __restrict__ slice_base,
+    const uint32_t* __restrict__ slice_flags, const double* __restrict__ carry_head,
+    const double* __restrict__ carry_tail, int64_t row_begin, float* __restrict__ grad_dense,
+    int64_t* __restrict__ uniq_rows, float* __restrict__ uniq_grad) {
+    constexpr int EPC = BF16 ? 8 : 4;
+    const int cpr = CPR_T ? CPR_T : cpr_rt;
+    const int wpw = 64 / cpr;
+    const int lane = threadIdx.x & 63;
+    const int sub = lane / cpr;
+    const int c = lane - sub * cpr;
+    const int64_t wave = (int64_t)blockIdx.x * (kBlock / 64) + (threadIdx.x >> 6);
+    const int64_t j = wave * wpw + sub;
+    if (sub >= wpw || j >= num_slices) return;
+    if (!(slice_flags[j] & kFlagTail)) return;
+    double acc[EPC];
+#pragma unroll
+    for (int e = 0; e < EPC; ++e) acc[e] = 0.0;
+    add_partial<EPC>(acc, carry_tail + (size_t)j * dim + c * EPC);
+    for (int64_t k = j + 1; k < num_slices; ++k) {
+        add_partial<EPC>(acc, carry_head + (size_t)k * dim + c * EPC);
+        if (!(slice_flags[k] & kFlagWhole)) break;
+    }
+    const uint32_t key = keys[(uint32_t)(j + 1) * kSlice - 1];
+    const uint32_t u = slice_base[j] + slice_runs[j] - 1;
+    write_run<EPC, DENSE>(acc, key, u, c, dim, n, num_rows, row_begin, grad_dense, uniq_rows, uniq_grad);
+}
+
+template <int CPR_T, bool BF16, bool DENSE>
+hipError_t launch_reduce(const Layout& L, char* ws, const void* grad_out, uint32_t n, uint32_t num_rows, int cpr,
+                         int dim, int64_t row_begin,
+                         float* grad_dense, int64_t* uniq_rows, float* uniq_grad, const uint32_t* sorted_keys,
+                         const uint32_t* sorted_vals, hipStream_t stream) {
+    const int wpw = 64 / cpr;
+    const int64_t waves = (L.num_slices + wpw - 1) / wpw;
+    const int64_t grid = (waves + (kBlock / 64) - 1) / (kBlock / 64);
+    const uint32_t ns = (uint32_t)L.num_slices;
+    hipLaunchKernelGGL((segment_reduce_kernel<CPR_T, BF16, DENSE>), dim3((unsigned)grid), dim3(kBlock), 0, stream,
+                       sorted_keys, sorted_vals, (const uint32_t*)(ws + L.counters), (const u32x4*)grad_out, n,
+                       num_rows, cpr, dim, ns, (const uint32_t*)(ws + L.slice_base), row_begin, grad_dense, uniq_rows, uniq_grad,
+                       (double*)(ws + L.carry_head), (double*)(ws + L.carry_tail),
+                       (uint32_t*)(ws + L.slice_flags));
+    hipError_t err = hipGetLastError();
+    if (err != hipSuccess) return err;
+    hipLaunchKernelGGL((carry_fixup_kernel<CPR_T, BF16, DENSE>), dim3((unsigned)grid), dim3(kBlock), 0, stream,
+                       sorted_keys, n, num_rows, cpr, dim, ns, (const uint32_t*)(ws + L.slice_runs),
+                       (const uint32_t*)(ws + L.slice_base), (const uint32_t*)(ws + L.slice_flags),
+                       (const double*)(ws + L.carry_head), (const double*)(ws + L.carry_tail), row_begin,
+                       grad_dense, uniq_rows, uniq_grad);
+    return hipGetLastError();
+}
+
+template <bool BF16, bool DENSE>
+hipError_t dispatch_reduce(const Layout& L, char* ws, const void* grad_out, uint32_t n, uint32_t num_rows, int cpr,
+                           int dim, int64_t row_begin,
+                           float* grad_dense, int64_t* uniq_rows, float* uniq_grad, const uint32_t* k,
+                           const uint32_t* v, hipStream_t stream) {
+    if (BF16 && cpr == 20)
+        return launch_reduce<20, BF16, DENSE>(L, ws, grad_out, n, num_rows, cpr, dim, row_begin, grad_dense, uniq_rows,
+                                              uniq_grad, k, v, stream);
+    if (!BF16 && cpr == 40)
+        return launch_reduce<40, BF16, DENSE>(L, ws, grad_out, n, num_rows, cpr, dim, row_begin, grad_dense, uniq_rows,
+                                              uniq_grad, k, v, stream);
+    return launch_reduce<0, BF16, DENSE>(L, ws, grad_out, n, num_rows, cpr, dim, row_begin, grad_dense, uniq_rows, uniq_grad,
+                                         k, v, stream);
+}
+
+}  // namespace
+
+size_t scatter_workspace_bytes(int64_t n, int64_t num_rows, int dim) {
+    (void)num_rows;
+    return make_layout(n, dim).total;
+}
+
+hipError_t launch_scatter_add(const int64_t* rows, int64_t n, const void* grad_out, int elem_bytes, int dim,
+                              int64_t row_begin, int64_t num_rows, float* grad_dense, int64_t* uniq_rows,
+                              float* uniq_grad, int64_t* num_uniq, void* workspace, int64_t* status,
+                              hipStream_t stream) {
+    const Layout L = make_layout(n, dim);
+    char* ws = (char*)workspace;
+    uint32_t* counters = (uint32_t*)(ws + L.counters);
+    hipLaunchKernelGGL(scatter_init_kernel, dim3(1), dim3(1), 0, stream, status, counters, num_uniq);
+    hipError_t err = hipGetLastError();
+    if (err != hipSuccess || n == 0) return err;
+
+    const uint32_t nn = (uint32_t)n, tiles = (uint32_t)L.num_tiles;
+    uint32_t* hist = (uint32_t*)(ws + L.hist);
+    uint32_t* digit_total = (uint32_t*)(ws + L.digit_total);
+    uint32_t *k_cur = (uint32_t*)(ws + L.keys_a), *k_nxt = (uint32_t*)(ws + L.keys_b);
+    uint32_t *v_cur = (uint32_t*)(ws + L.vals_a), *v_nxt = (uint32_t*)(ws + L.vals_b);
+
+    hipLaunchKernelGGL(keys_kernel, dim3(tiles), dim3(kBlock), 0, stream, rows, nn, row_begin, (uint64_t)num_rows,
+                       k_cur, v_cur, hist, tiles, status, counters);
+    if ((err = hipGetLastError()) != hipSuccess) return err;
+
+    // The sentinel num_rows must sort after every valid key: sort its bit length.
+    int bits = 0;
+    while (bits < 32 && ((uint64_t)num_rows >> bits) != 0) ++bits;
+    for (int shift = 0; shift < bits; shift += 8) {
+        if (shift > 0) {
+            hipLaunchKernelGGL(upsweep_kernel, dim3(tiles), dim3(kBlock), 0, stream, k_cur, nn, shift, hist, tiles);
+            if ((err = hipGetLastError()) != hipSuccess) return err;
+        }
+        hipLaunchKernelGGL(digit_scan_kernel, dim3(kRadix), dim3(kBlock), 0, stream, hist, tiles, digit_total);
+        hipLaunchKernelGGL(downsweep_kernel, dim3(tiles), dim3(kBlock), 0, stream, k_cur, v_cur, k_nxt, v_nxt, nn,
+                           shift, hist, digit_total, tiles);
+        if ((err = hipGetLastError()) != hipSuccess) return err;
+        uint32_t* t = k_cur; k_cur = k_nxt; k_nxt = t;
+        t = v_cur; v_cur = v_nxt; v_nxt = t;
+    }
+
+    const uint32_t ns = (uint32_t)L.num_slices;
+    hipLaunchKernelGGL(run_count_kernel, dim3(ns), dim3(kBlock), 0, stream, k_cur, counters,
+                       (uint32_t*)(ws + L.slice_runs));
+    hipLaunchKernelGGL(slice_scan_kernel, dim3(1), dim3(kBlock), 0, stream, (const uint32_t*)(ws + L.slice_runs), ns,
+                       (uint32_t*)(ws + L.slice_base), num_uniq);
+    if ((err = hipGetLastError()) != hipSuccess) return err;
+
+    const int cpr = dim * elem_bytes / 16;
+    const bool bf16 = elem_bytes == 2, dense = grad_dense != nullptr;
+    if (bf16 && dense)
+        return dispatch_reduce<true, true>(L, ws, grad_out, nn, (uint32_t)num_rows, cpr, dim, row_begin, grad_dense,
+                                           uniq_rows, uniq_grad, k_cur, v_cur, stream);
+    if (bf16)
+        return dispatch_reduce<true, false>(L, ws, grad_out, nn, (uint32_t)num_rows, cpr, dim, row_begin, grad_dense,
+                                            uniq_rows, uniq_grad, k_cur, v_cur, stream);
+    if (dense)
+        return dispatch_reduce<false, true>(L, ws, grad_out, nn, (uint32_t)num_rows, cpr, dim, row_begin, grad_dense,
+                                            uniq_rows, uniq_grad, k_cur, v_cur, stream);
+    return dispatch_reduce<false, false>(L, ws, grad_out, nn, (uint32_t)num_rows, cpr, dim, row_begin, grad_dense,
+                                         uniq_rows, uniq_grad, k_cur, v_cur, stream);
+}
+
+}  // namespace engram

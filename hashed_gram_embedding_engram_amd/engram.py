@@ -1,0 +1,237 @@
+"""Thin Python binding of libengram (include/engram.h): argument marshalling only.
+
+Every step of the path runs in the library's HIP kernels.  torch supplies
+device memory and the current HIP stream; nothing here computes on tensors.
+If the library is missing, loading fails with an error — there is no CPU or
+PyTorch fallback.
+
+The functions keep the names of the C ABI (``engram_hash``, ``engram_hash_slice``,
+``engram_gather``, ``engram_scatter_add``, ``engram_scatter_add_workspace``) and
+take torch tensors in place of raw pointers.
+"""
+import ctypes
+import os
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libengram.so")
+
+ENGRAM_OK, ENGRAM_EINVAL, ENGRAM_EDTYPE, ENGRAM_EWORKSPACE, ENGRAM_ELAUNCH, ENGRAM_ESPEC = 0, -1, -2, -3, -4, -5
+ENGRAM_F32, ENGRAM_BF16 = 0, 1
+MAX_NGRAM, MAX_HEADS = 8, 64
+
+# Released Qwen3.8-Flash-Next configuration (engram API page,
+# "nemo_automodel.components.models.qwen3_8_flash_next.engram": module data and
+# the Qwen3_8_FlashNextNGramEmbedding signature).  The page prints the first
+# eight head moduli and offsets before cutting the tuples off; the remaining
+# eight moduli continue the run of consecutive primes above 20,000,000 that the
+# printed ones start, and every offset is the running total of the moduli
+# before it.  Their sum, rounded up to a multiple of 128, is the printed
+# padded row count.
+QWEN3_8_FLASH_NEXT_LAYER_MULTIPLIERS = (23703573157769, 20109073645365, 8052911324071)
+QWEN3_8_FLASH_NEXT_NGRAM_HEAD_VOCAB_SIZES = (
+    20000003, 20000023, 20000033, 20000047, 20000059, 20000063, 20000069, 20000077,
+    20000081, 20000093, 20000107, 20000147, 20000153, 20000159, 20000161, 20000171)
+QWEN3_8_FLASH_NEXT_NGRAM_HEAD_OFFSETS = (
+    0, 20000003, 40000026, 60000059, 80000106, 100000165, 120000228, 140000297,
+    160000374, 180000455, 200000548, 220000655, 240000802, 260000955, 280001114, 300001275)
+QWEN3_8_FLASH_NEXT_NGRAM_PADDED_ROWS = 320001536
+QWEN3_8_FLASH_NEXT_EOS_TOKEN_ID = 248044
+QWEN3_8_FLASH_NEXT_EMBEDDING_DIM = 160
+
+
+class EngramHashSpec(ctypes.Structure):
+    """Mirror of ``engram_hash_spec``."""
+    _fields_ = [("ngram_size", ctypes.c_int32), ("heads_per_ngram", ctypes.c_int32),
+                ("eos_id", ctypes.c_int64), ("fill_id", ctypes.c_int64),
+                ("multipliers", ctypes.c_int64 * MAX_NGRAM), ("head_mod", ctypes.c_int64 * MAX_HEADS),
+                ("head_offset", ctypes.c_int64 * MAX_HEADS)]
+
+    @property
+    def num_heads(self):
+        return (self.ngram_size - 1) * self.heads_per_ngram
+
+
+def make_hash_spec(ngram_size, heads_per_ngram, eos_id, multipliers, head_mod, head_offset, fill_id=0):
+    s = EngramHashSpec()
+    s.ngram_size, s.heads_per_ngram = int(ngram_size), int(heads_per_ngram)
+    s.eos_id, s.fill_id = int(eos_id), int(fill_id)
+    if len(multipliers) > MAX_NGRAM or len(head_mod) > MAX_HEADS or len(head_offset) != len(head_mod):
+        raise ValueError("hash spec arrays too long or mismatched")
+    for k, m in enumerate(multipliers):
+        s.multipliers[k] = int(m)
+    for h, (m, o) in enumerate(zip(head_mod, head_offset)):
+        s.head_mod[h], s.head_offset[h] = int(m), int(o)
+    return s
+
+
+def qwen3_8_flash_next_spec(fill_id=0):
+    """The released hash configuration: 3-gram, 8 heads per order, EOS 248044."""
+    return make_hash_spec(3, 8, QWEN3_8_FLASH_NEXT_EOS_TOKEN_ID, QWEN3_8_FLASH_NEXT_LAYER_MULTIPLIERS,
+                          QWEN3_8_FLASH_NEXT_NGRAM_HEAD_VOCAB_SIZES, QWEN3_8_FLASH_NEXT_NGRAM_HEAD_OFFSETS,
+                          fill_id)
+
+
+_lib = None
+
+
+def load_library(path=LIB_PATH):
+    """Load libengram.so; raises if it has not been built (no fallback path exists)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise RuntimeError("libengram.so not found at %s: build it with "
+                           "`python -m hashed_gram_embedding_engram_amd.build`" % path)
+    lib = ctypes.CDLL(path)
+    p, i64, i32, sz = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_size_t
+    lib.engram_hash.restype = ctypes.c_int
+    lib.engram_hash.argtypes = [p, i64, i64, ctypes.POINTER(EngramHashSpec), p, p]
+    lib.engram_hash_slice.restype = ctypes.c_int
+    lib.engram_hash_slice.argtypes = [p, i64, i64, i64, i64, ctypes.POINTER(EngramHashSpec), p, p]
+    lib.engram_gather.restype = ctypes.c_int
+    lib.engram_gather.argtypes = [p, i32, i64, i64, i32, p, i64, p, p, p]
+    lib.engram_scatter_add_workspace.restype = sz
+    lib.engram_scatter_add_workspace.argtypes = [i64, i64, i32]
+    lib.engram_scatter_add.restype = ctypes.c_int
+    lib.engram_scatter_add.argtypes = [p, i64, p, i32, i32, i64, i64, p, p, p, p, p, sz, p, p]
+    lib.engram_strerror.restype = ctypes.c_char_p
+    lib.engram_strerror.argtypes = [ctypes.c_int]
+    _lib = lib
+    return lib
+
+
+class EngramError(RuntimeError):
+    pass
+
+
+def _check(rc, what):
+    if rc != ENGRAM_OK:
+        raise EngramError("%s: %s (%d)" % (what, load_library().engram_strerror(rc).decode(), rc))
+
+
+def _stream_handle(stream):
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _dev_ptr(t, name, dtype=None):
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError("%s must be a GPU tensor" % name)
+    if not t.is_contiguous():
+        raise ValueError("%s must be contiguous" % name)
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError("%s must be %s, got %s" % (name, dtype, t.dtype))
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _dtype_code(t):
+    if t.dtype == torch.float32:
+        return ENGRAM_F32
+    if t.dtype == torch.bfloat16:
+        return ENGRAM_BF16
+    raise ValueError("table and gradients must be float32 or bfloat16, got %s" % t.dtype)
+
+
+def _raise_on_status(status, what, rows):
+    bad = int(status.item())
+    if bad >= 0:
+        raise EngramError("%s: row id %d at lookup %d is outside the owned range" %
+                          (what, int(rows.reshape(-1)[bad].item()), bad))
+
+
+def engram_hash(tokens, spec, rows_out=None, stream=None):
+    """tokens: int64 [batch, seq] on the GPU -> int64 [batch, seq, H] global rows."""
+    lib = load_library()
+    if tokens.dim() != 2:
+        raise ValueError("tokens must be [batch, seq]")
+    batch, seq = tokens.shape
+    if rows_out is None:
+        rows_out = torch.empty((batch, seq, spec.num_heads), dtype=torch.int64, device=tokens.device)
+    _check(lib.engram_hash(_dev_ptr(tokens, "tokens", torch.int64), batch, seq, ctypes.byref(spec),
+                           _dev_ptr(rows_out, "rows_out", torch.int64), _stream_handle(stream)), "engram_hash")
+    return rows_out
+
+
+def engram_hash_slice(tokens, seq_begin, seq_end, spec, rows_out=None, stream=None):
+    """Rows of positions [seq_begin, seq_end) of every batch row, hashed with the full history."""
+    lib = load_library()
+    if tokens.dim() != 2:
+        raise ValueError("tokens must be [batch, seq]")
+    batch, seq = tokens.shape
+    if rows_out is None:
+        rows_out = torch.empty((batch, max(seq_end - seq_begin, 0), spec.num_heads), dtype=torch.int64,
+                               device=tokens.device)
+    _check(lib.engram_hash_slice(_dev_ptr(tokens, "tokens", torch.int64), batch, seq, seq_begin, seq_end,
+                                 ctypes.byref(spec), _dev_ptr(rows_out, "rows_out", torch.int64),
+                                 _stream_handle(stream)), "engram_hash_slice")
+    return rows_out
+
+
+def engram_gather(table, rows, row_begin=0, out=None, status=None, validate=True, stream=None):
+    """table: [num_rows, dim] (fp32/bf16) holding global rows [row_begin, row_begin+num_rows);
+    rows: int64 [...] -> out [..., dim].  With ``validate`` the call synchronises and
+    raises on an out-of-range row (the output row is zero in any case)."""
+    lib = load_library()
+    num_rows, dim = table.shape
+    n = rows.numel()
+    if out is None:
+        out = torch.empty(tuple(rows.shape) + (dim,), dtype=table.dtype, device=table.device)
+    if validate and status is None:
+        status = torch.empty((), dtype=torch.int64, device=table.device)
+    _check(lib.engram_gather(_dev_ptr(table, "table", table.dtype), _dtype_code(table), row_begin, num_rows, dim,
+                             _dev_ptr(rows, "rows", torch.int64), n, _dev_ptr(out, "out", table.dtype),
+                             _dev_ptr(status, "status", torch.int64), _stream_handle(stream)), "engram_gather")
+    if validate:
+        _raise_on_status(status, "engram_gather", rows)
+    return out
+
+
+def engram_scatter_add_workspace(n, num_rows, dim):
+    return int(load_library().engram_scatter_add_workspace(n, num_rows, dim))
+
+
+def engram_scatter_add(rows, grad_out, num_rows, row_begin=0, grad_dense=None, compact=None, workspace=None,
+                       status=None, validate=True, stream=None):
+    """Backward of engram_gather.
+
+    Dense form: pass ``grad_dense`` fp32 [num_rows, dim]; it is updated in place and returned.
+    Compact form (default): returns (uniq_rows int64 [U], uniq_grad fp32 [U, dim]); pass
+    ``compact=(uniq_rows [n], uniq_grad [n, dim], num_uniq [])`` to reuse buffers, in which
+    case the full buffers and the device count are returned without synchronising."""
+    lib = load_library()
+    dim = grad_out.shape[-1]
+    n = rows.numel()
+    dev = grad_out.device
+    if grad_out.numel() != n * dim:
+        raise ValueError("grad_out must hold one row per lookup")
+    if workspace is None:
+        workspace = torch.empty(engram_scatter_add_workspace(n, num_rows, dim), dtype=torch.uint8, device=dev)
+    if validate and status is None:
+        status = torch.empty((), dtype=torch.int64, device=dev)
+    own_compact = grad_dense is None and compact is None
+    if own_compact:
+        compact = (torch.empty(max(n, 1), dtype=torch.int64, device=dev),
+                   torch.empty((max(n, 1), dim), dtype=torch.float32, device=dev),
+                   torch.empty((), dtype=torch.int64, device=dev))
+    ur, ug, nu = compact if compact is not None else (None, None, None)
+    rc = lib.engram_scatter_add(_dev_ptr(rows, "rows", torch.int64), n, _dev_ptr(grad_out, "grad_out"),
+                                _dtype_code(grad_out), dim, row_begin, num_rows,
+                                _dev_ptr(grad_dense, "grad_dense", torch.float32),
+                                _dev_ptr(ur, "uniq_rows", torch.int64), _dev_ptr(ug, "uniq_grad", torch.float32),
+                                _dev_ptr(nu, "num_uniq", torch.int64), _dev_ptr(workspace, "workspace"),
+                                workspace.numel() * workspace.element_size(),
+                                _dev_ptr(status, "status", torch.int64), _stream_handle(stream))
+    _check(rc, "engram_scatter_add")
+    if validate:
+        _raise_on_status(status, "engram_scatter_add", rows)
+    if grad_dense is not None:
+        return grad_dense
+    if own_compact:
+        u = int(nu.item())
+        return ur[:u], ug[:u]
+    return ur, ug, nu

@@ -1,0 +1,157 @@
+/*
+ * engram.h — C ABI of the Engram n-gram embedding hot path on MI355X (gfx950).
+ *
+ * Three calls carry the whole path: raw token IDs -> hashed head rows
+ * (engram_hash), head rows -> table values (engram_gather), and output
+ * gradients -> per-row gradient sums (engram_scatter_add).
+ *
+ * Passages defining the operations ("engram API page" = the page titled
+ * nemo_automodel.components.models.qwen3_8_flash_next.engram; "model-coverage
+ * page" = the page titled Qwen3.8-Flash-Next):
+ *   - hash: engram API page, Qwen3_8_FlashNextNGramEmbedding (class
+ *     description, _hash_input_ids, _shift_right_after_eos);
+ *   - gather: engram API page, Qwen3_8_FlashNextNGramEmbedding._lookup_ngram_ids
+ *     and Qwen3_8_FlashNextOwnerShardedEmbedding (class description, forward):
+ *     an owner looks up only its contiguous rows [row_begin, row_begin+num_rows);
+ *   - scatter-add: the same class description and the model-coverage page,
+ *     Validated Configuration: the backward pass routes gradients back so that
+ *     only the owner accumulates each row's gradient;
+ *   - errors: engram API page, _validate_global_ids / _validate_received_ids:
+ *     an ID outside the owned range is an error reported with a diagnostic,
+ *     never clamped; the model-coverage page, Current Scope: GPU paths never
+ *     fall back silently.
+ *
+ * Conventions for every call:
+ *   - Pointers named "device" point to GPU memory owned by the caller; the
+ *     library allocates nothing and keeps no mutable global state, so calls on
+ *     different streams are independent and the library is thread-safe.
+ *   - Work is enqueued asynchronously on `stream` (0 = the null stream); a
+ *     returned ENGRAM_OK means "launched", results are ready when the stream is.
+ *   - Host-checkable argument errors return a negative engram_status at once
+ *     and enqueue nothing.
+ *   - Data errors (a row outside the owned range) never cause an out-of-bounds
+ *     access: gather writes a zero row for it, scatter-add drops it, and when
+ *     `status` is non-NULL the lowest offending lookup index is stored there
+ *     (-1 when every row is in range).  The library itself first sets
+ *     *status = -1 on the stream, so the caller needs no initialisation.
+ *   - Sizes are int64; all arrays are dense and row-major.
+ */
+#ifndef ENGRAM_H
+#define ENGRAM_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    ENGRAM_OK = 0,
+    ENGRAM_EINVAL = -1,     /* null pointer, negative or too large size, unsupported dim */
+    ENGRAM_EDTYPE = -2,     /* unknown element type */
+    ENGRAM_EWORKSPACE = -3, /* scatter-add workspace missing or smaller than required */
+    ENGRAM_ELAUNCH = -4,    /* the HIP runtime refused a kernel launch */
+    ENGRAM_ESPEC = -5       /* hash spec outside the supported range */
+} engram_status;
+
+typedef enum { ENGRAM_F32 = 0, ENGRAM_BF16 = 1 } engram_dtype;
+
+#define ENGRAM_MAX_NGRAM 8
+#define ENGRAM_MAX_HEADS 64
+
+/* Hash configuration: the constructor arguments of Qwen3_8_FlashNextNGramEmbedding
+ * (engram API page).  H = (ngram_size - 1) * heads_per_ngram heads; heads
+ * [0, heads_per_ngram) hash bigrams, the next heads_per_ngram trigrams, and so on.
+ *   ngram_size       largest n-gram order including the current token, 2..8 (released: 3)
+ *   heads_per_ngram  heads per order, >= 1, H <= 64 (released: 8)
+ *   eos_id           raw ID after which the context resets (released: 248044)
+ *   fill_id          value of a missing history token (before the sequence start
+ *                    or across an EOS); the page's description of it is cut off,
+ *                    0 is the value this project uses
+ *   multipliers[k]   signed int64 multiplier of the token k positions back, k < ngram_size
+ *   head_mod[h]      positive modulus of head h, 2 <= head_mod[h] <= 2^62
+ *   head_offset[h]   global row offset of head h, >= 0, head_offset[h] + head_mod[h] - 1
+ *                    must not overflow int64
+ * Each position's order-n mix is the 64-bit XOR of the wrapped products of the
+ * current token and its n-1 predecessors; row = mix mod head_mod (positive
+ * remainder) + head_offset. */
+typedef struct {
+    int32_t ngram_size;
+    int32_t heads_per_ngram;
+    int64_t eos_id;
+    int64_t fill_id;
+    int64_t multipliers[ENGRAM_MAX_NGRAM];
+    int64_t head_mod[ENGRAM_MAX_HEADS];
+    int64_t head_offset[ENGRAM_MAX_HEADS];
+} engram_hash_spec;
+
+/* Hash raw token IDs into global table rows (engram API page,
+ * Qwen3_8_FlashNextNGramEmbedding._hash_input_ids).
+ *   tokens    device int64 [batch][seq_len], raw tokenizer IDs (any int64 value)
+ *   spec      host pointer, read during the call only
+ *   rows_out  device int64 [batch][seq_len][H]
+ * Batch rows are independent; a packed (THD) stream is batch = 1 whose
+ * documents are separated by EOS.  batch * seq_len == 0 is a no-op.
+ * Returns ENGRAM_OK, ENGRAM_EINVAL or ENGRAM_ESPEC. */
+int engram_hash(const int64_t* tokens, int64_t batch, int64_t seq_len, const engram_hash_spec* spec,
+                int64_t* rows_out, hipStream_t stream);
+
+/* Hash the whole raw sequence but emit rows only for positions [seq_begin, seq_end)
+ * of every batch row (engram API page, _forward_global_slice): the two (in general
+ * ngram_size - 1) preceding tokens and EOS resets before seq_begin are honoured,
+ * so the slice equals columns [seq_begin, seq_end) of engram_hash on the full row.
+ *   tokens    device int64 [batch][seq_len]
+ *   rows_out  device int64 [batch][seq_end - seq_begin][H]
+ * Requires 0 <= seq_begin <= seq_end <= seq_len. */
+int engram_hash_slice(const int64_t* tokens, int64_t batch, int64_t seq_len, int64_t seq_begin,
+                      int64_t seq_end, const engram_hash_spec* spec, int64_t* rows_out,
+                      hipStream_t stream);
+
+/* Owner-local row gather (engram API page, Qwen3_8_FlashNextOwnerShardedEmbedding.forward
+ * on the owner's shard; _lookup_ngram_ids concatenates the H heads of a position,
+ * which is this output viewed as [..., H * dim]).
+ *   table     device [num_rows][dim] of `dtype`: global rows [row_begin, row_begin + num_rows)
+ *   rows      device int64 [n] global row IDs
+ *   out       device [n][dim] of `dtype`; out[i] = table[rows[i] - row_begin], bit for bit
+ *   status    device int64 scalar or NULL (see conventions)
+ * dim * element size must be a multiple of 16 bytes and at most 1024 bytes.
+ * Returns ENGRAM_OK, ENGRAM_EINVAL or ENGRAM_EDTYPE. */
+int engram_gather(const void* table, int32_t dtype, int64_t row_begin, int64_t num_rows, int32_t dim,
+                  const int64_t* rows, int64_t n, void* out, int64_t* status, hipStream_t stream);
+
+/* Bytes of device workspace engram_scatter_add needs for n lookups into a
+ * num_rows-row shard with rows of dim values (256-byte aligned start). */
+size_t engram_scatter_add_workspace(int64_t n, int64_t num_rows, int32_t dim);
+
+/* Owner-local gradient scatter-add: the backward of engram_gather.  For every
+ * distinct in-range row r, S[r] = sum of grad_out[i] over the lookups i with
+ * rows[i] == r, accumulated in fp64 in a fixed order (deterministic run to run)
+ * and rounded once to fp32.  Exactly one output form:
+ *   dense    grad_dense device fp32 [num_rows][dim]: grad_dense[r] = fp32(grad_dense[r] + S[r])
+ *            (the caller zeroes it, or passes an existing gradient to add to);
+ *            uniq_rows, uniq_grad, num_uniq must be NULL;
+ *   compact  uniq_rows device int64 [n], uniq_grad device fp32 [n][dim], num_uniq device
+ *            int64 scalar: the U distinct rows in ascending order (global IDs) and
+ *            their S; *num_uniq = U; entries past U are left untouched;
+ *            grad_dense must be NULL.
+ *   rows      device int64 [n] global row IDs (as given to engram_gather)
+ *   grad_out  device [n][dim] of `dtype` (the gradient of engram_gather's output)
+ *   workspace device, at least engram_scatter_add_workspace(n, num_rows, dim) bytes,
+ *             256-byte aligned; contents need no initialisation and are scratch
+ * Limits: n < 2^31, num_rows < 2^32 - 1, dim as for engram_gather.
+ * Returns ENGRAM_OK, ENGRAM_EINVAL, ENGRAM_EDTYPE or ENGRAM_EWORKSPACE. */
+int engram_scatter_add(const int64_t* rows, int64_t n, const void* grad_out, int32_t dtype, int32_t dim,
+                       int64_t row_begin, int64_t num_rows, float* grad_dense, int64_t* uniq_rows,
+                       float* uniq_grad, int64_t* num_uniq, void* workspace, size_t workspace_bytes,
+                       int64_t* status, hipStream_t stream);
+
+/* Static English text for an engram_status code. */
+const char* engram_strerror(int code);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* ENGRAM_H */

@@ -87,13 +87,12 @@ int64_t oracle_gather(const void* table, int32_t elem_bytes, int32_t dim, int64_
     int64_t first_bad = -1;
     for (int64_t i = 0; i < n; ++i) {
         char* dst = (char*)out + (size_t)i * row_bytes;
-        int64_t local = rows[i] - row_begin;
-        if (rows[i] < row_begin || local >= num_rows) {
+        if (rows[i] < row_begin || rows[i] - row_begin >= num_rows) {
             memset(dst, 0, row_bytes);
             if (first_bad < 0) first_bad = i;
             continue;
         }
-        memcpy(dst, (const char*)table + (size_t)local * row_bytes, row_bytes);
+        memcpy(dst, (const char*)table + (size_t)(rows[i] - row_begin) * row_bytes, row_bytes);
     }
     return first_bad;
 }
@@ -126,12 +125,11 @@ static int64_t sorted_valid(const int64_t* rows, int64_t n, int64_t row_begin, i
     int64_t m = 0;
     *first_bad = -1;
     for (int64_t i = 0; i < n; ++i) {
-        int64_t local = rows[i] - row_begin;
-        if (rows[i] < row_begin || local >= num_rows) {
+        if (rows[i] < row_begin || rows[i] - row_begin >= num_rows) {
             if (*first_bad < 0) *first_bad = i;
             continue;
         }
-        refs[m].row = local;
+        refs[m].row = rows[i] - row_begin;
         refs[m].idx = i;
         ++m;
     }

@@ -1,0 +1,140 @@
+"""The C-ABI library: it loads, exports every function include/engram.h declares,
+and rejects bad host arguments before enqueuing anything.  No GPU is touched:
+every call here fails host validation and returns before any HIP call."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import hashed_gram_embedding_engram_amd as E
+from hashed_gram_embedding_engram_amd import engram as B
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(B.LIB_PATH):
+        from hashed_gram_embedding_engram_amd import build
+        build.build()
+    return B.load_library()
+
+
+def declared_functions():
+    text = open(os.path.join(ROOT, "include", "engram.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?[A-Za-z_][A-Za-z0-9_]*\s*\*?\s*(engram_[a-z_]+)\s*\(", text, re.M)))
+
+
+def test_exports_every_declared_function(lib):
+    names = declared_functions()
+    assert {"engram_hash", "engram_hash_slice", "engram_gather", "engram_scatter_add",
+            "engram_scatter_add_workspace", "engram_strerror"} <= set(names)
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_status_codes_match_header(lib):
+    text = open(os.path.join(ROOT, "include", "engram.h")).read()
+    for name, val in re.findall(r"(ENGRAM_E?[A-Z]+)\s*=\s*(-?\d+)", text):
+        if hasattr(B, name):
+            assert getattr(B, name) == int(val), name
+    for code in (0, -1, -2, -3, -4, -5):
+        assert lib.engram_strerror(code) and lib.engram_strerror(code) != b"unknown engram status"
+    assert lib.engram_strerror(-99) == b"unknown engram status"
+
+
+def test_spec_struct_layout():
+    # int32, int32, int64 x2, int64[8], int64[64], int64[64]
+    assert ctypes.sizeof(B.EngramHashSpec) == 8 + 16 + 8 * 8 + 2 * 64 * 8
+
+
+def test_hash_rejects_bad_spec(lib):
+    s = E.qwen3_8_flash_next_spec()
+    fake = ctypes.c_void_p(0x1000)       # never dereferenced: validation fails first
+    for field, value, code in (("ngram_size", 1, B.ENGRAM_ESPEC), ("ngram_size", 9, B.ENGRAM_ESPEC),
+                               ("heads_per_ngram", 0, B.ENGRAM_ESPEC), ("heads_per_ngram", 65, B.ENGRAM_ESPEC)):
+        t = E.qwen3_8_flash_next_spec()
+        setattr(t, field, value)
+        assert lib.engram_hash(fake, 1, 4, ctypes.byref(t), fake, None) == code
+    for h, m in ((3, 1), (0, 0), (15, -7), (2, (1 << 62) + 1)):
+        t = E.qwen3_8_flash_next_spec()
+        t.head_mod[h] = m
+        assert lib.engram_hash(fake, 1, 4, ctypes.byref(t), fake, None) == B.ENGRAM_ESPEC
+    t = E.qwen3_8_flash_next_spec()
+    t.head_offset[5] = -1
+    assert lib.engram_hash(fake, 1, 4, ctypes.byref(t), fake, None) == B.ENGRAM_ESPEC
+    t = E.qwen3_8_flash_next_spec()
+    t.head_offset[5] = (1 << 63) - 5
+    assert lib.engram_hash(fake, 1, 4, ctypes.byref(t), fake, None) == B.ENGRAM_ESPEC
+    assert lib.engram_hash(None, 1, 4, ctypes.byref(s), fake, None) == B.ENGRAM_EINVAL
+    assert lib.engram_hash(fake, 1, 4, ctypes.byref(s), None, None) == B.ENGRAM_EINVAL
+    assert lib.engram_hash(fake, -1, 4, ctypes.byref(s), fake, None) == B.ENGRAM_EINVAL
+    assert lib.engram_hash(fake, 1, 4, None, fake, None) == B.ENGRAM_EINVAL
+    assert lib.engram_hash_slice(fake, 1, 4, 3, 2, ctypes.byref(s), fake, None) == B.ENGRAM_EINVAL
+    assert lib.engram_hash_slice(fake, 1, 4, 0, 5, ctypes.byref(s), fake, None) == B.ENGRAM_EINVAL
+    assert lib.engram_hash_slice(fake, 1, 4, -1, 2, ctypes.byref(s), fake, None) == B.ENGRAM_EINVAL
+    # empty work is a successful no-op, with or without pointers
+    assert lib.engram_hash(None, 0, 4, ctypes.byref(s), None, None) == B.ENGRAM_OK
+    assert lib.engram_hash_slice(None, 2, 4, 2, 2, ctypes.byref(s), None, None) == B.ENGRAM_OK
+
+
+def test_gather_rejects_bad_arguments(lib):
+    f = ctypes.c_void_p(0x1000)
+    assert lib.engram_gather(f, 7, 0, 10, 160, f, 4, f, None, None) == B.ENGRAM_EDTYPE
+    for dim in (0, -8, 100, 12, 1024):               # bytes not a multiple of 16, or above 1024
+        assert lib.engram_gather(f, B.ENGRAM_BF16, 0, 10, dim, f, 4, f, None, None) == B.ENGRAM_EINVAL
+    assert lib.engram_gather(f, B.ENGRAM_F32, 0, 10, 257, f, 4, f, None, None) == B.ENGRAM_EINVAL
+    assert lib.engram_gather(None, B.ENGRAM_BF16, 0, 10, 160, f, 4, f, None, None) == B.ENGRAM_EINVAL
+    assert lib.engram_gather(f, B.ENGRAM_BF16, 0, 10, 160, None, 4, f, None, None) == B.ENGRAM_EINVAL
+    assert lib.engram_gather(f, B.ENGRAM_BF16, 0, 10, 160, f, 4, None, None, None) == B.ENGRAM_EINVAL
+    assert lib.engram_gather(f, B.ENGRAM_BF16, -1, 10, 160, f, 4, f, None, None) == B.ENGRAM_EINVAL
+    assert lib.engram_gather(f, B.ENGRAM_BF16, 0, -10, 160, f, 4, f, None, None) == B.ENGRAM_EINVAL
+    assert lib.engram_gather(f, B.ENGRAM_BF16, 0, 10, 160, f, -4, f, None, None) == B.ENGRAM_EINVAL
+
+
+def test_scatter_rejects_bad_arguments(lib):
+    f = ctypes.c_void_p(0x1000)
+    ws_ok = ctypes.c_void_p(0x100000)                # 256-aligned, never dereferenced
+    n, R, D = 1000, 5000, 160
+    need = lib.engram_scatter_add_workspace(n, R, D)
+    assert need > 0
+
+    def call(rows=f, nn=n, g=f, dt=B.ENGRAM_BF16, dim=D, rb=0, nr=R, dense=None, ur=f, ug=f, nu=f,
+             ws=ws_ok, wsb=need):
+        return lib.engram_scatter_add(rows, nn, g, dt, dim, rb, nr, dense, ur, ug, nu, ws, wsb, None, None)
+
+    assert call(dt=3) == B.ENGRAM_EDTYPE
+    assert call(dim=100) == B.ENGRAM_EINVAL
+    assert call(nn=-1) == B.ENGRAM_EINVAL
+    assert call(nn=1 << 31) == B.ENGRAM_EINVAL
+    assert call(nr=0xFFFFFFFF) == B.ENGRAM_EINVAL
+    assert call(rb=-1) == B.ENGRAM_EINVAL
+    assert call(dense=f) == B.ENGRAM_EINVAL                       # both output forms
+    assert call(ur=None, ug=None, nu=None) == B.ENGRAM_EINVAL     # neither
+    assert call(nu=None) == B.ENGRAM_EINVAL                       # incomplete compact form
+    assert call(rows=None) == B.ENGRAM_EINVAL
+    assert call(g=None) == B.ENGRAM_EINVAL
+    assert call(ws=None) == B.ENGRAM_EWORKSPACE
+    assert call(wsb=need - 1) == B.ENGRAM_EWORKSPACE
+    assert call(ws=ctypes.c_void_p(0x100010)) == B.ENGRAM_EWORKSPACE
+
+
+def test_workspace_grows_with_n(lib):
+    a = lib.engram_scatter_add_workspace(1 << 16, 320001536, 160)
+    b = lib.engram_scatter_add_workspace(1 << 20, 320001536, 160)
+    assert 0 < a < b
+    # four 32-bit key/index arrays dominate: at least 16 bytes per lookup
+    assert b >= 16 * (1 << 20)
+    assert lib.engram_scatter_add_workspace(-1, 10, 160) == 0
+
+
+def test_product_constants_match_oracle_derivation():
+    """The binding's literal Qwen3.8-Flash-Next constants equal the oracle's derived ones."""
+    from oracle import constants as C
+    assert E.QWEN3_8_FLASH_NEXT_NGRAM_HEAD_VOCAB_SIZES == C.head_vocab_sizes()
+    assert E.QWEN3_8_FLASH_NEXT_NGRAM_HEAD_OFFSETS == C.head_offsets()
+    assert E.QWEN3_8_FLASH_NEXT_NGRAM_PADDED_ROWS == C.padded_rows()
+    assert E.QWEN3_8_FLASH_NEXT_LAYER_MULTIPLIERS == C.LAYER_MULTIPLIERS
+    assert E.QWEN3_8_FLASH_NEXT_EOS_TOKEN_ID == C.EOS_TOKEN_ID

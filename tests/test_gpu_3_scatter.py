@@ -1,0 +1,196 @@
+"""Gradient scatter-add parity: fp32 results within 1e-5 relative / 1e-6 absolute
+of the fp64 oracle; bit-exact where the sums are exact; deterministic."""
+import numpy as np
+import pytest
+import torch
+
+import hashed_gram_embedding_engram_amd as E
+import workloads as W
+from oracle import c_oracle
+from tests.gpu_common import assert_close_to_fp64, oracle_hash, requires_gpu, to_host
+
+pytestmark = [pytest.mark.gpu, requires_gpu]
+
+
+def run_compact(rows_np, dy_gpu, num_rows, row_begin=0):
+    rows = torch.from_numpy(np.ascontiguousarray(rows_np, dtype=np.int64).reshape(-1)).cuda()
+    status = torch.empty((), dtype=torch.int64, device="cuda")
+    ur, ug, nu = E.engram_scatter_add(rows, dy_gpu, num_rows, row_begin, status=status, validate=False,
+                                      compact=(torch.full((max(rows.numel(), 1),), -7, dtype=torch.int64, device="cuda"),
+                                               torch.empty((max(rows.numel(), 1), dy_gpu.shape[-1]),
+                                                           dtype=torch.float32, device="cuda"),
+                                               torch.empty((), dtype=torch.int64, device="cuda")))
+    torch.cuda.synchronize()
+    u = int(nu.item())
+    return ur[:u].cpu().numpy(), ug[:u].cpu().numpy(), int(status.item()), ur.cpu().numpy()
+
+
+def run_dense(rows_np, dy_gpu, num_rows, row_begin=0, grad_in=None):
+    rows = torch.from_numpy(np.ascontiguousarray(rows_np, dtype=np.int64).reshape(-1)).cuda()
+    status = torch.empty((), dtype=torch.int64, device="cuda")
+    g = torch.zeros((num_rows, dy_gpu.shape[-1]), dtype=torch.float32, device="cuda") if grad_in is None \
+        else torch.from_numpy(grad_in).cuda()
+    E.engram_scatter_add(rows, dy_gpu, num_rows, row_begin, grad_dense=g, status=status, validate=False)
+    torch.cuda.synchronize()
+    return g.cpu().numpy(), int(status.item())
+
+
+def check_compact(rows_np, dy_gpu, num_rows, row_begin=0, exact=False):
+    ur, ug, bad, _ = run_compact(rows_np, dy_gpu, num_rows, row_begin)
+    rur, rug, rbad = c_oracle.scatter_add_compact(rows_np, to_host(dy_gpu), num_rows, row_begin)
+    assert bad == rbad
+    assert np.array_equal(ur, rur)
+    if exact:
+        assert np.array_equal(ug.astype(np.float64), rug)
+    else:
+        assert_close_to_fp64(ug, rug, "compact sums")
+    return ur, ug
+
+
+def grads(n, dim=160, dtype=torch.bfloat16, seed=0):
+    g = torch.Generator(device="cuda")
+    g.manual_seed(seed)
+    return torch.randn((n, dim), generator=g, device="cuda").to(dtype)
+
+
+def test_tiny_case():
+    """Tiny: fp32 table and grad_out, compact and dense, against the oracle."""
+    ws = W.tiny_spec()
+    rows = oracle_hash(W.tiny_tokens(), ws).reshape(-1)
+    dy = torch.from_numpy(W.tiny_grad(rows.size)).cuda()
+    check_compact(rows, dy, ws["num_rows"])
+    gin = np.random.default_rng(4).standard_normal((ws["num_rows"], 160)).astype(np.float32)
+    got, bad = run_dense(rows, dy, ws["num_rows"], grad_in=gin)
+    ref, rbad = c_oracle.scatter_add_dense(rows, W.tiny_grad(rows.size), ws["num_rows"], 0, gin)
+    assert bad == rbad == -1
+    assert_close_to_fp64(got, ref, "dense tiny")
+
+
+@pytest.mark.parametrize("n", [1, 2, 255, 256, 257, 4095, 4096, 4097, 3 * 4096 + 17, 70001])
+def test_ragged_counts(n):
+    rng = np.random.default_rng(n)
+    rows = (rng.zipf(1.2, size=n) % 5000).astype(np.int64)
+    check_compact(rows, grads(n, seed=n), 5000)
+
+
+@pytest.mark.parametrize("num_rows", [1, 2, 255, 256, 257, 65536, 65537, 5_000_024, (1 << 31) + 5, 0xFFFFFFFE])
+def test_key_widths(num_rows):
+    """Sort passes follow the bit length of the shard (1 to 32 bits)."""
+    rng = np.random.default_rng(num_rows % 1000)
+    n = 20000
+    hot = rng.integers(0, num_rows, size=50)
+    rows = np.where(rng.random(n) < 0.5, hot[rng.integers(0, 50, size=n)], rng.integers(0, num_rows, size=n))
+    check_compact(rows.astype(np.int64), grads(n, seed=7), num_rows)
+
+
+def test_ones_give_histogram():
+    rng = np.random.default_rng(2)
+    rows = rng.integers(100, 400, size=300000).astype(np.int64)
+    dy = torch.ones((rows.size, 160), dtype=torch.bfloat16, device="cuda")
+    ur, ug, _, _ = run_compact(rows, dy, 300, row_begin=100)
+    counts = np.bincount(rows - 100, minlength=300)
+    assert np.array_equal(ur, np.nonzero(counts)[0] + 100)
+    assert np.array_equal(ug, np.repeat(counts[ur - 100][:, None], 160, axis=1).astype(np.float32))
+
+
+def test_integer_grads_exact():
+    """Small-integer gradients: every sum is exact in fp64 and fp32, so bit-exact."""
+    rng = np.random.default_rng(3)
+    rows = (rng.zipf(1.3, size=200000) % 10000).astype(np.int64)
+    dy = torch.from_numpy(rng.integers(-8, 9, size=(rows.size, 160)).astype(np.float32)).cuda().to(torch.bfloat16)
+    check_compact(rows, dy, 10000, exact=True)
+    got, _ = run_dense(rows, dy, 10000)
+    ref, _ = c_oracle.scatter_add_dense(rows, to_host(dy), 10000)
+    assert np.array_equal(got.astype(np.float64), ref)
+
+
+def test_hot_row_stress():
+    """One row taking 300,000 hits spans ~1,200 reduce slices: carried partials."""
+    rng = np.random.default_rng(4)
+    n = 400000
+    rows = rng.integers(0, 100000, size=n).astype(np.int64)
+    rows[rng.random(n) < 0.75] = 31337
+    assert (rows == 31337).sum() >= 100000
+    dy = grads(n, seed=4)
+    check_compact(rows, dy, 100000)
+    got, _ = run_dense(rows, dy, 100000)
+    ref, _ = c_oracle.scatter_add_dense(rows, to_host(dy), 100000)
+    assert_close_to_fp64(got, ref, "dense hot row")
+
+
+def test_all_same_row_and_sorted_input():
+    n = 100000
+    dy = grads(n, seed=5)
+    check_compact(np.full(n, 7, dtype=np.int64), dy, 10)
+    check_compact(np.arange(n, dtype=np.int64) // 3, dy, n)
+    check_compact(np.arange(n, dtype=np.int64)[::-1].copy() // 300, dy, n)
+
+
+def test_deterministic():
+    rng = np.random.default_rng(6)
+    rows = (rng.zipf(1.1, size=300000) % 200000).astype(np.int64)
+    dy = grads(rows.size, seed=6)
+    a = run_compact(rows, dy, 200000)
+    b = run_compact(rows, dy, 200000)
+    assert np.array_equal(a[0], b[0]) and np.array_equal(a[1].view(np.uint32), b[1].view(np.uint32))
+    da, _ = run_dense(rows, dy, 200000)
+    db, _ = run_dense(rows, dy, 200000)
+    assert np.array_equal(da.view(np.uint32), db.view(np.uint32))
+    # dense from zero and compact agree bit for bit on the touched rows; untouched rows stay zero
+    assert np.array_equal(da[a[0]].view(np.uint32), a[1].view(np.uint32))
+    mask = np.ones(200000, bool)
+    mask[a[0]] = False
+    assert not da[mask].any()
+
+
+def test_out_of_range_dropped():
+    rng = np.random.default_rng(8)
+    rb, R = 5000, 3000
+    rows = rng.integers(rb, rb + R, size=50000).astype(np.int64)
+    rows[[40000, 1234, 49999]] = [rb - 1, rb + R, -(1 << 63)]
+    dy = grads(rows.size, seed=8)
+    ur, ug, bad, full_ur = run_compact(rows, dy, R, rb)
+    rur, rug, rbad = c_oracle.scatter_add_compact(rows, to_host(dy), R, rb)
+    assert bad == rbad == 1234
+    assert np.array_equal(ur, rur)
+    assert_close_to_fp64(ug, rug, "compact with bad rows")
+    assert (full_ur[ur.size:] == -7).all()          # entries past U untouched
+    got, bad = run_dense(rows, dy, R, rb)
+    ref, _ = c_oracle.scatter_add_dense(rows, to_host(dy), R, rb)
+    assert bad == 1234
+    assert_close_to_fp64(got, ref, "dense with bad rows")
+    with pytest.raises(E.EngramError, match="outside the owned range"):
+        E.engram_scatter_add(torch.from_numpy(rows).cuda(), dy, R, rb)
+
+
+def test_empty_and_all_invalid():
+    dy = grads(3, seed=9)
+    ur, ug, bad, _ = run_compact(np.zeros(0, dtype=np.int64), dy[:0], 100)
+    assert ur.size == 0 and bad == -1
+    ur, ug, bad, _ = run_compact(np.array([100, 101, -1], dtype=np.int64), dy, 100)
+    assert ur.size == 0 and bad == 0
+    got, bad = run_dense(np.array([100, 101, -1], dtype=np.int64), dy, 100)
+    assert bad == 0 and not got.any()
+    ur, _, bad, _ = run_compact(np.array([0, 0, 0], dtype=np.int64), dy, 0)   # an empty shard
+    assert ur.size == 0 and bad == 0
+
+
+@pytest.mark.parametrize("dtype,dim", [(torch.bfloat16, 8), (torch.bfloat16, 64), (torch.bfloat16, 512),
+                                       (torch.float32, 4), (torch.float32, 12), (torch.float32, 160),
+                                       (torch.float32, 256)])
+def test_other_widths(dtype, dim):
+    rng = np.random.default_rng(dim)
+    rows = (rng.zipf(1.2, size=30000) % 2000).astype(np.int64)
+    dy = grads(rows.size, dim=dim, dtype=dtype, seed=dim)
+    check_compact(rows, dy, 2000)
+    got, _ = run_dense(rows, dy, 2000)
+    ref, _ = c_oracle.scatter_add_dense(rows, to_host(dy), 2000)
+    assert_close_to_fp64(got, ref, "dense width %d" % dim)
+
+
+def test_sft_shape_backward():
+    """SFT-shaped lookups (524,288) into the 10,000,000-row table, bf16 grad_out."""
+    ws = W.sft_spec()
+    ids, _ = W.sft_batch(0)
+    rows = oracle_hash(ids, ws).reshape(-1)
+    check_compact(rows, grads(rows.size, seed=10), ws["num_rows"])
