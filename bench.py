@@ -135,6 +135,8 @@ def build_workload(name, rotations, dev):
 
 
 def run_step(wl, b, ev=None):
+    """hash -> gather -> (backward) plan -> apply, all on the current stream.
+    ev: five events recorded between the phases."""
     import hashed_gram_embedding_engram_amd as E
     if ev:
         ev[0].record()
@@ -146,11 +148,17 @@ def run_step(wl, b, ev=None):
     if ev:
         ev[2].record()
     if wl["backward"]:
-        E.engram_scatter_add(b["rows"], b["dy"], wl["table_rows"], wl["row_begin"], grad_dense=wl["grad_dense"],
-                             compact=b.get("compact"), workspace=wl["workspace"], status=b["status"],
-                             validate=False)
+        compact = b.get("compact")
+        E.engram_scatter_add_plan(b["rows"], wl["table_rows"], b["dy"].shape[-1], wl["row_begin"],
+                                  workspace=wl["workspace"], uniq_rows=compact[0] if compact else None,
+                                  num_uniq=compact[2] if compact else None, status=b["status"])
     if ev:
         ev[3].record()
+    if wl["backward"]:
+        E.engram_scatter_add_apply(b["dy"], b["n"], wl["table_rows"], wl["workspace"], wl["row_begin"],
+                                   grad_dense=wl["grad_dense"], uniq_grad=compact[1] if compact else None)
+    if ev:
+        ev[4].record()
 
 
 def cpu_baseline(wl, max_tokens=None):
@@ -223,7 +231,7 @@ def main():
         run_step(wl, wl["batches"][i % R])
     torch.cuda.synchronize()
 
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
@@ -233,11 +241,11 @@ def main():
 
     lookups = sum(wl["batches"][i % R]["n"] for i in range(args.steps))
     elapsed = t1 - t0
-    phase = {"hash": 0.0, "gather": 0.0, "scatter_add": 0.0}
+    names = ("hash", "gather", "scatter_plan", "scatter_apply")
+    phase = {k: 0.0 for k in names}
     for e in evs:
-        phase["hash"] += e[0].elapsed_time(e[1])
-        phase["gather"] += e[1].elapsed_time(e[2])
-        phase["scatter_add"] += e[2].elapsed_time(e[3])
+        for k, name in enumerate(names):
+            phase[name] += e[k].elapsed_time(e[k + 1])
     phase = {k: v / args.steps for k, v in phase.items()}
     n_avg = lookups / args.steps
     U = None
@@ -245,13 +253,30 @@ def main():
     if "compact" in b0:
         U = int(b0["compact"][2].item())
 
-    # Dominant kernel: the row gather (one kernel per engram_gather call, plus a
-    # 1-thread status-reset kernel).  Algorithmic bytes per lookup: one 320 B
-    # table row read + one 320 B output row written + one 8 B row id read.
+    # Algorithmic bytes (what the method must move, per launch):
+    #   gather: per lookup one 320 B table row read, one 320 B output row
+    #           written and one 8 B row id read -> 648 B;
+    #   apply (segment reduce + carry fix-up): per lookup one 320 B bf16
+    #           gradient row read and its 8 B sorted (key, index) pair; per
+    #           distinct row one 640 B fp32 sum written (compact) or a 640 B
+    #           read + 640 B write (dense).
     gather_bytes = 648.0 * n_avg
-    gather_s = phase["gather"] / 1e3
-    achieved = gather_bytes / gather_s / 1e9
-    traffic = counter_traffic("gather.hip", "gather_%s_counters.txt" % args.workload)
+    if wl["backward"]:
+        u_rows = sum(int(b["compact"][2].item()) for b in wl["batches"]) / R if "compact" in b0 else None
+        if u_rows is None:  # dense: distinct rows counted from the plan of rotation 0
+            import numpy as np
+            u_rows = float(np.unique(b0["rows"].cpu().numpy()).size)
+            apply_bytes = 328.0 * n_avg + 1280.0 * u_rows
+        else:
+            apply_bytes = 328.0 * n_avg + 640.0 * u_rows
+    kern = {"gather": (gather_bytes, phase["gather"], "gather_rows_kernel<20,16,true>", "gather.hip")}
+    if wl["backward"]:
+        kern["scatter_apply"] = (apply_bytes, phase["scatter_apply"],
+                                 "segment_reduce_kernel<20,bf16> + carry_fixup_kernel", "scatter.hip")
+    dom = max(kern, key=lambda k: kern[k][1])
+    dbytes, dms, dname, dsrc = kern[dom]
+    achieved = dbytes / (dms / 1e3) / 1e9
+    traffic = counter_traffic(dsrc, "%s_%s_counters.txt" % (dom, args.workload))
     result = {
         "metric": METRIC,
         "value": lookups / elapsed,
@@ -275,9 +300,10 @@ def main():
             "distinct_rows_rotation0": U, "rotations": R,
         },
         "phases_ms": {k: round(v, 4) for k, v in phase.items()},
-        "roofline": {"kernel": "gather_rows_kernel<20,16>", "bound": "hbm", "achieved": achieved,
-                     "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBPS,
-                     "traffic": traffic, "bytes_per_lookup": 648},
+        "roofline": {"kernel": dname, "bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS,
+                     "unit": "GB/s", "frac": achieved / HBM_PEAK_GBPS, "traffic": traffic,
+                     "algorithmic_bytes_per_launch": dbytes, "avg_launch_ms": dms},
+        "phase_gbps_algorithmic": {k: round(v[0] / (v[1] / 1e3) / 1e9, 1) for k, v in kern.items()},
         "cpu_baseline": None,
     }
     if not args.no_cpu_baseline:

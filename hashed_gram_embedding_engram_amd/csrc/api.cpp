@@ -88,24 +88,67 @@ size_t engram_scatter_add_workspace(int64_t n, int64_t num_rows, int32_t dim) {
     return engram::scatter_workspace_bytes(n, num_rows, dim);
 }
 
+namespace {
+
+int scatter_check_common(int32_t dtype, int32_t dim, int64_t n, int64_t row_begin, int64_t num_rows, int* eb) {
+    if (!dtype_ok(dtype)) return ENGRAM_EDTYPE;
+    if (!row_bytes_ok(dtype, dim, eb)) return ENGRAM_EINVAL;
+    if (n < 0 || n >= ((int64_t)1 << 31)) return ENGRAM_EINVAL;
+    if (num_rows < 0 || num_rows >= (int64_t)0xFFFFFFFFll || row_begin < 0) return ENGRAM_EINVAL;
+    return ENGRAM_OK;
+}
+
+int workspace_check(const void* workspace, size_t workspace_bytes, int64_t n, int64_t num_rows, int32_t dim) {
+    if (((uintptr_t)workspace & 255) != 0) return ENGRAM_EWORKSPACE;
+    if (!workspace || workspace_bytes < engram::scatter_workspace_bytes(n, num_rows, dim)) return ENGRAM_EWORKSPACE;
+    return ENGRAM_OK;
+}
+
+}  // namespace
+
+int engram_scatter_add_plan(const int64_t* rows, int64_t n, int64_t row_begin, int64_t num_rows, int32_t dim,
+                            int64_t* uniq_rows, int64_t* num_uniq, void* workspace, size_t workspace_bytes,
+                            int64_t* status, hipStream_t stream) {
+    int eb;
+    int rc = scatter_check_common(ENGRAM_F32, dim, n, row_begin, num_rows, &eb);
+    if (rc != ENGRAM_OK) return rc;
+    if (n > 0 && !rows) return ENGRAM_EINVAL;
+    if ((rc = workspace_check(workspace, workspace_bytes, n, num_rows, dim)) != ENGRAM_OK) return rc;
+    return launch_result(engram::launch_scatter_plan(rows, n, row_begin, num_rows, dim, uniq_rows, num_uniq,
+                                                     workspace, status, stream));
+}
+
+int engram_scatter_add_apply(const void* grad_out, int32_t dtype, int32_t dim, int64_t n, int64_t row_begin,
+                             int64_t num_rows, float* grad_dense, float* uniq_grad, const void* workspace,
+                             size_t workspace_bytes, hipStream_t stream) {
+    int eb;
+    int rc = scatter_check_common(dtype, dim, n, row_begin, num_rows, &eb);
+    if (rc != ENGRAM_OK) return rc;
+    if ((grad_dense != nullptr) == (uniq_grad != nullptr)) return ENGRAM_EINVAL;
+    if (n > 0 && !grad_out) return ENGRAM_EINVAL;
+    if ((rc = workspace_check(workspace, workspace_bytes, n, num_rows, dim)) != ENGRAM_OK) return rc;
+    return launch_result(engram::launch_scatter_apply(grad_out, eb, dim, n, num_rows, grad_dense, uniq_grad,
+                                                      workspace, stream));
+}
+
 int engram_scatter_add(const int64_t* rows, int64_t n, const void* grad_out, int32_t dtype, int32_t dim,
                        int64_t row_begin, int64_t num_rows, float* grad_dense, int64_t* uniq_rows, float* uniq_grad,
                        int64_t* num_uniq, void* workspace, size_t workspace_bytes, int64_t* status,
                        hipStream_t stream) {
-    if (!dtype_ok(dtype)) return ENGRAM_EDTYPE;
     int eb;
-    if (!row_bytes_ok(dtype, dim, &eb)) return ENGRAM_EINVAL;
-    if (n < 0 || n >= ((int64_t)1 << 31)) return ENGRAM_EINVAL;
-    if (num_rows < 0 || num_rows >= (int64_t)0xFFFFFFFFll || row_begin < 0) return ENGRAM_EINVAL;
+    int rc = scatter_check_common(dtype, dim, n, row_begin, num_rows, &eb);
+    if (rc != ENGRAM_OK) return rc;
     const bool dense = grad_dense != nullptr;
     const bool compact = uniq_rows != nullptr || uniq_grad != nullptr || num_uniq != nullptr;
     if (dense == compact) return ENGRAM_EINVAL;
     if (compact && (!uniq_rows || !uniq_grad || !num_uniq)) return ENGRAM_EINVAL;
     if (n > 0 && (!rows || !grad_out)) return ENGRAM_EINVAL;
-    if (((uintptr_t)workspace & 255) != 0) return ENGRAM_EWORKSPACE;
-    if (!workspace || workspace_bytes < engram::scatter_workspace_bytes(n, num_rows, dim)) return ENGRAM_EWORKSPACE;
-    return launch_result(engram::launch_scatter_add(rows, n, grad_out, eb, dim, row_begin, num_rows, grad_dense,
-                                                    uniq_rows, uniq_grad, num_uniq, workspace, status, stream));
+    if ((rc = workspace_check(workspace, workspace_bytes, n, num_rows, dim)) != ENGRAM_OK) return rc;
+    hipError_t e = engram::launch_scatter_plan(rows, n, row_begin, num_rows, dim, uniq_rows, num_uniq, workspace,
+                                               status, stream);
+    if (e != hipSuccess) return ENGRAM_ELAUNCH;
+    return launch_result(engram::launch_scatter_apply(grad_out, eb, dim, n, num_rows, grad_dense, uniq_grad,
+                                                      workspace, stream));
 }
 
 const char* engram_strerror(int code) {

@@ -37,10 +37,15 @@ hipError_t launch_gather(const void* table, int elem_bytes, int64_t row_begin, i
 
 size_t scatter_workspace_bytes(int64_t n, int64_t num_rows, int dim);
 
-hipError_t launch_scatter_add(const int64_t* rows, int64_t n, const void* grad_out, int elem_bytes, int dim,
-                              int64_t row_begin, int64_t num_rows, float* grad_dense, int64_t* uniq_rows,
-                              float* uniq_grad, int64_t* num_uniq, void* workspace, int64_t* status,
-                              hipStream_t stream);
+// Backward phase 1: sort the lookups by row, count the runs, optionally write
+// the distinct rows; the plan stays in the workspace.
+hipError_t launch_scatter_plan(const int64_t* rows, int64_t n, int64_t row_begin, int64_t num_rows, int dim,
+                               int64_t* uniq_rows, int64_t* num_uniq, void* workspace, int64_t* status,
+                               hipStream_t stream);
+
+// Backward phase 2: per-row fp64 sums of grad_out along a plan.
+hipError_t launch_scatter_apply(const void* grad_out, int elem_bytes, int dim, int64_t n, int64_t num_rows,
+                                float* grad_dense, float* uniq_grad, const void* workspace, hipStream_t stream);
 
 // Sets *status = -1 on the stream (a kernel, not a memset, so the call can be
 // captured in a graph).

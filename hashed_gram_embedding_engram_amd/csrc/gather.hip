@@ -23,47 +23,64 @@
 namespace engram {
 namespace {
 
+// Read by lanes that have no row to copy, so loads never need a branch.
+__device__ u32x4 kZeroChunk = {0u, 0u, 0u, 0u};  // never written
+
 __device__ __forceinline__ void report_bad(int64_t* status, int64_t idx) {
     if (status) atomicMin((unsigned long long*)status, (unsigned long long)idx);
 }
 
-template <int CPR, int G>
+// ROW32: the shard has fewer than 2^32 - 1 rows, so a local row id (or the
+// out-of-range marker 0xFFFFFFFF) fits one 32-bit shuffle.
+template <int CPR, int G, bool ROW32>
 __global__ __launch_bounds__(256) void gather_rows_kernel(const u32x4* __restrict__ table, int64_t row_begin,
                                                           uint64_t num_rows, const int64_t* __restrict__ rows,
                                                           int64_t n, u32x4* __restrict__ out,
                                                           int64_t* __restrict__ status) {
     constexpr int PER_LANE = CPR * G / 64;
-    static_assert(CPR * G % 64 == 0, "wave tile must be whole dwordx4 per lane");
+    static_assert(CPR * G % 64 == 0 && G <= 64, "wave tile must be whole dwordx4 per lane");
     const int lane = threadIdx.x & 63;
     const int64_t wave = (int64_t)blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6);
     const int64_t n0 = wave * G;
     if (n0 >= n) return;
 
-    int64_t src[PER_LANE];
+    // Lane i < G reads and checks row id n0 + i; the others fetch it by shuffle.
+    const bool mine_live = lane < G && n0 + lane < n;
+    uint64_t local = ~0ull;
+    if (mine_live) {
+        local = (uint64_t)rows[n0 + lane] - (uint64_t)row_begin;
+        if (local >= num_rows) {
+            report_bad(status, n0 + lane);
+            local = ~0ull;
+        }
+    }
+    // Every load is issued unconditionally (a lane with nothing to copy reads a
+    // zero chunk), so all PER_LANE loads of the wave are in flight together.
+    const int rem = (int)(n - n0 < G ? n - n0 : G);
+    const u32x4* src[PER_LANE];
 #pragma unroll
     for (int j = 0; j < PER_LANE; ++j) {
         const int c = lane + 64 * j;
-        const int64_t i = n0 + c / CPR;
-        src[j] = -1;
-        if (i < n) {
-            const uint64_t local = (uint64_t)rows[i] - (uint64_t)row_begin;
-            if (local < num_rows) {
-                src[j] = (int64_t)local * CPR + c % CPR;
-            } else if (c % CPR == 0) {
-                report_bad(status, i);
-            }
+        const int i = c / CPR, k = c % CPR;
+        if (ROW32) {
+            const uint32_t r = __shfl((uint32_t)local, i, 64);
+            src[j] = (i < rem && r != 0xFFFFFFFFu) ? table + ((uint64_t)r * CPR + k) : &kZeroChunk;
+        } else {
+            const uint64_t r = __shfl(local, i, 64);
+            src[j] = (i < rem && r != ~0ull) ? table + (r * CPR + k) : &kZeroChunk;
         }
     }
     u32x4 v[PER_LANE];
 #pragma unroll
-    for (int j = 0; j < PER_LANE; ++j) {
-        v[j] = (u32x4){0u, 0u, 0u, 0u};
-        if (src[j] >= 0) v[j] = table[src[j]];
-    }
+    for (int j = 0; j < PER_LANE; ++j) v[j] = *src[j];
+    u32x4* dst = out + n0 * CPR + lane;
+    if (rem == G) {  // every wave but the last: no per-store condition
 #pragma unroll
-    for (int j = 0; j < PER_LANE; ++j) {
-        const int c = lane + 64 * j;
-        if (n0 + c / CPR < n) __builtin_nontemporal_store(v[j], out + n0 * CPR + c);
+        for (int j = 0; j < PER_LANE; ++j) __builtin_nontemporal_store(v[j], dst + 64 * j);
+    } else {
+#pragma unroll
+        for (int j = 0; j < PER_LANE; ++j)
+            if ((lane + 64 * j) / CPR < rem) __builtin_nontemporal_store(v[j], dst + 64 * j);
     }
 }
 
@@ -105,16 +122,23 @@ hipError_t launch_gather(const void* table, int elem_bytes, int64_t row_begin, i
     const u32x4* t = (const u32x4*)table;
     u32x4* o = (u32x4*)out;
     const int block = 256, waves_per_block = block / 64;
-    if (cpr == 20) {
-        const int64_t waves = (n + 15) / 16;
-        const int64_t grid = (waves + waves_per_block - 1) / waves_per_block;
-        hipLaunchKernelGGL((gather_rows_kernel<20, 16>), dim3((unsigned)grid), dim3(block), 0, stream, t,
-                           row_begin, (uint64_t)num_rows, rows, n, o, status);
-    } else if (cpr == 40) {
-        const int64_t waves = (n + 7) / 8;
-        const int64_t grid = (waves + waves_per_block - 1) / waves_per_block;
-        hipLaunchKernelGGL((gather_rows_kernel<40, 8>), dim3((unsigned)grid), dim3(block), 0, stream, t,
-                           row_begin, (uint64_t)num_rows, rows, n, o, status);
+    const bool row32 = (uint64_t)num_rows < 0xFFFFFFFFull;
+    if (cpr == 20 || cpr == 40) {
+        const int g = cpr == 20 ? 16 : 8;
+        const int64_t waves = (n + g - 1) / g;
+        const dim3 grid((unsigned)((waves + waves_per_block - 1) / waves_per_block));
+        if (cpr == 20 && row32)
+            hipLaunchKernelGGL((gather_rows_kernel<20, 16, true>), grid, dim3(block), 0, stream, t, row_begin,
+                               (uint64_t)num_rows, rows, n, o, status);
+        else if (cpr == 20)
+            hipLaunchKernelGGL((gather_rows_kernel<20, 16, false>), grid, dim3(block), 0, stream, t, row_begin,
+                               (uint64_t)num_rows, rows, n, o, status);
+        else if (row32)
+            hipLaunchKernelGGL((gather_rows_kernel<40, 8, true>), grid, dim3(block), 0, stream, t, row_begin,
+                               (uint64_t)num_rows, rows, n, o, status);
+        else
+            hipLaunchKernelGGL((gather_rows_kernel<40, 8, false>), grid, dim3(block), 0, stream, t, row_begin,
+                               (uint64_t)num_rows, rows, n, o, status);
     } else {
         const int64_t grid = (n * cpr + block - 1) / block;
         hipLaunchKernelGGL(gather_rows_generic_kernel, dim3((unsigned)grid), dim3(block), 0, stream, t,

@@ -9,7 +9,8 @@
 //
 // Hot rows (Zipf token streams repeat the same n-grams thousands of times)
 // must not serialise on atomics, and the sums must not depend on scheduling.
-// So the path sorts instead of atomically adding:
+// So the path sorts instead of atomically adding, in two phases:
+// plan (depends on the row ids only)
 //   1. keys     key = row - row_begin (or the sentinel num_rows for a row out
 //               of range), value = lookup index; per-tile histogram of the
 //               first digit in the same pass.
@@ -18,9 +19,11 @@
 //               Per pass: tile histograms, a per-digit scan over tiles, and a
 //               stable scatter that ranks digits inside each wave with ballots
 //               (no atomics) and writes each tile digit-grouped through LDS.
-//   3. runs     run starts per slice of S sorted entries and their prefix
-//               sum: the unique-row index of every run (compact output).
-//   4. reduce   one worker (CPR lanes, one 16-byte chunk of the row each)
+//   3. runs     run starts per slice of S sorted entries, their prefix sum
+//               (the distinct-row index of every run) and, for the compact
+//               form, the distinct rows themselves.
+// apply (once per gradient)
+//   4. reduce   one worker (cpr lanes, one 16-byte chunk of the row each)
 //               per slice walks its S entries in order, accumulating the
 //               gradient rows in fp64.  A run that ends inside the slice is
 //               written once; a run cut by a slice edge leaves an fp64 partial.
@@ -37,12 +40,25 @@ constexpr int kItems = 16;                        // keys per thread in a sort t
 constexpr int kTile = kBlock * kItems;            // 4096 keys per sort tile
 constexpr int kWaveSpan = 64 * kItems;            // contiguous keys owned by one wave
 constexpr int kRadix = 256;
-constexpr uint32_t kSlice = 256;                  // sorted entries per reduce worker
+#ifndef ENGRAM_REDUCE_SLICE
+#define ENGRAM_REDUCE_SLICE 64
+#endif
+#ifndef ENGRAM_REDUCE_NT
+#define ENGRAM_REDUCE_NT 1
+#endif
+#ifndef ENGRAM_REDUCE_BATCH
+#define ENGRAM_REDUCE_BATCH 16
+#endif
+constexpr uint32_t kSlice = ENGRAM_REDUCE_SLICE;  // sorted entries per reduce worker
+static_assert((kSlice & (kSlice - 1)) == 0 && kSlice >= 32, "slices are powers of two, at least 32 entries");
+// Blocks of the slice bookkeeping kernels cover kSliceSpan entries: one slice,
+// or kBlock / kSlice slices when slices are shorter than a block.
+constexpr uint32_t kSliceSpan = kSlice > (uint32_t)kBlock ? kSlice : (uint32_t)kBlock;
 constexpr uint32_t kFlagHead = 1, kFlagWhole = 2, kFlagTail = 4;
 
 struct Layout {
-    size_t keys_a, keys_b, vals_a, vals_b, hist, digit_total, counters, slice_runs, slice_base, slice_flags,
-        carry_head, carry_tail, total;
+    size_t sorted_keys, spare_keys, sorted_vals, spare_vals, hist, digit_total, counters, slice_runs, slice_base,
+        slice_flags, long_runs, carry_head, carry_tail, total;
     int64_t num_tiles, num_slices;
 };
 
@@ -54,16 +70,17 @@ Layout make_layout(int64_t n, int dim) {
     L.num_slices = (n + kSlice - 1) / kSlice;
     size_t off = 0;
     auto take = [&](size_t bytes) { size_t at = off; off = align256(off + bytes); return at; };
-    L.keys_a = take(4 * (size_t)n);
-    L.keys_b = take(4 * (size_t)n);
-    L.vals_a = take(4 * (size_t)n);
-    L.vals_b = take(4 * (size_t)n);
+    L.sorted_keys = take(4 * (size_t)n);
+    L.spare_keys = take(4 * (size_t)n);
+    L.sorted_vals = take(4 * (size_t)n);
+    L.spare_vals = take(4 * (size_t)n);
     L.hist = take(4 * (size_t)kRadix * (size_t)L.num_tiles);
     L.digit_total = take(4 * kRadix);
     L.counters = take(16);
     L.slice_runs = take(4 * (size_t)L.num_slices);
     L.slice_base = take(4 * (size_t)L.num_slices);
     L.slice_flags = take(4 * (size_t)L.num_slices);
+    L.long_runs = take(8 * (size_t)L.num_slices);
     L.carry_head = take(8 * (size_t)L.num_slices * (size_t)dim);
     L.carry_tail = take(8 * (size_t)L.num_slices * (size_t)dim);
     L.total = off;
@@ -117,23 +134,19 @@ __global__ void scatter_init_kernel(int64_t* status, uint32_t* counters, int64_t
     if (num_uniq) *num_uniq = 0;
 }
 
-// Tile histogram of one digit (per-wave ballot aggregation, one LDS add per
-// distinct digit per wave instead of one per key).
-__device__ __forceinline__ void tile_histogram_add(uint32_t* s_cnt, uint32_t digit, bool live, int lane) {
-    const uint64_t peers = match_digit(digit, live);
-    if (live && (peers & lanemask_lt(lane)) == 0) atomicAdd(&s_cnt[digit], (uint32_t)__popcll(peers));
-}
-
+// Tile histograms count with LDS atomics into one sub-histogram per wave
+// (summed at the end), which keeps same-address conflicts inside a wave.
 // Step 1: keys, lookup indices, digit-0 tile histograms, in-range count.
 __global__ __launch_bounds__(kBlock) void keys_kernel(const int64_t* __restrict__ rows, uint32_t n,
                                                       int64_t row_begin, uint64_t num_rows,
                                                       uint32_t* __restrict__ keys, uint32_t* __restrict__ vals,
                                                       uint32_t* __restrict__ hist, uint32_t num_tiles,
                                                       int64_t* __restrict__ status, uint32_t* __restrict__ counters) {
-    __shared__ uint32_t s_cnt[kRadix];
+    __shared__ uint32_t s_cnt[kBlock / 64][kRadix];
     __shared__ uint32_t s_valid;
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-    s_cnt[tid] = 0;
+#pragma unroll
+    for (int k = 0; k < kBlock / 64; ++k) s_cnt[k][tid] = 0;
     if (tid == 0) s_valid = 0;
     __syncthreads();
     const uint32_t base = blockIdx.x * (uint32_t)kTile + (uint32_t)w * kWaveSpan;
@@ -142,9 +155,8 @@ __global__ __launch_bounds__(kBlock) void keys_kernel(const int64_t* __restrict_
 #pragma unroll 4
     for (int it = 0; it < kItems; ++it) {
         const uint32_t e = base + (uint32_t)it * 64 + (uint32_t)lane;
-        const bool live = e < n;
-        uint32_t key = sentinel;
-        if (live) {
+        if (e < n) {
+            uint32_t key = sentinel;
             const uint64_t local = (uint64_t)rows[e] - (uint64_t)row_begin;
             if (local < num_rows) {
                 key = (uint32_t)local;
@@ -154,34 +166,43 @@ __global__ __launch_bounds__(kBlock) void keys_kernel(const int64_t* __restrict_
             }
             keys[e] = key;
             vals[e] = e;
+            atomicAdd(&s_cnt[w][key & 0xFFu], 1u);
         }
-        tile_histogram_add(s_cnt, key & 0xFFu, live, lane);
     }
 #pragma unroll
     for (int o = 32; o > 0; o >>= 1) my_valid += __shfl_xor(my_valid, o, 64);
     if (lane == 0 && my_valid) atomicAdd(&s_valid, my_valid);
     __syncthreads();
-    hist[(size_t)tid * num_tiles + blockIdx.x] = s_cnt[tid];
+    uint32_t c = 0;
+#pragma unroll
+    for (int k = 0; k < kBlock / 64; ++k) c += s_cnt[k][tid];
+    hist[(size_t)tid * num_tiles + blockIdx.x] = c;
     if (tid == 0 && s_valid) atomicAdd(&counters[0], s_valid);
 }
 
 // Tile histograms of the digit at `shift` (passes after the first).
 __global__ __launch_bounds__(kBlock) void upsweep_kernel(const uint32_t* __restrict__ keys, uint32_t n, int shift,
                                                          uint32_t* __restrict__ hist, uint32_t num_tiles) {
-    __shared__ uint32_t s_cnt[kRadix];
+    __shared__ uint32_t s_cnt[kBlock / 64][kRadix];
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-    s_cnt[tid] = 0;
+#pragma unroll
+    for (int k = 0; k < kBlock / 64; ++k) s_cnt[k][tid] = 0;
     __syncthreads();
     const uint32_t base = blockIdx.x * (uint32_t)kTile + (uint32_t)w * kWaveSpan;
-#pragma unroll 4
+    uint32_t key[kItems];
+#pragma unroll
     for (int it = 0; it < kItems; ++it) {
         const uint32_t e = base + (uint32_t)it * 64 + (uint32_t)lane;
-        const bool live = e < n;
-        const uint32_t key = live ? keys[e] : 0u;
-        tile_histogram_add(s_cnt, (key >> shift) & 0xFFu, live, lane);
+        key[it] = e < n ? keys[min(e, n - 1)] : 0xFFFFFFFFu;
     }
+#pragma unroll
+    for (int it = 0; it < kItems; ++it)
+        if (base + (uint32_t)it * 64 + (uint32_t)lane < n) atomicAdd(&s_cnt[w][(key[it] >> shift) & 0xFFu], 1u);
     __syncthreads();
-    hist[(size_t)tid * num_tiles + blockIdx.x] = s_cnt[tid];
+    uint32_t c = 0;
+#pragma unroll
+    for (int k = 0; k < kBlock / 64; ++k) c += s_cnt[k][tid];
+    hist[(size_t)tid * num_tiles + blockIdx.x] = c;
 }
 
 // hist[d][tile] -> exclusive prefix over tiles (in place); digit_total[d] = sum.
@@ -286,40 +307,155 @@ __global__ __launch_bounds__(kBlock) void downsweep_kernel(const uint32_t* __res
 }
 
 // Step 3a: number of runs that start in each slice of sorted in-range keys.
-__global__ __launch_bounds__(kBlock) void run_count_kernel(const uint32_t* __restrict__ keys,
+// One block per kSliceSpan entries.
+__global__ __launch_bounds__(kBlock) void run_count_kernel(const uint32_t* __restrict__ keys, uint32_t n,
                                                            const uint32_t* __restrict__ counters,
-                                                           uint32_t* __restrict__ slice_runs) {
-    __shared__ uint32_t s_part[kBlock / 64];
-    const uint32_t nv = counters[0];
-    const uint32_t i = blockIdx.x * kSlice + threadIdx.x;
-    const bool start = i < nv && (i == 0 || keys[i] != keys[i - 1]);
-    const uint64_t b = __ballot(start);
-    if ((threadIdx.x & 63) == 0) s_part[threadIdx.x >> 6] = (uint32_t)__popcll(b);
+                                                           uint32_t* __restrict__ slice_runs, uint32_t num_slices) {
+    constexpr uint32_t kPer = kSliceSpan / kSlice;  // slices per block
+    __shared__ uint32_t s_cnt[kPer];
+    const uint32_t nv = min(counters[0], n);
+    if (threadIdx.x < kPer) s_cnt[threadIdx.x] = 0;
     __syncthreads();
-    if (threadIdx.x == 0) {
-        uint32_t s = 0;
-        for (int k = 0; k < kBlock / 64; ++k) s += s_part[k];
-        slice_runs[blockIdx.x] = s;
+    for (uint32_t off = 0; off < kSliceSpan; off += kBlock) {
+        const uint32_t t = off + threadIdx.x;
+        const uint32_t i = blockIdx.x * kSliceSpan + t;
+        const bool start = i < nv && (i == 0 || keys[i] != keys[i - 1]);
+        const uint64_t b = __ballot(start);
+        // one LDS add per wave when a wave lies in one slice, else one per run start
+        const uint32_t q = t / kSlice;
+        if (kSlice >= 64) {
+            if ((threadIdx.x & 63) == 0) atomicAdd(&s_cnt[q], (uint32_t)__popcll(b));
+        } else if (start) {
+            atomicAdd(&s_cnt[q], 1u);
+        }
+    }
+    __syncthreads();
+    if (threadIdx.x < kPer) {
+        const uint32_t j = blockIdx.x * kPer + threadIdx.x;
+        if (j < num_slices) slice_runs[j] = s_cnt[threadIdx.x];
     }
 }
 
-// Step 3b: exclusive prefix of the slice run counts (one block); the total is
-// the number of distinct rows.
-__global__ __launch_bounds__(kBlock) void slice_scan_kernel(const uint32_t* __restrict__ slice_runs,
-                                                            uint32_t num_slices, uint32_t* __restrict__ slice_base,
-                                                            int64_t* __restrict__ num_uniq) {
-    __shared__ uint32_t s_tmp[kBlock / 64];
-    uint32_t running = 0;
-    for (uint32_t b = 0; b < num_slices; b += kBlock) {
-        const uint32_t i = b + threadIdx.x;
-        const uint32_t v = i < num_slices ? slice_runs[i] : 0u;
-        uint32_t tot;
-        const uint32_t ex = block_exclusive_scan(v, &tot, s_tmp);
-        if (i < num_slices) slice_base[i] = running + ex;
-        running += tot;
+// Exclusive prefix sum over the threads of a BLOCK-thread block.
+template <int BLOCK>
+__device__ __forceinline__ uint32_t block_scan_wide(uint32_t v, uint32_t* total, uint32_t* s_tmp) {
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    uint32_t x = v;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+        const uint32_t y = __shfl_up(x, o, 64);
+        if (lane >= o) x += y;
     }
-    if (threadIdx.x == 0 && num_uniq) *num_uniq = running;
+    if (lane == 63) s_tmp[w] = x;
+    __syncthreads();
+    uint32_t wave_off = 0, tot = 0;
+#pragma unroll
+    for (int k = 0; k < BLOCK / 64; ++k) {
+        const uint32_t t = s_tmp[k];
+        if (k < w) wave_off += t;
+        tot += t;
+    }
+    __syncthreads();
+    *total = tot;
+    return wave_off + x - v;
 }
+
+// Step 3b: exclusive prefix of the slice run counts in one 1024-thread block.
+// Rounds of 16,384 counts: a coalesced load into LDS, a serial scan of 16
+// contiguous counts per thread, one block scan of the thread totals, and a
+// coalesced store.  The total is the number of distinct rows.
+constexpr int kScanBlock = 1024;
+constexpr int kScanPer = 16;
+constexpr int kScanRound = kScanBlock * kScanPer;
+__device__ __forceinline__ int scan_pad(int e) { return e + (e >> 4); }  // one spare word per 16: no bank conflicts
+
+__global__ __launch_bounds__(kScanBlock) void slice_scan_kernel(const uint32_t* __restrict__ slice_runs,
+                                                                uint32_t num_slices, uint32_t* __restrict__ slice_base,
+                                                                int64_t* __restrict__ num_uniq) {
+    __shared__ uint32_t s_val[kScanRound + kScanRound / 16];
+    __shared__ uint32_t s_tmp[kScanBlock / 64];
+    const int tid = threadIdx.x;
+    uint32_t carry = 0;
+    for (uint32_t base = 0; base < num_slices; base += kScanRound) {
+#pragma unroll
+        for (int k = 0; k < kScanPer; ++k) {
+            const uint32_t i = base + (uint32_t)(k * kScanBlock + tid);
+            s_val[scan_pad(k * kScanBlock + tid)] = i < num_slices ? slice_runs[i] : 0u;
+        }
+        __syncthreads();
+        uint32_t loc[kScanPer], sum = 0;
+#pragma unroll
+        for (int k = 0; k < kScanPer; ++k) {
+            loc[k] = s_val[scan_pad(tid * kScanPer + k)];
+            sum += loc[k];
+        }
+        uint32_t tot;
+        uint32_t run = carry + block_scan_wide<kScanBlock>(sum, &tot, s_tmp);
+#pragma unroll
+        for (int k = 0; k < kScanPer; ++k) {
+            s_val[scan_pad(tid * kScanPer + k)] = run;
+            run += loc[k];
+        }
+        __syncthreads();
+#pragma unroll
+        for (int k = 0; k < kScanPer; ++k) {
+            const uint32_t i = base + (uint32_t)(k * kScanBlock + tid);
+            if (i < num_slices) slice_base[i] = s_val[scan_pad(k * kScanBlock + tid)];
+        }
+        carry += tot;
+        __syncthreads();
+    }
+    if (tid == 0 && num_uniq) *num_uniq = carry;
+}
+
+// Step 3c (compact form): the distinct rows in ascending order, written by the
+// thread that holds each run's first entry (consecutive runs -> consecutive
+// addresses).
+__global__ __launch_bounds__(kBlock) void uniq_rows_kernel(const uint32_t* __restrict__ keys, uint32_t n,
+                                                           const uint32_t* __restrict__ counters,
+                                                           const uint32_t* __restrict__ slice_base, int64_t row_begin,
+                                                           int64_t* __restrict__ uniq_rows) {
+    constexpr uint32_t kPer = kSliceSpan / kSlice;
+    __shared__ uint64_t s_mask[kBlock / 64];
+    __shared__ uint32_t s_before[kBlock / 64 + 1];
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    const uint32_t nv = min(counters[0], n);
+    uint32_t carried = 0;  // starts in earlier chunks of a slice longer than a block
+    for (uint32_t off = 0; off < kSliceSpan; off += kBlock) {
+        const uint32_t t = off + threadIdx.x;
+        const uint32_t i = blockIdx.x * kSliceSpan + t;
+        const uint32_t key = i < nv ? keys[i] : 0u;
+        const bool start = i < nv && (i == 0 || key != keys[i - 1]);
+        const uint64_t b = __ballot(start);
+        if (lane == 0) s_mask[w] = b;
+        __syncthreads();
+        if (threadIdx.x == 0) {
+            uint32_t acc = 0;
+            for (int k = 0; k < kBlock / 64; ++k) {
+                s_before[k] = acc;
+                acc += (uint32_t)__popcll(s_mask[k]);
+            }
+            s_before[kBlock / 64] = acc;
+        }
+        __syncthreads();
+        // starts in this chunk before position p (p < kBlock)
+        auto before = [&](uint32_t p) -> uint32_t {
+            const uint32_t pw = p >> 6, pl = p & 63;
+            return s_before[pw] + (uint32_t)__popcll(s_mask[pw] & lanemask_lt((int)pl));
+        };
+        if (start) {
+            const uint32_t q = t / kSlice;                        // slice within the block
+            const uint32_t slice_first = (kSlice >= (uint32_t)kBlock) ? 0u : (q * kSlice - off);
+            const uint32_t u = slice_base[blockIdx.x * kPer + q] + carried + before(threadIdx.x) - before(slice_first);
+            if (u < n) uniq_rows[u] = (int64_t)key + row_begin;
+        }
+        carried += s_before[kBlock / 64];
+        __syncthreads();
+    }
+}
+
+// Read by lanes with nothing to load, so gradient loads never need a branch.
+__device__ u32x4 kZeroChunk = {0u, 0u, 0u, 0u};  // never written
 
 // 16 bytes of gradient -> EPC fp64 addends (bf16 = upper half of a binary32).
 template <bool BF16>
@@ -357,13 +493,12 @@ __device__ __forceinline__ void add_partial(double* acc, const double* src) {
     }
 }
 
-// Final write of one run's chunk: dense RMW (fp64 add, one rounding) or compact.
-// The key < num_rows and u < n checks hold for every run of a correct sort;
-// they keep each store in bounds regardless.
+// Final write of one run's chunk: dense RMW (fp64 add, one rounding) or the
+// compact sum.  key < num_rows and u < n hold for every run of a correct plan;
+// the checks keep each store in bounds regardless.
 template <int EPC, bool DENSE>
 __device__ __forceinline__ void write_run(const double* acc, uint32_t key, uint32_t u, int c, int dim, uint32_t n,
-                                          uint32_t num_rows, int64_t row_begin, float* grad_dense,
-                                          int64_t* uniq_rows, float* uniq_grad) {
+                                          uint32_t num_rows, float* grad_dense, float* uniq_grad) {
     typedef float f32x4 __attribute__((ext_vector_type(4)));
     if (DENSE ? key >= num_rows : u >= n) return;
     if (DENSE) {
@@ -378,7 +513,6 @@ __device__ __forceinline__ void write_run(const double* acc, uint32_t key, uint3
             g[q] = nw;
         }
     } else {
-        if (c == 0) uniq_rows[u] = (int64_t)key + row_begin;
         f32x4* g = (f32x4*)(uniq_grad + (size_t)u * dim + c * EPC);
 #pragma unroll
         for (int q = 0; q < EPC / 4; ++q) {
@@ -387,33 +521,43 @@ __device__ __forceinline__ void write_run(const double* acc, uint32_t key, uint3
             v.y = (float)acc[4 * q + 1];
             v.z = (float)acc[4 * q + 2];
             v.w = (float)acc[4 * q + 3];
+#if ENGRAM_REDUCE_NT
             __builtin_nontemporal_store(v, g + q);
+#else
+            g[q] = v;
+#endif
         }
     }
 }
 
-constexpr int kReduceBatch = 8;  // sorted entries whose gradient chunks are in flight per lane
+constexpr int kReduceBatch = ENGRAM_REDUCE_BATCH;  // sorted entries in flight per lane
 
-// Step 4.  Worker = CPR consecutive lanes (one 16-byte chunk of the row each);
-// 64 / CPR workers per wave (bf16 x 160: 3 workers of 20 lanes).  CPR_T == 0
-// takes the chunk count at run time.
+// Step 4.  Worker = cpr consecutive lanes, lane c owning 16-byte chunk c of
+// the row; 64 / cpr workers per wave (bf16 x 160: 3 workers of 20 lanes).
+// Per batch of bb <= 8 sorted entries, lanes c < bb load entry c's key, the
+// key after it and its lookup index; one ballot marks where runs end, and the
+// lookup indices reach the other lanes by shuffle.  The next batch's keys are
+// fetched while the current batch's gradient chunks are summed.
 template <int CPR_T, bool BF16, bool DENSE>
 __global__ __launch_bounds__(kBlock) void segment_reduce_kernel(
-    const uint32_t* __restrict__ keys, const uint32_t* __restrict__ vals, const uint32_t* __restrict__ counters,
+    const uint32_t* __restrict__ keys, const uint32_t* __restrict__ vals, uint32_t* __restrict__ counters,
     const u32x4* __restrict__ dy, uint32_t n, uint32_t num_rows, int cpr_rt, int dim, uint32_t num_slices,
-    const uint32_t* __restrict__ slice_base, int64_t row_begin, float* __restrict__ grad_dense,
-    int64_t* __restrict__ uniq_rows, float* __restrict__ uniq_grad, double* __restrict__ carry_head,
-    double* __restrict__ carry_tail, uint32_t* __restrict__ slice_flags) {
+    const uint32_t* __restrict__ slice_base, float* __restrict__ grad_dense, float* __restrict__ uniq_grad,
+    double* __restrict__ carry_head, double* __restrict__ carry_tail, uint32_t* __restrict__ slice_flags) {
     constexpr int EPC = BF16 ? 8 : 4;
+    constexpr int B = kReduceBatch;
     const int cpr = CPR_T ? CPR_T : cpr_rt;
     const int wpw = 64 / cpr;
     const int lane = threadIdx.x & 63;
     const int sub = lane / cpr;
     const int c = lane - sub * cpr;
+    const int wl0 = sub * cpr;
+    const int bb = cpr < B ? cpr : B;
     const int64_t wave = (int64_t)blockIdx.x * (kBlock / 64) + (threadIdx.x >> 6);
     const int64_t j = wave * wpw + sub;
+    if (blockIdx.x == 0 && threadIdx.x == 0) counters[1] = 0;  // long-run list of the fix-up that follows
     if (sub >= wpw || j >= num_slices) return;
-    const uint32_t nv = counters[0];
+    const uint32_t nv = min(counters[0], n);
     const uint32_t s0 = (uint32_t)j * kSlice;
     if (s0 >= nv) {
         if (c == 0) slice_flags[j] = 0;
@@ -427,41 +571,55 @@ __global__ __launch_bounds__(kBlock) void segment_reduce_kernel(
 #pragma unroll
     for (int e = 0; e < EPC; ++e) acc[e] = 0.0;
 
-    for (uint32_t i = s0; i < s1; i += kReduceBatch) {
-        uint32_t kk[kReduceBatch + 1], vv[kReduceBatch];
-        u32x4 x[kReduceBatch];
+    // Entry i + c of a batch: key, next key (0xFFFFFFFF past the end), lookup index.
+    // Indices are clamped so every load is in bounds and unconditional.
+    uint32_t k_cur, k_nxt, v_cur;
+    {
+        const uint32_t p = s0 + (uint32_t)c;
+        const uint32_t kc = keys[min(p, nv - 1)], kn = keys[min(p + 1, nv - 1)], vc = vals[min(p, s1 - 1)];
+        k_cur = p < nv ? kc : 0xFFFFFFFFu;
+        k_nxt = p + 1 < nv ? kn : 0xFFFFFFFFu;
+        v_cur = vc;
+    }
+    for (uint32_t i = s0; i < s1; i += bb) {
+        const uint32_t mk = k_cur, mv = v_cur;
+        const bool ends = c < bb && i + c < s1 && k_cur != k_nxt;
+        const uint32_t emask = (uint32_t)(__ballot(ends) >> wl0);
+        u32x4 x[B];
 #pragma unroll
-        for (int b = 0; b <= kReduceBatch; ++b) {
-            const uint32_t p = i + b;
-            kk[b] = p < nv ? keys[p] : 0xFFFFFFFFu;  // the entry after the batch decides its last run
+        for (int b = 0; b < B; ++b) {
+            const uint32_t vb = __shfl(mv, wl0 + b, 64);
+            const u32x4* src = (b < bb && i + b < s1 && vb < n) ? dy + ((size_t)vb * cpr + c) : &kZeroChunk;
+            x[b] = *src;
+        }
+        if (i + bb < s1) {
+            const uint32_t p = i + bb + (uint32_t)c;
+            const uint32_t kc = keys[min(p, nv - 1)], kn = keys[min(p + 1, nv - 1)], vc = vals[min(p, s1 - 1)];
+            k_cur = p < nv ? kc : 0xFFFFFFFFu;
+            k_nxt = p + 1 < nv ? kn : 0xFFFFFFFFu;
+            v_cur = vc;
         }
 #pragma unroll
-        for (int b = 0; b < kReduceBatch; ++b) vv[b] = (i + b < s1) ? vals[i + b] : 0u;
-#pragma unroll
-        for (int b = 0; b < kReduceBatch; ++b) {
-            x[b] = (u32x4){0u, 0u, 0u, 0u};
-            if (i + b < s1 && vv[b] < n) x[b] = dy[(size_t)vv[b] * cpr + c];
-        }
-#pragma unroll
-        for (int b = 0; b < kReduceBatch; ++b) {
+        for (int b = 0; b < B; ++b) {
             const uint32_t p = i + b;
-            if (p >= s1) break;
+            if (b >= bb || p >= s1) break;
             accumulate<BF16>(acc, x[b]);
-            const bool next_same = (p + 1 < nv) && kk[b + 1] == kk[b];
-            if (p + 1 < s1 && next_same) continue;
+            const bool run_end = (emask >> b) & 1u;
+            if (!run_end && p + 1 < s1) continue;
+            // Flush: the run ends at p, or the slice ends at p inside a run.
+            const uint32_t key = __shfl(mk, wl0 + b, 64);
             if (head_open) {
                 // first run of the slice, begun in an earlier slice
                 store_partial<EPC>(carry_head + (size_t)j * dim + c * EPC, acc);
-                flags |= kFlagHead | (next_same ? kFlagWhole : 0u);
+                flags |= kFlagHead | (run_end ? 0u : kFlagWhole);
                 head_open = false;
-            } else if (next_same) {
+            } else if (!run_end) {
                 // begins here and runs on into the next slice
                 store_partial<EPC>(carry_tail + (size_t)j * dim + c * EPC, acc);
                 flags |= kFlagTail;
                 ++u;
             } else {
-                write_run<EPC, DENSE>(acc, kk[b], u, c, dim, n, num_rows, row_begin, grad_dense, uniq_rows,
-                                      uniq_grad);
+                write_run<EPC, DENSE>(acc, key, u, c, dim, n, num_rows, grad_dense, uniq_grad);
                 ++u;
             }
 #pragma unroll
@@ -471,15 +629,21 @@ __global__ __launch_bounds__(kBlock) void segment_reduce_kernel(
     if (c == 0) slice_flags[j] = flags;
 }
 
-// Step 5: runs cut by slice edges, summed in slice order by the slice where
-// they begin.
+// Step 5: runs cut by slice edges, summed in slice order by the slice j where
+// they begin.  The run's last slice m comes from its last entry, found by a
+// galloping then binary search over the sorted keys (about 2 log2(run / S)
+// dependent loads).  A run over at most kLongRun slices is summed here by
+// one worker; a longer one (a hot row) is listed for long_run_kernel, which
+// splits its sum over a whole block.
+constexpr int64_t kLongRun = 32;
+
 template <int CPR_T, bool BF16, bool DENSE>
 __global__ __launch_bounds__(kBlock) void carry_fixup_kernel(
-    const uint32_t* __restrict__ keys, uint32_t n, uint32_t num_rows, int cpr_rt, int dim, uint32_t num_slices,
-    const uint32_t* __restrict__ slice_runs, const uint32_t* __restrict__ slice_base,
-    const uint32_t* __restrict__ slice_flags, const double* __restrict__ carry_head,
-    const double* __restrict__ carry_tail, int64_t row_begin, float* __restrict__ grad_dense,
-    int64_t* __restrict__ uniq_rows, float* __restrict__ uniq_grad) {
+    const uint32_t* __restrict__ keys, uint32_t* __restrict__ counters, uint32_t n, uint32_t num_rows,
+    int cpr_rt, int dim, uint32_t num_slices, const uint32_t* __restrict__ slice_runs,
+    const uint32_t* __restrict__ slice_base, const uint32_t* __restrict__ slice_flags,
+    const double* __restrict__ carry_head, const double* __restrict__ carry_tail, uint32_t* __restrict__ long_runs,
+    float* __restrict__ grad_dense, float* __restrict__ uniq_grad) {
     constexpr int EPC = BF16 ? 8 : 4;
     const int cpr = CPR_T ? CPR_T : cpr_rt;
     const int wpw = 64 / cpr;
@@ -490,56 +654,136 @@ __global__ __launch_bounds__(kBlock) void carry_fixup_kernel(
     const int64_t j = wave * wpw + sub;
     if (sub >= wpw || j >= num_slices) return;
     if (!(slice_flags[j] & kFlagTail)) return;
+    const uint32_t nv = min(counters[0], n);
+    // A tail run continues past the slice, so (j + 1) * kSlice < nv.
+    uint32_t lo = (uint32_t)(j + 1) * kSlice - 1;
+    if (lo + 1 >= nv) return;
+    const uint32_t key = keys[lo];
+    uint32_t step = kSlice, hi = lo + step;
+    while (hi < nv && keys[hi] == key) {
+        lo = hi;
+        step = step < 0x40000000u ? 2 * step : step;
+        hi = lo + step < lo ? nv : lo + step;
+    }
+    hi = min(hi, nv);  // keys[lo] == key; hi == nv or keys[hi] != key
+    while (hi - lo > 1) {
+        const uint32_t mid = lo + (hi - lo) / 2;
+        if (keys[mid] == key) lo = mid; else hi = mid;
+    }
+    const int64_t m = min((int64_t)(lo / kSlice), (int64_t)num_slices - 1);
+    if (m - j > kLongRun) {
+        if (c == 0) {
+            const uint32_t at = atomicAdd(&counters[1], 1u);
+            if (at < num_slices) {
+                long_runs[2 * at] = (uint32_t)j;
+                long_runs[2 * at + 1] = (uint32_t)m;
+            }
+        }
+        return;
+    }
     double acc[EPC];
 #pragma unroll
     for (int e = 0; e < EPC; ++e) acc[e] = 0.0;
     add_partial<EPC>(acc, carry_tail + (size_t)j * dim + c * EPC);
-    for (int64_t k = j + 1; k < num_slices; ++k) {
-        add_partial<EPC>(acc, carry_head + (size_t)k * dim + c * EPC);
-        if (!(slice_flags[k] & kFlagWhole)) break;
-    }
-    const uint32_t key = keys[(uint32_t)(j + 1) * kSlice - 1];
+#pragma unroll 8
+    for (int64_t k = j + 1; k <= m; ++k) add_partial<EPC>(acc, carry_head + (size_t)k * dim + c * EPC);
     const uint32_t u = slice_base[j] + slice_runs[j] - 1;
-    write_run<EPC, DENSE>(acc, key, u, c, dim, n, num_rows, row_begin, grad_dense, uniq_rows, uniq_grad);
+    write_run<EPC, DENSE>(acc, key, u, c, dim, n, num_rows, grad_dense, uniq_grad);
+}
+
+// Long runs: the block's sub-workers (cpr lanes each) sum equal contiguous
+// shares of the head partials j+1 .. m; the shares are then added in
+// sub-worker order after the tail partial, so the result does not depend on
+// scheduling.  The list order may vary; each run's sum does not.
+template <int CPR_T, bool BF16, bool DENSE>
+__global__ __launch_bounds__(kBlock) void long_run_kernel(
+    const uint32_t* __restrict__ keys, const uint32_t* __restrict__ counters, uint32_t n, uint32_t num_rows,
+    int cpr_rt, int dim, uint32_t num_slices, const uint32_t* __restrict__ slice_runs,
+    const uint32_t* __restrict__ slice_base, const double* __restrict__ carry_head,
+    const double* __restrict__ carry_tail, const uint32_t* __restrict__ long_runs, float* __restrict__ grad_dense,
+    float* __restrict__ uniq_grad) {
+    constexpr int EPC = BF16 ? 8 : 4;
+    extern __shared__ double s_share[];  // [sub-workers][dim]
+    const int cpr = CPR_T ? CPR_T : cpr_rt;
+    const int wpw = 64 / cpr;
+    const int lane = threadIdx.x & 63;
+    const int sub = lane / cpr;
+    const int c = lane - sub * cpr;
+    const int nsub = wpw * (kBlock / 64);
+    const int w = (threadIdx.x >> 6) * wpw + sub;  // sub-worker index in the block
+    const bool active = sub < wpw;
+    const uint32_t count = min(counters[1], num_slices);
+    for (uint32_t r = blockIdx.x; r < count; r += gridDim.x) {
+        const int64_t j = long_runs[2 * r], m = long_runs[2 * r + 1];
+        const int64_t total = m - j;  // head partials j+1 .. m
+        const int64_t per = (total + nsub - 1) / nsub;
+        double acc[EPC];
+#pragma unroll
+        for (int e = 0; e < EPC; ++e) acc[e] = 0.0;
+        if (active) {
+            const int64_t b = j + 1 + (int64_t)w * per, end = min(b + per, m + 1);
+#pragma unroll 8
+            for (int64_t k = b; k < end; ++k) add_partial<EPC>(acc, carry_head + (size_t)k * dim + c * EPC);
+#pragma unroll
+            for (int e = 0; e < EPC; ++e) s_share[(size_t)w * dim + c * EPC + e] = acc[e];
+        }
+        __syncthreads();
+        if (w == 0 && active) {
+#pragma unroll
+            for (int e = 0; e < EPC; ++e) acc[e] = 0.0;
+            add_partial<EPC>(acc, carry_tail + (size_t)j * dim + c * EPC);
+            for (int q = 0; q < nsub; ++q)
+#pragma unroll
+                for (int e = 0; e < EPC; ++e) acc[e] += s_share[(size_t)q * dim + c * EPC + e];
+            const uint32_t key = keys[min((uint32_t)(j + 1) * kSlice - 1, n - 1)];
+            const uint32_t u = slice_base[j] + slice_runs[j] - 1;
+            write_run<EPC, DENSE>(acc, key, u, c, dim, n, num_rows, grad_dense, uniq_grad);
+        }
+        __syncthreads();
+    }
 }
 
 template <int CPR_T, bool BF16, bool DENSE>
-hipError_t launch_reduce(const Layout& L, char* ws, const void* grad_out, uint32_t n, uint32_t num_rows, int cpr,
-                         int dim, int64_t row_begin,
-                         float* grad_dense, int64_t* uniq_rows, float* uniq_grad, const uint32_t* sorted_keys,
-                         const uint32_t* sorted_vals, hipStream_t stream) {
+hipError_t launch_reduce(const Layout& L, const char* ws, const void* grad_out, uint32_t n, uint32_t num_rows,
+                         int cpr, int dim, float* grad_dense, float* uniq_grad, hipStream_t stream) {
     const int wpw = 64 / cpr;
     const int64_t waves = (L.num_slices + wpw - 1) / wpw;
     const int64_t grid = (waves + (kBlock / 64) - 1) / (kBlock / 64);
     const uint32_t ns = (uint32_t)L.num_slices;
+    const uint32_t* sorted_keys = (const uint32_t*)(ws + L.sorted_keys);
+    const uint32_t* sorted_vals = (const uint32_t*)(ws + L.sorted_vals);
+    double* carry_head = (double*)(ws + L.carry_head);
+    double* carry_tail = (double*)(ws + L.carry_tail);
+    uint32_t* flags = (uint32_t*)(ws + L.slice_flags);
+    uint32_t* counters = (uint32_t*)(ws + L.counters);
+    uint32_t* long_runs = (uint32_t*)(ws + L.long_runs);
     hipLaunchKernelGGL((segment_reduce_kernel<CPR_T, BF16, DENSE>), dim3((unsigned)grid), dim3(kBlock), 0, stream,
-                       sorted_keys, sorted_vals, (const uint32_t*)(ws + L.counters), (const u32x4*)grad_out, n,
-                       num_rows, cpr, dim, ns, (const uint32_t*)(ws + L.slice_base), row_begin, grad_dense, uniq_rows, uniq_grad,
-                       (double*)(ws + L.carry_head), (double*)(ws + L.carry_tail),
-                       (uint32_t*)(ws + L.slice_flags));
+                       sorted_keys, sorted_vals, counters, (const u32x4*)grad_out, n, num_rows, cpr, dim, ns,
+                       (const uint32_t*)(ws + L.slice_base), grad_dense, uniq_grad, carry_head, carry_tail, flags);
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
     hipLaunchKernelGGL((carry_fixup_kernel<CPR_T, BF16, DENSE>), dim3((unsigned)grid), dim3(kBlock), 0, stream,
-                       sorted_keys, n, num_rows, cpr, dim, ns, (const uint32_t*)(ws + L.slice_runs),
-                       (const uint32_t*)(ws + L.slice_base), (const uint32_t*)(ws + L.slice_flags),
-                       (const double*)(ws + L.carry_head), (const double*)(ws + L.carry_tail), row_begin,
-                       grad_dense, uniq_rows, uniq_grad);
+                       sorted_keys, counters, n, num_rows, cpr, dim, ns, (const uint32_t*)(ws + L.slice_runs),
+                       (const uint32_t*)(ws + L.slice_base), (const uint32_t*)flags, (const double*)carry_head,
+                       (const double*)carry_tail, long_runs, grad_dense, uniq_grad);
+    if ((err = hipGetLastError()) != hipSuccess) return err;
+    const size_t share_bytes = (size_t)wpw * (kBlock / 64) * dim * sizeof(double);
+    hipLaunchKernelGGL((long_run_kernel<CPR_T, BF16, DENSE>), dim3(256), dim3(kBlock), share_bytes, stream,
+                       sorted_keys, (const uint32_t*)counters, n, num_rows, cpr, dim, ns,
+                       (const uint32_t*)(ws + L.slice_runs), (const uint32_t*)(ws + L.slice_base),
+                       (const double*)carry_head, (const double*)carry_tail, (const uint32_t*)long_runs, grad_dense,
+                       uniq_grad);
     return hipGetLastError();
 }
 
 template <bool BF16, bool DENSE>
-hipError_t dispatch_reduce(const Layout& L, char* ws, const void* grad_out, uint32_t n, uint32_t num_rows, int cpr,
-                           int dim, int64_t row_begin,
-                           float* grad_dense, int64_t* uniq_rows, float* uniq_grad, const uint32_t* k,
-                           const uint32_t* v, hipStream_t stream) {
+hipError_t dispatch_reduce(const Layout& L, const char* ws, const void* grad_out, uint32_t n, uint32_t num_rows,
+                           int cpr, int dim, float* grad_dense, float* uniq_grad, hipStream_t stream) {
     if (BF16 && cpr == 20)
-        return launch_reduce<20, BF16, DENSE>(L, ws, grad_out, n, num_rows, cpr, dim, row_begin, grad_dense, uniq_rows,
-                                              uniq_grad, k, v, stream);
+        return launch_reduce<20, BF16, DENSE>(L, ws, grad_out, n, num_rows, cpr, dim, grad_dense, uniq_grad, stream);
     if (!BF16 && cpr == 40)
-        return launch_reduce<40, BF16, DENSE>(L, ws, grad_out, n, num_rows, cpr, dim, row_begin, grad_dense, uniq_rows,
-                                              uniq_grad, k, v, stream);
-    return launch_reduce<0, BF16, DENSE>(L, ws, grad_out, n, num_rows, cpr, dim, row_begin, grad_dense, uniq_rows, uniq_grad,
-                                         k, v, stream);
+        return launch_reduce<40, BF16, DENSE>(L, ws, grad_out, n, num_rows, cpr, dim, grad_dense, uniq_grad, stream);
+    return launch_reduce<0, BF16, DENSE>(L, ws, grad_out, n, num_rows, cpr, dim, grad_dense, uniq_grad, stream);
 }
 
 }  // namespace
@@ -549,10 +793,9 @@ size_t scatter_workspace_bytes(int64_t n, int64_t num_rows, int dim) {
     return make_layout(n, dim).total;
 }
 
-hipError_t launch_scatter_add(const int64_t* rows, int64_t n, const void* grad_out, int elem_bytes, int dim,
-                              int64_t row_begin, int64_t num_rows, float* grad_dense, int64_t* uniq_rows,
-                              float* uniq_grad, int64_t* num_uniq, void* workspace, int64_t* status,
-                              hipStream_t stream) {
+hipError_t launch_scatter_plan(const int64_t* rows, int64_t n, int64_t row_begin, int64_t num_rows, int dim,
+                               int64_t* uniq_rows, int64_t* num_uniq, void* workspace, int64_t* status,
+                               hipStream_t stream) {
     const Layout L = make_layout(n, dim);
     char* ws = (char*)workspace;
     uint32_t* counters = (uint32_t*)(ws + L.counters);
@@ -563,18 +806,24 @@ hipError_t launch_scatter_add(const int64_t* rows, int64_t n, const void* grad_o
     const uint32_t nn = (uint32_t)n, tiles = (uint32_t)L.num_tiles;
     uint32_t* hist = (uint32_t*)(ws + L.hist);
     uint32_t* digit_total = (uint32_t*)(ws + L.digit_total);
-    uint32_t *k_cur = (uint32_t*)(ws + L.keys_a), *k_nxt = (uint32_t*)(ws + L.keys_b);
-    uint32_t *v_cur = (uint32_t*)(ws + L.vals_a), *v_nxt = (uint32_t*)(ws + L.vals_b);
-
+    // Passes ping-pong between the two buffers and must end in the sorted slots.
+    int bits = 0;
+    while (bits < 32 && ((uint64_t)num_rows >> bits) != 0) ++bits;  // the sentinel num_rows sorts last
+    const int passes = (bits + 7) / 8;
+    uint32_t *k_cur, *k_nxt, *v_cur, *v_nxt;
+    if (passes % 2 == 0) {
+        k_cur = (uint32_t*)(ws + L.sorted_keys); k_nxt = (uint32_t*)(ws + L.spare_keys);
+        v_cur = (uint32_t*)(ws + L.sorted_vals); v_nxt = (uint32_t*)(ws + L.spare_vals);
+    } else {
+        k_cur = (uint32_t*)(ws + L.spare_keys); k_nxt = (uint32_t*)(ws + L.sorted_keys);
+        v_cur = (uint32_t*)(ws + L.spare_vals); v_nxt = (uint32_t*)(ws + L.sorted_vals);
+    }
     hipLaunchKernelGGL(keys_kernel, dim3(tiles), dim3(kBlock), 0, stream, rows, nn, row_begin, (uint64_t)num_rows,
                        k_cur, v_cur, hist, tiles, status, counters);
     if ((err = hipGetLastError()) != hipSuccess) return err;
-
-    // The sentinel num_rows must sort after every valid key: sort its bit length.
-    int bits = 0;
-    while (bits < 32 && ((uint64_t)num_rows >> bits) != 0) ++bits;
-    for (int shift = 0; shift < bits; shift += 8) {
-        if (shift > 0) {
+    for (int p = 0; p < passes; ++p) {
+        const int shift = 8 * p;
+        if (p > 0) {
             hipLaunchKernelGGL(upsweep_kernel, dim3(tiles), dim3(kBlock), 0, stream, k_cur, nn, shift, hist, tiles);
             if ((err = hipGetLastError()) != hipSuccess) return err;
         }
@@ -587,25 +836,29 @@ hipError_t launch_scatter_add(const int64_t* rows, int64_t n, const void* grad_o
     }
 
     const uint32_t ns = (uint32_t)L.num_slices;
-    hipLaunchKernelGGL(run_count_kernel, dim3(ns), dim3(kBlock), 0, stream, k_cur, counters,
-                       (uint32_t*)(ws + L.slice_runs));
-    hipLaunchKernelGGL(slice_scan_kernel, dim3(1), dim3(kBlock), 0, stream, (const uint32_t*)(ws + L.slice_runs), ns,
-                       (uint32_t*)(ws + L.slice_base), num_uniq);
-    if ((err = hipGetLastError()) != hipSuccess) return err;
+    const uint32_t span_blocks = (uint32_t)((n + kSliceSpan - 1) / kSliceSpan);
+    hipLaunchKernelGGL(run_count_kernel, dim3(span_blocks), dim3(kBlock), 0, stream, k_cur, nn, counters,
+                       (uint32_t*)(ws + L.slice_runs), ns);
+    hipLaunchKernelGGL(slice_scan_kernel, dim3(1), dim3(kScanBlock), 0, stream, (const uint32_t*)(ws + L.slice_runs),
+                       ns, (uint32_t*)(ws + L.slice_base), num_uniq);
+    if (uniq_rows)
+        hipLaunchKernelGGL(uniq_rows_kernel, dim3(span_blocks), dim3(kBlock), 0, stream, k_cur, nn, counters,
+                           (const uint32_t*)(ws + L.slice_base), row_begin, uniq_rows);
+    return hipGetLastError();
+}
 
+hipError_t launch_scatter_apply(const void* grad_out, int elem_bytes, int dim, int64_t n, int64_t num_rows,
+                                float* grad_dense, float* uniq_grad, const void* workspace, hipStream_t stream) {
+    if (n == 0) return hipSuccess;
+    const Layout L = make_layout(n, dim);
+    const char* ws = (const char*)workspace;
     const int cpr = dim * elem_bytes / 16;
+    const uint32_t nn = (uint32_t)n, nr = (uint32_t)num_rows;
     const bool bf16 = elem_bytes == 2, dense = grad_dense != nullptr;
-    if (bf16 && dense)
-        return dispatch_reduce<true, true>(L, ws, grad_out, nn, (uint32_t)num_rows, cpr, dim, row_begin, grad_dense,
-                                           uniq_rows, uniq_grad, k_cur, v_cur, stream);
-    if (bf16)
-        return dispatch_reduce<true, false>(L, ws, grad_out, nn, (uint32_t)num_rows, cpr, dim, row_begin, grad_dense,
-                                            uniq_rows, uniq_grad, k_cur, v_cur, stream);
-    if (dense)
-        return dispatch_reduce<false, true>(L, ws, grad_out, nn, (uint32_t)num_rows, cpr, dim, row_begin, grad_dense,
-                                            uniq_rows, uniq_grad, k_cur, v_cur, stream);
-    return dispatch_reduce<false, false>(L, ws, grad_out, nn, (uint32_t)num_rows, cpr, dim, row_begin, grad_dense,
-                                         uniq_rows, uniq_grad, k_cur, v_cur, stream);
+    if (bf16 && dense) return dispatch_reduce<true, true>(L, ws, grad_out, nn, nr, cpr, dim, grad_dense, uniq_grad, stream);
+    if (bf16) return dispatch_reduce<true, false>(L, ws, grad_out, nn, nr, cpr, dim, grad_dense, uniq_grad, stream);
+    if (dense) return dispatch_reduce<false, true>(L, ws, grad_out, nn, nr, cpr, dim, grad_dense, uniq_grad, stream);
+    return dispatch_reduce<false, false>(L, ws, grad_out, nn, nr, cpr, dim, grad_dense, uniq_grad, stream);
 }
 
 }  // namespace engram

@@ -96,6 +96,10 @@ def load_library(path=LIB_PATH):
     lib.engram_scatter_add_workspace.argtypes = [i64, i64, i32]
     lib.engram_scatter_add.restype = ctypes.c_int
     lib.engram_scatter_add.argtypes = [p, i64, p, i32, i32, i64, i64, p, p, p, p, p, sz, p, p]
+    lib.engram_scatter_add_plan.restype = ctypes.c_int
+    lib.engram_scatter_add_plan.argtypes = [p, i64, i64, i64, i32, p, p, p, sz, p, p]
+    lib.engram_scatter_add_apply.restype = ctypes.c_int
+    lib.engram_scatter_add_apply.argtypes = [p, i32, i32, i64, i64, i64, p, p, p, sz, p]
     lib.engram_strerror.restype = ctypes.c_char_p
     lib.engram_strerror.argtypes = [ctypes.c_int]
     _lib = lib
@@ -235,3 +239,34 @@ def engram_scatter_add(rows, grad_out, num_rows, row_begin=0, grad_dense=None, c
         u = int(nu.item())
         return ur[:u], ug[:u]
     return ur, ug, nu
+
+
+def engram_scatter_add_plan(rows, num_rows, dim, row_begin=0, workspace=None, uniq_rows=None, num_uniq=None,
+                            status=None, stream=None):
+    """Phase 1 of engram_scatter_add: sort the lookups by row into ``workspace``.
+    Returns the workspace (allocated when not given)."""
+    lib = load_library()
+    n = rows.numel()
+    if workspace is None:
+        workspace = torch.empty(engram_scatter_add_workspace(n, num_rows, dim), dtype=torch.uint8, device=rows.device)
+    _check(lib.engram_scatter_add_plan(_dev_ptr(rows, "rows", torch.int64), n, row_begin, num_rows, dim,
+                                       _dev_ptr(uniq_rows, "uniq_rows", torch.int64),
+                                       _dev_ptr(num_uniq, "num_uniq", torch.int64), _dev_ptr(workspace, "workspace"),
+                                       workspace.numel() * workspace.element_size(),
+                                       _dev_ptr(status, "status", torch.int64), _stream_handle(stream)),
+           "engram_scatter_add_plan")
+    return workspace
+
+
+def engram_scatter_add_apply(grad_out, n, num_rows, workspace, row_begin=0, grad_dense=None, uniq_grad=None,
+                             stream=None):
+    """Phase 2: per-row sums of ``grad_out`` along the plan in ``workspace`` (dense or compact)."""
+    lib = load_library()
+    dim = grad_out.shape[-1]
+    _check(lib.engram_scatter_add_apply(_dev_ptr(grad_out, "grad_out"), _dtype_code(grad_out), dim, n, row_begin,
+                                        num_rows, _dev_ptr(grad_dense, "grad_dense", torch.float32),
+                                        _dev_ptr(uniq_grad, "uniq_grad", torch.float32),
+                                        _dev_ptr(workspace, "workspace"),
+                                        workspace.numel() * workspace.element_size(), _stream_handle(stream)),
+           "engram_scatter_add_apply")
+    return grad_dense if grad_dense is not None else uniq_grad

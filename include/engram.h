@@ -147,6 +147,32 @@ int engram_scatter_add(const int64_t* rows, int64_t n, const void* grad_out, int
                        float* uniq_grad, int64_t* num_uniq, void* workspace, size_t workspace_bytes,
                        int64_t* status, hipStream_t stream);
 
+/* The two phases of engram_scatter_add, for callers that reuse one set of row ids
+ * (several gradients over the same lookups) or time the phases apart.
+ *
+ * engram_scatter_add_plan: sorts the lookups by row (stable, so each row's lookups
+ * keep ascending index order) and records the runs of equal rows in `workspace`.
+ *   rows       device int64 [n] global row IDs
+ *   uniq_rows  device int64 [n] or NULL: when given, the U distinct in-range rows in
+ *              ascending order (global IDs) are written to uniq_rows[0, U)
+ *   num_uniq   device int64 scalar or NULL: receives U
+ *   status     as for engram_gather (out-of-range rows are left out of the plan)
+ * engram_scatter_add_apply: the per-row fp64 sums of grad_out along the plan in
+ * `workspace`, in exactly one output form (dense grad_dense += S, or compact
+ * uniq_grad[u] = S of the u-th distinct row).  n, row_begin, num_rows and dim must
+ * be those of the plan call, and the workspace must not have been reused since;
+ * mismatched use gives unspecified sums but no access outside the buffers sized
+ * by these arguments.
+ * engram_scatter_add(rows, ...) is exactly plan followed by apply on one stream.
+ * Same limits and return codes as engram_scatter_add. */
+int engram_scatter_add_plan(const int64_t* rows, int64_t n, int64_t row_begin, int64_t num_rows, int32_t dim,
+                            int64_t* uniq_rows, int64_t* num_uniq, void* workspace, size_t workspace_bytes,
+                            int64_t* status, hipStream_t stream);
+
+int engram_scatter_add_apply(const void* grad_out, int32_t dtype, int32_t dim, int64_t n, int64_t row_begin,
+                             int64_t num_rows, float* grad_dense, float* uniq_grad, const void* workspace,
+                             size_t workspace_bytes, hipStream_t stream);
+
 /* Static English text for an engram_status code. */
 const char* engram_strerror(int code);
 

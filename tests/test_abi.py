@@ -138,3 +138,25 @@ def test_product_constants_match_oracle_derivation():
     assert E.QWEN3_8_FLASH_NEXT_NGRAM_PADDED_ROWS == C.padded_rows()
     assert E.QWEN3_8_FLASH_NEXT_LAYER_MULTIPLIERS == C.LAYER_MULTIPLIERS
     assert E.QWEN3_8_FLASH_NEXT_EOS_TOKEN_ID == C.EOS_TOKEN_ID
+
+
+def test_plan_apply_reject_bad_arguments(lib):
+    f = ctypes.c_void_p(0x1000)
+    ws = ctypes.c_void_p(0x100000)
+    n, R, D = 1000, 5000, 160
+    need = lib.engram_scatter_add_workspace(n, R, D)
+    plan = lambda rows=f, nn=n, rb=0, nr=R, dim=D, w=ws, wb=need: lib.engram_scatter_add_plan(
+        rows, nn, rb, nr, dim, None, None, w, wb, None, None)
+    assert plan(rows=None) == B.ENGRAM_EINVAL
+    assert plan(nn=-5) == B.ENGRAM_EINVAL
+    assert plan(dim=6) == B.ENGRAM_EINVAL               # valid for neither element type
+    assert plan(nr=-1) == B.ENGRAM_EINVAL
+    assert plan(w=None) == B.ENGRAM_EWORKSPACE
+    assert plan(wb=need - 1) == B.ENGRAM_EWORKSPACE
+    apply = lambda g=f, dt=B.ENGRAM_BF16, dim=D, nn=n, dense=None, ug=f, w=ws, wb=need: lib.engram_scatter_add_apply(
+        g, dt, dim, nn, 0, R, dense, ug, w, wb, None)
+    assert apply(dt=9) == B.ENGRAM_EDTYPE
+    assert apply(g=None) == B.ENGRAM_EINVAL
+    assert apply(dense=f) == B.ENGRAM_EINVAL          # both forms
+    assert apply(ug=None) == B.ENGRAM_EINVAL          # neither form
+    assert apply(w=ctypes.c_void_p(0x100008)) == B.ENGRAM_EWORKSPACE

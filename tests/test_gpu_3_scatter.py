@@ -194,3 +194,58 @@ def test_sft_shape_backward():
     ids, _ = W.sft_batch(0)
     rows = oracle_hash(ids, ws).reshape(-1)
     check_compact(rows, grads(rows.size, seed=10), ws["num_rows"])
+
+
+def test_plan_apply_reuse():
+    """One plan, several gradients: each apply equals a full scatter-add bit for bit,
+    in both output forms."""
+    rng = np.random.default_rng(12)
+    R = 50000
+    rows_np = (rng.zipf(1.2, size=150000) % R).astype(np.int64)
+    rows = torch.from_numpy(rows_np).cuda()
+    n = rows.numel()
+    ur = torch.empty(n, dtype=torch.int64, device="cuda")
+    nu = torch.empty((), dtype=torch.int64, device="cuda")
+    ws = E.engram_scatter_add_plan(rows, R, 160, uniq_rows=ur, num_uniq=nu)
+    for seed in (1, 2):
+        dy = grads(n, seed=seed)
+        ug = torch.empty((n, 160), dtype=torch.float32, device="cuda")
+        E.engram_scatter_add_apply(dy, n, R, ws, uniq_grad=ug)
+        g = torch.zeros((R, 160), dtype=torch.float32, device="cuda")
+        E.engram_scatter_add_apply(dy, n, R, ws, grad_dense=g)
+        ref_r, ref_g = E.engram_scatter_add(rows, dy, R)
+        u = int(nu.item())
+        assert u == ref_r.numel()
+        assert torch.equal(ur[:u], ref_r)
+        assert torch.equal(ug[:u].view(torch.int32), ref_g.view(torch.int32))
+        assert torch.equal(g[ref_r].view(torch.int32), ref_g.view(torch.int32))
+        rur, rug, _ = c_oracle.scatter_add_compact(rows_np, to_host(dy), R)
+        assert_close_to_fp64(ug[:u].cpu().numpy(), rug, "apply seed %d" % seed)
+
+
+def test_plan_without_outputs():
+    """A plan needs neither uniq_rows nor num_uniq; apply still writes the compact sums."""
+    rng = np.random.default_rng(13)
+    rows_np = rng.integers(0, 1000, size=20000).astype(np.int64)
+    rows = torch.from_numpy(rows_np).cuda()
+    ws = E.engram_scatter_add_plan(rows, 1000, 160)
+    dy = grads(rows.numel(), seed=13)
+    ug = torch.empty((rows.numel(), 160), dtype=torch.float32, device="cuda")
+    E.engram_scatter_add_apply(dy, rows.numel(), 1000, ws, uniq_grad=ug)
+    rur, rug, _ = c_oracle.scatter_add_compact(rows_np, to_host(dy), 1000)
+    assert_close_to_fp64(ug[:rur.size].cpu().numpy(), rug, "apply without plan outputs")
+
+
+def test_many_long_runs():
+    """Dozens of rows with thousands of hits each (several slices per run), shuffled
+    among singletons, in both output forms."""
+    rng = np.random.default_rng(14)
+    hot = rng.choice(200000, size=40, replace=False)
+    rows = np.concatenate([np.repeat(hot, rng.integers(2000, 20000, size=40)),
+                           rng.integers(0, 200000, size=100000)]).astype(np.int64)
+    rng.shuffle(rows)
+    dy = grads(rows.size, seed=14)
+    check_compact(rows, dy, 200000)
+    got, _ = run_dense(rows, dy, 200000)
+    ref, _ = c_oracle.scatter_add_dense(rows, to_host(dy), 200000)
+    assert_close_to_fp64(got, ref, "dense many long runs")
