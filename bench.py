@@ -114,7 +114,8 @@ def build_workload(name, rotations, dev):
         g.manual_seed(1000 + r)
         b = {"ids": ids, "tokens": tokens, "rows": rows, "n": n,
              "out": torch.empty((n, W.DIM), dtype=torch.bfloat16, device=dev),
-             "status": torch.empty((), dtype=torch.int64, device=dev)}
+             "status": torch.empty((), dtype=torch.int64, device=dev),
+             "plan_status": torch.empty((), dtype=torch.int64, device=dev)}
         if name in ("long", "owner"):
             b["dy"] = torch.randn((n, W.DIM), generator=g, device=dev).to(torch.bfloat16)
         if name == "long":
@@ -130,35 +131,46 @@ def build_workload(name, rotations, dev):
     if name in ("long", "owner"):
         workspace = torch.empty(E.engram_scatter_add_workspace(n_max, table_rows, W.DIM), dtype=torch.uint8,
                                 device=dev)
-    return {"name": name, "spec": spec, "table": table, "row_begin": row_begin, "table_rows": table_rows, "batches": batches,
+    return {"side": torch.cuda.Stream(device=dev), "name": name, "spec": spec, "table": table, "row_begin": row_begin, "table_rows": table_rows, "batches": batches,
             "grad_dense": grad_dense, "workspace": workspace, "backward": name in ("long", "owner")}
 
 
 def run_step(wl, b, ev=None):
-    """hash -> gather -> (backward) plan -> apply, all on the current stream.
-    ev: five events recorded between the phases."""
+    """hash -> gather, with the backward plan (sort by row) on a side stream
+    concurrently with the gather, then apply once both are done.  ev: events
+    (hash start, hash end, gather end, plan start, plan end, apply start, apply end)."""
+    import torch
+
     import hashed_gram_embedding_engram_amd as E
+    main = torch.cuda.current_stream()
+    side = wl["side"]
     if ev:
-        ev[0].record()
+        ev[0].record(main)
     if b["tokens"] is not None:
         E.engram_hash(b["tokens"], wl["spec"], rows_out=b["rows"])
     if ev:
-        ev[1].record()
-    E.engram_gather(wl["table"], b["rows"], wl["row_begin"], out=b["out"], status=b["status"], validate=False)
-    if ev:
-        ev[2].record()
+        ev[1].record(main)
     if wl["backward"]:
+        side.wait_stream(main)
         compact = b.get("compact")
+        if ev:
+            ev[3].record(side)
         E.engram_scatter_add_plan(b["rows"], wl["table_rows"], b["dy"].shape[-1], wl["row_begin"],
                                   workspace=wl["workspace"], uniq_rows=compact[0] if compact else None,
-                                  num_uniq=compact[2] if compact else None, status=b["status"])
+                                  num_uniq=compact[2] if compact else None, status=b["plan_status"], stream=side)
+        if ev:
+            ev[4].record(side)
+    E.engram_gather(wl["table"], b["rows"], wl["row_begin"], out=b["out"], status=b["status"], validate=False)
     if ev:
-        ev[3].record()
+        ev[2].record(main)
     if wl["backward"]:
+        main.wait_stream(side)
+        if ev:
+            ev[5].record(main)
         E.engram_scatter_add_apply(b["dy"], b["n"], wl["table_rows"], wl["workspace"], wl["row_begin"],
                                    grad_dense=wl["grad_dense"], uniq_grad=compact[1] if compact else None)
-    if ev:
-        ev[4].record()
+        if ev:
+            ev[6].record(main)
 
 
 def cpu_baseline(wl, max_tokens=None):
@@ -231,7 +243,7 @@ def main():
         run_step(wl, wl["batches"][i % R])
     torch.cuda.synchronize()
 
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(7)] for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
@@ -241,12 +253,10 @@ def main():
 
     lookups = sum(wl["batches"][i % R]["n"] for i in range(args.steps))
     elapsed = t1 - t0
-    names = ("hash", "gather", "scatter_plan", "scatter_apply")
-    phase = {k: 0.0 for k in names}
-    for e in evs:
-        for k, name in enumerate(names):
-            phase[name] += e[k].elapsed_time(e[k + 1])
-    phase = {k: v / args.steps for k, v in phase.items()}
+    spans = {"hash": (0, 1), "gather": (1, 2)}
+    if wl["backward"]:
+        spans.update({"scatter_plan (side stream)": (3, 4), "wait_for_plan": (2, 5), "scatter_apply": (5, 6)})
+    phase = {k: sum(e[a].elapsed_time(e[b]) for e in evs) / args.steps for k, (a, b) in spans.items()}
     n_avg = lookups / args.steps
     U = None
     b0 = wl["batches"][0]
@@ -270,6 +280,8 @@ def main():
         else:
             apply_bytes = 328.0 * n_avg + 640.0 * u_rows
     kern = {"gather": (gather_bytes, phase["gather"], "gather_rows_kernel<20,16,true>", "gather.hip")}
+    # The plan runs on a side stream during the gather; apply is timed from
+    # after the main stream's wait for it.
     if wl["backward"]:
         kern["scatter_apply"] = (apply_bytes, phase["scatter_apply"],
                                  "segment_reduce_kernel<20,bf16> + carry_fixup_kernel", "scatter.hip")

@@ -58,7 +58,7 @@ constexpr uint32_t kFlagHead = 1, kFlagWhole = 2, kFlagTail = 4;
 
 struct Layout {
     size_t sorted_keys, spare_keys, sorted_vals, spare_vals, hist, digit_total, counters, slice_runs, slice_base,
-        slice_flags, long_runs, carry_head, carry_tail, total;
+        slice_first, slice_flags, long_runs, carry_head, carry_tail, total;
     int64_t num_tiles, num_slices;
 };
 
@@ -79,6 +79,7 @@ Layout make_layout(int64_t n, int dim) {
     L.counters = take(16);
     L.slice_runs = take(4 * (size_t)L.num_slices);
     L.slice_base = take(4 * (size_t)L.num_slices);
+    L.slice_first = take(4 * (size_t)L.num_slices);
     L.slice_flags = take(4 * (size_t)L.num_slices);
     L.long_runs = take(8 * (size_t)L.num_slices);
     L.carry_head = take(8 * (size_t)L.num_slices * (size_t)dim);
@@ -152,12 +153,17 @@ __global__ __launch_bounds__(kBlock) void keys_kernel(const int64_t* __restrict_
     const uint32_t base = blockIdx.x * (uint32_t)kTile + (uint32_t)w * kWaveSpan;
     const uint32_t sentinel = (uint32_t)num_rows;
     uint32_t my_valid = 0;
-#pragma unroll 4
+    // Loads are clamped rather than guarded, so all of a thread's loads are in
+    // flight together (a guarded load becomes a branch that waits for it).
+    int64_t r[kItems];
+#pragma unroll
+    for (int it = 0; it < kItems; ++it) r[it] = rows[min(base + (uint32_t)it * 64 + (uint32_t)lane, n - 1)];
+#pragma unroll
     for (int it = 0; it < kItems; ++it) {
         const uint32_t e = base + (uint32_t)it * 64 + (uint32_t)lane;
         if (e < n) {
             uint32_t key = sentinel;
-            const uint64_t local = (uint64_t)rows[e] - (uint64_t)row_begin;
+            const uint64_t local = (uint64_t)r[it] - (uint64_t)row_begin;
             if (local < num_rows) {
                 key = (uint32_t)local;
                 ++my_valid;
@@ -213,7 +219,8 @@ __global__ __launch_bounds__(kBlock) void digit_scan_kernel(uint32_t* __restrict
     uint32_t running = 0;
     for (uint32_t b = 0; b < num_tiles; b += kBlock) {
         const uint32_t i = b + threadIdx.x;
-        const uint32_t v = i < num_tiles ? row[i] : 0u;
+        const uint32_t raw = row[min(i, num_tiles - 1)];
+        const uint32_t v = i < num_tiles ? raw : 0u;
         uint32_t tot;
         const uint32_t ex = block_exclusive_scan(v, &tot, s_tmp);
         if (i < num_tiles) row[i] = running + ex;
@@ -245,10 +252,9 @@ __global__ __launch_bounds__(kBlock) void downsweep_kernel(const uint32_t* __res
     uint32_t key[kItems], val[kItems], rank[kItems];
 #pragma unroll
     for (int it = 0; it < kItems; ++it) {
-        const uint32_t e = base + (uint32_t)it * 64 + (uint32_t)lane;
-        const bool live = e < n;
-        key[it] = live ? keys_in[e] : 0u;
-        val[it] = live ? vals_in[e] : 0u;
+        const uint32_t e = min(base + (uint32_t)it * 64 + (uint32_t)lane, n - 1);
+        key[it] = keys_in[e];
+        val[it] = vals_in[e];
     }
     // Rank every key among the equal digits before it in this wave's span:
     // items are visited in index order and the lowest lane of each digit group
@@ -306,33 +312,46 @@ __global__ __launch_bounds__(kBlock) void downsweep_kernel(const uint32_t* __res
     }
 }
 
-// Step 3a: number of runs that start in each slice of sorted in-range keys.
-// One block per kSliceSpan entries.
+// Step 3a: per slice, the number of runs that start in it and the index of
+// the first such start (0xFFFFFFFF when a run covers the whole slice).  One
+// block per kSliceSpan entries.
+constexpr uint32_t kNoStart = 0xFFFFFFFFu;
 __global__ __launch_bounds__(kBlock) void run_count_kernel(const uint32_t* __restrict__ keys, uint32_t n,
                                                            const uint32_t* __restrict__ counters,
-                                                           uint32_t* __restrict__ slice_runs, uint32_t num_slices) {
+                                                           uint32_t* __restrict__ slice_runs,
+                                                           uint32_t* __restrict__ slice_first, uint32_t num_slices) {
     constexpr uint32_t kPer = kSliceSpan / kSlice;  // slices per block
-    __shared__ uint32_t s_cnt[kPer];
+    __shared__ uint32_t s_cnt[kPer], s_first[kPer];
     const uint32_t nv = min(counters[0], n);
-    if (threadIdx.x < kPer) s_cnt[threadIdx.x] = 0;
+    if (threadIdx.x < kPer) {
+        s_cnt[threadIdx.x] = 0;
+        s_first[threadIdx.x] = kNoStart;
+    }
     __syncthreads();
     for (uint32_t off = 0; off < kSliceSpan; off += kBlock) {
         const uint32_t t = off + threadIdx.x;
         const uint32_t i = blockIdx.x * kSliceSpan + t;
-        const bool start = i < nv && (i == 0 || keys[i] != keys[i - 1]);
+        const uint32_t kc = keys[min(i, n - 1)], kp = keys[i == 0 ? 0u : min(i - 1, n - 1)];
+        const bool start = i < nv && (i == 0 || kc != kp);
         const uint64_t b = __ballot(start);
-        // one LDS add per wave when a wave lies in one slice, else one per run start
         const uint32_t q = t / kSlice;
-        if (kSlice >= 64) {
-            if ((threadIdx.x & 63) == 0) atomicAdd(&s_cnt[q], (uint32_t)__popcll(b));
+        if (kSlice >= 64) {  // a wave lies inside one slice: one LDS update per wave
+            if ((threadIdx.x & 63) == 0 && b) {
+                atomicAdd(&s_cnt[q], (uint32_t)__popcll(b));
+                atomicMin(&s_first[q], i + (uint32_t)(__ffsll((unsigned long long)b) - 1));
+            }
         } else if (start) {
             atomicAdd(&s_cnt[q], 1u);
+            atomicMin(&s_first[q], i);
         }
     }
     __syncthreads();
     if (threadIdx.x < kPer) {
         const uint32_t j = blockIdx.x * kPer + threadIdx.x;
-        if (j < num_slices) slice_runs[j] = s_cnt[threadIdx.x];
+        if (j < num_slices) {
+            slice_runs[j] = s_cnt[threadIdx.x];
+            slice_first[j] = s_first[threadIdx.x];
+        }
     }
 }
 
@@ -380,7 +399,8 @@ __global__ __launch_bounds__(kScanBlock) void slice_scan_kernel(const uint32_t* 
 #pragma unroll
         for (int k = 0; k < kScanPer; ++k) {
             const uint32_t i = base + (uint32_t)(k * kScanBlock + tid);
-            s_val[scan_pad(k * kScanBlock + tid)] = i < num_slices ? slice_runs[i] : 0u;
+            const uint32_t raw = slice_runs[min(i, num_slices - 1)];
+            s_val[scan_pad(k * kScanBlock + tid)] = i < num_slices ? raw : 0u;
         }
         __syncthreads();
         uint32_t loc[kScanPer], sum = 0;
@@ -424,8 +444,8 @@ __global__ __launch_bounds__(kBlock) void uniq_rows_kernel(const uint32_t* __res
     for (uint32_t off = 0; off < kSliceSpan; off += kBlock) {
         const uint32_t t = off + threadIdx.x;
         const uint32_t i = blockIdx.x * kSliceSpan + t;
-        const uint32_t key = i < nv ? keys[i] : 0u;
-        const bool start = i < nv && (i == 0 || key != keys[i - 1]);
+        const uint32_t key = keys[min(i, n - 1)], kp = keys[i == 0 ? 0u : min(i - 1, n - 1)];
+        const bool start = i < nv && (i == 0 || key != kp);
         const uint64_t b = __ballot(start);
         if (lane == 0) s_mask[w] = b;
         __syncthreads();
@@ -542,7 +562,8 @@ template <int CPR_T, bool BF16, bool DENSE>
 __global__ __launch_bounds__(kBlock) void segment_reduce_kernel(
     const uint32_t* __restrict__ keys, const uint32_t* __restrict__ vals, uint32_t* __restrict__ counters,
     const u32x4* __restrict__ dy, uint32_t n, uint32_t num_rows, int cpr_rt, int dim, uint32_t num_slices,
-    const uint32_t* __restrict__ slice_base, float* __restrict__ grad_dense, float* __restrict__ uniq_grad,
+    const uint32_t* __restrict__ slice_base, const uint32_t* __restrict__ slice_first,
+    float* __restrict__ grad_dense, float* __restrict__ uniq_grad,
     double* __restrict__ carry_head, double* __restrict__ carry_tail, uint32_t* __restrict__ slice_flags) {
     constexpr int EPC = BF16 ? 8 : 4;
     constexpr int B = kReduceBatch;
@@ -558,13 +579,18 @@ __global__ __launch_bounds__(kBlock) void segment_reduce_kernel(
     if (blockIdx.x == 0 && threadIdx.x == 0) counters[1] = 0;  // long-run list of the fix-up that follows
     if (sub >= wpw || j >= num_slices) return;
     const uint32_t nv = min(counters[0], n);
-    const uint32_t s0 = (uint32_t)j * kSlice;
-    if (s0 >= nv) {
+    // Worker j covers [first run start in slice j, first run start in slice
+    // j+1): runs are cut only where a slice holds no run start at all (inside
+    // a run longer than a slice); there the cut falls on the slice edge.
+    const uint32_t f0 = slice_first[j];
+    const uint32_t f1 = j + 1 < num_slices ? slice_first[j + 1] : kNoStart;
+    const uint32_t s0 = min(f0 != kNoStart ? f0 : (uint32_t)j * kSlice, nv);
+    const uint32_t s1 = j + 1 < num_slices ? min(f1 != kNoStart ? f1 : (uint32_t)(j + 1) * kSlice, nv) : nv;
+    if (s0 >= s1) {
         if (c == 0) slice_flags[j] = 0;
         return;
     }
-    const uint32_t s1 = min(s0 + kSlice, nv);
-    bool head_open = s0 > 0 && keys[s0 - 1] == keys[s0];
+    bool head_open = f0 == kNoStart && s0 > 0 && keys[s0 - 1] == keys[s0];
     uint32_t u = slice_base[j];
     uint32_t flags = 0;
     double acc[EPC];
@@ -641,8 +667,9 @@ template <int CPR_T, bool BF16, bool DENSE>
 __global__ __launch_bounds__(kBlock) void carry_fixup_kernel(
     const uint32_t* __restrict__ keys, uint32_t* __restrict__ counters, uint32_t n, uint32_t num_rows,
     int cpr_rt, int dim, uint32_t num_slices, const uint32_t* __restrict__ slice_runs,
-    const uint32_t* __restrict__ slice_base, const uint32_t* __restrict__ slice_flags,
-    const double* __restrict__ carry_head, const double* __restrict__ carry_tail, uint32_t* __restrict__ long_runs,
+    const uint32_t* __restrict__ slice_base, const uint32_t* __restrict__ slice_first,
+    const uint32_t* __restrict__ slice_flags, const double* __restrict__ carry_head,
+    const double* __restrict__ carry_tail, uint32_t* __restrict__ long_runs,
     float* __restrict__ grad_dense, float* __restrict__ uniq_grad) {
     constexpr int EPC = BF16 ? 8 : 4;
     const int cpr = CPR_T ? CPR_T : cpr_rt;
@@ -659,18 +686,33 @@ __global__ __launch_bounds__(kBlock) void carry_fixup_kernel(
     uint32_t lo = (uint32_t)(j + 1) * kSlice - 1;
     if (lo + 1 >= nv) return;
     const uint32_t key = keys[lo];
-    uint32_t step = kSlice, hi = lo + step;
-    while (hi < nv && keys[hi] == key) {
-        lo = hi;
-        step = step < 0x40000000u ? 2 * step : step;
-        hi = lo + step < lo ? nv : lo + step;
+    int64_t m = j + 1;
+    if (slice_flags[j + 1] & kFlagWhole) {
+        // The run covers slice j+1 entirely.  Its last worker is the one just
+        // before the first later slice holding a run start (or the last slice
+        // with entries): scan slice_first, 4 * cpr slices per step.
+        const int wl0 = sub * cpr;
+        const int64_t last = (int64_t)(nv - 1) / kSlice;
+        int64_t kstar = last + 1;
+        for (int64_t b0 = j + 2; b0 <= last; b0 += 4 * cpr) {
+            int q_first = 4;
+#pragma unroll
+            for (int q = 3; q >= 0; --q) {
+                const int64_t idx = b0 + 4 * c + q;
+                const uint32_t f = slice_first[min(idx, last)];
+                if (idx <= last && f != kNoStart) q_first = q;
+            }
+            const uint64_t worker_lanes = cpr >= 64 ? ~0ull : ((1ull << cpr) - 1ull);
+            const uint64_t any = (__ballot(q_first < 4) >> wl0) & worker_lanes;
+            if (any) {
+                const int l = __ffsll((unsigned long long)any) - 1;
+                const int qf = __shfl(q_first, wl0 + l, 64);
+                kstar = b0 + 4 * l + qf;
+                break;
+            }
+        }
+        m = min(kstar - 1, (int64_t)num_slices - 1);
     }
-    hi = min(hi, nv);  // keys[lo] == key; hi == nv or keys[hi] != key
-    while (hi - lo > 1) {
-        const uint32_t mid = lo + (hi - lo) / 2;
-        if (keys[mid] == key) lo = mid; else hi = mid;
-    }
-    const int64_t m = min((int64_t)(lo / kSlice), (int64_t)num_slices - 1);
     if (m - j > kLongRun) {
         if (c == 0) {
             const uint32_t at = atomicAdd(&counters[1], 1u);
@@ -759,12 +801,14 @@ hipError_t launch_reduce(const Layout& L, const char* ws, const void* grad_out, 
     uint32_t* long_runs = (uint32_t*)(ws + L.long_runs);
     hipLaunchKernelGGL((segment_reduce_kernel<CPR_T, BF16, DENSE>), dim3((unsigned)grid), dim3(kBlock), 0, stream,
                        sorted_keys, sorted_vals, counters, (const u32x4*)grad_out, n, num_rows, cpr, dim, ns,
-                       (const uint32_t*)(ws + L.slice_base), grad_dense, uniq_grad, carry_head, carry_tail, flags);
+                       (const uint32_t*)(ws + L.slice_base), (const uint32_t*)(ws + L.slice_first), grad_dense,
+                       uniq_grad, carry_head, carry_tail, flags);
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
     hipLaunchKernelGGL((carry_fixup_kernel<CPR_T, BF16, DENSE>), dim3((unsigned)grid), dim3(kBlock), 0, stream,
                        sorted_keys, counters, n, num_rows, cpr, dim, ns, (const uint32_t*)(ws + L.slice_runs),
-                       (const uint32_t*)(ws + L.slice_base), (const uint32_t*)flags, (const double*)carry_head,
+                       (const uint32_t*)(ws + L.slice_base), (const uint32_t*)(ws + L.slice_first),
+                       (const uint32_t*)flags, (const double*)carry_head,
                        (const double*)carry_tail, long_runs, grad_dense, uniq_grad);
     if ((err = hipGetLastError()) != hipSuccess) return err;
     const size_t share_bytes = (size_t)wpw * (kBlock / 64) * dim * sizeof(double);
@@ -838,7 +882,7 @@ hipError_t launch_scatter_plan(const int64_t* rows, int64_t n, int64_t row_begin
     const uint32_t ns = (uint32_t)L.num_slices;
     const uint32_t span_blocks = (uint32_t)((n + kSliceSpan - 1) / kSliceSpan);
     hipLaunchKernelGGL(run_count_kernel, dim3(span_blocks), dim3(kBlock), 0, stream, k_cur, nn, counters,
-                       (uint32_t*)(ws + L.slice_runs), ns);
+                       (uint32_t*)(ws + L.slice_runs), (uint32_t*)(ws + L.slice_first), ns);
     hipLaunchKernelGGL(slice_scan_kernel, dim3(1), dim3(kScanBlock), 0, stream, (const uint32_t*)(ws + L.slice_runs),
                        ns, (uint32_t*)(ws + L.slice_base), num_uniq);
     if (uniq_rows)
