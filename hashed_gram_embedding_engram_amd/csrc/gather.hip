@@ -20,6 +20,10 @@
 // repeat (hot n-grams) from L2 and the Infinity Cache.
 #include "engram_internal.h"
 
+#ifndef ENGRAM_GATHER_NT_LOAD
+#define ENGRAM_GATHER_NT_LOAD 0
+#endif
+
 namespace engram {
 namespace {
 
@@ -72,7 +76,13 @@ __global__ __launch_bounds__(256) void gather_rows_kernel(const u32x4* __restric
     }
     u32x4 v[PER_LANE];
 #pragma unroll
-    for (int j = 0; j < PER_LANE; ++j) v[j] = *src[j];
+    for (int j = 0; j < PER_LANE; ++j) {
+#if ENGRAM_GATHER_NT_LOAD
+        v[j] = __builtin_nontemporal_load(src[j]);
+#else
+        v[j] = *src[j];
+#endif
+    }
     u32x4* dst = out + n0 * CPR + lane;
     if (rem == G) {  // every wave but the last: no per-store condition
 #pragma unroll

@@ -46,6 +46,9 @@ constexpr int kRadix = 256;
 #ifndef ENGRAM_REDUCE_NT
 #define ENGRAM_REDUCE_NT 1
 #endif
+#ifndef ENGRAM_REDUCE_NT_LOAD
+#define ENGRAM_REDUCE_NT_LOAD 0
+#endif
 #ifndef ENGRAM_REDUCE_BATCH
 #define ENGRAM_REDUCE_BATCH 16
 #endif
@@ -513,38 +516,69 @@ __device__ __forceinline__ void add_partial(double* acc, const double* src) {
     }
 }
 
-// Final write of one run's chunk: dense RMW (fp64 add, one rounding) or the
-// compact sum.  key < num_rows and u < n hold for every run of a correct plan;
-// the checks keep each store in bounds regardless.
+// Final write of one run: dense RMW (fp64 add, one rounding) or the compact
+// sum.  key < num_rows and u < n hold for every run of a correct plan; the
+// checks keep each store in bounds regardless.  Compact form with bf16
+// gradients: a lane holds 8 sums = fp32 output chunks 2c and 2c+1 (16 B
+// each); the worker's lanes exchange them so that store q writes chunks
+// [q*cpr, (q+1)*cpr), one contiguous span per store instruction (whole
+// cache lines, no half-written lines).  All lanes of the worker call this
+// together.
 template <int EPC, bool DENSE>
 __device__ __forceinline__ void write_run(const double* acc, uint32_t key, uint32_t u, int c, int dim, uint32_t n,
                                           uint32_t num_rows, float* grad_dense, float* uniq_grad) {
     typedef float f32x4 __attribute__((ext_vector_type(4)));
     if (DENSE ? key >= num_rows : u >= n) return;
-    if (DENSE) {
-        f32x4* g = (f32x4*)(grad_dense + (size_t)key * dim + c * EPC);
+    f32x4* g = (f32x4*)(DENSE ? grad_dense + (size_t)key * dim : uniq_grad + (size_t)u * dim);
+    f32x4 v[EPC / 4];
+    int chunk[EPC / 4];
+    if (EPC == 8 && !DENSE) {
+        const int cpr = dim / EPC;
+        const int wl0 = (int)(threadIdx.x & 63) - c;
+        float h[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) h[e] = (float)acc[e];
 #pragma unroll
         for (int q = 0; q < EPC / 4; ++q) {
-            f32x4 old = g[q], nw;
-            nw.x = (float)((double)old.x + acc[4 * q]);
-            nw.y = (float)((double)old.y + acc[4 * q + 1]);
-            nw.z = (float)((double)old.z + acc[4 * q + 2]);
-            nw.w = (float)((double)old.w + acc[4 * q + 3]);
-            g[q] = nw;
+            chunk[q] = q * cpr + c;
+            const int src = wl0 + chunk[q] / 2, half = chunk[q] & 1;
+            const float a0 = __shfl(h[0], src, 64), a1 = __shfl(h[1], src, 64), a2 = __shfl(h[2], src, 64),
+                        a3 = __shfl(h[3], src, 64), b0 = __shfl(h[4], src, 64), b1 = __shfl(h[5], src, 64),
+                        b2 = __shfl(h[6], src, 64), b3 = __shfl(h[7], src, 64);
+            v[q].x = half ? b0 : a0;
+            v[q].y = half ? b1 : a1;
+            v[q].z = half ? b2 : a2;
+            v[q].w = half ? b3 : a3;
         }
     } else {
-        f32x4* g = (f32x4*)(uniq_grad + (size_t)u * dim + c * EPC);
+        // Dense (a read-modify-write keeps the lines in L2, so lane order does
+        // not matter there) and fp32 gradients (4 sums = one chunk per lane).
 #pragma unroll
         for (int q = 0; q < EPC / 4; ++q) {
-            f32x4 v;
-            v.x = (float)acc[4 * q];
-            v.y = (float)acc[4 * q + 1];
-            v.z = (float)acc[4 * q + 2];
-            v.w = (float)acc[4 * q + 3];
+            chunk[q] = c * (EPC / 4) + q;
+            if (DENSE) {
+                const f32x4 old = g[chunk[q]];
+                v[q].x = (float)((double)old.x + acc[4 * q]);
+                v[q].y = (float)((double)old.y + acc[4 * q + 1]);
+                v[q].z = (float)((double)old.z + acc[4 * q + 2]);
+                v[q].w = (float)((double)old.w + acc[4 * q + 3]);
+            } else {
+                v[q].x = (float)acc[4 * q];
+                v[q].y = (float)acc[4 * q + 1];
+                v[q].z = (float)acc[4 * q + 2];
+                v[q].w = (float)acc[4 * q + 3];
+            }
+        }
+    }
+#pragma unroll
+    for (int q = 0; q < EPC / 4; ++q) {
+        if (DENSE) {
+            g[chunk[q]] = v[q];
+        } else {
 #if ENGRAM_REDUCE_NT
-            __builtin_nontemporal_store(v, g + q);
+            __builtin_nontemporal_store(v[q], g + chunk[q]);
 #else
-            g[q] = v;
+            g[chunk[q]] = v[q];
 #endif
         }
     }
@@ -616,7 +650,11 @@ __global__ __launch_bounds__(kBlock) void segment_reduce_kernel(
         for (int b = 0; b < B; ++b) {
             const uint32_t vb = __shfl(mv, wl0 + b, 64);
             const u32x4* src = (b < bb && i + b < s1 && vb < n) ? dy + ((size_t)vb * cpr + c) : &kZeroChunk;
+#if ENGRAM_REDUCE_NT_LOAD
+            x[b] = __builtin_nontemporal_load(src);
+#else
             x[b] = *src;
+#endif
         }
         if (i + bb < s1) {
             const uint32_t p = i + bb + (uint32_t)c;
