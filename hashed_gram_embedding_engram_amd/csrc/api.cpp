@@ -151,6 +151,80 @@ int engram_scatter_add(const int64_t* rows, int64_t n, const void* grad_out, int
                                                       workspace, stream));
 }
 
+size_t engram_route_workspace(int64_t n) { return n < 0 ? 0 : engram::route_workspace_bytes(n); }
+
+namespace {
+
+int route_geometry(int64_t num_embeddings, int32_t world, int64_t* local_rows) {
+    if (world < 1 || world > 255 || num_embeddings < 1 || num_embeddings % world != 0) return ENGRAM_EINVAL;
+    *local_rows = num_embeddings / world;
+    return ENGRAM_OK;
+}
+
+bool row_layout_ok(int64_t row_bytes) { return row_bytes > 0 && row_bytes % 4 == 0 && row_bytes <= (1 << 20); }
+
+}  // namespace
+
+int engram_route_plan(const int64_t* global_ids, int64_t n, int64_t num_embeddings, int32_t world,
+                      int64_t* sorted_ids, int64_t* order, int64_t* send_counts, void* workspace,
+                      size_t workspace_bytes, int64_t* status, hipStream_t stream) {
+    int64_t local_rows;
+    if (route_geometry(num_embeddings, world, &local_rows) != ENGRAM_OK) return ENGRAM_EINVAL;
+    if (n < 0 || n >= ((int64_t)1 << 31) || !send_counts) return ENGRAM_EINVAL;
+    if (n > 0 && (!global_ids || !sorted_ids || !order)) return ENGRAM_EINVAL;
+    if (((uintptr_t)workspace & 255) != 0 || !workspace || workspace_bytes < engram::route_workspace_bytes(n))
+        return ENGRAM_EWORKSPACE;
+    return launch_result(engram::launch_route_plan(global_ids, n, local_rows, world, sorted_ids, order, send_counts,
+                                                   workspace, status, stream));
+}
+
+int engram_route_validate(const int64_t* sorted_ids, int64_t n, const int64_t* send_counts, int32_t world,
+                          int64_t num_embeddings, int64_t* status, hipStream_t stream) {
+    int64_t local_rows;
+    if (route_geometry(num_embeddings, world, &local_rows) != ENGRAM_OK) return ENGRAM_EINVAL;
+    if (n < 0 || !send_counts || !status || (n > 0 && !sorted_ids)) return ENGRAM_EINVAL;
+    return launch_result(engram::launch_route_validate(sorted_ids, n, send_counts, world, local_rows, status, stream));
+}
+
+int engram_pack_fixed_capacity(const void* src, int64_t row_bytes, const int64_t* split_sizes, int32_t world,
+                               int64_t capacity, const void* fill, int32_t fill_bytes, void* dst, int64_t* status,
+                               hipStream_t stream) {
+    if (world < 1 || world > 255 || capacity < 0 || !row_layout_ok(row_bytes) || !split_sizes) return ENGRAM_EINVAL;
+    if (!(fill_bytes == 1 || fill_bytes == 2 || fill_bytes == 4 || fill_bytes == 8) || !fill) return ENGRAM_EINVAL;
+    if (row_bytes % fill_bytes != 0) return ENGRAM_EINVAL;
+    if (capacity > 0 && (!dst || !src)) return ENGRAM_EINVAL;
+    if ((int64_t)world * capacity > ((int64_t)1 << 40) / row_bytes) return ENGRAM_EINVAL;
+    uint32_t fill16[4];
+    unsigned char bytes[16];
+    for (int i = 0; i < 16; ++i) bytes[i] = ((const unsigned char*)fill)[i % fill_bytes];
+    for (int i = 0; i < 4; ++i)
+        fill16[i] = (uint32_t)bytes[4 * i] | ((uint32_t)bytes[4 * i + 1] << 8) | ((uint32_t)bytes[4 * i + 2] << 16) |
+                    ((uint32_t)bytes[4 * i + 3] << 24);
+    if (capacity == 0) return launch_result(engram::launch_status_init(status, stream));
+    return launch_result(engram::launch_pack(src, row_bytes, split_sizes, world, capacity, fill16, dst, status, stream));
+}
+
+int engram_unpack_fixed_capacity(const void* src, int64_t row_bytes, const int64_t* split_sizes, int32_t world,
+                                 int64_t capacity, void* dst, int64_t dst_rows, int64_t* status, hipStream_t stream) {
+    if (world < 1 || world > 255 || capacity < 0 || dst_rows < 0 || !row_layout_ok(row_bytes) || !split_sizes)
+        return ENGRAM_EINVAL;
+    if (capacity > 0 && dst_rows > 0 && (!dst || !src)) return ENGRAM_EINVAL;
+    return launch_result(engram::launch_unpack(src, row_bytes, split_sizes, world, capacity, dst, dst_rows, status,
+                                               stream));
+}
+
+int engram_permute_rows(const void* src, int64_t row_bytes, const int64_t* order, int64_t n, void* dst,
+                        hipStream_t stream) {
+    if (n < 0 || !row_layout_ok(row_bytes) || (n > 0 && (!src || !order || !dst))) return ENGRAM_EINVAL;
+    return launch_result(engram::launch_permute(src, row_bytes, order, n, dst, true, stream));
+}
+
+int engram_unpermute_rows(const void* src, int64_t row_bytes, const int64_t* order, int64_t n, void* dst,
+                          hipStream_t stream) {
+    if (n < 0 || !row_layout_ok(row_bytes) || (n > 0 && (!src || !order || !dst))) return ENGRAM_EINVAL;
+    return launch_result(engram::launch_permute(src, row_bytes, order, n, dst, false, stream));
+}
+
 const char* engram_strerror(int code) {
     switch (code) {
         case ENGRAM_OK: return "success";

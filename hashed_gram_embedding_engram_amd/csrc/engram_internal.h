@@ -47,6 +47,20 @@ hipError_t launch_scatter_plan(const int64_t* rows, int64_t n, int64_t row_begin
 hipError_t launch_scatter_apply(const void* grad_out, int elem_bytes, int dim, int64_t n, int64_t num_rows,
                                 float* grad_dense, float* uniq_grad, const void* workspace, hipStream_t stream);
 
+// Owner routing (route.hip).
+size_t route_workspace_bytes(int64_t n);
+hipError_t launch_route_plan(const int64_t* ids, int64_t n, int64_t local_rows, int world, int64_t* sorted_ids,
+                             int64_t* order, int64_t* send_counts, void* workspace, int64_t* status,
+                             hipStream_t stream);
+hipError_t launch_route_validate(const int64_t* sorted_ids, int64_t n, const int64_t* send_counts, int world,
+                                 int64_t local_rows, int64_t* status, hipStream_t stream);
+hipError_t launch_pack(const void* src, int64_t row_bytes, const int64_t* counts, int world, int64_t capacity,
+                       const uint32_t fill16[4], void* dst, int64_t* status, hipStream_t stream);
+hipError_t launch_unpack(const void* src, int64_t row_bytes, const int64_t* counts, int world, int64_t capacity,
+                         void* dst, int64_t dst_rows, int64_t* status, hipStream_t stream);
+hipError_t launch_permute(const void* src, int64_t row_bytes, const int64_t* order, int64_t n, void* dst, bool gather,
+                          hipStream_t stream);
+
 // Sets *status = -1 on the stream (a kernel, not a memset, so the call can be
 // captured in a graph).
 hipError_t launch_status_init(int64_t* status, hipStream_t stream);

@@ -270,3 +270,116 @@ def engram_scatter_add_apply(grad_out, n, num_rows, workspace, row_begin=0, grad
                                         workspace.numel() * workspace.element_size(), _stream_handle(stream)),
            "engram_scatter_add_apply")
     return grad_dense if grad_dense is not None else uniq_grad
+
+
+# ---------------------------------------------------------------- owner routing
+
+def _bind_route(lib):
+    if getattr(lib, "_route_bound", False):
+        return
+    p, i64, i32, sz = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_size_t
+    lib.engram_route_workspace.restype = sz
+    lib.engram_route_workspace.argtypes = [i64]
+    lib.engram_route_plan.restype = ctypes.c_int
+    lib.engram_route_plan.argtypes = [p, i64, i64, i32, p, p, p, p, sz, p, p]
+    lib.engram_route_validate.restype = ctypes.c_int
+    lib.engram_route_validate.argtypes = [p, i64, p, i32, i64, p, p]
+    lib.engram_pack_fixed_capacity.restype = ctypes.c_int
+    lib.engram_pack_fixed_capacity.argtypes = [p, i64, p, i32, i64, p, i32, p, p, p]
+    lib.engram_unpack_fixed_capacity.restype = ctypes.c_int
+    lib.engram_unpack_fixed_capacity.argtypes = [p, i64, p, i32, i64, p, i64, p, p]
+    lib.engram_permute_rows.restype = ctypes.c_int
+    lib.engram_permute_rows.argtypes = [p, i64, p, i64, p, p]
+    lib.engram_unpermute_rows.restype = ctypes.c_int
+    lib.engram_unpermute_rows.argtypes = [p, i64, p, i64, p, p]
+    lib._route_bound = True
+
+
+def _route_lib():
+    lib = load_library()
+    _bind_route(lib)
+    return lib
+
+
+def _row_bytes(t):
+    return (t.numel() // max(t.shape[0], 1)) * t.element_size() if t.dim() > 1 else t.element_size()
+
+
+def engram_route_plan(global_ids, num_embeddings, world, status=None, stream=None):
+    """Group global row IDs by owner.  Returns (sorted_ids [n], order [n], send_counts [world])."""
+    lib = _route_lib()
+    ids = global_ids.reshape(-1)
+    n = ids.numel()
+    dev = ids.device
+    sorted_ids = torch.empty(n, dtype=torch.int64, device=dev)
+    order = torch.empty(n, dtype=torch.int64, device=dev)
+    counts = torch.empty(world, dtype=torch.int64, device=dev)
+    ws = torch.empty(max(int(lib.engram_route_workspace(n)), 256), dtype=torch.uint8, device=dev)
+    _check(lib.engram_route_plan(_dev_ptr(ids, "global_ids", torch.int64), n, num_embeddings, world,
+                                 _dev_ptr(sorted_ids, "sorted_ids"), _dev_ptr(order, "order"),
+                                 _dev_ptr(counts, "send_counts"), _dev_ptr(ws, "workspace"), ws.numel(),
+                                 _dev_ptr(status, "status", torch.int64), _stream_handle(stream)), "engram_route_plan")
+    return sorted_ids, order, counts
+
+
+def engram_route_validate(sorted_ids, send_counts, num_embeddings, world, stream=None):
+    """Returns the device status word (lowest offending sorted index, n for bad counts, or -1)."""
+    lib = _route_lib()
+    status = torch.empty((), dtype=torch.int64, device=sorted_ids.device)
+    _check(lib.engram_route_validate(_dev_ptr(sorted_ids, "sorted_ids", torch.int64), sorted_ids.numel(),
+                                     _dev_ptr(send_counts, "send_counts", torch.int64), world, num_embeddings,
+                                     _dev_ptr(status, "status"), _stream_handle(stream)), "engram_route_validate")
+    return status
+
+
+def engram_pack_fixed_capacity(src, split_sizes, world, capacity, fill=0, status=None, stream=None):
+    """Compact rows [sum(split_sizes), ...] -> [world, capacity, ...] padded with ``fill``."""
+    lib = _route_lib()
+    row_shape = tuple(src.shape[1:])
+    esize = src.element_size()
+    row_bytes = esize * int(torch.Size(row_shape).numel()) if row_shape else esize
+    dst = torch.empty((world, capacity) + row_shape, dtype=src.dtype, device=src.device)
+    fill_t = torch.tensor([fill], dtype=src.dtype)
+    fill_bytes = (ctypes.c_ubyte * esize).from_buffer_copy(fill_t.view(torch.uint8).numpy().tobytes())
+    _check(lib.engram_pack_fixed_capacity(_dev_ptr(src, "src"), row_bytes,
+                                          _dev_ptr(split_sizes, "split_sizes", torch.int64), world, capacity,
+                                          ctypes.cast(fill_bytes, ctypes.c_void_p), esize, _dev_ptr(dst, "dst"),
+                                          _dev_ptr(status, "status", torch.int64), _stream_handle(stream)),
+           "engram_pack_fixed_capacity")
+    return dst
+
+
+def engram_unpack_fixed_capacity(src, split_sizes, dst_rows, status=None, stream=None):
+    """[world, capacity, ...] -> compact [dst_rows, ...] (rank order; rows past the counts untouched)."""
+    lib = _route_lib()
+    world, capacity = src.shape[0], src.shape[1]
+    row_shape = tuple(src.shape[2:])
+    esize = src.element_size()
+    row_bytes = esize * int(torch.Size(row_shape).numel()) if row_shape else esize
+    dst = torch.empty((dst_rows,) + row_shape, dtype=src.dtype, device=src.device)
+    _check(lib.engram_unpack_fixed_capacity(_dev_ptr(src, "src"), row_bytes,
+                                            _dev_ptr(split_sizes, "split_sizes", torch.int64), world, capacity,
+                                            _dev_ptr(dst, "dst"), dst_rows, _dev_ptr(status, "status", torch.int64),
+                                            _stream_handle(stream)), "engram_unpack_fixed_capacity")
+    return dst
+
+
+def _permute(src, order, gather, stream):
+    lib = _route_lib()
+    n = order.numel()
+    row_bytes = src[0].numel() * src.element_size() if src.dim() > 1 else src.element_size()
+    dst = torch.empty_like(src)
+    fn = lib.engram_permute_rows if gather else lib.engram_unpermute_rows
+    _check(fn(_dev_ptr(src, "src"), row_bytes, _dev_ptr(order, "order", torch.int64), n, _dev_ptr(dst, "dst"),
+              _stream_handle(stream)), "engram_permute_rows" if gather else "engram_unpermute_rows")
+    return dst
+
+
+def engram_permute_rows(src, order, stream=None):
+    """dst[i] = src[order[i]]."""
+    return _permute(src, order, True, stream)
+
+
+def engram_unpermute_rows(src, order, stream=None):
+    """dst[order[i]] = src[i]."""
+    return _permute(src, order, False, stream)

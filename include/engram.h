@@ -173,6 +173,61 @@ int engram_scatter_add_apply(const void* grad_out, int32_t dtype, int32_t dim, i
                              int64_t num_rows, float* grad_dense, float* uniq_grad, const void* workspace,
                              size_t workspace_bytes, hipStream_t stream);
 
+/* ---- Owner routing: the single-GPU half of the row-owner exchange ----------
+ * Engram API page, Qwen3_8_FlashNextOwnerShardedEmbedding: with `world` owners,
+ * rank r owns global rows [r * local_rows, (r + 1) * local_rows), local_rows =
+ * num_embeddings / world (num_embeddings must divide by world); a request rank
+ * groups its IDs by owner before the first All-to-All (_exchange_ids), checks
+ * the destination segments (_validate_sorted_send_ids), and exchanges segments
+ * padded to one agreed capacity (_fixed_capacity_all_to_all).  The collective
+ * itself is not part of this library.  1 <= world <= 255.  Rows handled by pack,
+ * unpack and permute are opaque: row_bytes is a multiple of 4, at most 1 MiB. */
+
+/* Bytes of device workspace engram_route_plan needs for n IDs. */
+size_t engram_route_workspace(int64_t n);
+
+/* Group IDs by owner, keeping request order inside each owner's segment.
+ *   global_ids   device int64 [n]
+ *   sorted_ids   device int64 [n]: segment of owner 0, then owner 1, ...; IDs
+ *                outside [0, num_embeddings) come last, after every segment
+ *   order        device int64 [n]: request position of each sorted entry
+ *   send_counts  device int64 [world]: segment lengths (out-of-range IDs excluded)
+ *   status       device int64 or NULL: lowest request index holding an ID
+ *                outside the table, else -1
+ * n < 2^31.  Returns ENGRAM_OK, ENGRAM_EINVAL or ENGRAM_EWORKSPACE. */
+int engram_route_plan(const int64_t* global_ids, int64_t n, int64_t num_embeddings, int32_t world,
+                      int64_t* sorted_ids, int64_t* order, int64_t* send_counts, void* workspace,
+                      size_t workspace_bytes, int64_t* status, hipStream_t stream);
+
+/* _validate_sorted_send_ids: every ID of segment w (send_counts, device int64
+ * [world]) lies in owner w's rows.  *status (device, required) = lowest sorted
+ * index that breaks this, n if a count is negative or the counts exceed n, else -1. */
+int engram_route_validate(const int64_t* sorted_ids, int64_t n, const int64_t* send_counts, int32_t world,
+                          int64_t num_embeddings, int64_t* status, hipStream_t stream);
+
+/* Send side of _fixed_capacity_all_to_all: compact rows src [sum(split_sizes)][row],
+ * segments ordered by rank -> dst [world][capacity][row], segment w in block w,
+ * the rest of each block filled with the element `fill` (host pointer to
+ * fill_bytes = 1, 2, 4 or 8 bytes, repeated over the row).  *status (device or
+ * NULL) = lowest rank whose split size is negative or above capacity (its rows
+ * are cut at capacity), else -1. */
+int engram_pack_fixed_capacity(const void* src, int64_t row_bytes, const int64_t* split_sizes, int32_t world,
+                               int64_t capacity, const void* fill, int32_t fill_bytes, void* dst, int64_t* status,
+                               hipStream_t stream);
+
+/* Receive side: src [world][capacity][row] -> compact dst [sum(split_sizes)][row] in
+ * rank order; dst has room for dst_rows rows.  *status = lowest rank whose split size
+ * is negative or above capacity, world if the compact rows exceed dst_rows, else -1. */
+int engram_unpack_fixed_capacity(const void* src, int64_t row_bytes, const int64_t* split_sizes, int32_t world,
+                                 int64_t capacity, void* dst, int64_t dst_rows, int64_t* status, hipStream_t stream);
+
+/* dst[i] = src[order[i]] (into grouped order) and dst[order[i]] = src[i] (back to
+ * request order), rows of row_bytes; an order entry outside [0, n) is skipped. */
+int engram_permute_rows(const void* src, int64_t row_bytes, const int64_t* order, int64_t n, void* dst,
+                        hipStream_t stream);
+int engram_unpermute_rows(const void* src, int64_t row_bytes, const int64_t* order, int64_t n, void* dst,
+                          hipStream_t stream);
+
 /* Static English text for an engram_status code. */
 const char* engram_strerror(int code);
 

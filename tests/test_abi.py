@@ -160,3 +160,32 @@ def test_plan_apply_reject_bad_arguments(lib):
     assert apply(dense=f) == B.ENGRAM_EINVAL          # both forms
     assert apply(ug=None) == B.ENGRAM_EINVAL          # neither form
     assert apply(w=ctypes.c_void_p(0x100008)) == B.ENGRAM_EWORKSPACE
+
+
+def test_route_entry_points_reject_bad_arguments(lib):
+    from hashed_gram_embedding_engram_amd import engram as EB
+    EB._bind_route(lib)
+    f = ctypes.c_void_p(0x1000)
+    ws = ctypes.c_void_p(0x100000)
+    need = lib.engram_route_workspace(1000)
+    plan = lambda E=8000, W=8, n=1000, w=ws, wb=need, ids=f: lib.engram_route_plan(
+        ids, n, E, W, f, f, f, w, wb, None, None)
+    assert plan(E=8001) == B.ENGRAM_EINVAL          # rows do not divide by the owner count
+    assert plan(W=0) == B.ENGRAM_EINVAL
+    assert plan(W=256, E=256000) == B.ENGRAM_EINVAL
+    assert plan(n=-1) == B.ENGRAM_EINVAL
+    assert plan(ids=None) == B.ENGRAM_EINVAL
+    assert plan(w=None) == B.ENGRAM_EWORKSPACE
+    assert plan(wb=need - 1) == B.ENGRAM_EWORKSPACE
+    assert lib.engram_route_validate(f, 10, f, 8, 8000, None, None) == B.ENGRAM_EINVAL   # status required
+    one = (ctypes.c_ubyte * 8)()
+    pack = lambda rb=320, cap=16, fb=2, W=8, fill=ctypes.cast(one, ctypes.c_void_p): lib.engram_pack_fixed_capacity(
+        f, rb, f, W, cap, fill, fb, f, None, None)
+    assert pack(rb=10) == B.ENGRAM_EINVAL            # rows are whole 4-byte words
+    assert pack(fb=3) == B.ENGRAM_EINVAL
+    assert pack(fb=8, rb=12) == B.ENGRAM_EINVAL       # the fill element must tile the row
+    assert pack(cap=-1) == B.ENGRAM_EINVAL
+    assert pack(fill=None) == B.ENGRAM_EINVAL
+    assert lib.engram_unpack_fixed_capacity(f, 320, f, 8, 16, f, -1, None, None) == B.ENGRAM_EINVAL
+    assert lib.engram_permute_rows(f, 6, f, 10, f, None) == B.ENGRAM_EINVAL
+    assert lib.engram_unpermute_rows(None, 8, f, 10, f, None) == B.ENGRAM_EINVAL
