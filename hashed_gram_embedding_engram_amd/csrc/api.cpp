@@ -225,6 +225,85 @@ int engram_unpermute_rows(const void* src, int64_t row_bytes, const int64_t* ord
     return launch_result(engram::launch_permute(src, row_bytes, order, n, dst, false, stream));
 }
 
+namespace {
+
+int ple_dims_ok(int32_t dtype, int64_t a, int64_t b, int64_t channels, int* eb) {
+    if (!dtype_ok(dtype)) return ENGRAM_EDTYPE;
+    *eb = dtype == ENGRAM_F32 ? 4 : 2;
+    if (a < 0 || b < 0 || channels <= 0 || (channels * *eb) % 16 != 0) return ENGRAM_EINVAL;
+    if (a > 0 && b > INT64_MAX / a / channels) return ENGRAM_EINVAL;
+    return ENGRAM_OK;
+}
+
+}  // namespace
+
+size_t engram_short_conv_workspace(int64_t batch, int64_t seq, int64_t channels, int32_t kernel) {
+    if (batch < 0 || seq < 0 || channels <= 0 || kernel < 1 || kernel > 4) return 0;
+    return engram::short_conv_workspace_bytes(batch, seq, channels, kernel);
+}
+
+int engram_short_conv(const void* x, int32_t dtype, int64_t batch, int64_t seq, int64_t channels,
+                      const float* weight, const float* bias, int32_t kernel, int32_t dilation, const void* halo,
+                      void* y, hipStream_t stream) {
+    int eb;
+    int rc = ple_dims_ok(dtype, batch, seq, channels, &eb);
+    if (rc != ENGRAM_OK) return rc;
+    if (kernel < 1 || kernel > 4 || dilation < 1 || !weight) return ENGRAM_EINVAL;
+    if (batch * seq > 0 && (!x || !y)) return ENGRAM_EINVAL;
+    return launch_result(engram::launch_short_conv(x, eb, batch, seq, channels, weight, bias, kernel, dilation, halo,
+                                                   y, stream));
+}
+
+int engram_short_conv_backward(const void* x, const void* dy, int32_t dtype, int64_t batch, int64_t seq,
+                               int64_t channels, const float* weight, int32_t kernel, int32_t dilation,
+                               const void* halo, void* dx, float* dweight, float* dbias, void* dhalo, void* workspace,
+                               size_t workspace_bytes, hipStream_t stream) {
+    int eb;
+    int rc = ple_dims_ok(dtype, batch, seq, channels, &eb);
+    if (rc != ENGRAM_OK) return rc;
+    if (kernel < 1 || kernel > 4 || dilation < 1 || !weight || !dweight) return ENGRAM_EINVAL;
+    if (batch * seq > 0 && (!x || !dy || !dx)) return ENGRAM_EINVAL;
+    if (((uintptr_t)workspace & 255) != 0) return ENGRAM_EWORKSPACE;
+    const size_t need = engram::short_conv_workspace_bytes(batch, seq, channels, kernel);
+    if (need > 0 && (!workspace || workspace_bytes < need)) return ENGRAM_EWORKSPACE;
+    return launch_result(engram::launch_short_conv_backward(x, dy, eb, batch, seq, channels, weight, kernel, dilation,
+                                                            halo, dx, dweight, dbias, dhalo, workspace, stream));
+}
+
+size_t engram_grouped_rms_norm_workspace(int64_t rows, int64_t hidden) {
+    if (rows < 0 || hidden <= 0) return 0;
+    return engram::rms_norm_workspace_bytes(rows, hidden);
+}
+
+int engram_grouped_rms_norm(const void* x, int32_t dtype, int64_t rows, int64_t hidden, int64_t group_size,
+                            const float* weight, float eps, void* y, hipStream_t stream) {
+    int eb;
+    int rc = ple_dims_ok(dtype, rows, 1, hidden, &eb);
+    if (rc != ENGRAM_OK) return rc;
+    if (group_size <= 0 || hidden % group_size != 0 || !engram::rms_norm_group_ok(eb, group_size) || !weight ||
+        !(eps >= 0.0f))
+        return ENGRAM_EINVAL;
+    if (rows > 0 && (!x || !y)) return ENGRAM_EINVAL;
+    return launch_result(engram::launch_rms_norm(x, eb, rows, hidden, group_size, weight, eps, y, stream));
+}
+
+int engram_grouped_rms_norm_backward(const void* x, const void* dy, int32_t dtype, int64_t rows, int64_t hidden,
+                                     int64_t group_size, const float* weight, float eps, void* dx, float* dweight,
+                                     void* workspace, size_t workspace_bytes, hipStream_t stream) {
+    int eb;
+    int rc = ple_dims_ok(dtype, rows, 1, hidden, &eb);
+    if (rc != ENGRAM_OK) return rc;
+    if (group_size <= 0 || hidden % group_size != 0 || !engram::rms_norm_group_ok(eb, group_size) || !weight ||
+        !dweight || !(eps >= 0.0f))
+        return ENGRAM_EINVAL;
+    if (rows > 0 && (!x || !dy || !dx)) return ENGRAM_EINVAL;
+    if (((uintptr_t)workspace & 255) != 0) return ENGRAM_EWORKSPACE;
+    const size_t need = engram::rms_norm_workspace_bytes(rows, hidden);
+    if (need > 0 && (!workspace || workspace_bytes < need)) return ENGRAM_EWORKSPACE;
+    return launch_result(engram::launch_rms_norm_backward(x, dy, eb, rows, hidden, group_size, weight, eps, dx,
+                                                          dweight, workspace, stream));
+}
+
 const char* engram_strerror(int code) {
     switch (code) {
         case ENGRAM_OK: return "success";

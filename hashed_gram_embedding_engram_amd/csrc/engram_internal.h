@@ -61,6 +61,21 @@ hipError_t launch_unpack(const void* src, int64_t row_bytes, const int64_t* coun
 hipError_t launch_permute(const void* src, int64_t row_bytes, const int64_t* order, int64_t n, void* dst, bool gather,
                           hipStream_t stream);
 
+// PLE short convolution and grouped RMSNorm (ple.hip).
+size_t short_conv_workspace_bytes(int64_t batch, int64_t seq, int64_t channels, int kernel);
+size_t rms_norm_workspace_bytes(int64_t rows, int64_t hidden);
+bool rms_norm_group_ok(int elem_bytes, int64_t group);
+hipError_t launch_short_conv(const void* x, int elem_bytes, int64_t B, int64_t S, int64_t C, const float* w,
+                             const float* bias, int K, int d, const void* halo, void* y, hipStream_t stream);
+hipError_t launch_short_conv_backward(const void* x, const void* dy, int elem_bytes, int64_t B, int64_t S, int64_t C,
+                                      const float* w, int K, int d, const void* halo, void* dx, float* dw, float* db,
+                                      void* dhalo, void* workspace, hipStream_t stream);
+hipError_t launch_rms_norm(const void* x, int elem_bytes, int64_t rows, int64_t hidden, int64_t group, const float* w,
+                           float eps, void* y, hipStream_t stream);
+hipError_t launch_rms_norm_backward(const void* x, const void* dy, int elem_bytes, int64_t rows, int64_t hidden,
+                                    int64_t group, const float* w, float eps, void* dx, float* dw, void* workspace,
+                                    hipStream_t stream);
+
 // Sets *status = -1 on the stream (a kernel, not a memset, so the call can be
 // captured in a graph).
 hipError_t launch_status_init(int64_t* status, hipStream_t stream);

@@ -1,0 +1,472 @@
+// PLE causal short convolution and grouped Gemma RMSNorm for gfx950.
+//
+// Engram API page ("nemo_automodel.components.models.qwen3_8_flash_next.engram"),
+// Qwen3_8_FlashNextPLELayer._causal_short_conv: causal depthwise convolution
+// over the sequence of [batch, sequence, channels], kernel width K (4) and
+// dilation d (ngram_size = 3), left zero history; under context parallelism a
+// shard receives the preceding (K - 1) * d = 9 tokens as a halo.  Tap k
+// multiplies the input (K - 1 - k) * d positions back.
+// Layers API page ("nemo_automodel.components.models.qwen3_8_flash_next.layers"),
+// Qwen3_8_FlashNextGroupedRMSNorm / _grouped_rms_norm_fp32: each group of
+// `group` features is scaled by 1 / sqrt(mean(x^2) + eps) and by (1 + weight),
+// in fp32.
+//
+// All of these are HBM-bound streams: one read of each input and one write of
+// each output per element.  Arithmetic is fp32 per element; the weight
+// gradients (sums over every batch row and position) are accumulated per tile
+// and then reduced over the tiles in a fixed order in fp64, so they are
+// deterministic.
+#include "engram_internal.h"
+
+namespace engram {
+namespace {
+
+constexpr int kPleBlock = 256;
+
+// 16-byte chunk of VEC elements: bf16 (VEC 8) or fp32 (VEC 4), as fp32 values.
+template <bool BF16>
+__device__ __forceinline__ void unpack16(u32x4 v, float* f) {
+    if (BF16) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            f[2 * q] = __uint_as_float(v[q] << 16);
+            f[2 * q + 1] = __uint_as_float(v[q] & 0xFFFF0000u);
+        }
+    } else {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) f[q] = __uint_as_float(v[q]);
+    }
+}
+
+// fp32 -> bf16, round to nearest even (NaN kept quiet).
+__device__ __forceinline__ uint32_t bf16_bits(float f) {
+    const uint32_t u = __float_as_uint(f);
+    if ((u & 0x7FFFFFFFu) > 0x7F800000u) return (u >> 16) | 0x40u;
+    return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+}
+
+template <bool BF16>
+__device__ __forceinline__ u32x4 pack16(const float* f) {
+    u32x4 v;
+    if (BF16) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) v[q] = bf16_bits(f[2 * q]) | (bf16_bits(f[2 * q + 1]) << 16);
+    } else {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) v[q] = __float_as_uint(f[q]);
+    }
+    return v;
+}
+
+__device__ u32x4 kPleZero = {0u, 0u, 0u, 0u};  // never written
+
+// ---------------------------------------------------------------- convolution
+
+// Input chunk at sequence position ts of batch row b: x when ts >= 0, the halo
+// when -H <= ts < 0 and a halo is given, else zero (left zero history).
+__device__ __forceinline__ const u32x4* conv_src(const u32x4* x, const u32x4* halo, int64_t b, int64_t S, int64_t H,
+                                                  int64_t chunks, int64_t ch, int64_t ts) {
+    if (ts >= 0) return x + ((b * S + ts) * chunks + ch);
+    if (halo && ts >= -H) return halo + ((b * H + H + ts) * chunks + ch);
+    return &kPleZero;
+}
+
+template <bool BF16, int K>
+__global__ __launch_bounds__(kPleBlock) void short_conv_fwd_kernel(const u32x4* __restrict__ x,
+                                                                   const u32x4* __restrict__ halo,
+                                                                   const float* __restrict__ w,
+                                                                   const float* __restrict__ bias, int64_t B,
+                                                                   int64_t S, int64_t C, int d, int tile,
+                                                                   u32x4* __restrict__ y) {
+    constexpr int VEC = BF16 ? 8 : 4;
+    const int64_t chunks = C / VEC, tiles = (S + tile - 1) / tile;
+    const int64_t idx = (int64_t)blockIdx.x * kPleBlock + threadIdx.x;
+    if (idx >= B * tiles * chunks) return;
+    const int64_t ch = idx % chunks, rest = idx / chunks, tt = rest % tiles, b = rest / tiles;
+    const int64_t H = (int64_t)(K - 1) * d;
+    float wv[VEC][K], bv[VEC];
+#pragma unroll
+    for (int e = 0; e < VEC; ++e) {
+#pragma unroll
+        for (int k = 0; k < K; ++k) wv[e][k] = w[(ch * VEC + e) * K + k];
+        bv[e] = bias ? bias[ch * VEC + e] : 0.0f;
+    }
+    const int64_t t1 = min(S, (tt + 1) * tile);
+    for (int64_t t = tt * tile; t < t1; ++t) {
+        u32x4 raw[K];
+#pragma unroll
+        for (int k = 0; k < K; ++k) raw[k] = *conv_src(x, halo, b, S, H, chunks, ch, t - (int64_t)(K - 1 - k) * d);
+        float acc[VEC];
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) acc[e] = bv[e];
+#pragma unroll
+        for (int k = 0; k < K; ++k) {
+            float f[VEC];
+            unpack16<BF16>(raw[k], f);
+#pragma unroll
+            for (int e = 0; e < VEC; ++e) acc[e] = fmaf(wv[e][k], f[e], acc[e]);
+        }
+        y[(b * S + t) * chunks + ch] = pack16<BF16>(acc);
+    }
+}
+
+// dx (and the halo's gradient for the first tile) plus per-tile fp64 partial
+// sums of dweight and dbias.  partial: [B * tiles][C][K + 1].
+template <bool BF16, int K>
+__global__ __launch_bounds__(kPleBlock) void short_conv_bwd_kernel(
+    const u32x4* __restrict__ x, const u32x4* __restrict__ dy, const u32x4* __restrict__ halo,
+    const float* __restrict__ w, int64_t B, int64_t S, int64_t C, int d, int tile, u32x4* __restrict__ dx,
+    u32x4* __restrict__ dhalo, double* __restrict__ partial) {
+    constexpr int VEC = BF16 ? 8 : 4;
+    const int64_t chunks = C / VEC, tiles = (S + tile - 1) / tile;
+    const int64_t idx = (int64_t)blockIdx.x * kPleBlock + threadIdx.x;
+    if (idx >= B * tiles * chunks) return;
+    const int64_t ch = idx % chunks, rest = idx / chunks, tt = rest % tiles, b = rest / tiles;
+    const int64_t H = (int64_t)(K - 1) * d;
+    float wv[VEC][K];
+#pragma unroll
+    for (int e = 0; e < VEC; ++e)
+#pragma unroll
+        for (int k = 0; k < K; ++k) wv[e][k] = w[(ch * VEC + e) * K + k];
+    float pw[VEC][K + 1];  // fp32 within a tile, fp64 across tiles
+#pragma unroll
+    for (int e = 0; e < VEC; ++e)
+#pragma unroll
+        for (int k = 0; k <= K; ++k) pw[e][k] = 0.0f;
+    // dy at positions past the end is zero: it reads the zero chunk
+    auto dy_src = [&](int64_t ts) -> const u32x4* {
+        return ts < S ? dy + ((b * S + ts) * chunks + ch) : &kPleZero;
+    };
+    const int64_t t0 = tt * tile, t1 = min(S, t0 + tile);
+    for (int64_t t = t0; t < t1; ++t) {
+        u32x4 g[K], xs[K];
+#pragma unroll
+        for (int k = 0; k < K; ++k) {
+            g[k] = *dy_src(t + (int64_t)(K - 1 - k) * d);
+            xs[k] = *conv_src(x, halo, b, S, H, chunks, ch, t - (int64_t)(K - 1 - k) * d);
+        }
+        float acc[VEC], gt[VEC];
+        unpack16<BF16>(g[K - 1], gt);  // dy at t itself
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) acc[e] = 0.0f;
+#pragma unroll
+        for (int k = 0; k < K; ++k) {
+            float f[VEC], xf[VEC];
+            unpack16<BF16>(g[k], f);
+            unpack16<BF16>(xs[k], xf);
+#pragma unroll
+            for (int e = 0; e < VEC; ++e) {
+                acc[e] = fmaf(wv[e][k], f[e], acc[e]);
+                pw[e][k] = fmaf(gt[e], xf[e], pw[e][k]);
+            }
+        }
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) pw[e][K] += gt[e];
+        dx[(b * S + t) * chunks + ch] = pack16<BF16>(acc);
+    }
+    if (dhalo && tt == 0) {
+        for (int64_t j = 0; j < H; ++j) {  // halo position j is sequence position j - H
+            float acc[VEC];
+#pragma unroll
+            for (int e = 0; e < VEC; ++e) acc[e] = 0.0f;
+#pragma unroll
+            for (int k = 0; k < K; ++k) {
+                const int64_t ts = j - H + (int64_t)(K - 1 - k) * d;
+                float f[VEC];
+                unpack16<BF16>(ts >= 0 ? *dy_src(ts) : kPleZero, f);
+#pragma unroll
+                for (int e = 0; e < VEC; ++e) acc[e] = fmaf(wv[e][k], f[e], acc[e]);
+            }
+            dhalo[(b * H + j) * chunks + ch] = pack16<BF16>(acc);
+        }
+    }
+    double* p = partial + ((b * tiles + tt) * C + ch * VEC) * (K + 1);
+#pragma unroll
+    for (int e = 0; e < VEC; ++e)
+#pragma unroll
+        for (int k = 0; k <= K; ++k) p[e * (K + 1) + k] = (double)pw[e][k];
+}
+
+// Sum the per-tile partials in tile order: dweight [C][K], dbias [C].
+__global__ __launch_bounds__(kPleBlock) void conv_grad_reduce_kernel(const double* __restrict__ partial,
+                                                                     int64_t parts, int64_t C, int K,
+                                                                     float* __restrict__ dw,
+                                                                     float* __restrict__ db) {
+    const int64_t i = (int64_t)blockIdx.x * kPleBlock + threadIdx.x;  // over C * (K + 1)
+    if (i >= C * (K + 1)) return;
+    double s = 0.0;
+    for (int64_t p = 0; p < parts; ++p) s += partial[p * C * (K + 1) + i];
+    const int64_t c = i / (K + 1), k = i % (K + 1);
+    if (k < K)
+        dw[c * K + k] = (float)s;
+    else if (db)
+        db[c] = (float)s;
+}
+
+// ---------------------------------------------------------------- grouped RMSNorm
+
+constexpr int kNormMaxChunks = 10;  // 16-byte chunks per lane: group * elem_bytes <= 10240
+
+// One wave per (row, group); lanes own chunks lane, lane + 64, ...; CH is the
+// number of chunks per lane, ceil(group / VEC / 64).
+template <bool BF16, int CH>
+__global__ __launch_bounds__(kPleBlock) void rms_norm_fwd_kernel(const u32x4* __restrict__ x,
+                                                                 const float* __restrict__ w, int64_t rows,
+                                                                 int64_t hidden, int64_t group, float eps,
+                                                                 u32x4* __restrict__ y) {
+    constexpr int VEC = BF16 ? 8 : 4;
+    const int lane = threadIdx.x & 63;
+    const int64_t groups = hidden / group, gchunks = group / VEC, hchunks = hidden / VEC;
+    const int64_t wave = (int64_t)blockIdx.x * (kPleBlock / 64) + (threadIdx.x >> 6);
+    if (wave >= rows * groups) return;
+    const int64_t r = wave / groups, g = wave - r * groups;
+    const u32x4* xr = x + r * hchunks + g * gchunks;
+    u32x4 v[CH];
+    float ss = 0.0f;
+#pragma unroll
+    for (int q = 0; q < CH; ++q) {
+        const int64_t c = lane + 64 * q;
+        v[q] = *(c < gchunks ? xr + c : &kPleZero);  // unconditional load
+        float f[VEC];
+        unpack16<BF16>(v[q], f);
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) ss = fmaf(f[e], f[e], ss);
+    }
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) ss += __shfl_xor(ss, o, 64);
+    const float inv = 1.0f / sqrtf(ss / (float)group + eps);
+#pragma unroll
+    for (int q = 0; q < CH; ++q) {
+        const int64_t c = lane + 64 * q;
+        if (c >= gchunks) break;
+        float f[VEC];
+        unpack16<BF16>(v[q], f);
+        const float* wg = w + g * group + c * VEC;
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) f[e] = f[e] * inv * (1.0f + wg[e]);
+        y[r * hchunks + g * gchunks + c] = pack16<BF16>(f);
+    }
+}
+
+// dx per row, and fp32 partial sums of dweight over rows_per_block rows per
+// wave: partial [row_blocks][hidden] in fp64.
+template <bool BF16, int CH>
+__global__ __launch_bounds__(kPleBlock) void rms_norm_bwd_kernel(const u32x4* __restrict__ x,
+                                                                 const u32x4* __restrict__ dy,
+                                                                 const float* __restrict__ w, int64_t rows,
+                                                                 int64_t hidden, int64_t group, float eps,
+                                                                 int rows_per_block, u32x4* __restrict__ dx,
+                                                                 double* __restrict__ partial) {
+    constexpr int VEC = BF16 ? 8 : 4;
+    const int lane = threadIdx.x & 63;
+    const int64_t groups = hidden / group, gchunks = group / VEC, hchunks = hidden / VEC;
+    const int64_t blocks = (rows + rows_per_block - 1) / rows_per_block;
+    const int64_t wave = (int64_t)blockIdx.x * (kPleBlock / 64) + (threadIdx.x >> 6);
+    if (wave >= blocks * groups) return;
+    const int64_t rb = wave / groups, g = wave - rb * groups;
+    float pw[CH][VEC];
+#pragma unroll
+    for (int q = 0; q < CH; ++q)
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) pw[q][e] = 0.0f;
+    float wp[CH][VEC];  // 1 + weight of this lane's features
+#pragma unroll
+    for (int q = 0; q < CH; ++q) {
+        const int64_t c = lane + 64 * q;
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) wp[q][e] = c < gchunks ? 1.0f + w[g * group + c * VEC + e] : 0.0f;
+    }
+    const int64_t r1 = min(rows, (rb + 1) * rows_per_block);
+    for (int64_t r = rb * rows_per_block; r < r1; ++r) {
+        const int64_t base = r * hchunks + g * gchunks;
+        u32x4 xv[CH], gv[CH];
+#pragma unroll
+        for (int q = 0; q < CH; ++q) {
+            const int64_t c = lane + 64 * q;
+            xv[q] = *(c < gchunks ? x + base + c : &kPleZero);
+            gv[q] = *(c < gchunks ? dy + base + c : &kPleZero);
+        }
+        float ss = 0.0f, sdx = 0.0f;  // sum x^2, sum (dy * (1 + w)) * x
+#pragma unroll
+        for (int q = 0; q < CH; ++q) {
+            float xf[VEC], gf[VEC];
+            unpack16<BF16>(xv[q], xf);
+            unpack16<BF16>(gv[q], gf);
+#pragma unroll
+            for (int e = 0; e < VEC; ++e) {
+                ss = fmaf(xf[e], xf[e], ss);
+                sdx = fmaf(gf[e] * wp[q][e], xf[e], sdx);
+            }
+        }
+#pragma unroll
+        for (int o = 32; o > 0; o >>= 1) {
+            ss += __shfl_xor(ss, o, 64);
+            sdx += __shfl_xor(sdx, o, 64);
+        }
+        const float inv = 1.0f / sqrtf(ss / (float)group + eps);
+        const float coef = inv * inv * inv * sdx / (float)group;
+#pragma unroll
+        for (int q = 0; q < CH; ++q) {
+            const int64_t c = lane + 64 * q;
+            if (c >= gchunks) break;
+            float xf[VEC], gf[VEC], out[VEC];
+            unpack16<BF16>(xv[q], xf);
+            unpack16<BF16>(gv[q], gf);
+#pragma unroll
+            for (int e = 0; e < VEC; ++e) {
+                out[e] = inv * gf[e] * wp[q][e] - coef * xf[e];
+                pw[q][e] = fmaf(gf[e], xf[e] * inv, pw[q][e]);
+            }
+            dx[base + c] = pack16<BF16>(out);
+        }
+    }
+#pragma unroll
+    for (int q = 0; q < CH; ++q) {
+        const int64_t c = lane + 64 * q;
+        if (c >= gchunks) break;
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) partial[rb * hidden + g * group + c * VEC + e] = (double)pw[q][e];
+    }
+}
+
+__global__ __launch_bounds__(kPleBlock) void norm_grad_reduce_kernel(const double* __restrict__ partial,
+                                                                     int64_t parts, int64_t hidden,
+                                                                     float* __restrict__ dw) {
+    const int64_t h = (int64_t)blockIdx.x * kPleBlock + threadIdx.x;
+    if (h >= hidden) return;
+    double s = 0.0;
+    for (int64_t p = 0; p < parts; ++p) s += partial[p * hidden + h];
+    dw[h] = (float)s;
+}
+
+__global__ __launch_bounds__(kPleBlock) void ple_zero_kernel(u32x4* __restrict__ p, int64_t n) {
+    const int64_t i = (int64_t)blockIdx.x * kPleBlock + threadIdx.x;
+    if (i < n) p[i] = u32x4{0u, 0u, 0u, 0u};
+}
+
+constexpr int kConvTileFwd = 16;
+constexpr int kConvTileBwd = 64;
+constexpr int kNormRowsPerBlock = 32;
+
+unsigned blocks_for(int64_t threads) { return (unsigned)((threads + kPleBlock - 1) / kPleBlock); }
+
+}  // namespace
+
+size_t short_conv_workspace_bytes(int64_t batch, int64_t seq, int64_t channels, int kernel) {
+    const int64_t tiles = (seq + kConvTileBwd - 1) / kConvTileBwd;
+    return (size_t)batch * (size_t)tiles * (size_t)channels * (size_t)(kernel + 1) * sizeof(double);
+}
+
+size_t rms_norm_workspace_bytes(int64_t rows, int64_t hidden) {
+    return (size_t)((rows + kNormRowsPerBlock - 1) / kNormRowsPerBlock) * (size_t)hidden * sizeof(double);
+}
+
+bool rms_norm_group_ok(int elem_bytes, int64_t group) {
+    const int vec = 16 / elem_bytes;
+    return group % vec == 0 && group / vec <= 64 * kNormMaxChunks;
+}
+
+#define ENGRAM_CONV_DISPATCH(KERNEL, ...)                                                              \
+    switch (K * 4 + elem_bytes) {                                                                     \
+        case 1 * 4 + 2: hipLaunchKernelGGL((KERNEL<true, 1>), grid, block, 0, stream, __VA_ARGS__); break;  \
+        case 2 * 4 + 2: hipLaunchKernelGGL((KERNEL<true, 2>), grid, block, 0, stream, __VA_ARGS__); break;  \
+        case 3 * 4 + 2: hipLaunchKernelGGL((KERNEL<true, 3>), grid, block, 0, stream, __VA_ARGS__); break;  \
+        case 4 * 4 + 2: hipLaunchKernelGGL((KERNEL<true, 4>), grid, block, 0, stream, __VA_ARGS__); break;  \
+        case 1 * 4 + 4: hipLaunchKernelGGL((KERNEL<false, 1>), grid, block, 0, stream, __VA_ARGS__); break; \
+        case 2 * 4 + 4: hipLaunchKernelGGL((KERNEL<false, 2>), grid, block, 0, stream, __VA_ARGS__); break; \
+        case 3 * 4 + 4: hipLaunchKernelGGL((KERNEL<false, 3>), grid, block, 0, stream, __VA_ARGS__); break; \
+        default: hipLaunchKernelGGL((KERNEL<false, 4>), grid, block, 0, stream, __VA_ARGS__); break;        \
+    }
+
+hipError_t launch_short_conv(const void* x, int elem_bytes, int64_t B, int64_t S, int64_t C, const float* w,
+                             const float* bias, int K, int d, const void* halo, void* y, hipStream_t stream) {
+    if (B * S == 0) return hipSuccess;
+    const int vec = 16 / elem_bytes;
+    const int64_t threads = B * ((S + kConvTileFwd - 1) / kConvTileFwd) * (C / vec);
+    const dim3 grid(blocks_for(threads)), block(kPleBlock);
+    ENGRAM_CONV_DISPATCH(short_conv_fwd_kernel, (const u32x4*)x, (const u32x4*)halo, w, bias, B, S, C, d,
+                         kConvTileFwd, (u32x4*)y)
+    return hipGetLastError();
+}
+
+hipError_t launch_short_conv_backward(const void* x, const void* dy, int elem_bytes, int64_t B, int64_t S, int64_t C,
+                                      const float* w, int K, int d, const void* halo, void* dx, float* dw, float* db,
+                                      void* dhalo, void* workspace, hipStream_t stream) {
+    const int vec = 16 / elem_bytes;
+    const int64_t tiles = (S + kConvTileBwd - 1) / kConvTileBwd;
+    const int64_t threads = B * tiles * (C / vec);
+    double* partial = (double*)workspace;
+    if (threads > 0) {
+        const dim3 grid(blocks_for(threads)), block(kPleBlock);
+        ENGRAM_CONV_DISPATCH(short_conv_bwd_kernel, (const u32x4*)x, (const u32x4*)dy, (const u32x4*)halo, w, B, S,
+                             C, d, kConvTileBwd, (u32x4*)dx, (u32x4*)dhalo, partial)
+        hipError_t err = hipGetLastError();
+        if (err != hipSuccess) return err;
+    } else if (dhalo && B > 0) {  // no positions: the halo's gradient is zero
+        const int64_t n = B * (int64_t)(K - 1) * d * (C / vec);
+        hipLaunchKernelGGL(ple_zero_kernel, dim3(blocks_for(n)), dim3(kPleBlock), 0, stream, (u32x4*)dhalo, n);
+        hipError_t err = hipGetLastError();
+        if (err != hipSuccess) return err;
+    }
+    hipLaunchKernelGGL(conv_grad_reduce_kernel, dim3(blocks_for(C * (K + 1))), dim3(kPleBlock), 0, stream,
+                       (const double*)partial, B * tiles, C, K, dw, db);
+    return hipGetLastError();
+}
+
+#define ENGRAM_NORM_CASE(KERNEL, BF, CHN, ...) \
+    case CHN: hipLaunchKernelGGL((KERNEL<BF, CHN>), grid, block, 0, stream, __VA_ARGS__); break;
+#define ENGRAM_NORM_DISPATCH(KERNEL, ...)                                                               \
+    if (elem_bytes == 2) {                                                                             \
+        switch (ch) {                                                                                  \
+            ENGRAM_NORM_CASE(KERNEL, true, 1, __VA_ARGS__) ENGRAM_NORM_CASE(KERNEL, true, 2, __VA_ARGS__)   \
+            ENGRAM_NORM_CASE(KERNEL, true, 3, __VA_ARGS__) ENGRAM_NORM_CASE(KERNEL, true, 4, __VA_ARGS__)   \
+            ENGRAM_NORM_CASE(KERNEL, true, 5, __VA_ARGS__) ENGRAM_NORM_CASE(KERNEL, true, 6, __VA_ARGS__)   \
+            ENGRAM_NORM_CASE(KERNEL, true, 7, __VA_ARGS__) ENGRAM_NORM_CASE(KERNEL, true, 8, __VA_ARGS__)   \
+            ENGRAM_NORM_CASE(KERNEL, true, 9, __VA_ARGS__) default: ENGRAM_NORM_CASE(KERNEL, true, 10, __VA_ARGS__) \
+        }                                                                                              \
+    } else {                                                                                           \
+        switch (ch) {                                                                                  \
+            ENGRAM_NORM_CASE(KERNEL, false, 1, __VA_ARGS__) ENGRAM_NORM_CASE(KERNEL, false, 2, __VA_ARGS__) \
+            ENGRAM_NORM_CASE(KERNEL, false, 3, __VA_ARGS__) ENGRAM_NORM_CASE(KERNEL, false, 4, __VA_ARGS__) \
+            ENGRAM_NORM_CASE(KERNEL, false, 5, __VA_ARGS__) ENGRAM_NORM_CASE(KERNEL, false, 6, __VA_ARGS__) \
+            ENGRAM_NORM_CASE(KERNEL, false, 7, __VA_ARGS__) ENGRAM_NORM_CASE(KERNEL, false, 8, __VA_ARGS__)   \
+            ENGRAM_NORM_CASE(KERNEL, false, 9, __VA_ARGS__) default: ENGRAM_NORM_CASE(KERNEL, false, 10, __VA_ARGS__) \
+        }                                                                                              \
+    }
+
+// Chunks per lane for a group: ceil(group / VEC / 64), at most kNormMaxChunks.
+int norm_chunks_per_lane(int elem_bytes, int64_t group) {
+    const int64_t gchunks = group / (16 / elem_bytes);
+    return (int)((gchunks + 63) / 64);
+}
+
+hipError_t launch_rms_norm(const void* x, int elem_bytes, int64_t rows, int64_t hidden, int64_t group, const float* w,
+                           float eps, void* y, hipStream_t stream) {
+    if (rows == 0) return hipSuccess;
+    const int ch = norm_chunks_per_lane(elem_bytes, group);
+    const int64_t waves = rows * (hidden / group);
+    const dim3 grid(blocks_for(waves * 64)), block(kPleBlock);
+    ENGRAM_NORM_DISPATCH(rms_norm_fwd_kernel, (const u32x4*)x, w, rows, hidden, group, eps, (u32x4*)y)
+    return hipGetLastError();
+}
+
+hipError_t launch_rms_norm_backward(const void* x, const void* dy, int elem_bytes, int64_t rows, int64_t hidden,
+                                    int64_t group, const float* w, float eps, void* dx, float* dw, void* workspace,
+                                    hipStream_t stream) {
+    const int64_t blocks = (rows + kNormRowsPerBlock - 1) / kNormRowsPerBlock;
+    double* partial = (double*)workspace;
+    if (rows > 0) {
+        const int ch = norm_chunks_per_lane(elem_bytes, group);
+        const int64_t waves = blocks * (hidden / group);
+        const dim3 grid(blocks_for(waves * 64)), block(kPleBlock);
+        ENGRAM_NORM_DISPATCH(rms_norm_bwd_kernel, (const u32x4*)x, (const u32x4*)dy, w, rows, hidden, group, eps,
+                             kNormRowsPerBlock, (u32x4*)dx, partial)
+        hipError_t err = hipGetLastError();
+        if (err != hipSuccess) return err;
+    }
+    hipLaunchKernelGGL(norm_grad_reduce_kernel, dim3(blocks_for(hidden)), dim3(kPleBlock), 0, stream,
+                       (const double*)partial, blocks, hidden, dw);
+    return hipGetLastError();
+}
+
+}  // namespace engram

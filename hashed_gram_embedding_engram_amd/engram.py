@@ -383,3 +383,98 @@ def engram_permute_rows(src, order, stream=None):
 def engram_unpermute_rows(src, order, stream=None):
     """dst[order[i]] = src[i]."""
     return _permute(src, order, False, stream)
+
+
+# ---- PLE short convolution and grouped RMSNorm --------------------------------
+
+def _bind_ple(lib):
+    if getattr(lib, "_ple_bound", False):
+        return
+    p, i64, i32, sz, f32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_size_t, ctypes.c_float
+    lib.engram_short_conv_workspace.restype = sz
+    lib.engram_short_conv_workspace.argtypes = [i64, i64, i64, i32]
+    lib.engram_short_conv.restype = ctypes.c_int
+    lib.engram_short_conv.argtypes = [p, i32, i64, i64, i64, p, p, i32, i32, p, p, p]
+    lib.engram_short_conv_backward.restype = ctypes.c_int
+    lib.engram_short_conv_backward.argtypes = [p, p, i32, i64, i64, i64, p, i32, i32, p, p, p, p, p, p, sz, p]
+    lib.engram_grouped_rms_norm_workspace.restype = sz
+    lib.engram_grouped_rms_norm_workspace.argtypes = [i64, i64]
+    lib.engram_grouped_rms_norm.restype = ctypes.c_int
+    lib.engram_grouped_rms_norm.argtypes = [p, i32, i64, i64, i64, p, f32, p, p]
+    lib.engram_grouped_rms_norm_backward.restype = ctypes.c_int
+    lib.engram_grouped_rms_norm_backward.argtypes = [p, p, i32, i64, i64, i64, p, f32, p, p, p, sz, p]
+    lib._ple_bound = True
+
+
+def _ple_lib():
+    lib = load_library()
+    _bind_ple(lib)
+    return lib
+
+
+def _workspace(nbytes, device):
+    return torch.empty(max(int(nbytes), 256), dtype=torch.uint8, device=device)
+
+
+def engram_short_conv(x, weight, bias=None, dilation=3, halo=None, out=None, stream=None):
+    """Causal depthwise convolution of x [batch, seq, channels]; weight fp32 [channels, K]."""
+    lib = _ple_lib()
+    B, S, C = x.shape
+    K = weight.shape[1]
+    y = torch.empty_like(x) if out is None else out
+    _check(lib.engram_short_conv(_dev_ptr(x, "x"), _dtype_code(x), B, S, C,
+                                 _dev_ptr(weight, "weight", torch.float32), _dev_ptr(bias, "bias", torch.float32),
+                                 K, dilation, _dev_ptr(halo, "halo", x.dtype), _dev_ptr(y, "y", x.dtype),
+                                 _stream_handle(stream)), "engram_short_conv")
+    return y
+
+
+def engram_short_conv_backward(x, dy, weight, dilation=3, halo=None, want_bias=True, want_halo=False,
+                               workspace=None, stream=None):
+    """Returns (dx, dweight, dbias or None, dhalo or None)."""
+    lib = _ple_lib()
+    B, S, C = x.shape
+    K = weight.shape[1]
+    dev = x.device
+    dx = torch.empty_like(x)
+    dw = torch.empty((C, K), dtype=torch.float32, device=dev)
+    db = torch.empty(C, dtype=torch.float32, device=dev) if want_bias else None
+    dhalo = torch.empty((B, (K - 1) * dilation, C), dtype=x.dtype, device=dev) if want_halo else None
+    if workspace is None:
+        workspace = _workspace(lib.engram_short_conv_workspace(B, S, C, K), dev)
+    _check(lib.engram_short_conv_backward(_dev_ptr(x, "x"), _dev_ptr(dy, "dy", x.dtype), _dtype_code(x), B, S, C,
+                                          _dev_ptr(weight, "weight", torch.float32), K, dilation,
+                                          _dev_ptr(halo, "halo", x.dtype), _dev_ptr(dx, "dx"), _dev_ptr(dw, "dw"),
+                                          _dev_ptr(db, "db"), _dev_ptr(dhalo, "dhalo"),
+                                          _dev_ptr(workspace, "workspace"), workspace.numel(),
+                                          _stream_handle(stream)), "engram_short_conv_backward")
+    return dx, dw, db, dhalo
+
+
+def engram_grouped_rms_norm(x, weight, group_size, eps=1e-6, out=None, stream=None):
+    """Grouped Gemma RMSNorm over the last dim of x; weight fp32 [hidden]."""
+    lib = _ple_lib()
+    hidden = x.shape[-1]
+    rows = x.numel() // hidden if hidden else 0
+    y = torch.empty_like(x) if out is None else out
+    _check(lib.engram_grouped_rms_norm(_dev_ptr(x, "x"), _dtype_code(x), rows, hidden, group_size,
+                                       _dev_ptr(weight, "weight", torch.float32), eps, _dev_ptr(y, "y", x.dtype),
+                                       _stream_handle(stream)), "engram_grouped_rms_norm")
+    return y
+
+
+def engram_grouped_rms_norm_backward(x, dy, weight, group_size, eps=1e-6, workspace=None, stream=None):
+    """Returns (dx, dweight)."""
+    lib = _ple_lib()
+    hidden = x.shape[-1]
+    rows = x.numel() // hidden if hidden else 0
+    dx = torch.empty_like(x)
+    dw = torch.empty(hidden, dtype=torch.float32, device=x.device)
+    if workspace is None:
+        workspace = _workspace(lib.engram_grouped_rms_norm_workspace(rows, hidden), x.device)
+    _check(lib.engram_grouped_rms_norm_backward(_dev_ptr(x, "x"), _dev_ptr(dy, "dy", x.dtype), _dtype_code(x), rows,
+                                                hidden, group_size, _dev_ptr(weight, "weight", torch.float32), eps,
+                                                _dev_ptr(dx, "dx"), _dev_ptr(dw, "dw"),
+                                                _dev_ptr(workspace, "workspace"), workspace.numel(),
+                                                _stream_handle(stream)), "engram_grouped_rms_norm_backward")
+    return dx, dw

@@ -228,6 +228,63 @@ int engram_permute_rows(const void* src, int64_t row_bytes, const int64_t* order
 int engram_unpermute_rows(const void* src, int64_t row_bytes, const int64_t* order, int64_t n, void* dst,
                           hipStream_t stream);
 
+/* ---- PLE: causal short convolution and grouped RMSNorm ----------------------
+ * Engram API page, Qwen3_8_FlashNextPLELayer (_causal_short_conv, init_weights):
+ * a causal depthwise convolution over the sequence of x [batch][seq][channels]
+ * with kernel width K = conv_kernel_size (4) and dilation d = ngram_size (3):
+ *     y[b][t][c] = bias[c] + sum_k weight[c][k] * x[b][t - (K - 1 - k) * d][c]
+ * (tap K - 1 is the current token); positions before 0 read the halo when one
+ * is given, else zero ("left zero history").  The halo [batch][(K-1)*d][channels]
+ * holds the (K-1)*d tokens that precede position 0 (9 for the released
+ * settings), as a context-parallel shard receives them.
+ * Layers API page, Qwen3_8_FlashNextGroupedRMSNorm and _grouped_rms_norm_fp32:
+ * each run of group_size features of a row is scaled by
+ * 1 / sqrt(mean(x^2) + eps) and then by (1 + weight[feature]), in fp32.
+ *
+ * Activations are ENGRAM_BF16 or ENGRAM_F32 (x, dy, y, dx, halo, dhalo all of
+ * that type); weights, biases and their gradients are fp32.  channels (conv)
+ * and group_size (norm) times the element size must be a multiple of 16 bytes;
+ * group_size * element size <= 10240 bytes (5120 bf16, 2560 fp32 features);
+ * hidden % group_size == 0.
+ * 1 <= K <= 4, d >= 1.  Gradients of weight and bias are sums over every batch
+ * row and position, reduced in a fixed order (deterministic), and overwrite
+ * dweight / dbias.  The backward calls need a device workspace (256-byte
+ * aligned) of the size returned by the *_workspace call; it holds fp64
+ * partial sums and is not read after the call completes.
+ * Returns ENGRAM_OK, ENGRAM_EINVAL, ENGRAM_EDTYPE, ENGRAM_EWORKSPACE or
+ * ENGRAM_ELAUNCH. */
+
+/* Bytes of workspace engram_short_conv_backward needs (0 for bad sizes). */
+size_t engram_short_conv_workspace(int64_t batch, int64_t seq, int64_t channels, int32_t kernel);
+
+/* y = conv(x) as above.  weight device fp32 [channels][K]; bias device fp32
+ * [channels] or NULL; halo device or NULL (zero history); y device, same
+ * shape and type as x, must not overlap x or halo. */
+int engram_short_conv(const void* x, int32_t dtype, int64_t batch, int64_t seq, int64_t channels,
+                      const float* weight, const float* bias, int32_t kernel, int32_t dilation, const void* halo,
+                      void* y, hipStream_t stream);
+
+/* Gradients of engram_short_conv given dy (same shape as x): dx (same shape),
+ * dweight [channels][K], dbias [channels] or NULL (not wanted), dhalo
+ * [batch][(K-1)*d][channels] or NULL (not wanted).  x and halo are those of
+ * the forward call (halo NULL = zero history). */
+int engram_short_conv_backward(const void* x, const void* dy, int32_t dtype, int64_t batch, int64_t seq,
+                               int64_t channels, const float* weight, int32_t kernel, int32_t dilation,
+                               const void* halo, void* dx, float* dweight, float* dbias, void* dhalo, void* workspace,
+                               size_t workspace_bytes, hipStream_t stream);
+
+/* Bytes of workspace engram_grouped_rms_norm_backward needs (0 for bad sizes). */
+size_t engram_grouped_rms_norm_workspace(int64_t rows, int64_t hidden);
+
+/* y = grouped RMSNorm of x [rows][hidden], weight device fp32 [hidden], eps >= 0. */
+int engram_grouped_rms_norm(const void* x, int32_t dtype, int64_t rows, int64_t hidden, int64_t group_size,
+                            const float* weight, float eps, void* y, hipStream_t stream);
+
+/* dx [rows][hidden] and dweight [hidden] of engram_grouped_rms_norm given dy. */
+int engram_grouped_rms_norm_backward(const void* x, const void* dy, int32_t dtype, int64_t rows, int64_t hidden,
+                                     int64_t group_size, const float* weight, float eps, void* dx, float* dweight,
+                                     void* workspace, size_t workspace_bytes, hipStream_t stream);
+
 /* Static English text for an engram_status code. */
 const char* engram_strerror(int code);
 

@@ -189,3 +189,48 @@ def test_route_entry_points_reject_bad_arguments(lib):
     assert lib.engram_unpack_fixed_capacity(f, 320, f, 8, 16, f, -1, None, None) == B.ENGRAM_EINVAL
     assert lib.engram_permute_rows(f, 6, f, 10, f, None) == B.ENGRAM_EINVAL
     assert lib.engram_unpermute_rows(None, 8, f, 10, f, None) == B.ENGRAM_EINVAL
+
+
+def test_ple_rejects_bad_arguments(lib):
+    B._bind_ple(lib)
+    fake = ctypes.c_void_p(0x1000)
+    bf, f32 = B.ENGRAM_BF16, B.ENGRAM_F32
+    conv = lib.engram_short_conv
+    # (x, dtype, batch, seq, channels, weight, bias, K, d, halo, y, stream)
+    assert conv(fake, 7, 1, 4, 16, fake, None, 4, 3, None, fake, None) == B.ENGRAM_EDTYPE
+    assert conv(fake, bf, 1, 4, 12, fake, None, 4, 3, None, fake, None) == B.ENGRAM_EINVAL   # 24 B rows
+    assert conv(fake, f32, 1, 4, 6, fake, None, 4, 3, None, fake, None) == B.ENGRAM_EINVAL
+    assert conv(fake, bf, 1, 4, 16, fake, None, 5, 3, None, fake, None) == B.ENGRAM_EINVAL   # K > 4
+    assert conv(fake, bf, 1, 4, 16, fake, None, 0, 3, None, fake, None) == B.ENGRAM_EINVAL
+    assert conv(fake, bf, 1, 4, 16, fake, None, 4, 0, None, fake, None) == B.ENGRAM_EINVAL   # dilation
+    assert conv(fake, bf, 1, 4, 16, None, None, 4, 3, None, fake, None) == B.ENGRAM_EINVAL   # weight
+    assert conv(None, bf, 1, 4, 16, fake, None, 4, 3, None, fake, None) == B.ENGRAM_EINVAL
+    assert conv(fake, bf, -1, 4, 16, fake, None, 4, 3, None, fake, None) == B.ENGRAM_EINVAL
+    assert conv(None, bf, 0, 4, 16, fake, None, 4, 3, None, None, None) == B.ENGRAM_OK      # empty: no-op
+    assert lib.engram_short_conv_workspace(2, 100, 16, 4) == 2 * 2 * 16 * 5 * 8
+    assert lib.engram_short_conv_workspace(2, 100, 16, 5) == 0
+    bwd = lib.engram_short_conv_backward
+    # (x, dy, dtype, B, S, C, w, K, d, halo, dx, dw, db, dhalo, ws, ws_bytes, stream)
+    assert bwd(fake, fake, bf, 1, 4, 16, fake, 4, 3, None, fake, fake, None, None, None, 0, None) == \
+        B.ENGRAM_EWORKSPACE
+    assert bwd(fake, fake, bf, 1, 4, 16, fake, 4, 3, None, fake, fake, None, None, ctypes.c_void_p(0x1010), 4096,
+               None) == B.ENGRAM_EWORKSPACE                                                   # misaligned
+    assert bwd(fake, fake, bf, 1, 4, 16, fake, 4, 3, None, fake, None, None, None, fake, 4096, None) == \
+        B.ENGRAM_EINVAL                                                                       # dweight
+    assert bwd(fake, None, bf, 1, 4, 16, fake, 4, 3, None, fake, fake, None, None, fake, 4096, None) == \
+        B.ENGRAM_EINVAL
+    norm = lib.engram_grouped_rms_norm
+    # (x, dtype, rows, hidden, group, weight, eps, y, stream)
+    assert norm(fake, bf, 2, 64, 24, fake, 1e-6, fake, None) == B.ENGRAM_EINVAL        # hidden % group
+    assert norm(fake, bf, 2, 60, 12, fake, 1e-6, fake, None) == B.ENGRAM_EINVAL        # 24-byte group
+    assert norm(fake, bf, 1, 5128, 5128, fake, 1e-6, fake, None) == B.ENGRAM_EINVAL    # group > 5120 bf16
+    assert norm(fake, f32, 1, 2564, 2564, fake, 1e-6, fake, None) == B.ENGRAM_EINVAL   # group > 2560 fp32
+    assert norm(fake, bf, 2, 64, 32, fake, -1.0, fake, None) == B.ENGRAM_EINVAL        # eps < 0
+    assert norm(fake, bf, 2, 64, 32, fake, float("nan"), fake, None) == B.ENGRAM_EINVAL
+    assert norm(fake, bf, 2, 64, 32, None, 1e-6, fake, None) == B.ENGRAM_EINVAL
+    assert norm(fake, 3, 2, 64, 32, fake, 1e-6, fake, None) == B.ENGRAM_EDTYPE
+    assert norm(None, bf, 0, 64, 32, fake, 1e-6, None, None) == B.ENGRAM_OK            # empty: no-op
+    assert lib.engram_grouped_rms_norm_workspace(65, 64) == 3 * 64 * 8
+    nb = lib.engram_grouped_rms_norm_backward
+    assert nb(fake, fake, bf, 2, 64, 32, fake, 1e-6, fake, fake, None, 0, None) == B.ENGRAM_EWORKSPACE
+    assert nb(fake, fake, bf, 2, 64, 32, fake, 1e-6, fake, None, fake, 4096, None) == B.ENGRAM_EINVAL
