@@ -16,6 +16,8 @@
 // gradients (sums over every batch row and position) are accumulated per tile
 // and then reduced over the tiles in a fixed order in fp64, so they are
 // deterministic.
+#include <type_traits>
+
 #include "engram_internal.h"
 
 namespace engram {
@@ -59,6 +61,38 @@ __device__ __forceinline__ u32x4 pack16(const float* f) {
 }
 
 __device__ u32x4 kPleZero = {0u, 0u, 0u, 0u};  // never written
+
+// Four channels per thread: 8 bytes in bf16, 16 bytes in fp32.
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+template <bool BF16>
+using Quad = typename std::conditional<BF16, u32x2, u32x4>::type;
+
+template <bool BF16>
+__device__ __forceinline__ void unpack4(Quad<BF16> v, float* f) {
+    if constexpr (BF16) {
+#pragma unroll
+        for (int q = 0; q < 2; ++q) {
+            f[2 * q] = __uint_as_float(v[q] << 16);
+            f[2 * q + 1] = __uint_as_float(v[q] & 0xFFFF0000u);
+        }
+    } else {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) f[q] = __uint_as_float(v[q]);
+    }
+}
+
+template <bool BF16>
+__device__ __forceinline__ Quad<BF16> pack4(const float* f) {
+    Quad<BF16> v;
+    if constexpr (BF16) {
+        v[0] = bf16_bits(f[0]) | (bf16_bits(f[1]) << 16);
+        v[1] = bf16_bits(f[2]) | (bf16_bits(f[3]) << 16);
+    } else {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) v[q] = __float_as_uint(f[q]);
+    }
+    return v;
+}
 
 // ---------------------------------------------------------------- convolution
 
@@ -187,20 +221,216 @@ __global__ __launch_bounds__(kPleBlock) void short_conv_bwd_kernel(
         for (int k = 0; k <= K; ++k) p[e * (K + 1) + k] = (double)pw[e][k];
 }
 
-// Sum the per-tile partials in tile order: dweight [C][K], dbias [C].
-__global__ __launch_bounds__(kPleBlock) void conv_grad_reduce_kernel(const double* __restrict__ partial,
-                                                                     int64_t parts, int64_t C, int K,
-                                                                     float* __restrict__ dw,
-                                                                     float* __restrict__ db) {
-    const int64_t i = (int64_t)blockIdx.x * kPleBlock + threadIdx.x;  // over C * (K + 1)
-    if (i >= C * (K + 1)) return;
+// ---- dilation 3 (the released layer): sliding register windows
+//
+// One thread owns four channels of one batch row over kConvTile positions and
+// walks them kConvStep positions at a time.  Its window holds the inputs from
+// HIST = (K - 1) * 3 positions back up to the current step, so every input is
+// loaded once per tile (plus the HIST-position overlap with the previous tile)
+// instead of once per tap.  Window indices are compile-time constants: the
+// window lives in registers.
+
+constexpr int kConvD = 3;
+constexpr int kConvStep = 6;
+constexpr int kConvTile = 96;            // positions per thread (multiple of kConvStep)
+constexpr int kConvWavesPerBlock = kPleBlock / 64;
+
+template <bool BF16, int K>
+__global__ __launch_bounds__(kPleBlock) void short_conv_fwd_d3_kernel(const void* __restrict__ xp,
+                                                                      const void* __restrict__ halop,
+                                                                      const float* __restrict__ w,
+                                                                      const float* __restrict__ bias, int64_t B,
+                                                                      int64_t S, int64_t C, void* __restrict__ yp) {
+    using Q = Quad<BF16>;
+    constexpr int HIST = (K - 1) * kConvD, P = kConvStep;
+    const Q* x = (const Q*)xp;
+    const Q* halo = (const Q*)halop;
+    const Q* zero = (const Q*)&kPleZero;
+    const int64_t quads = C / 4, tiles = (S + kConvTile - 1) / kConvTile;
+    const int64_t idx = (int64_t)blockIdx.x * kPleBlock + threadIdx.x;
+    if (idx >= B * tiles * quads) return;
+    const int64_t q = idx % quads, rest = idx / quads, tt = rest % tiles, b = rest / tiles;
+    float wv[4][K], bv[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+#pragma unroll
+        for (int k = 0; k < K; ++k) wv[e][k] = w[(q * 4 + e) * K + k];
+        bv[e] = bias ? bias[q * 4 + e] : 0.0f;
+    }
+    const Q* xb = x + b * S * quads + q;  // position t of this row and quad: xb[t * quads]
+    const int64_t t0 = tt * kConvTile, t1 = min(S, t0 + kConvTile);
+    Q win[HIST + P];  // positions t - HIST .. t + P - 1
+#pragma unroll
+    for (int i = 0; i < HIST; ++i) {
+        const int64_t ts = t0 - HIST + i;
+        const Q* src = ts >= 0 ? xb + ts * quads : (halo ? halo + ((b * HIST + HIST + ts) * quads + q) : zero);
+        win[i] = *src;
+    }
+    Q* yb = (Q*)yp + b * S * quads + q;
+    for (int64_t t = t0; t < t1; t += P) {
+#pragma unroll
+        for (int j = 0; j < P; ++j) win[HIST + j] = *(t + j < S ? xb + (t + j) * quads : zero);
+#pragma unroll
+        for (int j = 0; j < P; ++j) {
+            float acc[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) acc[e] = bv[e];
+#pragma unroll
+            for (int k = 0; k < K; ++k) {
+                float f[4];
+                unpack4<BF16>(win[HIST + j - (K - 1 - k) * kConvD], f);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) acc[e] = fmaf(wv[e][k], f[e], acc[e]);
+            }
+            if (t + j < t1) yb[(t + j) * quads] = pack4<BF16>(acc);
+        }
+#pragma unroll
+        for (int i = 0; i < HIST; ++i) win[i] = win[i + P];
+    }
+}
+
+// Backward, dilation 3.  A block is four waves over four consecutive tiles of
+// the same 64 quads; wave w takes tile 4 * tile_group + w.  Every wave keeps
+// fp32 sums of dweight / dbias over its tile; the four are added in wave order
+// in fp64 and written as one partial per (batch row, tile group):
+// partial [B * tile_groups][C][K + 1].
+template <bool BF16, int K>
+__global__ __launch_bounds__(kPleBlock) void short_conv_bwd_d3_kernel(
+    const void* __restrict__ xp, const void* __restrict__ dyp, const void* __restrict__ halop,
+    const float* __restrict__ w, int64_t B, int64_t S, int64_t C, void* __restrict__ dxp, void* __restrict__ dhalop,
+    double* __restrict__ partial) {
+    using Q = Quad<BF16>;
+    constexpr int HIST = (K - 1) * kConvD, P = kConvStep;
+    __shared__ float s_part[kConvWavesPerBlock][K + 1][4][64];
+    const Q* zero = (const Q*)&kPleZero;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int64_t quads = C / 4, tiles = (S + kConvTile - 1) / kConvTile;
+    const int64_t tgroups = (tiles + kConvWavesPerBlock - 1) / kConvWavesPerBlock, qgroups = (quads + 63) / 64;
+    const int64_t qg = blockIdx.x % qgroups, rest = blockIdx.x / qgroups, tg = rest % tgroups, b = rest / tgroups;
+    const int64_t q = qg * 64 + lane, tt = tg * kConvWavesPerBlock + wave;
+    const bool live = q < quads;
+    const int64_t qc = live ? q : quads - 1;  // clamped: loads stay in bounds, nothing is stored
+    float wv[4][K], pw[4][K + 1];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+#pragma unroll
+        for (int k = 0; k < K; ++k) wv[e][k] = w[(qc * 4 + e) * K + k];
+#pragma unroll
+        for (int k = 0; k <= K; ++k) pw[e][k] = 0.0f;
+    }
+    const Q* xb = (const Q*)xp + b * S * quads + qc;
+    const Q* gb = (const Q*)dyp + b * S * quads + qc;
+    const Q* halo = (const Q*)halop;
+    const int64_t t0 = min(S, tt * kConvTile), t1 = min(S, t0 + kConvTile);  // empty for a tile past the end
+    Q xw[HIST + P];  // x at t - HIST .. t + P - 1
+    Q gw[HIST + P];  // dy at t .. t + HIST + P - 1
+#pragma unroll
+    for (int i = 0; i < HIST; ++i) {
+        const int64_t ts = t0 - HIST + i;
+        xw[i] = *(ts >= 0 ? xb + ts * quads : (halo ? halo + ((b * HIST + HIST + ts) * quads + qc) : zero));
+        gw[i] = *(t0 + i < S ? gb + (t0 + i) * quads : zero);
+    }
+    if (dhalop && tt == 0 && t1 > t0 && live) {
+        // halo position i (sequence position i - HIST): taps reach dy at i - HIST + (K - 1 - k) * 3
+#pragma unroll
+        for (int i = 0; i < HIST; ++i) {
+            float acc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+            for (int k = 0; k < K; ++k) {
+                const int off = i - HIST + (K - 1 - k) * kConvD;
+                if (off >= 0) {
+                    float f[4];
+                    unpack4<BF16>(gw[off], f);
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) acc[e] = fmaf(wv[e][k], f[e], acc[e]);
+                }
+            }
+            ((Q*)dhalop)[(b * HIST + i) * quads + q] = pack4<BF16>(acc);
+        }
+    }
+    Q* dxb = (Q*)dxp + b * S * quads + q;
+    for (int64_t t = t0; t < t1; t += P) {
+#pragma unroll
+        for (int j = 0; j < P; ++j) {
+            xw[HIST + j] = *(t + j < S ? xb + (t + j) * quads : zero);
+            gw[HIST + j] = *(t + HIST + j < S ? gb + (t + HIST + j) * quads : zero);
+        }
+#pragma unroll
+        for (int j = 0; j < P; ++j) {
+            if (t + j >= t1) break;  // wave-uniform
+            float acc[4] = {0.0f, 0.0f, 0.0f, 0.0f}, g[4];
+#pragma unroll
+            for (int k = 0; k < K; ++k) {
+                float f[4];
+                unpack4<BF16>(gw[j + (K - 1 - k) * kConvD], f);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) acc[e] = fmaf(wv[e][k], f[e], acc[e]);
+            }
+            if (live) dxb[(t + j) * quads] = pack4<BF16>(acc);
+            unpack4<BF16>(gw[j], g);
+#pragma unroll
+            for (int k = 0; k < K; ++k) {
+                float xf[4];
+                unpack4<BF16>(xw[HIST + j - (K - 1 - k) * kConvD], xf);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) pw[e][k] = fmaf(g[e], xf[e], pw[e][k]);
+            }
+#pragma unroll
+            for (int e = 0; e < 4; ++e) pw[e][K] += g[e];
+        }
+#pragma unroll
+        for (int i = 0; i < HIST; ++i) {
+            xw[i] = xw[i + P];
+            gw[i] = gw[i + P];
+        }
+    }
+#pragma unroll
+    for (int k = 0; k <= K; ++k)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) s_part[wave][k][e][lane] = pw[e][k];
+    __syncthreads();
+    if (wave == 0 && live) {
+        double* out = partial + ((b * tgroups + tg) * C + q * 4) * (K + 1);
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+#pragma unroll
+            for (int k = 0; k <= K; ++k) {
+                double sum = 0.0;
+#pragma unroll
+                for (int v = 0; v < kConvWavesPerBlock; ++v) sum += (double)s_part[v][k][e][lane];
+                out[e * (K + 1) + k] = sum;
+            }
+    }
+}
+
+// Column sums of partial [parts][cols] in fp64, in part order within four
+// contiguous slices that are then added in slice order (deterministic).  With
+// K1 = K + 1 > 0 the columns are (channel, tap or bias) of the convolution:
+// column c * K1 + k goes to dw[c * K + k] for k < K and to db[c] for k == K;
+// with K1 == 0 column i goes to dw[i].
+__global__ __launch_bounds__(kPleBlock) void column_sum_kernel(const double* __restrict__ partial, int64_t parts,
+                                                               int64_t cols, int K1, float* __restrict__ dw,
+                                                               float* __restrict__ db) {
+    __shared__ double s_sum[kPleBlock / 64][64];
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int64_t col = (int64_t)blockIdx.x * 64 + lane;
+    const int64_t cc = col < cols ? col : cols - 1;
+    const int64_t per = (parts + 3) / 4, p0 = min(parts, wave * per), p1 = min(parts, p0 + per);
     double s = 0.0;
-    for (int64_t p = 0; p < parts; ++p) s += partial[p * C * (K + 1) + i];
-    const int64_t c = i / (K + 1), k = i % (K + 1);
-    if (k < K)
-        dw[c * K + k] = (float)s;
-    else if (db)
-        db[c] = (float)s;
+    for (int64_t p = p0; p < p1; ++p) s += partial[p * cols + cc];
+    s_sum[wave][lane] = s;
+    __syncthreads();
+    if (wave != 0 || col >= cols) return;
+    const double total = ((s_sum[0][lane] + s_sum[1][lane]) + s_sum[2][lane]) + s_sum[3][lane];
+    if (K1 == 0) {
+        dw[col] = (float)total;
+    } else {
+        const int64_t c = col / K1, k = col % K1;
+        if (k < K1 - 1)
+            dw[c * (K1 - 1) + k] = (float)total;
+        else if (db)
+            db[c] = (float)total;
+    }
 }
 
 // ---------------------------------------------------------------- grouped RMSNorm
@@ -248,8 +478,10 @@ __global__ __launch_bounds__(kPleBlock) void rms_norm_fwd_kernel(const u32x4* __
     }
 }
 
-// dx per row, and fp32 partial sums of dweight over rows_per_block rows per
-// wave: partial [row_blocks][hidden] in fp64.
+// dx per row, and sums of dweight over rows_per_block rows per wave: fp32
+// per wave, kept in LDS (each lane owns its features' slots, so no atomics),
+// then written as fp64: partial [row_blocks][hidden].  The next row's loads
+// are issued before the current row's reductions.
 template <bool BF16, int CH>
 __global__ __launch_bounds__(kPleBlock) void rms_norm_bwd_kernel(const u32x4* __restrict__ x,
                                                                  const u32x4* __restrict__ dy,
@@ -258,40 +490,43 @@ __global__ __launch_bounds__(kPleBlock) void rms_norm_bwd_kernel(const u32x4* __
                                                                  int rows_per_block, u32x4* __restrict__ dx,
                                                                  double* __restrict__ partial) {
     constexpr int VEC = BF16 ? 8 : 4;
-    const int lane = threadIdx.x & 63;
+    __shared__ float4 s_pw[kPleBlock / 64][CH * (VEC / 4)][64];
+    const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
     const int64_t groups = hidden / group, gchunks = group / VEC, hchunks = hidden / VEC;
     const int64_t blocks = (rows + rows_per_block - 1) / rows_per_block;
-    const int64_t wave = (int64_t)blockIdx.x * (kPleBlock / 64) + (threadIdx.x >> 6);
+    const int64_t wave = (int64_t)blockIdx.x * (kPleBlock / 64) + wid;
     if (wave >= blocks * groups) return;
     const int64_t rb = wave / groups, g = wave - rb * groups;
-    float pw[CH][VEC];
-#pragma unroll
-    for (int q = 0; q < CH; ++q)
-#pragma unroll
-        for (int e = 0; e < VEC; ++e) pw[q][e] = 0.0f;
     float wp[CH][VEC];  // 1 + weight of this lane's features
 #pragma unroll
     for (int q = 0; q < CH; ++q) {
         const int64_t c = lane + 64 * q;
 #pragma unroll
         for (int e = 0; e < VEC; ++e) wp[q][e] = c < gchunks ? 1.0f + w[g * group + c * VEC + e] : 0.0f;
+#pragma unroll
+        for (int h = 0; h < VEC / 4; ++h) s_pw[wid][q * (VEC / 4) + h][lane] = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
     }
-    const int64_t r1 = min(rows, (rb + 1) * rows_per_block);
-    for (int64_t r = rb * rows_per_block; r < r1; ++r) {
+    const int64_t r0 = rb * rows_per_block, r1 = min(rows, r0 + rows_per_block);
+    u32x4 xa[CH], ga[CH];
+    auto load_row = [&](int64_t r, u32x4* xv, u32x4* gv) {
         const int64_t base = r * hchunks + g * gchunks;
-        u32x4 xv[CH], gv[CH];
 #pragma unroll
         for (int q = 0; q < CH; ++q) {
             const int64_t c = lane + 64 * q;
-            xv[q] = *(c < gchunks ? x + base + c : &kPleZero);
+            xv[q] = *(c < gchunks ? x + base + c : &kPleZero);  // unconditional loads
             gv[q] = *(c < gchunks ? dy + base + c : &kPleZero);
         }
-        float ss = 0.0f, sdx = 0.0f;  // sum x^2, sum (dy * (1 + w)) * x
+    };
+    load_row(r0, xa, ga);
+    for (int64_t r = r0; r < r1; ++r) {
+        u32x4 xn[CH], gn[CH];
+        load_row(min(r + 1, r1 - 1), xn, gn);  // the last row reloads itself: in bounds, unused
+        float ss = 0.0f, sdx = 0.0f;             // sum x^2, sum (dy * (1 + w)) * x
 #pragma unroll
         for (int q = 0; q < CH; ++q) {
             float xf[VEC], gf[VEC];
-            unpack16<BF16>(xv[q], xf);
-            unpack16<BF16>(gv[q], gf);
+            unpack16<BF16>(xa[q], xf);
+            unpack16<BF16>(ga[q], gf);
 #pragma unroll
             for (int e = 0; e < VEC; ++e) {
                 ss = fmaf(xf[e], xf[e], ss);
@@ -305,38 +540,47 @@ __global__ __launch_bounds__(kPleBlock) void rms_norm_bwd_kernel(const u32x4* __
         }
         const float inv = 1.0f / sqrtf(ss / (float)group + eps);
         const float coef = inv * inv * inv * sdx / (float)group;
+        const int64_t base = r * hchunks + g * gchunks;
 #pragma unroll
         for (int q = 0; q < CH; ++q) {
             const int64_t c = lane + 64 * q;
             if (c >= gchunks) break;
             float xf[VEC], gf[VEC], out[VEC];
-            unpack16<BF16>(xv[q], xf);
-            unpack16<BF16>(gv[q], gf);
+            unpack16<BF16>(xa[q], xf);
+            unpack16<BF16>(ga[q], gf);
 #pragma unroll
-            for (int e = 0; e < VEC; ++e) {
-                out[e] = inv * gf[e] * wp[q][e] - coef * xf[e];
-                pw[q][e] = fmaf(gf[e], xf[e] * inv, pw[q][e]);
-            }
+            for (int e = 0; e < VEC; ++e) out[e] = inv * gf[e] * wp[q][e] - coef * xf[e];
             dx[base + c] = pack16<BF16>(out);
+#pragma unroll
+            for (int h = 0; h < VEC / 4; ++h) {
+                float4 a = s_pw[wid][q * (VEC / 4) + h][lane];
+                a.x = fmaf(gf[4 * h + 0], xf[4 * h + 0] * inv, a.x);
+                a.y = fmaf(gf[4 * h + 1], xf[4 * h + 1] * inv, a.y);
+                a.z = fmaf(gf[4 * h + 2], xf[4 * h + 2] * inv, a.z);
+                a.w = fmaf(gf[4 * h + 3], xf[4 * h + 3] * inv, a.w);
+                s_pw[wid][q * (VEC / 4) + h][lane] = a;
+            }
+        }
+#pragma unroll
+        for (int q = 0; q < CH; ++q) {
+            xa[q] = xn[q];
+            ga[q] = gn[q];
         }
     }
 #pragma unroll
     for (int q = 0; q < CH; ++q) {
         const int64_t c = lane + 64 * q;
         if (c >= gchunks) break;
+        double* out = partial + rb * hidden + g * group + c * VEC;
 #pragma unroll
-        for (int e = 0; e < VEC; ++e) partial[rb * hidden + g * group + c * VEC + e] = (double)pw[q][e];
+        for (int h = 0; h < VEC / 4; ++h) {
+            const float4 a = s_pw[wid][q * (VEC / 4) + h][lane];
+            out[4 * h + 0] = (double)a.x;
+            out[4 * h + 1] = (double)a.y;
+            out[4 * h + 2] = (double)a.z;
+            out[4 * h + 3] = (double)a.w;
+        }
     }
-}
-
-__global__ __launch_bounds__(kPleBlock) void norm_grad_reduce_kernel(const double* __restrict__ partial,
-                                                                     int64_t parts, int64_t hidden,
-                                                                     float* __restrict__ dw) {
-    const int64_t h = (int64_t)blockIdx.x * kPleBlock + threadIdx.x;
-    if (h >= hidden) return;
-    double s = 0.0;
-    for (int64_t p = 0; p < parts; ++p) s += partial[p * hidden + h];
-    dw[h] = (float)s;
 }
 
 __global__ __launch_bounds__(kPleBlock) void ple_zero_kernel(u32x4* __restrict__ p, int64_t n) {
@@ -346,7 +590,7 @@ __global__ __launch_bounds__(kPleBlock) void ple_zero_kernel(u32x4* __restrict__
 
 constexpr int kConvTileFwd = 16;
 constexpr int kConvTileBwd = 64;
-constexpr int kNormRowsPerBlock = 32;
+constexpr int kNormRowsPerBlock = 64;
 
 unsigned blocks_for(int64_t threads) { return (unsigned)((threads + kPleBlock - 1) / kPleBlock); }
 
@@ -381,11 +625,17 @@ bool rms_norm_group_ok(int elem_bytes, int64_t group) {
 hipError_t launch_short_conv(const void* x, int elem_bytes, int64_t B, int64_t S, int64_t C, const float* w,
                              const float* bias, int K, int d, const void* halo, void* y, hipStream_t stream) {
     if (B * S == 0) return hipSuccess;
-    const int vec = 16 / elem_bytes;
-    const int64_t threads = B * ((S + kConvTileFwd - 1) / kConvTileFwd) * (C / vec);
-    const dim3 grid(blocks_for(threads)), block(kPleBlock);
-    ENGRAM_CONV_DISPATCH(short_conv_fwd_kernel, (const u32x4*)x, (const u32x4*)halo, w, bias, B, S, C, d,
-                         kConvTileFwd, (u32x4*)y)
+    if (d == kConvD) {
+        const int64_t threads = B * ((S + kConvTile - 1) / kConvTile) * (C / 4);
+        const dim3 grid(blocks_for(threads)), block(kPleBlock);
+        ENGRAM_CONV_DISPATCH(short_conv_fwd_d3_kernel, x, halo, w, bias, B, S, C, y)
+    } else {
+        const int vec = 16 / elem_bytes;
+        const int64_t threads = B * ((S + kConvTileFwd - 1) / kConvTileFwd) * (C / vec);
+        const dim3 grid(blocks_for(threads)), block(kPleBlock);
+        ENGRAM_CONV_DISPATCH(short_conv_fwd_kernel, (const u32x4*)x, (const u32x4*)halo, w, bias, B, S, C, d,
+                             kConvTileFwd, (u32x4*)y)
+    }
     return hipGetLastError();
 }
 
@@ -393,23 +643,31 @@ hipError_t launch_short_conv_backward(const void* x, const void* dy, int elem_by
                                       const float* w, int K, int d, const void* halo, void* dx, float* dw, float* db,
                                       void* dhalo, void* workspace, hipStream_t stream) {
     const int vec = 16 / elem_bytes;
-    const int64_t tiles = (S + kConvTileBwd - 1) / kConvTileBwd;
-    const int64_t threads = B * tiles * (C / vec);
     double* partial = (double*)workspace;
-    if (threads > 0) {
-        const dim3 grid(blocks_for(threads)), block(kPleBlock);
+    int64_t parts = 0;
+    if (B * S > 0 && d == kConvD) {
+        const int64_t tiles = (S + kConvTile - 1) / kConvTile;
+        const int64_t tgroups = (tiles + kConvWavesPerBlock - 1) / kConvWavesPerBlock;
+        const int64_t blocks = B * tgroups * ((C / 4 + 63) / 64);
+        parts = B * tgroups;
+        const dim3 grid((unsigned)blocks), block(kPleBlock);
+        ENGRAM_CONV_DISPATCH(short_conv_bwd_d3_kernel, x, dy, halo, w, B, S, C, dx, dhalo, partial)
+    } else if (B * S > 0) {
+        const int64_t tiles = (S + kConvTileBwd - 1) / kConvTileBwd;
+        parts = B * tiles;
+        const dim3 grid(blocks_for(B * tiles * (C / vec))), block(kPleBlock);
         ENGRAM_CONV_DISPATCH(short_conv_bwd_kernel, (const u32x4*)x, (const u32x4*)dy, (const u32x4*)halo, w, B, S,
                              C, d, kConvTileBwd, (u32x4*)dx, (u32x4*)dhalo, partial)
-        hipError_t err = hipGetLastError();
-        if (err != hipSuccess) return err;
     } else if (dhalo && B > 0) {  // no positions: the halo's gradient is zero
         const int64_t n = B * (int64_t)(K - 1) * d * (C / vec);
-        hipLaunchKernelGGL(ple_zero_kernel, dim3(blocks_for(n)), dim3(kPleBlock), 0, stream, (u32x4*)dhalo, n);
-        hipError_t err = hipGetLastError();
-        if (err != hipSuccess) return err;
+        if (n > 0)
+            hipLaunchKernelGGL(ple_zero_kernel, dim3(blocks_for(n)), dim3(kPleBlock), 0, stream, (u32x4*)dhalo, n);
     }
-    hipLaunchKernelGGL(conv_grad_reduce_kernel, dim3(blocks_for(C * (K + 1))), dim3(kPleBlock), 0, stream,
-                       (const double*)partial, B * tiles, C, K, dw, db);
+    hipError_t err = hipGetLastError();
+    if (err != hipSuccess) return err;
+    const int64_t cols = C * (K + 1);
+    hipLaunchKernelGGL(column_sum_kernel, dim3((unsigned)((cols + 63) / 64)), dim3(kPleBlock), 0, stream,
+                       (const double*)partial, parts, cols, K + 1, dw, db);
     return hipGetLastError();
 }
 
@@ -464,8 +722,8 @@ hipError_t launch_rms_norm_backward(const void* x, const void* dy, int elem_byte
         hipError_t err = hipGetLastError();
         if (err != hipSuccess) return err;
     }
-    hipLaunchKernelGGL(norm_grad_reduce_kernel, dim3(blocks_for(hidden)), dim3(kPleBlock), 0, stream,
-                       (const double*)partial, blocks, hidden, dw);
+    hipLaunchKernelGGL(column_sum_kernel, dim3((unsigned)((hidden + 63) / 64)), dim3(kPleBlock), 0, stream,
+                       (const double*)partial, rows > 0 ? blocks : 0, hidden, 0, dw, (float*)nullptr);
     return hipGetLastError();
 }
 

@@ -207,7 +207,7 @@ def test_ple_rejects_bad_arguments(lib):
     assert conv(None, bf, 1, 4, 16, fake, None, 4, 3, None, fake, None) == B.ENGRAM_EINVAL
     assert conv(fake, bf, -1, 4, 16, fake, None, 4, 3, None, fake, None) == B.ENGRAM_EINVAL
     assert conv(None, bf, 0, 4, 16, fake, None, 4, 3, None, None, None) == B.ENGRAM_OK      # empty: no-op
-    assert lib.engram_short_conv_workspace(2, 100, 16, 4) == 2 * 2 * 16 * 5 * 8
+    assert lib.engram_short_conv_workspace(2, 100, 16, 4) >= 2 * 16 * 5 * 8     # one fp64 partial per batch row at least
     assert lib.engram_short_conv_workspace(2, 100, 16, 5) == 0
     bwd = lib.engram_short_conv_backward
     # (x, dy, dtype, B, S, C, w, K, d, halo, dx, dw, db, dhalo, ws, ws_bytes, stream)
@@ -230,7 +230,8 @@ def test_ple_rejects_bad_arguments(lib):
     assert norm(fake, bf, 2, 64, 32, None, 1e-6, fake, None) == B.ENGRAM_EINVAL
     assert norm(fake, 3, 2, 64, 32, fake, 1e-6, fake, None) == B.ENGRAM_EDTYPE
     assert norm(None, bf, 0, 64, 32, fake, 1e-6, None, None) == B.ENGRAM_OK            # empty: no-op
-    assert lib.engram_grouped_rms_norm_workspace(65, 64) == 3 * 64 * 8
+    assert lib.engram_grouped_rms_norm_workspace(65, 64) >= 64 * 8
+    assert lib.engram_grouped_rms_norm_workspace(-1, 64) == 0
     nb = lib.engram_grouped_rms_norm_backward
     assert nb(fake, fake, bf, 2, 64, 32, fake, 1e-6, fake, fake, None, 0, None) == B.ENGRAM_EWORKSPACE
     assert nb(fake, fake, bf, 2, 64, 32, fake, 1e-6, fake, None, fake, 4096, None) == B.ENGRAM_EINVAL
