@@ -15,6 +15,11 @@ the full 320,001,536 x 160 bf16 table (102.4 GB) held whole on the GPU, forward
 plus backward with the compact (distinct rows + sums) gradient output:
 4,194,304 (token x head) lookups per step.
 
+Workload "ple" times the step after the lookup instead: the PLE causal short
+convolution (kernel 4, dilation 3) followed by the grouped RMSNorm over the
+four 2,560-wide HyperConnection branches, forward and backward, on a batch of
+8 x 4,096 tokens x 10,240 bf16 channels; its line reports tokens/s.
+
 Printed: one JSON line with lookups/s, the roofline of the dominant kernel
 (timed with HIP events on the stream the kernels run on) and the oracle's CPU
 throughput on the same stream (rank 0, N = 1).
@@ -41,7 +46,7 @@ def parse_args():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--workload", default="long", choices=["long", "full-sft", "owner", "sft"])
+    ap.add_argument("--workload", default="long", choices=["long", "full-sft", "owner", "sft", "ple"])
     ap.add_argument("--rotations", type=int, default=4)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -215,6 +220,147 @@ def cpu_baseline(wl, max_tokens=None):
             "seconds": {"hash": round(t1 - t0, 3), "gather": round(t2 - t1, 3), "scatter_add": round(t3 - t2, 3)}}
 
 
+# ---------------------------------------------------------------- PLE conv + norm
+
+PLE_METRIC = "PLE short-conv + grouped-RMSNorm tokens/sec fwd+bwd and achieved HBM GB/s vs peak"
+
+
+def ple_build(rotations, dev, batch=8, seq=4096):
+    import torch
+
+    import hashed_gram_embedding_engram_amd as E
+    import workloads as W
+    from hashed_gram_embedding_engram_amd import engram as EB
+
+    lib = EB._ple_lib()
+    C = W.HC_COUNT * W.HC_WIDTH
+    rots = []
+    for r in range(rotations):
+        t = W.ple_tensors(dev, 2000 + r, batch, seq, C)
+        t["c"] = torch.empty_like(t["x"])        # conv output = norm input
+        t["z"] = torch.empty_like(t["x"])        # norm output
+        t["dc"] = torch.empty_like(t["x"])       # norm input gradient = conv output gradient
+        t["dx"] = torch.empty_like(t["x"])
+        t["dhalo"] = torch.empty_like(t["halo"])
+        t["dconv_w"] = torch.empty_like(t["conv_w"])
+        t["dconv_b"] = torch.empty_like(t["conv_b"])
+        t["dnorm_w"] = torch.empty_like(t["norm_w"])
+        rots.append(t)
+    ws_conv = torch.empty(max(lib.engram_short_conv_workspace(batch, seq, C, 4), 256), dtype=torch.uint8, device=dev)
+    ws_norm = torch.empty(max(lib.engram_grouped_rms_norm_workspace(batch * seq, C), 256), dtype=torch.uint8,
+                          device=dev)
+    return {"rots": rots, "ws_conv": ws_conv, "ws_norm": ws_norm, "batch": batch, "seq": seq, "channels": C,
+            "group": W.HC_WIDTH}
+
+
+def ple_step(wl, t, ev=None):
+    """conv forward -> grouped norm forward -> norm backward -> conv backward."""
+    import hashed_gram_embedding_engram_amd as E
+    rows, C, G = wl["batch"] * wl["seq"], wl["channels"], wl["group"]
+    if ev:
+        ev[0].record()
+    E.engram_short_conv(t["x"], t["conv_w"], t["conv_b"], 3, t["halo"], out=t["c"])
+    if ev:
+        ev[1].record()
+    E.engram_grouped_rms_norm(t["c"].view(rows, C), t["norm_w"], G, 1e-6, out=t["z"].view(rows, C))
+    if ev:
+        ev[2].record()
+    E.engram_grouped_rms_norm_backward(t["c"].view(rows, C), t["dy"].view(rows, C), t["norm_w"], G, 1e-6,
+                                       workspace=wl["ws_norm"], out=(t["dc"].view(rows, C), t["dnorm_w"]))
+    if ev:
+        ev[3].record()
+    E.engram_short_conv_backward(t["x"], t["dc"], t["conv_w"], 3, t["halo"], workspace=wl["ws_conv"],
+                                 out=(t["dx"], t["dconv_w"], t["dconv_b"], t["dhalo"]))
+    if ev:
+        ev[4].record()
+
+
+def ple_cpu_baseline(wl, sample_rows=2):
+    """The fp64 numpy oracle on the first ``sample_rows`` batch rows of rotation 0."""
+    import torch
+
+    from oracle import ple_ref as P
+    t = wl["rots"][0]
+    x = t["x"][:sample_rows].double().cpu().numpy()
+    dy = t["dy"][:sample_rows].double().cpu().numpy()
+    halo = t["halo"][:sample_rows].double().cpu().numpy()
+    cw, cb, nw = (t[k].double().cpu().numpy() for k in ("conv_w", "conv_b", "norm_w"))
+    G = wl["group"]
+    t0 = time.perf_counter()
+    c = P.short_conv(x, cw, cb, 3, halo)
+    P.grouped_rms_norm(c, nw, G)
+    dc, _ = P.grouped_rms_norm_backward(c, dy, nw, G)
+    P.short_conv_backward(x, dc, cw, 3, halo)
+    t1 = time.perf_counter()
+    tokens = sample_rows * wl["seq"]
+    return {"value": tokens / (t1 - t0), "unit": "tokens/s", "cores": 1, "kind": "oracle",
+            "sample": "%d of the %d batch rows of rotation 0 (%d tokens x %d channels): conv, norm, their "
+                      "backwards in fp64 numpy, single-threaded" % (sample_rows, wl["batch"], tokens,
+                                                                    wl["channels"]),
+            "seconds": round(t1 - t0, 3)}
+
+
+def ple_main(args, dev):
+    import torch
+
+    wl = ple_build(args.rotations, dev)
+    torch.cuda.synchronize()
+    R = len(wl["rots"])
+    for i in range(args.warmup):
+        ple_step(wl, wl["rots"][i % R])
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        ple_step(wl, wl["rots"][i % R], evs[i])
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    tokens = wl["batch"] * wl["seq"]
+    C = wl["channels"]
+    names = ["conv_fwd", "norm_fwd", "norm_bwd", "conv_bwd"]
+    phase = {n: sum(e[k].elapsed_time(e[k + 1]) for e in evs) / args.steps for k, n in enumerate(names)}
+    # Algorithmic bytes per launch (bf16 activations, 2 B per element): forward
+    # passes read x and write y (4 B per element); backward passes read x and
+    # dy and write dx (6 B per element).  Weights, halos and the weight
+    # gradients are under 0.1 %; the fp64 partial sums are scratch.
+    elems = float(tokens * C)
+    alg = {"conv_fwd": 4 * elems, "norm_fwd": 4 * elems, "norm_bwd": 6 * elems, "conv_bwd": 6 * elems}
+    kname = {"conv_fwd": ("short_conv_fwd_d3_kernel<bf16,4>", "ple.hip"),
+             "norm_fwd": ("rms_norm_fwd_kernel<bf16,5>", "ple.hip"),
+             "norm_bwd": ("rms_norm_bwd_kernel<bf16,5> + column_sum_kernel", "ple.hip"),
+             "conv_bwd": ("short_conv_bwd_d3_kernel<bf16,4> + column_sum_kernel", "ple.hip")}
+    dom = max(phase, key=phase.get)
+    achieved = alg[dom] / (phase[dom] / 1e3) / 1e9
+    elapsed = t1 - t0
+    result = {
+        "metric": PLE_METRIC,
+        "value": tokens * args.steps / elapsed,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": elapsed / args.steps * 1e3,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "PLE causal short conv (kernel 4, dilation 3, 9-token halo) + grouped RMSNorm "
+                               "(4 branches x 2,560), fwd+bwd", "batch": wl["batch"], "seq_len": wl["seq"],
+                   "channels": C, "rotations": R},
+        "phases_ms": {k: round(v, 4) for k, v in phase.items()},
+        "roofline": {"kernel": kname[dom][0], "bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS,
+                     "unit": "GB/s", "frac": achieved / HBM_PEAK_GBPS,
+                     "traffic": counter_traffic(kname[dom][1], "%s_ple_counters.txt" % dom),
+                     "algorithmic_bytes_per_launch": alg[dom], "avg_launch_ms": phase[dom]},
+        "phase_gbps_algorithmic": {k: round(alg[k] / (phase[k] / 1e3) / 1e9, 1) for k in names},
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = ple_cpu_baseline(wl)
+    print(json.dumps(result), flush=True)
+
+
 def main():
     args = parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -235,6 +381,9 @@ def main():
         dst.copy_(src)
         torch.cuda.synchronize()
         del src, dst
+    if args.workload == "ple":
+        ple_main(args, dev)
+        return
     wl = build_workload(args.workload, args.rotations, dev)
     torch.cuda.synchronize()
 

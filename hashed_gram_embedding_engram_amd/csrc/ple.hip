@@ -16,6 +16,7 @@
 // gradients (sums over every batch row and position) are accumulated per tile
 // and then reduced over the tiles in a fixed order in fp64, so they are
 // deterministic.
+#include <algorithm>
 #include <type_traits>
 
 #include "engram_internal.h"
@@ -230,9 +231,15 @@ __global__ __launch_bounds__(kPleBlock) void short_conv_bwd_kernel(
 // instead of once per tap.  Window indices are compile-time constants: the
 // window lives in registers.
 
+#ifndef ENGRAM_CONV_STEP
+#define ENGRAM_CONV_STEP 3
+#endif
+#ifndef ENGRAM_CONV_TILE
+#define ENGRAM_CONV_TILE 96
+#endif
 constexpr int kConvD = 3;
-constexpr int kConvStep = 6;
-constexpr int kConvTile = 96;            // positions per thread (multiple of kConvStep)
+constexpr int kConvStep = ENGRAM_CONV_STEP;
+constexpr int kConvTile = ENGRAM_CONV_TILE;  // positions per thread (multiple of kConvStep)
 constexpr int kConvWavesPerBlock = kPleBlock / 64;
 
 template <bool BF16, int K>
@@ -403,25 +410,30 @@ __global__ __launch_bounds__(kPleBlock) void short_conv_bwd_d3_kernel(
     }
 }
 
-// Column sums of partial [parts][cols] in fp64, in part order within four
-// contiguous slices that are then added in slice order (deterministic).  With
+// Column sums of partial [parts][cols] in fp64: each of the block's
+// kSumWaves waves sums one contiguous slice of the parts in part order, and
+// the slice sums are then added in slice order (deterministic).  With
 // K1 = K + 1 > 0 the columns are (channel, tap or bias) of the convolution:
 // column c * K1 + k goes to dw[c * K + k] for k < K and to db[c] for k == K;
 // with K1 == 0 column i goes to dw[i].
-__global__ __launch_bounds__(kPleBlock) void column_sum_kernel(const double* __restrict__ partial, int64_t parts,
-                                                               int64_t cols, int K1, float* __restrict__ dw,
-                                                               float* __restrict__ db) {
-    __shared__ double s_sum[kPleBlock / 64][64];
+constexpr int kSumWaves = 16;
+
+__global__ __launch_bounds__(64 * kSumWaves) void column_sum_kernel(const double* __restrict__ partial, int64_t parts,
+                                                                    int64_t cols, int K1, float* __restrict__ dw,
+                                                                    float* __restrict__ db) {
+    __shared__ double s_sum[kSumWaves][64];
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int64_t col = (int64_t)blockIdx.x * 64 + lane;
     const int64_t cc = col < cols ? col : cols - 1;
-    const int64_t per = (parts + 3) / 4, p0 = min(parts, wave * per), p1 = min(parts, p0 + per);
+    const int64_t per = (parts + kSumWaves - 1) / kSumWaves, p0 = min(parts, wave * per), p1 = min(parts, p0 + per);
     double s = 0.0;
     for (int64_t p = p0; p < p1; ++p) s += partial[p * cols + cc];
     s_sum[wave][lane] = s;
     __syncthreads();
     if (wave != 0 || col >= cols) return;
-    const double total = ((s_sum[0][lane] + s_sum[1][lane]) + s_sum[2][lane]) + s_sum[3][lane];
+    double total = 0.0;
+#pragma unroll
+    for (int v = 0; v < kSumWaves; ++v) total += s_sum[v][lane];
     if (K1 == 0) {
         dw[col] = (float)total;
     } else {
@@ -478,35 +490,42 @@ __global__ __launch_bounds__(kPleBlock) void rms_norm_fwd_kernel(const u32x4* __
     }
 }
 
-// dx per row, and sums of dweight over rows_per_block rows per wave: fp32
-// per wave, kept in LDS (each lane owns its features' slots, so no atomics),
-// then written as fp64: partial [row_blocks][hidden].  The next row's loads
+// dx per row, and the weight gradient's sums.  A block's four waves share
+// one group g (its 1 + weight is staged once in LDS) and take four
+// consecutive blocks of rows_per_wave rows.  Each wave keeps fp32 sums over
+// its rows in LDS (each lane owns its features' slots, so no atomics); the
+// four are added in wave order in fp64 and written as one partial per block:
+// partial [ceil(rows / (4 * rows_per_wave))][hidden].  The next row's loads
 // are issued before the current row's reductions.
 template <bool BF16, int CH>
 __global__ __launch_bounds__(kPleBlock) void rms_norm_bwd_kernel(const u32x4* __restrict__ x,
                                                                  const u32x4* __restrict__ dy,
                                                                  const float* __restrict__ w, int64_t rows,
                                                                  int64_t hidden, int64_t group, float eps,
-                                                                 int rows_per_block, u32x4* __restrict__ dx,
+                                                                 int rows_per_wave, u32x4* __restrict__ dx,
                                                                  double* __restrict__ partial) {
-    constexpr int VEC = BF16 ? 8 : 4;
-    __shared__ float4 s_pw[kPleBlock / 64][CH * (VEC / 4)][64];
+    constexpr int VEC = BF16 ? 8 : 4, H4 = VEC / 4, WAVES = kPleBlock / 64;
+    __shared__ float4 s_pw[WAVES][CH * H4][64];
+    __shared__ float4 s_wp[CH * H4][64];
     const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
     const int64_t groups = hidden / group, gchunks = group / VEC, hchunks = hidden / VEC;
-    const int64_t blocks = (rows + rows_per_block - 1) / rows_per_block;
-    const int64_t wave = (int64_t)blockIdx.x * (kPleBlock / 64) + wid;
-    if (wave >= blocks * groups) return;
-    const int64_t rb = wave / groups, g = wave - rb * groups;
-    float wp[CH][VEC];  // 1 + weight of this lane's features
-#pragma unroll
-    for (int q = 0; q < CH; ++q) {
-        const int64_t c = lane + 64 * q;
-#pragma unroll
-        for (int e = 0; e < VEC; ++e) wp[q][e] = c < gchunks ? 1.0f + w[g * group + c * VEC + e] : 0.0f;
-#pragma unroll
-        for (int h = 0; h < VEC / 4; ++h) s_pw[wid][q * (VEC / 4) + h][lane] = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+    const int64_t g = blockIdx.x % groups, bb = blockIdx.x / groups;
+    for (int i = threadIdx.x; i < CH * H4 * 64; i += kPleBlock) {
+        const int ln = i & 63, qh = i >> 6, q = qh / H4, h = qh % H4;
+        const int64_t c = ln + 64 * q;
+        float4 v = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+        if (c < gchunks) {
+            const float* wg = w + g * group + c * VEC + 4 * h;
+            v = make_float4(1.0f + wg[0], 1.0f + wg[1], 1.0f + wg[2], 1.0f + wg[3]);
+        }
+        s_wp[qh][ln] = v;
+        s_pw[0][qh][ln] = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+        s_pw[1][qh][ln] = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+        s_pw[2][qh][ln] = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+        s_pw[3][qh][ln] = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
     }
-    const int64_t r0 = rb * rows_per_block, r1 = min(rows, r0 + rows_per_block);
+    __syncthreads();
+    const int64_t r0 = min(rows, (bb * WAVES + wid) * rows_per_wave), r1 = min(rows, r0 + rows_per_wave);
     u32x4 xa[CH], ga[CH];
     auto load_row = [&](int64_t r, u32x4* xv, u32x4* gv) {
         const int64_t base = r * hchunks + g * gchunks;
@@ -517,7 +536,7 @@ __global__ __launch_bounds__(kPleBlock) void rms_norm_bwd_kernel(const u32x4* __
             gv[q] = *(c < gchunks ? dy + base + c : &kPleZero);
         }
     };
-    load_row(r0, xa, ga);
+    if (r0 < r1) load_row(r0, xa, ga);
     for (int64_t r = r0; r < r1; ++r) {
         u32x4 xn[CH], gn[CH];
         load_row(min(r + 1, r1 - 1), xn, gn);  // the last row reloads itself: in bounds, unused
@@ -528,9 +547,14 @@ __global__ __launch_bounds__(kPleBlock) void rms_norm_bwd_kernel(const u32x4* __
             unpack16<BF16>(xa[q], xf);
             unpack16<BF16>(ga[q], gf);
 #pragma unroll
-            for (int e = 0; e < VEC; ++e) {
-                ss = fmaf(xf[e], xf[e], ss);
-                sdx = fmaf(gf[e] * wp[q][e], xf[e], sdx);
+            for (int h = 0; h < H4; ++h) {
+                const float4 wp = s_wp[q * H4 + h][lane];
+                const float wv[4] = {wp.x, wp.y, wp.z, wp.w};
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    ss = fmaf(xf[4 * h + e], xf[4 * h + e], ss);
+                    sdx = fmaf(gf[4 * h + e] * wv[e], xf[4 * h + e], sdx);
+                }
             }
         }
 #pragma unroll
@@ -541,6 +565,10 @@ __global__ __launch_bounds__(kPleBlock) void rms_norm_bwd_kernel(const u32x4* __
         const float inv = 1.0f / sqrtf(ss / (float)group + eps);
         const float coef = inv * inv * inv * sdx / (float)group;
         const int64_t base = r * hchunks + g * gchunks;
+        // Unpack again below rather than keep 2 * CH * VEC unpacked floats live
+        // across the reductions (an empty asm the compiler cannot see through).
+#pragma unroll
+        for (int q = 0; q < CH; ++q) asm volatile("" : "+v"(xa[q]), "+v"(ga[q]));
 #pragma unroll
         for (int q = 0; q < CH; ++q) {
             const int64_t c = lane + 64 * q;
@@ -549,17 +577,19 @@ __global__ __launch_bounds__(kPleBlock) void rms_norm_bwd_kernel(const u32x4* __
             unpack16<BF16>(xa[q], xf);
             unpack16<BF16>(ga[q], gf);
 #pragma unroll
-            for (int e = 0; e < VEC; ++e) out[e] = inv * gf[e] * wp[q][e] - coef * xf[e];
-            dx[base + c] = pack16<BF16>(out);
+            for (int h = 0; h < H4; ++h) {
+                const float4 wp = s_wp[q * H4 + h][lane];
+                const float wv[4] = {wp.x, wp.y, wp.z, wp.w};
+                float4 a = s_pw[wid][q * H4 + h][lane];
+                float av[4] = {a.x, a.y, a.z, a.w};
 #pragma unroll
-            for (int h = 0; h < VEC / 4; ++h) {
-                float4 a = s_pw[wid][q * (VEC / 4) + h][lane];
-                a.x = fmaf(gf[4 * h + 0], xf[4 * h + 0] * inv, a.x);
-                a.y = fmaf(gf[4 * h + 1], xf[4 * h + 1] * inv, a.y);
-                a.z = fmaf(gf[4 * h + 2], xf[4 * h + 2] * inv, a.z);
-                a.w = fmaf(gf[4 * h + 3], xf[4 * h + 3] * inv, a.w);
-                s_pw[wid][q * (VEC / 4) + h][lane] = a;
+                for (int e = 0; e < 4; ++e) {
+                    out[4 * h + e] = inv * gf[4 * h + e] * wv[e] - coef * xf[4 * h + e];
+                    av[e] = fmaf(gf[4 * h + e], xf[4 * h + e] * inv, av[e]);
+                }
+                s_pw[wid][q * H4 + h][lane] = make_float4(av[0], av[1], av[2], av[3]);
             }
+            dx[base + c] = pack16<BF16>(out);
         }
 #pragma unroll
         for (int q = 0; q < CH; ++q) {
@@ -567,19 +597,23 @@ __global__ __launch_bounds__(kPleBlock) void rms_norm_bwd_kernel(const u32x4* __
             ga[q] = gn[q];
         }
     }
+    __syncthreads();
+    for (int i = threadIdx.x; i < CH * H4 * 64; i += kPleBlock) {
+        const int ln = i & 63, qh = i >> 6, q = qh / H4, h = qh % H4;
+        const int64_t c = ln + 64 * q;
+        if (c >= gchunks) continue;
+        double sum[4] = {0.0, 0.0, 0.0, 0.0};
 #pragma unroll
-    for (int q = 0; q < CH; ++q) {
-        const int64_t c = lane + 64 * q;
-        if (c >= gchunks) break;
-        double* out = partial + rb * hidden + g * group + c * VEC;
-#pragma unroll
-        for (int h = 0; h < VEC / 4; ++h) {
-            const float4 a = s_pw[wid][q * (VEC / 4) + h][lane];
-            out[4 * h + 0] = (double)a.x;
-            out[4 * h + 1] = (double)a.y;
-            out[4 * h + 2] = (double)a.z;
-            out[4 * h + 3] = (double)a.w;
+        for (int v = 0; v < WAVES; ++v) {
+            const float4 a = s_pw[v][qh][ln];
+            sum[0] += (double)a.x;
+            sum[1] += (double)a.y;
+            sum[2] += (double)a.z;
+            sum[3] += (double)a.w;
         }
+        double* out = partial + bb * hidden + g * group + c * VEC + 4 * h;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) out[e] = sum[e];
     }
 }
 
@@ -590,7 +624,13 @@ __global__ __launch_bounds__(kPleBlock) void ple_zero_kernel(u32x4* __restrict__
 
 constexpr int kConvTileFwd = 16;
 constexpr int kConvTileBwd = 64;
-constexpr int kNormRowsPerBlock = 64;
+// Rows per wave of the norm backward: enough waves to fill the chip (about
+// 2,048 row blocks per group), at most 64 rows so the LDS sums stay short.
+int norm_rows_per_wave(int64_t rows) { return (int)std::min<int64_t>(64, std::max<int64_t>(4, rows / 2048)); }
+int64_t norm_partials(int64_t rows) {
+    const int64_t rpw = norm_rows_per_wave(rows);
+    return (rows + 4 * rpw - 1) / (4 * rpw);
+}
 
 unsigned blocks_for(int64_t threads) { return (unsigned)((threads + kPleBlock - 1) / kPleBlock); }
 
@@ -602,7 +642,7 @@ size_t short_conv_workspace_bytes(int64_t batch, int64_t seq, int64_t channels, 
 }
 
 size_t rms_norm_workspace_bytes(int64_t rows, int64_t hidden) {
-    return (size_t)((rows + kNormRowsPerBlock - 1) / kNormRowsPerBlock) * (size_t)hidden * sizeof(double);
+    return (size_t)norm_partials(rows) * (size_t)hidden * sizeof(double);
 }
 
 bool rms_norm_group_ok(int elem_bytes, int64_t group) {
@@ -666,7 +706,7 @@ hipError_t launch_short_conv_backward(const void* x, const void* dy, int elem_by
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
     const int64_t cols = C * (K + 1);
-    hipLaunchKernelGGL(column_sum_kernel, dim3((unsigned)((cols + 63) / 64)), dim3(kPleBlock), 0, stream,
+    hipLaunchKernelGGL(column_sum_kernel, dim3((unsigned)((cols + 63) / 64)), dim3(64 * kSumWaves), 0, stream,
                        (const double*)partial, parts, cols, K + 1, dw, db);
     return hipGetLastError();
 }
@@ -711,19 +751,18 @@ hipError_t launch_rms_norm(const void* x, int elem_bytes, int64_t rows, int64_t 
 hipError_t launch_rms_norm_backward(const void* x, const void* dy, int elem_bytes, int64_t rows, int64_t hidden,
                                     int64_t group, const float* w, float eps, void* dx, float* dw, void* workspace,
                                     hipStream_t stream) {
-    const int64_t blocks = (rows + kNormRowsPerBlock - 1) / kNormRowsPerBlock;
+    const int64_t parts = rows > 0 ? norm_partials(rows) : 0;
     double* partial = (double*)workspace;
     if (rows > 0) {
         const int ch = norm_chunks_per_lane(elem_bytes, group);
-        const int64_t waves = blocks * (hidden / group);
-        const dim3 grid(blocks_for(waves * 64)), block(kPleBlock);
+        const dim3 grid((unsigned)(parts * (hidden / group))), block(kPleBlock);
         ENGRAM_NORM_DISPATCH(rms_norm_bwd_kernel, (const u32x4*)x, (const u32x4*)dy, w, rows, hidden, group, eps,
-                             kNormRowsPerBlock, (u32x4*)dx, partial)
+                             norm_rows_per_wave(rows), (u32x4*)dx, partial)
         hipError_t err = hipGetLastError();
         if (err != hipSuccess) return err;
     }
-    hipLaunchKernelGGL(column_sum_kernel, dim3((unsigned)((hidden + 63) / 64)), dim3(kPleBlock), 0, stream,
-                       (const double*)partial, rows > 0 ? blocks : 0, hidden, 0, dw, (float*)nullptr);
+    hipLaunchKernelGGL(column_sum_kernel, dim3((unsigned)((hidden + 63) / 64)), dim3(64 * kSumWaves), 0, stream,
+                       (const double*)partial, parts, hidden, 0, dw, (float*)nullptr);
     return hipGetLastError();
 }
 

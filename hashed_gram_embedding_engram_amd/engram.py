@@ -430,16 +430,20 @@ def engram_short_conv(x, weight, bias=None, dilation=3, halo=None, out=None, str
 
 
 def engram_short_conv_backward(x, dy, weight, dilation=3, halo=None, want_bias=True, want_halo=False,
-                               workspace=None, stream=None):
-    """Returns (dx, dweight, dbias or None, dhalo or None)."""
+                               workspace=None, out=None, stream=None):
+    """Returns (dx, dweight, dbias or None, dhalo or None); ``out`` may supply
+    that tuple's buffers (then want_bias / want_halo follow its entries)."""
     lib = _ple_lib()
     B, S, C = x.shape
     K = weight.shape[1]
     dev = x.device
-    dx = torch.empty_like(x)
-    dw = torch.empty((C, K), dtype=torch.float32, device=dev)
-    db = torch.empty(C, dtype=torch.float32, device=dev) if want_bias else None
-    dhalo = torch.empty((B, (K - 1) * dilation, C), dtype=x.dtype, device=dev) if want_halo else None
+    if out is not None:
+        dx, dw, db, dhalo = out
+    else:
+        dx = torch.empty_like(x)
+        dw = torch.empty((C, K), dtype=torch.float32, device=dev)
+        db = torch.empty(C, dtype=torch.float32, device=dev) if want_bias else None
+        dhalo = torch.empty((B, (K - 1) * dilation, C), dtype=x.dtype, device=dev) if want_halo else None
     if workspace is None:
         workspace = _workspace(lib.engram_short_conv_workspace(B, S, C, K), dev)
     _check(lib.engram_short_conv_backward(_dev_ptr(x, "x"), _dev_ptr(dy, "dy", x.dtype), _dtype_code(x), B, S, C,
@@ -463,13 +467,16 @@ def engram_grouped_rms_norm(x, weight, group_size, eps=1e-6, out=None, stream=No
     return y
 
 
-def engram_grouped_rms_norm_backward(x, dy, weight, group_size, eps=1e-6, workspace=None, stream=None):
-    """Returns (dx, dweight)."""
+def engram_grouped_rms_norm_backward(x, dy, weight, group_size, eps=1e-6, workspace=None, out=None, stream=None):
+    """Returns (dx, dweight); ``out`` may supply those two buffers."""
     lib = _ple_lib()
     hidden = x.shape[-1]
     rows = x.numel() // hidden if hidden else 0
-    dx = torch.empty_like(x)
-    dw = torch.empty(hidden, dtype=torch.float32, device=x.device)
+    if out is not None:
+        dx, dw = out
+    else:
+        dx = torch.empty_like(x)
+        dw = torch.empty(hidden, dtype=torch.float32, device=x.device)
     if workspace is None:
         workspace = _workspace(lib.engram_grouped_rms_norm_workspace(rows, hidden), x.device)
     _check(lib.engram_grouped_rms_norm_backward(_dev_ptr(x, "x"), _dev_ptr(dy, "dy", x.dtype), _dtype_code(x), rows,

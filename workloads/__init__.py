@@ -20,6 +20,8 @@ DIM = 160                # model-coverage page, Architecture: table rows of widt
 FULL_ROWS = 320_001_536  # engram API page, QWEN3_8_FLASH_NEXT_NGRAM_PADDED_ROWS
 OWNER_WORLD = 64         # model-coverage page, Validated Configuration: 64 contiguous shards
 OWNER_ROWS = FULL_ROWS // OWNER_WORLD
+HC_COUNT = 4             # model-coverage page, Architecture: four persistent HyperConnection streams
+HC_WIDTH = 2_560         # ... each 2,560 wide (the width of one branch, the grouped norm's group)
 
 _zipf_cdf_cache = {}
 
@@ -173,3 +175,25 @@ def fill_normal_(tensor, seed, std=0.02, chunk_rows=1 << 22):
     for a in range(0, rows, chunk_rows):
         tensor[a:a + chunk_rows].normal_(0.0, std, generator=g)
     return tensor
+
+
+def ple_tensors(dev, seed, batch, seq, channels=HC_COUNT * HC_WIDTH, dtype=None):
+    """PLE-layer inputs on ``dev``: activations x and output gradients dy
+    [batch, seq, channels] ~ N(0, 1) in bf16, one batch row's halo of the
+    preceding 9 tokens, conv weights [channels, 4] ~ N(0, 0.5^2) and bias
+    [channels] ~ N(0, 0.1^2), grouped-norm weights [channels] ~ N(0, 0.3^2)
+    (fp32).  The pages start the conv and the norm weights at zero; random
+    values here make every tap and scale visible in the results."""
+    import torch
+    dtype = dtype or torch.bfloat16
+    g = torch.Generator(device=dev)
+    g.manual_seed(int(seed))
+    shape = (batch, seq, channels)
+    return {
+        "x": torch.randn(shape, generator=g, device=dev).to(dtype),
+        "dy": torch.randn(shape, generator=g, device=dev).to(dtype),
+        "halo": torch.randn((batch, 9, channels), generator=g, device=dev).to(dtype),
+        "conv_w": torch.randn((channels, 4), generator=g, device=dev) * 0.5,
+        "conv_b": torch.randn(channels, generator=g, device=dev) * 0.1,
+        "norm_w": torch.randn(channels, generator=g, device=dev) * 0.3,
+    }
