@@ -20,6 +20,13 @@ convolution (kernel 4, dilation 3) followed by the grouped RMSNorm over the
 four 2,560-wide HyperConnection branches, forward and backward, on a batch of
 8 x 4,096 tokens x 10,240 bf16 channels; its line reports tokens/s.
 
+Workload "route" times the single-GPU half of the row-owner exchange for one
+request rank of a world-64 owner group (8 x 4,096 Zipf(1.2) tokens, 524,288
+lookups): group by owner, validate the segments, pack the IDs to the agreed
+capacity, the owner's unpack of them, the owner's pack of the 320-B value rows,
+the requester's unpack and its return to request order.  The all-to-all
+itself needs several GPUs and is not timed; the exchange is the identity.
+
 Printed: one JSON line with lookups/s, the roofline of the dominant kernel
 (timed with HIP events on the stream the kernels run on) and the oracle's CPU
 throughput on the same stream (rank 0, N = 1).
@@ -46,7 +53,7 @@ def parse_args():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--workload", default="long", choices=["long", "full-sft", "owner", "sft", "ple"])
+    ap.add_argument("--workload", default="long", choices=["long", "full-sft", "owner", "sft", "ple", "route"])
     ap.add_argument("--rotations", type=int, default=4)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -361,6 +368,164 @@ def ple_main(args, dev):
     print(json.dumps(result), flush=True)
 
 
+# ---------------------------------------------------------------- owner routing
+
+ROUTE_METRIC = "Owner-routing (token x head) lookups/sec, request + owner side of one exchange, and HBM GB/s vs peak"
+
+
+def route_build(rotations, dev, world=64):
+    import torch
+
+    import hashed_gram_embedding_engram_amd as E
+    import workloads as W
+    from hashed_gram_embedding_engram_amd import engram as EB
+
+    lib = EB._route_lib()
+    spec = E.qwen3_8_flash_next_spec()
+    rots = []
+    for r in range(rotations):
+        ids = W.owner_token_batches(seeds=[100 + r])[0]
+        gids = E.engram_hash(torch.from_numpy(ids).to(dev), spec).reshape(-1).contiguous()
+        n = gids.numel()
+        t = {"ids": gids, "n": n,
+             "sorted": torch.empty(n, dtype=torch.int64, device=dev),
+             "order": torch.empty(n, dtype=torch.int64, device=dev),
+             "counts": torch.empty(world, dtype=torch.int64, device=dev),
+             "status": torch.empty((), dtype=torch.int64, device=dev),
+             "ws": torch.empty(max(int(lib.engram_route_workspace(n)), 256), dtype=torch.uint8, device=dev)}
+        E.engram_route_plan(gids, W.FULL_ROWS, world, out=(t["sorted"], t["order"], t["counts"]), workspace=t["ws"])
+        cap = int(t["counts"].max().item())
+        g = torch.Generator(device=dev)
+        g.manual_seed(3000 + r)
+        t["cap"] = cap
+        t["ids_packed"] = torch.empty((world, cap), dtype=torch.int64, device=dev)
+        t["ids_recv"] = torch.empty(n, dtype=torch.int64, device=dev)
+        # the owner's looked-up values, in the received (grouped) order
+        t["vals"] = torch.randn((n, W.DIM), generator=g, device=dev).to(torch.bfloat16)
+        t["vals_packed"] = torch.empty((world, cap, W.DIM), dtype=torch.bfloat16, device=dev)
+        t["vals_grouped"] = torch.empty((n, W.DIM), dtype=torch.bfloat16, device=dev)
+        t["vals_out"] = torch.empty((n, W.DIM), dtype=torch.bfloat16, device=dev)
+        rots.append(t)
+    return {"rots": rots, "world": world, "num_embeddings": W.FULL_ROWS}
+
+
+def route_step(wl, t, ev=None):
+    import hashed_gram_embedding_engram_amd as E
+    W_, NE = wl["world"], wl["num_embeddings"]
+    k = 0
+
+    def mark():
+        nonlocal k
+        if ev:
+            ev[k].record()
+        k += 1
+    mark()
+    E.engram_route_plan(t["ids"], NE, W_, status=t["status"], workspace=t["ws"],
+                        out=(t["sorted"], t["order"], t["counts"]))
+    mark()
+    E.engram_route_validate(t["sorted"], t["counts"], NE, W_)
+    mark()
+    E.engram_pack_fixed_capacity(t["sorted"], t["counts"], W_, t["cap"], fill=-1, out=t["ids_packed"])
+    mark()
+    E.engram_unpack_fixed_capacity(t["ids_packed"], t["counts"], t["n"], out=t["ids_recv"])
+    mark()
+    E.engram_pack_fixed_capacity(t["vals"], t["counts"], W_, t["cap"], fill=0, out=t["vals_packed"])
+    mark()
+    E.engram_unpack_fixed_capacity(t["vals_packed"], t["counts"], t["n"], out=t["vals_grouped"])
+    mark()
+    E.engram_unpermute_rows(t["vals_grouped"], t["order"], out=t["vals_out"])
+    mark()
+
+
+def route_cpu_baseline(wl):
+    import numpy as np
+
+    from oracle import route_ref as RR
+    t = wl["rots"][0]
+    ids = t["ids"].cpu().numpy()
+    vals = t["vals"].float().cpu().numpy()
+    W_, NE, cap = wl["world"], wl["num_embeddings"], t["cap"]
+    t0 = time.perf_counter()
+    s, order, counts, _ = RR.route_plan(ids, NE, W_)
+    RR.validate(s, counts, NE, W_)
+    packed_ids, _ = RR.pack(s, counts, W_, cap, -1)
+    RR.unpack(packed_ids, counts, ids.size)
+    packed, _ = RR.pack(vals, counts, W_, cap, 0.0)
+    grouped = RR.unpack(packed, counts, ids.size)
+    out = np.empty_like(grouped)
+    out[order] = grouped
+    t1 = time.perf_counter()
+    return {"value": ids.size / (t1 - t0), "unit": "lookups/s", "cores": 1, "kind": "oracle",
+            "sample": "rotation 0 in full (%d lookups, world %d, capacity %d), plain Python loops over segments "
+                      "with numpy arrays, single-threaded" % (ids.size, W_, cap),
+            "seconds": round(t1 - t0, 3)}
+
+
+def route_main(args, dev):
+    import torch
+
+    import workloads as W
+    wl = route_build(args.rotations, dev)
+    torch.cuda.synchronize()
+    R = len(wl["rots"])
+    for i in range(args.warmup):
+        route_step(wl, wl["rots"][i % R])
+    torch.cuda.synchronize()
+    names = ["plan", "validate", "pack_ids", "unpack_ids", "pack_values", "unpack_values", "unpermute_values"]
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(names) + 1)] for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        route_step(wl, wl["rots"][i % R], evs[i])
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    phase = {nm: sum(e[k].elapsed_time(e[k + 1]) for e in evs) / args.steps for k, nm in enumerate(names)}
+    n = sum(wl["rots"][i % R]["n"] for i in range(args.steps)) / args.steps
+    cap = sum(wl["rots"][i % R]["cap"] for i in range(args.steps)) / args.steps
+    Wd, row = wl["world"], 2.0 * W.DIM
+    # Algorithmic bytes per launch: the plan reads the 8-B IDs and writes the
+    # sorted IDs and their 8-B request positions; validation reads the sorted
+    # IDs; a pack reads the compact rows and writes the whole padded
+    # [world][capacity] block; an unpack reads the valid rows and writes them
+    # compact; the unpermute reads and writes every row plus its 8-B position.
+    alg = {"plan": 24.0 * n, "validate": 8.0 * n, "pack_ids": 8.0 * n + 8.0 * Wd * cap,
+           "unpack_ids": 16.0 * n, "pack_values": row * n + row * Wd * cap, "unpack_values": 2 * row * n,
+           "unpermute_values": (2 * row + 8.0) * n}
+    dom = max(phase, key=phase.get)
+    kname = {"plan": "route_keys_kernel + radix pass + route_output_kernel", "validate": "route_validate_kernel",
+             "pack_ids": "pack_kernel<uint32_t,uint32_t>", "unpack_ids": "unpack_kernel<uint32_t,uint32_t>",
+             "pack_values": "pack_kernel<u32x4,uint32_t>", "unpack_values": "unpack_kernel<u32x4,uint32_t>",
+             "unpermute_values": "permute_kernel<u32x4,false>"}
+    achieved = alg[dom] / (phase[dom] / 1e3) / 1e9
+    elapsed = t1 - t0
+    result = {
+        "metric": ROUTE_METRIC,
+        "value": n * args.steps / elapsed,
+        "unit": "lookups/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": elapsed / args.steps * 1e3,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "owner routing, one request rank of world 64: 8x4096 Zipf(1.2) tokens, "
+                               "full-table row IDs, 320-B bf16 value rows; exchange = identity",
+                   "lookups_per_step": int(n), "world": Wd, "capacity": int(cap), "rotations": R},
+        "phases_ms": {k: round(v, 4) for k, v in phase.items()},
+        "roofline": {"kernel": kname[dom], "bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS,
+                     "unit": "GB/s", "frac": achieved / HBM_PEAK_GBPS,
+                     "traffic": counter_traffic("route.hip", "%s_route_counters.txt" % dom),
+                     "algorithmic_bytes_per_launch": alg[dom], "avg_launch_ms": phase[dom]},
+        "phase_gbps_algorithmic": {k: round(alg[k] / (phase[k] / 1e3) / 1e9, 1) for k in names},
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = route_cpu_baseline(wl)
+    print(json.dumps(result), flush=True)
+
+
 def main():
     args = parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -383,6 +548,9 @@ def main():
         del src, dst
     if args.workload == "ple":
         ple_main(args, dev)
+        return
+    if args.workload == "route":
+        route_main(args, dev)
         return
     wl = build_workload(args.workload, args.rotations, dev)
     torch.cuda.synchronize()

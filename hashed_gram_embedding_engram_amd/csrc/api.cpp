@@ -200,7 +200,6 @@ int engram_pack_fixed_capacity(const void* src, int64_t row_bytes, const int64_t
     for (int i = 0; i < 4; ++i)
         fill16[i] = (uint32_t)bytes[4 * i] | ((uint32_t)bytes[4 * i + 1] << 8) | ((uint32_t)bytes[4 * i + 2] << 16) |
                     ((uint32_t)bytes[4 * i + 3] << 24);
-    if (capacity == 0) return launch_result(engram::launch_status_init(status, stream));
     return launch_result(engram::launch_pack(src, row_bytes, split_sizes, world, capacity, fill16, dst, status, stream));
 }
 

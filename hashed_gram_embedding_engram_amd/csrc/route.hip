@@ -24,7 +24,8 @@
 namespace engram {
 namespace {
 
-constexpr int kMaxWorld = 255;  // owners fit one 8-bit digit, with 255 left for out-of-range IDs
+// World sizes are 1..255 (checked by the API): owners fit one 8-bit digit with
+// 255 left for out-of-range IDs, and one thread per count fits a block.
 
 struct RouteLayout {
     size_t keys_a, keys_b, vals_a, vals_b, hist, digit_total, counters, total;
@@ -108,98 +109,128 @@ __global__ __launch_bounds__(kBlock) void route_output_kernel(const uint32_t* __
     order[i] = v;
 }
 
-// Exclusive prefix of up to 255 int64 counts into LDS (offs[0..world]);
-// returns false (and leaves the block consistent) if any count is negative.
-__device__ bool load_segment_offsets(const int64_t* counts, int world, int64_t* offs) {
-    __shared__ int s_bad;
-    if (threadIdx.x == 0) {
-        int64_t acc = 0;
-        int bad = 0;
-        for (int w = 0; w < world; ++w) {
-            const int64_t c = counts[w];
-            if (c < 0) bad = 1;
-            offs[w] = acc;
-            acc += c < 0 ? 0 : c;
-        }
-        offs[world] = acc;
-        s_bad = bad;
+// Per-segment facts every block of segment w needs, from the counts (up to
+// 255, one per thread) by one block reduction:
+//   off      sum over v < w of the segment lengths before w
+//   total    sum over every segment
+//   any_bad  some count is negative
+// A segment's length is its count clamped below at 0 and, with clamp_cap,
+// above at the capacity.
+struct SegmentInfo {
+    int64_t off, total;
+    bool any_bad;
+};
+
+__device__ SegmentInfo segment_info(const int64_t* __restrict__ counts, int world, int w, int64_t capacity,
+                                    bool clamp_cap) {
+    __shared__ int64_t s_off[kBlock / 64], s_tot[kBlock / 64];
+    __shared__ int s_bad[kBlock / 64];
+    const int t = threadIdx.x, lane = t & 63, wv = t >> 6;
+    int64_t c = t < world ? counts[t] : 0;
+    const int bad = c < 0;
+    c = c < 0 ? 0 : (clamp_cap && c > capacity ? capacity : c);
+    int64_t before = t < w ? c : 0, all = c;
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) {
+        before += __shfl_xor(before, o, 64);
+        all += __shfl_xor(all, o, 64);
+    }
+    const int any = __any(bad);
+    if (lane == 0) {
+        s_off[wv] = before;
+        s_tot[wv] = all;
+        s_bad[wv] = any;
     }
     __syncthreads();
-    return s_bad == 0;
-}
-
-__device__ __forceinline__ int segment_of(const int64_t* offs, int world, int64_t i) {
-    int lo = 0, hi = world;  // offs[lo] <= i < offs[hi]
-    while (hi - lo > 1) {
-        const int mid = (lo + hi) >> 1;
-        if (offs[mid] <= i) lo = mid; else hi = mid;
+    SegmentInfo r{0, 0, false};
+#pragma unroll
+    for (int k = 0; k < kBlock / 64; ++k) {
+        r.off += s_off[k];
+        r.total += s_tot[k];
+        r.any_bad = r.any_bad || s_bad[k];
     }
-    return lo;
+    return r;
 }
 
+// Blocks are laid out as grid (x, world): blockIdx.y is the segment, x strides
+// over its units.  Segment offsets come from segment_info; unit indices are
+// 32-bit when a segment has fewer than 2^31 units (I = uint32_t), which keeps
+// the per-unit division cheap.
+
+// Segment w of sorted_ids must hold only owner w's IDs.  Counts that are
+// negative or add up to more than n are reported as n and nothing is checked.
+template <typename I>
 __global__ __launch_bounds__(kBlock) void route_validate_kernel(const int64_t* __restrict__ sorted_ids, int64_t n,
                                                                 const int64_t* __restrict__ send_counts, int world,
                                                                 int64_t local_rows, int64_t* __restrict__ status) {
-    __shared__ int64_t offs[kMaxWorld + 1];
-    const bool ok = load_segment_offsets(send_counts, world, offs);
-    if (!ok || offs[world] > n) {
-        if (blockIdx.x == 0 && threadIdx.x == 0) report_bad(status, n);
+    const int w = blockIdx.y;
+    const SegmentInfo si = segment_info(send_counts, world, w, 0, false);
+    if (si.any_bad || si.total > n) {
+        if (blockIdx.x == 0 && w == 0 && threadIdx.x == 0) report_bad(status, n);
         return;
     }
-    const int64_t total = offs[world];
-    for (int64_t i = (int64_t)blockIdx.x * kBlock + threadIdx.x; i < total; i += (int64_t)gridDim.x * kBlock) {
-        const int w = segment_of(offs, world, i);
-        const int64_t id = sorted_ids[i];
-        if (id < (int64_t)w * local_rows || id >= ((int64_t)w + 1) * local_rows) report_bad(status, i);
+    const I len = (I)send_counts[w];
+    const int64_t lo = (int64_t)w * local_rows, hi = lo + local_rows;
+    for (I e = (I)blockIdx.x * kBlock + threadIdx.x; e < len; e += (I)gridDim.x * kBlock) {
+        const int64_t id = sorted_ids[si.off + (int64_t)e];
+        if (id < lo || id >= hi) report_bad(status, si.off + (int64_t)e);
     }
 }
 
-// Copy unit: 16 bytes when rows allow it, else 4 bytes.
+// The fill of unit k of a row: `fill` is the fill element repeated over 16
+// bytes, and rows start on a multiple of the element, so a 4-byte unit at byte
+// 4k of the row takes word k mod 4 and a 16-byte unit takes all of it.
 template <typename U>
+__device__ __forceinline__ U fill_unit(u32x4 fill, uint32_t k);
+template <>
+__device__ __forceinline__ u32x4 fill_unit<u32x4>(u32x4 fill, uint32_t) { return fill; }
+template <>
+__device__ __forceinline__ uint32_t fill_unit<uint32_t>(u32x4 fill, uint32_t k) {
+    const uint32_t j = k & 3u;
+    return j == 0 ? fill[0] : (j == 1 ? fill[1] : (j == 2 ? fill[2] : fill[3]));
+}
+
+// Copy unit U: 16 bytes when rows allow it, else 4 bytes.  Segment w's
+// min(count, capacity) rows go to block w, the rest of the block is the fill.
+template <typename U, typename I>
 __global__ __launch_bounds__(kBlock) void pack_kernel(const U* __restrict__ src, int64_t row_units,
                                                       const int64_t* __restrict__ counts, int world, int64_t capacity,
-                                                      U fill, U* __restrict__ dst, int64_t* __restrict__ status) {
-    __shared__ int64_t offs[kMaxWorld + 1];
-    const bool ok = load_segment_offsets(counts, world, offs);
-    const int64_t total_units = (int64_t)world * capacity * row_units;
-    if (blockIdx.x == 0 && threadIdx.x < (unsigned)world) {
-        const int64_t c = counts[threadIdx.x];
-        if (c < 0 || c > capacity) report_bad(status, threadIdx.x);
-    }
-    for (int64_t e = (int64_t)blockIdx.x * kBlock + threadIdx.x; e < total_units; e += (int64_t)gridDim.x * kBlock) {
-        const int64_t row = e / row_units, k = e - row * row_units;
-        const int w = (int)(row / capacity);
-        const int64_t s = row - (int64_t)w * capacity;
-        const int64_t c = counts[w];
-        U v = fill;
-        if (ok && s < c) v = src[(offs[w] + s) * row_units + k];
-        dst[e] = v;
+                                                      u32x4 fill, U* __restrict__ dst, int64_t* __restrict__ status) {
+    const int w = blockIdx.y;
+    const SegmentInfo si = segment_info(counts, world, w, capacity, false);
+    const int64_t c = counts[w];
+    if (blockIdx.x == 0 && threadIdx.x == 0 && (c < 0 || c > capacity)) report_bad(status, w);
+    const I rows = (I)(c < 0 ? 0 : (c > capacity ? capacity : c));
+    const I units = (I)row_units, seg_units = (I)(capacity * row_units);
+    const U* __restrict__ s = src + si.off * row_units;
+    U* __restrict__ d = dst + (int64_t)w * capacity * row_units;
+    for (I e = (I)blockIdx.x * kBlock + threadIdx.x; e < seg_units; e += (I)gridDim.x * kBlock) {
+        const I r = e / units;
+        d[e] = r < rows ? s[e] : fill_unit<U>(fill, (uint32_t)(e - r * units));
     }
 }
 
-template <typename U>
+// Segment w's first min(count, capacity) rows of block w, appended in rank
+// order to the compact output; rows at or past dst_rows are dropped (status
+// world).
+template <typename U, typename I>
 __global__ __launch_bounds__(kBlock) void unpack_kernel(const U* __restrict__ src, int64_t row_units,
                                                         const int64_t* __restrict__ counts, int world, int64_t capacity,
                                                         U* __restrict__ dst, int64_t dst_rows,
                                                         int64_t* __restrict__ status) {
-    __shared__ int64_t offs[kMaxWorld + 1];
-    const bool ok = load_segment_offsets(counts, world, offs);
-    if (blockIdx.x == 0 && threadIdx.x <= (unsigned)world) {
-        if (threadIdx.x < (unsigned)world) {
-            const int64_t c = counts[threadIdx.x];
-            if (c < 0 || c > capacity) report_bad(status, threadIdx.x);
-        } else if (ok && offs[world] > dst_rows) {
-            report_bad(status, world);
-        }
+    const int w = blockIdx.y;
+    const SegmentInfo si = segment_info(counts, world, w, capacity, true);
+    const int64_t c = counts[w];
+    if (blockIdx.x == 0 && threadIdx.x == 0) {
+        if (c < 0 || c > capacity) report_bad(status, w);
+        if (w == world - 1 && si.total > dst_rows) report_bad(status, world);
     }
-    if (!ok) return;
-    const int64_t total_units = min(offs[world], dst_rows) * row_units;
-    for (int64_t e = (int64_t)blockIdx.x * kBlock + threadIdx.x; e < total_units; e += (int64_t)gridDim.x * kBlock) {
-        const int64_t i = e / row_units, k = e - i * row_units;
-        const int w = segment_of(offs, world, i);
-        const int64_t s = i - offs[w];
-        if (s < capacity) dst[e] = src[((int64_t)w * capacity + s) * row_units + k];
-    }
+    const int64_t rows = c < 0 ? 0 : (c > capacity ? capacity : c);
+    const int64_t fit = min(rows, max((int64_t)0, dst_rows - si.off));  // rows of this segment that fit
+    const I seg_units = (I)(fit * row_units);
+    const U* __restrict__ s = src + (int64_t)w * capacity * row_units;
+    U* __restrict__ d = dst + si.off * row_units;
+    for (I e = (I)blockIdx.x * kBlock + threadIdx.x; e < seg_units; e += (I)gridDim.x * kBlock) d[e] = s[e];
 }
 
 // dst[i] = src[order[i]] (gather) or dst[order[i]] = src[i] (scatter); an
@@ -257,14 +288,31 @@ hipError_t launch_route_plan(const int64_t* ids, int64_t n, int64_t local_rows, 
     return hipGetLastError();
 }
 
+// x blocks per segment for `units` units: enough to cover them, at most 4096 (the rest by striding).
+dim3 segment_grid(int64_t units, int world) {
+    int64_t x = (units + kBlock - 1) / kBlock;
+    x = x < 1 ? 1 : (x > 4096 ? 4096 : x);
+    return dim3((unsigned)x, (unsigned)world);
+}
+
 hipError_t launch_route_validate(const int64_t* sorted_ids, int64_t n, const int64_t* send_counts, int world,
                                  int64_t local_rows, int64_t* status, hipStream_t stream) {
     hipError_t err = launch_status_init(status, stream);
     if (err != hipSuccess) return err;
-    hipLaunchKernelGGL(route_validate_kernel, dim3(grid_for(n)), dim3(kBlock), 0, stream, sorted_ids, n, send_counts,
-                       world, local_rows, status);
+    // A segment holds at most n IDs when the counts are consistent (n < 2^31 by the API).
+    hipLaunchKernelGGL((route_validate_kernel<uint32_t>), segment_grid(n / world + 1, world), dim3(kBlock), 0, stream,
+                       sorted_ids, n, send_counts, world, local_rows, status);
     return hipGetLastError();
 }
+
+#define ENGRAM_SEGMENT_LAUNCH(KERNEL, U, UNITS, ...)                                                       \
+    do {                                                                                                   \
+        const dim3 grid = segment_grid(UNITS, world);                                                     \
+        if ((UNITS) < ((int64_t)1 << 31) - (int64_t)grid.x * kBlock)                                       \
+            hipLaunchKernelGGL((KERNEL<U, uint32_t>), grid, dim3(kBlock), 0, stream, __VA_ARGS__);        \
+        else                                                                                               \
+            hipLaunchKernelGGL((KERNEL<U, uint64_t>), grid, dim3(kBlock), 0, stream, __VA_ARGS__);        \
+    } while (0)
 
 hipError_t launch_pack(const void* src, int64_t row_bytes, const int64_t* counts, int world, int64_t capacity,
                        const uint32_t fill16[4], void* dst, int64_t* status, hipStream_t stream) {
@@ -274,13 +322,13 @@ hipError_t launch_pack(const void* src, int64_t row_bytes, const int64_t* counts
     if (wide) {
         const int64_t units = row_bytes / 16;
         const u32x4 f = {fill16[0], fill16[1], fill16[2], fill16[3]};
-        hipLaunchKernelGGL((pack_kernel<u32x4>), dim3(grid_for((int64_t)world * capacity * units)), dim3(kBlock), 0,
-                           stream, (const u32x4*)src, units, counts, world, capacity, f, (u32x4*)dst, status);
+        ENGRAM_SEGMENT_LAUNCH(pack_kernel, u32x4, capacity * units, (const u32x4*)src, units, counts, world, capacity,
+                              f, (u32x4*)dst, status);
     } else {
         const int64_t units = row_bytes / 4;
-        hipLaunchKernelGGL((pack_kernel<uint32_t>), dim3(grid_for((int64_t)world * capacity * units)), dim3(kBlock),
-                           0, stream, (const uint32_t*)src, units, counts, world, capacity, fill16[0],
-                           (uint32_t*)dst, status);
+        const u32x4 f = {fill16[0], fill16[1], fill16[2], fill16[3]};
+        ENGRAM_SEGMENT_LAUNCH(pack_kernel, uint32_t, capacity * units, (const uint32_t*)src, units, counts, world,
+                              capacity, f, (uint32_t*)dst, status);
     }
     return hipGetLastError();
 }
@@ -289,16 +337,16 @@ hipError_t launch_unpack(const void* src, int64_t row_bytes, const int64_t* coun
                          void* dst, int64_t dst_rows, int64_t* status, hipStream_t stream) {
     hipError_t err = launch_status_init(status, stream);
     if (err != hipSuccess) return err;
-    const int64_t max_rows = dst_rows < (int64_t)world * capacity ? dst_rows : (int64_t)world * capacity;
     const bool wide = row_bytes % 16 == 0 && ((uintptr_t)src % 16) == 0 && ((uintptr_t)dst % 16) == 0;
+    const int64_t rows = capacity < dst_rows ? capacity : dst_rows;  // at most per segment
     if (wide) {
         const int64_t units = row_bytes / 16;
-        hipLaunchKernelGGL((unpack_kernel<u32x4>), dim3(grid_for(max_rows * units)), dim3(kBlock), 0, stream,
-                           (const u32x4*)src, units, counts, world, capacity, (u32x4*)dst, dst_rows, status);
+        ENGRAM_SEGMENT_LAUNCH(unpack_kernel, u32x4, rows * units, (const u32x4*)src, units, counts, world, capacity,
+                              (u32x4*)dst, dst_rows, status);
     } else {
         const int64_t units = row_bytes / 4;
-        hipLaunchKernelGGL((unpack_kernel<uint32_t>), dim3(grid_for(max_rows * units)), dim3(kBlock), 0, stream,
-                           (const uint32_t*)src, units, counts, world, capacity, (uint32_t*)dst, dst_rows, status);
+        ENGRAM_SEGMENT_LAUNCH(unpack_kernel, uint32_t, rows * units, (const uint32_t*)src, units, counts, world,
+                              capacity, (uint32_t*)dst, dst_rows, status);
     }
     return hipGetLastError();
 }

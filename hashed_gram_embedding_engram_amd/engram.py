@@ -305,16 +305,21 @@ def _row_bytes(t):
     return (t.numel() // max(t.shape[0], 1)) * t.element_size() if t.dim() > 1 else t.element_size()
 
 
-def engram_route_plan(global_ids, num_embeddings, world, status=None, stream=None):
-    """Group global row IDs by owner.  Returns (sorted_ids [n], order [n], send_counts [world])."""
+def engram_route_plan(global_ids, num_embeddings, world, status=None, workspace=None, out=None, stream=None):
+    """Group global row IDs by owner.  Returns (sorted_ids [n], order [n], send_counts [world]);
+    ``out`` may supply those three buffers."""
     lib = _route_lib()
     ids = global_ids.reshape(-1)
     n = ids.numel()
     dev = ids.device
-    sorted_ids = torch.empty(n, dtype=torch.int64, device=dev)
-    order = torch.empty(n, dtype=torch.int64, device=dev)
-    counts = torch.empty(world, dtype=torch.int64, device=dev)
-    ws = torch.empty(max(int(lib.engram_route_workspace(n)), 256), dtype=torch.uint8, device=dev)
+    if out is not None:
+        sorted_ids, order, counts = out
+    else:
+        sorted_ids = torch.empty(n, dtype=torch.int64, device=dev)
+        order = torch.empty(n, dtype=torch.int64, device=dev)
+        counts = torch.empty(world, dtype=torch.int64, device=dev)
+    ws = workspace if workspace is not None else \
+        torch.empty(max(int(lib.engram_route_workspace(n)), 256), dtype=torch.uint8, device=dev)
     _check(lib.engram_route_plan(_dev_ptr(ids, "global_ids", torch.int64), n, num_embeddings, world,
                                  _dev_ptr(sorted_ids, "sorted_ids"), _dev_ptr(order, "order"),
                                  _dev_ptr(counts, "send_counts"), _dev_ptr(ws, "workspace"), ws.numel(),
@@ -332,13 +337,13 @@ def engram_route_validate(sorted_ids, send_counts, num_embeddings, world, stream
     return status
 
 
-def engram_pack_fixed_capacity(src, split_sizes, world, capacity, fill=0, status=None, stream=None):
+def engram_pack_fixed_capacity(src, split_sizes, world, capacity, fill=0, status=None, out=None, stream=None):
     """Compact rows [sum(split_sizes), ...] -> [world, capacity, ...] padded with ``fill``."""
     lib = _route_lib()
     row_shape = tuple(src.shape[1:])
     esize = src.element_size()
     row_bytes = esize * int(torch.Size(row_shape).numel()) if row_shape else esize
-    dst = torch.empty((world, capacity) + row_shape, dtype=src.dtype, device=src.device)
+    dst = torch.empty((world, capacity) + row_shape, dtype=src.dtype, device=src.device) if out is None else out
     fill_t = torch.tensor([fill], dtype=src.dtype)
     fill_bytes = (ctypes.c_ubyte * esize).from_buffer_copy(fill_t.view(torch.uint8).numpy().tobytes())
     _check(lib.engram_pack_fixed_capacity(_dev_ptr(src, "src"), row_bytes,
@@ -349,14 +354,14 @@ def engram_pack_fixed_capacity(src, split_sizes, world, capacity, fill=0, status
     return dst
 
 
-def engram_unpack_fixed_capacity(src, split_sizes, dst_rows, status=None, stream=None):
+def engram_unpack_fixed_capacity(src, split_sizes, dst_rows, status=None, out=None, stream=None):
     """[world, capacity, ...] -> compact [dst_rows, ...] (rank order; rows past the counts untouched)."""
     lib = _route_lib()
     world, capacity = src.shape[0], src.shape[1]
     row_shape = tuple(src.shape[2:])
     esize = src.element_size()
     row_bytes = esize * int(torch.Size(row_shape).numel()) if row_shape else esize
-    dst = torch.empty((dst_rows,) + row_shape, dtype=src.dtype, device=src.device)
+    dst = torch.empty((dst_rows,) + row_shape, dtype=src.dtype, device=src.device) if out is None else out
     _check(lib.engram_unpack_fixed_capacity(_dev_ptr(src, "src"), row_bytes,
                                             _dev_ptr(split_sizes, "split_sizes", torch.int64), world, capacity,
                                             _dev_ptr(dst, "dst"), dst_rows, _dev_ptr(status, "status", torch.int64),
@@ -364,25 +369,25 @@ def engram_unpack_fixed_capacity(src, split_sizes, dst_rows, status=None, stream
     return dst
 
 
-def _permute(src, order, gather, stream):
+def _permute(src, order, gather, stream, out=None):
     lib = _route_lib()
     n = order.numel()
     row_bytes = src[0].numel() * src.element_size() if src.dim() > 1 else src.element_size()
-    dst = torch.empty_like(src)
+    dst = torch.empty_like(src) if out is None else out
     fn = lib.engram_permute_rows if gather else lib.engram_unpermute_rows
     _check(fn(_dev_ptr(src, "src"), row_bytes, _dev_ptr(order, "order", torch.int64), n, _dev_ptr(dst, "dst"),
               _stream_handle(stream)), "engram_permute_rows" if gather else "engram_unpermute_rows")
     return dst
 
 
-def engram_permute_rows(src, order, stream=None):
+def engram_permute_rows(src, order, out=None, stream=None):
     """dst[i] = src[order[i]]."""
-    return _permute(src, order, True, stream)
+    return _permute(src, order, True, stream, out)
 
 
-def engram_unpermute_rows(src, order, stream=None):
+def engram_unpermute_rows(src, order, out=None, stream=None):
     """dst[order[i]] = src[i]."""
-    return _permute(src, order, False, stream)
+    return _permute(src, order, False, stream, out)
 
 
 # ---- PLE short convolution and grouped RMSNorm --------------------------------

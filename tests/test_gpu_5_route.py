@@ -93,6 +93,35 @@ def test_pack_capacity_overflow_reported():
     assert out.cpu().tolist() == [0, 1, 2, 3, 4]
 
 
+def test_pack_unpack_bad_counts_match_oracle():
+    """A negative count and a count above capacity: both are reported (lowest
+    rank), and the rows written equal the oracle's."""
+    rng = np.random.default_rng(11)
+    world, capacity = 6, 40
+    counts = np.array([12, -3, 55, 0, 40, 7], dtype=np.int64)
+    m = int(np.maximum(counts, 0).sum())
+    src = torch.from_numpy(rng.integers(-1000, 1000, size=(m, 3)).astype(np.int64)).cuda()
+    c = torch.from_numpy(counts).cuda()
+    status = torch.empty((), dtype=torch.int64, device="cuda")
+    packed = E.engram_pack_fixed_capacity(src, c, world, capacity, fill=-9, status=status)
+    ref, rbad = RR.pack(src.cpu().numpy(), counts, world, capacity, -9)
+    assert np.array_equal(packed.cpu().numpy(), ref) and int(status.item()) == rbad == 1
+    kept = int(np.clip(counts, 0, capacity).sum())
+    back = E.engram_unpack_fixed_capacity(packed, c, kept, status=status)
+    assert int(status.item()) == 1
+    assert np.array_equal(back.cpu().numpy(), RR.unpack(ref, counts, kept))
+    short = E.engram_unpack_fixed_capacity(packed, c, kept - 5, status=status)
+    assert int(status.item()) == 1          # rank errors come before the overflow (world)
+    assert np.array_equal(short.cpu().numpy(), RR.unpack(ref, counts, kept - 5))
+
+
+def test_pack_zero_capacity_reports_counts():
+    status = torch.empty((), dtype=torch.int64, device="cuda")
+    src = torch.arange(4, dtype=torch.int64, device="cuda")
+    out = E.engram_pack_fixed_capacity(src, torch.tensor([0, 3, 1], device="cuda"), 3, 0, fill=0, status=status)
+    assert out.shape == (3, 0) and int(status.item()) == 1
+
+
 def test_permute_unpermute():
     rng = np.random.default_rng(6)
     x = torch.from_numpy(rng.standard_normal((777, 5)).astype(np.float32)).cuda()
