@@ -1,9 +1,13 @@
 /*
  * engram.h — C ABI of the Engram n-gram embedding hot path on MI355X (gfx950).
  *
- * Three calls carry the whole path: raw token IDs -> hashed head rows
+ * Three calls carry the lookup path: raw token IDs -> hashed head rows
  * (engram_hash), head rows -> table values (engram_gather), and output
- * gradients -> per-row gradient sums (engram_scatter_add).
+ * gradients -> per-row gradient sums (engram_scatter_add).  Around them: the
+ * single-GPU half of the row-owner exchange (engram_route_*, pack/unpack,
+ * permute) and the PLE layer's causal short convolution and grouped RMSNorm
+ * (engram_short_conv*, engram_grouped_rms_norm*), each declared with the
+ * passage that defines it.
  *
  * Passages defining the operations ("engram API page" = the page titled
  * nemo_automodel.components.models.qwen3_8_flash_next.engram; "model-coverage
