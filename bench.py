@@ -606,6 +606,28 @@ def main():
     dbytes, dms, dname, dsrc = kern[dom]
     achieved = dbytes / (dms / 1e3) / 1e9
     traffic = counter_traffic(dsrc, "%s_%s_counters.txt" % (dom, args.workload))
+
+    # Three GB/s figures per kernel: per-lookup bytes (above); compulsory
+    # bytes, which count each distinct table row's read once (the gather reads
+    # (U/L) * 320 + 328 B per lookup); and the HBM bytes the committed
+    # rocprofv3 counters measured for that kernel (null when they were taken
+    # on other kernel sources).
+    import torch as _t
+    u_fwd = int(_t.unique(b0["rows"].reshape(-1)).numel())
+    compulsory = {"gather": 320.0 * u_fwd + 328.0 * n_avg}
+    if wl["backward"]:
+        compulsory["scatter_apply"] = apply_bytes   # every gradient row is read once already
+    gbps = {}
+    for k, (byts, ms, _, src) in kern.items():
+        hbm = counter_traffic(src, "%s_%s_counters.txt" % (k, args.workload))
+        gbps[k] = {"per_lookup": round(byts / (ms / 1e3) / 1e9, 1),
+                   "compulsory": round(compulsory[k] / (ms / 1e3) / 1e9, 1),
+                   "counters": None if hbm is None else round(hbm / (ms / 1e3) / 1e9, 1)}
+    # Step time distribution from the events (first to last event of a step).
+    last = 6 if wl["backward"] else 2
+    step_ms = sorted(e[0].elapsed_time(e[last]) for e in evs)
+    pct = lambda q: step_ms[min(len(step_ms) - 1, int(q * (len(step_ms) - 1) + 0.5))]
+    fwd_ms = phase["hash"] + phase["gather"]
     result = {
         "metric": METRIC,
         "value": lookups / elapsed,
@@ -633,6 +655,10 @@ def main():
                      "unit": "GB/s", "frac": achieved / HBM_PEAK_GBPS, "traffic": traffic,
                      "algorithmic_bytes_per_launch": dbytes, "avg_launch_ms": dms},
         "phase_gbps_algorithmic": {k: round(v[0] / (v[1] / 1e3) / 1e9, 1) for k, v in kern.items()},
+        "phase_gbps": gbps,
+        "distinct_rows_forward_rotation0": u_fwd,
+        "step_ms_events": {"p10": round(pct(0.1), 4), "p50": round(pct(0.5), 4), "p90": round(pct(0.9), 4)},
+        "forward_lookups_per_s": n_avg / (fwd_ms / 1e3),
         "cpu_baseline": None,
     }
     if not args.no_cpu_baseline:

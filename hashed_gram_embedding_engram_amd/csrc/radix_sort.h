@@ -107,7 +107,8 @@ __global__ __launch_bounds__(kBlock) void digit_scan_kernel(uint32_t* __restrict
     if (threadIdx.x == 0) digit_total[blockIdx.x] = running;
 }
 
-// One stable scatter pass of the LSD radix sort.
+// One stable scatter pass of the LSD radix sort.  vals_in == nullptr means
+// the value of entry e is e itself.
 __global__ __launch_bounds__(kBlock) void downsweep_kernel(const uint32_t* __restrict__ keys_in,
                                                            const uint32_t* __restrict__ vals_in,
                                                            uint32_t* __restrict__ keys_out,
@@ -132,7 +133,7 @@ __global__ __launch_bounds__(kBlock) void downsweep_kernel(const uint32_t* __res
     for (int it = 0; it < kItems; ++it) {
         const uint32_t e = min(base + (uint32_t)it * 64 + (uint32_t)lane, n - 1);
         key[it] = keys_in[e];
-        val[it] = vals_in[e];
+        val[it] = vals_in ? vals_in[e] : e;  // no values: the input order itself (a first pass)
     }
     // Rank every key among the equal digits before it in this wave's span:
     // items are visited in index order and the lowest lane of each digit group

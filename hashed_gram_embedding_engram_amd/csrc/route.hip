@@ -28,7 +28,7 @@ namespace {
 // 255 left for out-of-range IDs, and one thread per count fits a block.
 
 struct RouteLayout {
-    size_t keys_a, keys_b, vals_a, vals_b, hist, digit_total, counters, total;
+    size_t keys_a, keys_b, vals_b, hist, digit_total, counters, total;
     int64_t num_tiles;
 };
 
@@ -39,7 +39,6 @@ RouteLayout route_layout(int64_t n) {
     auto take = [&](size_t bytes) { size_t at = off; off = (off + bytes + 255) & ~(size_t)255; return at; };
     L.keys_a = take(4 * (size_t)n);
     L.keys_b = take(4 * (size_t)n);
-    L.vals_a = take(4 * (size_t)n);
     L.vals_b = take(4 * (size_t)n);
     L.hist = take(4 * (size_t)kRadix * (size_t)L.num_tiles);
     L.digit_total = take(4 * kRadix);
@@ -57,11 +56,11 @@ __global__ void route_init_kernel(int64_t* status, uint32_t* counters) {
     counters[0] = 0;
 }
 
-// Owner keys (sentinel `world` for an ID outside the table), request indices,
-// and the per-tile owner histogram.
+// Owner keys (sentinel `world` for an ID outside the table) and the per-tile
+// owner histogram; the request index of each key is its position.
 __global__ __launch_bounds__(kBlock) void route_keys_kernel(const int64_t* __restrict__ ids, uint32_t n,
                                                             int64_t local_rows, int world, uint32_t* __restrict__ keys,
-                                                            uint32_t* __restrict__ vals, uint32_t* __restrict__ hist,
+                                                            uint32_t* __restrict__ hist,
                                                             uint32_t num_tiles, int64_t* __restrict__ status) {
     __shared__ uint32_t s_cnt[kBlock / 64][kRadix];
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
@@ -83,7 +82,6 @@ __global__ __launch_bounds__(kBlock) void route_keys_kernel(const int64_t* __res
             else
                 report_bad(status, e);
             keys[e] = key;
-            vals[e] = e;
             atomicAdd(&s_cnt[w][key], 1u);
         }
     }
@@ -277,12 +275,12 @@ hipError_t launch_route_plan(const int64_t* ids, int64_t n, int64_t local_rows, 
     uint32_t* hist = (uint32_t*)(ws + L.hist);
     uint32_t* digit_total = (uint32_t*)(ws + L.digit_total);
     uint32_t *ka = (uint32_t*)(ws + L.keys_a), *kb = (uint32_t*)(ws + L.keys_b);
-    uint32_t *va = (uint32_t*)(ws + L.vals_a), *vb = (uint32_t*)(ws + L.vals_b);
-    hipLaunchKernelGGL(route_keys_kernel, dim3(tiles), dim3(kBlock), 0, stream, ids, nn, local_rows, world, ka, va,
-                       hist, tiles, status);
+    uint32_t* vb = (uint32_t*)(ws + L.vals_b);
+    hipLaunchKernelGGL(route_keys_kernel, dim3(tiles), dim3(kBlock), 0, stream, ids, nn, local_rows, world, ka, hist,
+                       tiles, status);
     hipLaunchKernelGGL(digit_scan_kernel, dim3(kRadix), dim3(kBlock), 0, stream, hist, tiles, digit_total);
-    hipLaunchKernelGGL(downsweep_kernel, dim3(tiles), dim3(kBlock), 0, stream, ka, va, kb, vb, nn, 0, hist,
-                       digit_total, tiles);
+    hipLaunchKernelGGL(downsweep_kernel, dim3(tiles), dim3(kBlock), 0, stream, ka, (const uint32_t*)nullptr, kb, vb,
+                       nn, 0, hist, digit_total, tiles);
     hipLaunchKernelGGL(route_output_kernel, dim3((nn + kBlock - 1) / kBlock), dim3(kBlock), 0, stream, vb, ids, nn,
                        world, digit_total, sorted_ids, order, send_counts);
     return hipGetLastError();

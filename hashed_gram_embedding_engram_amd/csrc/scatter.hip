@@ -94,12 +94,13 @@ __global__ void scatter_init_kernel(int64_t* status, uint32_t* counters, int64_t
 
 // Tile histograms count with LDS atomics into one sub-histogram per wave
 // (summed at the end), which keeps same-address conflicts inside a wave.
-// Step 1: keys, lookup indices, digit-0 tile histograms, in-range count.
+// Step 1: keys, digit-0 tile histograms, in-range count.  A key's lookup
+// index is its position, so the first sort pass reads no value array.
 __global__ __launch_bounds__(kBlock) void keys_kernel(const int64_t* __restrict__ rows, uint32_t n,
                                                       int64_t row_begin, uint64_t num_rows,
-                                                      uint32_t* __restrict__ keys, uint32_t* __restrict__ vals,
-                                                      uint32_t* __restrict__ hist, uint32_t num_tiles,
-                                                      int64_t* __restrict__ status, uint32_t* __restrict__ counters) {
+                                                      uint32_t* __restrict__ keys, uint32_t* __restrict__ hist,
+                                                      uint32_t num_tiles, int64_t* __restrict__ status,
+                                                      uint32_t* __restrict__ counters) {
     __shared__ uint32_t s_cnt[kBlock / 64][kRadix];
     __shared__ uint32_t s_valid;
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
@@ -128,7 +129,6 @@ __global__ __launch_bounds__(kBlock) void keys_kernel(const int64_t* __restrict_
                 report_bad(status, e);
             }
             keys[e] = key;
-            vals[e] = e;
             atomicAdd(&s_cnt[w][key & 0xFFu], 1u);
         }
     }
@@ -729,7 +729,7 @@ hipError_t launch_scatter_plan(const int64_t* rows, int64_t n, int64_t row_begin
         v_cur = (uint32_t*)(ws + L.spare_vals); v_nxt = (uint32_t*)(ws + L.sorted_vals);
     }
     hipLaunchKernelGGL(keys_kernel, dim3(tiles), dim3(kBlock), 0, stream, rows, nn, row_begin, (uint64_t)num_rows,
-                       k_cur, v_cur, hist, tiles, status, counters);
+                       k_cur, hist, tiles, status, counters);
     if ((err = hipGetLastError()) != hipSuccess) return err;
     for (int p = 0; p < passes; ++p) {
         const int shift = 8 * p;
@@ -738,8 +738,9 @@ hipError_t launch_scatter_plan(const int64_t* rows, int64_t n, int64_t row_begin
             if ((err = hipGetLastError()) != hipSuccess) return err;
         }
         hipLaunchKernelGGL(digit_scan_kernel, dim3(kRadix), dim3(kBlock), 0, stream, hist, tiles, digit_total);
-        hipLaunchKernelGGL(downsweep_kernel, dim3(tiles), dim3(kBlock), 0, stream, k_cur, v_cur, k_nxt, v_nxt, nn,
-                           shift, hist, digit_total, tiles);
+        hipLaunchKernelGGL(downsweep_kernel, dim3(tiles), dim3(kBlock), 0, stream, k_cur,
+                           p == 0 ? (const uint32_t*)nullptr : v_cur, k_nxt, v_nxt, nn, shift, hist, digit_total,
+                           tiles);
         if ((err = hipGetLastError()) != hipSuccess) return err;
         uint32_t* t = k_cur; k_cur = k_nxt; k_nxt = t;
         t = v_cur; v_cur = v_nxt; v_nxt = t;

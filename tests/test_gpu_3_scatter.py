@@ -249,3 +249,64 @@ def test_many_long_runs():
     got, _ = run_dense(rows, dy, 200000)
     ref, _ = c_oracle.scatter_add_dense(rows, to_host(dy), 200000)
     assert_close_to_fp64(got, ref, "dense many long runs")
+
+
+# ---- Over a million lookups: 256 or more sort tiles, wide key ranges, rows
+# repeated hundreds of thousands of times next to uniform ones.  Narrow rows
+# (dim 8) keep the oracle's work small; the sort does not depend on the width.
+LARGE_N = (1 << 20) + 4097
+
+
+@pytest.mark.parametrize("num_rows", [1000, 70001, 5_000_024, 320_001_536, 0xFFFFFFFE])
+def test_large_key_widths(num_rows):
+    rng = np.random.default_rng(num_rows % 977)
+    n = LARGE_N
+    hot = rng.integers(0, num_rows, size=64)
+    rows = np.where(rng.random(n) < 0.3, hot[rng.integers(0, 64, size=n)], rng.integers(0, num_rows, size=n))
+    check_compact(rows.astype(np.int64), grads(n, dim=8, seed=21), num_rows)
+
+
+def test_large_hot_rows():
+    """One row repeated 300,000 times, one 25,000 times and 60,000 rows packed
+    into one 2^20-row range, among uniform rows; out-of-range rows too."""
+    rng = np.random.default_rng(22)
+    R = 320_001_536
+    n = LARGE_N + 200_000
+    rows = rng.integers(0, R, size=n).astype(np.int64)
+    idx = rng.permutation(n)
+    rows[idx[:300_000]] = 123_456_789
+    rows[idx[300_000:325_000]] = 5
+    narrow = rng.integers(7 << 20, (7 << 20) + (1 << 20), size=60_000)   # 60,000 rows within 2^20 of each other
+    rows[idx[325_000:385_000]] = narrow
+    rows[idx[385_000:385_010]] = [-1, R, R + 5, 1 << 40, -(1 << 62), R, R, -3, R + 1, 2 * R]
+    first_bad = int(np.sort(idx[385_000:385_010])[0])
+    dy = grads(n, dim=8, seed=22)
+    ur, ug, bad, _ = run_compact(rows, dy, R)
+    rur, rug, rbad = c_oracle.scatter_add_compact(rows, to_host(dy), R, 0)
+    assert bad == rbad == first_bad
+    assert np.array_equal(ur, rur)
+    assert_close_to_fp64(ug, rug, "large n, hot rows")
+
+
+def test_large_dense_and_deterministic():
+    rng = np.random.default_rng(23)
+    R = 150_000
+    n = LARGE_N
+    rows = (rng.zipf(1.1, size=n) % R).astype(np.int64)
+    dy = grads(n, dim=160, seed=23)
+    a = run_compact(rows, dy, R)
+    b = run_compact(rows, dy, R)
+    assert np.array_equal(a[0], b[0]) and np.array_equal(a[1].view(np.uint32), b[1].view(np.uint32))
+    rur, rug, _ = c_oracle.scatter_add_compact(rows, to_host(dy), R, 0)
+    assert np.array_equal(a[0], rur)
+    assert_close_to_fp64(a[1], rug, "large n, dim 160")
+    got, bad = run_dense(rows, dy, R)
+    assert bad == -1
+    assert np.array_equal(got[a[0]].view(np.uint32), a[1].view(np.uint32))   # the two forms agree bit for bit
+
+
+def test_large_all_one_row():
+    """Every lookup on one row: every sort pass leaves the order as it is."""
+    n = LARGE_N
+    dy = grads(n, dim=8, seed=24)
+    check_compact(np.full(n, 99_999, dtype=np.int64), dy, 320_001_536)
