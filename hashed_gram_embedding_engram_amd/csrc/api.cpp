@@ -4,6 +4,8 @@
 // work is enqueued.
 #include "engram.h"
 
+#include <initializer_list>
+
 #include "engram_internal.h"
 
 namespace {
@@ -17,6 +19,11 @@ bool row_bytes_ok(int32_t dtype, int32_t dim, int* elem_bytes) {
 }
 
 bool dtype_ok(int32_t dtype) { return dtype == ENGRAM_F32 || dtype == ENGRAM_BF16; }
+
+// Device arrays must be aligned to their access width: 16 bytes for row data
+// (loaded and stored as 16-byte chunks), 8 for int64 and fp64, 4 for fp32.
+// NULL passes (the callers check which pointers are required).
+bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
 
 int launch_result(hipError_t e) { return e == hipSuccess ? ENGRAM_OK : ENGRAM_ELAUNCH; }
 
@@ -53,7 +60,7 @@ int hash_common(const int64_t* tokens, int64_t batch, int64_t seq_len, int64_t s
     if (rc != ENGRAM_OK) return rc;
     const int64_t width = seq_end - seq_begin;
     if (batch == 0 || width == 0) return ENGRAM_OK;
-    if (!tokens || !rows_out) return ENGRAM_EINVAL;
+    if (!tokens || !rows_out || !aligned(tokens, 8) || !aligned(rows_out, 8)) return ENGRAM_EINVAL;
     if (batch > INT64_MAX / width / ENGRAM_MAX_HEADS || batch * width > ((int64_t)1 << 40)) return ENGRAM_EINVAL;
     return launch_result(engram::launch_hash(tokens, batch, seq_len, seq_begin, seq_end, p, rows_out, stream));
 }
@@ -80,6 +87,7 @@ int engram_gather(const void* table, int32_t dtype, int64_t row_begin, int64_t n
     if (n < 0 || num_rows < 0 || row_begin < 0) return ENGRAM_EINVAL;
     if (n > ((int64_t)1 << 40)) return ENGRAM_EINVAL;
     if (n > 0 && (!rows || !out || (num_rows > 0 && !table))) return ENGRAM_EINVAL;
+    if (!aligned(table, 16) || !aligned(out, 16) || !aligned(rows, 8) || !aligned(status, 8)) return ENGRAM_EINVAL;
     return launch_result(engram::launch_gather(table, eb, row_begin, num_rows, dim, rows, n, out, status, stream));
 }
 
@@ -113,6 +121,8 @@ int engram_scatter_add_plan(const int64_t* rows, int64_t n, int64_t row_begin, i
     int rc = scatter_check_common(ENGRAM_F32, dim, n, row_begin, num_rows, &eb);
     if (rc != ENGRAM_OK) return rc;
     if (n > 0 && !rows) return ENGRAM_EINVAL;
+    if (!aligned(rows, 8) || !aligned(uniq_rows, 8) || !aligned(num_uniq, 8) || !aligned(status, 8))
+        return ENGRAM_EINVAL;
     if ((rc = workspace_check(workspace, workspace_bytes, n, num_rows, dim)) != ENGRAM_OK) return rc;
     return launch_result(engram::launch_scatter_plan(rows, n, row_begin, num_rows, dim, uniq_rows, num_uniq,
                                                      workspace, status, stream));
@@ -126,6 +136,7 @@ int engram_scatter_add_apply(const void* grad_out, int32_t dtype, int32_t dim, i
     if (rc != ENGRAM_OK) return rc;
     if ((grad_dense != nullptr) == (uniq_grad != nullptr)) return ENGRAM_EINVAL;
     if (n > 0 && !grad_out) return ENGRAM_EINVAL;
+    if (!aligned(grad_out, 16) || !aligned(grad_dense, 16) || !aligned(uniq_grad, 16)) return ENGRAM_EINVAL;
     if ((rc = workspace_check(workspace, workspace_bytes, n, num_rows, dim)) != ENGRAM_OK) return rc;
     return launch_result(engram::launch_scatter_apply(grad_out, eb, dim, n, num_rows, grad_dense, uniq_grad,
                                                       workspace, stream));
@@ -143,6 +154,9 @@ int engram_scatter_add(const int64_t* rows, int64_t n, const void* grad_out, int
     if (dense == compact) return ENGRAM_EINVAL;
     if (compact && (!uniq_rows || !uniq_grad || !num_uniq)) return ENGRAM_EINVAL;
     if (n > 0 && (!rows || !grad_out)) return ENGRAM_EINVAL;
+    if (!aligned(rows, 8) || !aligned(grad_out, 16) || !aligned(grad_dense, 16) || !aligned(uniq_grad, 16) ||
+        !aligned(uniq_rows, 8) || !aligned(num_uniq, 8) || !aligned(status, 8))
+        return ENGRAM_EINVAL;
     if ((rc = workspace_check(workspace, workspace_bytes, n, num_rows, dim)) != ENGRAM_OK) return rc;
     hipError_t e = engram::launch_scatter_plan(rows, n, row_begin, num_rows, dim, uniq_rows, num_uniq, workspace,
                                                status, stream);
@@ -172,6 +186,9 @@ int engram_route_plan(const int64_t* global_ids, int64_t n, int64_t num_embeddin
     if (route_geometry(num_embeddings, world, &local_rows) != ENGRAM_OK) return ENGRAM_EINVAL;
     if (n < 0 || n >= ((int64_t)1 << 31) || !send_counts) return ENGRAM_EINVAL;
     if (n > 0 && (!global_ids || !sorted_ids || !order)) return ENGRAM_EINVAL;
+    if (!aligned(global_ids, 8) || !aligned(sorted_ids, 8) || !aligned(order, 8) || !aligned(send_counts, 8) ||
+        !aligned(status, 8))
+        return ENGRAM_EINVAL;
     if (((uintptr_t)workspace & 255) != 0 || !workspace || workspace_bytes < engram::route_workspace_bytes(n))
         return ENGRAM_EWORKSPACE;
     return launch_result(engram::launch_route_plan(global_ids, n, local_rows, world, sorted_ids, order, send_counts,
@@ -183,6 +200,7 @@ int engram_route_validate(const int64_t* sorted_ids, int64_t n, const int64_t* s
     int64_t local_rows;
     if (route_geometry(num_embeddings, world, &local_rows) != ENGRAM_OK) return ENGRAM_EINVAL;
     if (n < 0 || !send_counts || !status || (n > 0 && !sorted_ids)) return ENGRAM_EINVAL;
+    if (!aligned(sorted_ids, 8) || !aligned(send_counts, 8) || !aligned(status, 8)) return ENGRAM_EINVAL;
     return launch_result(engram::launch_route_validate(sorted_ids, n, send_counts, world, local_rows, status, stream));
 }
 
@@ -193,6 +211,7 @@ int engram_pack_fixed_capacity(const void* src, int64_t row_bytes, const int64_t
     if (!(fill_bytes == 1 || fill_bytes == 2 || fill_bytes == 4 || fill_bytes == 8) || !fill) return ENGRAM_EINVAL;
     if (row_bytes % fill_bytes != 0) return ENGRAM_EINVAL;
     if (capacity > 0 && (!dst || !src)) return ENGRAM_EINVAL;
+    if (!aligned(src, 4) || !aligned(dst, 4) || !aligned(split_sizes, 8) || !aligned(status, 8)) return ENGRAM_EINVAL;
     if ((int64_t)world * capacity > ((int64_t)1 << 40) / row_bytes) return ENGRAM_EINVAL;
     uint32_t fill16[4];
     unsigned char bytes[16];
@@ -208,6 +227,9 @@ int engram_unpack_fixed_capacity(const void* src, int64_t row_bytes, const int64
     if (world < 1 || world > 255 || capacity < 0 || dst_rows < 0 || !row_layout_ok(row_bytes) || !split_sizes)
         return ENGRAM_EINVAL;
     if (capacity > 0 && dst_rows > 0 && (!dst || !src)) return ENGRAM_EINVAL;
+    if (!aligned(src, 4) || !aligned(dst, 4) || !aligned(split_sizes, 8) || !aligned(status, 8)) return ENGRAM_EINVAL;
+    if ((int64_t)world * capacity > ((int64_t)1 << 40) / row_bytes || dst_rows > ((int64_t)1 << 40) / row_bytes)
+        return ENGRAM_EINVAL;
     return launch_result(engram::launch_unpack(src, row_bytes, split_sizes, world, capacity, dst, dst_rows, status,
                                                stream));
 }
@@ -215,23 +237,39 @@ int engram_unpack_fixed_capacity(const void* src, int64_t row_bytes, const int64
 int engram_permute_rows(const void* src, int64_t row_bytes, const int64_t* order, int64_t n, void* dst,
                         hipStream_t stream) {
     if (n < 0 || !row_layout_ok(row_bytes) || (n > 0 && (!src || !order || !dst))) return ENGRAM_EINVAL;
+    if (!aligned(src, 4) || !aligned(dst, 4) || !aligned(order, 8) || n > ((int64_t)1 << 40) / row_bytes)
+        return ENGRAM_EINVAL;
     return launch_result(engram::launch_permute(src, row_bytes, order, n, dst, true, stream));
 }
 
 int engram_unpermute_rows(const void* src, int64_t row_bytes, const int64_t* order, int64_t n, void* dst,
                           hipStream_t stream) {
     if (n < 0 || !row_layout_ok(row_bytes) || (n > 0 && (!src || !order || !dst))) return ENGRAM_EINVAL;
+    if (!aligned(src, 4) || !aligned(dst, 4) || !aligned(order, 8) || n > ((int64_t)1 << 40) / row_bytes)
+        return ENGRAM_EINVAL;
     return launch_result(engram::launch_permute(src, row_bytes, order, n, dst, false, stream));
 }
 
 namespace {
 
+// Sizes of a PLE call over a x b rows of `channels` features: every row a
+// whole number of 16-byte chunks, at most 2^26 features per row and 2^40
+// elements in all (so every launch grid fits).
 int ple_dims_ok(int32_t dtype, int64_t a, int64_t b, int64_t channels, int* eb) {
     if (!dtype_ok(dtype)) return ENGRAM_EDTYPE;
     *eb = dtype == ENGRAM_F32 ? 4 : 2;
-    if (a < 0 || b < 0 || channels <= 0 || (channels * *eb) % 16 != 0) return ENGRAM_EINVAL;
-    if (a > 0 && b > INT64_MAX / a / channels) return ENGRAM_EINVAL;
+    if (a < 0 || b < 0 || channels <= 0 || channels > ((int64_t)1 << 26) || (channels * *eb) % 16 != 0)
+        return ENGRAM_EINVAL;
+    if (a > 0 && b > 0 && (b > ((int64_t)1 << 40) / a || a * b > ((int64_t)1 << 40) / channels)) return ENGRAM_EINVAL;
     return ENGRAM_OK;
+}
+
+bool ple_ptrs_ok(std::initializer_list<const void*> rows16, std::initializer_list<const void*> words4) {
+    for (const void* p : rows16)
+        if (!aligned(p, 16)) return false;
+    for (const void* p : words4)
+        if (!aligned(p, 4)) return false;
+    return true;
 }
 
 }  // namespace
@@ -249,6 +287,7 @@ int engram_short_conv(const void* x, int32_t dtype, int64_t batch, int64_t seq, 
     if (rc != ENGRAM_OK) return rc;
     if (kernel < 1 || kernel > 4 || dilation < 1 || !weight) return ENGRAM_EINVAL;
     if (batch * seq > 0 && (!x || !y)) return ENGRAM_EINVAL;
+    if (!ple_ptrs_ok({x, y, halo}, {weight, bias})) return ENGRAM_EINVAL;
     return launch_result(engram::launch_short_conv(x, eb, batch, seq, channels, weight, bias, kernel, dilation, halo,
                                                    y, stream));
 }
@@ -262,6 +301,7 @@ int engram_short_conv_backward(const void* x, const void* dy, int32_t dtype, int
     if (rc != ENGRAM_OK) return rc;
     if (kernel < 1 || kernel > 4 || dilation < 1 || !weight || !dweight) return ENGRAM_EINVAL;
     if (batch * seq > 0 && (!x || !dy || !dx)) return ENGRAM_EINVAL;
+    if (!ple_ptrs_ok({x, dy, halo, dx, dhalo}, {weight, dweight, dbias})) return ENGRAM_EINVAL;
     if (((uintptr_t)workspace & 255) != 0) return ENGRAM_EWORKSPACE;
     const size_t need = engram::short_conv_workspace_bytes(batch, seq, channels, kernel);
     if (need > 0 && (!workspace || workspace_bytes < need)) return ENGRAM_EWORKSPACE;
@@ -283,6 +323,8 @@ int engram_grouped_rms_norm(const void* x, int32_t dtype, int64_t rows, int64_t 
         !(eps >= 0.0f))
         return ENGRAM_EINVAL;
     if (rows > 0 && (!x || !y)) return ENGRAM_EINVAL;
+    if (rows > 0 && rows > (((int64_t)1 << 31) - 1) / (hidden / group_size)) return ENGRAM_EINVAL;  // waves
+    if (!ple_ptrs_ok({x, y}, {weight})) return ENGRAM_EINVAL;
     return launch_result(engram::launch_rms_norm(x, eb, rows, hidden, group_size, weight, eps, y, stream));
 }
 
@@ -296,6 +338,8 @@ int engram_grouped_rms_norm_backward(const void* x, const void* dy, int32_t dtyp
         !dweight || !(eps >= 0.0f))
         return ENGRAM_EINVAL;
     if (rows > 0 && (!x || !dy || !dx)) return ENGRAM_EINVAL;
+    if (rows > 0 && rows > (((int64_t)1 << 31) - 1) / (hidden / group_size)) return ENGRAM_EINVAL;
+    if (!ple_ptrs_ok({x, dy, dx}, {weight, dweight})) return ENGRAM_EINVAL;
     if (((uintptr_t)workspace & 255) != 0) return ENGRAM_EWORKSPACE;
     const size_t need = engram::rms_norm_workspace_bytes(rows, hidden);
     if (need > 0 && (!workspace || workspace_bytes < need)) return ENGRAM_EWORKSPACE;
@@ -306,9 +350,9 @@ int engram_grouped_rms_norm_backward(const void* x, const void* dy, int32_t dtyp
 const char* engram_strerror(int code) {
     switch (code) {
         case ENGRAM_OK: return "success";
-        case ENGRAM_EINVAL: return "invalid argument (null pointer, size out of range or unsupported row width)";
+        case ENGRAM_EINVAL: return "invalid argument (null or misaligned pointer, size out of range or unsupported row width)";
         case ENGRAM_EDTYPE: return "unsupported element type";
-        case ENGRAM_EWORKSPACE: return "scatter-add workspace missing, misaligned or too small";
+        case ENGRAM_EWORKSPACE: return "workspace missing, misaligned or too small";
         case ENGRAM_ELAUNCH: return "kernel launch failed";
         case ENGRAM_ESPEC: return "hash spec out of range (ngram_size, heads, moduli or offsets)";
         default: return "unknown engram status";

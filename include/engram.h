@@ -39,6 +39,11 @@
  *     (-1 when every row is in range).  The library itself first sets
  *     *status = -1 on the stream, so the caller needs no initialisation.
  *   - Sizes are int64; all arrays are dense and row-major.
+ *   - Device arrays are aligned to their access width: 16 bytes for arrays
+ *     of rows (tables, gathered values, gradients, PLE activations), 8 bytes
+ *     for int64 arrays and status words, 4 bytes for fp32 weights and for
+ *     the opaque rows of the routing calls.  A misaligned pointer returns
+ *     ENGRAM_EINVAL.  Memory from hipMalloc (or torch) is always aligned.
  */
 #ifndef ENGRAM_H
 #define ENGRAM_H
@@ -53,9 +58,9 @@ extern "C" {
 
 typedef enum {
     ENGRAM_OK = 0,
-    ENGRAM_EINVAL = -1,     /* null pointer, negative or too large size, unsupported dim */
+    ENGRAM_EINVAL = -1,     /* null or misaligned pointer, negative or too large size, unsupported dim */
     ENGRAM_EDTYPE = -2,     /* unknown element type */
-    ENGRAM_EWORKSPACE = -3, /* scatter-add workspace missing or smaller than required */
+    ENGRAM_EWORKSPACE = -3, /* workspace missing, not 256-byte aligned or smaller than required */
     ENGRAM_ELAUNCH = -4,    /* the HIP runtime refused a kernel launch */
     ENGRAM_ESPEC = -5       /* hash spec outside the supported range */
 } engram_status;

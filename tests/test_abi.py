@@ -235,3 +235,39 @@ def test_ple_rejects_bad_arguments(lib):
     nb = lib.engram_grouped_rms_norm_backward
     assert nb(fake, fake, bf, 2, 64, 32, fake, 1e-6, fake, fake, None, 0, None) == B.ENGRAM_EWORKSPACE
     assert nb(fake, fake, bf, 2, 64, 32, fake, 1e-6, fake, None, fake, 4096, None) == B.ENGRAM_EINVAL
+
+
+def test_misaligned_pointers_rejected(lib):
+    """Every call checks device pointers against their access width before
+    anything is enqueued (the pointers here are never dereferenced)."""
+    B._bind_route(lib)
+    B._bind_ple(lib)
+    ok, odd8, odd16 = ctypes.c_void_p(0x10000), ctypes.c_void_p(0x10004), ctypes.c_void_p(0x10008)
+    s = E.qwen3_8_flash_next_spec()
+    assert lib.engram_hash(odd8, 1, 4, ctypes.byref(s), ok, None) == B.ENGRAM_EINVAL
+    assert lib.engram_hash(ok, 1, 4, ctypes.byref(s), odd8, None) == B.ENGRAM_EINVAL
+    g = lambda table=ok, rows=ok, out=ok: lib.engram_gather(table, B.ENGRAM_BF16, 0, 100, 160, rows, 10, out, None, None)
+    assert g(table=odd16) == B.ENGRAM_EINVAL
+    assert g(out=odd16) == B.ENGRAM_EINVAL
+    assert g(rows=odd8) == B.ENGRAM_EINVAL
+    ws = ctypes.c_void_p(0x100000)
+    need = lib.engram_scatter_add_workspace(10, 100, 160)
+    assert lib.engram_scatter_add_plan(odd8, 10, 0, 100, 160, None, None, ws, need, None, None) == B.ENGRAM_EINVAL
+    assert lib.engram_scatter_add_apply(odd16, B.ENGRAM_BF16, 160, 10, 0, 100, None, ok, ws, need, None) == \
+        B.ENGRAM_EINVAL
+    assert lib.engram_pack_fixed_capacity(ctypes.c_void_p(0x10002), 8, ok, 2, 4, ok, 4, ok, None, None) == \
+        B.ENGRAM_EINVAL
+    assert lib.engram_permute_rows(ok, 8, odd8, 10, ctypes.c_void_p(0x10001), None) == B.ENGRAM_EINVAL
+    assert lib.engram_short_conv(odd16, B.ENGRAM_BF16, 1, 4, 16, ok, None, 4, 3, None, ok, None) == B.ENGRAM_EINVAL
+    assert lib.engram_short_conv(ok, B.ENGRAM_BF16, 1, 4, 16, ctypes.c_void_p(0x10002), None, 4, 3, None, ok,
+                                 None) == B.ENGRAM_EINVAL
+    assert lib.engram_grouped_rms_norm(ok, B.ENGRAM_BF16, 2, 64, 32, ok, 1e-6, odd16, None) == B.ENGRAM_EINVAL
+
+
+def test_oversized_ple_calls_rejected(lib):
+    B._bind_ple(lib)
+    ok = ctypes.c_void_p(0x10000)
+    bf = B.ENGRAM_BF16
+    assert lib.engram_short_conv(ok, bf, 1 << 20, 1 << 20, 8, ok, None, 4, 3, None, ok, None) == B.ENGRAM_EINVAL
+    assert lib.engram_short_conv(ok, bf, 1, 1, 1 << 27, ok, None, 4, 3, None, ok, None) == B.ENGRAM_EINVAL
+    assert lib.engram_grouped_rms_norm(ok, bf, 1 << 30, 16, 8, ok, 1e-6, ok, None) == B.ENGRAM_EINVAL  # 2^31 waves
