@@ -68,10 +68,47 @@ __global__ __launch_bounds__(256) void hash_kernel(const int64_t* __restrict__ t
         const int64_t ctx = valid ? prev : p.fill;
         prod[s] = (uint64_t)ctx * (uint64_t)p.mult[s];
     }
-    if (!live) return;
-
-    int64_t* out = rows_out + g * heads;
     uint64_t mix = prod[0];
+    if (NG == 3 && HPN == 8) {
+        // 16 rows per position.  A wave's 64 positions own one contiguous
+        // 8 KiB span of the output; the rows go through LDS so that every
+        // store instruction writes 1 KiB of consecutive 16-byte chunks.
+        typedef long long i64x2 __attribute__((ext_vector_type(2)));
+        constexpr int kPad = 18;  // int64 per position in LDS: 16 rows + 16 bytes against bank conflicts
+        __shared__ int64_t s_rows[256 / 64][64 * kPad];
+        int64_t* mine = &s_rows[threadIdx.x >> 6][lane * kPad];
+        if (live) {
+#pragma unroll
+            for (int o = 2; o <= 3; ++o) {
+                mix ^= prod[o - 1];
+#pragma unroll
+                for (int j = 0; j < 8; ++j) {
+                    const int h = (o - 2) * 8 + j;
+                    mine[h] = (int64_t)floor_mod((int64_t)mix, p.mod[h], p.magic[h]) + p.off[h];
+                }
+            }
+        }
+        __syncthreads();  // every thread of the block reaches this barrier (none has returned)
+        const int64_t wave_first = g - lane;                                // first position of this wave
+        const int live_pos = (int)min((int64_t)64, total - wave_first);    // positions of the wave in range
+        const int64_t* src = s_rows[threadIdx.x >> 6];
+        i64x2* dst = (i64x2*)(rows_out + wave_first * 16);
+#pragma unroll
+        for (int it = 0; it < 8; ++it) {
+            const int c = it * 64 + lane;  // 16-byte chunk of the wave's span: position c / 8, rows 2 (c % 8)
+            const int pos = c >> 3;
+            if (pos < live_pos) {
+                const int64_t* q = src + pos * kPad + (c & 7) * 2;
+                i64x2 v;
+                v.x = q[0];
+                v.y = q[1];
+                dst[c] = v;
+            }
+        }
+        return;
+    }
+    if (!live) return;
+    int64_t* out = rows_out + g * heads;
     if (HPN == 8) {
 #pragma unroll
         for (int o = 2; o <= kMaxNgram; ++o) {
