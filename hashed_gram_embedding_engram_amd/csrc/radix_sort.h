@@ -89,19 +89,58 @@ __global__ __launch_bounds__(kBlock) void upsweep_kernel(const uint32_t* __restr
     hist[(size_t)tid * num_tiles + blockIdx.x] = c;
 }
 
+// Exclusive prefix sum over the threads of a BLOCK-thread block; *total gets the sum.
+template <int BLOCK>
+__device__ __forceinline__ uint32_t block_exclusive_scan_n(uint32_t v, uint32_t* total, uint32_t* s_tmp) {
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    uint32_t x = v;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+        const uint32_t y = __shfl_up(x, o, 64);
+        if (lane >= o) x += y;
+    }
+    if (lane == 63) s_tmp[w] = x;
+    __syncthreads();
+    uint32_t wave_off = 0, tot = 0;
+#pragma unroll
+    for (int k = 0; k < BLOCK / 64; ++k) {
+        const uint32_t t = s_tmp[k];
+        if (k < w) wave_off += t;
+        tot += t;
+    }
+    __syncthreads();
+    *total = tot;
+    return wave_off + x - v;
+}
+
 // hist[d][tile] -> exclusive prefix over tiles (in place); digit_total[d] = sum.
-__global__ __launch_bounds__(kBlock) void digit_scan_kernel(uint32_t* __restrict__ hist, uint32_t num_tiles,
-                                                            uint32_t* __restrict__ digit_total) {
-    __shared__ uint32_t s_tmp[kBlock / 64];
+// One block per digit; 1024 threads of 4 consecutive tiles each cover 4,096
+// tiles (16.7 M keys) per round.
+constexpr int kDigitScanThreads = 1024;
+constexpr int kDigitScanItems = 4;
+__global__ __launch_bounds__(kDigitScanThreads) void digit_scan_kernel(uint32_t* __restrict__ hist,
+                                                                       uint32_t num_tiles,
+                                                                       uint32_t* __restrict__ digit_total) {
+    __shared__ uint32_t s_tmp[kDigitScanThreads / 64];
     uint32_t* row = hist + (size_t)blockIdx.x * num_tiles;
     uint32_t running = 0;
-    for (uint32_t b = 0; b < num_tiles; b += kBlock) {
-        const uint32_t i = b + threadIdx.x;
-        const uint32_t raw = row[min(i, num_tiles - 1)];
-        const uint32_t v = i < num_tiles ? raw : 0u;
+    for (uint32_t b = 0; b < num_tiles; b += kDigitScanThreads * kDigitScanItems) {
+        const uint32_t i0 = b + threadIdx.x * kDigitScanItems;
+        uint32_t v[kDigitScanItems], sum = 0;
+#pragma unroll
+        for (int k = 0; k < kDigitScanItems; ++k) {
+            const uint32_t i = i0 + k;
+            const uint32_t raw = row[min(i, num_tiles - 1)];  // clamped: every load in bounds
+            v[k] = i < num_tiles ? raw : 0u;
+            sum += v[k];
+        }
         uint32_t tot;
-        const uint32_t ex = block_exclusive_scan(v, &tot, s_tmp);
-        if (i < num_tiles) row[i] = running + ex;
+        uint32_t r = running + block_exclusive_scan_n<kDigitScanThreads>(sum, &tot, s_tmp);
+#pragma unroll
+        for (int k = 0; k < kDigitScanItems; ++k) {
+            if (i0 + k < num_tiles) row[i0 + k] = r;
+            r += v[k];
+        }
         running += tot;
     }
     if (threadIdx.x == 0) digit_total[blockIdx.x] = running;

@@ -186,30 +186,6 @@ __global__ __launch_bounds__(kBlock) void run_count_kernel(const uint32_t* __res
     }
 }
 
-// Exclusive prefix sum over the threads of a BLOCK-thread block.
-template <int BLOCK>
-__device__ __forceinline__ uint32_t block_scan_wide(uint32_t v, uint32_t* total, uint32_t* s_tmp) {
-    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-    uint32_t x = v;
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-        const uint32_t y = __shfl_up(x, o, 64);
-        if (lane >= o) x += y;
-    }
-    if (lane == 63) s_tmp[w] = x;
-    __syncthreads();
-    uint32_t wave_off = 0, tot = 0;
-#pragma unroll
-    for (int k = 0; k < BLOCK / 64; ++k) {
-        const uint32_t t = s_tmp[k];
-        if (k < w) wave_off += t;
-        tot += t;
-    }
-    __syncthreads();
-    *total = tot;
-    return wave_off + x - v;
-}
-
 // Step 3b: exclusive prefix of the slice run counts in one 1024-thread block.
 // Rounds of 16,384 counts: a coalesced load into LDS, a serial scan of 16
 // contiguous counts per thread, one block scan of the thread totals, and a
@@ -241,7 +217,7 @@ __global__ __launch_bounds__(kScanBlock) void slice_scan_kernel(const uint32_t* 
             sum += loc[k];
         }
         uint32_t tot;
-        uint32_t run = carry + block_scan_wide<kScanBlock>(sum, &tot, s_tmp);
+        uint32_t run = carry + block_exclusive_scan_n<kScanBlock>(sum, &tot, s_tmp);
 #pragma unroll
         for (int k = 0; k < kScanPer; ++k) {
             s_val[scan_pad(tid * kScanPer + k)] = run;
@@ -737,7 +713,7 @@ hipError_t launch_scatter_plan(const int64_t* rows, int64_t n, int64_t row_begin
             hipLaunchKernelGGL(upsweep_kernel, dim3(tiles), dim3(kBlock), 0, stream, k_cur, nn, shift, hist, tiles);
             if ((err = hipGetLastError()) != hipSuccess) return err;
         }
-        hipLaunchKernelGGL(digit_scan_kernel, dim3(kRadix), dim3(kBlock), 0, stream, hist, tiles, digit_total);
+        hipLaunchKernelGGL(digit_scan_kernel, dim3(kRadix), dim3(kDigitScanThreads), 0, stream, hist, tiles, digit_total);
         hipLaunchKernelGGL(downsweep_kernel, dim3(tiles), dim3(kBlock), 0, stream, k_cur,
                            p == 0 ? (const uint32_t*)nullptr : v_cur, k_nxt, v_nxt, nn, shift, hist, digit_total,
                            tiles);
