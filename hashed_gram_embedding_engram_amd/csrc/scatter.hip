@@ -49,15 +49,35 @@ namespace {
 #endif
 constexpr uint32_t kSlice = ENGRAM_REDUCE_SLICE;  // sorted entries per reduce worker
 static_assert((kSlice & (kSlice - 1)) == 0 && kSlice >= 32, "slices are powers of two, at least 32 entries");
-// Blocks of the slice bookkeeping kernels cover kSliceSpan entries: one slice,
-// or kBlock / kSlice slices when slices are shorter than a block.
-constexpr uint32_t kSliceSpan = kSlice > (uint32_t)kBlock ? kSlice : (uint32_t)kBlock;
+// Blocks of the slice bookkeeping kernels cover `span` sorted entries: a power
+// of two from kBlock (and at least one slice) to kRunSpanMax, the smallest that
+// keeps the block count at most about 4,096 (fewer, fuller blocks for large n;
+// enough blocks to fill the chip for small n).
+constexpr uint32_t kRunSpanMax = 4096;
+constexpr uint32_t kRunSpanMin = kSlice > (uint32_t)kBlock ? kSlice : (uint32_t)kBlock;
+constexpr uint32_t kRunSlicesMax = kRunSpanMax / kSlice;  // slices per bookkeeping block, at most
+static_assert(kRunSpanMax % kSlice == 0 && kRunSlicesMax <= (uint32_t)kBlock, "whole slices per bookkeeping block");
+
+uint32_t run_span(int64_t n) {
+    uint32_t span = kRunSpanMin;
+    while (span < kRunSpanMax && (n + span - 1) / span > 4096) span *= 2;
+    return span;
+}
+
+// Index of the first run starting in slice j among all runs: the runs before
+// it in its bookkeeping block plus the runs of the blocks before.
+struct RunBase {
+    const uint32_t* slice;  // per slice, within its block
+    const uint32_t* block;  // per block, exclusive prefix over blocks
+    uint32_t shift;         // log2(slices per block)
+    __device__ __forceinline__ uint32_t operator()(uint32_t j) const { return slice[j] + block[j >> shift]; }
+};
 constexpr uint32_t kFlagHead = 1, kFlagWhole = 2, kFlagTail = 4;
 
 struct Layout {
     size_t sorted_keys, spare_keys, sorted_vals, spare_vals, hist, digit_total, counters, slice_runs, slice_base,
-        slice_first, slice_flags, long_runs, carry_head, carry_tail, total;
-    int64_t num_tiles, num_slices;
+        slice_first, slice_flags, long_runs, carry_head, carry_tail, block_runs, block_base, total;
+    int64_t num_tiles, num_slices, num_run_blocks;
 };
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
@@ -66,6 +86,7 @@ Layout make_layout(int64_t n, int dim) {
     Layout L;
     L.num_tiles = (n + kTile - 1) / kTile;
     L.num_slices = (n + kSlice - 1) / kSlice;
+    L.num_run_blocks = (n + run_span(n) - 1) / run_span(n);
     size_t off = 0;
     auto take = [&](size_t bytes) { size_t at = off; off = align256(off + bytes); return at; };
     L.sorted_keys = take(4 * (size_t)n);
@@ -82,6 +103,8 @@ Layout make_layout(int64_t n, int dim) {
     L.long_runs = take(8 * (size_t)L.num_slices);
     L.carry_head = take(8 * (size_t)L.num_slices * (size_t)dim);
     L.carry_tail = take(8 * (size_t)L.num_slices * (size_t)dim);
+    L.block_runs = take(4 * (size_t)L.num_run_blocks);
+    L.block_base = take(4 * (size_t)L.num_run_blocks);
     L.total = off;
     return L;
 }
@@ -143,25 +166,29 @@ __global__ __launch_bounds__(kBlock) void keys_kernel(const int64_t* __restrict_
     if (tid == 0 && s_valid) atomicAdd(&counters[0], s_valid);
 }
 
-// Step 3a: per slice, the number of runs that start in it and the index of
-// the first such start (0xFFFFFFFF when a run covers the whole slice).  One
-// block per kSliceSpan entries.
+// Step 3a: per slice, the number of runs that start in it, the index of the
+// first such start (0xFFFFFFFF when a run covers the whole slice) and the
+// runs starting before it inside its block of `span` entries; per block, the
+// runs starting in it.
 constexpr uint32_t kNoStart = 0xFFFFFFFFu;
 __global__ __launch_bounds__(kBlock) void run_count_kernel(const uint32_t* __restrict__ keys, uint32_t n,
                                                            const uint32_t* __restrict__ counters,
                                                            uint32_t* __restrict__ slice_runs,
-                                                           uint32_t* __restrict__ slice_first, uint32_t num_slices) {
-    constexpr uint32_t kPer = kSliceSpan / kSlice;  // slices per block
-    __shared__ uint32_t s_cnt[kPer], s_first[kPer];
+                                                           uint32_t* __restrict__ slice_first,
+                                                           uint32_t* __restrict__ slice_base, uint32_t num_slices,
+                                                           uint32_t* __restrict__ block_runs, uint32_t span) {
+    __shared__ uint32_t s_cnt[kRunSlicesMax], s_first[kRunSlicesMax];
+    __shared__ uint32_t s_tmp[kBlock / 64];
     const uint32_t nv = min(counters[0], n);
-    if (threadIdx.x < kPer) {
+    const uint32_t slices = span / kSlice;
+    if (threadIdx.x < slices) {
         s_cnt[threadIdx.x] = 0;
         s_first[threadIdx.x] = kNoStart;
     }
     __syncthreads();
-    for (uint32_t off = 0; off < kSliceSpan; off += kBlock) {
+    for (uint32_t off = 0; off < span; off += kBlock) {
         const uint32_t t = off + threadIdx.x;
-        const uint32_t i = blockIdx.x * kSliceSpan + t;
+        const uint32_t i = blockIdx.x * span + t;
         const uint32_t kc = keys[min(i, n - 1)], kp = keys[i == 0 ? 0u : min(i - 1, n - 1)];
         const bool start = i < nv && (i == 0 || kc != kp);
         const uint64_t b = __ballot(start);
@@ -177,37 +204,42 @@ __global__ __launch_bounds__(kBlock) void run_count_kernel(const uint32_t* __res
         }
     }
     __syncthreads();
-    if (threadIdx.x < kPer) {
-        const uint32_t j = blockIdx.x * kPer + threadIdx.x;
+    const uint32_t c = threadIdx.x < slices ? s_cnt[threadIdx.x] : 0u;
+    uint32_t total;
+    const uint32_t before = block_exclusive_scan_n<kBlock>(c, &total, s_tmp);
+    if (threadIdx.x < slices) {
+        const uint32_t j = blockIdx.x * slices + threadIdx.x;
         if (j < num_slices) {
-            slice_runs[j] = s_cnt[threadIdx.x];
+            slice_runs[j] = c;
             slice_first[j] = s_first[threadIdx.x];
+            slice_base[j] = before;  // within the block; RunBase adds the block's base
         }
     }
+    if (threadIdx.x == 0) block_runs[blockIdx.x] = total;
 }
 
-// Step 3b: exclusive prefix of the slice run counts in one 1024-thread block.
-// Rounds of 16,384 counts: a coalesced load into LDS, a serial scan of 16
-// contiguous counts per thread, one block scan of the thread totals, and a
+// Step 3b: exclusive prefix of the blocks' run counts in one 1024-thread
+// block.  Rounds of 16,384 counts: a coalesced load into LDS, a serial scan of
+// 16 contiguous counts per thread, one block scan of the thread totals, and a
 // coalesced store.  The total is the number of distinct rows.
 constexpr int kScanBlock = 1024;
 constexpr int kScanPer = 16;
 constexpr int kScanRound = kScanBlock * kScanPer;
 __device__ __forceinline__ int scan_pad(int e) { return e + (e >> 4); }  // one spare word per 16: no bank conflicts
 
-__global__ __launch_bounds__(kScanBlock) void slice_scan_kernel(const uint32_t* __restrict__ slice_runs,
-                                                                uint32_t num_slices, uint32_t* __restrict__ slice_base,
+__global__ __launch_bounds__(kScanBlock) void block_scan_kernel(const uint32_t* __restrict__ counts,
+                                                                uint32_t count, uint32_t* __restrict__ prefix,
                                                                 int64_t* __restrict__ num_uniq) {
     __shared__ uint32_t s_val[kScanRound + kScanRound / 16];
     __shared__ uint32_t s_tmp[kScanBlock / 64];
     const int tid = threadIdx.x;
     uint32_t carry = 0;
-    for (uint32_t base = 0; base < num_slices; base += kScanRound) {
+    for (uint32_t base = 0; base < count; base += kScanRound) {
 #pragma unroll
         for (int k = 0; k < kScanPer; ++k) {
             const uint32_t i = base + (uint32_t)(k * kScanBlock + tid);
-            const uint32_t raw = slice_runs[min(i, num_slices - 1)];
-            s_val[scan_pad(k * kScanBlock + tid)] = i < num_slices ? raw : 0u;
+            const uint32_t raw = counts[min(i, count - 1)];
+            s_val[scan_pad(k * kScanBlock + tid)] = i < count ? raw : 0u;
         }
         __syncthreads();
         uint32_t loc[kScanPer], sum = 0;
@@ -227,7 +259,7 @@ __global__ __launch_bounds__(kScanBlock) void slice_scan_kernel(const uint32_t* 
 #pragma unroll
         for (int k = 0; k < kScanPer; ++k) {
             const uint32_t i = base + (uint32_t)(k * kScanBlock + tid);
-            if (i < num_slices) slice_base[i] = s_val[scan_pad(k * kScanBlock + tid)];
+            if (i < count) prefix[i] = s_val[scan_pad(k * kScanBlock + tid)];
         }
         carry += tot;
         __syncthreads();
@@ -235,48 +267,37 @@ __global__ __launch_bounds__(kScanBlock) void slice_scan_kernel(const uint32_t* 
     if (tid == 0 && num_uniq) *num_uniq = carry;
 }
 
-// Step 3c (compact form): the distinct rows in ascending order, written by the
-// thread that holds each run's first entry (consecutive runs -> consecutive
-// addresses).
+// Step 3c (compact form): the distinct rows in ascending order, written by
+// the thread that holds each run's first entry (consecutive runs ->
+// consecutive addresses).  One block per bookkeeping block.
 __global__ __launch_bounds__(kBlock) void uniq_rows_kernel(const uint32_t* __restrict__ keys, uint32_t n,
                                                            const uint32_t* __restrict__ counters,
-                                                           const uint32_t* __restrict__ slice_base, int64_t row_begin,
-                                                           int64_t* __restrict__ uniq_rows) {
-    constexpr uint32_t kPer = kSliceSpan / kSlice;
-    __shared__ uint64_t s_mask[kBlock / 64];
-    __shared__ uint32_t s_before[kBlock / 64 + 1];
+                                                           const uint32_t* __restrict__ block_base, int64_t row_begin,
+                                                           int64_t* __restrict__ uniq_rows, uint32_t span) {
+    __shared__ uint32_t s_cnt[kBlock / 64];
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    const uint32_t base = block_base[blockIdx.x];
     const uint32_t nv = min(counters[0], n);
-    uint32_t carried = 0;  // starts in earlier chunks of a slice longer than a block
-    for (uint32_t off = 0; off < kSliceSpan; off += kBlock) {
-        const uint32_t t = off + threadIdx.x;
-        const uint32_t i = blockIdx.x * kSliceSpan + t;
+    uint32_t carried = base;  // runs starting in this block before the current round
+    for (uint32_t off = 0; off < span; off += kBlock) {
+        const uint32_t i = blockIdx.x * span + off + threadIdx.x;
         const uint32_t key = keys[min(i, n - 1)], kp = keys[i == 0 ? 0u : min(i - 1, n - 1)];
         const bool start = i < nv && (i == 0 || key != kp);
         const uint64_t b = __ballot(start);
-        if (lane == 0) s_mask[w] = b;
+        if (lane == 0) s_cnt[w] = (uint32_t)__popcll(b);
         __syncthreads();
-        if (threadIdx.x == 0) {
-            uint32_t acc = 0;
-            for (int k = 0; k < kBlock / 64; ++k) {
-                s_before[k] = acc;
-                acc += (uint32_t)__popcll(s_mask[k]);
-            }
-            s_before[kBlock / 64] = acc;
+        uint32_t before = 0, round = 0;
+#pragma unroll
+        for (int k = 0; k < kBlock / 64; ++k) {
+            const uint32_t c = s_cnt[k];
+            before += k < w ? c : 0u;
+            round += c;
         }
-        __syncthreads();
-        // starts in this chunk before position p (p < kBlock)
-        auto before = [&](uint32_t p) -> uint32_t {
-            const uint32_t pw = p >> 6, pl = p & 63;
-            return s_before[pw] + (uint32_t)__popcll(s_mask[pw] & lanemask_lt((int)pl));
-        };
         if (start) {
-            const uint32_t q = t / kSlice;                        // slice within the block
-            const uint32_t slice_first = (kSlice >= (uint32_t)kBlock) ? 0u : (q * kSlice - off);
-            const uint32_t u = slice_base[blockIdx.x * kPer + q] + carried + before(threadIdx.x) - before(slice_first);
+            const uint32_t u = carried + before + (uint32_t)__popcll(b & lanemask_lt(lane));
             if (u < n) uniq_rows[u] = (int64_t)key + row_begin;
         }
-        carried += s_before[kBlock / 64];
+        carried += round;
         __syncthreads();
     }
 }
@@ -400,7 +421,7 @@ template <int CPR_T, bool BF16, bool DENSE>
 __global__ __launch_bounds__(kBlock) void segment_reduce_kernel(
     const uint32_t* __restrict__ keys, const uint32_t* __restrict__ vals, uint32_t* __restrict__ counters,
     const u32x4* __restrict__ dy, uint32_t n, uint32_t num_rows, int cpr_rt, int dim, uint32_t num_slices,
-    const uint32_t* __restrict__ slice_base, const uint32_t* __restrict__ slice_first,
+    RunBase slice_base, const uint32_t* __restrict__ slice_first,
     float* __restrict__ grad_dense, float* __restrict__ uniq_grad,
     double* __restrict__ carry_head, double* __restrict__ carry_tail, uint32_t* __restrict__ slice_flags) {
     constexpr int EPC = BF16 ? 8 : 4;
@@ -429,7 +450,7 @@ __global__ __launch_bounds__(kBlock) void segment_reduce_kernel(
         return;
     }
     bool head_open = f0 == kNoStart && s0 > 0 && keys[s0 - 1] == keys[s0];
-    uint32_t u = slice_base[j];
+    uint32_t u = slice_base(j);
     uint32_t flags = 0;
     double acc[EPC];
 #pragma unroll
@@ -509,7 +530,7 @@ template <int CPR_T, bool BF16, bool DENSE>
 __global__ __launch_bounds__(kBlock) void carry_fixup_kernel(
     const uint32_t* __restrict__ keys, uint32_t* __restrict__ counters, uint32_t n, uint32_t num_rows,
     int cpr_rt, int dim, uint32_t num_slices, const uint32_t* __restrict__ slice_runs,
-    const uint32_t* __restrict__ slice_base, const uint32_t* __restrict__ slice_first,
+    RunBase slice_base, const uint32_t* __restrict__ slice_first,
     const uint32_t* __restrict__ slice_flags, const double* __restrict__ carry_head,
     const double* __restrict__ carry_tail, uint32_t* __restrict__ long_runs,
     float* __restrict__ grad_dense, float* __restrict__ uniq_grad) {
@@ -571,7 +592,7 @@ __global__ __launch_bounds__(kBlock) void carry_fixup_kernel(
     add_partial<EPC>(acc, carry_tail + (size_t)j * dim + c * EPC);
 #pragma unroll 8
     for (int64_t k = j + 1; k <= m; ++k) add_partial<EPC>(acc, carry_head + (size_t)k * dim + c * EPC);
-    const uint32_t u = slice_base[j] + slice_runs[j] - 1;
+    const uint32_t u = slice_base(j) + slice_runs[j] - 1;
     write_run<EPC, DENSE>(acc, key, u, c, dim, n, num_rows, grad_dense, uniq_grad);
 }
 
@@ -583,7 +604,7 @@ template <int CPR_T, bool BF16, bool DENSE>
 __global__ __launch_bounds__(kBlock) void long_run_kernel(
     const uint32_t* __restrict__ keys, const uint32_t* __restrict__ counters, uint32_t n, uint32_t num_rows,
     int cpr_rt, int dim, uint32_t num_slices, const uint32_t* __restrict__ slice_runs,
-    const uint32_t* __restrict__ slice_base, const double* __restrict__ carry_head,
+    RunBase slice_base, const double* __restrict__ carry_head,
     const double* __restrict__ carry_tail, const uint32_t* __restrict__ long_runs, float* __restrict__ grad_dense,
     float* __restrict__ uniq_grad) {
     constexpr int EPC = BF16 ? 8 : 4;
@@ -620,7 +641,7 @@ __global__ __launch_bounds__(kBlock) void long_run_kernel(
 #pragma unroll
                 for (int e = 0; e < EPC; ++e) acc[e] += s_share[(size_t)q * dim + c * EPC + e];
             const uint32_t key = keys[min((uint32_t)(j + 1) * kSlice - 1, n - 1)];
-            const uint32_t u = slice_base[j] + slice_runs[j] - 1;
+            const uint32_t u = slice_base(j) + slice_runs[j] - 1;
             write_run<EPC, DENSE>(acc, key, u, c, dim, n, num_rows, grad_dense, uniq_grad);
         }
         __syncthreads();
@@ -641,23 +662,25 @@ hipError_t launch_reduce(const Layout& L, const char* ws, const void* grad_out, 
     uint32_t* flags = (uint32_t*)(ws + L.slice_flags);
     uint32_t* counters = (uint32_t*)(ws + L.counters);
     uint32_t* long_runs = (uint32_t*)(ws + L.long_runs);
+    uint32_t shift = 0;
+    while ((kSlice << shift) < run_span(n)) ++shift;
+    const RunBase base{(const uint32_t*)(ws + L.slice_base), (const uint32_t*)(ws + L.block_base), shift};
     hipLaunchKernelGGL((segment_reduce_kernel<CPR_T, BF16, DENSE>), dim3((unsigned)grid), dim3(kBlock), 0, stream,
                        sorted_keys, sorted_vals, counters, (const u32x4*)grad_out, n, num_rows, cpr, dim, ns,
-                       (const uint32_t*)(ws + L.slice_base), (const uint32_t*)(ws + L.slice_first), grad_dense,
-                       uniq_grad, carry_head, carry_tail, flags);
+                       base, (const uint32_t*)(ws + L.slice_first), grad_dense, uniq_grad, carry_head, carry_tail,
+                       flags);
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
     hipLaunchKernelGGL((carry_fixup_kernel<CPR_T, BF16, DENSE>), dim3((unsigned)grid), dim3(kBlock), 0, stream,
-                       sorted_keys, counters, n, num_rows, cpr, dim, ns, (const uint32_t*)(ws + L.slice_runs),
-                       (const uint32_t*)(ws + L.slice_base), (const uint32_t*)(ws + L.slice_first),
+                       sorted_keys, counters, n, num_rows, cpr, dim, ns, (const uint32_t*)(ws + L.slice_runs), base,
+                       (const uint32_t*)(ws + L.slice_first),
                        (const uint32_t*)flags, (const double*)carry_head,
                        (const double*)carry_tail, long_runs, grad_dense, uniq_grad);
     if ((err = hipGetLastError()) != hipSuccess) return err;
     const size_t share_bytes = (size_t)wpw * (kBlock / 64) * dim * sizeof(double);
     hipLaunchKernelGGL((long_run_kernel<CPR_T, BF16, DENSE>), dim3(256), dim3(kBlock), share_bytes, stream,
                        sorted_keys, (const uint32_t*)counters, n, num_rows, cpr, dim, ns,
-                       (const uint32_t*)(ws + L.slice_runs), (const uint32_t*)(ws + L.slice_base),
-                       (const double*)carry_head, (const double*)carry_tail, (const uint32_t*)long_runs, grad_dense,
+                       (const uint32_t*)(ws + L.slice_runs), base, (const double*)carry_head, (const double*)carry_tail, (const uint32_t*)long_runs, grad_dense,
                        uniq_grad);
     return hipGetLastError();
 }
@@ -723,14 +746,15 @@ hipError_t launch_scatter_plan(const int64_t* rows, int64_t n, int64_t row_begin
     }
 
     const uint32_t ns = (uint32_t)L.num_slices;
-    const uint32_t span_blocks = (uint32_t)((n + kSliceSpan - 1) / kSliceSpan);
-    hipLaunchKernelGGL(run_count_kernel, dim3(span_blocks), dim3(kBlock), 0, stream, k_cur, nn, counters,
-                       (uint32_t*)(ws + L.slice_runs), (uint32_t*)(ws + L.slice_first), ns);
-    hipLaunchKernelGGL(slice_scan_kernel, dim3(1), dim3(kScanBlock), 0, stream, (const uint32_t*)(ws + L.slice_runs),
-                       ns, (uint32_t*)(ws + L.slice_base), num_uniq);
+    const uint32_t run_blocks = (uint32_t)L.num_run_blocks, span = run_span(n);
+    hipLaunchKernelGGL(run_count_kernel, dim3(run_blocks), dim3(kBlock), 0, stream, k_cur, nn, counters,
+                       (uint32_t*)(ws + L.slice_runs), (uint32_t*)(ws + L.slice_first),
+                       (uint32_t*)(ws + L.slice_base), ns, (uint32_t*)(ws + L.block_runs), span);
+    hipLaunchKernelGGL(block_scan_kernel, dim3(1), dim3(kScanBlock), 0, stream, (const uint32_t*)(ws + L.block_runs),
+                       run_blocks, (uint32_t*)(ws + L.block_base), num_uniq);
     if (uniq_rows)
-        hipLaunchKernelGGL(uniq_rows_kernel, dim3(span_blocks), dim3(kBlock), 0, stream, k_cur, nn, counters,
-                           (const uint32_t*)(ws + L.slice_base), row_begin, uniq_rows);
+        hipLaunchKernelGGL(uniq_rows_kernel, dim3(run_blocks), dim3(kBlock), 0, stream, k_cur, nn, counters,
+                           (const uint32_t*)(ws + L.block_base), row_begin, uniq_rows, span);
     return hipGetLastError();
 }
 
