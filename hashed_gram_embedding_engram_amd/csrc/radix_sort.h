@@ -114,33 +114,21 @@ __device__ __forceinline__ uint32_t block_exclusive_scan_n(uint32_t v, uint32_t*
 }
 
 // hist[d][tile] -> exclusive prefix over tiles (in place); digit_total[d] = sum.
-// One block per digit; 1024 threads of 4 consecutive tiles each cover 4,096
-// tiles (16.7 M keys) per round.
-constexpr int kDigitScanThreads = 1024;
-constexpr int kDigitScanItems = 4;
-__global__ __launch_bounds__(kDigitScanThreads) void digit_scan_kernel(uint32_t* __restrict__ hist,
-                                                                       uint32_t num_tiles,
-                                                                       uint32_t* __restrict__ digit_total) {
-    __shared__ uint32_t s_tmp[kDigitScanThreads / 64];
+// One 256-thread block per digit.  Small blocks on purpose: the plan usually
+// runs beside the gather, and a block that needs few wave slots starts as
+// soon as a compute unit has room.
+__global__ __launch_bounds__(kBlock) void digit_scan_kernel(uint32_t* __restrict__ hist, uint32_t num_tiles,
+                                                            uint32_t* __restrict__ digit_total) {
+    __shared__ uint32_t s_tmp[kBlock / 64];
     uint32_t* row = hist + (size_t)blockIdx.x * num_tiles;
     uint32_t running = 0;
-    for (uint32_t b = 0; b < num_tiles; b += kDigitScanThreads * kDigitScanItems) {
-        const uint32_t i0 = b + threadIdx.x * kDigitScanItems;
-        uint32_t v[kDigitScanItems], sum = 0;
-#pragma unroll
-        for (int k = 0; k < kDigitScanItems; ++k) {
-            const uint32_t i = i0 + k;
-            const uint32_t raw = row[min(i, num_tiles - 1)];  // clamped: every load in bounds
-            v[k] = i < num_tiles ? raw : 0u;
-            sum += v[k];
-        }
+    for (uint32_t b = 0; b < num_tiles; b += kBlock) {
+        const uint32_t i = b + threadIdx.x;
+        const uint32_t raw = row[min(i, num_tiles - 1)];
+        const uint32_t v = i < num_tiles ? raw : 0u;
         uint32_t tot;
-        uint32_t r = running + block_exclusive_scan_n<kDigitScanThreads>(sum, &tot, s_tmp);
-#pragma unroll
-        for (int k = 0; k < kDigitScanItems; ++k) {
-            if (i0 + k < num_tiles) row[i0 + k] = r;
-            r += v[k];
-        }
+        const uint32_t ex = block_exclusive_scan(v, &tot, s_tmp);
+        if (i < num_tiles) row[i] = running + ex;
         running += tot;
     }
     if (threadIdx.x == 0) digit_total[blockIdx.x] = running;

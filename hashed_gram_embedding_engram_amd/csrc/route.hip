@@ -278,7 +278,7 @@ hipError_t launch_route_plan(const int64_t* ids, int64_t n, int64_t local_rows, 
     uint32_t* vb = (uint32_t*)(ws + L.vals_b);
     hipLaunchKernelGGL(route_keys_kernel, dim3(tiles), dim3(kBlock), 0, stream, ids, nn, local_rows, world, ka, hist,
                        tiles, status);
-    hipLaunchKernelGGL(digit_scan_kernel, dim3(kRadix), dim3(kDigitScanThreads), 0, stream, hist, tiles, digit_total);
+    hipLaunchKernelGGL(digit_scan_kernel, dim3(kRadix), dim3(kBlock), 0, stream, hist, tiles, digit_total);
     hipLaunchKernelGGL(downsweep_kernel, dim3(tiles), dim3(kBlock), 0, stream, ka, (const uint32_t*)nullptr, kb, vb,
                        nn, 0, hist, digit_total, tiles);
     hipLaunchKernelGGL(route_output_kernel, dim3((nn + kBlock - 1) / kBlock), dim3(kBlock), 0, stream, vb, ids, nn,

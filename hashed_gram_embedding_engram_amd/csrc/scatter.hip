@@ -218,11 +218,12 @@ __global__ __launch_bounds__(kBlock) void run_count_kernel(const uint32_t* __res
     if (threadIdx.x == 0) block_runs[blockIdx.x] = total;
 }
 
-// Step 3b: exclusive prefix of the blocks' run counts in one 1024-thread
-// block.  Rounds of 16,384 counts: a coalesced load into LDS, a serial scan of
-// 16 contiguous counts per thread, one block scan of the thread totals, and a
-// coalesced store.  The total is the number of distinct rows.
-constexpr int kScanBlock = 1024;
+// Step 3b: exclusive prefix of the blocks' run counts in one 256-thread block
+// (a small block starts quickly beside the gather).  Rounds of 4,096 counts:
+// a coalesced load into LDS, a serial scan of 16 contiguous counts per
+// thread, one block scan of the thread totals, and a coalesced store.  The
+// total is the number of distinct rows.
+constexpr int kScanBlock = 256;
 constexpr int kScanPer = 16;
 constexpr int kScanRound = kScanBlock * kScanPer;
 __device__ __forceinline__ int scan_pad(int e) { return e + (e >> 4); }  // one spare word per 16: no bank conflicts
@@ -736,7 +737,7 @@ hipError_t launch_scatter_plan(const int64_t* rows, int64_t n, int64_t row_begin
             hipLaunchKernelGGL(upsweep_kernel, dim3(tiles), dim3(kBlock), 0, stream, k_cur, nn, shift, hist, tiles);
             if ((err = hipGetLastError()) != hipSuccess) return err;
         }
-        hipLaunchKernelGGL(digit_scan_kernel, dim3(kRadix), dim3(kDigitScanThreads), 0, stream, hist, tiles, digit_total);
+        hipLaunchKernelGGL(digit_scan_kernel, dim3(kRadix), dim3(kBlock), 0, stream, hist, tiles, digit_total);
         hipLaunchKernelGGL(downsweep_kernel, dim3(tiles), dim3(kBlock), 0, stream, k_cur,
                            p == 0 ? (const uint32_t*)nullptr : v_cur, k_nxt, v_nxt, nn, shift, hist, digit_total,
                            tiles);
