@@ -36,6 +36,11 @@ def test_validate_finds_misrouted():
     s2 = s.copy()
     s2[int(c[0]) + 3] = 0          # an owner-0 ID in owner 1's segment
     assert RR.validate(s2, c, 8000, 8) == int(c[0]) + 3
+    s3 = s.copy()
+    s3[5] = 1000                   # owner 1's first row at the end of owner 0's range
+    assert RR.validate(s3, c, 8000, 8) == 5
+    s3[5] = 999                    # owner 0's last row is fine
+    assert RR.validate(s3, c, 8000, 8) == -1
     assert RR.validate(s, c + np.eye(8, dtype=np.int64)[2] * 5000, 8000, 8) == 1000
 
 
