@@ -19,6 +19,8 @@
 //   pack / unpack  compact segments <-> [world][capacity] padded blocks.
 //   permute        rows into / out of the grouped order.
 // The collective itself (RCCL all-to-all over xGMI) is outside this library.
+#include <algorithm>
+
 #include "radix_sort.h"
 
 namespace engram {
@@ -28,7 +30,7 @@ namespace {
 // 255 left for out-of-range IDs, and one thread per count fits a block.
 
 struct RouteLayout {
-    size_t keys_a, keys_b, vals_b, hist, digit_total, counters, total;
+    size_t keys_a, keys_b, vals_b, hist, count_totals, counters, total;
     int64_t num_tiles;
 };
 
@@ -41,7 +43,7 @@ RouteLayout route_layout(int64_t n) {
     L.keys_b = take(4 * (size_t)n);
     L.vals_b = take(4 * (size_t)n);
     L.hist = take(4 * (size_t)kRadix * (size_t)L.num_tiles);
-    L.digit_total = take(4 * kRadix);
+    L.count_totals = take(4 * count_words(L.num_tiles));
     L.counters = take(16);
     L.total = off;
     return L;
@@ -51,17 +53,21 @@ __global__ void zero_counts_kernel(int64_t* counts, int world) {
     if (threadIdx.x < (unsigned)world) counts[threadIdx.x] = 0;
 }
 
-__global__ void route_init_kernel(int64_t* status, uint32_t* counters) {
-    if (status) *status = -1;
-    counters[0] = 0;
+__global__ __launch_bounds__(kBlock) void route_init_kernel(int64_t* status, uint32_t* counters,
+                                                            uint32_t* count_totals, uint32_t total_words) {
+    if (blockIdx.x == 0 && threadIdx.x == 0) {
+        if (status) *status = -1;
+        counters[0] = 0;
+    }
+    for (uint32_t i = blockIdx.x * kBlock + threadIdx.x; i < total_words; i += gridDim.x * kBlock)
+        count_totals[i] = 0;
 }
 
 // Owner keys (sentinel `world` for an ID outside the table) and the per-tile
 // owner histogram; the request index of each key is its position.
 __global__ __launch_bounds__(kBlock) void route_keys_kernel(const int64_t* __restrict__ ids, uint32_t n,
                                                             int64_t local_rows, int world, uint32_t* __restrict__ keys,
-                                                            uint32_t* __restrict__ hist,
-                                                            uint32_t num_tiles, int64_t* __restrict__ status) {
+                                                            DigitCounts dc, int64_t* __restrict__ status) {
     __shared__ uint32_t s_cnt[kBlock / 64][kRadix];
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
 #pragma unroll
@@ -89,18 +95,22 @@ __global__ __launch_bounds__(kBlock) void route_keys_kernel(const int64_t* __res
     uint32_t c = 0;
 #pragma unroll
     for (int k = 0; k < kBlock / 64; ++k) c += s_cnt[k][tid];
-    hist[(size_t)tid * num_tiles + blockIdx.x] = c;
+    publish_tile_counts(dc, blockIdx.x, tid, c);
 }
 
 // Grouped IDs, their request positions, and the per-owner send counts.
 __global__ __launch_bounds__(kBlock) void route_output_kernel(const uint32_t* __restrict__ sorted_vals,
                                                               const int64_t* __restrict__ ids, uint32_t n, int world,
-                                                              const uint32_t* __restrict__ digit_total,
+                                                              DigitCounts dc,
                                                               int64_t* __restrict__ sorted_ids,
                                                               int64_t* __restrict__ order,
                                                               int64_t* __restrict__ send_counts) {
     const uint32_t i = blockIdx.x * kBlock + threadIdx.x;
-    if (blockIdx.x == 0 && threadIdx.x < (unsigned)world) send_counts[threadIdx.x] = digit_total[threadIdx.x];
+    if (blockIdx.x == 0 && threadIdx.x < (unsigned)world) {
+        uint32_t total = 0;  // all groups' counts of owner threadIdx.x
+        for (uint32_t g = 0; g < dc.num_groups; ++g) total += dc.group[(size_t)g * kRadix + threadIdx.x];
+        send_counts[threadIdx.x] = total;
+    }
     if (i >= n) return;
     const uint32_t v = min(sorted_vals[i], n - 1);
     sorted_ids[i] = ids[v];
@@ -264,7 +274,11 @@ hipError_t launch_route_plan(const int64_t* ids, int64_t n, int64_t local_rows, 
     const RouteLayout L = route_layout(n);
     char* ws = (char*)workspace;
     uint32_t* counters = (uint32_t*)(ws + L.counters);
-    hipLaunchKernelGGL(route_init_kernel, dim3(1), dim3(1), 0, stream, status, counters);
+    uint32_t* count_totals = (uint32_t*)(ws + L.count_totals);
+    const uint32_t total_words = (uint32_t)count_words(L.num_tiles);
+    const uint32_t init_grid = std::max(1u, std::min(64u, (total_words + kBlock - 1) / kBlock));
+    hipLaunchKernelGGL(route_init_kernel, dim3(init_grid), dim3(kBlock), 0, stream, status, counters, count_totals,
+                       total_words);
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
     if (n == 0) {  // no lookups: every send count is zero
@@ -272,17 +286,19 @@ hipError_t launch_route_plan(const int64_t* ids, int64_t n, int64_t local_rows, 
         return hipGetLastError();
     }
     const uint32_t nn = (uint32_t)n, tiles = (uint32_t)L.num_tiles;
-    uint32_t* hist = (uint32_t*)(ws + L.hist);
-    uint32_t* digit_total = (uint32_t*)(ws + L.digit_total);
+    const DigitCounts dc = make_digit_counts(ws + L.hist, count_totals, L.num_tiles);
     uint32_t *ka = (uint32_t*)(ws + L.keys_a), *kb = (uint32_t*)(ws + L.keys_b);
     uint32_t* vb = (uint32_t*)(ws + L.vals_b);
-    hipLaunchKernelGGL(route_keys_kernel, dim3(tiles), dim3(kBlock), 0, stream, ids, nn, local_rows, world, ka, hist,
-                       tiles, status);
-    hipLaunchKernelGGL(digit_scan_kernel, dim3(kRadix), dim3(kBlock), 0, stream, hist, tiles, digit_total);
-    hipLaunchKernelGGL(downsweep_kernel, dim3(tiles), dim3(kBlock), 0, stream, ka, (const uint32_t*)nullptr, kb, vb,
-                       nn, 0, hist, digit_total, tiles);
+    hipLaunchKernelGGL(route_keys_kernel, dim3(tiles), dim3(kBlock), 0, stream, ids, nn, local_rows, world, ka, dc,
+                       status);
+    if (small_counts(dc))
+        hipLaunchKernelGGL(downsweep_kernel<true>, dim3(tiles), dim3(kBlock), 0, stream, ka, (const uint32_t*)nullptr,
+                           kb, vb, nn, 0, dc);
+    else
+        hipLaunchKernelGGL(downsweep_kernel<false>, dim3(tiles), dim3(kBlock), 0, stream, ka, (const uint32_t*)nullptr,
+                           kb, vb, nn, 0, dc);
     hipLaunchKernelGGL(route_output_kernel, dim3((nn + kBlock - 1) / kBlock), dim3(kBlock), 0, stream, vb, ids, nn,
-                       world, digit_total, sorted_ids, order, send_counts);
+                       world, dc, sorted_ids, order, send_counts);
     return hipGetLastError();
 }
 

@@ -16,9 +16,10 @@
 //               first digit in the same pass.
 //   2. sort     stable LSD radix sort of (key, index), 8-bit digits, as many
 //               passes as the bit length of num_rows needs (29 bits -> 4).
-//               Per pass: tile histograms, a per-digit scan over tiles, and a
-//               stable scatter that ranks digits inside each wave with ballots
-//               (no atomics) and writes each tile digit-grouped through LDS.
+//               Per pass: tile histograms (also summed per chunk of tiles),
+//               then a stable scatter that derives its digit offsets from
+//               those counts, ranks digits inside each wave with ballots (no
+//               atomics) and writes each tile digit-grouped through LDS.
 //   3. runs     run starts per slice of S sorted entries, their prefix sum
 //               (the distinct-row index of every run) and, for the compact
 //               form, the distinct rows themselves.
@@ -30,6 +31,8 @@
 //   5. fix-up   the slice where a cut run starts adds the partials of the
 //               following slices in slice order and writes the run.
 // Every step has a fixed order, so two calls give bit-identical results.
+#include <algorithm>
+
 #include "radix_sort.h"
 
 namespace engram {
@@ -75,10 +78,11 @@ struct RunBase {
 constexpr uint32_t kFlagHead = 1, kFlagWhole = 2, kFlagTail = 4;
 
 struct Layout {
-    size_t sorted_keys, spare_keys, sorted_vals, spare_vals, hist, digit_total, counters, slice_runs, slice_base,
+    size_t sorted_keys, spare_keys, sorted_vals, spare_vals, hist, count_totals, counters, slice_runs, slice_base,
         slice_first, slice_flags, long_runs, carry_head, carry_tail, block_runs, block_base, total;
     int64_t num_tiles, num_slices, num_run_blocks;
 };
+constexpr int kMaxPasses = 4;  // 32-bit keys, 8-bit digits
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
@@ -94,7 +98,7 @@ Layout make_layout(int64_t n, int dim) {
     L.sorted_vals = take(4 * (size_t)n);
     L.spare_vals = take(4 * (size_t)n);
     L.hist = take(4 * (size_t)kRadix * (size_t)L.num_tiles);
-    L.digit_total = take(4 * kRadix);
+    L.count_totals = take(4 * count_words(L.num_tiles) * kMaxPasses);  // one set per pass
     L.counters = take(16);
     L.slice_runs = take(4 * (size_t)L.num_slices);
     L.slice_base = take(4 * (size_t)L.num_slices);
@@ -109,10 +113,16 @@ Layout make_layout(int64_t n, int dim) {
     return L;
 }
 
-__global__ void scatter_init_kernel(int64_t* status, uint32_t* counters, int64_t* num_uniq) {
-    if (status) *status = -1;
-    counters[0] = 0;  // number of in-range lookups
-    if (num_uniq) *num_uniq = 0;
+__global__ __launch_bounds__(kBlock) void scatter_init_kernel(int64_t* status, uint32_t* counters,
+                                                              int64_t* num_uniq, uint32_t* count_totals,
+                                                              uint32_t total_words) {
+    if (blockIdx.x == 0 && threadIdx.x == 0) {
+        if (status) *status = -1;
+        counters[0] = 0;  // number of in-range lookups
+        if (num_uniq) *num_uniq = 0;
+    }
+    for (uint32_t i = blockIdx.x * kBlock + threadIdx.x; i < total_words; i += gridDim.x * kBlock)
+        count_totals[i] = 0;
 }
 
 // Tile histograms count with LDS atomics into one sub-histogram per wave
@@ -121,8 +131,8 @@ __global__ void scatter_init_kernel(int64_t* status, uint32_t* counters, int64_t
 // index is its position, so the first sort pass reads no value array.
 __global__ __launch_bounds__(kBlock) void keys_kernel(const int64_t* __restrict__ rows, uint32_t n,
                                                       int64_t row_begin, uint64_t num_rows,
-                                                      uint32_t* __restrict__ keys, uint32_t* __restrict__ hist,
-                                                      uint32_t num_tiles, int64_t* __restrict__ status,
+                                                      uint32_t* __restrict__ keys, DigitCounts dc,
+                                                      int64_t* __restrict__ status,
                                                       uint32_t* __restrict__ counters) {
     __shared__ uint32_t s_cnt[kBlock / 64][kRadix];
     __shared__ uint32_t s_valid;
@@ -162,7 +172,7 @@ __global__ __launch_bounds__(kBlock) void keys_kernel(const int64_t* __restrict_
     uint32_t c = 0;
 #pragma unroll
     for (int k = 0; k < kBlock / 64; ++k) c += s_cnt[k][tid];
-    hist[(size_t)tid * num_tiles + blockIdx.x] = c;
+    publish_tile_counts(dc, blockIdx.x, tid, c);
     if (tid == 0 && s_valid) atomicAdd(&counters[0], s_valid);
 }
 
@@ -709,17 +719,20 @@ hipError_t launch_scatter_plan(const int64_t* rows, int64_t n, int64_t row_begin
     const Layout L = make_layout(n, dim);
     char* ws = (char*)workspace;
     uint32_t* counters = (uint32_t*)(ws + L.counters);
-    hipLaunchKernelGGL(scatter_init_kernel, dim3(1), dim3(1), 0, stream, status, counters, num_uniq);
+    int bits = 0;
+    while (bits < 32 && ((uint64_t)num_rows >> bits) != 0) ++bits;  // the sentinel num_rows sorts last
+    const int passes = (bits + 7) / 8;
+    const size_t pass_words = count_words(L.num_tiles);  // chunk and group totals of one pass
+    uint32_t* count_totals = (uint32_t*)(ws + L.count_totals);
+    const uint32_t total_words = (uint32_t)(pass_words * passes);
+    const uint32_t init_grid = std::max(1u, std::min(64u, (total_words + kBlock - 1) / kBlock));
+    hipLaunchKernelGGL(scatter_init_kernel, dim3(init_grid), dim3(kBlock), 0, stream, status, counters, num_uniq,
+                       count_totals, total_words);
     hipError_t err = hipGetLastError();
     if (err != hipSuccess || n == 0) return err;
 
     const uint32_t nn = (uint32_t)n, tiles = (uint32_t)L.num_tiles;
-    uint32_t* hist = (uint32_t*)(ws + L.hist);
-    uint32_t* digit_total = (uint32_t*)(ws + L.digit_total);
     // Passes ping-pong between the two buffers and must end in the sorted slots.
-    int bits = 0;
-    while (bits < 32 && ((uint64_t)num_rows >> bits) != 0) ++bits;  // the sentinel num_rows sorts last
-    const int passes = (bits + 7) / 8;
     uint32_t *k_cur, *k_nxt, *v_cur, *v_nxt;
     if (passes % 2 == 0) {
         k_cur = (uint32_t*)(ws + L.sorted_keys); k_nxt = (uint32_t*)(ws + L.spare_keys);
@@ -728,19 +741,24 @@ hipError_t launch_scatter_plan(const int64_t* rows, int64_t n, int64_t row_begin
         k_cur = (uint32_t*)(ws + L.spare_keys); k_nxt = (uint32_t*)(ws + L.sorted_keys);
         v_cur = (uint32_t*)(ws + L.spare_vals); v_nxt = (uint32_t*)(ws + L.sorted_vals);
     }
+    auto pass_counts = [&](int p) { return make_digit_counts(ws + L.hist, count_totals + p * pass_words, L.num_tiles); };
     hipLaunchKernelGGL(keys_kernel, dim3(tiles), dim3(kBlock), 0, stream, rows, nn, row_begin, (uint64_t)num_rows,
-                       k_cur, hist, tiles, status, counters);
+                       k_cur, pass_counts(0), status, counters);
     if ((err = hipGetLastError()) != hipSuccess) return err;
     for (int p = 0; p < passes; ++p) {
         const int shift = 8 * p;
+        const DigitCounts dc = pass_counts(p);
         if (p > 0) {
-            hipLaunchKernelGGL(upsweep_kernel, dim3(tiles), dim3(kBlock), 0, stream, k_cur, nn, shift, hist, tiles);
+            hipLaunchKernelGGL(upsweep_kernel, dim3(tiles), dim3(kBlock), 0, stream, k_cur, nn, shift, dc);
             if ((err = hipGetLastError()) != hipSuccess) return err;
         }
-        hipLaunchKernelGGL(digit_scan_kernel, dim3(kRadix), dim3(kBlock), 0, stream, hist, tiles, digit_total);
-        hipLaunchKernelGGL(downsweep_kernel, dim3(tiles), dim3(kBlock), 0, stream, k_cur,
-                           p == 0 ? (const uint32_t*)nullptr : v_cur, k_nxt, v_nxt, nn, shift, hist, digit_total,
-                           tiles);
+        const uint32_t* v_in = p == 0 ? nullptr : v_cur;
+        if (small_counts(dc))
+            hipLaunchKernelGGL(downsweep_kernel<true>, dim3(tiles), dim3(kBlock), 0, stream, k_cur, v_in, k_nxt,
+                               v_nxt, nn, shift, dc);
+        else
+            hipLaunchKernelGGL(downsweep_kernel<false>, dim3(tiles), dim3(kBlock), 0, stream, k_cur, v_in, k_nxt,
+                               v_nxt, nn, shift, dc);
         if ((err = hipGetLastError()) != hipSuccess) return err;
         uint32_t* t = k_cur; k_cur = k_nxt; k_nxt = t;
         t = v_cur; v_cur = v_nxt; v_nxt = t;
