@@ -43,6 +43,12 @@ __global__ __launch_bounds__(256) void gather_rows_kernel(const u32x4* __restric
                                                           int64_t* __restrict__ status) {
     constexpr int PER_LANE = CPR * G / 64;
     static_assert(CPR * G % 64 == 0 && G <= 64, "wave tile must be whole dwordx4 per lane");
+    // Claim 128 VGPRs (the body needs about 34) so that at most four of these
+    // waves share a SIMD.  Sixteen waves per compute unit, each with PER_LANE
+    // 16-byte loads per lane in flight, already cover HBM latency; with fewer
+    // of them resident the gather alone runs faster (less cache thrashing),
+    // and a plan running beside it on another stream finds room to run.
+    asm volatile("" ::: "v127");
     const int lane = threadIdx.x & 63;
     const int64_t wave = (int64_t)blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6);
     const int64_t n0 = wave * G;
