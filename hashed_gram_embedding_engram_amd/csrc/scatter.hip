@@ -352,6 +352,64 @@ __device__ __forceinline__ void add_partial(double* acc, const double* src) {
     }
 }
 
+// acc += the partials of slices k0 .. k1-1 (rows `dim` doubles apart), added in
+// slice order.  AHEAD slices' loads are issued before any of their adds: the
+// partials come from HBM, and a walk with only a few loads in flight is bound
+// by their latency.
+template <int EPC, int AHEAD>
+__device__ __forceinline__ void add_partials(double* acc, const double* src, int64_t k0, int64_t k1, int dim) {
+    typedef double __attribute__((ext_vector_type(2))) d2;
+    constexpr int kAhead = AHEAD;
+    int64_t k = k0;
+    for (; k + kAhead <= k1; k += kAhead) {
+        d2 v[kAhead][EPC / 2];
+#pragma unroll
+        for (int q = 0; q < kAhead; ++q)
+#pragma unroll
+            for (int e = 0; e < EPC / 2; ++e) v[q][e] = *(const d2*)(src + (size_t)(k + q) * dim + 2 * e);
+        __builtin_amdgcn_sched_barrier(0);  // keep the scheduler from interleaving the adds into the loads
+#pragma unroll
+        for (int q = 0; q < kAhead; ++q)
+#pragma unroll
+            for (int e = 0; e < EPC / 2; ++e) {
+                acc[2 * e] += v[q][e].x;
+                acc[2 * e + 1] += v[q][e].y;
+            }
+    }
+    for (; k < k1; ++k) add_partial<EPC>(acc, src + (size_t)k * dim);
+}
+
+// The same sum with the lanes of a cpr-lane worker reading interleaved 16-byte
+// pairs: lane c adds pairs c, c + cpr, c + 2 cpr, ... of each row into
+// acc2[0], acc2[1], ..., so one load instruction of the worker covers
+// consecutive bytes of a row (a lane reading its own contiguous EPC doubles
+// makes every instruction touch a line per lane).  Each element's additions
+// stay in slice order.
+template <int EPC, int AHEAD>
+__device__ __forceinline__ void add_partials_interleaved(double __attribute__((ext_vector_type(2)))* acc2,
+                                                         const double* rows, int64_t k0, int64_t k1, int dim,
+                                                         int cpr, int c) {
+    typedef double __attribute__((ext_vector_type(2))) d2;
+    int64_t k = k0;
+    for (; k + AHEAD <= k1; k += AHEAD) {
+        d2 v[AHEAD][EPC / 2];
+#pragma unroll
+        for (int q = 0; q < AHEAD; ++q) {
+            const d2* row = (const d2*)(rows + (size_t)(k + q) * dim) + c;
+#pragma unroll
+            for (int e = 0; e < EPC / 2; ++e) v[q][e] = row[e * cpr];
+        }
+        __builtin_amdgcn_sched_barrier(0);  // keep the scheduler from interleaving the adds into the loads
+#pragma unroll
+        for (int q = 0; q < AHEAD; ++q)
+#pragma unroll
+            for (int e = 0; e < EPC / 2; ++e) acc2[e] += v[q][e];
+    }
+    for (; k < k1; ++k)
+#pragma unroll
+        for (int e = 0; e < EPC / 2; ++e) acc2[e] += *(const d2*)(rows + (size_t)k * dim + 2 * (e * cpr + c));
+}
+
 // Final write of one run: dense RMW (fp64 add, one rounding) or the compact
 // sum.  key < num_rows and u < n hold for every run of a correct plan; the
 // checks keep each store in bounds regardless.  Compact form with bf16
@@ -601,8 +659,7 @@ __global__ __launch_bounds__(kBlock) void carry_fixup_kernel(
 #pragma unroll
     for (int e = 0; e < EPC; ++e) acc[e] = 0.0;
     add_partial<EPC>(acc, carry_tail + (size_t)j * dim + c * EPC);
-#pragma unroll 8
-    for (int64_t k = j + 1; k <= m; ++k) add_partial<EPC>(acc, carry_head + (size_t)k * dim + c * EPC);
+    add_partials<EPC, 4>(acc, carry_head + c * EPC, j + 1, m + 1, dim);
     const uint32_t u = slice_base(j) + slice_runs[j] - 1;
     write_run<EPC, DENSE>(acc, key, u, c, dim, n, num_rows, grad_dense, uniq_grad);
 }
@@ -610,9 +667,12 @@ __global__ __launch_bounds__(kBlock) void carry_fixup_kernel(
 // Long runs: the block's sub-workers (cpr lanes each) sum equal contiguous
 // shares of the head partials j+1 .. m; the shares are then added in
 // sub-worker order after the tail partial, so the result does not depend on
-// scheduling.  The list order may vary; each run's sum does not.
+// scheduling.  The list order may vary; each run's sum does not.  A block
+// has 8 waves, each lane holding 512 bytes of loads in flight: a long run is
+// few blocks, so their memory parallelism bounds the kernel.
+constexpr int kLongBlock = 512;
 template <int CPR_T, bool BF16, bool DENSE>
-__global__ __launch_bounds__(kBlock) void long_run_kernel(
+__global__ __launch_bounds__(kLongBlock) void long_run_kernel(
     const uint32_t* __restrict__ keys, const uint32_t* __restrict__ counters, uint32_t n, uint32_t num_rows,
     int cpr_rt, int dim, uint32_t num_slices, const uint32_t* __restrict__ slice_runs,
     RunBase slice_base, const double* __restrict__ carry_head,
@@ -625,7 +685,7 @@ __global__ __launch_bounds__(kBlock) void long_run_kernel(
     const int lane = threadIdx.x & 63;
     const int sub = lane / cpr;
     const int c = lane - sub * cpr;
-    const int nsub = wpw * (kBlock / 64);
+    const int nsub = wpw * (kLongBlock / 64);
     const int w = (threadIdx.x >> 6) * wpw + sub;  // sub-worker index in the block
     const bool active = sub < wpw;
     const uint32_t count = min(counters[1], num_slices);
@@ -633,21 +693,25 @@ __global__ __launch_bounds__(kBlock) void long_run_kernel(
         const int64_t j = long_runs[2 * r], m = long_runs[2 * r + 1];
         const int64_t total = m - j;  // head partials j+1 .. m
         const int64_t per = (total + nsub - 1) / nsub;
-        double acc[EPC];
-#pragma unroll
-        for (int e = 0; e < EPC; ++e) acc[e] = 0.0;
         if (active) {
-            const int64_t b = j + 1 + (int64_t)w * per, end = min(b + per, m + 1);
-#pragma unroll 8
-            for (int64_t k = b; k < end; ++k) add_partial<EPC>(acc, carry_head + (size_t)k * dim + c * EPC);
+            double __attribute__((ext_vector_type(2))) acc2[EPC / 2];
 #pragma unroll
-            for (int e = 0; e < EPC; ++e) s_share[(size_t)w * dim + c * EPC + e] = acc[e];
+            for (int e = 0; e < EPC / 2; ++e) acc2[e] = 0.0;
+            const int64_t b = j + 1 + (int64_t)w * per, end = min(b + per, m + 1);
+            add_partials_interleaved<EPC, 64 / EPC>(acc2, carry_head, b, end, dim, cpr, c);  // 512 B per lane in flight
+#pragma unroll
+            for (int e = 0; e < EPC / 2; ++e) {
+                s_share[(size_t)w * dim + 2 * (e * cpr + c)] = acc2[e].x;
+                s_share[(size_t)w * dim + 2 * (e * cpr + c) + 1] = acc2[e].y;
+            }
         }
         __syncthreads();
+        double acc[EPC];
         if (w == 0 && active) {
 #pragma unroll
             for (int e = 0; e < EPC; ++e) acc[e] = 0.0;
             add_partial<EPC>(acc, carry_tail + (size_t)j * dim + c * EPC);
+#pragma unroll 2
             for (int q = 0; q < nsub; ++q)
 #pragma unroll
                 for (int e = 0; e < EPC; ++e) acc[e] += s_share[(size_t)q * dim + c * EPC + e];
@@ -688,8 +752,8 @@ hipError_t launch_reduce(const Layout& L, const char* ws, const void* grad_out, 
                        (const uint32_t*)flags, (const double*)carry_head,
                        (const double*)carry_tail, long_runs, grad_dense, uniq_grad);
     if ((err = hipGetLastError()) != hipSuccess) return err;
-    const size_t share_bytes = (size_t)wpw * (kBlock / 64) * dim * sizeof(double);
-    hipLaunchKernelGGL((long_run_kernel<CPR_T, BF16, DENSE>), dim3(256), dim3(kBlock), share_bytes, stream,
+    const size_t share_bytes = (size_t)wpw * (kLongBlock / 64) * dim * sizeof(double);
+    hipLaunchKernelGGL((long_run_kernel<CPR_T, BF16, DENSE>), dim3(256), dim3(kLongBlock), share_bytes, stream,
                        sorted_keys, (const uint32_t*)counters, n, num_rows, cpr, dim, ns,
                        (const uint32_t*)(ws + L.slice_runs), base, (const double*)carry_head, (const double*)carry_tail, (const uint32_t*)long_runs, grad_dense,
                        uniq_grad);
