@@ -601,7 +601,7 @@ def main():
     # after the main stream's wait for it.
     if wl["backward"]:
         kern["scatter_apply"] = (apply_bytes, phase["scatter_apply"],
-                                 "segment_reduce_kernel<20,bf16> + carry_fixup_kernel", "scatter.hip")
+                                 "segment_reduce_kernel<20,bf16> + carry_fixup_kernel + long_run_kernel", "scatter.hip")
     dom = max(kern, key=lambda k: kern[k][1])
     dbytes, dms, dname, dsrc = kern[dom]
     achieved = dbytes / (dms / 1e3) / 1e9
