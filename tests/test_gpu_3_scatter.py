@@ -305,6 +305,17 @@ def test_large_dense_and_deterministic():
     assert np.array_equal(got[a[0]].view(np.uint32), a[1].view(np.uint32))   # the two forms agree bit for bit
 
 
+def test_sort_beyond_one_shot_counts():
+    """2^22 + 12,305 lookups (1,028 sort tiles): beyond 2^22 the scatter pass
+    sums its tiles' digit counts in loops instead of loading them in one go."""
+    rng = np.random.default_rng(25)
+    R = 320_001_536
+    n = (1 << 22) + 3 * 4096 + 17
+    hot = rng.integers(0, R, size=32)
+    rows = np.where(rng.random(n) < 0.2, hot[rng.integers(0, 32, size=n)], rng.integers(0, R, size=n))
+    check_compact(rows.astype(np.int64), grads(n, dim=8, seed=25), R)
+
+
 def test_large_all_one_row():
     """Every lookup on one row: every sort pass leaves the order as it is."""
     n = LARGE_N

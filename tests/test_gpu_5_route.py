@@ -18,7 +18,10 @@ def ids_for(rng, n, num_embeddings, bad=0.0):
     return ids
 
 
-@pytest.mark.parametrize("world,n", [(1, 1000), (8, 1), (8, 4095), (8, 50000), (64, 70001), (255, 100000)])
+# 2^22 IDs are the most whose sort tiles' counts are each loaded in one go;
+# 2^22 + 12,305 IDs (1,028 tiles) take the looped sums.
+@pytest.mark.parametrize("world,n", [(1, 1000), (8, 1), (8, 4095), (8, 50000), (64, 70001), (255, 100000),
+                                     (64, 1 << 22), (64, (1 << 22) + 3 * 4096 + 17)])
 def test_route_plan_parity(world, n):
     rng = np.random.default_rng(world * 7 + n)
     num_embeddings = world * 12345
