@@ -51,8 +51,8 @@ CSRC = os.path.join(ROOT, "hashed_gram_embedding_engram_amd", "csrc")
 def parse_args():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="long", choices=["long", "full-sft", "owner", "sft", "ple", "route"])
     ap.add_argument("--rotations", type=int, default=4)
     ap.add_argument("--no-cpu-baseline", action="store_true")
