@@ -185,6 +185,20 @@ def run_step(wl, b, ev=None):
             ev[6].record(main)
 
 
+def host_info():
+    """The CPUs this process may run on and their model name (the baseline uses one)."""
+    model = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return {"cpus_available": len(os.sched_getaffinity(0)), "cpu_model": model}
+
+
 def cpu_baseline(wl, max_tokens=None):
     """The oracle (plain single-threaded C) on the same stream as rotation 0."""
     import numpy as np
@@ -221,7 +235,7 @@ def cpu_baseline(wl, max_tokens=None):
         c_oracle.scatter_add_compact(rows, dy, wl["table_rows"], wl["row_begin"])
     t3 = time.perf_counter()
     del out
-    return {"value": n / (t3 - t0), "unit": "lookups/s", "cores": 1, "kind": "oracle",
+    return {"value": n / (t3 - t0), "unit": "lookups/s", "cores": 1, "kind": "oracle", "host": host_info(),
             "sample": "%d tokens (%d lookups) of rotation 0: hash, gather from a host copy of the %d distinct "
                       "rows read, compact scatter-add; single-threaded C" % (ids.size, n, uniq.size),
             "seconds": {"hash": round(t1 - t0, 3), "gather": round(t2 - t1, 3), "scatter_add": round(t3 - t2, 3)}}
@@ -300,7 +314,7 @@ def ple_cpu_baseline(wl, sample_rows=2):
     P.short_conv_backward(x, dc, cw, 3, halo)
     t1 = time.perf_counter()
     tokens = sample_rows * wl["seq"]
-    return {"value": tokens / (t1 - t0), "unit": "tokens/s", "cores": 1, "kind": "oracle",
+    return {"value": tokens / (t1 - t0), "unit": "tokens/s", "cores": 1, "kind": "oracle", "host": host_info(),
             "sample": "%d of the %d batch rows of rotation 0 (%d tokens x %d channels): conv, norm, their "
                       "backwards in fp64 numpy, single-threaded" % (sample_rows, wl["batch"], tokens,
                                                                     wl["channels"]),
@@ -455,7 +469,7 @@ def route_cpu_baseline(wl):
     out = np.empty_like(grouped)
     out[order] = grouped
     t1 = time.perf_counter()
-    return {"value": ids.size / (t1 - t0), "unit": "lookups/s", "cores": 1, "kind": "oracle",
+    return {"value": ids.size / (t1 - t0), "unit": "lookups/s", "cores": 1, "kind": "oracle", "host": host_info(),
             "sample": "rotation 0 in full (%d lookups, world %d, capacity %d), plain Python loops over segments "
                       "with numpy arrays, single-threaded" % (ids.size, W_, cap),
             "seconds": round(t1 - t0, 3)}
