@@ -146,6 +146,24 @@ def test_slice_equals_full_columns():
     assert np.array_equal(E.engram_hash_slice(t2, 1234, 4321, spec).cpu().numpy(), full2[:, 1234:4321])
 
 
+def test_rehash_in_backward():
+    """Rows need not be kept from the forward: rows hashed again in the backward,
+    slice by slice as context-parallel ranks would, give the same gradient bits."""
+    ids, _ = W.long_context_stream(5, total=30000)
+    t = torch.from_numpy(ids).cuda()
+    spec = E.qwen3_8_flash_next_spec()
+    kept = E.engram_hash(t, spec).reshape(-1)
+    g = torch.Generator(device="cuda")
+    g.manual_seed(9)
+    dy = torch.randn((kept.numel(), 160), generator=g, device="cuda").to(torch.bfloat16)
+    ur, ug = E.engram_scatter_add(kept, dy, W.FULL_ROWS)
+    again = torch.cat([E.engram_hash_slice(t, a, b, spec).reshape(-1)
+                       for a, b in ((0, 7000), (7000, 7001), (7001, 30000))])
+    ur2, ug2 = E.engram_scatter_add(again, dy, W.FULL_ROWS)
+    assert torch.equal(ur, ur2)
+    assert torch.equal(ug.view(torch.int32), ug2.view(torch.int32))
+
+
 def test_empty():
     spec = E.qwen3_8_flash_next_spec()
     out = E.engram_hash(torch.empty((0, 5), dtype=torch.int64, device="cuda"), spec)
