@@ -27,15 +27,22 @@ constexpr int kRadix = 256;
 __device__ __forceinline__ uint64_t lanemask_lt(int lane) { return (1ull << lane) - 1ull; }
 
 // Lanes of the wave whose 8-bit digit equals this lane's, among lanes with `live`.
+// Per bit: the lanes whose bit matches this lane's are ~(ballot ^ rep), rep
+// being this lane's bit spread over a word; keeping them is one three-input
+// bitwise instruction per half of the mask.
 __device__ __forceinline__ uint64_t match_digit(uint32_t d, bool live) {
-    uint64_t m = __ballot(live);
+    const uint64_t l = __ballot(live);
+    uint32_t lo = (uint32_t)l, hi = (uint32_t)(l >> 32);
 #pragma unroll
     for (int b = 0; b < 8; ++b) {
-        const bool bit = (d >> b) & 1u;
-        const uint64_t bb = __ballot(bit);
-        m &= bit ? bb : ~bb;
+        const int32_t srep = (int32_t)(d << (31 - b)) >> 31;  // one signed bit-field extract
+        const uint32_t rep = (uint32_t)srep;
+        const uint64_t bb = __ballot(srep < 0);
+        // a & ~(b ^ c): truth table 0x90 with a, b, c as index bits 2, 1, 0
+        lo = __builtin_amdgcn_bitop3_b32(lo, (uint32_t)bb, rep, 0x90);
+        hi = __builtin_amdgcn_bitop3_b32(hi, (uint32_t)(bb >> 32), rep, 0x90);
     }
-    return m;
+    return (uint64_t)hi << 32 | lo;
 }
 
 // Exclusive prefix sum over the 256 threads of a block; *total gets the sum.
