@@ -185,6 +185,13 @@ def run_step(wl, b, ev=None):
             ev[6].record(main)
 
 
+def percentiles(ms):
+    """p10, p50 and p90 of a list of times (nearest rank), rounded to 0.1 us."""
+    v = sorted(ms)
+    at = lambda q: v[min(len(v) - 1, int(q * (len(v) - 1) + 0.5))]
+    return [round(at(0.1), 4), round(at(0.5), 4), round(at(0.9), 4)]
+
+
 def host_info():
     """The CPUs this process may run on and their model name (the baseline uses one)."""
     model = None
@@ -340,6 +347,7 @@ def ple_main(args, dev):
     C = wl["channels"]
     names = ["conv_fwd", "norm_fwd", "norm_bwd", "conv_bwd"]
     phase = {n: sum(e[k].elapsed_time(e[k + 1]) for e in evs) / args.steps for k, n in enumerate(names)}
+    phase_pct = {n: percentiles([e[k].elapsed_time(e[k + 1]) for e in evs]) for k, n in enumerate(names)}
     # Algorithmic bytes per launch (bf16 activations, 2 B per element): forward
     # passes read x and write y (4 B per element); backward passes read x and
     # dy and write dx (6 B per element).  Weights, halos and the weight
@@ -370,6 +378,7 @@ def ple_main(args, dev):
                                "(4 branches x 2,560), fwd+bwd", "batch": wl["batch"], "seq_len": wl["seq"],
                    "channels": C, "rotations": R},
         "phases_ms": {k: round(v, 4) for k, v in phase.items()},
+        "phases_ms_p10_p50_p90": phase_pct,
         "roofline": {"kernel": kname[dom][0], "bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS,
                      "unit": "GB/s", "frac": achieved / HBM_PEAK_GBPS,
                      "traffic": counter_traffic(kname[dom][1], "%s_ple_counters.txt" % dom),
@@ -493,6 +502,7 @@ def route_main(args, dev):
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     phase = {nm: sum(e[k].elapsed_time(e[k + 1]) for e in evs) / args.steps for k, nm in enumerate(names)}
+    phase_pct = {nm: percentiles([e[k].elapsed_time(e[k + 1]) for e in evs]) for k, nm in enumerate(names)}
     n = sum(wl["rots"][i % R]["n"] for i in range(args.steps)) / args.steps
     cap = sum(wl["rots"][i % R]["cap"] for i in range(args.steps)) / args.steps
     Wd, row = wl["world"], 2.0 * W.DIM
@@ -528,6 +538,7 @@ def route_main(args, dev):
                                "full-table row IDs, 320-B bf16 value rows; exchange = identity",
                    "lookups_per_step": int(n), "world": Wd, "capacity": int(cap), "rotations": R},
         "phases_ms": {k: round(v, 4) for k, v in phase.items()},
+        "phases_ms_p10_p50_p90": phase_pct,
         "roofline": {"kernel": kname[dom], "bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS,
                      "unit": "GB/s", "frac": achieved / HBM_PEAK_GBPS,
                      "traffic": counter_traffic("route.hip", "%s_route_counters.txt" % dom),
@@ -588,6 +599,7 @@ def main():
     if wl["backward"]:
         spans.update({"scatter_plan (side stream)": (3, 4), "wait_for_plan": (2, 5), "scatter_apply": (5, 6)})
     phase = {k: sum(e[a].elapsed_time(e[b]) for e in evs) / args.steps for k, (a, b) in spans.items()}
+    phase_pct = {k: percentiles([e[a].elapsed_time(e[b]) for e in evs]) for k, (a, b) in spans.items()}
     n_avg = lookups / args.steps
     U = None
     b0 = wl["batches"][0]
@@ -665,6 +677,7 @@ def main():
             "distinct_rows_rotation0": U, "rotations": R,
         },
         "phases_ms": {k: round(v, 4) for k, v in phase.items()},
+        "phases_ms_p10_p50_p90": phase_pct,
         "roofline": {"kernel": dname, "bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS,
                      "unit": "GB/s", "frac": achieved / HBM_PEAK_GBPS, "traffic": traffic,
                      "algorithmic_bytes_per_launch": dbytes, "avg_launch_ms": dms},
