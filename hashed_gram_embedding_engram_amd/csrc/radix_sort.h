@@ -5,7 +5,8 @@
 // A tile of kTile pairs is owned by one 256-thread block, each wave owning a
 // contiguous span of 64 * kItems pairs.  Per 8-bit digit pass:
 //   histogram   per-tile digit counts (per-wave LDS atomics, then summed),
-//               stored per tile and added into the total of the tile's chunk;
+//               stored per tile and added into the totals of the tile's
+//               chunk and group (see DigitCounts);
 //   downsweep   finds where each of its digits starts from those counts,
 //               ranks every key among the equal digits before it in its wave
 //               span with ballots (no atomics, hence stable), orders the tile
