@@ -516,9 +516,9 @@ def route_main(args, dev):
            "unpermute_values": (2 * row + 8.0) * n}
     dom = max(phase, key=phase.get)
     kname = {"plan": "route_keys_kernel + radix pass + route_output_kernel", "validate": "route_validate_kernel",
-             "pack_ids": "pack_kernel<uint32_t,uint32_t>", "unpack_ids": "unpack_kernel<uint32_t,uint32_t>",
-             "pack_values": "pack_kernel<u32x4,uint32_t>", "unpack_values": "unpack_kernel<u32x4,uint32_t>",
-             "unpermute_values": "permute_kernel<u32x4,false>"}
+             "pack_ids": "pack_kernel<uint32_t,uint32_t,4>", "unpack_ids": "unpack_kernel<uint32_t,uint32_t,4>",
+             "pack_values": "pack_kernel<u32x4,uint32_t,2>", "unpack_values": "unpack_kernel<u32x4,uint32_t,4>",
+             "unpermute_values": "permute_kernel<u32x4,false,1>"}
     achieved = alg[dom] / (phase[dom] / 1e3) / 1e9
     elapsed = t1 - t0
     result = {

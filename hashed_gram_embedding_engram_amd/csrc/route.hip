@@ -200,7 +200,12 @@ __device__ __forceinline__ uint32_t fill_unit<uint32_t>(u32x4 fill, uint32_t k) 
 
 // Copy unit U: 16 bytes when rows allow it, else 4 bytes.  Segment w's
 // min(count, capacity) rows go to block w, the rest of the block is the fill.
-template <typename U, typename I>
+// The copy kernels move K 16-byte (or 4-byte) units per thread per loop
+// step, all loads issued before the stores.  Measured on the world-64 step:
+// K = 4 helps the unpack (the compact side is written sequentially) and the
+// 4-byte units; the pack of 16-byte units gains little and the scattering
+// permute loses, so each launch picks its own K.
+template <typename U, typename I, int K>
 __global__ __launch_bounds__(kBlock) void pack_kernel(const U* __restrict__ src, int64_t row_units,
                                                       const int64_t* __restrict__ counts, int world, int64_t capacity,
                                                       u32x4 fill, U* __restrict__ dst, int64_t* __restrict__ status) {
@@ -212,16 +217,27 @@ __global__ __launch_bounds__(kBlock) void pack_kernel(const U* __restrict__ src,
     const I units = (I)row_units, seg_units = (I)(capacity * row_units);
     const U* __restrict__ s = src + si.off * row_units;
     U* __restrict__ d = dst + (int64_t)w * capacity * row_units;
-    for (I e = (I)blockIdx.x * kBlock + threadIdx.x; e < seg_units; e += (I)gridDim.x * kBlock) {
-        const I r = e / units;
-        d[e] = r < rows ? s[e] : fill_unit<U>(fill, (uint32_t)(e - r * units));
+    const I step = (I)gridDim.x * (I)(kBlock * K);
+    for (I e0 = (I)blockIdx.x * (I)(kBlock * K) + threadIdx.x; e0 < seg_units; e0 += step) {
+        U v[K];
+#pragma unroll
+        for (int k = 0; k < K; ++k) {
+            const I e = e0 + (I)(k * kBlock);
+            const I r = e / units;
+            v[k] = (e < seg_units && r < rows) ? s[e] : fill_unit<U>(fill, (uint32_t)(e - r * units));
+        }
+#pragma unroll
+        for (int k = 0; k < K; ++k) {
+            const I e = e0 + (I)(k * kBlock);
+            if (e < seg_units) d[e] = v[k];
+        }
     }
 }
 
 // Segment w's first min(count, capacity) rows of block w, appended in rank
 // order to the compact output; rows at or past dst_rows are dropped (status
 // world).
-template <typename U, typename I>
+template <typename U, typename I, int K>
 __global__ __launch_bounds__(kBlock) void unpack_kernel(const U* __restrict__ src, int64_t row_units,
                                                         const int64_t* __restrict__ counts, int world, int64_t capacity,
                                                         U* __restrict__ dst, int64_t dst_rows,
@@ -238,24 +254,54 @@ __global__ __launch_bounds__(kBlock) void unpack_kernel(const U* __restrict__ sr
     const I seg_units = (I)(fit * row_units);
     const U* __restrict__ s = src + (int64_t)w * capacity * row_units;
     U* __restrict__ d = dst + si.off * row_units;
-    for (I e = (I)blockIdx.x * kBlock + threadIdx.x; e < seg_units; e += (I)gridDim.x * kBlock) d[e] = s[e];
+    const I step = (I)gridDim.x * (I)(kBlock * K);
+    for (I e0 = (I)blockIdx.x * (I)(kBlock * K) + threadIdx.x; e0 < seg_units; e0 += step) {
+        U v[K];
+#pragma unroll
+        for (int k = 0; k < K; ++k) {
+            const I e = e0 + (I)(k * kBlock);
+            if (e < seg_units) v[k] = s[e];
+        }
+#pragma unroll
+        for (int k = 0; k < K; ++k) {
+            const I e = e0 + (I)(k * kBlock);
+            if (e < seg_units) d[e] = v[k];
+        }
+    }
 }
 
 // dst[i] = src[order[i]] (gather) or dst[order[i]] = src[i] (scatter); an
 // index outside [0, n) is skipped.
-template <typename U, bool GATHER>
+template <typename U, bool GATHER, int K>
 __global__ __launch_bounds__(kBlock) void permute_kernel(const U* __restrict__ src, int64_t row_units,
                                                          const int64_t* __restrict__ order, int64_t n,
                                                          U* __restrict__ dst) {
     const int64_t total = n * row_units;
-    for (int64_t e = (int64_t)blockIdx.x * kBlock + threadIdx.x; e < total; e += (int64_t)gridDim.x * kBlock) {
-        const int64_t i = e / row_units, k = e - i * row_units;
-        const int64_t o = order[i];
-        if ((uint64_t)o >= (uint64_t)n) continue;
-        if (GATHER)
-            dst[e] = src[o * row_units + k];
-        else
-            dst[o * row_units + k] = src[e];
+    const int64_t step = (int64_t)gridDim.x * (kBlock * K);
+    for (int64_t e0 = (int64_t)blockIdx.x * (kBlock * K) + threadIdx.x; e0 < total; e0 += step) {
+        int64_t at[K];  // the other side's unit, or -1
+        U v[K];
+#pragma unroll
+        for (int k = 0; k < K; ++k) {
+            const int64_t e = e0 + k * kBlock;
+            at[k] = -1;
+            if (e < total) {
+                const int64_t i = e / row_units;
+                const int64_t o = order[i];
+                if ((uint64_t)o < (uint64_t)n) at[k] = o * row_units + (e - i * row_units);
+            }
+        }
+#pragma unroll
+        for (int k = 0; k < K; ++k)
+            if (at[k] >= 0) v[k] = GATHER ? src[at[k]] : src[e0 + k * kBlock];
+#pragma unroll
+        for (int k = 0; k < K; ++k)
+            if (at[k] >= 0) {
+                if (GATHER)
+                    dst[e0 + k * kBlock] = v[k];
+                else
+                    dst[at[k]] = v[k];
+            }
     }
 }
 
@@ -319,13 +365,13 @@ hipError_t launch_route_validate(const int64_t* sorted_ids, int64_t n, const int
     return hipGetLastError();
 }
 
-#define ENGRAM_SEGMENT_LAUNCH(KERNEL, U, UNITS, ...)                                                       \
+#define ENGRAM_SEGMENT_LAUNCH(KERNEL, U, K, UNITS, ...)                                                    \
     do {                                                                                                   \
-        const dim3 grid = segment_grid(UNITS, world);                                                     \
-        if ((UNITS) < ((int64_t)1 << 31) - (int64_t)grid.x * kBlock)                                       \
-            hipLaunchKernelGGL((KERNEL<U, uint32_t>), grid, dim3(kBlock), 0, stream, __VA_ARGS__);        \
+        const dim3 grid = segment_grid(((UNITS) + (K) - 1) / (K), world);                                 \
+        if ((UNITS) < ((int64_t)1 << 31) - (int64_t)grid.x * kBlock * (K))                                 \
+            hipLaunchKernelGGL((KERNEL<U, uint32_t, K>), grid, dim3(kBlock), 0, stream, __VA_ARGS__);     \
         else                                                                                               \
-            hipLaunchKernelGGL((KERNEL<U, uint64_t>), grid, dim3(kBlock), 0, stream, __VA_ARGS__);        \
+            hipLaunchKernelGGL((KERNEL<U, uint64_t, K>), grid, dim3(kBlock), 0, stream, __VA_ARGS__);     \
     } while (0)
 
 hipError_t launch_pack(const void* src, int64_t row_bytes, const int64_t* counts, int world, int64_t capacity,
@@ -336,12 +382,12 @@ hipError_t launch_pack(const void* src, int64_t row_bytes, const int64_t* counts
     if (wide) {
         const int64_t units = row_bytes / 16;
         const u32x4 f = {fill16[0], fill16[1], fill16[2], fill16[3]};
-        ENGRAM_SEGMENT_LAUNCH(pack_kernel, u32x4, capacity * units, (const u32x4*)src, units, counts, world, capacity,
+        ENGRAM_SEGMENT_LAUNCH(pack_kernel, u32x4, 2, capacity * units, (const u32x4*)src, units, counts, world, capacity,
                               f, (u32x4*)dst, status);
     } else {
         const int64_t units = row_bytes / 4;
         const u32x4 f = {fill16[0], fill16[1], fill16[2], fill16[3]};
-        ENGRAM_SEGMENT_LAUNCH(pack_kernel, uint32_t, capacity * units, (const uint32_t*)src, units, counts, world,
+        ENGRAM_SEGMENT_LAUNCH(pack_kernel, uint32_t, 4, capacity * units, (const uint32_t*)src, units, counts, world,
                               capacity, f, (uint32_t*)dst, status);
     }
     return hipGetLastError();
@@ -355,11 +401,11 @@ hipError_t launch_unpack(const void* src, int64_t row_bytes, const int64_t* coun
     const int64_t rows = capacity < dst_rows ? capacity : dst_rows;  // at most per segment
     if (wide) {
         const int64_t units = row_bytes / 16;
-        ENGRAM_SEGMENT_LAUNCH(unpack_kernel, u32x4, rows * units, (const u32x4*)src, units, counts, world, capacity,
+        ENGRAM_SEGMENT_LAUNCH(unpack_kernel, u32x4, 4, rows * units, (const u32x4*)src, units, counts, world, capacity,
                               (u32x4*)dst, dst_rows, status);
     } else {
         const int64_t units = row_bytes / 4;
-        ENGRAM_SEGMENT_LAUNCH(unpack_kernel, uint32_t, rows * units, (const uint32_t*)src, units, counts, world,
+        ENGRAM_SEGMENT_LAUNCH(unpack_kernel, uint32_t, 4, rows * units, (const uint32_t*)src, units, counts, world,
                               capacity, (uint32_t*)dst, dst_rows, status);
     }
     return hipGetLastError();
@@ -372,16 +418,16 @@ hipError_t launch_permute(const void* src, int64_t row_bytes, const int64_t* ord
     const int64_t units = wide ? row_bytes / 16 : row_bytes / 4;
     const dim3 grid(grid_for(n * units)), block(kBlock);
     if (wide && gather)
-        hipLaunchKernelGGL((permute_kernel<u32x4, true>), grid, block, 0, stream, (const u32x4*)src, units, order, n,
+        hipLaunchKernelGGL((permute_kernel<u32x4, true, 1>), grid, block, 0, stream, (const u32x4*)src, units, order, n,
                            (u32x4*)dst);
     else if (wide)
-        hipLaunchKernelGGL((permute_kernel<u32x4, false>), grid, block, 0, stream, (const u32x4*)src, units, order, n,
+        hipLaunchKernelGGL((permute_kernel<u32x4, false, 1>), grid, block, 0, stream, (const u32x4*)src, units, order, n,
                            (u32x4*)dst);
     else if (gather)
-        hipLaunchKernelGGL((permute_kernel<uint32_t, true>), grid, block, 0, stream, (const uint32_t*)src, units,
+        hipLaunchKernelGGL((permute_kernel<uint32_t, true, 1>), grid, block, 0, stream, (const uint32_t*)src, units,
                            order, n, (uint32_t*)dst);
     else
-        hipLaunchKernelGGL((permute_kernel<uint32_t, false>), grid, block, 0, stream, (const uint32_t*)src, units,
+        hipLaunchKernelGGL((permute_kernel<uint32_t, false, 1>), grid, block, 0, stream, (const uint32_t*)src, units,
                            order, n, (uint32_t*)dst);
     return hipGetLastError();
 }
