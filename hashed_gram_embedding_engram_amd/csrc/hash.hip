@@ -35,8 +35,13 @@ __device__ __forceinline__ uint64_t floor_mod(int64_t m, uint64_t p, uint64_t ma
     return neg ? p - 1 - r : r;
 }
 
+// One wave per block: a wave's positions share nothing with other waves (its
+// LDS rows are its own), and small token batches then spread over every
+// compute unit instead of a few four-wave blocks.
+constexpr int kHashBlock = 64;
+
 template <int NG, int HPN>
-__global__ __launch_bounds__(256) void hash_kernel(const int64_t* __restrict__ tokens, int64_t seq_len,
+__global__ __launch_bounds__(kHashBlock) void hash_kernel(const int64_t* __restrict__ tokens, int64_t seq_len,
                                                    int64_t seq_begin, int64_t width, int64_t total,
                                                    HashParams p, int64_t* __restrict__ rows_out) {
     const int ng = NG ? NG : p.ngram_size;
@@ -75,7 +80,7 @@ __global__ __launch_bounds__(256) void hash_kernel(const int64_t* __restrict__ t
         // store instruction writes 1 KiB of consecutive 16-byte chunks.
         typedef long long i64x2 __attribute__((ext_vector_type(2)));
         constexpr int kPad = 18;  // int64 per position in LDS: 16 rows + 16 bytes against bank conflicts
-        __shared__ int64_t s_rows[256 / 64][64 * kPad];
+        __shared__ int64_t s_rows[kHashBlock / 64][64 * kPad];
         int64_t* mine = &s_rows[threadIdx.x >> 6][lane * kPad];
         if (live) {
 #pragma unroll
@@ -150,7 +155,7 @@ hipError_t launch_hash(const int64_t* tokens, int64_t batch, int64_t seq_len, in
     const int64_t width = seq_end - seq_begin;
     const int64_t total = batch * width;
     if (total == 0) return hipSuccess;
-    const int block = 256;
+    const int block = kHashBlock;
     const int64_t grid = (total + block - 1) / block;
     if (p.ngram_size == 3 && p.heads_per_ngram == 8)
         hipLaunchKernelGGL((hash_kernel<3, 8>), dim3((unsigned)grid), dim3(block), 0, stream, tokens, seq_len,
