@@ -192,3 +192,39 @@ def test_loopback_world_forward_and_backward():
         mine = (rur >= d * local) & (rur < (d + 1) * local)
         got = shard_grad[torch.from_numpy(rur[mine] - d * local).cuda()].cpu().numpy()
         assert_close_to_fp64(got, rug[mine], "owner %d gradient" % d)
+
+
+def test_route_bench_shape():
+    """The benchmarked exchange half: one request rank of world 64 (8 x 4,096
+    Zipf tokens hashed into 524,288 full-table IDs), capacity the largest
+    count, 320-byte bf16 value rows; the same calls the benchmark times."""
+    world = 64
+    ids = W.owner_token_batches(seeds=[100])[0]
+    gids = E.engram_hash(torch.from_numpy(ids).cuda(), E.qwen3_8_flash_next_spec()).reshape(-1).contiguous()
+    n = gids.numel()
+    s, order, c = E.engram_route_plan(gids, W.FULL_ROWS, world)
+    ids_h = gids.cpu().numpy()
+    rs, ro, rc, rbad = RR.route_plan(ids_h, W.FULL_ROWS, world)
+    assert rbad == -1
+    assert np.array_equal(s.cpu().numpy(), rs) and np.array_equal(order.cpu().numpy(), ro)
+    assert np.array_equal(c.cpu().numpy(), rc)
+    assert int(E.engram_route_validate(s, c, W.FULL_ROWS, world).item()) == -1
+    cap = int(rc.max())
+    status = torch.empty((), dtype=torch.int64, device="cuda")
+    packed_ids = E.engram_pack_fixed_capacity(s, c, world, cap, fill=-1, status=status)
+    ref_ids, _ = RR.pack(rs, rc, world, cap, -1)
+    assert np.array_equal(packed_ids.cpu().numpy(), ref_ids) and int(status.item()) == -1
+    assert torch.equal(E.engram_unpack_fixed_capacity(packed_ids, c, n, status=status), s)
+    g = torch.Generator(device="cuda")
+    g.manual_seed(3000)
+    vals = torch.randn((n, 160), generator=g, device="cuda").to(torch.bfloat16)
+    packed = E.engram_pack_fixed_capacity(vals, c, world, cap, fill=0.0, status=status)
+    vals_h = vals.cpu().view(torch.int16).numpy()
+    ref_packed, _ = RR.pack(vals_h, rc, world, cap, 0)
+    assert np.array_equal(packed.cpu().view(torch.int16).numpy(), ref_packed)
+    back = E.engram_unpack_fixed_capacity(packed, c, n, status=status)
+    assert np.array_equal(back.cpu().view(torch.int16).numpy(), RR.unpack(ref_packed, rc, n))
+    out = E.engram_unpermute_rows(back, order)
+    ref_out = np.empty_like(vals_h)
+    ref_out[ro] = vals_h
+    assert np.array_equal(out.cpu().view(torch.int16).numpy(), ref_out)

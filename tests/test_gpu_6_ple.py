@@ -194,3 +194,75 @@ def test_grouped_rms_norm_empty():
     assert E.engram_grouped_rms_norm(x, w, 32).shape == (0, 64)
     dx, dw = E.engram_grouped_rms_norm_backward(x, x, w, 32)
     assert dx.shape == (0, 64) and not dw.any()
+
+
+def test_ple_bench_shape_sampled():
+    """The benchmarked layer shape, [8, 4096, 10240] bf16 with a halo, through the
+    same kernels the benchmark times.  Outputs are checked at sampled positions
+    (the oracle gets just the inputs they depend on), the weight gradients over
+    whole channels and one whole group of the norm."""
+    import workloads as W
+    B, S, C, G, d, K = 8, 4096, 10240, 2560, 3, 4
+    H = (K - 1) * d
+    t = W.ple_tensors(torch.device("cuda"), 2000, B, S, C)
+    x, dy, halo, w, b, nw = t["x"], t["dy"], t["halo"], t["conv_w"], t["conv_b"], t["norm_w"]
+    y = E.engram_short_conv(x, w, b, dilation=d, halo=halo)
+    dx, dw, db, dhalo = E.engram_short_conv_backward(x, dy, w, dilation=d, halo=halo, want_bias=True,
+                                                     want_halo=True)
+    z = E.engram_grouped_rms_norm(x.reshape(B * S, C), nw, G)
+    dxn, dnw = E.engram_grouped_rms_norm_backward(x.reshape(B * S, C), dy.reshape(B * S, C), nw, G)
+    w_np, b_np, nw_np = w.cpu().numpy(), b.cpu().numpy(), nw.cpu().numpy()
+    halo_h = halo.double().cpu().numpy()
+    rng = np.random.default_rng(77)
+    samples = [(0, 0), (0, 1), (7, 8), (3, 9), (5, S - 1), (1, S - 10)] + \
+        [(int(rng.integers(B)), int(rng.integers(S))) for _ in range(10)]
+    for bi, ti in samples:
+        # conv output at (bi, ti): its window and, near the start, the halo
+        lo = max(0, ti - H)
+        xs = x[bi, lo:ti + 1].double().cpu().numpy()[None]
+        hs = halo_h[bi:bi + 1] if lo == 0 else np.zeros((1, H, C))
+        ref = P.short_conv(xs, w_np, b_np, d, hs)[0, -1]
+        mag = conv_mag(xs, w_np, b_np, d, hs)[0, -1]
+        assert_within(y[bi, ti], ref, mag, True, "y at %s" % ((bi, ti),))
+        # conv input gradient at (bi, ti): the output gradients after it
+        hi = min(S, ti + H + 1)
+        xs2 = x[bi, ti:hi].double().cpu().numpy()[None]
+        dys2 = dy[bi, ti:hi].double().cpu().numpy()[None]
+        rdx = P.short_conv_backward(xs2, dys2, w_np, d, np.zeros((1, H, C)))[0][0, 0]
+        adx = P.short_conv_backward(np.abs(xs2), np.abs(dys2), np.abs(w_np), d, np.zeros((1, H, C)))[0][0, 0]
+        assert_within(dx[bi, ti], rdx, adx, True, "dx at %s" % ((bi, ti),))
+        # the norm of row (bi, ti) and its input gradient
+        r = bi * S + ti
+        xr = x.reshape(B * S, C)[r].double().cpu().numpy()[None]
+        dyr = dy.reshape(B * S, C)[r].double().cpu().numpy()[None]
+        zr = P.grouped_rms_norm(xr, nw_np, G)
+        assert_within(z[r], zr[0], np.abs(zr[0]), True, "norm at row %d" % r)
+        rdxn, _ = P.grouped_rms_norm_backward(xr, dyr, nw_np, G)
+        g3 = xr.reshape(1, C // G, G)
+        inv = 1.0 / np.sqrt((g3 * g3).mean(axis=-1, keepdims=True) + 1e-6)
+        dn = np.abs(dyr * (1.0 + nw_np)).reshape(g3.shape)
+        mag_dx = (inv * dn + inv ** 3 * np.abs(g3) * (dn * np.abs(g3)).mean(axis=-1, keepdims=True)).reshape(1, C)
+        assert_within(dxn[r], rdxn[0], mag_dx[0], True, "norm dx at row %d" % r)
+    # halo gradient: the first 9 positions' output gradients of every batch row
+    xs = x[:, :H].double().cpu().numpy()
+    dys = dy[:, :H].double().cpu().numpy()
+    rdh = P.short_conv_backward(xs, dys, w_np, d, halo_h)[3]
+    adh = P.short_conv_backward(np.abs(xs), np.abs(dys), np.abs(w_np), d, np.abs(halo_h))[3]
+    assert_within(dhalo, rdh, adh, True, "dhalo")
+    # conv weight and bias gradients of a few whole channels (channels are independent)
+    cs = np.array([0, 1, 2559, 2560, 5000, 7681, C - 1])
+    xc = x[:, :, cs].double().cpu().numpy()
+    dyc = dy[:, :, cs].double().cpu().numpy()
+    hc = halo_h[:, :, cs]
+    _, rdw, rdb, _ = P.short_conv_backward(xc, dyc, w_np[cs], d, hc)
+    _, adw, adb, _ = P.short_conv_backward(np.abs(xc), np.abs(dyc), np.abs(w_np[cs]), d, np.abs(hc))
+    assert_within(dw[torch.from_numpy(cs).cuda()], rdw, adw, False, "dweight")
+    assert_within(db[torch.from_numpy(cs).cuda()], rdb, adb, False, "dbias")
+    # norm weight gradient over every row for the features of one whole group
+    g0 = 2 * G
+    xg = x.reshape(B * S, C)[:, g0:g0 + G].double().cpu().numpy()
+    dyg = dy.reshape(B * S, C)[:, g0:g0 + G].double().cpu().numpy()
+    _, rdnw = P.grouped_rms_norm_backward(xg, dyg, nw_np[g0:g0 + G], G)
+    invg = 1.0 / np.sqrt((xg * xg).mean(axis=-1, keepdims=True) + 1e-6)
+    mag_dnw = (np.abs(dyg) * np.abs(xg * invg)).sum(axis=0)
+    assert_within(dnw[g0:g0 + G], rdnw, mag_dnw, False, "norm dweight")
