@@ -231,6 +231,8 @@ __global__ __launch_bounds__(kPleBlock) void short_conv_bwd_kernel(
 // instead of once per tap.  Window indices are compile-time constants: the
 // window lives in registers.
 
+// Build-time tuning parameters (positions per step, positions per tile), at
+// the measured best of steps 3, 6, 9 and tiles 96, 144, 192.
 #ifndef ENGRAM_CONV_STEP
 #define ENGRAM_CONV_STEP 3
 #endif

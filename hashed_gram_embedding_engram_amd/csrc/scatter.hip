@@ -38,6 +38,11 @@
 namespace engram {
 namespace {
 
+// Build-time tuning parameters of the reduce, at the values measured best on
+// the long-context and owner-shard workloads: entries per worker slice (32 and
+// 128 were slower), non-temporal sum stores (plain stores were slower),
+// non-temporal gradient loads (slower: off), gradient rows in flight per lane
+// (8, 12 and 24 were no better).
 #ifndef ENGRAM_REDUCE_SLICE
 #define ENGRAM_REDUCE_SLICE 64
 #endif
