@@ -118,6 +118,24 @@ def test_hot_row_stress():
     assert_close_to_fp64(got, ref, "dense hot row")
 
 
+@pytest.mark.parametrize("dtype,dim", [(torch.float32, 160), (torch.float32, 12), (torch.bfloat16, 64)])
+def test_hot_row_other_widths(dtype, dim):
+    """A row with 40,000 hits (625 reduce slices: a run summed in chunks) and one
+    with 3,000 (under the chunked size) among uniform rows, in both output forms,
+    for fp32 gradients and other row widths."""
+    rng = np.random.default_rng(dim + 3)
+    n = 120000
+    rows = rng.integers(0, 50000, size=n).astype(np.int64)
+    idx = rng.permutation(n)
+    rows[idx[:40000]] = 4242
+    rows[idx[40000:43000]] = 17
+    dy = grads(n, dim=dim, dtype=dtype, seed=dim)
+    check_compact(rows, dy, 50000)
+    got, _ = run_dense(rows, dy, 50000)
+    ref, _ = c_oracle.scatter_add_dense(rows, to_host(dy), 50000)
+    assert_close_to_fp64(got, ref, "dense hot rows, width %d" % dim)
+
+
 def test_all_same_row_and_sorted_input():
     n = 100000
     dy = grads(n, seed=5)
