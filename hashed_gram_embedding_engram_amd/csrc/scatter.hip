@@ -84,7 +84,7 @@ constexpr uint32_t kFlagHead = 1, kFlagWhole = 2, kFlagTail = 4;
 
 struct Layout {
     size_t sorted_keys, spare_keys, sorted_vals, spare_vals, hist, count_totals, counters, slice_runs, slice_base,
-        slice_first, slice_flags, long_runs, carry_head, carry_tail, block_runs, block_base, total;
+        slice_first, slice_flags, long_runs, long_done, carry_head, carry_tail, block_runs, block_base, total;
     int64_t num_tiles, num_slices, num_run_blocks;
 };
 constexpr int kMaxPasses = 4;  // 32-bit keys, 8-bit digits
@@ -110,6 +110,7 @@ Layout make_layout(int64_t n, int dim) {
     L.slice_first = take(4 * (size_t)L.num_slices);
     L.slice_flags = take(4 * (size_t)L.num_slices);
     L.long_runs = take(8 * (size_t)L.num_slices);
+    L.long_done = take(4 * (size_t)L.num_slices);
     L.carry_head = take(8 * (size_t)L.num_slices * (size_t)dim);
     L.carry_tail = take(8 * (size_t)L.num_slices * (size_t)dim);
     L.block_runs = take(4 * (size_t)L.num_run_blocks);
@@ -497,7 +498,8 @@ __global__ __launch_bounds__(kBlock) void segment_reduce_kernel(
     const u32x4* __restrict__ dy, uint32_t n, uint32_t num_rows, int cpr_rt, int dim, uint32_t num_slices,
     RunBase slice_base, const uint32_t* __restrict__ slice_first,
     float* __restrict__ grad_dense, float* __restrict__ uniq_grad,
-    double* __restrict__ carry_head, double* __restrict__ carry_tail, uint32_t* __restrict__ slice_flags) {
+    double* __restrict__ carry_head, double* __restrict__ carry_tail, uint32_t* __restrict__ slice_flags,
+    uint32_t* __restrict__ long_done) {
     constexpr int EPC = BF16 ? 8 : 4;
     constexpr int B = kReduceBatch;
     const int cpr = CPR_T ? CPR_T : cpr_rt;
@@ -510,6 +512,9 @@ __global__ __launch_bounds__(kBlock) void segment_reduce_kernel(
     const int64_t wave = (int64_t)blockIdx.x * (kBlock / 64) + (threadIdx.x >> 6);
     const int64_t j = wave * wpw + sub;
     if (blockIdx.x == 0 && threadIdx.x == 0) counters[1] = 0;  // long-run list of the fix-up that follows
+    // finished-part counts of the long-run sums two kernels on
+    for (uint64_t i = (uint64_t)blockIdx.x * kBlock + threadIdx.x; i < num_slices; i += (uint64_t)gridDim.x * kBlock)
+        long_done[i] = 0;
     if (sub >= wpw || j >= num_slices) return;
     const uint32_t nv = min(counters[0], n);
     // Worker j covers [first run start in slice j, first run start in slice
@@ -669,22 +674,33 @@ __global__ __launch_bounds__(kBlock) void carry_fixup_kernel(
     write_run<EPC, DENSE>(acc, key, u, c, dim, n, num_rows, grad_dense, uniq_grad);
 }
 
-// Long runs: the block's sub-workers (cpr lanes each) sum equal contiguous
-// shares of the head partials j+1 .. m; the shares are then added in
-// sub-worker order after the tail partial, so the result does not depend on
-// scheduling.  The list order may vary; each run's sum does not.  A block
-// has 8 waves, each lane holding 512 bytes of loads in flight: a long run is
-// few blocks, so their memory parallelism bounds the kernel.
+// Long runs.  A run's head partials j+1 .. m are cut into parts of about
+// kPartSlices slices (at most kMaxParts), each summed by one block: the
+// block's sub-workers (cpr lanes each) sum equal contiguous shares of the
+// part, and the shares are added in sub-worker order.  A one-part run is
+// finished by its block: tail partial plus the shares.  Otherwise each block
+// leaves its part's sum in place of the part's first partial and counts
+// itself done; the block that counts last (a fence before the count releases
+// its sum, a fence after it acquires the others') adds the tail partial and
+// the part sums in part order.  The sum of a run does not depend on
+// scheduling; the list order may vary.  Work items are (part, run) pairs with
+// the first parts of all runs first, so every run's first part goes to a
+// different block.  A block has 8 waves, each lane holding 512 bytes of loads
+// in flight.
 constexpr int kLongBlock = 512;
+constexpr int64_t kPartSlices = 128;  // 64 was slower (more fences), 256 no faster
+constexpr int64_t kMaxParts = 32;
+
 template <int CPR_T, bool BF16, bool DENSE>
 __global__ __launch_bounds__(kLongBlock) void long_run_kernel(
     const uint32_t* __restrict__ keys, const uint32_t* __restrict__ counters, uint32_t n, uint32_t num_rows,
     int cpr_rt, int dim, uint32_t num_slices, const uint32_t* __restrict__ slice_runs,
-    RunBase slice_base, const double* __restrict__ carry_head,
-    const double* __restrict__ carry_tail, const uint32_t* __restrict__ long_runs, float* __restrict__ grad_dense,
-    float* __restrict__ uniq_grad) {
+    RunBase slice_base, double* __restrict__ carry_head,
+    const double* __restrict__ carry_tail, const uint32_t* __restrict__ long_runs,
+    uint32_t* __restrict__ long_done, float* __restrict__ grad_dense, float* __restrict__ uniq_grad) {
     constexpr int EPC = BF16 ? 8 : 4;
     extern __shared__ double s_share[];  // [sub-workers][dim]
+    __shared__ uint32_t s_last;
     const int cpr = CPR_T ? CPR_T : cpr_rt;
     const int wpw = 64 / cpr;
     const int lane = threadIdx.x & 63;
@@ -694,15 +710,22 @@ __global__ __launch_bounds__(kLongBlock) void long_run_kernel(
     const int w = (threadIdx.x >> 6) * wpw + sub;  // sub-worker index in the block
     const bool active = sub < wpw;
     const uint32_t count = min(counters[1], num_slices);
-    for (uint32_t r = blockIdx.x; r < count; r += gridDim.x) {
+    const uint64_t items = (uint64_t)count * kMaxParts;
+    for (uint64_t it = blockIdx.x; it < items; it += gridDim.x) {
+        const uint32_t r = (uint32_t)(it % count);
+        const int64_t p = (int64_t)(it / count);
         const int64_t j = long_runs[2 * r], m = long_runs[2 * r + 1];
         const int64_t total = m - j;  // head partials j+1 .. m
-        const int64_t per = (total + nsub - 1) / nsub;
+        const int64_t parts = min(kMaxParts, (total + kPartSlices - 1) / kPartSlices);
+        if (p >= parts) continue;  // uniform over the block
+        const int64_t per_part = (total + parts - 1) / parts;
+        const int64_t p0 = j + 1 + p * per_part, p1 = min(p0 + per_part, m + 1);
+        const int64_t per = (p1 - p0 + nsub - 1) / nsub;
         if (active) {
             double __attribute__((ext_vector_type(2))) acc2[EPC / 2];
 #pragma unroll
             for (int e = 0; e < EPC / 2; ++e) acc2[e] = 0.0;
-            const int64_t b = j + 1 + (int64_t)w * per, end = min(b + per, m + 1);
+            const int64_t b = min(p0 + (int64_t)w * per, p1), end = min(b + per, p1);
             add_partials_interleaved<EPC, 64 / EPC>(acc2, carry_head, b, end, dim, cpr, c);  // 512 B per lane in flight
 #pragma unroll
             for (int e = 0; e < EPC / 2; ++e) {
@@ -715,11 +738,52 @@ __global__ __launch_bounds__(kLongBlock) void long_run_kernel(
         if (w == 0 && active) {
 #pragma unroll
             for (int e = 0; e < EPC; ++e) acc[e] = 0.0;
-            add_partial<EPC>(acc, carry_tail + (size_t)j * dim + c * EPC);
+            if (parts == 1) add_partial<EPC>(acc, carry_tail + (size_t)j * dim + c * EPC);
 #pragma unroll 2
             for (int q = 0; q < nsub; ++q)
 #pragma unroll
                 for (int e = 0; e < EPC; ++e) acc[e] += s_share[(size_t)q * dim + c * EPC + e];
+            if (parts > 1) store_partial<EPC>(carry_head + (size_t)p0 * dim + c * EPC, acc);
+        }
+        bool finish = parts == 1;
+        if (parts > 1) {
+            // Only wave 0 (sub-worker 0) writes and reads part sums, so only
+            // it fences: each fence writes back or invalidates a whole L2.
+            if (threadIdx.x < 64) __threadfence();
+            __syncthreads();
+            if (threadIdx.x == 0) s_last = atomicAdd(&long_done[r], 1u) == (uint32_t)(parts - 1) ? 1u : 0u;
+            __syncthreads();
+            finish = s_last != 0;
+            if (finish && threadIdx.x < 64) {
+                __threadfence();
+                if (w == 0 && active) {
+#pragma unroll
+                    for (int e = 0; e < EPC; ++e) acc[e] = 0.0;
+                    add_partial<EPC>(acc, carry_tail + (size_t)j * dim + c * EPC);
+                    // the part sums, eight loads at a time (indices clamped, so always in bounds)
+                    typedef double __attribute__((ext_vector_type(2))) d2;
+                    for (int64_t q0 = 0; q0 < parts; q0 += 8) {
+                        d2 v[8][EPC / 2];
+#pragma unroll
+                        for (int qq = 0; qq < 8; ++qq) {
+                            const int64_t q = min(q0 + qq, parts - 1);
+                            const d2* src = (const d2*)(carry_head + (size_t)(j + 1 + q * per_part) * dim + c * EPC);
+#pragma unroll
+                            for (int e = 0; e < EPC / 2; ++e) v[qq][e] = src[e];
+                        }
+#pragma unroll
+                        for (int qq = 0; qq < 8; ++qq)
+                            if (q0 + qq < parts)
+#pragma unroll
+                                for (int e = 0; e < EPC / 2; ++e) {
+                                    acc[2 * e] += v[qq][e].x;
+                                    acc[2 * e + 1] += v[qq][e].y;
+                                }
+                    }
+                }
+            }
+        }
+        if (finish && w == 0 && active) {
             const uint32_t key = keys[min((uint32_t)(j + 1) * kSlice - 1, n - 1)];
             const uint32_t u = slice_base(j) + slice_runs[j] - 1;
             write_run<EPC, DENSE>(acc, key, u, c, dim, n, num_rows, grad_dense, uniq_grad);
@@ -742,13 +806,14 @@ hipError_t launch_reduce(const Layout& L, const char* ws, const void* grad_out, 
     uint32_t* flags = (uint32_t*)(ws + L.slice_flags);
     uint32_t* counters = (uint32_t*)(ws + L.counters);
     uint32_t* long_runs = (uint32_t*)(ws + L.long_runs);
+    uint32_t* long_done = (uint32_t*)(ws + L.long_done);
     uint32_t shift = 0;
     while ((kSlice << shift) < run_span(n)) ++shift;
     const RunBase base{(const uint32_t*)(ws + L.slice_base), (const uint32_t*)(ws + L.block_base), shift};
     hipLaunchKernelGGL((segment_reduce_kernel<CPR_T, BF16, DENSE>), dim3((unsigned)grid), dim3(kBlock), 0, stream,
                        sorted_keys, sorted_vals, counters, (const u32x4*)grad_out, n, num_rows, cpr, dim, ns,
                        base, (const uint32_t*)(ws + L.slice_first), grad_dense, uniq_grad, carry_head, carry_tail,
-                       flags);
+                       flags, long_done);
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
     hipLaunchKernelGGL((carry_fixup_kernel<CPR_T, BF16, DENSE>), dim3((unsigned)grid), dim3(kBlock), 0, stream,
@@ -760,8 +825,8 @@ hipError_t launch_reduce(const Layout& L, const char* ws, const void* grad_out, 
     const size_t share_bytes = (size_t)wpw * (kLongBlock / 64) * dim * sizeof(double);
     hipLaunchKernelGGL((long_run_kernel<CPR_T, BF16, DENSE>), dim3(256), dim3(kLongBlock), share_bytes, stream,
                        sorted_keys, (const uint32_t*)counters, n, num_rows, cpr, dim, ns,
-                       (const uint32_t*)(ws + L.slice_runs), base, (const double*)carry_head, (const double*)carry_tail, (const uint32_t*)long_runs, grad_dense,
-                       uniq_grad);
+                       (const uint32_t*)(ws + L.slice_runs), base, carry_head, (const double*)carry_tail,
+                       (const uint32_t*)long_runs, long_done, grad_dense, uniq_grad);
     return hipGetLastError();
 }
 
