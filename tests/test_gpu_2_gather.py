@@ -102,3 +102,30 @@ def test_sft_table_full_parity():
     ref, bad = c_oracle.gather(to_host(table), rows_ref)
     assert bad == -1
     assert np.array_equal(to_host(out), ref)
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+def test_wide_shard_row_ids(dtype):
+    """A shard declared with 2^32 + 5 rows takes the 64-bit row-id path.  Only rows
+    inside the allocated 4,000-row prefix are looked up (plus rows outside the
+    declared shard, which are never read), so every access stays in the table."""
+    g = torch.Generator(device="cuda")
+    g.manual_seed(17)
+    rb, R, declared = 7, 4000, (1 << 32) + 5
+    table = torch.randn((R, 160), generator=g, device="cuda").to(dtype)
+    rng = np.random.default_rng(17)
+    rows = rng.integers(rb, rb + R, size=3001).astype(np.int64)
+    rows[[100, 2500]] = [rb + declared, rb - 1]
+    out = torch.empty((rows.size, 160), dtype=dtype, device="cuda")
+    status = torch.empty((), dtype=torch.int64, device="cuda")
+    rows_gpu = torch.from_numpy(rows).cuda()
+    lib = E.load_library()
+    rc = lib.engram_gather(table.data_ptr(), 1 if dtype == torch.bfloat16 else 0, rb, declared, 160,
+                           rows_gpu.data_ptr(), rows.size, out.data_ptr(), status.data_ptr(), None)
+    assert rc == 0
+    torch.cuda.synchronize()
+    in_table = (rows >= rb) & (rows < rb + R)
+    ref, _ = c_oracle.gather(to_host(table), np.where(in_table, rows, rb), rb)
+    ref[~in_table] = 0
+    assert np.array_equal(to_host(out).view(np.uint8), ref.view(np.uint8))
+    assert int(status.item()) == 100
