@@ -29,7 +29,9 @@ itself needs several GPUs and is not timed; the exchange is the identity.
 
 Printed: one JSON line with lookups/s, the roofline of the dominant kernel
 (timed with HIP events on the stream the kernels run on) and the oracle's CPU
-throughput on the same stream (rank 0, N = 1).
+throughput on the same stream (rank 0, N = 1).  After the timed steps the
+gather, the plan and the apply also run one at a time, untimed by the step
+clock (phases_alone_ms_p50, gather_alone, backward_plan_then_apply).
 """
 import argparse
 import hashlib
@@ -58,6 +60,8 @@ def parse_args():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="run one plain 1 GiB device copy first (reference for HBM byte counters)")
+    ap.add_argument("--no-alone", action="store_true",
+                    help="skip the phases-one-at-a-time launches after the timed steps (profiler runs)")
     return ap.parse_args()
 
 
@@ -183,6 +187,44 @@ def run_step(wl, b, ev=None):
                                    grad_dense=wl["grad_dense"], uniq_grad=compact[1] if compact else None)
         if ev:
             ev[6].record(main)
+
+
+def phases_alone(wl, k):
+    """Median ms of the gather, the plan and the apply, each run by itself on
+    the main stream with nothing beside it, over k launches rotating through
+    the input sets (outside the timed steps)."""
+    import torch
+
+    import hashed_gram_embedding_engram_amd as E
+    R = len(wl["batches"])
+    ev = lambda: torch.cuda.Event(enable_timing=True)
+    ms = {"gather": [], "scatter_plan": [], "scatter_apply": []}
+    events = []
+    for i in range(k + 2):  # queued back to back, as in the steps
+        b = wl["batches"][i % R]
+        e = [ev() for _ in range(6)]
+        events.append(e)
+        e[0].record()
+        E.engram_gather(wl["table"], b["rows"], wl["row_begin"], out=b["out"], status=b["status"], validate=False)
+        e[1].record()
+        if wl["backward"]:
+            compact = b.get("compact")
+            e[2].record()
+            E.engram_scatter_add_plan(b["rows"], wl["table_rows"], b["dy"].shape[-1], wl["row_begin"],
+                                      workspace=wl["workspace"], uniq_rows=compact[0] if compact else None,
+                                      num_uniq=compact[2] if compact else None, status=b["plan_status"])
+            e[3].record()
+            e[4].record()
+            E.engram_scatter_add_apply(b["dy"], b["n"], wl["table_rows"], wl["workspace"], wl["row_begin"],
+                                       grad_dense=wl["grad_dense"], uniq_grad=compact[1] if compact else None)
+            e[5].record()
+    torch.cuda.synchronize()
+    for e in events[2:]:  # the first two are warm-up
+        ms["gather"].append(e[0].elapsed_time(e[1]))
+        if wl["backward"]:
+            ms["scatter_plan"].append(e[2].elapsed_time(e[3]))
+            ms["scatter_apply"].append(e[4].elapsed_time(e[5]))
+    return {key: round(sorted(v)[len(v) // 2], 4) for key, v in ms.items() if v}
 
 
 def percentiles(ms):
@@ -595,6 +637,7 @@ def main():
 
     lookups = sum(wl["batches"][i % R]["n"] for i in range(args.steps))
     elapsed = t1 - t0
+    alone = None if args.no_alone else phases_alone(wl, min(args.steps, 20))
     spans = {"hash": (0, 1), "gather": (1, 2)}
     if wl["backward"]:
         spans.update({"scatter_plan (side stream)": (3, 4), "wait_for_plan": (2, 5), "scatter_apply": (5, 6)})
@@ -686,8 +729,20 @@ def main():
         "distinct_rows_forward_rotation0": u_fwd,
         "step_ms_events": {"p10": round(pct(0.1), 4), "p50": round(pct(0.5), 4), "p90": round(pct(0.9), 4)},
         "forward_lookups_per_s": n_avg / (fwd_ms / 1e3),
+        "phases_alone_ms_p50": alone,
         "cpu_baseline": None,
     }
+    # The same phases one at a time (measured after the timed steps): the
+    # gather without the plan beside it, and the backward as plan then apply.
+    if alone:
+        ga = alone["gather"]
+        result["gather_alone"] = {"gbps_algorithmic": round(gather_bytes / (ga / 1e3) / 1e9, 1),
+                                  "frac": round(gather_bytes / (ga / 1e3) / 1e9 / HBM_PEAK_GBPS, 4)}
+    if alone and wl["backward"]:
+        bs = alone["scatter_plan"] + alone["scatter_apply"]
+        result["backward_plan_then_apply"] = {"ms": round(bs, 4),
+                                              "gbps_algorithmic": round(apply_bytes / (bs / 1e3) / 1e9, 1),
+                                              "frac": round(apply_bytes / (bs / 1e3) / 1e9 / HBM_PEAK_GBPS, 4)}
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(wl)
     print(json.dumps(result), flush=True)
