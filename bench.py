@@ -154,39 +154,38 @@ def build_workload(name, rotations, dev):
 def run_step(wl, b, ev=None):
     """hash -> gather, with the backward plan (sort by row) on a side stream
     concurrently with the gather, then apply once both are done.  ev: events
-    (hash start, hash end, gather end, plan start, plan end, apply start, apply end)."""
+    (hash start, hash end, gather end, plan start, plan end, apply start, apply
+    end); an entry may be None, and only the events given are recorded."""
     import torch
 
     import hashed_gram_embedding_engram_amd as E
     main = torch.cuda.current_stream()
     side = wl["side"]
-    if ev:
-        ev[0].record(main)
+
+    def mark(k, stream):
+        if ev and ev[k] is not None:
+            ev[k].record(stream)
+
+    mark(0, main)
     if b["tokens"] is not None:
         E.engram_hash(b["tokens"], wl["spec"], rows_out=b["rows"])
-    if ev:
-        ev[1].record(main)
+    mark(1, main)
     if wl["backward"]:
         side.wait_stream(main)
         compact = b.get("compact")
-        if ev:
-            ev[3].record(side)
+        mark(3, side)
         E.engram_scatter_add_plan(b["rows"], wl["table_rows"], b["dy"].shape[-1], wl["row_begin"],
                                   workspace=wl["workspace"], uniq_rows=compact[0] if compact else None,
                                   num_uniq=compact[2] if compact else None, status=b["plan_status"], stream=side)
-        if ev:
-            ev[4].record(side)
+        mark(4, side)
     E.engram_gather(wl["table"], b["rows"], wl["row_begin"], out=b["out"], status=b["status"], validate=False)
-    if ev:
-        ev[2].record(main)
+    mark(2, main)
     if wl["backward"]:
         main.wait_stream(side)
-        if ev:
-            ev[5].record(main)
+        mark(5, main)
         E.engram_scatter_add_apply(b["dy"], b["n"], wl["table_rows"], wl["workspace"], wl["row_begin"],
                                    grad_dense=wl["grad_dense"], uniq_grad=compact[1] if compact else None)
-        if ev:
-            ev[6].record(main)
+        mark(6, main)
 
 
 def phases_alone(wl, k):
@@ -327,22 +326,54 @@ def ple_step(wl, t, ev=None):
     """conv forward -> grouped norm forward -> norm backward -> conv backward."""
     import hashed_gram_embedding_engram_amd as E
     rows, C, G = wl["batch"] * wl["seq"], wl["channels"], wl["group"]
-    if ev:
+    if ev and ev[0] is not None:
         ev[0].record()
     E.engram_short_conv(t["x"], t["conv_w"], t["conv_b"], 3, t["halo"], out=t["c"])
-    if ev:
+    if ev and ev[1] is not None:
         ev[1].record()
     E.engram_grouped_rms_norm(t["c"].view(rows, C), t["norm_w"], G, 1e-6, out=t["z"].view(rows, C))
-    if ev:
+    if ev and ev[2] is not None:
         ev[2].record()
     E.engram_grouped_rms_norm_backward(t["c"].view(rows, C), t["dy"].view(rows, C), t["norm_w"], G, 1e-6,
                                        workspace=wl["ws_norm"], out=(t["dc"].view(rows, C), t["dnorm_w"]))
-    if ev:
+    if ev and ev[3] is not None:
         ev[3].record()
     E.engram_short_conv_backward(t["x"], t["dc"], t["conv_w"], 3, t["halo"], workspace=wl["ws_conv"],
                                  out=(t["dx"], t["dconv_w"], t["dconv_b"], t["dhalo"]))
-    if ev:
+    if ev and ev[4] is not None:
         ev[4].record()
+
+
+def timed_phases(step, rots, nphases, steps):
+    """Run `steps` timed steps of a multi-phase pipeline.  Each recorded event
+    costs the step a few microseconds, so a first pass of up to 20 steps with
+    events around every phase finds the dominant phase, and the timed steps
+    then carry only that phase's two events.  Returns (seconds, phase ms means,
+    phase percentiles, index of the dominant phase); the dominant phase's
+    figures come from the timed steps."""
+    import torch
+
+    R = len(rots)
+    mk = lambda: torch.cuda.Event(enable_timing=True)
+    kb = min(steps, 20)
+    bevs = [[mk() for _ in range(nphases + 1)] for _ in range(kb)]
+    for i in range(kb):
+        step(rots[i % R], bevs[i])
+    torch.cuda.synchronize()
+    mean = [sum(e[k].elapsed_time(e[k + 1]) for e in bevs) / kb for k in range(nphases)]
+    pct = [percentiles([e[k].elapsed_time(e[k + 1]) for e in bevs]) for k in range(nphases)]
+    dom = max(range(nphases), key=lambda k: mean[k])
+    tevs = [[mk() if j in (dom, dom + 1) else None for j in range(nphases + 1)] for _ in range(steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        step(rots[i % R], tevs[i])
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    dom_ms = [e[dom].elapsed_time(e[dom + 1]) for e in tevs]
+    mean[dom] = sum(dom_ms) / len(dom_ms)
+    pct[dom] = percentiles(dom_ms)
+    return t1 - t0, mean, pct, dom
 
 
 def ple_cpu_baseline(wl, sample_rows=2):
@@ -379,17 +410,12 @@ def ple_main(args, dev):
     for i in range(args.warmup):
         ple_step(wl, wl["rots"][i % R])
     torch.cuda.synchronize()
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
-    t0 = time.perf_counter()
-    for i in range(args.steps):
-        ple_step(wl, wl["rots"][i % R], evs[i])
-    torch.cuda.synchronize()
-    t1 = time.perf_counter()
+    names = ["conv_fwd", "norm_fwd", "norm_bwd", "conv_bwd"]
+    elapsed, mean, pct, di = timed_phases(lambda t, ev: ple_step(wl, t, ev), wl["rots"], len(names), args.steps)
     tokens = wl["batch"] * wl["seq"]
     C = wl["channels"]
-    names = ["conv_fwd", "norm_fwd", "norm_bwd", "conv_bwd"]
-    phase = {n: sum(e[k].elapsed_time(e[k + 1]) for e in evs) / args.steps for k, n in enumerate(names)}
-    phase_pct = {n: percentiles([e[k].elapsed_time(e[k + 1]) for e in evs]) for k, n in enumerate(names)}
+    phase = dict(zip(names, mean))
+    phase_pct = dict(zip(names, pct))
     # Algorithmic bytes per launch (bf16 activations, 2 B per element): forward
     # passes read x and write y (4 B per element); backward passes read x and
     # dy and write dx (6 B per element).  Weights, halos and the weight
@@ -400,9 +426,8 @@ def ple_main(args, dev):
              "norm_fwd": ("rms_norm_fwd_kernel<bf16,5>", "ple.hip"),
              "norm_bwd": ("rms_norm_bwd_kernel<bf16,5> + column_sum_kernel", "ple.hip"),
              "conv_bwd": ("short_conv_bwd_d3_kernel<bf16,4> + column_sum_kernel", "ple.hip")}
-    dom = max(phase, key=phase.get)
+    dom = names[di]
     achieved = alg[dom] / (phase[dom] / 1e3) / 1e9
-    elapsed = t1 - t0
     result = {
         "metric": PLE_METRIC,
         "value": tokens * args.steps / elapsed,
@@ -421,6 +446,8 @@ def ple_main(args, dev):
                    "channels": C, "rotations": R},
         "phases_ms": {k: round(v, 4) for k, v in phase.items()},
         "phases_ms_p10_p50_p90": phase_pct,
+        "phases_from": "%s: HIP events in the timed steps; other phases: %d earlier steps with events around "
+                       "every phase" % (dom, min(args.steps, 20)),
         "roofline": {"kernel": kname[dom][0], "bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS,
                      "unit": "GB/s", "frac": achieved / HBM_PEAK_GBPS,
                      "traffic": counter_traffic(kname[dom][1], "%s_ple_counters.txt" % dom),
@@ -481,7 +508,7 @@ def route_step(wl, t, ev=None):
 
     def mark():
         nonlocal k
-        if ev:
+        if ev and ev[k] is not None:
             ev[k].record()
         k += 1
     mark()
@@ -537,14 +564,9 @@ def route_main(args, dev):
         route_step(wl, wl["rots"][i % R])
     torch.cuda.synchronize()
     names = ["plan", "validate", "pack_ids", "unpack_ids", "pack_values", "unpack_values", "unpermute_values"]
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(names) + 1)] for _ in range(args.steps)]
-    t0 = time.perf_counter()
-    for i in range(args.steps):
-        route_step(wl, wl["rots"][i % R], evs[i])
-    torch.cuda.synchronize()
-    t1 = time.perf_counter()
-    phase = {nm: sum(e[k].elapsed_time(e[k + 1]) for e in evs) / args.steps for k, nm in enumerate(names)}
-    phase_pct = {nm: percentiles([e[k].elapsed_time(e[k + 1]) for e in evs]) for k, nm in enumerate(names)}
+    elapsed, mean, pct, di = timed_phases(lambda t, ev: route_step(wl, t, ev), wl["rots"], len(names), args.steps)
+    phase = dict(zip(names, mean))
+    phase_pct = dict(zip(names, pct))
     n = sum(wl["rots"][i % R]["n"] for i in range(args.steps)) / args.steps
     cap = sum(wl["rots"][i % R]["cap"] for i in range(args.steps)) / args.steps
     Wd, row = wl["world"], 2.0 * W.DIM
@@ -556,13 +578,12 @@ def route_main(args, dev):
     alg = {"plan": 24.0 * n, "validate": 8.0 * n, "pack_ids": 8.0 * n + 8.0 * Wd * cap,
            "unpack_ids": 16.0 * n, "pack_values": row * n + row * Wd * cap, "unpack_values": 2 * row * n,
            "unpermute_values": (2 * row + 8.0) * n}
-    dom = max(phase, key=phase.get)
+    dom = names[di]
     kname = {"plan": "route_keys_kernel + radix pass + route_output_kernel", "validate": "route_validate_kernel",
              "pack_ids": "pack_kernel<uint32_t,uint32_t,4>", "unpack_ids": "unpack_kernel<uint32_t,uint32_t,4>",
              "pack_values": "pack_kernel<u32x4,uint32_t,2>", "unpack_values": "unpack_kernel<u32x4,uint32_t,4>",
              "unpermute_values": "permute_kernel<u32x4,false,1>"}
     achieved = alg[dom] / (phase[dom] / 1e3) / 1e9
-    elapsed = t1 - t0
     result = {
         "metric": ROUTE_METRIC,
         "value": n * args.steps / elapsed,
@@ -581,6 +602,8 @@ def route_main(args, dev):
                    "lookups_per_step": int(n), "world": Wd, "capacity": int(cap), "rotations": R},
         "phases_ms": {k: round(v, 4) for k, v in phase.items()},
         "phases_ms_p10_p50_p90": phase_pct,
+        "phases_from": "%s: HIP events in the timed steps; other phases: %d earlier steps with events around "
+                       "every phase" % (dom, min(args.steps, 20)),
         "roofline": {"kernel": kname[dom], "bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS,
                      "unit": "GB/s", "frac": achieved / HBM_PEAK_GBPS,
                      "traffic": counter_traffic("route.hip", "%s_route_counters.txt" % dom),
@@ -627,22 +650,38 @@ def main():
         run_step(wl, wl["batches"][i % R])
     torch.cuda.synchronize()
 
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(7)] for _ in range(args.steps)]
+    # Each recorded event costs the step a few microseconds, so the timed
+    # steps carry only the two around the dominant phase (the apply, or the
+    # gather of a forward-only workload); a second pass with events around
+    # every phase gives the breakdown.
+    dom = "scatter_apply" if wl["backward"] else "gather"
+    dom_span = (5, 6) if wl["backward"] else (1, 2)
+    mk = lambda: torch.cuda.Event(enable_timing=True)
+    tevs = [[mk() if k in dom_span else None for k in range(7)] for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
-        run_step(wl, wl["batches"][i % R], evs[i])
+        run_step(wl, wl["batches"][i % R], tevs[i])
     torch.cuda.synchronize()
     t1 = time.perf_counter()
 
     lookups = sum(wl["batches"][i % R]["n"] for i in range(args.steps))
     elapsed = t1 - t0
+    dom_ms = [e[dom_span[0]].elapsed_time(e[dom_span[1]]) for e in tevs]
+
+    kb = min(args.steps, 20)
+    evs = [[mk() for _ in range(7)] for _ in range(kb)]
+    for i in range(kb):
+        run_step(wl, wl["batches"][i % R], evs[i])
+    torch.cuda.synchronize()
     alone = None if args.no_alone else phases_alone(wl, min(args.steps, 20))
     spans = {"hash": (0, 1), "gather": (1, 2)}
     if wl["backward"]:
         spans.update({"scatter_plan (side stream)": (3, 4), "wait_for_plan": (2, 5), "scatter_apply": (5, 6)})
-    phase = {k: sum(e[a].elapsed_time(e[b]) for e in evs) / args.steps for k, (a, b) in spans.items()}
+    phase = {k: sum(e[a].elapsed_time(e[b]) for e in evs) / kb for k, (a, b) in spans.items()}
     phase_pct = {k: percentiles([e[a].elapsed_time(e[b]) for e in evs]) for k, (a, b) in spans.items()}
+    phase[dom] = sum(dom_ms) / len(dom_ms)        # the dominant phase from the timed steps themselves
+    phase_pct[dom] = percentiles(dom_ms)
     n_avg = lookups / args.steps
     U = None
     b0 = wl["batches"][0]
@@ -671,7 +710,6 @@ def main():
     if wl["backward"]:
         kern["scatter_apply"] = (apply_bytes, phase["scatter_apply"],
                                  "segment_reduce_kernel<20,bf16> + carry_fixup_kernel + long_run_kernel", "scatter.hip")
-    dom = max(kern, key=lambda k: kern[k][1])
     dbytes, dms, dname, dsrc = kern[dom]
     achieved = dbytes / (dms / 1e3) / 1e9
     traffic = counter_traffic(dsrc, "%s_%s_counters.txt" % (dom, args.workload))
@@ -721,6 +759,8 @@ def main():
         },
         "phases_ms": {k: round(v, 4) for k, v in phase.items()},
         "phases_ms_p10_p50_p90": phase_pct,
+        "phases_from": "%s: HIP events in the timed steps; other phases and step_ms_events: %d more steps "
+                       "with events around every phase" % (dom, kb),
         "roofline": {"kernel": dname, "bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS,
                      "unit": "GB/s", "frac": achieved / HBM_PEAK_GBPS, "traffic": traffic,
                      "algorithmic_bytes_per_launch": dbytes, "avg_launch_ms": dms},
