@@ -46,6 +46,7 @@ if ROOT not in sys.path:
 
 METRIC = "Engram (token x head) lookups/sec fwd+bwd and achieved HBM GB/s vs peak"
 HBM_PEAK_GBPS = 8000.0
+EVENT_STRIDE = 4  # timed steps per step that carries the dominant phase's events
 PROFILES = os.path.join(ROOT, "profiles")
 CSRC = os.path.join(ROOT, "hashed_gram_embedding_engram_amd", "csrc")
 
@@ -347,10 +348,10 @@ def ple_step(wl, t, ev=None):
 def timed_phases(step, rots, nphases, steps):
     """Run `steps` timed steps of a multi-phase pipeline.  Each recorded event
     costs the step a few microseconds, so a first pass of up to 20 steps with
-    events around every phase finds the dominant phase, and the timed steps
-    then carry only that phase's two events.  Returns (seconds, phase ms means,
-    phase percentiles, index of the dominant phase); the dominant phase's
-    figures come from the timed steps."""
+    events around every phase finds the dominant phase, and every
+    EVENT_STRIDE-th timed step then carries only that phase's two events.
+    Returns (seconds, phase ms means, phase percentiles, index of the
+    dominant phase); the dominant phase's figures come from the timed steps."""
     import torch
 
     R = len(rots)
@@ -363,14 +364,15 @@ def timed_phases(step, rots, nphases, steps):
     mean = [sum(e[k].elapsed_time(e[k + 1]) for e in bevs) / kb for k in range(nphases)]
     pct = [percentiles([e[k].elapsed_time(e[k + 1]) for e in bevs]) for k in range(nphases)]
     dom = max(range(nphases), key=lambda k: mean[k])
-    tevs = [[mk() if j in (dom, dom + 1) else None for j in range(nphases + 1)] for _ in range(steps)]
+    tevs = [[mk() if j in (dom, dom + 1) else None for j in range(nphases + 1)] if i % EVENT_STRIDE == 0 else None
+            for i in range(steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(steps):
         step(rots[i % R], tevs[i])
     torch.cuda.synchronize()
     t1 = time.perf_counter()
-    dom_ms = [e[dom].elapsed_time(e[dom + 1]) for e in tevs]
+    dom_ms = [e[dom].elapsed_time(e[dom + 1]) for e in tevs if e]
     mean[dom] = sum(dom_ms) / len(dom_ms)
     pct[dom] = percentiles(dom_ms)
     return t1 - t0, mean, pct, dom
@@ -446,8 +448,8 @@ def ple_main(args, dev):
                    "channels": C, "rotations": R},
         "phases_ms": {k: round(v, 4) for k, v in phase.items()},
         "phases_ms_p10_p50_p90": phase_pct,
-        "phases_from": "%s: HIP events in the timed steps; other phases: %d earlier steps with events around "
-                       "every phase" % (dom, min(args.steps, 20)),
+        "phases_from": "%s: HIP events in every %dth timed step; other phases: %d earlier steps with events "
+                       "around every phase" % (dom, EVENT_STRIDE, min(args.steps, 20)),
         "roofline": {"kernel": kname[dom][0], "bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS,
                      "unit": "GB/s", "frac": achieved / HBM_PEAK_GBPS,
                      "traffic": counter_traffic(kname[dom][1], "%s_ple_counters.txt" % dom),
@@ -602,8 +604,8 @@ def route_main(args, dev):
                    "lookups_per_step": int(n), "world": Wd, "capacity": int(cap), "rotations": R},
         "phases_ms": {k: round(v, 4) for k, v in phase.items()},
         "phases_ms_p10_p50_p90": phase_pct,
-        "phases_from": "%s: HIP events in the timed steps; other phases: %d earlier steps with events around "
-                       "every phase" % (dom, min(args.steps, 20)),
+        "phases_from": "%s: HIP events in every %dth timed step; other phases: %d earlier steps with events "
+                       "around every phase" % (dom, EVENT_STRIDE, min(args.steps, 20)),
         "roofline": {"kernel": kname[dom], "bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS,
                      "unit": "GB/s", "frac": achieved / HBM_PEAK_GBPS,
                      "traffic": counter_traffic("route.hip", "%s_route_counters.txt" % dom),
@@ -650,14 +652,16 @@ def main():
         run_step(wl, wl["batches"][i % R])
     torch.cuda.synchronize()
 
-    # Each recorded event costs the step a few microseconds, so the timed
-    # steps carry only the two around the dominant phase (the apply, or the
-    # gather of a forward-only workload); a second pass with events around
-    # every phase gives the breakdown.
+    # Each recorded event costs the step a few microseconds (the two around
+    # the apply add about 9 us to a 1.29 ms step), so only every
+    # EVENT_STRIDE-th timed step carries events, and only the two around the
+    # dominant phase (the apply, or the gather of a forward-only workload); a
+    # second pass with events around every phase gives the breakdown.
     dom = "scatter_apply" if wl["backward"] else "gather"
     dom_span = (5, 6) if wl["backward"] else (1, 2)
     mk = lambda: torch.cuda.Event(enable_timing=True)
-    tevs = [[mk() if k in dom_span else None for k in range(7)] for _ in range(args.steps)]
+    tevs = [[mk() if k in dom_span else None for k in range(7)] if i % EVENT_STRIDE == 0 else None
+            for i in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
@@ -667,7 +671,7 @@ def main():
 
     lookups = sum(wl["batches"][i % R]["n"] for i in range(args.steps))
     elapsed = t1 - t0
-    dom_ms = [e[dom_span[0]].elapsed_time(e[dom_span[1]]) for e in tevs]
+    dom_ms = [e[dom_span[0]].elapsed_time(e[dom_span[1]]) for e in tevs if e]
 
     kb = min(args.steps, 20)
     evs = [[mk() for _ in range(7)] for _ in range(kb)]
@@ -759,8 +763,8 @@ def main():
         },
         "phases_ms": {k: round(v, 4) for k, v in phase.items()},
         "phases_ms_p10_p50_p90": phase_pct,
-        "phases_from": "%s: HIP events in the timed steps; other phases and step_ms_events: %d more steps "
-                       "with events around every phase" % (dom, kb),
+        "phases_from": "%s: HIP events in %d of the timed steps (every %dth); other phases and step_ms_events: "
+                       "%d more steps with events around every phase" % (dom, len(dom_ms), EVENT_STRIDE, kb),
         "roofline": {"kernel": dname, "bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS,
                      "unit": "GB/s", "frac": achieved / HBM_PEAK_GBPS, "traffic": traffic,
                      "algorithmic_bytes_per_launch": dbytes, "avg_launch_ms": dms},
