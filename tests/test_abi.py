@@ -271,3 +271,23 @@ def test_oversized_ple_calls_rejected(lib):
     assert lib.engram_short_conv(ok, bf, 1 << 20, 1 << 20, 8, ok, None, 4, 3, None, ok, None) == B.ENGRAM_EINVAL
     assert lib.engram_short_conv(ok, bf, 1, 1, 1 << 27, ok, None, 4, 3, None, ok, None) == B.ENGRAM_EINVAL
     assert lib.engram_grouped_rms_norm(ok, bf, 1 << 30, 16, 8, ok, 1e-6, ok, None) == B.ENGRAM_EINVAL  # 2^31 waves
+
+
+def test_missing_library_fails_loudly(monkeypatch):
+    """Without libengram.so every product call raises; there is no fallback path."""
+    import torch
+
+    import hashed_gram_embedding_engram_amd as E
+    from hashed_gram_embedding_engram_amd import engram as EB
+    monkeypatch.setattr(EB, "_lib", None)
+    monkeypatch.setattr(EB.load_library, "__defaults__", ("/nonexistent/libengram.so",))
+    with pytest.raises(RuntimeError, match="libengram.so not found"):
+        EB.load_library()
+    table = torch.zeros((4, 160), dtype=torch.bfloat16)
+    rows = torch.zeros(3, dtype=torch.int64)
+    with pytest.raises(RuntimeError, match="libengram.so not found"):
+        E.engram_gather(table, rows)
+    with pytest.raises(RuntimeError, match="libengram.so not found"):
+        E.engram_hash(torch.zeros((1, 8), dtype=torch.int64), E.qwen3_8_flash_next_spec())
+    with pytest.raises(RuntimeError, match="libengram.so not found"):
+        E.engram_scatter_add(rows, torch.zeros((3, 160), dtype=torch.bfloat16), 4)
