@@ -61,7 +61,8 @@ int hash_common(const int64_t* tokens, int64_t batch, int64_t seq_len, int64_t s
     const int64_t width = seq_end - seq_begin;
     if (batch == 0 || width == 0) return ENGRAM_OK;
     if (!tokens || !rows_out || !aligned(tokens, 8) || !aligned(rows_out, 8)) return ENGRAM_EINVAL;
-    if (batch > INT64_MAX / width / ENGRAM_MAX_HEADS || batch * width > ((int64_t)1 << 40)) return ENGRAM_EINVAL;
+    // one work-item per position: a launch holds fewer than 2^32
+    if (batch > INT64_MAX / width / ENGRAM_MAX_HEADS || batch * width > ((int64_t)1 << 32) - 64) return ENGRAM_EINVAL;
     return launch_result(engram::launch_hash(tokens, batch, seq_len, seq_begin, seq_end, p, rows_out, stream));
 }
 
@@ -253,15 +254,23 @@ int engram_unpermute_rows(const void* src, int64_t row_bytes, const int64_t* ord
 namespace {
 
 // Sizes of a PLE call over a x b rows of `channels` features: every row a
-// whole number of 16-byte chunks, at most 2^26 features per row and 2^40
-// elements in all (so every launch grid fits).
+// whole number of 16-byte chunks, at most 2^26 features per row and 2^36
+// elements in all (137 GB of bf16 per tensor), so that every convolution
+// launch holds fewer than 2^32 work-items (the smallest tile covers 16
+// positions x 4 channels per work-item).
 int ple_dims_ok(int32_t dtype, int64_t a, int64_t b, int64_t channels, int* eb) {
     if (!dtype_ok(dtype)) return ENGRAM_EDTYPE;
     *eb = dtype == ENGRAM_F32 ? 4 : 2;
     if (a < 0 || b < 0 || channels <= 0 || channels > ((int64_t)1 << 26) || (channels * *eb) % 16 != 0)
         return ENGRAM_EINVAL;
-    if (a > 0 && b > 0 && (b > ((int64_t)1 << 40) / a || a * b > ((int64_t)1 << 40) / channels)) return ENGRAM_EINVAL;
+    if (a > 0 && b > 0 && (b > ((int64_t)1 << 36) / a || a * b > ((int64_t)1 << 36) / channels)) return ENGRAM_EINVAL;
     return ENGRAM_OK;
+}
+
+// The norm runs one wave per (row, group): rows x groups at most 2^25 keeps
+// its launches below 2^31 work-items.
+bool norm_groups_ok(int64_t rows, int64_t hidden, int64_t group) {
+    return rows <= (((int64_t)1 << 25) / (hidden / group));
 }
 
 bool ple_ptrs_ok(std::initializer_list<const void*> rows16, std::initializer_list<const void*> words4) {
@@ -323,7 +332,7 @@ int engram_grouped_rms_norm(const void* x, int32_t dtype, int64_t rows, int64_t 
         !(eps >= 0.0f))
         return ENGRAM_EINVAL;
     if (rows > 0 && (!x || !y)) return ENGRAM_EINVAL;
-    if (rows > 0 && rows > (((int64_t)1 << 31) - 1) / (hidden / group_size)) return ENGRAM_EINVAL;  // waves
+    if (!norm_groups_ok(rows, hidden, group_size)) return ENGRAM_EINVAL;
     if (!ple_ptrs_ok({x, y}, {weight})) return ENGRAM_EINVAL;
     return launch_result(engram::launch_rms_norm(x, eb, rows, hidden, group_size, weight, eps, y, stream));
 }
@@ -338,7 +347,7 @@ int engram_grouped_rms_norm_backward(const void* x, const void* dy, int32_t dtyp
         !dweight || !(eps >= 0.0f))
         return ENGRAM_EINVAL;
     if (rows > 0 && (!x || !dy || !dx)) return ENGRAM_EINVAL;
-    if (rows > 0 && rows > (((int64_t)1 << 31) - 1) / (hidden / group_size)) return ENGRAM_EINVAL;
+    if (!norm_groups_ok(rows, hidden, group_size)) return ENGRAM_EINVAL;
     if (!ple_ptrs_ok({x, dy, dx}, {weight, dweight})) return ENGRAM_EINVAL;
     if (((uintptr_t)workspace & 255) != 0) return ENGRAM_EWORKSPACE;
     const size_t need = engram::rms_norm_workspace_bytes(rows, hidden);

@@ -18,6 +18,8 @@
 // fully read by consecutive lanes).  Output stores are non-temporal: the
 // output is not re-read by this kernel and should not evict table rows that
 // repeat (hot n-grams) from L2 and the Infinity Cache.
+#include <algorithm>
+
 #include "engram_internal.h"
 
 // Build-time switch for non-temporal table loads; off, because the gather then
@@ -103,23 +105,25 @@ __global__ __launch_bounds__(256) void gather_rows_kernel(const u32x4* __restric
 }
 
 // Any row size (multiple of 16 B, at most 64 chunks): one chunk per lane over
-// the flattened output.
+// the flattened output, striding by the whole grid (a launch holds fewer than
+// 2^32 work-items, and n * cpr can exceed that).
 __global__ __launch_bounds__(256) void gather_rows_generic_kernel(const u32x4* __restrict__ table,
                                                                   int64_t row_begin, uint64_t num_rows,
                                                                   const int64_t* __restrict__ rows, int64_t n,
                                                                   int cpr, u32x4* __restrict__ out,
                                                                   int64_t* __restrict__ status) {
-    const int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    if (e >= n * cpr) return;
-    const int64_t i = e / cpr;
-    const int k = (int)(e - i * cpr);
-    const uint64_t local = (uint64_t)rows[i] - (uint64_t)row_begin;
-    u32x4 v = (u32x4){0u, 0u, 0u, 0u};
-    if (local < num_rows)
-        v = table[(int64_t)local * cpr + k];
-    else if (k == 0)
-        report_bad(status, i);
-    __builtin_nontemporal_store(v, out + e);
+    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+    for (int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; e < n * cpr; e += stride) {
+        const int64_t i = e / cpr;
+        const int k = (int)(e - i * cpr);
+        const uint64_t local = (uint64_t)rows[i] - (uint64_t)row_begin;
+        u32x4 v = (u32x4){0u, 0u, 0u, 0u};
+        if (local < num_rows)
+            v = table[(int64_t)local * cpr + k];
+        else if (k == 0)
+            report_bad(status, i);
+        __builtin_nontemporal_store(v, out + e);
+    }
 }
 
 __global__ void status_init_kernel(int64_t* status) { *status = -1; }
@@ -141,8 +145,13 @@ hipError_t launch_gather(const void* table, int elem_bytes, int64_t row_begin, i
     u32x4* o = (u32x4*)out;
     const int block = 256, waves_per_block = block / 64;
     const bool row32 = (uint64_t)num_rows < 0xFFFFFFFFull;
-    if (cpr == 20 || cpr == 40) {
-        const int g = cpr == 20 ? 16 : 8;
+    // Work-items per launch must stay below 2^32: the one-wave-per-G-lookups
+    // kernels take 64 / G per lookup (fewer lookups than fit in HBM at these
+    // row sizes); the generic kernel strides over any count.
+    const int64_t kMaxItems = (int64_t)1 << 31;
+    const int gw = cpr == 20 ? 16 : 8;
+    if ((cpr == 20 || cpr == 40) && (n + gw - 1) / gw * 64 <= kMaxItems) {
+        const int g = gw;
         const int64_t waves = (n + g - 1) / g;
         const dim3 grid((unsigned)((waves + waves_per_block - 1) / waves_per_block));
         if (cpr == 20 && row32)
@@ -158,7 +167,7 @@ hipError_t launch_gather(const void* table, int elem_bytes, int64_t row_begin, i
             hipLaunchKernelGGL((gather_rows_kernel<40, 8, false>), grid, dim3(block), 0, stream, t, row_begin,
                                (uint64_t)num_rows, rows, n, o, status);
     } else {
-        const int64_t grid = (n * cpr + block - 1) / block;
+        const int64_t grid = std::min((n * cpr + block - 1) / block, kMaxItems / block);
         hipLaunchKernelGGL(gather_rows_generic_kernel, dim3((unsigned)grid), dim3(block), 0, stream, t,
                            row_begin, (uint64_t)num_rows, rows, n, cpr, o, status);
     }

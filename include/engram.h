@@ -102,7 +102,8 @@ typedef struct {
  *   spec      host pointer, read during the call only
  *   rows_out  device int64 [batch][seq_len][H]
  * Batch rows are independent; a packed (THD) stream is batch = 1 whose
- * documents are separated by EOS.  batch * seq_len == 0 is a no-op.
+ * documents are separated by EOS.  batch * seq_len == 0 is a no-op;
+ * batch * seq_len <= 2^32 - 64 (one work-item per position).
  * Returns ENGRAM_OK, ENGRAM_EINVAL or ENGRAM_ESPEC. */
 int engram_hash(const int64_t* tokens, int64_t batch, int64_t seq_len, const engram_hash_spec* spec,
                 int64_t* rows_out, hipStream_t stream);
@@ -113,7 +114,8 @@ int engram_hash(const int64_t* tokens, int64_t batch, int64_t seq_len, const eng
  * so the slice equals columns [seq_begin, seq_end) of engram_hash on the full row.
  *   tokens    device int64 [batch][seq_len]
  *   rows_out  device int64 [batch][seq_end - seq_begin][H]
- * Requires 0 <= seq_begin <= seq_end <= seq_len. */
+ * Requires 0 <= seq_begin <= seq_end <= seq_len and batch * (seq_end - seq_begin)
+ * <= 2^32 - 64. */
 int engram_hash_slice(const int64_t* tokens, int64_t batch, int64_t seq_len, int64_t seq_begin,
                       int64_t seq_end, const engram_hash_spec* spec, int64_t* rows_out,
                       hipStream_t stream);
@@ -125,7 +127,8 @@ int engram_hash_slice(const int64_t* tokens, int64_t batch, int64_t seq_len, int
  *   rows      device int64 [n] global row IDs
  *   out       device [n][dim] of `dtype`; out[i] = table[rows[i] - row_begin], bit for bit
  *   status    device int64 scalar or NULL (see conventions)
- * dim * element size must be a multiple of 16 bytes and at most 1024 bytes.
+ * dim * element size must be a multiple of 16 bytes and at most 1024 bytes;
+ * n <= 2^40 (any count that fits in memory).
  * Returns ENGRAM_OK, ENGRAM_EINVAL or ENGRAM_EDTYPE. */
 int engram_gather(const void* table, int32_t dtype, int64_t row_begin, int64_t num_rows, int32_t dim,
                   const int64_t* rows, int64_t n, void* out, int64_t* status, hipStream_t stream);
@@ -254,7 +257,8 @@ int engram_unpermute_rows(const void* src, int64_t row_bytes, const int64_t* ord
  * that type); weights, biases and their gradients are fp32.  channels (conv)
  * and group_size (norm) times the element size must be a multiple of 16 bytes;
  * group_size * element size <= 10240 bytes (5120 bf16, 2560 fp32 features);
- * hidden % group_size == 0.
+ * hidden % group_size == 0.  At most 2^36 elements per tensor, and for the
+ * norm at most 2^25 (row, group) pairs, so that every launch fits.
  * 1 <= K <= 4, d >= 1.  Gradients of weight and bias are sums over every batch
  * row and position, reduced in a fixed order (deterministic), and overwrite
  * dweight / dbias.  The backward calls need a device workspace (256-byte

@@ -270,7 +270,24 @@ def test_oversized_ple_calls_rejected(lib):
     bf = B.ENGRAM_BF16
     assert lib.engram_short_conv(ok, bf, 1 << 20, 1 << 20, 8, ok, None, 4, 3, None, ok, None) == B.ENGRAM_EINVAL
     assert lib.engram_short_conv(ok, bf, 1, 1, 1 << 27, ok, None, 4, 3, None, ok, None) == B.ENGRAM_EINVAL
-    assert lib.engram_grouped_rms_norm(ok, bf, 1 << 30, 16, 8, ok, 1e-6, ok, None) == B.ENGRAM_EINVAL  # 2^31 waves
+    assert lib.engram_grouped_rms_norm(ok, bf, 1 << 30, 16, 8, ok, 1e-6, ok, None) == B.ENGRAM_EINVAL
+
+
+def test_calls_past_the_launch_limits_rejected(lib):
+    """Sizes whose launches would hold 2^32 work-items or more are refused up front."""
+    B._bind_ple(lib)
+    ok = ctypes.c_void_p(0x10000)
+    bf = B.ENGRAM_BF16
+    s = E.qwen3_8_flash_next_spec()
+    assert lib.engram_hash(ok, 1, 1 << 32, ctypes.byref(s), ok, None) == B.ENGRAM_EINVAL
+    assert lib.engram_hash(ok, 1 << 26, 64, ctypes.byref(s), ok, None) == B.ENGRAM_EINVAL
+    assert lib.engram_hash_slice(ok, 1 << 26, 128, 0, 64, ctypes.byref(s), ok, None) == B.ENGRAM_EINVAL
+    # PLE: 2^36 elements per tensor at most
+    assert lib.engram_short_conv(ok, bf, 1 << 18, 1 << 10, 512, ok, None, 4, 3, None, ok, None) == B.ENGRAM_EINVAL
+    # norm: 2^25 (row, group) pairs at most
+    assert lib.engram_grouped_rms_norm(ok, bf, (1 << 24) + 1, 16, 8, ok, 1e-6, ok, None) == B.ENGRAM_EINVAL
+    assert lib.engram_grouped_rms_norm_backward(ok, ok, bf, (1 << 24) + 1, 16, 8, ok, 1e-6, ok, ok, ok, 1 << 40,
+                                                None) == B.ENGRAM_EINVAL
 
 
 def test_missing_library_fails_loudly(monkeypatch):

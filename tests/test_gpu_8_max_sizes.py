@@ -1,6 +1,8 @@
 """The largest lookup count the scatter-add accepts (n = 2^31 - 1) and the same
 count through the gather, with 16-byte rows (8 bf16 values) so that everything
-fits in HBM (about 92 GB for the scatter-add, 52 GB for the gather).
+fits in HBM (about 92 GB for the scatter-add, 52 GB for the gather); and
+gathers whose work passes what one launch can hold (2^32 work-items), up to
+172 GB of output.
 
 The oracle cannot run at this size, so both checks use properties that hold at
 any size.  Lookup i reads row (i * 7919) mod R with R = 1,000,003 (prime, and
@@ -67,9 +69,32 @@ def test_gather_at_max_lookups():
     out = E.engram_gather(table, rows)   # validates: raises on any out-of-range row
     torch.cuda.synchronize()
     assert out.shape == (N_MAX, DIM)
-    for a in range(0, N_MAX, REF_CHUNK):
-        b = min(N_MAX, a + REF_CHUNK)
+    gather_matches_index_select(table, rows, out)
+    del rows, out, table
+    torch.cuda.empty_cache()
+
+
+def gather_matches_index_select(table, rows, out):
+    n = rows.numel()
+    for a in range(0, n, REF_CHUNK):
+        b = min(n, a + REF_CHUNK)
         ref = torch.index_select(table, 0, rows[a:b])
         assert torch.equal(out[a:b].view(torch.int16), ref.view(torch.int16)), (a, b)
+
+
+@pytest.mark.parametrize("dim,n", [
+    (256, (1 << 27) + 5),    # generic kernel: n * 32 chunks > 2^32 work-items, 69 GB of output
+    (160, (1 << 29) + 3),    # the 160-wide kernel's grid would pass 2^31 work-items: generic kernel, 172 GB
+])
+def test_gather_past_one_launch_of_work_items(dim, n):
+    dev = torch.device("cuda")
+    torch.cuda.empty_cache()
+    g = torch.Generator(device=dev)
+    g.manual_seed(dim)
+    table = torch.randn((R, dim), generator=g, device=dev).to(torch.bfloat16)
+    rows = strided_rows(n, dev)
+    out = E.engram_gather(table, rows)   # validates: raises on any out-of-range row
+    torch.cuda.synchronize()
+    gather_matches_index_select(table, rows, out)
     del rows, out, table
     torch.cuda.empty_cache()
