@@ -511,7 +511,10 @@ __global__ __launch_bounds__(kBlock) void segment_reduce_kernel(
     const int bb = cpr < B ? cpr : B;
     const int64_t wave = (int64_t)blockIdx.x * (kBlock / 64) + (threadIdx.x >> 6);
     const int64_t j = wave * wpw + sub;
-    if (blockIdx.x == 0 && threadIdx.x == 0) counters[1] = 0;  // long-run list of the fix-up that follows
+    if (blockIdx.x == 0 && threadIdx.x == 0) {  // long-run list of the fix-up that follows, its most parts
+        counters[1] = 0;
+        counters[2] = 0;
+    }
     // finished-part counts of the long-run sums two kernels on
     for (uint64_t i = (uint64_t)blockIdx.x * kBlock + threadIdx.x; i < num_slices; i += (uint64_t)gridDim.x * kBlock)
         long_done[i] = 0;
@@ -602,8 +605,15 @@ __global__ __launch_bounds__(kBlock) void segment_reduce_kernel(
 // galloping then binary search over the sorted keys (about 2 log2(run / S)
 // dependent loads).  A run over at most kLongRun slices is summed here by
 // one worker; a longer one (a hot row) is listed for long_run_kernel, which
-// splits its sum over a whole block.
+// splits its sum over a whole block, in parts of about kPartSlices slices
+// (at most kMaxParts); the list's largest part count bounds that kernel's
+// work items.
 constexpr int64_t kLongRun = 32;
+constexpr int64_t kPartSlices = 128;  // 64 was slower (more fences), 256 no faster
+constexpr int64_t kMaxParts = 32;
+__device__ __forceinline__ int64_t long_run_parts(int64_t head_partials) {
+    return min(kMaxParts, (head_partials + kPartSlices - 1) / kPartSlices);
+}
 
 template <int CPR_T, bool BF16, bool DENSE>
 __global__ __launch_bounds__(kBlock) void carry_fixup_kernel(
@@ -658,6 +668,7 @@ __global__ __launch_bounds__(kBlock) void carry_fixup_kernel(
     if (m - j > kLongRun) {
         if (c == 0) {
             const uint32_t at = atomicAdd(&counters[1], 1u);
+            atomicMax(&counters[2], (uint32_t)long_run_parts(m - j));
             if (at < num_slices) {
                 long_runs[2 * at] = (uint32_t)j;
                 long_runs[2 * at + 1] = (uint32_t)m;
@@ -683,13 +694,11 @@ __global__ __launch_bounds__(kBlock) void carry_fixup_kernel(
 // itself done; the block that counts last (a fence before the count releases
 // its sum, a fence after it acquires the others') adds the tail partial and
 // the part sums in part order.  The sum of a run does not depend on
-// scheduling; the list order may vary.  Work items are (part, run) pairs with
-// the first parts of all runs first, so every run's first part goes to a
-// different block.  A block has 8 waves, each lane holding 512 bytes of loads
+// scheduling; the list order may vary.  Work items are (part, run) pairs,
+// part below the list's largest part count, with the first parts of all runs
+// first, so every run's first part goes to a different block.  A block has 8 waves, each lane holding 512 bytes of loads
 // in flight.
 constexpr int kLongBlock = 512;
-constexpr int64_t kPartSlices = 128;  // 64 was slower (more fences), 256 no faster
-constexpr int64_t kMaxParts = 32;
 
 template <int CPR_T, bool BF16, bool DENSE>
 __global__ __launch_bounds__(kLongBlock) void long_run_kernel(
@@ -710,13 +719,13 @@ __global__ __launch_bounds__(kLongBlock) void long_run_kernel(
     const int w = (threadIdx.x >> 6) * wpw + sub;  // sub-worker index in the block
     const bool active = sub < wpw;
     const uint32_t count = min(counters[1], num_slices);
-    const uint64_t items = (uint64_t)count * kMaxParts;
+    const uint64_t items = (uint64_t)count * min((uint64_t)counters[2], (uint64_t)kMaxParts);
     for (uint64_t it = blockIdx.x; it < items; it += gridDim.x) {
         const uint32_t r = (uint32_t)(it % count);
         const int64_t p = (int64_t)(it / count);
         const int64_t j = long_runs[2 * r], m = long_runs[2 * r + 1];
         const int64_t total = m - j;  // head partials j+1 .. m
-        const int64_t parts = min(kMaxParts, (total + kPartSlices - 1) / kPartSlices);
+        const int64_t parts = long_run_parts(total);
         if (p >= parts) continue;  // uniform over the block
         const int64_t per_part = (total + parts - 1) / parts;
         const int64_t p0 = j + 1 + p * per_part, p1 = min(p0 + per_part, m + 1);
