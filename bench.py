@@ -67,8 +67,26 @@ def parse_args():
 
 
 def source_sha(name):
-    with open(os.path.join(CSRC, name), "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+    """SHA-256 prefix of a kernel source together with the local headers it
+    includes (recursively, in include order), so that a header edit marks
+    the counter summaries of every kernel built from it as stale."""
+    h = hashlib.sha256()
+    seen = set()
+
+    def add(fname):
+        if fname in seen or not os.path.exists(os.path.join(CSRC, fname)):
+            return
+        seen.add(fname)
+        with open(os.path.join(CSRC, fname), "rb") as f:
+            data = f.read()
+        h.update(data)
+        for line in data.decode(errors="replace").splitlines():
+            line = line.strip()
+            if line.startswith('#include "') and line.endswith('"'):
+                add(line[len('#include "'):-1])
+
+    add(name)
+    return h.hexdigest()[:16]
 
 
 def counter_traffic(kernel_file, summary_name, launches_per_step=1):

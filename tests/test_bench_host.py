@@ -83,3 +83,13 @@ def test_several_gpus_refused():
                        text=True, timeout=120)
     assert r.returncode != 0
     assert "one GPU" in (r.stdout + r.stderr)
+
+
+def test_source_sha_covers_included_headers(tmp_path, monkeypatch):
+    (tmp_path / "k.hip").write_text('#include "a.h"\nkernel\n')
+    (tmp_path / "a.h").write_text('#include "b.h"\nheader a\n')
+    (tmp_path / "b.h").write_text("header b v1\n")
+    monkeypatch.setattr(bench, "CSRC", str(tmp_path))
+    first = bench.source_sha("k.hip")
+    (tmp_path / "b.h").write_text("header b v2\n")
+    assert bench.source_sha("k.hip") != first
