@@ -129,3 +129,19 @@ def test_wide_shard_row_ids(dtype):
     ref[~in_table] = 0
     assert np.array_equal(to_host(out).view(np.uint8), ref.view(np.uint8))
     assert int(status.item()) == 100
+
+
+@pytest.mark.parametrize("dtype,dim", [(torch.bfloat16, 160), (torch.float32, 160), (torch.bfloat16, 64)])
+def test_empty_shard(dtype, dim):
+    """An owner with no rows: every lookup is out of range, so every output row is
+    zero and the status names lookup 0; the (empty) table is never read."""
+    table = torch.empty((0, dim), dtype=dtype, device="cuda")
+    rows = torch.arange(37, dtype=torch.int64, device="cuda") * 1000
+    status = torch.empty((), dtype=torch.int64, device="cuda")
+    out = torch.full((37, dim), 7, dtype=dtype, device="cuda")
+    E.engram_gather(table, rows, 0, out=out, status=status, validate=False)
+    torch.cuda.synchronize()
+    assert int(status.item()) == 0
+    assert torch.equal(out, torch.zeros_like(out))
+    with pytest.raises(E.EngramError, match="outside the owned range"):
+        E.engram_gather(table, rows)
