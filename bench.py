@@ -266,46 +266,63 @@ def host_info():
     return {"cpus_available": len(os.sched_getaffinity(0)), "cpu_model": model}
 
 
-def cpu_baseline(wl, max_tokens=None):
-    """The oracle (plain single-threaded C) on the same stream as rotation 0."""
+def cpu_baseline(wl, max_tokens=None, target_seconds=10.0):
+    """The oracle (plain single-threaded C) on the same streams as the timed
+    steps: rotation after rotation until at least `target_seconds` of oracle
+    work (or every rotation) has been timed."""
     import numpy as np
     import torch
 
     import workloads as W
     from oracle import c_oracle, constants as C
 
-    b = wl["batches"][0]
-    if b["tokens"] is None:
-        return None
-    ids = b["ids"]
-    if max_tokens is not None and ids.shape[1] > max_tokens:
-        ids = ids[:, :max_tokens]
     if wl["name"] == "sft":
         ws = W.sft_spec()
         mods, offs = ws["vocab_sizes"], ws["offsets"]
     else:
         mods, offs = C.head_vocab_sizes(), C.head_offsets()
-    # Sample preparation (untimed): the oracle gathers from a host copy of exactly
-    # the table rows this stream reads, renumbered; the 102.4 GB table stays on the GPU.
-    rows_prep = c_oracle.hash_input_ids(ids, 3, 8, C.EOS_TOKEN_ID, 0, C.LAYER_MULTIPLIERS, mods, offs).reshape(-1)
-    uniq, inv = np.unique(rows_prep, return_inverse=True)
-    sub = wl["table"][torch.from_numpy(uniq).to(wl["table"].device)].cpu().view(torch.int16).numpy().view(np.uint16)
-    inv = inv.astype(np.int64)
-    n = rows_prep.size
-    dy = b["dy"][:n].cpu().view(torch.int16).numpy().view(np.uint16) if "dy" in b else None
-    t0 = time.perf_counter()
-    rows = c_oracle.hash_input_ids(ids, 3, 8, C.EOS_TOKEN_ID, 0, C.LAYER_MULTIPLIERS, mods, offs).reshape(-1)
-    t1 = time.perf_counter()
-    out, _ = c_oracle.gather(sub, inv)
-    t2 = time.perf_counter()
-    if dy is not None:
-        c_oracle.scatter_add_compact(rows, dy, wl["table_rows"], wl["row_begin"])
-    t3 = time.perf_counter()
-    del out
-    return {"value": n / (t3 - t0), "unit": "lookups/s", "cores": 1, "kind": "oracle", "host": host_info(),
-            "sample": "%d tokens (%d lookups) of rotation 0: hash, gather from a host copy of the %d distinct "
-                      "rows read, compact scatter-add; single-threaded C" % (ids.size, n, uniq.size),
-            "seconds": {"hash": round(t1 - t0, 3), "gather": round(t2 - t1, 3), "scatter_add": round(t3 - t2, 3)}}
+    secs = {"hash": 0.0, "gather": 0.0, "scatter_add": 0.0}
+    lookups, tokens, rotations, distinct = 0, 0, 0, []
+    for b in wl["batches"]:
+        if b["tokens"] is None:
+            return None
+        ids = b["ids"]
+        if max_tokens is not None and ids.shape[1] > max_tokens:
+            ids = ids[:, :max_tokens]
+        # Sample preparation (untimed): the oracle gathers from a host copy of exactly
+        # the table rows this stream reads, renumbered; the 102.4 GB table stays on the GPU.
+        rows_prep = c_oracle.hash_input_ids(ids, 3, 8, C.EOS_TOKEN_ID, 0, C.LAYER_MULTIPLIERS, mods,
+                                            offs).reshape(-1)
+        uniq, inv = np.unique(rows_prep, return_inverse=True)
+        sub = wl["table"][torch.from_numpy(uniq).to(wl["table"].device)].cpu().view(torch.int16).numpy() \
+            .view(np.uint16)
+        inv = inv.astype(np.int64)
+        n = rows_prep.size
+        dy = b["dy"][:n].cpu().view(torch.int16).numpy().view(np.uint16) if "dy" in b else None
+        t0 = time.perf_counter()
+        rows = c_oracle.hash_input_ids(ids, 3, 8, C.EOS_TOKEN_ID, 0, C.LAYER_MULTIPLIERS, mods, offs).reshape(-1)
+        t1 = time.perf_counter()
+        out, _ = c_oracle.gather(sub, inv)
+        t2 = time.perf_counter()
+        if dy is not None:
+            c_oracle.scatter_add_compact(rows, dy, wl["table_rows"], wl["row_begin"])
+        t3 = time.perf_counter()
+        del out, sub
+        secs["hash"] += t1 - t0
+        secs["gather"] += t2 - t1
+        secs["scatter_add"] += t3 - t2
+        lookups += n
+        tokens += ids.size
+        rotations += 1
+        distinct.append(int(uniq.size))
+        if sum(secs.values()) >= target_seconds:
+            break
+    total = sum(secs.values())
+    return {"value": lookups / total, "unit": "lookups/s", "cores": 1, "kind": "oracle", "host": host_info(),
+            "sample": "%d rotation(s), %d tokens (%d lookups) in all: hash, gather from a host copy of each "
+                      "rotation's distinct rows (%s), compact scatter-add; single-threaded C"
+                      % (rotations, tokens, lookups, ", ".join(str(u) for u in distinct)),
+            "seconds": {k: round(v, 3) for k, v in secs.items()}}
 
 
 # ---------------------------------------------------------------- PLE conv + norm
@@ -396,29 +413,38 @@ def timed_phases(step, rots, nphases, steps):
     return t1 - t0, mean, pct, dom
 
 
-def ple_cpu_baseline(wl, sample_rows=2):
-    """The fp64 numpy oracle on the first ``sample_rows`` batch rows of rotation 0."""
-    import torch
-
+def ple_cpu_baseline(wl, sample_rows=2, target_seconds=10.0):
+    """The fp64 numpy oracle on successive groups of ``sample_rows`` batch rows
+    (rotation 0 first, then the next rotations) until at least
+    `target_seconds` of oracle work has been timed."""
     from oracle import ple_ref as P
-    t = wl["rots"][0]
-    x = t["x"][:sample_rows].double().cpu().numpy()
-    dy = t["dy"][:sample_rows].double().cpu().numpy()
-    halo = t["halo"][:sample_rows].double().cpu().numpy()
-    cw, cb, nw = (t[k].double().cpu().numpy() for k in ("conv_w", "conv_b", "norm_w"))
     G = wl["group"]
-    t0 = time.perf_counter()
-    c = P.short_conv(x, cw, cb, 3, halo)
-    P.grouped_rms_norm(c, nw, G)
-    dc, _ = P.grouped_rms_norm_backward(c, dy, nw, G)
-    P.short_conv_backward(x, dc, cw, 3, halo)
-    t1 = time.perf_counter()
-    tokens = sample_rows * wl["seq"]
-    return {"value": tokens / (t1 - t0), "unit": "tokens/s", "cores": 1, "kind": "oracle", "host": host_info(),
-            "sample": "%d of the %d batch rows of rotation 0 (%d tokens x %d channels): conv, norm, their "
-                      "backwards in fp64 numpy, single-threaded" % (sample_rows, wl["batch"], tokens,
-                                                                    wl["channels"]),
-            "seconds": round(t1 - t0, 3)}
+    spent, tokens, groups = 0.0, 0, 0
+    for t in wl["rots"]:
+        cw, cb, nw = (t[k].double().cpu().numpy() for k in ("conv_w", "conv_b", "norm_w"))
+        for r0 in range(0, wl["batch"], sample_rows):
+            r1 = min(wl["batch"], r0 + sample_rows)
+            x = t["x"][r0:r1].double().cpu().numpy()
+            dy = t["dy"][r0:r1].double().cpu().numpy()
+            halo = t["halo"][r0:r1].double().cpu().numpy()
+            t0 = time.perf_counter()
+            c = P.short_conv(x, cw, cb, 3, halo)
+            P.grouped_rms_norm(c, nw, G)
+            dc, _ = P.grouped_rms_norm_backward(c, dy, nw, G)
+            P.short_conv_backward(x, dc, cw, 3, halo)
+            spent += time.perf_counter() - t0
+            tokens += (r1 - r0) * wl["seq"]
+            groups += 1
+            del x, dy, halo, c, dc
+            if spent >= target_seconds:
+                break
+        if spent >= target_seconds:
+            break
+    return {"value": tokens / spent, "unit": "tokens/s", "cores": 1, "kind": "oracle", "host": host_info(),
+            "sample": "%d groups of %d batch rows (%d tokens x %d channels in all), rotation 0 first: conv, norm, "
+                      "their backwards in fp64 numpy, single-threaded" % (groups, sample_rows, tokens,
+                                                                          wl["channels"]),
+            "seconds": round(spent, 3)}
 
 
 def ple_main(args, dev):
@@ -549,28 +575,33 @@ def route_step(wl, t, ev=None):
     mark()
 
 
-def route_cpu_baseline(wl):
+def route_cpu_baseline(wl, target_seconds=10.0):
+    """The routing oracle on whole rotations, cycling through them, until at
+    least `target_seconds` of oracle work has been timed."""
     import numpy as np
 
     from oracle import route_ref as RR
-    t = wl["rots"][0]
-    ids = t["ids"].cpu().numpy()
-    vals = t["vals"].float().cpu().numpy()
-    W_, NE, cap = wl["world"], wl["num_embeddings"], t["cap"]
-    t0 = time.perf_counter()
-    s, order, counts, _ = RR.route_plan(ids, NE, W_)
-    RR.validate(s, counts, NE, W_)
-    packed_ids, _ = RR.pack(s, counts, W_, cap, -1)
-    RR.unpack(packed_ids, counts, ids.size)
-    packed, _ = RR.pack(vals, counts, W_, cap, 0.0)
-    grouped = RR.unpack(packed, counts, ids.size)
-    out = np.empty_like(grouped)
-    out[order] = grouped
-    t1 = time.perf_counter()
-    return {"value": ids.size / (t1 - t0), "unit": "lookups/s", "cores": 1, "kind": "oracle", "host": host_info(),
-            "sample": "rotation 0 in full (%d lookups, world %d, capacity %d), plain Python loops over segments "
-                      "with numpy arrays, single-threaded" % (ids.size, W_, cap),
-            "seconds": round(t1 - t0, 3)}
+    W_, NE = wl["world"], wl["num_embeddings"]
+    host = [(t["ids"].cpu().numpy(), t["vals"].float().cpu().numpy(), t["cap"]) for t in wl["rots"]]
+    spent, lookups, passes = 0.0, 0, 0
+    while spent < target_seconds:
+        ids, vals, cap = host[passes % len(host)]
+        t0 = time.perf_counter()
+        s, order, counts, _ = RR.route_plan(ids, NE, W_)
+        RR.validate(s, counts, NE, W_)
+        packed_ids, _ = RR.pack(s, counts, W_, cap, -1)
+        RR.unpack(packed_ids, counts, ids.size)
+        packed, _ = RR.pack(vals, counts, W_, cap, 0.0)
+        grouped = RR.unpack(packed, counts, ids.size)
+        out = np.empty_like(grouped)
+        out[order] = grouped
+        spent += time.perf_counter() - t0
+        lookups += ids.size
+        passes += 1
+    return {"value": lookups / spent, "unit": "lookups/s", "cores": 1, "kind": "oracle", "host": host_info(),
+            "sample": "%d passes over the %d rotations in turn (%d lookups in all, world %d), plain Python loops "
+                      "over segments with numpy arrays, single-threaded" % (passes, len(host), lookups, W_),
+            "seconds": round(spent, 3)}
 
 
 def route_main(args, dev):
