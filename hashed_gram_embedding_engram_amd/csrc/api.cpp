@@ -60,7 +60,8 @@ int hash_common(const int64_t* tokens, int64_t batch, int64_t seq_len, int64_t s
     if (rc != ENGRAM_OK) return rc;
     const int64_t width = seq_end - seq_begin;
     if (batch == 0 || width == 0) return ENGRAM_OK;
-    if (!tokens || !rows_out || !aligned(tokens, 8) || !aligned(rows_out, 8)) return ENGRAM_EINVAL;
+    // rows are stored as 16-byte pairs of int64
+    if (!tokens || !rows_out || !aligned(tokens, 8) || !aligned(rows_out, 16)) return ENGRAM_EINVAL;
     // one work-item per position: a launch holds fewer than 2^32
     if (batch > INT64_MAX / width / ENGRAM_MAX_HEADS || batch * width > ((int64_t)1 << 32) - 64) return ENGRAM_EINVAL;
     return launch_result(engram::launch_hash(tokens, batch, seq_len, seq_begin, seq_end, p, rows_out, stream));
@@ -205,22 +206,25 @@ int engram_route_validate(const int64_t* sorted_ids, int64_t n, const int64_t* s
     return launch_result(engram::launch_route_validate(sorted_ids, n, send_counts, world, local_rows, status, stream));
 }
 
-int engram_pack_fixed_capacity(const void* src, int64_t row_bytes, const int64_t* split_sizes, int32_t world,
-                               int64_t capacity, const void* fill, int32_t fill_bytes, void* dst, int64_t* status,
-                               hipStream_t stream) {
-    if (world < 1 || world > 255 || capacity < 0 || !row_layout_ok(row_bytes) || !split_sizes) return ENGRAM_EINVAL;
+int engram_pack_fixed_capacity(const void* src, int64_t src_rows, int64_t row_bytes, const int64_t* split_sizes,
+                               int32_t world, int64_t capacity, const void* fill, int32_t fill_bytes, void* dst,
+                               int64_t* status, hipStream_t stream) {
+    if (world < 1 || world > 255 || capacity < 0 || src_rows < 0 || !row_layout_ok(row_bytes) || !split_sizes)
+        return ENGRAM_EINVAL;
     if (!(fill_bytes == 1 || fill_bytes == 2 || fill_bytes == 4 || fill_bytes == 8) || !fill) return ENGRAM_EINVAL;
     if (row_bytes % fill_bytes != 0) return ENGRAM_EINVAL;
-    if (capacity > 0 && (!dst || !src)) return ENGRAM_EINVAL;
+    if (capacity > 0 && (!dst || (src_rows > 0 && !src))) return ENGRAM_EINVAL;
     if (!aligned(src, 4) || !aligned(dst, 4) || !aligned(split_sizes, 8) || !aligned(status, 8)) return ENGRAM_EINVAL;
-    if ((int64_t)world * capacity > ((int64_t)1 << 40) / row_bytes) return ENGRAM_EINVAL;
+    if ((int64_t)world * capacity > ((int64_t)1 << 40) / row_bytes || src_rows > ((int64_t)1 << 40) / row_bytes)
+        return ENGRAM_EINVAL;
     uint32_t fill16[4];
     unsigned char bytes[16];
     for (int i = 0; i < 16; ++i) bytes[i] = ((const unsigned char*)fill)[i % fill_bytes];
     for (int i = 0; i < 4; ++i)
         fill16[i] = (uint32_t)bytes[4 * i] | ((uint32_t)bytes[4 * i + 1] << 8) | ((uint32_t)bytes[4 * i + 2] << 16) |
                     ((uint32_t)bytes[4 * i + 3] << 24);
-    return launch_result(engram::launch_pack(src, row_bytes, split_sizes, world, capacity, fill16, dst, status, stream));
+    return launch_result(
+        engram::launch_pack(src, src_rows, row_bytes, split_sizes, world, capacity, fill16, dst, status, stream));
 }
 
 int engram_unpack_fixed_capacity(const void* src, int64_t row_bytes, const int64_t* split_sizes, int32_t world,

@@ -54,8 +54,8 @@ hipError_t launch_route_plan(const int64_t* ids, int64_t n, int64_t local_rows, 
                              hipStream_t stream);
 hipError_t launch_route_validate(const int64_t* sorted_ids, int64_t n, const int64_t* send_counts, int world,
                                  int64_t local_rows, int64_t* status, hipStream_t stream);
-hipError_t launch_pack(const void* src, int64_t row_bytes, const int64_t* counts, int world, int64_t capacity,
-                       const uint32_t fill16[4], void* dst, int64_t* status, hipStream_t stream);
+hipError_t launch_pack(const void* src, int64_t src_rows, int64_t row_bytes, const int64_t* counts, int world,
+                       int64_t capacity, const uint32_t fill16[4], void* dst, int64_t* status, hipStream_t stream);
 hipError_t launch_unpack(const void* src, int64_t row_bytes, const int64_t* counts, int world, int64_t capacity,
                          void* dst, int64_t dst_rows, int64_t* status, hipStream_t stream);
 hipError_t launch_permute(const void* src, int64_t row_bytes, const int64_t* order, int64_t n, void* dst, bool gather,

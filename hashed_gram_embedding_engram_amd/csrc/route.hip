@@ -200,20 +200,27 @@ __device__ __forceinline__ uint32_t fill_unit<uint32_t>(u32x4 fill, uint32_t k) 
 
 // Copy unit U: 16 bytes when rows allow it, else 4 bytes.  Segment w's
 // min(count, capacity) rows go to block w, the rest of the block is the fill.
+// Only the first src_rows source rows are read: a block row whose source lies
+// past them takes the fill too (status world, unless a bad count is lower).
 // The copy kernels move K 16-byte (or 4-byte) units per thread per loop
 // step, all loads issued before the stores.  Measured on the world-64 step:
 // K = 4 helps the unpack (the compact side is written sequentially) and the
 // 4-byte units; the pack of 16-byte units gains little and the scattering
 // permute loses, so each launch picks its own K.
 template <typename U, typename I, int K>
-__global__ __launch_bounds__(kBlock) void pack_kernel(const U* __restrict__ src, int64_t row_units,
+__global__ __launch_bounds__(kBlock) void pack_kernel(const U* __restrict__ src, int64_t src_rows, int64_t row_units,
                                                       const int64_t* __restrict__ counts, int world, int64_t capacity,
                                                       u32x4 fill, U* __restrict__ dst, int64_t* __restrict__ status) {
     const int w = blockIdx.y;
     const SegmentInfo si = segment_info(counts, world, w, capacity, false);
     const int64_t c = counts[w];
-    if (blockIdx.x == 0 && threadIdx.x == 0 && (c < 0 || c > capacity)) report_bad(status, w);
-    const I rows = (I)(c < 0 ? 0 : (c > capacity ? capacity : c));
+    const int64_t kept = c < 0 ? 0 : (c > capacity ? capacity : c);
+    const int64_t avail = min(kept, max((int64_t)0, src_rows - si.off));  // kept rows that exist in src
+    if (blockIdx.x == 0 && threadIdx.x == 0) {
+        if (c < 0 || c > capacity) report_bad(status, w);
+        if (avail < kept) report_bad(status, world);
+    }
+    const I rows = (I)avail;
     const I units = (I)row_units, seg_units = (I)(capacity * row_units);
     const U* __restrict__ s = src + si.off * row_units;
     U* __restrict__ d = dst + (int64_t)w * capacity * row_units;
@@ -374,21 +381,21 @@ hipError_t launch_route_validate(const int64_t* sorted_ids, int64_t n, const int
             hipLaunchKernelGGL((KERNEL<U, uint64_t, K>), grid, dim3(kBlock), 0, stream, __VA_ARGS__);     \
     } while (0)
 
-hipError_t launch_pack(const void* src, int64_t row_bytes, const int64_t* counts, int world, int64_t capacity,
-                       const uint32_t fill16[4], void* dst, int64_t* status, hipStream_t stream) {
+hipError_t launch_pack(const void* src, int64_t src_rows, int64_t row_bytes, const int64_t* counts, int world,
+                       int64_t capacity, const uint32_t fill16[4], void* dst, int64_t* status, hipStream_t stream) {
     hipError_t err = launch_status_init(status, stream);
     if (err != hipSuccess) return err;
     const bool wide = row_bytes % 16 == 0 && ((uintptr_t)src % 16) == 0 && ((uintptr_t)dst % 16) == 0;
     if (wide) {
         const int64_t units = row_bytes / 16;
         const u32x4 f = {fill16[0], fill16[1], fill16[2], fill16[3]};
-        ENGRAM_SEGMENT_LAUNCH(pack_kernel, u32x4, 2, capacity * units, (const u32x4*)src, units, counts, world, capacity,
-                              f, (u32x4*)dst, status);
+        ENGRAM_SEGMENT_LAUNCH(pack_kernel, u32x4, 2, capacity * units, (const u32x4*)src, src_rows, units, counts, world,
+                              capacity, f, (u32x4*)dst, status);
     } else {
         const int64_t units = row_bytes / 4;
         const u32x4 f = {fill16[0], fill16[1], fill16[2], fill16[3]};
-        ENGRAM_SEGMENT_LAUNCH(pack_kernel, uint32_t, 4, capacity * units, (const uint32_t*)src, units, counts, world,
-                              capacity, f, (uint32_t*)dst, status);
+        ENGRAM_SEGMENT_LAUNCH(pack_kernel, uint32_t, 4, capacity * units, (const uint32_t*)src, src_rows, units, counts,
+                              world, capacity, f, (uint32_t*)dst, status);
     }
     return hipGetLastError();
 }

