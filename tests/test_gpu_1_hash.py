@@ -130,20 +130,26 @@ def test_slice_equals_full_columns():
     ids, lengths = W.long_context_stream(3, total=20000)
     t = torch.from_numpy(ids).cuda()
     spec = E.qwen3_8_flash_next_spec()
+    ref = oracle_hash(ids, full_oracle_spec())          # the oracle's hash of the whole sequence
     full = E.engram_hash(t, spec).cpu().numpy()
+    assert np.array_equal(full, ref)
     ends = np.cumsum(lengths)
+    assert ids[0, int(ends[0]) - 1] == C.EOS_TOKEN_ID   # the cuts below straddle EOS positions
     cuts = [0, 1, 2, 3, 63, 64, 65, 2500, 19999, 20000] + [int(e) + d for e in ends[:3] for d in (-2, -1, 0, 1, 2)]
     for a in cuts:
         for b in (a, a + 1, a + 2, a + 64, a + 1000, 20000):
             if not (0 <= a <= b <= 20000):
                 continue
             part = E.engram_hash_slice(t, a, b, spec).cpu().numpy()
+            assert np.array_equal(part, ref[:, a:b]), (a, b)
             assert np.array_equal(part, full[:, a:b]), (a, b)
-    # a batched slice
+    # a batched slice: two independent rows
     ids2 = np.stack([ids[0, :5000], ids[0, 5000:10000]])
     t2 = torch.from_numpy(np.ascontiguousarray(ids2)).cuda()
-    full2 = E.engram_hash(t2, spec).cpu().numpy()
-    assert np.array_equal(E.engram_hash_slice(t2, 1234, 4321, spec).cpu().numpy(), full2[:, 1234:4321])
+    ref2 = oracle_hash(ids2, full_oracle_spec())
+    part2 = E.engram_hash_slice(t2, 1234, 4321, spec).cpu().numpy()
+    assert np.array_equal(part2, ref2[:, 1234:4321])
+    assert np.array_equal(part2, E.engram_hash(t2, spec).cpu().numpy()[:, 1234:4321])
 
 
 def test_rehash_in_backward():
@@ -159,6 +165,7 @@ def test_rehash_in_backward():
     ur, ug = E.engram_scatter_add(kept, dy, W.FULL_ROWS)
     again = torch.cat([E.engram_hash_slice(t, a, b, spec).reshape(-1)
                        for a, b in ((0, 7000), (7000, 7001), (7001, 30000))])
+    assert np.array_equal(again.cpu().numpy(), oracle_hash(ids, full_oracle_spec()).reshape(-1))
     ur2, ug2 = E.engram_scatter_add(again, dy, W.FULL_ROWS)
     assert torch.equal(ur, ur2)
     assert torch.equal(ug.view(torch.int32), ug2.view(torch.int32))
