@@ -253,7 +253,7 @@ def percentiles(ms):
 
 
 def host_info():
-    """The CPUs this process may run on and their model name (the baseline uses one)."""
+    """The CPUs this process may run on, their model name and the host memory."""
     model = None
     try:
         with open("/proc/cpuinfo") as f:
@@ -263,13 +263,46 @@ def host_info():
                     break
     except OSError:
         pass
-    return {"cpus_available": len(os.sched_getaffinity(0)), "cpu_model": model}
+    info = {"cpus_available": len(os.sched_getaffinity(0)), "cpu_model": model}
+    try:
+        import psutil
+        vm = psutil.virtual_memory()
+        info.update({"mem_total_gb": round(vm.total / 1e9, 1), "mem_available_gb": round(vm.available / 1e9, 1)})
+    except Exception:
+        pass
+    return info
 
 
-def cpu_baseline(wl, max_tokens=None, target_seconds=10.0):
-    """The oracle (plain single-threaded C) on the same streams as the timed
-    steps: rotation after rotation until at least `target_seconds` of oracle
-    work (or every rotation) has been timed."""
+def host_table(wl, margin=64e9):
+    """The table as the oracle reads it: a host copy of the whole table when host
+    memory holds it with `margin` to spare (copied from the GPU in 1 GiB
+    chunks), else None."""
+    import numpy as np
+    import torch
+    table = wl["table"]
+    need = table.numel() * table.element_size()
+    try:
+        import psutil
+        if psutil.virtual_memory().available < need + margin:
+            return None
+    except Exception:
+        return None
+    host = np.empty(tuple(table.shape), dtype=np.uint16)
+    step = max(1, (1 << 30) // (table.shape[1] * table.element_size()))
+    for r0 in range(0, table.shape[0], step):
+        r1 = min(table.shape[0], r0 + step)
+        torch.from_numpy(host[r0:r1].view(np.int16)).copy_(table[r0:r1].view(torch.int16))
+    return host
+
+
+def cpu_baseline(wl, target_seconds=10.0, mt_seconds=5.0):
+    """The oracle on the same streams as the timed steps, twice: the plain
+    single-threaded C oracle, rotation after rotation until at least
+    `target_seconds` of its work has been timed, then its OpenMP twin (same
+    bits, every host core the process may use) until at least `mt_seconds`.
+    Each pass is hash, gather, compact scatter-add.  The gather reads a host
+    copy of the whole table when host memory holds one, else a host copy of
+    exactly the rows the stream reads (renumbered)."""
     import numpy as np
     import torch
 
@@ -281,48 +314,63 @@ def cpu_baseline(wl, max_tokens=None, target_seconds=10.0):
         mods, offs = ws["vocab_sizes"], ws["offsets"]
     else:
         mods, offs = C.head_vocab_sizes(), C.head_offsets()
-    secs = {"hash": 0.0, "gather": 0.0, "scatter_add": 0.0}
-    lookups, tokens, rotations, distinct = 0, 0, 0, []
+    if any(b["tokens"] is None for b in wl["batches"]):
+        return None
+    full = host_table(wl)
+    prep = []
     for b in wl["batches"]:
-        if b["tokens"] is None:
-            return None
         ids = b["ids"]
-        if max_tokens is not None and ids.shape[1] > max_tokens:
-            ids = ids[:, :max_tokens]
-        # Sample preparation (untimed): the oracle gathers from a host copy of exactly
-        # the table rows this stream reads, renumbered; the 102.4 GB table stays on the GPU.
-        rows_prep = c_oracle.hash_input_ids(ids, 3, 8, C.EOS_TOKEN_ID, 0, C.LAYER_MULTIPLIERS, mods,
-                                            offs).reshape(-1)
+        n = ids.size * 16
+        dy = b["dy"][:n].cpu().view(torch.int16).numpy().view(np.uint16) if "dy" in b else None
+        if full is not None:
+            prep.append((ids, full, None, dy, wl["row_begin"]))
+            continue
+        # no room for the whole table: the rows this stream reads, renumbered (untimed)
+        rows_prep = c_oracle.hash_input_ids(ids, 3, 8, C.EOS_TOKEN_ID, 0, C.LAYER_MULTIPLIERS, mods, offs).reshape(-1)
         uniq, inv = np.unique(rows_prep, return_inverse=True)
         sub = wl["table"][torch.from_numpy(uniq).to(wl["table"].device)].cpu().view(torch.int16).numpy() \
             .view(np.uint16)
-        inv = inv.astype(np.int64)
-        n = rows_prep.size
-        dy = b["dy"][:n].cpu().view(torch.int16).numpy().view(np.uint16) if "dy" in b else None
-        t0 = time.perf_counter()
-        rows = c_oracle.hash_input_ids(ids, 3, 8, C.EOS_TOKEN_ID, 0, C.LAYER_MULTIPLIERS, mods, offs).reshape(-1)
-        t1 = time.perf_counter()
-        out, _ = c_oracle.gather(sub, inv)
-        t2 = time.perf_counter()
-        if dy is not None:
-            c_oracle.scatter_add_compact(rows, dy, wl["table_rows"], wl["row_begin"])
-        t3 = time.perf_counter()
-        del out, sub
-        secs["hash"] += t1 - t0
-        secs["gather"] += t2 - t1
-        secs["scatter_add"] += t3 - t2
-        lookups += n
-        tokens += ids.size
-        rotations += 1
-        distinct.append(int(uniq.size))
-        if sum(secs.values()) >= target_seconds:
-            break
-    total = sum(secs.values())
-    return {"value": lookups / total, "unit": "lookups/s", "cores": 1, "kind": "oracle", "host": host_info(),
-            "sample": "%d rotation(s), %d tokens (%d lookups) in all: hash, gather from a host copy of each "
-                      "rotation's distinct rows (%s), compact scatter-add; single-threaded C"
-                      % (rotations, tokens, lookups, ", ".join(str(u) for u in distinct)),
-            "seconds": {k: round(v, 3) for k, v in secs.items()}}
+        prep.append((ids, sub, inv.astype(np.int64), dy, 0))
+
+    def run(mt, budget):
+        hash_fn = c_oracle.hash_input_ids_mt if mt else c_oracle.hash_input_ids
+        gather_fn = c_oracle.gather_mt if mt else c_oracle.gather
+        scatter_fn = c_oracle.scatter_add_compact_mt if mt else c_oracle.scatter_add_compact
+        secs = {"hash": 0.0, "gather": 0.0, "scatter_add": 0.0}
+        lookups, passes = 0, 0
+        while sum(secs.values()) < budget and passes < 64:
+            ids, tab, remap, dy, row_begin = prep[passes % len(prep)]
+            t0 = time.perf_counter()
+            rows = hash_fn(ids, 3, 8, C.EOS_TOKEN_ID, 0, C.LAYER_MULTIPLIERS, mods, offs).reshape(-1)
+            t1 = time.perf_counter()
+            out, bad = gather_fn(tab, rows if remap is None else remap, row_begin)
+            t2 = time.perf_counter()
+            if dy is not None:
+                scatter_fn(rows, dy, wl["table_rows"], wl["row_begin"])
+            t3 = time.perf_counter()
+            assert bad == -1
+            del out
+            secs["hash"] += t1 - t0
+            secs["gather"] += t2 - t1
+            secs["scatter_add"] += t3 - t2
+            lookups += rows.size
+            passes += 1
+        return lookups, passes, secs
+
+    l1, p1, s1 = run(False, target_seconds)
+    lm, pm, sm = run(True, mt_seconds)
+    threads = c_oracle.mt_threads()
+    what = "hash, gather, compact scatter-add" if prep[0][3] is not None else "hash, gather"
+    table_note = ("a host copy of the whole %d-row table" % wl["table_rows"] if full is not None else
+                  "a host copy of only the rows each stream reads (host memory cannot hold the whole table)")
+    return {"value": lm / sum(sm.values()), "unit": "lookups/s", "cores": threads, "kind": "oracle",
+            "host": host_info(),
+            "sample": "OpenMP oracle on %d threads: %d passes over the %d rotations in turn (%d lookups in all): "
+                      "%s; the gather reads %s" % (threads, pm, len(prep), lm, what, table_note),
+            "seconds": {k: round(v, 3) for k, v in sm.items()},
+            "single_thread": {"value": l1 / sum(s1.values()), "cores": 1,
+                              "sample": "plain single-threaded C oracle: %d passes (%d lookups)" % (p1, l1),
+                              "seconds": {k: round(v, 3) for k, v in s1.items()}}}
 
 
 # ---------------------------------------------------------------- PLE conv + norm

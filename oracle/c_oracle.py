@@ -2,7 +2,10 @@
 
 numpy arrays in, numpy arrays out; no GPU, no torch.  ``build()`` compiles the
 C file with gcc into ``oracle/libengram_oracle.so``; ``load()`` builds it when
-it is missing.
+it is missing.  The ``*_mt`` functions call the OpenMP twins in
+``engram_oracle_mt.c`` (``oracle/libengram_oracle_mt.so``), which spread the
+same computation over every host core for the CPU baseline and give the same
+bits.
 """
 import ctypes
 import os
@@ -13,7 +16,10 @@ import numpy as np
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "engram_oracle.c")
 _LIB = os.path.join(_HERE, "libengram_oracle.so")
+_SRC_MT = os.path.join(_HERE, "engram_oracle_mt.c")
+_LIB_MT = os.path.join(_HERE, "libengram_oracle_mt.so")
 _lib = None
+_lib_mt = None
 
 _p = ctypes.c_void_p
 _i64 = ctypes.c_int64
@@ -21,10 +27,13 @@ _i32 = ctypes.c_int32
 
 
 def build():
-    """Compile the oracle (plain -O2 C, single-threaded)."""
+    """Compile the oracle (plain -O2 C, single-threaded) and its OpenMP twin."""
     tmp = _LIB + ".tmp"
     subprocess.check_call(["gcc", "-O2", "-std=c11", "-fPIC", "-shared", "-o", tmp, _SRC])
     os.replace(tmp, _LIB)
+    tmp = _LIB_MT + ".tmp"
+    subprocess.check_call(["gcc", "-O2", "-std=gnu11", "-fopenmp", "-fPIC", "-shared", "-o", tmp, _SRC_MT])
+    os.replace(tmp, _LIB_MT)
     return _LIB
 
 
@@ -126,5 +135,78 @@ def scatter_add_compact(rows, dy, num_rows, row_begin=0):
     nu = np.zeros(1, dtype=np.int64)
     bad = lib.oracle_scatter_add_compact(_ptr(rows_flat), n, _ptr(dy), is_bf16, dim, int(row_begin),
                                          num_rows, _ptr(uniq_rows), _ptr(uniq_grad), _ptr(nu))
+    u = int(nu[0])
+    return uniq_rows[:u].copy(), uniq_grad[:u].copy(), int(bad)
+
+
+# ---- the OpenMP twins (same results, every host core)
+
+def load_mt():
+    global _lib_mt
+    if _lib_mt is not None:
+        return _lib_mt
+    if not os.path.exists(_LIB_MT) or os.path.getmtime(_LIB_MT) < os.path.getmtime(_SRC_MT):
+        build()
+    lib = ctypes.CDLL(_LIB_MT)
+    lib.oracle_mt_threads.restype = ctypes.c_int
+    lib.oracle_mt_threads.argtypes = []
+    lib.oracle_mt_hash.restype = ctypes.c_int
+    lib.oracle_mt_hash.argtypes = [_p, _i64, _i64, _i32, _i32, _i64, _i64, _p, _p, _p, _p]
+    lib.oracle_mt_gather.restype = _i64
+    lib.oracle_mt_gather.argtypes = [_p, _i32, _i32, _i64, _i64, _p, _i64, _p]
+    lib.oracle_mt_scatter_add_compact.restype = _i64
+    lib.oracle_mt_scatter_add_compact.argtypes = [_p, _i64, _p, _i32, _i32, _i64, _i64, _p, _p, _p]
+    _lib_mt = lib
+    return lib
+
+
+def mt_threads():
+    """OpenMP threads the *_mt functions run on."""
+    return int(load_mt().oracle_mt_threads())
+
+
+def hash_input_ids_mt(ids, ngram_size, heads_per_ngram, eos, fill, multipliers, vocab_sizes, offsets):
+    lib = load_mt()
+    ids = np.ascontiguousarray(ids, dtype=np.int64)
+    assert ids.ndim == 2
+    batch, seq = ids.shape
+    heads = (ngram_size - 1) * heads_per_ngram
+    mult = np.ascontiguousarray(multipliers, dtype=np.int64)
+    mods = np.ascontiguousarray(vocab_sizes, dtype=np.int64)
+    offs = np.ascontiguousarray(offsets, dtype=np.int64)
+    assert mult.size >= ngram_size and mods.size == heads and offs.size == heads
+    rows = np.empty((batch, seq, heads), dtype=np.int64)
+    rc = lib.oracle_mt_hash(_ptr(ids), batch, seq, ngram_size, heads_per_ngram, int(eos), int(fill),
+                            _ptr(mult), _ptr(mods), _ptr(offs), _ptr(rows))
+    if rc != 0:
+        raise ValueError("oracle_mt_hash rejected the configuration")
+    return rows
+
+
+def gather_mt(table, rows, row_begin=0):
+    lib = load_mt()
+    table = np.ascontiguousarray(table)
+    rows_flat = np.ascontiguousarray(rows, dtype=np.int64).reshape(-1)
+    num_rows, dim = table.shape
+    esize, _ = _elem(table)
+    out = np.empty((rows_flat.size, dim), dtype=table.dtype)
+    bad = lib.oracle_mt_gather(_ptr(table), esize, dim, int(row_begin), num_rows, _ptr(rows_flat), rows_flat.size,
+                               _ptr(out))
+    return out.reshape(tuple(np.shape(rows)) + (dim,)), int(bad)
+
+
+def scatter_add_compact_mt(rows, dy, num_rows, row_begin=0):
+    lib = load_mt()
+    rows_flat = np.ascontiguousarray(rows, dtype=np.int64).reshape(-1)
+    n = rows_flat.size
+    dy = np.ascontiguousarray(dy)
+    dy = dy.reshape(n, dy.shape[-1])
+    dim = dy.shape[1]
+    _, is_bf16 = _elem(dy)
+    uniq_rows = np.empty(max(n, 1), dtype=np.int64)
+    uniq_grad = np.empty((max(n, 1), dim), dtype=np.float64)
+    nu = np.zeros(1, dtype=np.int64)
+    bad = lib.oracle_mt_scatter_add_compact(_ptr(rows_flat), n, _ptr(dy), is_bf16, dim, int(row_begin), num_rows,
+                                            _ptr(uniq_rows), _ptr(uniq_grad), _ptr(nu))
     u = int(nu[0])
     return uniq_rows[:u].copy(), uniq_grad[:u].copy(), int(bad)
