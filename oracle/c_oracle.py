@@ -15,9 +15,12 @@ import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "engram_oracle.c")
-_LIB = os.path.join(_HERE, "libengram_oracle.so")
 _SRC_MT = os.path.join(_HERE, "engram_oracle_mt.c")
-_LIB_MT = os.path.join(_HERE, "libengram_oracle_mt.so")
+# ENGRAM_ORACLE_LIBDIR points at another build of the two libraries (the
+# sanitizer test builds them with AddressSanitizer and UBSan there).
+_LIBDIR = os.environ.get("ENGRAM_ORACLE_LIBDIR", _HERE)
+_LIB = os.path.join(_LIBDIR, "libengram_oracle.so")
+_LIB_MT = os.path.join(_LIBDIR, "libengram_oracle_mt.so")
 _lib = None
 _lib_mt = None
 

@@ -10,6 +10,13 @@ if ROOT not in sys.path:
 
 def pytest_configure(config):
     config.addinivalue_line("markers", "gpu: needs an MI355X (gfx950) GPU and the built HIP library")
+    # The sanitizer test runs CPU tests against a host-only build of libengram
+    # made with AddressSanitizer and UBSan (tests/test_host_sanitizers.py).
+    lib = os.environ.get("ENGRAM_TEST_LIB")
+    if lib:
+        from hashed_gram_embedding_engram_amd import engram as B
+        B.LIB_PATH = lib
+        B.load_library.__defaults__ = (lib,)
 
 
 def read_golden(name):
