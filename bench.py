@@ -51,6 +51,14 @@ PROFILES = os.path.join(ROOT, "profiles")
 CSRC = os.path.join(ROOT, "hashed_gram_embedding_engram_amd", "csrc")
 
 
+def log(msg):
+    """A progress line on stderr (the JSON result is the only line on stdout)."""
+    print("[bench %7.1fs] %s" % (time.perf_counter() - _T0, msg), file=sys.stderr, flush=True)
+
+
+_T0 = time.perf_counter()
+
+
 def parse_args():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -316,7 +324,9 @@ def cpu_baseline(wl, target_seconds=10.0, mt_seconds=5.0):
         mods, offs = C.head_vocab_sizes(), C.head_offsets()
     if any(b["tokens"] is None for b in wl["batches"]):
         return None
+    log("cpu baseline: host copy of the table")
     full = host_table(wl)
+    log("cpu baseline: %s" % ("whole table on the host" if full is not None else "distinct rows only"))
     prep = []
     for b in wl["batches"]:
         ids = b["ids"]
@@ -358,7 +368,9 @@ def cpu_baseline(wl, target_seconds=10.0, mt_seconds=5.0):
         return lookups, passes, secs
 
     l1, p1, s1 = run(False, target_seconds)
+    log("cpu baseline: single-threaded oracle done")
     lm, pm, sm = run(True, mt_seconds)
+    log("cpu baseline: OpenMP oracle done")
     threads = c_oracle.mt_threads()
     what = "hash, gather, compact scatter-add" if prep[0][3] is not None else "hash, gather"
     table_note = ("a host copy of the whole %d-row table" % wl["table_rows"] if full is not None else
@@ -741,8 +753,10 @@ def main():
     if args.workload == "route":
         route_main(args, dev)
         return
+    log("building the %s workload" % args.workload)
     wl = build_workload(args.workload, args.rotations, dev)
     torch.cuda.synchronize()
+    log("workload resident")
 
     R = len(wl["batches"])
     for i in range(args.warmup):
@@ -766,6 +780,7 @@ def main():
     torch.cuda.synchronize()
     t1 = time.perf_counter()
 
+    log("timed steps done")
     lookups = sum(wl["batches"][i % R]["n"] for i in range(args.steps))
     elapsed = t1 - t0
     dom_ms = [e[dom_span[0]].elapsed_time(e[dom_span[1]]) for e in tevs if e]

@@ -40,19 +40,18 @@ __device__ __forceinline__ void report_bad(int64_t* status, int64_t idx) {
 
 // ROW32: the shard has fewer than 2^32 - 1 rows, so a local row id (or the
 // out-of-range marker 0xFFFFFFFF) fits one 32-bit shuffle.
+// At most four of these waves share a SIMD: amdgpu_waves_per_eu's upper bound
+// makes the compiler reserve the registers of a four-wave occupancy (128
+// VGPRs; the body needs about 34).  Sixteen waves per compute unit, each with
+// PER_LANE 16-byte loads per lane in flight, already cover HBM latency; with
+// fewer of them resident the gather alone runs faster (less cache thrashing),
+// and a plan running beside it on another stream finds room to run.
 template <int CPR, int G, bool ROW32>
-__global__ __launch_bounds__(256) void gather_rows_kernel(const u32x4* __restrict__ table, int64_t row_begin,
-                                                          uint64_t num_rows, const int64_t* __restrict__ rows,
-                                                          int64_t n, u32x4* __restrict__ out,
-                                                          int64_t* __restrict__ status) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 4))) void gather_rows_kernel(
+    const u32x4* __restrict__ table, int64_t row_begin, uint64_t num_rows, const int64_t* __restrict__ rows,
+    int64_t n, u32x4* __restrict__ out, int64_t* __restrict__ status) {
     constexpr int PER_LANE = CPR * G / 64;
     static_assert(CPR * G % 64 == 0 && G <= 64, "wave tile must be whole dwordx4 per lane");
-    // Claim 128 VGPRs (the body needs about 34) so that at most four of these
-    // waves share a SIMD.  Sixteen waves per compute unit, each with PER_LANE
-    // 16-byte loads per lane in flight, already cover HBM latency; with fewer
-    // of them resident the gather alone runs faster (less cache thrashing),
-    // and a plan running beside it on another stream finds room to run.
-    asm volatile("" ::: "v127");
     const int lane = threadIdx.x & 63;
     const int64_t wave = (int64_t)blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6);
     const int64_t n0 = wave * G;
