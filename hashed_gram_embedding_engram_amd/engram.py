@@ -100,6 +100,8 @@ def load_library(path=LIB_PATH):
     lib.engram_scatter_add_plan.argtypes = [p, i64, i64, i64, i32, p, p, p, sz, p, p]
     lib.engram_scatter_add_apply.restype = ctypes.c_int
     lib.engram_scatter_add_apply.argtypes = [p, i32, i32, i64, i64, i64, p, p, p, sz, p]
+    lib.engram_scatter_add_noalloc.restype = ctypes.c_int
+    lib.engram_scatter_add_noalloc.argtypes = [p, i64, p, i32, i32, i64, i64, p, p, p, p, p, p]
     lib.engram_strerror.restype = ctypes.c_char_p
     lib.engram_strerror.argtypes = [ctypes.c_int]
     _lib = lib
@@ -260,6 +262,32 @@ def engram_scatter_add(rows, grad_out, num_rows, row_begin=0, grad_dense=None, c
         u = int(nu.item())
         return ur[:u], ug[:u]
     return ur, ug, nu
+
+
+NOALLOC_SCRATCH_BYTES = 64 << 20
+
+
+def engram_scatter_add_noalloc(rows, grad_out, num_rows, row_begin=0, grad_dense=None, compact=None, status=None,
+                               stream=None):
+    """engram_scatter_add on the library's fixed scratch array: allocates nothing.
+    Exactly one output form: ``grad_dense`` fp32 [num_rows, dim] (updated in place),
+    or ``compact=(uniq_rows [>= n], uniq_grad [>= n, dim], num_uniq [])``; both are
+    returned as given.  Raises EngramError when n lookups need more than the 64 MiB
+    scratch.  Calls that overlap on one GPU race."""
+    lib = load_library()
+    dim = grad_out.shape[-1]
+    n = rows.numel()
+    if grad_out.numel() != n * dim:
+        raise ValueError("grad_out must hold one row per lookup")
+    ur, ug, nu = compact if compact is not None else (None, None, None)
+    _check(lib.engram_scatter_add_noalloc(_dev_ptr(rows, "rows", torch.int64), n, _dev_ptr(grad_out, "grad_out"),
+                                          _dtype_code(grad_out), dim, row_begin, num_rows,
+                                          _dev_ptr(grad_dense, "grad_dense", torch.float32, shape=(num_rows, dim)),
+                                          _dev_ptr(ur, "uniq_rows", torch.int64, min_numel=n),
+                                          _dev_ptr(ug, "uniq_grad", torch.float32, min_numel=n * dim),
+                                          _dev_ptr(nu, "num_uniq", torch.int64, numel=1), _status_ptr(status),
+                                          _stream_handle(stream)), "engram_scatter_add_noalloc")
+    return grad_dense if grad_dense is not None else compact
 
 
 def engram_scatter_add_plan(rows, num_rows, dim, row_begin=0, workspace=None, uniq_rows=None, num_uniq=None,

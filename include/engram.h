@@ -160,6 +160,24 @@ int engram_scatter_add(const int64_t* rows, int64_t n, const void* grad_out, int
                        float* uniq_grad, int64_t* num_uniq, void* workspace, size_t workspace_bytes,
                        int64_t* status, hipStream_t stream);
 
+/* For callers that cannot allocate device memory (code under HIP graph capture,
+ * tight serving loops, harnesses that forbid hipMalloc): engram_scatter_add with
+ * its workspace taken from a fixed device array inside the library, of
+ * ENGRAM_NOALLOC_SCRATCH_BYTES (64 MiB) on each GPU it runs on, held until the
+ * process ends.  The call allocates nothing.  Arguments, output forms, limits
+ * and results are those of engram_scatter_add; sizes whose workspace
+ * (engram_scatter_add_workspace) exceeds the array return ENGRAM_EWORKSPACE
+ * before anything is enqueued: at dim 160, up to about 1.18 M lookups.  Every
+ * call on one GPU shares that GPU's array, so calls that overlap on one GPU
+ * (other streams, other host threads) race and give undefined results;
+ * calls ordered on one stream are safe, each starting from scratch contents
+ * it initialises itself.  Returns ENGRAM_ELAUNCH when the array's device
+ * address cannot be obtained. */
+#define ENGRAM_NOALLOC_SCRATCH_BYTES (64u << 20)
+int engram_scatter_add_noalloc(const int64_t* rows, int64_t n, const void* grad_out, int32_t dtype, int32_t dim,
+                               int64_t row_begin, int64_t num_rows, float* grad_dense, int64_t* uniq_rows,
+                               float* uniq_grad, int64_t* num_uniq, int64_t* status, hipStream_t stream);
+
 /* The two phases of engram_scatter_add, for callers that reuse one set of row ids
  * (several gradients over the same lookups) or time the phases apart.
  *

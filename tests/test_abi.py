@@ -311,3 +311,15 @@ def test_missing_library_fails_loudly(monkeypatch):
         E.engram_hash(torch.zeros((1, 8), dtype=torch.int64), E.qwen3_8_flash_next_spec())
     with pytest.raises(RuntimeError, match="libengram.so not found"):
         E.engram_scatter_add(rows, torch.zeros((3, 160), dtype=torch.bfloat16), 4)
+
+
+def test_noalloc_refuses_sizes_past_its_scratch(lib):
+    """The no-allocation scatter-add refuses lookup counts whose workspace exceeds its
+    fixed scratch before it looks up the scratch or touches a device."""
+    fake = ctypes.c_void_p(0x10000)
+    n = 1_300_000
+    assert lib.engram_scatter_add_workspace(n, 1000, 160) > B.NOALLOC_SCRATCH_BYTES
+    assert lib.engram_scatter_add_noalloc(fake, n, fake, B.ENGRAM_BF16, 160, 0, 1000, fake, None, None, None, None,
+                                          None) == B.ENGRAM_EWORKSPACE
+    text = open(os.path.join(ROOT, "include", "engram.h")).read()
+    assert "#define ENGRAM_NOALLOC_SCRATCH_BYTES (64u << 20)" in text and B.NOALLOC_SCRATCH_BYTES == 64 << 20
