@@ -71,6 +71,9 @@ def parse_args():
                     help="run one plain 1 GiB device copy first (reference for HBM byte counters)")
     ap.add_argument("--no-alone", action="store_true",
                     help="skip the phases-one-at-a-time launches after the timed steps (profiler runs)")
+    ap.add_argument("--no-ceilings", action="store_true", help="skip the HBM ceiling probes")
+    ap.add_argument("--no-extra-configs", action="store_true",
+                    help="long workload: skip the full-table SFT forward and owner-shard lines after the headline")
     return ap.parse_args()
 
 
@@ -116,7 +119,7 @@ def counter_traffic(kernel_file, summary_name, launches_per_step=1):
         return None
 
 
-def build_workload(name, rotations, dev):
+def build_workload(name, rotations, dev, table=None):
     import numpy as np
     import torch
 
@@ -133,8 +136,9 @@ def build_workload(name, rotations, dev):
         spec = E.make_hash_spec(3, 8, ws["eos"], E.QWEN3_8_FLASH_NEXT_LAYER_MULTIPLIERS, ws["vocab_sizes"],
                                 ws["offsets"])
         table_rows, row_begin = ws["num_rows"], 0
-    table = torch.empty((table_rows, W.DIM), dtype=torch.bfloat16, device=dev)
-    W.fill_normal_(table, seed=1234)
+    if table is None or tuple(table.shape) != (table_rows, W.DIM):
+        table = torch.empty((table_rows, W.DIM), dtype=torch.bfloat16, device=dev)
+        W.fill_normal_(table, seed=1234)
 
     batches = []
     for r in range(rotations):
@@ -727,34 +731,16 @@ def route_main(args, dev):
     print(json.dumps(result), flush=True)
 
 
-def main():
-    args = parse_args()
-    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU: the Engram path here is built and timed on a single MI355X; "
-              "--gpus %d is not supported" % args.gpus, file=sys.stderr)
-        sys.exit(2)
+def lookup_line(name, args, dev, table=None):
+    """Warm-up, timed steps, phase breakdown and phases one at a time of one
+    lookup workload; returns (the JSON line's dict without the CPU baseline,
+    the workload)."""
     import torch
 
-    import hashed_gram_embedding_engram_amd as E
     import workloads as W
 
-    E.load_library()
-    dev = torch.device("cuda:0")
-    torch.cuda.set_device(dev)
-    if args.calibrate_copy:
-        src = torch.empty(1 << 29, dtype=torch.int16, device=dev).fill_(1)   # 1 GiB
-        dst = torch.empty_like(src)
-        dst.copy_(src)
-        torch.cuda.synchronize()
-        del src, dst
-    if args.workload == "ple":
-        ple_main(args, dev)
-        return
-    if args.workload == "route":
-        route_main(args, dev)
-        return
-    log("building the %s workload" % args.workload)
-    wl = build_workload(args.workload, args.rotations, dev)
+    log("building the %s workload" % name)
+    wl = build_workload(name, args.rotations, dev, table=table)
     torch.cuda.synchronize()
     log("workload resident")
 
@@ -828,21 +814,20 @@ def main():
                                  "segment_reduce_kernel<20,bf16> + carry_fixup_kernel + long_run_kernel", "scatter.hip")
     dbytes, dms, dname, dsrc = kern[dom]
     achieved = dbytes / (dms / 1e3) / 1e9
-    traffic = counter_traffic(dsrc, "%s_%s_counters.txt" % (dom, args.workload))
+    traffic = counter_traffic(dsrc, "%s_%s_counters.txt" % (dom, name))
 
     # Three GB/s figures per kernel: per-lookup bytes (above); compulsory
     # bytes, which count each distinct table row's read once (the gather reads
     # (U/L) * 320 + 328 B per lookup); and the HBM bytes the committed
     # rocprofv3 counters measured for that kernel (null when they were taken
     # on other kernel sources).
-    import torch as _t
-    u_fwd = int(_t.unique(b0["rows"].reshape(-1)).numel())
+    u_fwd = int(torch.unique(b0["rows"].reshape(-1)).numel())
     compulsory = {"gather": 320.0 * u_fwd + 328.0 * n_avg}
     if wl["backward"]:
         compulsory["scatter_apply"] = apply_bytes   # every gradient row is read once already
     gbps = {}
     for k, (byts, ms, _, src) in kern.items():
-        hbm = counter_traffic(src, "%s_%s_counters.txt" % (k, args.workload))
+        hbm = counter_traffic(src, "%s_%s_counters.txt" % (k, name))
         gbps[k] = {"per_lookup": round(byts / (ms / 1e3) / 1e9, 1),
                    "compulsory": round(compulsory[k] / (ms / 1e3) / 1e9, 1),
                    "counters": None if hbm is None else round(hbm / (ms / 1e3) / 1e9, 1)}
@@ -865,10 +850,7 @@ def main():
         "dtype": "bf16",
         "data": "synthetic",
         "config": {
-            "workload": {"long": "long-context packed THD stream, full table, fwd+bwd (compact grad)",
-                         "full-sft": "SFT batch 8x4096, full table, fwd",
-                         "owner": "owner shard 1/64 of a world-64 step, fwd+bwd (dense grad)",
-                         "sft": "SFT batch 8x4096, 10M-row table, fwd"}[args.workload],
+            "workload": WORKLOAD_NAMES[name],
             "tokens": int(b0["ids"].size), "lookups_per_step": int(n_avg), "table_rows": wl["table_rows"],
             "dim": W.DIM, "table_dtype": "bf16", "grad_dtype": "bf16" if wl["backward"] else None,
             "distinct_rows_rotation0": U, "rotations": R,
@@ -893,14 +875,101 @@ def main():
     if alone:
         ga = alone["gather"]
         result["gather_alone"] = {"gbps_algorithmic": round(gather_bytes / (ga / 1e3) / 1e9, 1),
-                                  "frac": round(gather_bytes / (ga / 1e3) / 1e9 / HBM_PEAK_GBPS, 4)}
+                                  "gbps_compulsory": round(compulsory["gather"] / (ga / 1e3) / 1e9, 1),
+                                  "frac": round(gather_bytes / (ga / 1e3) / 1e9 / HBM_PEAK_GBPS, 4),
+                                  "frac_compulsory": round(compulsory["gather"] / (ga / 1e3) / 1e9 / HBM_PEAK_GBPS, 4)}
     if alone and wl["backward"]:
         bs = alone["scatter_plan"] + alone["scatter_apply"]
         result["backward_plan_then_apply"] = {"ms": round(bs, 4),
                                               "gbps_algorithmic": round(apply_bytes / (bs / 1e3) / 1e9, 1),
                                               "frac": round(apply_bytes / (bs / 1e3) / 1e9 / HBM_PEAK_GBPS, 4)}
+    return result, wl
+
+
+WORKLOAD_NAMES = {"long": "long-context packed THD stream, full table, fwd+bwd (compact grad)",
+                  "full-sft": "SFT batch 8x4096, full table, fwd",
+                  "owner": "owner shard 1/64 of a world-64 step, fwd+bwd (dense grad)",
+                  "sft": "SFT batch 8x4096, 10M-row table, fwd"}
+
+# The ceiling a kernel's traffic is compared with: the probe with the same
+# mix and access distribution.  The backward's sums read a random permutation
+# of the gradient rows, as row_expand does; the gather's Zipf-skewed rows hit
+# in cache more often than row_gather's uniform ones, so it has no such probe.
+CEILING_OF = {"scatter_apply": "row_expand"}
+
+# Fields of the other configurations' lines kept in the default line.
+EXTRA_KEYS = ("value", "unit", "ms_per_step", "config", "phases_ms", "roofline", "phase_gbps", "gather_alone",
+              "backward_plan_then_apply", "phases_alone_ms_p50", "distinct_rows_forward_rotation0")
+
+
+def add_ceiling_fracs(result, ceilings):
+    """The dominant kernel's achieved rate against the probe with its traffic mix."""
+    if not ceilings:
+        return
+    dom = "scatter_apply" if "scatter_apply" in result["phase_gbps"] else "gather"
+    c = ceilings.get(CEILING_OF.get(dom))
+    if c:
+        result["roofline"]["measured_ceiling"] = {"probe": CEILING_OF[dom], "gbps": c,
+                                                  "frac": round(result["roofline"]["achieved"] / c, 4)}
+
+
+def main():
+    args = parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: the Engram path here is built and timed on a single MI355X; "
+              "--gpus %d is not supported" % args.gpus, file=sys.stderr)
+        sys.exit(2)
+    import torch
+
+    import hashed_gram_embedding_engram_amd as E
+
+    E.load_library()
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    if args.calibrate_copy:
+        src = torch.empty(1 << 29, dtype=torch.int16, device=dev).fill_(1)   # 1 GiB
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+    if args.workload == "ple":
+        ple_main(args, dev)
+        return
+    if args.workload == "route":
+        route_main(args, dev)
+        return
+    ceilings = None
+    if not args.no_ceilings:
+        from hashed_gram_embedding_engram_amd import probe
+        log("HBM ceilings")
+        ceilings = probe.measure_ceilings(dev)
+    result, wl = lookup_line(args.workload, args, dev)
+    if ceilings:
+        result["ceilings_gbps"] = ceilings
+        result["ceilings_from"] = ("libengram_probe.so: streaming 16-byte reads and writes of 4 GiB; row_gather "
+                                   "reads 4,194,304 uniform-random 320-B rows of a 25 M-row bf16 table and writes "
+                                   "them in order; row_expand reads 3,163,052 distinct random 320-B bf16 rows and "
+                                   "writes them as 640-B fp32 rows; GB/s = bytes moved / median of 10 launches")
+        add_ceiling_fracs(result, ceilings)
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(wl)
+    if args.workload == "long" and not args.no_extra_configs:
+        # The other full-table and owner-shard configurations, measured after
+        # the headline in the same run: the SFT batch's forward against the
+        # same 102.4 GB table, then the owner shard's forward and dense backward.
+        table = wl["table"]
+        del wl
+        extra = {}
+        line, wl = lookup_line("full-sft", args, dev, table=table)
+        add_ceiling_fracs(line, ceilings)
+        extra["full_table_sft_forward"] = {k: line[k] for k in EXTRA_KEYS if k in line}
+        del wl, table
+        torch.cuda.empty_cache()
+        line, wl = lookup_line("owner", args, dev)
+        add_ceiling_fracs(line, ceilings)
+        extra["owner_shard_step"] = {k: line[k] for k in EXTRA_KEYS if k in line}
+        del wl
+        result["other_configs"] = extra
     print(json.dumps(result), flush=True)
 
 

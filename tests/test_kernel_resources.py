@@ -34,7 +34,7 @@ def resource_report(src):
 
 @pytest.mark.skipif(not os.path.exists(B.HIPCC), reason="hipcc is missing")
 def test_no_kernel_uses_scratch():
-    srcs = [s for s in B.SOURCES if s.endswith(".hip")]
+    srcs = [s for s in B.SOURCES + B.PROBE_SOURCES if s.endswith(".hip")]
     with ThreadPoolExecutor(max_workers=min(8, len(srcs))) as ex:
         reports = list(ex.map(resource_report, srcs))
     seen = 0
