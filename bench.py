@@ -913,7 +913,130 @@ def add_ceiling_fracs(result, ceilings):
                                                   "frac": round(result["roofline"]["achieved"] / c, 4)}
 
 
+# ---------------------------------------------------------------- profile summaries
+
+# Kernels of each phase of a lookup workload, as rocprofv3 names them.
+PHASE_KERNELS = {
+    "hash": ["hash_kernel"],
+    "gather": ["gather_rows_kernel"],
+    "scatter_plan": ["scatter_init_kernel", "keys_kernel", "upsweep_kernel", "downsweep_kernel", "run_count_kernel",
+                     "block_scan_kernel", "uniq_rows_kernel"],
+    "scatter_apply": ["segment_reduce_kernel", "carry_fixup_kernel", "long_run_kernel"],
+}
+PHASE_SOURCE = {"hash": "hash.hip", "gather": "gather.hip", "scatter_plan": "scatter.hip",
+                "scatter_apply": "scatter.hip"}
+PROFILE_FLAGS = "--steps 5 --warmup 2 --no-cpu-baseline --no-alone --no-ceilings --no-extra-configs --calibrate-copy"
+TRACE_FILE = {"long": "kernel_trace_long_context.md", "full-sft": "kernel_trace_full_sft.md",
+              "owner": "kernel_trace_owner.md"}
+
+
+def profile_commands(name):
+    """The three rocprofv3 runs behind a workload's summaries (REPO = repository root)."""
+    pre = "cd /tmp && export TMPDIR=/tmp && "
+    run = "-- python3 $REPO/bench.py --workload %s %s" % (name, PROFILE_FLAGS)
+    regex = "|".join(k for ks in PHASE_KERNELS.values() for k in ks) + "|copyBuffer"
+    out = "$REPO/gpurun_out/prof/%s" % name
+    return {
+        "trace": pre + "timeout -k 10 300 rocprofv3 --kernel-trace --stats -f csv -d %s_kt -o kt %s > %s_line.json"
+                       % (out, run, out),
+        "fetch": pre + 'timeout -s KILL 300 rocprofv3 --pmc FETCH_SIZE -f csv --kernel-include-regex "%s" -d %s_fetch '
+                       "-o f %s" % (regex, out, run),
+        "write": pre + 'timeout -s KILL 300 rocprofv3 --pmc WRITE_SIZE -f csv --kernel-include-regex "%s" -d %s_write '
+                       "-o w %s" % (regex, out, run),
+    }
+
+
+def _short_kernel(name):
+    """A kernel's name without its argument list and anonymous namespaces."""
+    name = name.replace("(anonymous namespace)::", "")
+    if name.startswith("void "):
+        name = name[5:]
+    return name.split("(")[0]
+
+
+def summarize_profiles(name, raw):
+    """Write profiles/<trace file> and <phase>_<workload>_counters.txt from the
+    rocprofv3 output of profile_commands(name) under `raw`."""
+    import csv
+    cmds = profile_commands(name)
+    line = json.loads(open(os.path.join(raw, "%s_line.json" % name)).read().strip().splitlines()[-1])
+    n = line["config"]["lookups_per_step"]
+    stats = list(csv.DictReader(open(os.path.join(raw, "%s_kt" % name, "kt_kernel_stats.csv"))))
+    avg_us = {_short_kernel(r["Name"]): float(r["AverageNs"]) / 1e3 for r in stats}
+    calls = {_short_kernel(r["Name"]): int(r["Calls"]) for r in stats}
+
+    def counters(kind, cname):
+        per = {}
+        for r in csv.DictReader(open(os.path.join(raw, "%s_%s" % (name, kind), "%s_counter_collection.csv" % kind[0]))):
+            if r["Counter_Name"] == cname:
+                per.setdefault(_short_kernel(r["Kernel_Name"]), []).append(float(r["Counter_Value"]))
+        # the 1 GiB calibration copy is the largest device copy of the run
+        calib = max(v for k, vs in per.items() if "copyBuffer" in k for v in vs)
+        return {k: sum(v) / len(v) for k, v in per.items()}, {k: len(v) for k, v in per.items()}, calib
+    fetch, nf, f_copy = counters("fetch", "FETCH_SIZE")
+    write, _, w_copy = counters("write", "WRITE_SIZE")
+    f_scale, w_scale = 1048576.0 / f_copy, 1048576.0 / w_copy
+    # trace summary
+    lines = ["# Kernel trace: %s, one MI355X" % WORKLOAD_NAMES[name], "",
+             "Command (REPO = repository root on the MI355X machine):", "", "    " + cmds["trace"], "",
+             "Workload: %s; %d (token x head) lookups per step; 2 warm-up steps, 5 timed steps, then 5 steps with "
+             "events around every phase; 4 rotating input sets.  In the step the plan (sort) runs on a second "
+             "stream beside the gather, so the two share HBM." % (WORKLOAD_NAMES[name], n), "",
+             "Step from the same run: %.4f ms (%.3e lookups/s); phases (ms): %s." % (
+                 line["ms_per_step"], line["value"], ", ".join("%s %.4f" % kv for kv in line["phases_ms"].items())),
+             "", "| kernel | calls | avg us | phase |", "|---|---:|---:|---|"]
+    for k in sorted(avg_us, key=lambda k: -avg_us[k] * calls[k]):
+        phase = next((p for p, ks in PHASE_KERNELS.items() if any(x in k for x in ks)), "setup")
+        lines.append("| `%s` | %d | %.1f | %s |" % (k, calls[k], avg_us[k], phase))
+    lines += ["", "Setup kernels of the benchmark (table fill, gradient generation, the distinct-row count) are "
+                  "listed as setup."]
+    with open(os.path.join(PROFILES, TRACE_FILE[name]), "w") as f:
+        f.write("\n".join(lines) + "\n")
+    # counter summaries of the phases whose algorithmic bytes the line states
+    alg = {"gather": 648.0 * n}
+    # compulsory bytes read each distinct table row once (rotation 0's count)
+    comp = {"gather": 320.0 * line["distinct_rows_forward_rotation0"] + 328.0 * n}
+    if "scatter_apply" in line["phase_gbps"]:
+        alg["scatter_apply"] = comp["scatter_apply"] = line["roofline"]["algorithmic_bytes_per_launch"]
+    for phase, alg_bytes in alg.items():
+        ks = [k for k in fetch if any(x in k for x in PHASE_KERNELS[phase])]
+        fb = sum(fetch[k] for k in ks) * 1024 * f_scale
+        wb = sum(write.get(k, 0.0) for k in ks) * 1024 * w_scale
+        t_us = sum(avg_us.get(k, 0.0) for k in ks)
+        out = ["# HBM traffic of one launch of the %s phase, %s (%d lookups per step), MI355X, rocprofv3 counters."
+               % (phase, WORKLOAD_NAMES[name], n),
+               "# Commands (REPO = repository root on the MI355X machine):", "#   " + cmds["fetch"],
+               "#   " + cmds["write"], "#   " + cmds["trace"],
+               "# Counters are KiB per dispatch, averaged over the dispatches of each kernel (%s)."
+               % ", ".join("%d" % nf[k] for k in ks),
+               "# Scale: the 1 GiB device copy that --calibrate-copy runs first reads FETCH_SIZE %.0f KiB and "
+               "WRITE_SIZE %.0f KiB" % (f_copy, w_copy),
+               "#   for 1,048,576 KiB each way, so FETCH_SIZE is scaled x%.3f and WRITE_SIZE x%.3f." % (f_scale, w_scale),
+               "# Kernels of one launch:"]
+        for k in ks:
+            out.append("#   %-55s FETCH %11.1f KiB  WRITE %11.1f KiB  avg %8.1f us" % (
+                k, fetch[k], write.get(k, 0.0), avg_us.get(k, 0.0)))
+        out += ["# Algorithmic bytes per launch: %.0f; compulsory bytes (each distinct table row moved once): %.0f"
+                % (alg_bytes, comp[phase]),
+                "# Average kernel time per launch (kernel-trace run): %.1f us" % t_us,
+                "# source_sha256_16: SHA-256 prefix of the kernel source and the local headers it includes",
+                "source_sha256_16 %s" % source_sha(PHASE_SOURCE[phase]),
+                "fetch_bytes_per_launch %.0f" % fb, "write_bytes_per_launch %.0f" % wb,
+                "hbm_bytes_per_launch %.0f" % (fb + wb), "algorithmic_bytes_per_launch %.0f" % alg_bytes,
+                "compulsory_bytes_per_launch %.0f" % comp[phase],
+                "kernel_time_us_per_launch %.1f" % t_us]
+        with open(os.path.join(PROFILES, "%s_%s_counters.txt" % (phase, name)), "w") as f:
+            f.write("\n".join(out) + "\n")
+
+
 def main():
+    if len(sys.argv) >= 2 and sys.argv[1] == "--profile-commands":
+        for c in profile_commands(sys.argv[2]).values():
+            print(c)
+        return
+    if len(sys.argv) >= 2 and sys.argv[1] == "--summarize-profiles":
+        summarize_profiles(sys.argv[2], sys.argv[3] if len(sys.argv) > 3 else os.path.join(ROOT, "gpurun_out", "prof"))
+        return
     args = parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: the Engram path here is built and timed on a single MI355X; "

@@ -15,6 +15,9 @@ import bench  # noqa: E402
 SUMMARIES = {
     "scatter_apply_long_counters.txt": "scatter.hip",
     "gather_long_counters.txt": "gather.hip",
+    "gather_full-sft_counters.txt": "gather.hip",
+    "gather_owner_counters.txt": "gather.hip",
+    "scatter_apply_owner_counters.txt": "scatter.hip",
     "conv_fwd_ple_counters.txt": "ple.hip",
     "conv_bwd_ple_counters.txt": "ple.hip",
     "norm_fwd_ple_counters.txt": "ple.hip",
@@ -44,8 +47,9 @@ def fields(path):
 def test_committed_summaries_are_current_and_plausible(name):
     """Every counter summary names the kernel source it was taken on.  A summary
     taken on another source is never used (the bench line's traffic is null
-    for it).  A current one's measured HBM bytes are at least the algorithmic
-    bytes less 5% (a summary below that would mean a counter or scale slip)."""
+    for it).  A current one's measured HBM bytes are at least the compulsory
+    bytes (each distinct row moved once; for kernels without row reuse, the
+    algorithmic bytes) less 5%: below that would mean a counter or scale slip."""
     path = os.path.join(bench.PROFILES, name)
     f = fields(path)
     text = open(path).read()
@@ -56,7 +60,9 @@ def test_committed_summaries_are_current_and_plausible(name):
     hbm = float(f["hbm_bytes_per_launch"])
     alg = float(f["algorithmic_bytes_per_launch"])
     assert hbm == pytest.approx(float(f["fetch_bytes_per_launch"]) + float(f["write_bytes_per_launch"]), abs=2)  # each printed rounded
-    assert hbm >= 0.95 * alg
+    comp = float(f.get("compulsory_bytes_per_launch", alg))
+    assert comp <= alg
+    assert hbm >= 0.95 * comp
     assert hbm <= 2.0 * alg
     assert bench.counter_traffic(SUMMARIES[name], name) == pytest.approx(hbm)
 
@@ -75,7 +81,8 @@ def test_counter_traffic_refuses_other_sources(tmp_path, monkeypatch):
 
 
 def test_kernel_trace_summaries_name_their_command():
-    for name in ("kernel_trace_long_context.md", "kernel_trace_ple.md", "kernel_trace_route.md"):
+    for name in ("kernel_trace_long_context.md", "kernel_trace_full_sft.md", "kernel_trace_owner.md",
+                 "kernel_trace_ple.md", "kernel_trace_route.md"):
         text = open(os.path.join(bench.PROFILES, name)).read()
         assert re.search(r"rocprofv3 --kernel-trace --stats .* -- python3 \$REPO/bench.py", text), name
 
