@@ -37,6 +37,7 @@ import argparse
 import hashlib
 import json
 import os
+import re
 import sys
 import time
 
@@ -563,6 +564,7 @@ def ple_main(args, dev):
                      "traffic": counter_traffic(kname[dom][1], "%s_ple_counters.txt" % dom),
                      "algorithmic_bytes_per_launch": alg[dom], "avg_launch_ms": phase[dom]},
         "phase_gbps_algorithmic": {k: round(alg[k] / (phase[k] / 1e3) / 1e9, 1) for k in names},
+        "phase_algorithmic_bytes": alg,
         "cpu_baseline": None,
     }
     if not args.no_cpu_baseline:
@@ -724,6 +726,7 @@ def route_main(args, dev):
                      "traffic": counter_traffic("route.hip", "%s_route_counters.txt" % dom),
                      "algorithmic_bytes_per_launch": alg[dom], "avg_launch_ms": phase[dom]},
         "phase_gbps_algorithmic": {k: round(alg[k] / (phase[k] / 1e3) / 1e9, 1) for k in names},
+        "phase_algorithmic_bytes": alg,
         "cpu_baseline": None,
     }
     if not args.no_cpu_baseline:
@@ -890,6 +893,7 @@ WORKLOAD_NAMES = {"long": "long-context packed THD stream, full table, fwd+bwd (
                   "full-sft": "SFT batch 8x4096, full table, fwd",
                   "owner": "owner shard 1/64 of a world-64 step, fwd+bwd (dense grad)",
                   "sft": "SFT batch 8x4096, 10M-row table, fwd"}
+LOOKUP_WORKLOADS = tuple(WORKLOAD_NAMES)
 
 # The ceiling a kernel's traffic is compared with: the probe with the same
 # mix and access distribution.  The backward's sums read a random permutation
@@ -915,26 +919,63 @@ def add_ceiling_fracs(result, ceilings):
 
 # ---------------------------------------------------------------- profile summaries
 
-# Kernels of each phase of a lookup workload, as rocprofv3 names them.
-PHASE_KERNELS = {
-    "hash": ["hash_kernel"],
-    "gather": ["gather_rows_kernel"],
-    "scatter_plan": ["scatter_init_kernel", "keys_kernel", "upsweep_kernel", "downsweep_kernel", "run_count_kernel",
-                     "block_scan_kernel", "uniq_rows_kernel"],
-    "scatter_apply": ["segment_reduce_kernel", "carry_fixup_kernel", "long_run_kernel"],
+# Kernels of each phase, as rocprofv3 names them (regular expressions over the
+# name without its argument list), and the source each phase's kernels are
+# built from.  A kernel that matches several phases of a workload (the column
+# sum shared by both PLE backwards) is charged to the phase of the dispatch
+# before it.
+LOOKUP_PHASES = {
+    "hash": ("hash.hip", [r"\bhash_kernel"]),
+    "gather": ("gather.hip", [r"\bgather_rows_kernel"]),
+    "scatter_plan": ("scatter.hip", [r"\bscatter_init_kernel", r"\bkeys_kernel", r"\bupsweep_kernel",
+                                     r"\bdownsweep_kernel", r"\brun_count_kernel", r"\bblock_scan_kernel",
+                                     r"\buniq_rows_kernel"]),
+    "scatter_apply": ("scatter.hip", [r"\bsegment_reduce_kernel", r"\bcarry_fixup_kernel", r"\blong_run_kernel"]),
 }
-PHASE_SOURCE = {"hash": "hash.hip", "gather": "gather.hip", "scatter_plan": "scatter.hip",
-                "scatter_apply": "scatter.hip"}
+PROFILED = {
+    "long": LOOKUP_PHASES, "full-sft": LOOKUP_PHASES, "owner": LOOKUP_PHASES,
+    "ple": {"conv_fwd": ("ple.hip", [r"\bshort_conv_fwd"]), "norm_fwd": ("ple.hip", [r"\brms_norm_fwd"]),
+            "norm_bwd": ("ple.hip", [r"\brms_norm_bwd", r"\bcolumn_sum_kernel"]),
+            "conv_bwd": ("ple.hip", [r"\bshort_conv_bwd", r"\bcolumn_sum_kernel"])},
+    "route": {"plan": ("route.hip", [r"\broute_init_kernel", r"\broute_keys_kernel", r"\bupsweep_kernel",
+                                     r"\bdownsweep_kernel", r"\broute_output_kernel"]),
+              "validate": ("route.hip", [r"\broute_validate_kernel"]),
+              "pack_ids": ("route.hip", [r"\bpack_kernel<unsigned int,"]),
+              "unpack_ids": ("route.hip", [r"\bunpack_kernel<unsigned int,"]),
+              "pack_values": ("route.hip", [r"\bpack_kernel<u32x4"]),
+              "unpack_values": ("route.hip", [r"\bunpack_kernel<u32x4"]),
+              "unpermute_values": ("route.hip", [r"\bpermute_kernel<u32x4"])},
+}
+# Phases whose counter summaries are written (the ones a bench line can name
+# as its dominant kernel).
+COUNTED = {"long": ["gather", "scatter_apply"], "full-sft": ["gather"], "owner": ["gather", "scatter_apply"],
+           "ple": ["conv_fwd", "norm_fwd", "norm_bwd", "conv_bwd"],
+           "route": ["pack_values", "unpack_values", "unpermute_values"]}
 PROFILE_FLAGS = "--steps 5 --warmup 2 --no-cpu-baseline --no-alone --no-ceilings --no-extra-configs --calibrate-copy"
 TRACE_FILE = {"long": "kernel_trace_long_context.md", "full-sft": "kernel_trace_full_sft.md",
-              "owner": "kernel_trace_owner.md"}
+              "owner": "kernel_trace_owner.md", "ple": "kernel_trace_ple.md", "route": "kernel_trace_route.md"}
+WORKLOAD_TEXT = {
+    "ple": "activations [8, 4,096, 10,240] bf16 (four 2,560-wide branches); per step the causal depthwise conv "
+           "(kernel 4, dilation 3, 9-token halo), the grouped RMSNorm (groups of 2,560), the norm backward and "
+           "the conv backward, each backward followed by a column sum of its weight-gradient partials",
+    "route": "one request rank of a world-64 owner group: 8 x 4,096 Zipf(1.2) tokens hashed into 524,288 "
+             "full-table row IDs; per step: group by owner (route keys, one radix digit pass, route output), "
+             "segment validation, pack of the IDs to the step's capacity, the owner's unpack, the owner's pack "
+             "of 320-B bf16 value rows, the requester's unpack and the unpermute to request order",
+}
 
 
 def profile_commands(name):
     """The three rocprofv3 runs behind a workload's summaries (REPO = repository root)."""
     pre = "cd /tmp && export TMPDIR=/tmp && "
     run = "-- python3 $REPO/bench.py --workload %s %s" % (name, PROFILE_FLAGS)
-    regex = "|".join(k for ks in PHASE_KERNELS.values() for k in ks) + "|copyBuffer"
+    pats = []
+    for _, ks in PROFILED[name].values():
+        for k in ks:
+            k = k.replace(r"\b", "").split("<")[0]
+            if k not in pats:
+                pats.append(k)
+    regex = "|".join(pats) + "|copyBuffer"
     out = "$REPO/gpurun_out/prof/%s" % name
     return {
         "trace": pre + "timeout -k 10 300 rocprofv3 --kernel-trace --stats -f csv -d %s_kt -o kt %s > %s_line.json"
@@ -947,84 +988,136 @@ def profile_commands(name):
 
 
 def _short_kernel(name):
-    """A kernel's name without its argument list and anonymous namespaces."""
-    name = name.replace("(anonymous namespace)::", "")
+    """A kernel's name without its argument list and anonymous namespaces,
+    with the 16-byte vector type spelled u32x4."""
+    name = name.replace("(anonymous namespace)::", "").replace("unsigned int __vector(4)", "u32x4")
     if name.startswith("void "):
         name = name[5:]
-    return name.split("(")[0]
+    depth = 0
+    for i, c in enumerate(name):   # the argument list opens outside every template bracket
+        depth += (c == "<") - (c == ">")
+        if c == "(" and depth == 0:
+            return name[:i]
+    return name
+
+
+def _phases_of(kernel, phases):
+    return [p for p, (_, ks) in phases.items() if any(re.search(x, kernel) for x in ks)]
+
+
+def _charge(dispatches, phases):
+    """[(kernel, value)] in dispatch order -> {phase: [value per launch]}: a
+    dispatch of a phase's first kernel starts a launch of that phase; a kernel
+    matching several phases goes to the phase of the dispatch before it."""
+    per, prev = {}, None
+    for kernel, value in dispatches:
+        ps = _phases_of(kernel, phases)
+        p = ps[0] if len(ps) == 1 else (prev if prev in ps else None)
+        prev = p
+        if p is None:
+            continue
+        if re.search(phases[p][1][0], kernel) or p not in per:
+            per.setdefault(p, []).append(0.0)
+        per[p][-1] += value
+    return per
 
 
 def summarize_profiles(name, raw):
     """Write profiles/<trace file> and <phase>_<workload>_counters.txt from the
     rocprofv3 output of profile_commands(name) under `raw`."""
     import csv
+    phases = PROFILED[name]
     cmds = profile_commands(name)
     line = json.loads(open(os.path.join(raw, "%s_line.json" % name)).read().strip().splitlines()[-1])
-    n = line["config"]["lookups_per_step"]
     stats = list(csv.DictReader(open(os.path.join(raw, "%s_kt" % name, "kt_kernel_stats.csv"))))
     avg_us = {_short_kernel(r["Name"]): float(r["AverageNs"]) / 1e3 for r in stats}
     calls = {_short_kernel(r["Name"]): int(r["Calls"]) for r in stats}
+    trace = sorted(csv.DictReader(open(os.path.join(raw, "%s_kt" % name, "kt_kernel_trace.csv"))),
+                   key=lambda r: int(r["Dispatch_Id"]))
+    t_us = _charge([(_short_kernel(r["Kernel_Name"]),
+                     (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3) for r in trace], phases)
 
     def counters(kind, cname):
-        per = {}
-        for r in csv.DictReader(open(os.path.join(raw, "%s_%s" % (name, kind), "%s_counter_collection.csv" % kind[0]))):
-            if r["Counter_Name"] == cname:
-                per.setdefault(_short_kernel(r["Kernel_Name"]), []).append(float(r["Counter_Value"]))
+        rows = [r for r in csv.DictReader(open(os.path.join(raw, "%s_%s" % (name, kind),
+                                                            "%s_counter_collection.csv" % kind[0])))
+                if r["Counter_Name"] == cname]
+        rows.sort(key=lambda r: int(r["Dispatch_Id"]))
+        disp = [(_short_kernel(r["Kernel_Name"]), float(r["Counter_Value"])) for r in rows]
+        per_kernel = {}
+        for k, v in disp:
+            per_kernel.setdefault(k, []).append(v)
         # the 1 GiB calibration copy is the largest device copy of the run
-        calib = max(v for k, vs in per.items() if "copyBuffer" in k for v in vs)
-        return {k: sum(v) / len(v) for k, v in per.items()}, {k: len(v) for k, v in per.items()}, calib
-    fetch, nf, f_copy = counters("fetch", "FETCH_SIZE")
-    write, _, w_copy = counters("write", "WRITE_SIZE")
+        calib = max(v for k, v in disp if "copyBuffer" in k)
+        return _charge(disp, phases), per_kernel, calib
+    fetch, fetch_k, f_copy = counters("fetch", "FETCH_SIZE")
+    write, write_k, w_copy = counters("write", "WRITE_SIZE")
     f_scale, w_scale = 1048576.0 / f_copy, 1048576.0 / w_copy
+    mean = lambda v: sum(v) / len(v)
+
     # trace summary
-    lines = ["# Kernel trace: %s, one MI355X" % WORKLOAD_NAMES[name], "",
+    if name in WORKLOAD_TEXT:
+        desc = "%s; 2 warm-up steps, 5 steps with events around every phase, then 5 timed steps, over 4 " \
+               "rotating input sets." % WORKLOAD_TEXT[name]
+    else:
+        desc = "%s; %d (token x head) lookups per step; 2 warm-up steps, 5 timed steps, then 5 steps with events " \
+               "around every phase; 4 rotating input sets.  In the step the plan (sort) runs on a second stream " \
+               "beside the gather, so the two share HBM." % (WORKLOAD_NAMES[name], line["config"]["lookups_per_step"])
+    title = WORKLOAD_NAMES.get(name) or line["config"]["workload"]
+    lines = ["# Kernel trace: %s, one MI355X" % title, "",
              "Command (REPO = repository root on the MI355X machine):", "", "    " + cmds["trace"], "",
-             "Workload: %s; %d (token x head) lookups per step; 2 warm-up steps, 5 timed steps, then 5 steps with "
-             "events around every phase; 4 rotating input sets.  In the step the plan (sort) runs on a second "
-             "stream beside the gather, so the two share HBM." % (WORKLOAD_NAMES[name], n), "",
-             "Step from the same run: %.4f ms (%.3e lookups/s); phases (ms): %s." % (
-                 line["ms_per_step"], line["value"], ", ".join("%s %.4f" % kv for kv in line["phases_ms"].items())),
-             "", "| kernel | calls | avg us | phase |", "|---|---:|---:|---|"]
+             "Workload: " + desc, "",
+             "Step from the same run: %.4f ms (%.4g %s); phases (ms): %s." % (
+                 line["ms_per_step"], line["value"], line["unit"],
+                 ", ".join("%s %.4f" % kv for kv in line["phases_ms"].items())), "",
+             "| kernel | calls | avg us | phase |", "|---|---:|---:|---|"]
     for k in sorted(avg_us, key=lambda k: -avg_us[k] * calls[k]):
-        phase = next((p for p, ks in PHASE_KERNELS.items() if any(x in k for x in ks)), "setup")
-        lines.append("| `%s` | %d | %.1f | %s |" % (k, calls[k], avg_us[k], phase))
-    lines += ["", "Setup kernels of the benchmark (table fill, gradient generation, the distinct-row count) are "
-                  "listed as setup."]
+        lines.append("| `%s` | %d | %.1f | %s |" % (k, calls[k], avg_us[k], ", ".join(_phases_of(k, phases)) or "setup"))
+    lines += ["", "Phase time per launch (sum of its kernels' durations, averaged over its launches): " +
+              ", ".join("%s %.1f us" % (p, mean(t_us[p])) for p in phases if p in t_us) + ".",
+              "Kernels of no phase (input generation, the 1 GiB calibration copy%s) are setup."
+              % (", the distinct-row count" if name in LOOKUP_WORKLOADS else "")]
     with open(os.path.join(PROFILES, TRACE_FILE[name]), "w") as f:
         f.write("\n".join(lines) + "\n")
+
     # counter summaries of the phases whose algorithmic bytes the line states
-    alg = {"gather": 648.0 * n}
-    # compulsory bytes read each distinct table row once (rotation 0's count)
-    comp = {"gather": 320.0 * line["distinct_rows_forward_rotation0"] + 328.0 * n}
-    if "scatter_apply" in line["phase_gbps"]:
-        alg["scatter_apply"] = comp["scatter_apply"] = line["roofline"]["algorithmic_bytes_per_launch"]
-    for phase, alg_bytes in alg.items():
-        ks = [k for k in fetch if any(x in k for x in PHASE_KERNELS[phase])]
-        fb = sum(fetch[k] for k in ks) * 1024 * f_scale
-        wb = sum(write.get(k, 0.0) for k in ks) * 1024 * w_scale
-        t_us = sum(avg_us.get(k, 0.0) for k in ks)
-        out = ["# HBM traffic of one launch of the %s phase, %s (%d lookups per step), MI355X, rocprofv3 counters."
-               % (phase, WORKLOAD_NAMES[name], n),
+    alg = dict(line.get("phase_algorithmic_bytes") or {})
+    comp = dict(alg)
+    if name in LOOKUP_WORKLOADS:
+        n = line["config"]["lookups_per_step"]
+        alg = {"gather": 648.0 * n}
+        # compulsory bytes read each distinct table row once (rotation 0's count)
+        comp = {"gather": 320.0 * line["distinct_rows_forward_rotation0"] + 328.0 * n}
+        if "scatter_apply" in line["phase_gbps"]:
+            alg["scatter_apply"] = comp["scatter_apply"] = line["roofline"]["algorithmic_bytes_per_launch"]
+    for phase in COUNTED[name]:
+        if phase not in alg or phase not in fetch:
+            continue
+        ks = [k for k in fetch_k if phase in _phases_of(k, phases)]
+        fb = mean(fetch[phase]) * 1024 * f_scale
+        wb = mean(write[phase]) * 1024 * w_scale
+        tp = mean(t_us[phase])
+        out = ["# HBM traffic of one launch of the %s phase, %s, MI355X, rocprofv3 counters." % (phase, title),
                "# Commands (REPO = repository root on the MI355X machine):", "#   " + cmds["fetch"],
                "#   " + cmds["write"], "#   " + cmds["trace"],
-               "# Counters are KiB per dispatch, averaged over the dispatches of each kernel (%s)."
-               % ", ".join("%d" % nf[k] for k in ks),
+               "# Counters are KiB per dispatch; a launch sums its dispatches, averaged over the %d launches of the "
+               "run." % len(fetch[phase]),
                "# Scale: the 1 GiB device copy that --calibrate-copy runs first reads FETCH_SIZE %.0f KiB and "
                "WRITE_SIZE %.0f KiB" % (f_copy, w_copy),
                "#   for 1,048,576 KiB each way, so FETCH_SIZE is scaled x%.3f and WRITE_SIZE x%.3f." % (f_scale, w_scale),
-               "# Kernels of one launch:"]
+               "# Kernels of the phase (KiB per dispatch, unscaled; a kernel shared with another phase shows its "
+               "mean over both):"]
         for k in ks:
             out.append("#   %-55s FETCH %11.1f KiB  WRITE %11.1f KiB  avg %8.1f us" % (
-                k, fetch[k], write.get(k, 0.0), avg_us.get(k, 0.0)))
+                k, mean(fetch_k[k]), mean(write_k.get(k, [0.0])), avg_us.get(k, 0.0)))
         out += ["# Algorithmic bytes per launch: %.0f; compulsory bytes (each distinct table row moved once): %.0f"
-                % (alg_bytes, comp[phase]),
-                "# Average kernel time per launch (kernel-trace run): %.1f us" % t_us,
+                % (alg[phase], comp[phase]),
+                "# Average time per launch (kernel-trace run): %.1f us" % tp,
                 "# source_sha256_16: SHA-256 prefix of the kernel source and the local headers it includes",
-                "source_sha256_16 %s" % source_sha(PHASE_SOURCE[phase]),
+                "source_sha256_16 %s" % source_sha(phases[phase][0]),
                 "fetch_bytes_per_launch %.0f" % fb, "write_bytes_per_launch %.0f" % wb,
-                "hbm_bytes_per_launch %.0f" % (fb + wb), "algorithmic_bytes_per_launch %.0f" % alg_bytes,
+                "hbm_bytes_per_launch %.0f" % (fb + wb), "algorithmic_bytes_per_launch %.0f" % alg[phase],
                 "compulsory_bytes_per_launch %.0f" % comp[phase],
-                "kernel_time_us_per_launch %.1f" % t_us]
+                "kernel_time_us_per_launch %.1f" % tp]
         with open(os.path.join(PROFILES, "%s_%s_counters.txt" % (phase, name)), "w") as f:
             f.write("\n".join(out) + "\n")
 
