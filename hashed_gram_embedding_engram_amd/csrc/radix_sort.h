@@ -20,6 +20,8 @@ namespace engram {
 namespace {
 
 constexpr int kBlock = 256;                       // threads per block, 4 waves
+// Keys per thread in a sort tile is a template parameter of the sort kernels
+// (ITEMS); these are the defaults, which the routing sort uses.
 constexpr int kItems = 16;                        // keys per thread in a sort tile
 constexpr int kTile = kBlock * kItems;            // 4096 keys per sort tile
 constexpr int kWaveSpan = 64 * kItems;            // contiguous keys owned by one wave
@@ -196,6 +198,7 @@ __device__ __forceinline__ void sum_tile_counts(const DigitCounts& dc, uint32_t 
 }
 
 // Tile histograms of the digit at `shift` (passes after the first).
+template <int ITEMS = kItems>
 __global__ __launch_bounds__(kBlock) void upsweep_kernel(const uint32_t* __restrict__ keys, uint32_t n, int shift,
                                                          DigitCounts dc) {
     __shared__ uint32_t s_cnt[kBlock / 64][kRadix];
@@ -203,15 +206,15 @@ __global__ __launch_bounds__(kBlock) void upsweep_kernel(const uint32_t* __restr
 #pragma unroll
     for (int k = 0; k < kBlock / 64; ++k) s_cnt[k][tid] = 0;
     __syncthreads();
-    const uint32_t base = blockIdx.x * (uint32_t)kTile + (uint32_t)w * kWaveSpan;
-    uint32_t key[kItems];
+    const uint32_t base = blockIdx.x * (uint32_t)(kBlock * ITEMS) + (uint32_t)w * (64 * ITEMS);
+    uint32_t key[ITEMS];
 #pragma unroll
-    for (int it = 0; it < kItems; ++it) {
+    for (int it = 0; it < ITEMS; ++it) {
         const uint32_t e = base + (uint32_t)it * 64 + (uint32_t)lane;
         key[it] = e < n ? keys[min(e, n - 1)] : 0xFFFFFFFFu;
     }
 #pragma unroll
-    for (int it = 0; it < kItems; ++it)
+    for (int it = 0; it < ITEMS; ++it)
         if (base + (uint32_t)it * 64 + (uint32_t)lane < n) atomicAdd(&s_cnt[w][(key[it] >> shift) & 0xFFu], 1u);
     __syncthreads();
     uint32_t c = 0;
@@ -246,29 +249,31 @@ __device__ __forceinline__ uint32_t block_exclusive_scan_n(uint32_t v, uint32_t*
 
 // One stable scatter pass of the LSD radix sort.  vals_in == nullptr means
 // the value of entry e is e itself.  SMALL as for load_tile_counts.
-template <bool SMALL>
+template <bool SMALL, int ITEMS = kItems>
 __global__ __launch_bounds__(kBlock) void downsweep_kernel(const uint32_t* __restrict__ keys_in,
                                                            const uint32_t* __restrict__ vals_in,
                                                            uint32_t* __restrict__ keys_out,
                                                            uint32_t* __restrict__ vals_out, uint32_t n, int shift,
                                                            DigitCounts dc) {
-    __shared__ uint32_t s_keys[kTile];
-    __shared__ uint32_t s_vals[kTile];
+    __shared__ uint32_t s_keys[kBlock * ITEMS];
+    __shared__ uint32_t s_vals[kBlock * ITEMS];
+    // per wave and digit: the wave's count, then its offset inside the tile;
+    // row 0 finally holds, per digit, where the tile's digit run goes
+    // globally less where it starts in the tile
     __shared__ uint32_t s_wave_cnt[kBlock / 64][kRadix];
     __shared__ uint32_t s_digit_start[kRadix];
-    __shared__ uint32_t s_global[kRadix];
-    __shared__ uint32_t s_tmp[kBlock / 64];
+    uint32_t* const s_tmp = s_keys;  // the scans' scratch: s_keys is written only after them
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     for (int i = tid; i < (kBlock / 64) * kRadix; i += kBlock) (&s_wave_cnt[0][0])[i] = 0;
     __syncthreads();
 
-    const uint32_t tile_base = blockIdx.x * (uint32_t)kTile;
-    const uint32_t base = tile_base + (uint32_t)w * kWaveSpan;
+    const uint32_t tile_base = blockIdx.x * (uint32_t)(kBlock * ITEMS);
+    const uint32_t base = tile_base + (uint32_t)w * (64 * ITEMS);
     TileCounts tc;
     load_tile_counts<SMALL>(dc, blockIdx.x, tid, tc);
-    uint32_t key[kItems], val[kItems], rank[kItems];
+    uint32_t key[ITEMS], val[ITEMS], rank[ITEMS];
 #pragma unroll
-    for (int it = 0; it < kItems; ++it) {
+    for (int it = 0; it < ITEMS; ++it) {
         const uint32_t e = min(base + (uint32_t)it * 64 + (uint32_t)lane, n - 1);
         key[it] = keys_in[e];
         val[it] = vals_in ? vals_in[e] : e;  // no values: the input order itself (a first pass)
@@ -283,7 +288,7 @@ __global__ __launch_bounds__(kBlock) void downsweep_kernel(const uint32_t* __res
     // items are visited in index order and the lowest lane of each digit group
     // advances the wave's counter for that digit.
 #pragma unroll
-    for (int it = 0; it < kItems; ++it) {
+    for (int it = 0; it < ITEMS; ++it) {
         const bool live = base + (uint32_t)it * 64 + (uint32_t)lane < n;
         const uint32_t d = (key[it] >> shift) & 0xFFu;
         const uint64_t peers = match_digit(d, live);
@@ -295,6 +300,7 @@ __global__ __launch_bounds__(kBlock) void downsweep_kernel(const uint32_t* __res
     }
     __syncthreads();
     // Per digit: offsets of the waves inside the tile and the tile total.
+    uint32_t global_start;  // thread d: where the tile's digit-d keys go
     {
         const int d = tid;
         uint32_t sum = 0;
@@ -306,11 +312,11 @@ __global__ __launch_bounds__(kBlock) void downsweep_kernel(const uint32_t* __res
         }
         uint32_t tot;
         s_digit_start[d] = block_exclusive_scan(sum, &tot, s_tmp);
-        s_global[d] = block_exclusive_scan(digit_total, &tot, s_tmp) + digit_before;
+        global_start = block_exclusive_scan(digit_total, &tot, s_tmp) + digit_before;
     }
     __syncthreads();
 #pragma unroll
-    for (int it = 0; it < kItems; ++it) {
+    for (int it = 0; it < ITEMS; ++it) {
         const bool live = base + (uint32_t)it * 64 + (uint32_t)lane < n;
         if (live) {
             const uint32_t d = (key[it] >> shift) & 0xFFu;
@@ -320,11 +326,13 @@ __global__ __launch_bounds__(kBlock) void downsweep_kernel(const uint32_t* __res
         }
     }
     __syncthreads();
-    const uint32_t count = min((uint32_t)kTile, n - tile_base);
+    s_wave_cnt[0][tid] = global_start - s_digit_start[tid];  // the wave offsets are no longer read
+    __syncthreads();
+    const uint32_t count = min((uint32_t)(kBlock * ITEMS), n - tile_base);
     for (uint32_t j = tid; j < count; j += kBlock) {
         const uint32_t k = s_keys[j];
         const uint32_t d = (k >> shift) & 0xFFu;
-        const uint32_t g = s_global[d] + (j - s_digit_start[d]);
+        const uint32_t g = s_wave_cnt[0][d] + j;  // unsigned wrap-around cancels
         if (g < n) {  // always true for a consistent histogram; keeps every store in bounds
             keys_out[g] = k;
             vals_out[g] = s_vals[j];

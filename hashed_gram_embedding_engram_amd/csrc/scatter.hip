@@ -91,9 +91,17 @@ constexpr int kMaxPasses = 4;  // 32-bit keys, 8-bit digits
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
+// Keys per thread of the plan's sort tiles, by lookup count.  Small tiles
+// suit small sorts (more blocks; the plan's dependent launches finish
+// sooner); large tiles suit large ones, where the plan runs beside the
+// gather: each digit run a tile writes is longer, so fewer lines are written
+// in part, and fewer blocks compete with the gather for wave slots.
+int sort_items(int64_t n) { return n <= ((int64_t)1 << 20) ? 8 : n >= ((int64_t)1 << 21) ? 24 : 16; }
+
 Layout make_layout(int64_t n, int dim) {
     Layout L;
-    L.num_tiles = (n + kTile - 1) / kTile;
+    const int64_t tile = (int64_t)kBlock * sort_items(n);
+    L.num_tiles = (n + tile - 1) / tile;
     L.num_slices = (n + kSlice - 1) / kSlice;
     L.num_run_blocks = (n + run_span(n) - 1) / run_span(n);
     size_t off = 0;
@@ -135,6 +143,7 @@ __global__ __launch_bounds__(kBlock) void scatter_init_kernel(int64_t* status, u
 // (summed at the end), which keeps same-address conflicts inside a wave.
 // Step 1: keys, digit-0 tile histograms, in-range count.  A key's lookup
 // index is its position, so the first sort pass reads no value array.
+template <int ITEMS>
 __global__ __launch_bounds__(kBlock) void keys_kernel(const int64_t* __restrict__ rows, uint32_t n,
                                                       int64_t row_begin, uint64_t num_rows,
                                                       uint32_t* __restrict__ keys, DigitCounts dc,
@@ -147,16 +156,16 @@ __global__ __launch_bounds__(kBlock) void keys_kernel(const int64_t* __restrict_
     for (int k = 0; k < kBlock / 64; ++k) s_cnt[k][tid] = 0;
     if (tid == 0) s_valid = 0;
     __syncthreads();
-    const uint32_t base = blockIdx.x * (uint32_t)kTile + (uint32_t)w * kWaveSpan;
+    const uint32_t base = blockIdx.x * (uint32_t)(kBlock * ITEMS) + (uint32_t)w * (64 * ITEMS);
     const uint32_t sentinel = (uint32_t)num_rows;
     uint32_t my_valid = 0;
     // Loads are clamped rather than guarded, so all of a thread's loads are in
     // flight together (a guarded load becomes a branch that waits for it).
-    int64_t r[kItems];
+    int64_t r[ITEMS];
 #pragma unroll
-    for (int it = 0; it < kItems; ++it) r[it] = rows[min(base + (uint32_t)it * 64 + (uint32_t)lane, n - 1)];
+    for (int it = 0; it < ITEMS; ++it) r[it] = rows[min(base + (uint32_t)it * 64 + (uint32_t)lane, n - 1)];
 #pragma unroll
-    for (int it = 0; it < kItems; ++it) {
+    for (int it = 0; it < ITEMS; ++it) {
         const uint32_t e = base + (uint32_t)it * 64 + (uint32_t)lane;
         if (e < n) {
             uint32_t key = sentinel;
@@ -849,6 +858,49 @@ hipError_t dispatch_reduce(const Layout& L, const char* ws, const void* grad_out
     return launch_reduce<0, BF16, DENSE>(L, ws, grad_out, n, num_rows, cpr, dim, grad_dense, uniq_grad, stream);
 }
 
+// Steps 1-2: keys and the radix passes, ending in the sorted slots.
+template <int ITEMS>
+hipError_t run_sort(const Layout& L, char* ws, const int64_t* rows, int64_t n, int64_t row_begin, int64_t num_rows,
+                    int passes, int64_t* status, hipStream_t stream) {
+    uint32_t* counters = (uint32_t*)(ws + L.counters);
+    const size_t pass_words = count_words(L.num_tiles);  // chunk and group totals of one pass
+    uint32_t* count_totals = (uint32_t*)(ws + L.count_totals);
+    const uint32_t nn = (uint32_t)n, tiles = (uint32_t)L.num_tiles;
+    hipError_t err;
+    // Passes ping-pong between the two buffers and must end in the sorted slots.
+    uint32_t *k_cur, *k_nxt, *v_cur, *v_nxt;
+    if (passes % 2 == 0) {
+        k_cur = (uint32_t*)(ws + L.sorted_keys); k_nxt = (uint32_t*)(ws + L.spare_keys);
+        v_cur = (uint32_t*)(ws + L.sorted_vals); v_nxt = (uint32_t*)(ws + L.spare_vals);
+    } else {
+        k_cur = (uint32_t*)(ws + L.spare_keys); k_nxt = (uint32_t*)(ws + L.sorted_keys);
+        v_cur = (uint32_t*)(ws + L.spare_vals); v_nxt = (uint32_t*)(ws + L.sorted_vals);
+    }
+    auto pass_counts = [&](int p) { return make_digit_counts(ws + L.hist, count_totals + p * pass_words, L.num_tiles); };
+    hipLaunchKernelGGL(keys_kernel<ITEMS>, dim3(tiles), dim3(kBlock), 0, stream, rows, nn, row_begin, (uint64_t)num_rows,
+                       k_cur, pass_counts(0), status, counters);
+    if ((err = hipGetLastError()) != hipSuccess) return err;
+    for (int p = 0; p < passes; ++p) {
+        const int shift = 8 * p;
+        const DigitCounts dc = pass_counts(p);
+        if (p > 0) {
+            hipLaunchKernelGGL(upsweep_kernel<ITEMS>, dim3(tiles), dim3(kBlock), 0, stream, k_cur, nn, shift, dc);
+            if ((err = hipGetLastError()) != hipSuccess) return err;
+        }
+        const uint32_t* v_in = p == 0 ? nullptr : v_cur;
+        if (small_counts(dc))
+            hipLaunchKernelGGL((downsweep_kernel<true, ITEMS>), dim3(tiles), dim3(kBlock), 0, stream, k_cur, v_in, k_nxt,
+                               v_nxt, nn, shift, dc);
+        else
+            hipLaunchKernelGGL((downsweep_kernel<false, ITEMS>), dim3(tiles), dim3(kBlock), 0, stream, k_cur, v_in, k_nxt,
+                               v_nxt, nn, shift, dc);
+        if ((err = hipGetLastError()) != hipSuccess) return err;
+        uint32_t* t = k_cur; k_cur = k_nxt; k_nxt = t;
+        t = v_cur; v_cur = v_nxt; v_nxt = t;
+    }
+    return hipSuccess;
+}
+
 }  // namespace
 
 size_t scatter_workspace_bytes(int64_t n, int64_t num_rows, int dim) {
@@ -873,40 +925,14 @@ hipError_t launch_scatter_plan(const int64_t* rows, int64_t n, int64_t row_begin
                        count_totals, total_words);
     hipError_t err = hipGetLastError();
     if (err != hipSuccess || n == 0) return err;
+    const int items = sort_items(n);
+    if (items == 8) err = run_sort<8>(L, ws, rows, n, row_begin, num_rows, passes, status, stream);
+    else if (items == 16) err = run_sort<16>(L, ws, rows, n, row_begin, num_rows, passes, status, stream);
+    else err = run_sort<24>(L, ws, rows, n, row_begin, num_rows, passes, status, stream);
+    if (err != hipSuccess) return err;
 
-    const uint32_t nn = (uint32_t)n, tiles = (uint32_t)L.num_tiles;
-    // Passes ping-pong between the two buffers and must end in the sorted slots.
-    uint32_t *k_cur, *k_nxt, *v_cur, *v_nxt;
-    if (passes % 2 == 0) {
-        k_cur = (uint32_t*)(ws + L.sorted_keys); k_nxt = (uint32_t*)(ws + L.spare_keys);
-        v_cur = (uint32_t*)(ws + L.sorted_vals); v_nxt = (uint32_t*)(ws + L.spare_vals);
-    } else {
-        k_cur = (uint32_t*)(ws + L.spare_keys); k_nxt = (uint32_t*)(ws + L.sorted_keys);
-        v_cur = (uint32_t*)(ws + L.spare_vals); v_nxt = (uint32_t*)(ws + L.sorted_vals);
-    }
-    auto pass_counts = [&](int p) { return make_digit_counts(ws + L.hist, count_totals + p * pass_words, L.num_tiles); };
-    hipLaunchKernelGGL(keys_kernel, dim3(tiles), dim3(kBlock), 0, stream, rows, nn, row_begin, (uint64_t)num_rows,
-                       k_cur, pass_counts(0), status, counters);
-    if ((err = hipGetLastError()) != hipSuccess) return err;
-    for (int p = 0; p < passes; ++p) {
-        const int shift = 8 * p;
-        const DigitCounts dc = pass_counts(p);
-        if (p > 0) {
-            hipLaunchKernelGGL(upsweep_kernel, dim3(tiles), dim3(kBlock), 0, stream, k_cur, nn, shift, dc);
-            if ((err = hipGetLastError()) != hipSuccess) return err;
-        }
-        const uint32_t* v_in = p == 0 ? nullptr : v_cur;
-        if (small_counts(dc))
-            hipLaunchKernelGGL(downsweep_kernel<true>, dim3(tiles), dim3(kBlock), 0, stream, k_cur, v_in, k_nxt,
-                               v_nxt, nn, shift, dc);
-        else
-            hipLaunchKernelGGL(downsweep_kernel<false>, dim3(tiles), dim3(kBlock), 0, stream, k_cur, v_in, k_nxt,
-                               v_nxt, nn, shift, dc);
-        if ((err = hipGetLastError()) != hipSuccess) return err;
-        uint32_t* t = k_cur; k_cur = k_nxt; k_nxt = t;
-        t = v_cur; v_cur = v_nxt; v_nxt = t;
-    }
-
+    const uint32_t nn = (uint32_t)n;
+    const uint32_t* k_cur = (const uint32_t*)(ws + L.sorted_keys);
     const uint32_t ns = (uint32_t)L.num_slices;
     const uint32_t run_blocks = (uint32_t)L.num_run_blocks, span = run_span(n);
     hipLaunchKernelGGL(run_count_kernel, dim3(run_blocks), dim3(kBlock), 0, stream, k_cur, nn, counters,
