@@ -324,11 +324,12 @@ def test_large_dense_and_deterministic():
 
 
 def test_sort_beyond_one_shot_counts():
-    """2^22 + 12,305 lookups (1,028 sort tiles): beyond 2^22 the scatter pass
-    sums its tiles' digit counts in loops instead of loading them in one go."""
+    """6,291,456 + 12,305 lookups (1,027 sort tiles of 6,144 keys): beyond
+    1,024 tiles the scatter pass sums its tiles' digit counts in loops
+    instead of loading them in one go."""
     rng = np.random.default_rng(25)
     R = 320_001_536
-    n = (1 << 22) + 3 * 4096 + 17
+    n = 1024 * 6144 + 2 * 6144 + 17
     hot = rng.integers(0, R, size=32)
     rows = np.where(rng.random(n) < 0.2, hot[rng.integers(0, 32, size=n)], rng.integers(0, R, size=n))
     check_compact(rows.astype(np.int64), grads(n, dim=8, seed=25), R)
@@ -339,3 +340,23 @@ def test_large_all_one_row():
     n = LARGE_N
     dy = grads(n, dim=8, seed=24)
     check_compact(np.full(n, 99_999, dtype=np.int64), dy, 320_001_536)
+
+
+@pytest.mark.parametrize("n", [(1 << 20) - 1, 1 << 20, (1 << 20) + 1, (1 << 21) - 1, 1 << 21, (1 << 21) + 1])
+def test_sort_tile_size_boundaries(n):
+    """The plan's sort tiles hold 8 keys per thread up to 2^20 lookups, 16
+    below 2^21 and 24 from 2^21: both sides of each change, compact and dense,
+    with hot rows and a 29-bit key range."""
+    rng = np.random.default_rng(n % 1009)
+    R = 320_001_536
+    hot = rng.integers(0, R, size=48)
+    rows = np.where(rng.random(n) < 0.25, hot[rng.integers(0, 48, size=n)], rng.integers(0, R, size=n))
+    rows = rows.astype(np.int64)
+    dy = grads(n, dim=8, seed=n % 101)
+    ur, ug = check_compact(rows, dy, R)
+    R2 = 3_000_017
+    rows2 = rows % R2
+    got, bad = run_dense(rows2, dy, R2)
+    ref, rbad = c_oracle.scatter_add_dense(rows2, to_host(dy), R2)
+    assert bad == rbad == -1
+    assert_close_to_fp64(got, ref, "dense, n = %d" % n)
