@@ -881,6 +881,17 @@ def lookup_line(name, args, dev, table=None):
                                   "gbps_compulsory": round(compulsory["gather"] / (ga / 1e3) / 1e9, 1),
                                   "frac": round(gather_bytes / (ga / 1e3) / 1e9 / HBM_PEAK_GBPS, 4),
                                   "frac_compulsory": round(compulsory["gather"] / (ga / 1e3) / 1e9 / HBM_PEAK_GBPS, 4)}
+    # HBM bytes of every phase of the step from the committed counter
+    # summaries, against the step time (only when all are current).
+    counted = (["hash"] if b0["tokens"] is not None else []) + ["gather"] + \
+        (["scatter_plan", "scatter_apply"] if wl["backward"] else [])
+    per = {ph: counter_traffic(LOOKUP_PHASES[ph][0], "%s_%s_counters.txt" % (ph, name)) for ph in counted}
+    if all(v is not None for v in per.values()):
+        total = sum(per.values())
+        result["step_traffic"] = {"bytes_per_step": total, "gbps": round(total / (result["ms_per_step"] / 1e3) / 1e9, 1),
+                                  "phases_gb": {k: round(v / 1e9, 4) for k, v in per.items()},
+                                  "from": "FETCH_SIZE + WRITE_SIZE per launch in the committed rocprofv3 summaries of "
+                                          "every phase of the step, over ms_per_step"}
     if alone and wl["backward"]:
         bs = alone["scatter_plan"] + alone["scatter_apply"]
         result["backward_plan_then_apply"] = {"ms": round(bs, 4),
@@ -948,7 +959,8 @@ PROFILED = {
 }
 # Phases whose counter summaries are written (the ones a bench line can name
 # as its dominant kernel).
-COUNTED = {"long": ["gather", "scatter_apply"], "full-sft": ["gather"], "owner": ["gather", "scatter_apply"],
+COUNTED = {"long": ["hash", "gather", "scatter_plan", "scatter_apply"], "full-sft": ["hash", "gather"],
+           "owner": ["gather", "scatter_plan", "scatter_apply"],
            "ple": ["conv_fwd", "norm_fwd", "norm_bwd", "conv_bwd"],
            "route": ["pack_values", "unpack_values", "unpermute_values"]}
 PROFILE_FLAGS = "--steps 5 --warmup 2 --no-cpu-baseline --no-alone --no-ceilings --no-extra-configs --calibrate-copy"
@@ -963,6 +975,22 @@ WORKLOAD_TEXT = {
              "segment validation, pack of the IDs to the step's capacity, the owner's unpack, the owner's pack "
              "of 320-B bf16 value rows, the requester's unpack and the unpermute to request order",
 }
+
+
+def sort_nominal_bytes(n, num_rows, uniq=None):
+    """HBM bytes the backward plan's own traffic model gives for n lookups:
+    keys (8 B row read, 4 B key written), the first pass (4 B read, 8 B
+    written), each later pass (16 B) with its histogram (4 B), the run count's
+    read (4 B) and, in the compact form, the distinct rows' pass (4 B read,
+    8 B per distinct row written)."""
+    bits = 0
+    while bits < 32 and (num_rows >> bits) != 0:   # the out-of-range sentinel num_rows sorts last
+        bits += 1
+    passes = (bits + 7) // 8
+    total = 24 * n + (passes - 1) * 20 * n + 4 * n
+    if uniq is not None:
+        total += 4 * n + 8 * uniq
+    return float(total)
 
 
 def profile_commands(name):
@@ -1083,12 +1111,15 @@ def summarize_profiles(name, raw):
     alg = dict(line.get("phase_algorithmic_bytes") or {})
     comp = dict(alg)
     if name in LOOKUP_WORKLOADS:
-        n = line["config"]["lookups_per_step"]
-        alg = {"gather": 648.0 * n}
+        cfg = line["config"]
+        n = cfg["lookups_per_step"]
+        alg = {"gather": 648.0 * n, "hash": 8.0 * cfg["tokens"] + 8.0 * n}
         # compulsory bytes read each distinct table row once (rotation 0's count)
-        comp = {"gather": 320.0 * line["distinct_rows_forward_rotation0"] + 328.0 * n}
+        comp = {"gather": 320.0 * line["distinct_rows_forward_rotation0"] + 328.0 * n, "hash": alg["hash"]}
         if "scatter_apply" in line["phase_gbps"]:
             alg["scatter_apply"] = comp["scatter_apply"] = line["roofline"]["algorithmic_bytes_per_launch"]
+            alg["scatter_plan"] = comp["scatter_plan"] = sort_nominal_bytes(n, cfg["table_rows"],
+                                                                            cfg["distinct_rows_rotation0"])
     for phase in COUNTED[name]:
         if phase not in alg or phase not in fetch:
             continue

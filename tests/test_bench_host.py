@@ -18,6 +18,10 @@ SUMMARIES = {
     "gather_full-sft_counters.txt": "gather.hip",
     "gather_owner_counters.txt": "gather.hip",
     "scatter_apply_owner_counters.txt": "scatter.hip",
+    "hash_long_counters.txt": "hash.hip",
+    "hash_full-sft_counters.txt": "hash.hip",
+    "scatter_plan_long_counters.txt": "scatter.hip",
+    "scatter_plan_owner_counters.txt": "scatter.hip",
     "conv_fwd_ple_counters.txt": "ple.hip",
     "conv_bwd_ple_counters.txt": "ple.hip",
     "norm_fwd_ple_counters.txt": "ple.hip",
@@ -102,3 +106,12 @@ def test_source_sha_covers_included_headers(tmp_path, monkeypatch):
     first = bench.source_sha("k.hip")
     (tmp_path / "b.h").write_text("header b v2\n")
     assert bench.source_sha("k.hip") != first
+
+
+def test_sort_nominal_bytes():
+    """The plan's traffic model: 29-bit keys take four passes, 23-bit keys three."""
+    n, u = 1000, 600
+    assert bench.sort_nominal_bytes(n, 320_001_536, u) == 92 * n + 8 * u
+    assert bench.sort_nominal_bytes(n, 5_000_024) == 68 * n
+    assert bench.sort_nominal_bytes(n, (1 << 24) - 1) == 68 * n   # the sentinel fits 24 bits
+    assert bench.sort_nominal_bytes(n, 1 << 24) == 88 * n           # it needs a 25th
