@@ -914,7 +914,7 @@ CEILING_OF = {"scatter_apply": "row_expand"}
 
 # Fields of the other configurations' lines kept in the default line.
 EXTRA_KEYS = ("value", "unit", "ms_per_step", "config", "phases_ms", "roofline", "phase_gbps", "gather_alone",
-              "backward_plan_then_apply", "phases_alone_ms_p50", "distinct_rows_forward_rotation0")
+              "backward_plan_then_apply", "phases_alone_ms_p50", "distinct_rows_forward_rotation0", "step_traffic")
 
 
 def add_ceiling_fracs(result, ceilings):
