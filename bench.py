@@ -184,10 +184,14 @@ def build_workload(name, rotations, dev, table=None):
 
 
 def run_step(wl, b, ev=None):
-    """hash -> gather, with the backward plan (sort by row) on a side stream
-    concurrently with the gather, then apply once both are done.  ev: events
-    (hash start, hash end, gather end, plan start, plan end, apply start, apply
-    end); an entry may be None, and only the events given are recorded."""
+    """One step.  From tokens (long, sft, full-sft): the fused hash-and-gather
+    forward on the main stream; with a backward, the hash into the rows array
+    and then the plan (sort by row) on a side stream beside it; the apply once
+    both are done.  From rows (the owner shard, which receives its rows): the
+    plan on the side stream beside the gather, then the apply.  ev: events
+    (step start, side hash end, forward end, side start, plan end, apply
+    start, apply end); an entry may be None, and only the events given are
+    recorded."""
     import torch
 
     import hashed_gram_embedding_engram_amd as E
@@ -198,19 +202,27 @@ def run_step(wl, b, ev=None):
         if ev and ev[k] is not None:
             ev[k].record(stream)
 
-    mark(0, main)
-    if b["tokens"] is not None:
-        E.engram_hash(b["tokens"], wl["spec"], rows_out=b["rows"])
-    mark(1, main)
-    if wl["backward"]:
-        side.wait_stream(main)
-        compact = b.get("compact")
-        mark(3, side)
+    compact = b.get("compact")
+
+    def plan():
         E.engram_scatter_add_plan(b["rows"], wl["table_rows"], b["dy"].shape[-1], wl["row_begin"],
                                   workspace=wl["workspace"], uniq_rows=compact[0] if compact else None,
                                   num_uniq=compact[2] if compact else None, status=b["plan_status"], stream=side)
+
+    mark(0, main)
+    if wl["backward"]:
+        side.wait_stream(main)
+        mark(3, side)
+        if b["tokens"] is not None:
+            E.engram_hash(b["tokens"], wl["spec"], rows_out=b["rows"], stream=side)
+        mark(1, side)
+        plan()
         mark(4, side)
-    E.engram_gather(wl["table"], b["rows"], wl["row_begin"], out=b["out"], status=b["status"], validate=False)
+    if b["tokens"] is not None:
+        E.engram_hash_gather(b["tokens"], wl["spec"], wl["table"], wl["row_begin"], out=b["out"],
+                             status=b["status"], validate=False)
+    else:
+        E.engram_gather(wl["table"], b["rows"], wl["row_begin"], out=b["out"], status=b["status"], validate=False)
     mark(2, main)
     if wl["backward"]:
         main.wait_stream(side)
@@ -221,9 +233,11 @@ def run_step(wl, b, ev=None):
 
 
 def phases_alone(wl, k):
-    """Median ms of the gather, the plan and the apply, each run by itself on
-    the main stream with nothing beside it, over k launches rotating through
-    the input sets (outside the timed steps)."""
+    """Median ms of the forward gather (fused with the hash when the workload
+    starts from tokens), the plan (from the rows) and the apply, each run by
+    itself on the main stream with nothing beside it, over k launches rotating
+    through the input sets (outside the timed steps).  The rows arrays hold
+    every rotation's rows (the warm-up steps hashed them)."""
     import torch
 
     import hashed_gram_embedding_engram_amd as E
@@ -236,7 +250,12 @@ def phases_alone(wl, k):
         e = [ev() for _ in range(6)]
         events.append(e)
         e[0].record()
-        E.engram_gather(wl["table"], b["rows"], wl["row_begin"], out=b["out"], status=b["status"], validate=False)
+        if b["tokens"] is not None:  # the forward as the steps run it: fused hash and gather
+            E.engram_hash_gather(b["tokens"], wl["spec"], wl["table"], wl["row_begin"], out=b["out"],
+                                 status=b["status"], validate=False)
+        else:
+            E.engram_gather(wl["table"], b["rows"], wl["row_begin"], out=b["out"], status=b["status"],
+                            validate=False)
         e[1].record()
         if wl["backward"]:
             compact = b.get("compact")
@@ -757,8 +776,9 @@ def lookup_line(name, args, dev, table=None):
     # EVENT_STRIDE-th timed step carries events, and only the two around the
     # dominant phase (the apply, or the gather of a forward-only workload); a
     # second pass with events around every phase gives the breakdown.
+    fused = wl["batches"][0]["tokens"] is not None
     dom = "scatter_apply" if wl["backward"] else "gather"
-    dom_span = (5, 6) if wl["backward"] else (1, 2)
+    dom_span = (5, 6) if wl["backward"] else (0, 2)
     mk = lambda: torch.cuda.Event(enable_timing=True)
     tevs = [[mk() if k in dom_span else None for k in range(7)] if i % EVENT_STRIDE == 0 else None
             for i in range(args.steps)]
@@ -780,9 +800,13 @@ def lookup_line(name, args, dev, table=None):
         run_step(wl, wl["batches"][i % R], evs[i])
     torch.cuda.synchronize()
     alone = None if args.no_alone else phases_alone(wl, min(args.steps, 20))
-    spans = {"hash": (0, 1), "gather": (1, 2)}
+    # From tokens the forward is one fused kernel ("gather"), and the hash that
+    # feeds the plan runs on the side stream; from rows there is no hash.
+    spans = {"gather": (0, 2)}
     if wl["backward"]:
-        spans.update({"scatter_plan (side stream)": (3, 4), "wait_for_plan": (2, 5), "scatter_apply": (5, 6)})
+        if fused:
+            spans["hash (side stream)"] = (3, 1)
+        spans.update({"scatter_plan (side stream)": (1, 4), "wait_for_plan": (2, 5), "scatter_apply": (5, 6)})
     phase = {k: sum(e[a].elapsed_time(e[b]) for e in evs) / kb for k, (a, b) in spans.items()}
     phase_pct = {k: percentiles([e[a].elapsed_time(e[b]) for e in evs]) for k, (a, b) in spans.items()}
     phase[dom] = sum(dom_ms) / len(dom_ms)        # the dominant phase from the timed steps themselves
@@ -795,12 +819,14 @@ def lookup_line(name, args, dev, table=None):
 
     # Algorithmic bytes (what the method must move, per launch):
     #   gather: per lookup one 320 B table row read, one 320 B output row
-    #           written and one 8 B row id read -> 648 B;
+    #           written and one 8 B row id read -> 648 B; fused with the hash
+    #           (from tokens), 640 B per lookup and one 8 B token per position;
     #   apply (segment reduce + carry fix-up): per lookup one 320 B bf16
     #           gradient row read and its 8 B sorted (key, index) pair; per
     #           distinct row one 640 B fp32 sum written (compact) or a 640 B
     #           read + 640 B write (dense).
-    gather_bytes = 648.0 * n_avg
+    positions = int(b0["ids"].size)
+    gather_bytes = 640.0 * n_avg + 8.0 * positions if fused else 648.0 * n_avg
     if wl["backward"]:
         u_rows = sum(int(b["compact"][2].item()) for b in wl["batches"]) / R if "compact" in b0 else None
         if u_rows is None:  # dense: distinct rows counted from the plan of rotation 0
@@ -809,7 +835,9 @@ def lookup_line(name, args, dev, table=None):
             apply_bytes = 328.0 * n_avg + 1280.0 * u_rows
         else:
             apply_bytes = 328.0 * n_avg + 640.0 * u_rows
-    kern = {"gather": (gather_bytes, phase["gather"], "gather_rows_kernel<20,16,true>", "gather.hip")}
+    kern = {"gather": (gather_bytes, phase["gather"],
+                       "hash_gather_kernel<true,false> (hash and gather fused)" if fused
+                       else "gather_rows_kernel<20,16,true>", PROFILED[name]["gather"][0])}
     # The plan runs on a side stream during the gather; apply is timed from
     # after the main stream's wait for it.
     if wl["backward"]:
@@ -824,8 +852,11 @@ def lookup_line(name, args, dev, table=None):
     # (U/L) * 320 + 328 B per lookup); and the HBM bytes the committed
     # rocprofv3 counters measured for that kernel (null when they were taken
     # on other kernel sources).
-    u_fwd = int(torch.unique(b0["rows"].reshape(-1)).numel())
-    compulsory = {"gather": 320.0 * u_fwd + 328.0 * n_avg}
+    import hashed_gram_embedding_engram_amd as E
+    rows0 = E.engram_hash(b0["tokens"], wl["spec"]) if fused else b0["rows"]   # outside the timed steps
+    u_fwd = int(torch.unique(rows0.reshape(-1)).numel())
+    del rows0
+    compulsory = {"gather": 320.0 * u_fwd + (320.0 * n_avg + 8.0 * positions if fused else 328.0 * n_avg)}
     if wl["backward"]:
         compulsory["scatter_apply"] = apply_bytes   # every gradient row is read once already
     gbps = {}
@@ -838,7 +869,7 @@ def lookup_line(name, args, dev, table=None):
     last = 6 if wl["backward"] else 2
     step_ms = sorted(e[0].elapsed_time(e[last]) for e in evs)
     pct = lambda q: step_ms[min(len(step_ms) - 1, int(q * (len(step_ms) - 1) + 0.5))]
-    fwd_ms = phase["hash"] + phase["gather"]
+    fwd_ms = phase["gather"]
     result = {
         "metric": METRIC,
         "value": lookups / elapsed,
@@ -883,9 +914,9 @@ def lookup_line(name, args, dev, table=None):
                                   "frac_compulsory": round(compulsory["gather"] / (ga / 1e3) / 1e9 / HBM_PEAK_GBPS, 4)}
     # HBM bytes of every phase of the step from the committed counter
     # summaries, against the step time (only when all are current).
-    counted = (["hash"] if b0["tokens"] is not None else []) + ["gather"] + \
+    counted = (["hash"] if fused and wl["backward"] else []) + ["gather"] + \
         (["scatter_plan", "scatter_apply"] if wl["backward"] else [])
-    per = {ph: counter_traffic(LOOKUP_PHASES[ph][0], "%s_%s_counters.txt" % (ph, name)) for ph in counted}
+    per = {ph: counter_traffic(PROFILED[name][ph][0], "%s_%s_counters.txt" % (ph, name)) for ph in counted}
     if all(v is not None for v in per.values()):
         total = sum(per.values())
         result["step_traffic"] = {"bytes_per_step": total, "gbps": round(total / (result["ms_per_step"] / 1e3) / 1e9, 1),
@@ -943,8 +974,10 @@ LOOKUP_PHASES = {
                                      r"\buniq_rows_kernel"]),
     "scatter_apply": ("scatter.hip", [r"\bsegment_reduce_kernel", r"\bcarry_fixup_kernel", r"\blong_run_kernel"]),
 }
+# Workloads that start from tokens run the fused hash-and-gather forward.
+FUSED_PHASES = dict(LOOKUP_PHASES, gather=("lookup.hip", [r"\bhash_gather_kernel"]))
 PROFILED = {
-    "long": LOOKUP_PHASES, "full-sft": LOOKUP_PHASES, "owner": LOOKUP_PHASES,
+    "long": FUSED_PHASES, "full-sft": FUSED_PHASES, "sft": FUSED_PHASES, "owner": LOOKUP_PHASES,
     "ple": {"conv_fwd": ("ple.hip", [r"\bshort_conv_fwd"]), "norm_fwd": ("ple.hip", [r"\brms_norm_fwd"]),
             "norm_bwd": ("ple.hip", [r"\brms_norm_bwd", r"\bcolumn_sum_kernel"]),
             "conv_bwd": ("ple.hip", [r"\bshort_conv_bwd", r"\bcolumn_sum_kernel"])},
@@ -959,7 +992,7 @@ PROFILED = {
 }
 # Phases whose counter summaries are written (the ones a bench line can name
 # as its dominant kernel).
-COUNTED = {"long": ["hash", "gather", "scatter_plan", "scatter_apply"], "full-sft": ["hash", "gather"],
+COUNTED = {"long": ["hash", "gather", "scatter_plan", "scatter_apply"], "full-sft": ["gather"],
            "owner": ["gather", "scatter_plan", "scatter_apply"],
            "ple": ["conv_fwd", "norm_fwd", "norm_bwd", "conv_bwd"],
            "route": ["pack_values", "unpack_values", "unpermute_values"]}
@@ -1113,9 +1146,12 @@ def summarize_profiles(name, raw):
     if name in LOOKUP_WORKLOADS:
         cfg = line["config"]
         n = cfg["lookups_per_step"]
-        alg = {"gather": 648.0 * n, "hash": 8.0 * cfg["tokens"] + 8.0 * n}
+        fused = phases["gather"][0] == "lookup.hip"   # the forward hashes inside the gather
+        per_lookup = 640.0 * n + 8.0 * cfg["tokens"] if fused else 648.0 * n
+        alg = {"gather": per_lookup, "hash": 8.0 * cfg["tokens"] + 8.0 * n}
         # compulsory bytes read each distinct table row once (rotation 0's count)
-        comp = {"gather": 320.0 * line["distinct_rows_forward_rotation0"] + 328.0 * n, "hash": alg["hash"]}
+        comp = {"gather": 320.0 * line["distinct_rows_forward_rotation0"] + per_lookup - 320.0 * n,
+                "hash": alg["hash"]}
         if "scatter_apply" in line["phase_gbps"]:
             alg["scatter_apply"] = comp["scatter_apply"] = line["roofline"]["algorithmic_bytes_per_launch"]
             alg["scatter_plan"] = comp["scatter_plan"] = sort_nominal_bytes(n, cfg["table_rows"],

@@ -21,6 +21,7 @@
 #include <algorithm>
 
 #include "engram_internal.h"
+#include "row_copy.h"
 
 // Build-time switch for non-temporal table loads; off, because the gather then
 // ran 20% slower (repeated hot rows lose their cache hits).
@@ -50,8 +51,6 @@ template <int CPR, int G, bool ROW32>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 4))) void gather_rows_kernel(
     const u32x4* __restrict__ table, int64_t row_begin, uint64_t num_rows, const int64_t* __restrict__ rows,
     int64_t n, u32x4* __restrict__ out, int64_t* __restrict__ status) {
-    constexpr int PER_LANE = CPR * G / 64;
-    static_assert(CPR * G % 64 == 0 && G <= 64, "wave tile must be whole dwordx4 per lane");
     const int lane = threadIdx.x & 63;
     const int64_t wave = (int64_t)blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6);
     const int64_t n0 = wave * G;
@@ -67,40 +66,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 4))) voi
             local = ~0ull;
         }
     }
-    // Every load is issued unconditionally (a lane with nothing to copy reads a
-    // zero chunk), so all PER_LANE loads of the wave are in flight together.
-    const int rem = (int)(n - n0 < G ? n - n0 : G);
-    const u32x4* src[PER_LANE];
-#pragma unroll
-    for (int j = 0; j < PER_LANE; ++j) {
-        const int c = lane + 64 * j;
-        const int i = c / CPR, k = c % CPR;
-        if (ROW32) {
-            const uint32_t r = __shfl((uint32_t)local, i, 64);
-            src[j] = (i < rem && r != 0xFFFFFFFFu) ? table + ((uint64_t)r * CPR + k) : &kZeroChunk;
-        } else {
-            const uint64_t r = __shfl(local, i, 64);
-            src[j] = (i < rem && r != ~0ull) ? table + (r * CPR + k) : &kZeroChunk;
-        }
-    }
-    u32x4 v[PER_LANE];
-#pragma unroll
-    for (int j = 0; j < PER_LANE; ++j) {
-#if ENGRAM_GATHER_NT_LOAD
-        v[j] = __builtin_nontemporal_load(src[j]);
-#else
-        v[j] = *src[j];
-#endif
-    }
-    u32x4* dst = out + n0 * CPR + lane;
-    if (rem == G) {  // every wave but the last: no per-store condition
-#pragma unroll
-        for (int j = 0; j < PER_LANE; ++j) __builtin_nontemporal_store(v[j], dst + 64 * j);
-    } else {
-#pragma unroll
-        for (int j = 0; j < PER_LANE; ++j)
-            if ((lane + 64 * j) / CPR < rem) __builtin_nontemporal_store(v[j], dst + 64 * j);
-    }
+    copy_wave_rows<CPR, G, ROW32, ENGRAM_GATHER_NT_LOAD != 0>(table, local, n0, n, out, lane, &kZeroChunk);
 }
 
 // Any row size (multiple of 16 B, at most 64 chunks): one chunk per lane over

@@ -19,21 +19,10 @@
 // memory.  The modulus uses a Barrett reduction with per-head reciprocals
 // computed on the host: no 64-bit division on the GPU.
 #include "engram_internal.h"
+#include "hash_math.h"
 
 namespace engram {
 namespace {
-
-// Positive remainder of a signed 64-bit value by p (2 <= p <= 2^62).
-// For m < 0, m mod p = p - 1 - ((-m - 1) mod p), and -m - 1 = ~m fits in
-// [0, 2^63), so both signs reduce a value below 2^63.
-__device__ __forceinline__ uint64_t floor_mod(int64_t m, uint64_t p, uint64_t magic) {
-    const bool neg = m < 0;
-    const uint64_t v = neg ? ~(uint64_t)m : (uint64_t)m;
-    const uint64_t q = __umul64hi(v, magic);
-    uint64_t r = v - q * p;
-    if (r >= p) r -= p;
-    return neg ? p - 1 - r : r;
-}
 
 // One wave per block: a wave's positions share nothing with other waves (its
 // LDS rows are its own), and small token batches then spread over every

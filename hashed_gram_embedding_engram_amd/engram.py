@@ -6,8 +6,8 @@ If the library is missing, loading fails with an error — there is no CPU or
 PyTorch fallback.
 
 The functions keep the names of the C ABI (``engram_hash``, ``engram_hash_slice``,
-``engram_gather``, ``engram_scatter_add``, ``engram_scatter_add_workspace``) and
-take torch tensors in place of raw pointers.
+``engram_gather``, ``engram_hash_gather``, ``engram_scatter_add``, ...) and take
+torch tensors in place of raw pointers.
 """
 import ctypes
 import os
@@ -92,6 +92,8 @@ def load_library(path=LIB_PATH):
     lib.engram_hash_slice.argtypes = [p, i64, i64, i64, i64, ctypes.POINTER(EngramHashSpec), p, p]
     lib.engram_gather.restype = ctypes.c_int
     lib.engram_gather.argtypes = [p, i32, i64, i64, i32, p, i64, p, p, p]
+    lib.engram_hash_gather.restype = ctypes.c_int
+    lib.engram_hash_gather.argtypes = [p, i64, i64, ctypes.POINTER(EngramHashSpec), p, i32, i64, i64, i32, p, p, p, p]
     lib.engram_scatter_add_workspace.restype = sz
     lib.engram_scatter_add_workspace.argtypes = [i64, i64, i32]
     lib.engram_scatter_add.restype = ctypes.c_int
@@ -214,6 +216,38 @@ def engram_gather(table, rows, row_begin=0, out=None, status=None, validate=True
                              _status_ptr(status), _stream_handle(stream)), "engram_gather")
     if validate:
         _raise_on_status(status, "engram_gather", rows)
+    return out
+
+
+def engram_hash_gather(tokens, spec, table, row_begin=0, out=None, rows_out=None, status=None, validate=True,
+                       stream=None):
+    """Forward in one call: engram_hash of tokens int64 [batch, seq] then engram_gather
+    of every position's H rows -> out [batch, seq, H, dim].  ``rows_out`` (int64
+    [batch, seq, H]) also receives the hashed rows; it may be None for the released
+    layout with a 160-wide bf16 table, where one kernel does both.  With
+    ``validate`` the call synchronises and raises on a row outside the table's shard."""
+    lib = load_library()
+    if tokens.dim() != 2:
+        raise ValueError("tokens must be [batch, seq]")
+    if table.dim() != 2:
+        raise ValueError("table must be [num_rows, dim]")
+    batch, seq = tokens.shape
+    num_rows, dim = table.shape
+    heads = spec.num_heads
+    if out is None:
+        out = torch.empty((batch, seq, heads, dim), dtype=table.dtype, device=table.device)
+    if validate and status is None:
+        status = torch.empty((), dtype=torch.int64, device=table.device)
+    _check(lib.engram_hash_gather(_dev_ptr(tokens, "tokens", torch.int64), batch, seq, ctypes.byref(spec),
+                                  _dev_ptr(table, "table", table.dtype), _dtype_code(table), row_begin, num_rows, dim,
+                                  _dev_ptr(out, "out", table.dtype, numel=batch * seq * heads * dim),
+                                  _dev_ptr(rows_out, "rows_out", torch.int64, numel=batch * seq * heads),
+                                  _status_ptr(status), _stream_handle(stream)), "engram_hash_gather")
+    if validate:
+        bad = int(status.item())
+        if bad >= 0:
+            raise EngramError("engram_hash_gather: the row of lookup %d (position %d, head %d) is outside the owned "
+                              "range" % (bad, bad // heads, bad % heads))
     return out
 
 

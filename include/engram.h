@@ -134,6 +134,28 @@ int engram_hash_slice(const int64_t* tokens, int64_t batch, int64_t seq_len, int
 int engram_gather(const void* table, int32_t dtype, int64_t row_begin, int64_t num_rows, int32_t dim,
                   const int64_t* rows, int64_t n, void* out, int64_t* status, hipStream_t stream);
 
+/* The forward in one call: engram_hash of every position, then engram_gather of
+ * its H rows (engram API page, Qwen3_8_FlashNextNGramEmbedding: the input IDs are
+ * hashed (_hash_input_ids) and the head rows looked up (_lookup_ngram_ids), on
+ * the owner's shard as Qwen3_8_FlashNextOwnerShardedEmbedding does).
+ *   tokens    device int64 [batch][seq_len]
+ *   table, dtype, row_begin, num_rows, dim, status: as for engram_gather
+ *   out       device [batch][seq_len][H][dim] of `dtype`, 16-byte aligned:
+ *             out[b][t][h] = table[row(b, t, h) - row_begin], bit for bit what
+ *             engram_hash followed by engram_gather gives
+ *   rows_out  device int64 [batch][seq_len][H], 16-byte aligned, or NULL: the
+ *             hashed rows, as engram_hash writes them
+ * For the released layout (ngram_size 3, 8 heads per order), a 160-wide bf16
+ * table and at most 2^25 positions, one kernel hashes and gathers, and rows_out
+ * may be NULL (the rows are then neither written nor read).  Any other call runs
+ * the hash into rows_out and the gather from it, and rows_out is required.
+ * Lookup index i = (b * seq_len + t) * H + h in `status`.  Requires batch *
+ * seq_len <= 2^32 - 64.
+ * Returns ENGRAM_OK, ENGRAM_EINVAL, ENGRAM_EDTYPE or ENGRAM_ESPEC. */
+int engram_hash_gather(const int64_t* tokens, int64_t batch, int64_t seq_len, const engram_hash_spec* spec,
+                       const void* table, int32_t dtype, int64_t row_begin, int64_t num_rows, int32_t dim,
+                       void* out, int64_t* rows_out, int64_t* status, hipStream_t stream);
+
 /* Bytes of device workspace engram_scatter_add needs for n lookups into a
  * num_rows-row shard with rows of dim values (256-byte aligned start). */
 size_t engram_scatter_add_workspace(int64_t n, int64_t num_rows, int32_t dim);

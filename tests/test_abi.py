@@ -323,3 +323,36 @@ def test_noalloc_refuses_sizes_past_its_scratch(lib):
                                           None) == B.ENGRAM_EWORKSPACE
     text = open(os.path.join(ROOT, "include", "engram.h")).read()
     assert "#define ENGRAM_NOALLOC_SCRATCH_BYTES (64u << 20)" in text and B.NOALLOC_SCRATCH_BYTES == 64 << 20
+
+
+def test_hash_gather_rejects_bad_arguments(lib):
+    """engram_hash_gather checks everything engram_hash and engram_gather check, and
+    refuses a NULL rows_out where the forward needs it (any but the fused layout)."""
+    f = ctypes.c_void_p(0x10000)
+    mis = ctypes.c_void_p(0x10008)  # 8-byte but not 16-byte aligned
+    bf, f32 = B.ENGRAM_BF16, B.ENGRAM_F32
+    s = ctypes.byref(E.qwen3_8_flash_next_spec())
+    call = lib.engram_hash_gather
+    assert call(f, 1, 8, s, f, 7, 0, 10, 160, f, f, None, None) == B.ENGRAM_EDTYPE
+    for dim in (0, 100, 1024):
+        assert call(f, 1, 8, s, f, bf, 0, 10, dim, f, f, None, None) == B.ENGRAM_EINVAL
+    bad = E.qwen3_8_flash_next_spec()
+    bad.head_mod[3] = 1
+    assert call(f, 1, 8, ctypes.byref(bad), f, bf, 0, 10, 160, f, f, None, None) == B.ENGRAM_ESPEC
+    assert call(f, 1, 8, None, f, bf, 0, 10, 160, f, f, None, None) == B.ENGRAM_EINVAL
+    assert call(f, -1, 8, s, f, bf, 0, 10, 160, f, f, None, None) == B.ENGRAM_EINVAL
+    assert call(f, 1, 8, s, f, bf, -1, 10, 160, f, f, None, None) == B.ENGRAM_EINVAL
+    assert call(f, 1, 8, s, f, bf, 0, -10, 160, f, f, None, None) == B.ENGRAM_EINVAL
+    assert call(None, 1, 8, s, f, bf, 0, 10, 160, f, f, None, None) == B.ENGRAM_EINVAL
+    assert call(f, 1, 8, s, None, bf, 0, 10, 160, f, f, None, None) == B.ENGRAM_EINVAL
+    assert call(f, 1, 8, s, f, bf, 0, 10, 160, None, f, None, None) == B.ENGRAM_EINVAL
+    assert call(f, 1, 8, s, f, bf, 0, 10, 160, mis, f, None, None) == B.ENGRAM_EINVAL
+    assert call(f, 1, 8, s, f, bf, 0, 10, 160, f, mis, None, None) == B.ENGRAM_EINVAL
+    # rows_out may be NULL only for the fused layout (3-gram, 8 heads per order, bf16 x 160)
+    assert call(f, 1, 8, s, f, f32, 0, 10, 160, f, None, None, None) == B.ENGRAM_EINVAL
+    assert call(f, 1, 8, s, f, bf, 0, 10, 128, f, None, None, None) == B.ENGRAM_EINVAL
+    two = E.make_hash_spec(2, 8, 7, (3, 5), [101] * 8, [101 * h for h in range(8)])
+    assert call(f, 1, 8, ctypes.byref(two), f, bf, 0, 10, 160, f, None, None, None) == B.ENGRAM_EINVAL
+    # launches of 2^32 work-items or more are refused; empty work succeeds
+    assert call(f, 1 << 26, 64, s, f, bf, 0, 10, 160, f, f, None, None) == B.ENGRAM_EINVAL
+    assert call(None, 0, 8, s, None, bf, 0, 10, 160, None, None, None, None) == B.ENGRAM_OK

@@ -14,12 +14,11 @@ import bench  # noqa: E402
 # summary file -> kernel source it was measured on
 SUMMARIES = {
     "scatter_apply_long_counters.txt": "scatter.hip",
-    "gather_long_counters.txt": "gather.hip",
-    "gather_full-sft_counters.txt": "gather.hip",
+    "gather_long_counters.txt": "lookup.hip",
+    "gather_full-sft_counters.txt": "lookup.hip",
     "gather_owner_counters.txt": "gather.hip",
     "scatter_apply_owner_counters.txt": "scatter.hip",
     "hash_long_counters.txt": "hash.hip",
-    "hash_full-sft_counters.txt": "hash.hip",
     "scatter_plan_long_counters.txt": "scatter.hip",
     "scatter_plan_owner_counters.txt": "scatter.hip",
     "conv_fwd_ple_counters.txt": "ple.hip",

@@ -1,0 +1,129 @@
+"""Fused forward (engram_hash_gather): bit-exact against the oracle's hash followed
+by the oracle's gather.  The released head layout (3-gram, 8 heads per order)
+with a 160-wide bf16 table takes the one-kernel path; other layouts and fp32
+tables take the hash-then-gather path through rows_out."""
+import numpy as np
+import pytest
+import torch
+
+import hashed_gram_embedding_engram_amd as E
+import workloads as W
+from oracle import c_oracle
+from tests.gpu_common import full_oracle_spec, oracle_hash, product_spec_from, requires_gpu, to_host
+
+pytestmark = [pytest.mark.gpu, requires_gpu]
+
+INT64_MAX, INT64_MIN = (1 << 63) - 1, -(1 << 63)
+
+
+def bf16_table(num_rows, seed, dtype=torch.bfloat16):
+    g = torch.Generator(device="cuda")
+    g.manual_seed(seed)
+    return torch.randn((num_rows, 160), generator=g, device="cuda").to(dtype)
+
+
+def check(ids, ws, table, row_begin=0, fill=None, with_rows=True, spec=None):
+    """Run the fused forward and compare out, status and rows_out with the oracle."""
+    spec = spec if spec is not None else product_spec_from(ws, fill)
+    ids = np.ascontiguousarray(ids, dtype=np.int64)
+    batch, seq = ids.shape
+    heads = spec.num_heads
+    tokens = torch.from_numpy(ids).cuda()
+    status = torch.empty((), dtype=torch.int64, device="cuda")
+    rows_out = torch.full((batch, seq, heads), -7, dtype=torch.int64, device="cuda") if with_rows else None
+    out = E.engram_hash_gather(tokens, spec, table, row_begin, rows_out=rows_out, status=status, validate=False)
+    torch.cuda.synchronize()
+    ref_rows = oracle_hash(ids, ws, fill=fill)
+    ref, bad = c_oracle.gather(to_host(table), ref_rows.reshape(-1), row_begin)
+    assert out.shape == (batch, seq, heads, table.shape[1])
+    assert np.array_equal(to_host(out).reshape(ref.shape).view(np.uint8), ref.view(np.uint8))
+    assert int(status.item()) == bad
+    if with_rows:
+        assert np.array_equal(rows_out.cpu().numpy(), ref_rows)
+    return bad
+
+
+def uniform_ids(shape, seed, eos, p_eos=1.0 / 16, vocab=1000):
+    rng = np.random.default_rng(seed)
+    ids = rng.integers(0, vocab, size=shape, dtype=np.int64)
+    ids[rng.random(shape) < p_eos] = eos
+    return ids
+
+
+@pytest.mark.parametrize("with_rows", [True, False])
+def test_tiny_tokens_fused(with_rows):
+    ws = W.tiny_spec()
+    assert check(W.tiny_tokens(), ws, bf16_table(ws["num_rows"], 1), with_rows=with_rows) == -1
+
+
+@pytest.mark.parametrize("shape", [(1, 1), (1, 2), (1, 3), (3, 5), (2, 63), (2, 64), (2, 65), (4, 1000), (7, 333)])
+def test_ragged_shapes(shape):
+    """Batch rows of every short length (history before the row start is the fill)
+    and shapes whose positions end in a partial block."""
+    ws = W.tiny_spec()
+    ids = uniform_ids(shape, sum(shape), ws["eos"])
+    check(ids, ws, bf16_table(ws["num_rows"], 2), with_rows=shape[0] % 2 == 1)
+
+
+@pytest.mark.parametrize("fill", [0, -1, INT64_MAX, INT64_MIN, 998])
+def test_fill_values(fill):
+    ws = W.tiny_spec()
+    ids = uniform_ids((3, 200), 7, ws["eos"], p_eos=0.2)
+    check(ids, ws, bf16_table(ws["num_rows"], 3), fill=fill)
+
+
+def test_eos_runs_and_extreme_tokens():
+    """Runs of EOS, EOS at the first and last positions, and int64 extremes as tokens."""
+    ws = W.tiny_spec()
+    e = ws["eos"]
+    ids = np.array([[e, e, 5, e, e, e, 6, 7, 8, e, 9, e],
+                    [1, 2, 3, 4, e, 1, 2, e, e, 3, 4, 5],
+                    [INT64_MAX, INT64_MIN, -1, 0, e, INT64_MIN, INT64_MAX, 1 << 40, -(1 << 40), e, 2, 3]],
+                   dtype=np.int64)
+    check(ids, ws, bf16_table(ws["num_rows"], 4))
+
+
+def test_rows_outside_the_shard():
+    """A shard in the middle of the table: rows outside it give zero output rows and
+    the lowest such lookup index in status."""
+    ws = W.tiny_spec()
+    row_begin, num_rows = 20_000, 30_000
+    ids = uniform_ids((5, 300), 11, ws["eos"])
+    bad = check(ids, ws, bf16_table(num_rows, 5), row_begin=row_begin)
+    assert bad >= 0
+
+
+def test_released_constants_on_the_owner_shard():
+    """The released spec (moduli above 20,000,000, Barrett reduction) on owner 0's
+    5,000,024-row shard, with an SFT batch: most rows fall outside the shard."""
+    ws = full_oracle_spec()
+    ids, _ = W.sft_batch(seed=3)
+    table = bf16_table(W.OWNER_ROWS, 6)
+    check(ids, ws, table, spec=E.qwen3_8_flash_next_spec())
+
+
+def test_sft_batch_on_its_table():
+    """The SFT configuration's spec and 10,000,000-row table, all 524,288 lookups."""
+    ws = W.sft_spec()
+    ids, _ = W.sft_batch(seed=0)
+    check(ids, ws, bf16_table(ws["num_rows"], 7))
+
+
+def test_two_kernel_path():
+    """fp32 table and a 2-gram layout: the forward runs the hash into rows_out and
+    the gather from it; without rows_out such a call is refused."""
+    ws = W.tiny_spec()
+    ids = uniform_ids((2, 100), 13, ws["eos"])
+    check(ids, ws, bf16_table(ws["num_rows"], 8, torch.float32))
+    with pytest.raises(E.EngramError):
+        E.engram_hash_gather(torch.from_numpy(ids).cuda(), product_spec_from(ws),
+                             bf16_table(ws["num_rows"], 8, torch.float32))
+    two = dict(ws, ngram_size=2, vocab_sizes=ws["vocab_sizes"][:8], offsets=ws["offsets"][:8])
+    check(ids, two, bf16_table(ws["num_rows"], 9))
+
+
+def test_validate_raises_on_rows_outside_the_shard():
+    ws = W.tiny_spec()
+    ids = uniform_ids((1, 64), 17, ws["eos"])
+    with pytest.raises(E.EngramError, match="outside the owned range"):
+        E.engram_hash_gather(torch.from_numpy(ids).cuda(), product_spec_from(ws), bf16_table(10, 10), 0)

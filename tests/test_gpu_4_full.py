@@ -34,15 +34,17 @@ def full_table():
 CHUNK_BYTES = 1 << 30
 
 
-def streamed_gather_check(table, out, rows_ref, row_begin=0):
-    """Every lookup's output row equals the oracle's gather of the table row it
-    names.  The lookups are ordered by row on the host; for each chunk of table
-    rows holding at least one of them, the chunk is copied to the host and the
-    C oracle gathers exactly those lookups from it."""
+def streamed_gather_check(table, outs, rows_ref, row_begin=0):
+    """Every lookup's output row, in each of `outs` (one output or several), equals
+    the oracle's gather of the table row it names.  The lookups are ordered by row
+    on the host; for each chunk of table rows holding at least one of them, the
+    chunk is copied to the host and the C oracle gathers exactly those lookups
+    from it."""
     rows_ref = np.ascontiguousarray(rows_ref, dtype=np.int64).reshape(-1)
     num_rows, dim = table.shape
-    got_all = to_host(out.reshape(-1, dim))
-    assert got_all.shape[0] == rows_ref.size
+    outs = outs if isinstance(outs, (list, tuple)) else [outs]
+    got = [to_host(o.reshape(-1, dim)) for o in outs]
+    assert all(g.shape[0] == rows_ref.size for g in got)
     order = np.argsort(rows_ref, kind="stable")
     srt = rows_ref[order]
     assert srt[0] >= row_begin and srt[-1] < row_begin + num_rows     # every row lies in the table
@@ -59,21 +61,33 @@ def streamed_gather_check(table, out, rows_ref, row_begin=0):
         sel = order[lo:hi]
         ref, bad = c_oracle.gather(chunk, rows_ref[sel], row_begin=row_begin + c0)
         assert bad == -1
-        if not np.array_equal(got_all[sel], ref):
-            i = int(np.argwhere((got_all[sel] != ref).any(axis=1))[0][0])
-            raise AssertionError("lookup %d (row %d) differs from the oracle" % (sel[i], rows_ref[sel[i]]))
+        for k, got_all in enumerate(got):
+            if not np.array_equal(got_all[sel], ref):
+                i = int(np.argwhere((got_all[sel] != ref).any(axis=1))[0][0])
+                raise AssertionError("output %d: lookup %d (row %d) differs from the oracle"
+                                     % (k, sel[i], rows_ref[sel[i]]))
         checked += hi - lo
     assert checked == rows_ref.size
 
 
 def test_full_table_sft_forward(full_table):
+    """Hash then gather, and the fused forward (with and without its rows), on
+    the SFT batch: every lookup of both outputs against the oracle."""
     ids, _ = W.sft_batch(0)
-    rows = E.engram_hash(torch.from_numpy(ids).cuda(), E.qwen3_8_flash_next_spec())
+    tokens = torch.from_numpy(ids).cuda()
+    spec = E.qwen3_8_flash_next_spec()
+    rows = E.engram_hash(tokens, spec)
     out = E.engram_gather(full_table, rows)
+    fused_rows = torch.empty_like(rows)
+    fused = E.engram_hash_gather(tokens, spec, full_table, rows_out=fused_rows)
+    fused_bare = E.engram_hash_gather(tokens, spec, full_table)
     rows_ref = oracle_hash(ids, full_oracle_spec())
     assert np.array_equal(rows.cpu().numpy(), rows_ref)
-    assert out.shape == (8, 4096, 16, 160)
-    streamed_gather_check(full_table, out, rows_ref)
+    assert np.array_equal(fused_rows.cpu().numpy(), rows_ref)
+    assert out.shape == fused.shape == (8, 4096, 16, 160)
+    assert torch.equal(fused.view(torch.int16), fused_bare.view(torch.int16))
+    del fused_bare
+    streamed_gather_check(full_table, [out, fused], rows_ref)
 
 
 def test_full_table_long_context_step(full_table):
@@ -82,15 +96,16 @@ def test_full_table_long_context_step(full_table):
     tokens = torch.from_numpy(ids).cuda()
     rows = E.engram_hash(tokens, E.qwen3_8_flash_next_spec())
     out = E.engram_gather(full_table, rows)
+    fused = E.engram_hash_gather(tokens, E.qwen3_8_flash_next_spec(), full_table)   # the benchmark's forward
     g = torch.Generator(device="cuda")
     g.manual_seed(77)
     dy = torch.randn(out.shape, generator=g, device="cuda").to(torch.bfloat16)
     ur, ug = E.engram_scatter_add(rows, dy, W.FULL_ROWS)
     rows_ref = oracle_hash(ids, full_oracle_spec())
     assert np.array_equal(rows.cpu().numpy(), rows_ref)
-    streamed_gather_check(full_table, out, rows_ref)
+    streamed_gather_check(full_table, [out, fused], rows_ref)
     dy_host = to_host(dy).reshape(-1, 160)
-    del out, dy
+    del out, fused, dy
     rur, rug, bad = c_oracle.scatter_add_compact(rows_ref.reshape(-1), dy_host, W.FULL_ROWS)
     assert bad == -1
     assert np.array_equal(ur.cpu().numpy(), rur)

@@ -3,9 +3,11 @@ library's launches on the capture stream).  Every reset the library makes
 (status words, counters, count totals) is a kernel, never a memset, so a
 replay must equal the eager calls bit for bit.
 
-The graph holds the step as the benchmark runs it: hash and gather on the
-capture stream, the backward plan on a forked stream joined before the apply.
-Each replay gets fresh inputs copied into the captured buffers and poisoned
+The graph holds the step in both forms: hash and gather on the capture
+stream with the backward plan on a forked stream joined before the apply; and
+as the benchmark runs it, the fused hash-and-gather forward on the capture
+stream while the forked stream hashes into the rows array and plans.  Each
+replay gets fresh inputs copied into the captured buffers and poisoned
 outputs, with eager calls and synchronisations between replays."""
 import numpy as np
 import pytest
@@ -18,7 +20,8 @@ from tests.gpu_common import product_spec_from, requires_gpu
 pytestmark = [pytest.mark.gpu, requires_gpu]
 
 
-def test_step_graph_replays_equal_eager():
+@pytest.mark.parametrize("fused", [False, True])
+def test_step_graph_replays_equal_eager(fused):
     dev = torch.device("cuda")
     ws = W.sft_spec()
     R, D = ws["num_rows"], 160
@@ -48,12 +51,20 @@ def test_step_graph_replays_equal_eager():
 
     def step():
         main = torch.cuda.current_stream()
-        E.engram_hash(ids, spec, rows_out=rows)
-        side.wait_stream(main)
-        with torch.cuda.stream(side):
-            E.engram_scatter_add_plan(rows, R, D, workspace=workspace, uniq_rows=uniq_rows, num_uniq=num_uniq,
-                                      status=plan_status)
-        E.engram_gather(table, rows, out=out, status=status, validate=False)
+        if fused:
+            side.wait_stream(main)
+            with torch.cuda.stream(side):
+                E.engram_hash(ids, spec, rows_out=rows)
+                E.engram_scatter_add_plan(rows, R, D, workspace=workspace, uniq_rows=uniq_rows, num_uniq=num_uniq,
+                                          status=plan_status)
+            E.engram_hash_gather(ids, spec, table, out=out, status=status, validate=False)
+        else:
+            E.engram_hash(ids, spec, rows_out=rows)
+            side.wait_stream(main)
+            with torch.cuda.stream(side):
+                E.engram_scatter_add_plan(rows, R, D, workspace=workspace, uniq_rows=uniq_rows, num_uniq=num_uniq,
+                                          status=plan_status)
+            E.engram_gather(table, rows, out=out, status=status, validate=False)
         main.wait_stream(side)
         E.engram_scatter_add_apply(dy, n, R, workspace, uniq_grad=uniq_grad)
 
