@@ -185,13 +185,13 @@ def build_workload(name, rotations, dev, table=None):
 
 def run_step(wl, b, ev=None):
     """One step.  From tokens (long, sft, full-sft): the fused hash-and-gather
-    forward on the main stream; with a backward, the hash into the rows array
-    and then the plan (sort by row) on a side stream beside it; the apply once
-    both are done.  From rows (the owner shard, which receives its rows): the
-    plan on the side stream beside the gather, then the apply.  ev: events
-    (step start, side hash end, forward end, side start, plan end, apply
-    start, apply end); an entry may be None, and only the events given are
-    recorded."""
+    forward on the main stream; with a backward, the plan (sort by row) from
+    the same tokens, which hashes the rows itself, on a side stream beside it;
+    the apply once both are done.  No rows array is written or read.  From
+    rows (the owner shard, which receives its rows): the plan on the side
+    stream beside the gather, then the apply.  ev: events (step start, unused,
+    forward end, plan start, plan end, apply start, apply end); an entry may
+    be None, and only the events given are recorded."""
     import torch
 
     import hashed_gram_embedding_engram_amd as E
@@ -205,17 +205,18 @@ def run_step(wl, b, ev=None):
     compact = b.get("compact")
 
     def plan():
-        E.engram_scatter_add_plan(b["rows"], wl["table_rows"], b["dy"].shape[-1], wl["row_begin"],
-                                  workspace=wl["workspace"], uniq_rows=compact[0] if compact else None,
-                                  num_uniq=compact[2] if compact else None, status=b["plan_status"], stream=side)
+        args = dict(workspace=wl["workspace"], uniq_rows=compact[0] if compact else None,
+                    num_uniq=compact[2] if compact else None, status=b["plan_status"], stream=side)
+        if b["tokens"] is not None:   # the rows hashed inside the plan
+            E.engram_scatter_add_plan_from_tokens(b["tokens"], wl["spec"], wl["table_rows"], b["dy"].shape[-1],
+                                                  wl["row_begin"], **args)
+        else:
+            E.engram_scatter_add_plan(b["rows"], wl["table_rows"], b["dy"].shape[-1], wl["row_begin"], **args)
 
     mark(0, main)
     if wl["backward"]:
         side.wait_stream(main)
         mark(3, side)
-        if b["tokens"] is not None:
-            E.engram_hash(b["tokens"], wl["spec"], rows_out=b["rows"], stream=side)
-        mark(1, side)
         plan()
         mark(4, side)
     if b["tokens"] is not None:
@@ -233,11 +234,10 @@ def run_step(wl, b, ev=None):
 
 
 def phases_alone(wl, k):
-    """Median ms of the forward gather (fused with the hash when the workload
-    starts from tokens), the plan (from the rows) and the apply, each run by
+    """Median ms of the forward gather and the plan (each from tokens when the
+    workload starts from them, with the hash inside) and the apply, each run by
     itself on the main stream with nothing beside it, over k launches rotating
-    through the input sets (outside the timed steps).  The rows arrays hold
-    every rotation's rows (the warm-up steps hashed them)."""
+    through the input sets (outside the timed steps)."""
     import torch
 
     import hashed_gram_embedding_engram_amd as E
@@ -259,10 +259,14 @@ def phases_alone(wl, k):
         e[1].record()
         if wl["backward"]:
             compact = b.get("compact")
+            args = dict(workspace=wl["workspace"], uniq_rows=compact[0] if compact else None,
+                        num_uniq=compact[2] if compact else None, status=b["plan_status"])
             e[2].record()
-            E.engram_scatter_add_plan(b["rows"], wl["table_rows"], b["dy"].shape[-1], wl["row_begin"],
-                                      workspace=wl["workspace"], uniq_rows=compact[0] if compact else None,
-                                      num_uniq=compact[2] if compact else None, status=b["plan_status"])
+            if b["tokens"] is not None:   # as the steps run it: the rows hashed inside the plan
+                E.engram_scatter_add_plan_from_tokens(b["tokens"], wl["spec"], wl["table_rows"], b["dy"].shape[-1],
+                                                      wl["row_begin"], **args)
+            else:
+                E.engram_scatter_add_plan(b["rows"], wl["table_rows"], b["dy"].shape[-1], wl["row_begin"], **args)
             e[3].record()
             e[4].record()
             E.engram_scatter_add_apply(b["dy"], b["n"], wl["table_rows"], wl["workspace"], wl["row_begin"],
@@ -800,13 +804,11 @@ def lookup_line(name, args, dev, table=None):
         run_step(wl, wl["batches"][i % R], evs[i])
     torch.cuda.synchronize()
     alone = None if args.no_alone else phases_alone(wl, min(args.steps, 20))
-    # From tokens the forward is one fused kernel ("gather"), and the hash that
-    # feeds the plan runs on the side stream; from rows there is no hash.
+    # From tokens the forward is one fused kernel ("gather") and the plan
+    # hashes its rows itself; from rows there is no hash.
     spans = {"gather": (0, 2)}
     if wl["backward"]:
-        if fused:
-            spans["hash (side stream)"] = (3, 1)
-        spans.update({"scatter_plan (side stream)": (1, 4), "wait_for_plan": (2, 5), "scatter_apply": (5, 6)})
+        spans.update({"scatter_plan (side stream)": (3, 4), "wait_for_plan": (2, 5), "scatter_apply": (5, 6)})
     phase = {k: sum(e[a].elapsed_time(e[b]) for e in evs) / kb for k, (a, b) in spans.items()}
     phase_pct = {k: percentiles([e[a].elapsed_time(e[b]) for e in evs]) for k, (a, b) in spans.items()}
     phase[dom] = sum(dom_ms) / len(dom_ms)        # the dominant phase from the timed steps themselves
@@ -914,8 +916,7 @@ def lookup_line(name, args, dev, table=None):
                                   "frac_compulsory": round(compulsory["gather"] / (ga / 1e3) / 1e9 / HBM_PEAK_GBPS, 4)}
     # HBM bytes of every phase of the step from the committed counter
     # summaries, against the step time (only when all are current).
-    counted = (["hash"] if fused and wl["backward"] else []) + ["gather"] + \
-        (["scatter_plan", "scatter_apply"] if wl["backward"] else [])
+    counted = ["gather"] + (["scatter_plan", "scatter_apply"] if wl["backward"] else [])
     per = {ph: counter_traffic(PROFILED[name][ph][0], "%s_%s_counters.txt" % (ph, name)) for ph in counted}
     if all(v is not None for v in per.values()):
         total = sum(per.values())
@@ -992,7 +993,7 @@ PROFILED = {
 }
 # Phases whose counter summaries are written (the ones a bench line can name
 # as its dominant kernel).
-COUNTED = {"long": ["hash", "gather", "scatter_plan", "scatter_apply"], "full-sft": ["gather"],
+COUNTED = {"long": ["gather", "scatter_plan", "scatter_apply"], "full-sft": ["gather"],
            "owner": ["gather", "scatter_plan", "scatter_apply"],
            "ple": ["conv_fwd", "norm_fwd", "norm_bwd", "conv_bwd"],
            "route": ["pack_values", "unpack_values", "unpermute_values"]}
@@ -1010,17 +1011,18 @@ WORKLOAD_TEXT = {
 }
 
 
-def sort_nominal_bytes(n, num_rows, uniq=None):
+def sort_nominal_bytes(n, num_rows, uniq=None, from_tokens=False):
     """HBM bytes the backward plan's own traffic model gives for n lookups:
-    keys (8 B row read, 4 B key written), the first pass (4 B read, 8 B
-    written), each later pass (16 B) with its histogram (4 B), the run count's
-    read (4 B) and, in the compact form, the distinct rows' pass (4 B read,
-    8 B per distinct row written)."""
+    keys (8 B row read, or 8 B per token when the plan hashes the rows itself,
+    and 4 B key written), the first pass (4 B read, 8 B written), each later
+    pass (16 B) with its histogram (4 B), the run count's read (4 B) and, in
+    the compact form, the distinct rows' pass (4 B read, 8 B per distinct row
+    written)."""
     bits = 0
     while bits < 32 and (num_rows >> bits) != 0:   # the out-of-range sentinel num_rows sorts last
         bits += 1
     passes = (bits + 7) // 8
-    total = 24 * n + (passes - 1) * 20 * n + 4 * n
+    total = (n // 2 if from_tokens else 8 * n) + 16 * n + (passes - 1) * 20 * n + 4 * n
     if uniq is not None:
         total += 4 * n + 8 * uniq
     return float(total)
@@ -1155,7 +1157,7 @@ def summarize_profiles(name, raw):
         if "scatter_apply" in line["phase_gbps"]:
             alg["scatter_apply"] = comp["scatter_apply"] = line["roofline"]["algorithmic_bytes_per_launch"]
             alg["scatter_plan"] = comp["scatter_plan"] = sort_nominal_bytes(n, cfg["table_rows"],
-                                                                            cfg["distinct_rows_rotation0"])
+                                                                            cfg["distinct_rows_rotation0"], fused)
     for phase in COUNTED[name]:
         if phase not in alg or phase not in fetch:
             continue

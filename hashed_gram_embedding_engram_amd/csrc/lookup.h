@@ -19,4 +19,11 @@ hipError_t launch_hash_gather(const int64_t* tokens, int64_t batch, int64_t seq_
                               const void* table, int elem_bytes, int64_t row_begin, int64_t num_rows, int dim,
                               void* out, int64_t* rows_out, int64_t* status, hipStream_t stream);
 
+// Backward phase 1 from tokens: the plan of engram_scatter_add_plan for the
+// rows the released head layout hashes from `tokens` [batch][seq_len] (16
+// per position), hashed inside the plan's first kernel (scatter.hip).
+hipError_t launch_scatter_plan_tokens(const int64_t* tokens, int64_t batch, int64_t seq_len, const HashParams& p,
+                                      int64_t row_begin, int64_t num_rows, int dim, int64_t* uniq_rows,
+                                      int64_t* num_uniq, void* workspace, int64_t* status, hipStream_t stream);
+
 }  // namespace engram

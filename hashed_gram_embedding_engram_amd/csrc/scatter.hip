@@ -34,6 +34,8 @@
 #include <algorithm>
 
 #include "radix_sort.h"
+#include "hash_math.h"
+#include "lookup.h"
 
 namespace engram {
 namespace {
@@ -141,29 +143,88 @@ __global__ __launch_bounds__(kBlock) void scatter_init_kernel(int64_t* status, u
 
 // Tile histograms count with LDS atomics into one sub-histogram per wave
 // (summed at the end), which keeps same-address conflicts inside a wave.
+// Where the plan's rows come from when it starts from tokens: the token batch
+// they hash from, for the released head layout (3-gram, 8 heads per order:
+// lookup e is head e % 16 of flattened position e / 16; engram API page,
+// Qwen3_8_FlashNextNGramEmbedding: _hash_input_ids with the context of
+// _shift_right_after_eos).
+struct TokenRows {
+    const int64_t* tokens;  // [batch * seq_len], flattened
+    uint32_t seq_len;
+    HashParams p;
+};
+constexpr int kTokenHeads = 16;
+
 // Step 1: keys, digit-0 tile histograms, in-range count.  A key's lookup
-// index is its position, so the first sort pass reads no value array.
-template <int ITEMS>
-__global__ __launch_bounds__(kBlock) void keys_kernel(const int64_t* __restrict__ rows, uint32_t n,
+// index is its position, so the first sort pass reads no value array.  With
+// TOKENS the rows are hashed here: the tile's positions (and the two before
+// them) are staged in LDS, and lane l computes head l % 16 of its lookups'
+// positions (the context of shift s is the token s back unless that lies
+// before the batch row's start or an EOS sits in [t - s, t - 1]; missing
+// context takes the fill value).
+template <int ITEMS, bool TOKENS>
+__global__ __launch_bounds__(kBlock) void keys_kernel(const int64_t* __restrict__ rows, TokenRows tr, uint32_t n,
                                                       int64_t row_begin, uint64_t num_rows,
                                                       uint32_t* __restrict__ keys, DigitCounts dc,
                                                       int64_t* __restrict__ status,
                                                       uint32_t* __restrict__ counters) {
+    constexpr int TILE = kBlock * ITEMS, TILE_POS = TILE / kTokenHeads;
     __shared__ uint32_t s_cnt[kBlock / 64][kRadix];
     __shared__ uint32_t s_valid;
+    __shared__ int64_t s_tok[TOKENS ? TILE_POS + 2 : 1];  // positions p0 - 2 .. p0 + TILE_POS - 1
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
 #pragma unroll
     for (int k = 0; k < kBlock / 64; ++k) s_cnt[k][tid] = 0;
     if (tid == 0) s_valid = 0;
+    const uint32_t p0 = blockIdx.x * (uint32_t)TILE_POS;  // the tile's first position (TOKENS)
+    if (TOKENS) {
+        const uint32_t npos = n / kTokenHeads;
+        for (int i = tid; i < TILE_POS + 2; i += kBlock) {
+            const int64_t q = (int64_t)p0 - 2 + i;
+            s_tok[i] = q >= 0 && q < (int64_t)npos ? tr.tokens[q] : 0;
+        }
+    }
     __syncthreads();
-    const uint32_t base = blockIdx.x * (uint32_t)(kBlock * ITEMS) + (uint32_t)w * (64 * ITEMS);
+    const uint32_t base = blockIdx.x * (uint32_t)TILE + (uint32_t)w * (64 * ITEMS);
     const uint32_t sentinel = (uint32_t)num_rows;
     uint32_t my_valid = 0;
-    // Loads are clamped rather than guarded, so all of a thread's loads are in
-    // flight together (a guarded load becomes a branch that waits for it).
     int64_t r[ITEMS];
+    if (TOKENS) {
+        // This lane's head: modulus, reciprocal and offset selected with
+        // compile-time indices (the parameters stay kernel arguments).
+        const int h = lane & (kTokenHeads - 1);
+        uint64_t mod = tr.p.mod[0], magic = tr.p.magic[0];
+        int64_t off = tr.p.off[0];
 #pragma unroll
-    for (int it = 0; it < ITEMS; ++it) r[it] = rows[min(base + (uint32_t)it * 64 + (uint32_t)lane, n - 1)];
+        for (int j = 1; j < kTokenHeads; ++j)
+            if (h == j) {
+                mod = tr.p.mod[j];
+                magic = tr.p.magic[j];
+                off = tr.p.off[j];
+            }
+        // Item it of this lane is position pos0 + 4 it; its column t advances
+        // by 4 a step, wrapping at the row length.
+        const uint32_t pos0 = (base + (uint32_t)lane) / kTokenHeads;
+        uint32_t t = pos0 % tr.seq_len;
+#pragma unroll
+        for (int it = 0; it < ITEMS; ++it) {
+            const int li = (int)(pos0 + 4u * (uint32_t)it - p0) + 2;
+            const int64_t x0 = s_tok[li], x1 = s_tok[li - 1], x2 = s_tok[li - 2];
+            const bool valid1 = t >= 1 && x1 != tr.p.eos;
+            const bool valid2 = valid1 && t >= 2 && x2 != tr.p.eos;
+            const int64_t ctx1 = valid1 ? x1 : tr.p.fill, ctx2 = valid2 ? x2 : tr.p.fill;
+            const uint64_t mix2 = (uint64_t)x0 * (uint64_t)tr.p.mult[0] ^ (uint64_t)ctx1 * (uint64_t)tr.p.mult[1];
+            const uint64_t mix = h < 8 ? mix2 : mix2 ^ (uint64_t)ctx2 * (uint64_t)tr.p.mult[2];
+            r[it] = (int64_t)floor_mod((int64_t)mix, mod, magic) + off;
+            t += 4;
+            while (t >= tr.seq_len) t -= tr.seq_len;
+        }
+    } else {
+        // Loads are clamped rather than guarded, so all of a thread's loads are
+        // in flight together (a guarded load becomes a branch that waits for it).
+#pragma unroll
+        for (int it = 0; it < ITEMS; ++it) r[it] = rows[min(base + (uint32_t)it * 64 + (uint32_t)lane, n - 1)];
+    }
 #pragma unroll
     for (int it = 0; it < ITEMS; ++it) {
         const uint32_t e = base + (uint32_t)it * 64 + (uint32_t)lane;
@@ -860,8 +921,8 @@ hipError_t dispatch_reduce(const Layout& L, const char* ws, const void* grad_out
 
 // Steps 1-2: keys and the radix passes, ending in the sorted slots.
 template <int ITEMS>
-hipError_t run_sort(const Layout& L, char* ws, const int64_t* rows, int64_t n, int64_t row_begin, int64_t num_rows,
-                    int passes, int64_t* status, hipStream_t stream) {
+hipError_t run_sort(const Layout& L, char* ws, const int64_t* rows, const TokenRows* tr, int64_t n, int64_t row_begin,
+                    int64_t num_rows, int passes, int64_t* status, hipStream_t stream) {
     uint32_t* counters = (uint32_t*)(ws + L.counters);
     const size_t pass_words = count_words(L.num_tiles);  // chunk and group totals of one pass
     uint32_t* count_totals = (uint32_t*)(ws + L.count_totals);
@@ -877,8 +938,12 @@ hipError_t run_sort(const Layout& L, char* ws, const int64_t* rows, int64_t n, i
         v_cur = (uint32_t*)(ws + L.spare_vals); v_nxt = (uint32_t*)(ws + L.sorted_vals);
     }
     auto pass_counts = [&](int p) { return make_digit_counts(ws + L.hist, count_totals + p * pass_words, L.num_tiles); };
-    hipLaunchKernelGGL(keys_kernel<ITEMS>, dim3(tiles), dim3(kBlock), 0, stream, rows, nn, row_begin, (uint64_t)num_rows,
-                       k_cur, pass_counts(0), status, counters);
+    if (tr)
+        hipLaunchKernelGGL((keys_kernel<ITEMS, true>), dim3(tiles), dim3(kBlock), 0, stream, nullptr, *tr, nn,
+                           row_begin, (uint64_t)num_rows, k_cur, pass_counts(0), status, counters);
+    else
+        hipLaunchKernelGGL((keys_kernel<ITEMS, false>), dim3(tiles), dim3(kBlock), 0, stream, rows, TokenRows{}, nn,
+                           row_begin, (uint64_t)num_rows, k_cur, pass_counts(0), status, counters);
     if ((err = hipGetLastError()) != hipSuccess) return err;
     for (int p = 0; p < passes; ++p) {
         const int shift = 8 * p;
@@ -908,9 +973,11 @@ size_t scatter_workspace_bytes(int64_t n, int64_t num_rows, int dim) {
     return make_layout(n, dim).total;
 }
 
-hipError_t launch_scatter_plan(const int64_t* rows, int64_t n, int64_t row_begin, int64_t num_rows, int dim,
-                               int64_t* uniq_rows, int64_t* num_uniq, void* workspace, int64_t* status,
-                               hipStream_t stream) {
+namespace {
+
+hipError_t scatter_plan(const int64_t* rows, const TokenRows* tr, int64_t n, int64_t row_begin, int64_t num_rows,
+                        int dim, int64_t* uniq_rows, int64_t* num_uniq, void* workspace, int64_t* status,
+                        hipStream_t stream) {
     const Layout L = make_layout(n, dim);
     char* ws = (char*)workspace;
     uint32_t* counters = (uint32_t*)(ws + L.counters);
@@ -926,9 +993,9 @@ hipError_t launch_scatter_plan(const int64_t* rows, int64_t n, int64_t row_begin
     hipError_t err = hipGetLastError();
     if (err != hipSuccess || n == 0) return err;
     const int items = sort_items(n);
-    if (items == 8) err = run_sort<8>(L, ws, rows, n, row_begin, num_rows, passes, status, stream);
-    else if (items == 16) err = run_sort<16>(L, ws, rows, n, row_begin, num_rows, passes, status, stream);
-    else err = run_sort<24>(L, ws, rows, n, row_begin, num_rows, passes, status, stream);
+    if (items == 8) err = run_sort<8>(L, ws, rows, tr, n, row_begin, num_rows, passes, status, stream);
+    else if (items == 16) err = run_sort<16>(L, ws, rows, tr, n, row_begin, num_rows, passes, status, stream);
+    else err = run_sort<24>(L, ws, rows, tr, n, row_begin, num_rows, passes, status, stream);
     if (err != hipSuccess) return err;
 
     const uint32_t nn = (uint32_t)n;
@@ -944,6 +1011,22 @@ hipError_t launch_scatter_plan(const int64_t* rows, int64_t n, int64_t row_begin
         hipLaunchKernelGGL(uniq_rows_kernel, dim3(run_blocks), dim3(kBlock), 0, stream, k_cur, nn, counters,
                            (const uint32_t*)(ws + L.block_base), row_begin, uniq_rows, span);
     return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_scatter_plan(const int64_t* rows, int64_t n, int64_t row_begin, int64_t num_rows, int dim,
+                               int64_t* uniq_rows, int64_t* num_uniq, void* workspace, int64_t* status,
+                               hipStream_t stream) {
+    return scatter_plan(rows, nullptr, n, row_begin, num_rows, dim, uniq_rows, num_uniq, workspace, status, stream);
+}
+
+hipError_t launch_scatter_plan_tokens(const int64_t* tokens, int64_t batch, int64_t seq_len, const HashParams& p,
+                                      int64_t row_begin, int64_t num_rows, int dim, int64_t* uniq_rows,
+                                      int64_t* num_uniq, void* workspace, int64_t* status, hipStream_t stream) {
+    const TokenRows tr{tokens, (uint32_t)seq_len, p};
+    return scatter_plan(nullptr, &tr, batch * seq_len * kTokenHeads, row_begin, num_rows, dim, uniq_rows, num_uniq,
+                        workspace, status, stream);
 }
 
 hipError_t launch_scatter_apply(const void* grad_out, int elem_bytes, int dim, int64_t n, int64_t num_rows,

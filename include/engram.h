@@ -226,6 +226,24 @@ int engram_scatter_add_apply(const void* grad_out, int32_t dtype, int32_t dim, i
                              int64_t num_rows, float* grad_dense, float* uniq_grad, const void* workspace,
                              size_t workspace_bytes, hipStream_t stream);
 
+/* engram_scatter_add_plan for the rows engram_hash would write from `tokens`, hashed
+ * inside the plan (engram API page, Qwen3_8_FlashNextNGramEmbedding: the backward of
+ * _lookup_ngram_ids reaches the rows _hash_input_ids gives; the hash depends on the
+ * tokens alone, so the backward may hash again instead of keeping the rows).  The
+ * released layout only (ngram_size 3, 8 heads per order: n = batch * seq_len * 16
+ * lookups, lookup (b * seq_len + t) * 16 + h); the plan, its outputs and the apply
+ * that follows (with this n) are exactly those of engram_scatter_add_plan on the
+ * hashed rows.
+ *   tokens    device int64 [batch][seq_len]
+ *   other arguments as for engram_scatter_add_plan; the workspace is
+ *   engram_scatter_add_workspace(n, num_rows, dim) bytes
+ * Requires n < 2^31.  Returns ENGRAM_OK, ENGRAM_EINVAL (also for another head
+ * layout), ENGRAM_ESPEC or ENGRAM_EWORKSPACE. */
+int engram_scatter_add_plan_from_tokens(const int64_t* tokens, int64_t batch, int64_t seq_len,
+                                        const engram_hash_spec* spec, int64_t row_begin, int64_t num_rows, int32_t dim,
+                                        int64_t* uniq_rows, int64_t* num_uniq, void* workspace,
+                                        size_t workspace_bytes, int64_t* status, hipStream_t stream);
+
 /* ---- Owner routing: the single-GPU half of the row-owner exchange ----------
  * Engram API page, Qwen3_8_FlashNextOwnerShardedEmbedding: with `world` owners,
  * rank r owns global rows [r * local_rows, (r + 1) * local_rows), local_rows =

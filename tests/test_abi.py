@@ -356,3 +356,24 @@ def test_hash_gather_rejects_bad_arguments(lib):
     # launches of 2^32 work-items or more are refused; empty work succeeds
     assert call(f, 1 << 26, 64, s, f, bf, 0, 10, 160, f, f, None, None) == B.ENGRAM_EINVAL
     assert call(None, 0, 8, s, None, bf, 0, 10, 160, None, None, None, None) == B.ENGRAM_OK
+
+
+def test_plan_from_tokens_rejects_bad_arguments(lib):
+    f = ctypes.c_void_p(0x10000)
+    mis = ctypes.c_void_p(0x10004)
+    s = ctypes.byref(E.qwen3_8_flash_next_spec())
+    call = lib.engram_scatter_add_plan_from_tokens
+    ws = lib.engram_scatter_add_workspace(8 * 16, 1000, 160)
+    # (tokens, batch, seq_len, spec, row_begin, num_rows, dim, uniq_rows, num_uniq, workspace, bytes, status, stream)
+    two = E.make_hash_spec(2, 8, 7, (3, 5), [101] * 8, [101 * h for h in range(8)])
+    assert call(f, 1, 8, ctypes.byref(two), 0, 1000, 160, None, None, f, ws, None, None) == B.ENGRAM_EINVAL
+    bad = E.qwen3_8_flash_next_spec()
+    bad.head_mod[0] = 0
+    assert call(f, 1, 8, ctypes.byref(bad), 0, 1000, 160, None, None, f, ws, None, None) == B.ENGRAM_ESPEC
+    assert call(None, 1, 8, s, 0, 1000, 160, None, None, f, ws, None, None) == B.ENGRAM_EINVAL
+    assert call(mis, 1, 8, s, 0, 1000, 160, None, None, f, ws, None, None) == B.ENGRAM_EINVAL
+    assert call(f, -1, 8, s, 0, 1000, 160, None, None, f, ws, None, None) == B.ENGRAM_EINVAL
+    assert call(f, 1 << 20, 1 << 7, s, 0, 1000, 160, None, None, f, ws, None, None) == B.ENGRAM_EINVAL  # n = 2^31
+    assert call(f, 1, 8, s, 0, 1000, 160, None, None, f, ws - 1, None, None) == B.ENGRAM_EWORKSPACE
+    assert call(f, 1, 8, s, 0, 1000, 160, None, None, None, ws, None, None) == B.ENGRAM_EWORKSPACE
+    assert call(f, 1, 8, s, 0, 1000, 0, None, None, f, ws, None, None) == B.ENGRAM_EINVAL

@@ -18,7 +18,6 @@ SUMMARIES = {
     "gather_full-sft_counters.txt": "lookup.hip",
     "gather_owner_counters.txt": "gather.hip",
     "scatter_apply_owner_counters.txt": "scatter.hip",
-    "hash_long_counters.txt": "hash.hip",
     "scatter_plan_long_counters.txt": "scatter.hip",
     "scatter_plan_owner_counters.txt": "scatter.hip",
     "conv_fwd_ple_counters.txt": "ple.hip",
@@ -114,3 +113,4 @@ def test_sort_nominal_bytes():
     assert bench.sort_nominal_bytes(n, 5_000_024) == 68 * n
     assert bench.sort_nominal_bytes(n, (1 << 24) - 1) == 68 * n   # the sentinel fits 24 bits
     assert bench.sort_nominal_bytes(n, 1 << 24) == 88 * n           # it needs a 25th
+    assert bench.sort_nominal_bytes(n, 320_001_536, u, from_tokens=True) == 92 * n + 8 * u - 8 * n + n // 2

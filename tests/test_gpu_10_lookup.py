@@ -1,7 +1,9 @@
-"""Fused forward (engram_hash_gather): bit-exact against the oracle's hash followed
-by the oracle's gather.  The released head layout (3-gram, 8 heads per order)
-with a 160-wide bf16 table takes the one-kernel path; other layouts and fp32
-tables take the hash-then-gather path through rows_out."""
+"""The path from tokens without a rows array.  Fused forward (engram_hash_gather):
+bit-exact against the oracle's hash followed by the oracle's gather; the released
+head layout (3-gram, 8 heads per order) with a 160-wide bf16 table takes the
+one-kernel path, other layouts and fp32 tables the hash-then-gather path through
+rows_out.  The backward's plan from tokens (engram_scatter_add_plan_from_tokens):
+plan + apply against the oracle's scatter-add of the oracle's rows."""
 import numpy as np
 import pytest
 import torch
@@ -9,7 +11,7 @@ import torch
 import hashed_gram_embedding_engram_amd as E
 import workloads as W
 from oracle import c_oracle
-from tests.gpu_common import full_oracle_spec, oracle_hash, product_spec_from, requires_gpu, to_host
+from tests.gpu_common import assert_close_to_fp64, full_oracle_spec, oracle_hash, product_spec_from, requires_gpu, to_host
 
 pytestmark = [pytest.mark.gpu, requires_gpu]
 
@@ -127,3 +129,110 @@ def test_validate_raises_on_rows_outside_the_shard():
     ids = uniform_ids((1, 64), 17, ws["eos"])
     with pytest.raises(E.EngramError, match="outside the owned range"):
         E.engram_hash_gather(torch.from_numpy(ids).cuda(), product_spec_from(ws), bf16_table(10, 10), 0)
+
+
+# ---- The backward's plan from tokens (engram_scatter_add_plan_from_tokens): the
+# rows are hashed inside the plan's first kernel; plan + apply must equal the
+# oracle's scatter-add of the oracle's rows, compact and dense.
+
+def grads(n, seed, dim=160):
+    g = torch.Generator(device="cuda")
+    g.manual_seed(seed)
+    return torch.randn((n, dim), generator=g, device="cuda").to(torch.bfloat16)
+
+
+def check_plan_from_tokens(ids, ws, num_rows, row_begin=0, fill=None, dim=160, dense=False, seed=0):
+    spec = product_spec_from(ws, fill)
+    ids = np.ascontiguousarray(ids, dtype=np.int64)
+    tokens = torch.from_numpy(ids).cuda()
+    n = ids.size * 16
+    dy = grads(n, seed, dim)
+    status = torch.empty((), dtype=torch.int64, device="cuda")
+    ur = torch.full((n,), -7, dtype=torch.int64, device="cuda")
+    nu = torch.empty((), dtype=torch.int64, device="cuda")
+    ws_t = E.engram_scatter_add_plan_from_tokens(tokens, spec, num_rows, dim, row_begin, uniq_rows=ur, num_uniq=nu,
+                                                 status=status)
+    rows_ref = oracle_hash(ids, ws, fill=fill).reshape(-1)
+    dy_host = to_host(dy)
+    if dense:
+        g = torch.zeros((num_rows, dim), dtype=torch.float32, device="cuda")
+        E.engram_scatter_add_apply(dy, n, num_rows, ws_t, row_begin, grad_dense=g)
+        ref, rbad = c_oracle.scatter_add_dense(rows_ref, dy_host, num_rows, row_begin)
+        torch.cuda.synchronize()
+        assert int(status.item()) == rbad
+        assert_close_to_fp64(g.cpu().numpy(), ref, "dense sums from tokens")
+        return rbad
+    ug = torch.empty((n, dim), dtype=torch.float32, device="cuda")
+    E.engram_scatter_add_apply(dy, n, num_rows, ws_t, row_begin, uniq_grad=ug)
+    torch.cuda.synchronize()
+    rur, rug, rbad = c_oracle.scatter_add_compact(rows_ref, dy_host, num_rows, row_begin)
+    u = int(nu.item())
+    assert int(status.item()) == rbad
+    assert u == rur.size and np.array_equal(ur[:u].cpu().numpy(), rur)
+    assert_close_to_fp64(ug[:u].cpu().numpy(), rug, "compact sums from tokens")
+    return rbad
+
+
+@pytest.mark.parametrize("shape", [(1, 1), (1, 2), (1, 3), (3, 5), (2, 63), (4, 1000), (7, 333), (1, 4099)])
+def test_plan_from_tokens_ragged(shape):
+    ws = W.tiny_spec()
+    check_plan_from_tokens(uniform_ids(shape, sum(shape) + 1, ws["eos"]), ws, ws["num_rows"], seed=sum(shape))
+
+
+@pytest.mark.parametrize("fill", [0, -1, INT64_MAX, INT64_MIN])
+def test_plan_from_tokens_fill_values(fill):
+    ws = W.tiny_spec()
+    check_plan_from_tokens(uniform_ids((3, 300), 19, ws["eos"], p_eos=0.2), ws, ws["num_rows"], fill=fill,
+                           dense=fill == -1)
+
+
+def test_plan_from_tokens_outside_the_shard():
+    ws = W.tiny_spec()
+    bad = check_plan_from_tokens(uniform_ids((5, 300), 23, ws["eos"]), ws, 30_000, row_begin=20_000, dim=8)
+    assert bad >= 0
+
+
+@pytest.mark.parametrize("seq", [1 << 16, (1 << 16) + 3, (1 << 17) + 5, 1 << 18])
+def test_plan_from_tokens_every_tile_size(seq):
+    """One long row: 2^20, 2^20 + 48, 2^21 + 80 and 2^22 lookups take the three tile
+    sizes of the plan's sort, each with its own stretch of positions per tile."""
+    ws = W.tiny_spec()
+    check_plan_from_tokens(uniform_ids((1, seq), seq % 97, ws["eos"], p_eos=1 / 64), ws, ws["num_rows"], dim=8,
+                           seed=seq % 89)
+
+
+def test_plan_from_tokens_sft_batch():
+    ws = W.sft_spec()
+    ids, _ = W.sft_batch(seed=2)
+    check_plan_from_tokens(ids, ws, ws["num_rows"], dim=8, seed=5)
+
+
+def test_plan_from_tokens_equals_plan_from_rows_long_context():
+    """The long-context stream with the released constants over the full row range:
+    the plan from tokens and the plan from engram_hash's rows give the same distinct
+    rows and the same sums bit for bit (the rows path is checked against the oracle
+    in the full-table tests)."""
+    ids, _ = W.long_context_stream(1)
+    tokens = torch.from_numpy(ids).cuda()
+    spec = E.qwen3_8_flash_next_spec()
+    n = ids.size * 16
+    dy = grads(n, 31)
+    ur_a, ug_a = E.engram_scatter_add(E.engram_hash(tokens, spec), dy, W.FULL_ROWS)
+    ur_b = torch.empty(n, dtype=torch.int64, device="cuda")
+    nu_b = torch.empty((), dtype=torch.int64, device="cuda")
+    ug_b = torch.empty((n, 160), dtype=torch.float32, device="cuda")
+    wsb = E.engram_scatter_add_plan_from_tokens(tokens, spec, W.FULL_ROWS, 160, uniq_rows=ur_b, num_uniq=nu_b)
+    E.engram_scatter_add_apply(dy, n, W.FULL_ROWS, wsb, uniq_grad=ug_b)
+    torch.cuda.synchronize()
+    u = int(nu_b.item())
+    assert u == ur_a.numel()
+    assert torch.equal(ur_b[:u], ur_a)
+    assert torch.equal(ug_b[:u].view(torch.int32), ug_a.view(torch.int32))
+
+
+def test_plan_from_tokens_refuses_other_layouts():
+    ws = W.tiny_spec()
+    two = dict(ws, ngram_size=2, vocab_sizes=ws["vocab_sizes"][:8], offsets=ws["offsets"][:8])
+    with pytest.raises(E.EngramError):
+        E.engram_scatter_add_plan_from_tokens(torch.zeros((1, 8), dtype=torch.int64, device="cuda"),
+                                              product_spec_from(two), ws["num_rows"], 160)
