@@ -4,6 +4,8 @@ head layout (3-gram, 8 heads per order) with a 160-wide bf16 table takes the
 one-kernel path, other layouts and fp32 tables the hash-then-gather path through
 rows_out.  The backward's plan from tokens (engram_scatter_add_plan_from_tokens):
 plan + apply against the oracle's scatter-add of the oracle's rows."""
+import ctypes
+
 import numpy as np
 import pytest
 import torch
@@ -236,3 +238,29 @@ def test_plan_from_tokens_refuses_other_layouts():
     with pytest.raises(E.EngramError):
         E.engram_scatter_add_plan_from_tokens(torch.zeros((1, 8), dtype=torch.int64, device="cuda"),
                                               product_spec_from(two), ws["num_rows"], 160)
+
+
+def test_fused_wide_shard_row_ids():
+    """The fused kernel's 64-bit row-id path: a shard declared with 2^32 + 5 rows
+    from row_begin 100, of which the allocated table holds the tiny layout's rows;
+    rows below row_begin fall outside the shard (zero output, status)."""
+    ws = W.tiny_spec()
+    rb, declared = 100, (1 << 32) + 5
+    table = bf16_table(ws["num_rows"], 21)
+    ids = uniform_ids((3, 500), 21, ws["eos"])
+    spec = product_spec_from(ws)
+    tokens = torch.from_numpy(ids).cuda()
+    out = torch.empty((3, 500, 16, 160), dtype=torch.bfloat16, device="cuda")
+    status = torch.empty((), dtype=torch.int64, device="cuda")
+    lib = E.load_library()
+    rc = lib.engram_hash_gather(tokens.data_ptr(), 3, 500, ctypes.byref(spec), table.data_ptr(), E.ENGRAM_BF16, rb,
+                                declared, 160, out.data_ptr(), None, status.data_ptr(), None)
+    assert rc == 0
+    torch.cuda.synchronize()
+    rows = oracle_hash(ids, ws).reshape(-1)
+    assert rows.max() < rb + ws["num_rows"]          # every in-shard row lies in the allocated table
+    inside = rows >= rb
+    ref, _ = c_oracle.gather(to_host(table), np.where(inside, rows, rb), rb)
+    ref[~inside] = 0
+    assert np.array_equal(to_host(out).reshape(ref.shape), ref)
+    assert int(status.item()) == int(np.argmax(~inside)) and not inside.all()
