@@ -681,7 +681,7 @@ def route_cpu_baseline(wl, target_seconds=10.0):
         packed_ids, _ = RR.pack(s, counts, W_, cap, -1)
         RR.unpack(packed_ids, counts, ids.size)
         packed, _ = RR.pack(vals, counts, W_, cap, 0.0)
-        grouped = RR.unpack(packed, counts, ids.size)
+        grouped, _ = RR.unpack(packed, counts, ids.size)
         out = np.empty_like(grouped)
         out[order] = grouped
         spent += time.perf_counter() - t0

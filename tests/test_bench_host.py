@@ -114,3 +114,29 @@ def test_sort_nominal_bytes():
     assert bench.sort_nominal_bytes(n, (1 << 24) - 1) == 68 * n   # the sentinel fits 24 bits
     assert bench.sort_nominal_bytes(n, 1 << 24) == 88 * n           # it needs a 25th
     assert bench.sort_nominal_bytes(n, 320_001_536, u, from_tokens=True) == 92 * n + 8 * u - 8 * n + n // 2
+
+
+def test_route_cpu_baseline_runs_on_tiny_inputs():
+    """The routing line's oracle baseline (pack, unpack and unpermute through the
+    routing oracle) on CPU tensors of a tiny world."""
+    import numpy as np
+    import torch
+    rng = np.random.default_rng(3)
+    ids = torch.from_numpy(rng.integers(0, 1000, size=64).astype(np.int64))
+    vals = torch.from_numpy(rng.standard_normal((64, 8)).astype(np.float32))
+    counts = np.bincount(ids.numpy() // 250, minlength=4)
+    wl = {"world": 4, "num_embeddings": 1000, "rots": [{"ids": ids, "vals": vals, "cap": int(counts.max())}]}
+    out = bench.route_cpu_baseline(wl, target_seconds=0.01)
+    assert out["value"] > 0 and out["unit"] == "lookups/s" and out["kind"] == "oracle"
+
+
+def test_ple_cpu_baseline_runs_on_tiny_inputs():
+    import torch
+    g = torch.Generator().manual_seed(4)
+    B, S, C = 2, 16, 32
+    rot = {"x": torch.randn((B, S, C), generator=g), "dy": torch.randn((B, S, C), generator=g),
+           "halo": torch.randn((B, 9, C), generator=g), "conv_w": torch.randn((C, 4), generator=g),
+           "conv_b": torch.randn(C, generator=g), "norm_w": torch.randn(C, generator=g)}
+    wl = {"rots": [rot], "batch": B, "seq": S, "channels": C, "group": 8}
+    out = bench.ple_cpu_baseline(wl, sample_rows=1, target_seconds=0.01)
+    assert out["value"] > 0 and out["unit"] == "tokens/s" and out["kind"] == "oracle"

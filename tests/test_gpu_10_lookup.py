@@ -264,3 +264,25 @@ def test_fused_wide_shard_row_ids():
     ref[~inside] = 0
     assert np.array_equal(to_host(out).reshape(ref.shape), ref)
     assert int(status.item()) == int(np.argmax(~inside)) and not inside.all()
+
+
+def test_fused_empty_shard_and_empty_batches():
+    """An owner with no rows: every output row is zero and the status names lookup 0
+    (the empty table is never read).  Empty token batches write nothing and report
+    no bad row."""
+    ws = W.tiny_spec()
+    spec = product_spec_from(ws)
+    ids = torch.from_numpy(uniform_ids((2, 40), 29, ws["eos"])).cuda()
+    empty = torch.empty((0, 160), dtype=torch.bfloat16, device="cuda")
+    status = torch.empty((), dtype=torch.int64, device="cuda")
+    out = E.engram_hash_gather(ids, spec, empty, 5, status=status, validate=False)
+    torch.cuda.synchronize()
+    assert out.shape == (2, 40, 16, 160) and not out.view(torch.int16).any()
+    assert int(status.item()) == 0
+    table = bf16_table(ws["num_rows"], 30)
+    for shape in ((0, 7), (3, 0)):
+        status.fill_(-5)
+        out = E.engram_hash_gather(torch.empty(shape, dtype=torch.int64, device="cuda"), spec, table, status=status,
+                                   validate=False)
+        torch.cuda.synchronize()
+        assert out.numel() == 0 and int(status.item()) == -1
