@@ -924,6 +924,12 @@ def lookup_line(name, args, dev, table=None):
                                   "phases_gb": {k: round(v / 1e9, 4) for k, v in per.items()},
                                   "from": "FETCH_SIZE + WRITE_SIZE per launch in the committed rocprofv3 summaries of "
                                           "every phase of the step, over ms_per_step"}
+    if wl["backward"]:
+        # What the step pays for the backward: the plan runs beside the
+        # forward, so only the wait for it and the apply follow the forward.
+        bw = phase["wait_for_plan"] + phase["scatter_apply"]
+        result["backward_in_step"] = {"ms": round(bw, 4), "gbps_algorithmic": round(apply_bytes / (bw / 1e3) / 1e9, 1),
+                                      "frac": round(apply_bytes / (bw / 1e3) / 1e9 / HBM_PEAK_GBPS, 4)}
     if alone and wl["backward"]:
         bs = alone["scatter_plan"] + alone["scatter_apply"]
         result["backward_plan_then_apply"] = {"ms": round(bs, 4),
@@ -946,7 +952,7 @@ CEILING_OF = {"scatter_apply": "row_expand"}
 
 # Fields of the other configurations' lines kept in the default line.
 EXTRA_KEYS = ("value", "unit", "ms_per_step", "config", "phases_ms", "roofline", "phase_gbps", "gather_alone",
-              "backward_plan_then_apply", "phases_alone_ms_p50", "distinct_rows_forward_rotation0", "step_traffic")
+              "backward_in_step", "backward_plan_then_apply", "phases_alone_ms_p50", "distinct_rows_forward_rotation0", "step_traffic")
 
 
 def add_ceiling_fracs(result, ceilings):
