@@ -203,7 +203,8 @@ __device__ __forceinline__ uint32_t fill_unit<uint32_t>(u32x4 fill, uint32_t k) 
 // Only the first src_rows source rows are read: a block row whose source lies
 // past them takes the fill too (status world, unless a bad count is lower).
 // The copy kernels move K 16-byte (or 4-byte) units per thread per loop
-// step, all loads issued before the stores.  Measured on the world-64 step:
+// step, all loads issued before the stores; the stores of consecutive units
+// are non-temporal (the world-64 value pack went from 81 to 64 us with them).  Measured on the world-64 step:
 // K = 4 helps the unpack (the compact side is written sequentially) and the
 // 4-byte units; the pack of 16-byte units gains little and the scattering
 // permute loses, so each launch picks its own K.
@@ -236,7 +237,7 @@ __global__ __launch_bounds__(kBlock) void pack_kernel(const U* __restrict__ src,
 #pragma unroll
         for (int k = 0; k < K; ++k) {
             const I e = e0 + (I)(k * kBlock);
-            if (e < seg_units) d[e] = v[k];
+            if (e < seg_units) __builtin_nontemporal_store(v[k], d + e);
         }
     }
 }
@@ -272,7 +273,7 @@ __global__ __launch_bounds__(kBlock) void unpack_kernel(const U* __restrict__ sr
 #pragma unroll
         for (int k = 0; k < K; ++k) {
             const I e = e0 + (I)(k * kBlock);
-            if (e < seg_units) d[e] = v[k];
+            if (e < seg_units) __builtin_nontemporal_store(v[k], d + e);
         }
     }
 }
@@ -304,9 +305,9 @@ __global__ __launch_bounds__(kBlock) void permute_kernel(const U* __restrict__ s
 #pragma unroll
         for (int k = 0; k < K; ++k)
             if (at[k] >= 0) {
-                if (GATHER)
-                    dst[e0 + k * kBlock] = v[k];
-                else
+                if (GATHER)  // consecutive units: streamed past the caches
+                    __builtin_nontemporal_store(v[k], dst + e0 + k * kBlock);
+                else         // scattered units: plain stores (non-temporal ones measured slower)
                     dst[at[k]] = v[k];
             }
     }
