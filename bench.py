@@ -188,10 +188,13 @@ def run_step(wl, b, ev=None):
     forward on the main stream; with a backward, the plan (sort by row) from
     the same tokens, which hashes the rows itself, on a side stream beside it;
     the apply once both are done.  No rows array is written or read.  From
-    rows (the owner shard, which receives its rows): the plan on the side
-    stream beside the gather, then the apply.  ev: events (step start, unused,
-    forward end, plan start, plan end, apply start, apply end); an entry may
-    be None, and only the events given are recorded."""
+    rows (the owner shard, which receives its rows): the plan, a chain of
+    short launches and the longer of the two there, on the main stream, and
+    the gather beside it on the side stream, then the apply.  A stream that
+    waits on the other starts some microseconds late, so the longer chain goes
+    on the main stream.  ev: events (step start, unused, forward end, plan
+    start, plan end, apply start, apply end); an entry may be None, and only
+    the events given are recorded."""
     import torch
 
     import hashed_gram_embedding_engram_amd as E
@@ -204,9 +207,9 @@ def run_step(wl, b, ev=None):
 
     compact = b.get("compact")
 
-    def plan():
+    def plan(stream):
         args = dict(workspace=wl["workspace"], uniq_rows=compact[0] if compact else None,
-                    num_uniq=compact[2] if compact else None, status=b["plan_status"], stream=side)
+                    num_uniq=compact[2] if compact else None, status=b["plan_status"], stream=stream)
         if b["tokens"] is not None:   # the rows hashed inside the plan
             E.engram_scatter_add_plan_from_tokens(b["tokens"], wl["spec"], wl["table_rows"], b["dy"].shape[-1],
                                                   wl["row_begin"], **args)
@@ -214,17 +217,27 @@ def run_step(wl, b, ev=None):
             E.engram_scatter_add_plan(b["rows"], wl["table_rows"], b["dy"].shape[-1], wl["row_begin"], **args)
 
     mark(0, main)
-    if wl["backward"]:
-        side.wait_stream(main)
-        mark(3, side)
-        plan()
-        mark(4, side)
-    if b["tokens"] is not None:
-        E.engram_hash_gather(b["tokens"], wl["spec"], wl["table"], wl["row_begin"], out=b["out"],
-                             status=b["status"], validate=False)
+    if wl["backward"] and b["tokens"] is None:
+        side.wait_stream(main)        # the gather starts once the previous step is done
+        mark(3, main)
+        plan(main)
+        mark(4, main)
+        E.engram_gather(wl["table"], b["rows"], wl["row_begin"], out=b["out"], status=b["status"], validate=False,
+                        stream=side)
+        mark(2, side)
     else:
-        E.engram_gather(wl["table"], b["rows"], wl["row_begin"], out=b["out"], status=b["status"], validate=False)
-    mark(2, main)
+        if wl["backward"]:
+            side.wait_stream(main)
+            mark(3, side)
+            plan(side)
+            mark(4, side)
+        if b["tokens"] is not None:
+            E.engram_hash_gather(b["tokens"], wl["spec"], wl["table"], wl["row_begin"], out=b["out"],
+                                 status=b["status"], validate=False)
+        else:
+            E.engram_gather(wl["table"], b["rows"], wl["row_begin"], out=b["out"], status=b["status"],
+                            validate=False)
+        mark(2, main)
     if wl["backward"]:
         main.wait_stream(side)
         mark(5, main)
@@ -719,7 +732,7 @@ def route_main(args, dev):
            "unpack_ids": 16.0 * n, "pack_values": row * n + row * Wd * cap, "unpack_values": 2 * row * n,
            "unpermute_values": (2 * row + 8.0) * n}
     dom = names[di]
-    kname = {"plan": "route_keys_kernel + radix pass + route_output_kernel", "validate": "route_validate_kernel",
+    kname = {"plan": "route_keys_kernel + radix pass writing the grouped output", "validate": "route_validate_kernel",
              "pack_ids": "pack_kernel<uint32_t,uint32_t,4>", "unpack_ids": "unpack_kernel<uint32_t,uint32_t,4>",
              "pack_values": "pack_kernel<u32x4,uint32_t,2>", "unpack_values": "unpack_kernel<u32x4,uint32_t,4>",
              "unpermute_values": "permute_kernel<u32x4,false,1>"}
@@ -807,8 +820,10 @@ def lookup_line(name, args, dev, table=None):
     # From tokens the forward is one fused kernel ("gather") and the plan
     # hashes its rows itself; from rows there is no hash.
     spans = {"gather": (0, 2)}
-    if wl["backward"]:
+    if wl["backward"] and fused:
         spans.update({"scatter_plan (side stream)": (3, 4), "wait_for_plan": (2, 5), "scatter_apply": (5, 6)})
+    elif wl["backward"]:
+        spans.update({"scatter_plan": (3, 4), "wait_for_gather": (4, 5), "scatter_apply": (5, 6)})
     phase = {k: sum(e[a].elapsed_time(e[b]) for e in evs) / kb for k, (a, b) in spans.items()}
     phase_pct = {k: percentiles([e[a].elapsed_time(e[b]) for e in evs]) for k, (a, b) in spans.items()}
     phase[dom] = sum(dom_ms) / len(dom_ms)        # the dominant phase from the timed steps themselves
@@ -840,8 +855,8 @@ def lookup_line(name, args, dev, table=None):
     kern = {"gather": (gather_bytes, phase["gather"],
                        "hash_gather_kernel<true,false> (hash and gather fused)" if fused
                        else "gather_rows_kernel<20,16,true>", PROFILED[name]["gather"][0])}
-    # The plan runs on a side stream during the gather; apply is timed from
-    # after the main stream's wait for it.
+    # The plan and the gather run side by side; apply is timed from after the
+    # main stream's wait for both.
     if wl["backward"]:
         kern["scatter_apply"] = (apply_bytes, phase["scatter_apply"],
                                  "segment_reduce_kernel<20,bf16> + carry_fixup_kernel + long_run_kernel", "scatter.hip")
@@ -926,8 +941,10 @@ def lookup_line(name, args, dev, table=None):
                                           "every phase of the step, over ms_per_step"}
     if wl["backward"]:
         # What the step pays for the backward: the plan runs beside the
-        # forward, so only the wait for it and the apply follow the forward.
-        bw = phase["wait_for_plan"] + phase["scatter_apply"]
+        # forward, so only what follows the forward's end counts (the wait for
+        # the plan, if it ends later, and the apply).
+        after_forward = sum(e[2].elapsed_time(e[5]) for e in evs) / kb
+        bw = after_forward + phase["scatter_apply"]
         result["backward_in_step"] = {"ms": round(bw, 4), "gbps_algorithmic": round(apply_bytes / (bw / 1e3) / 1e9, 1),
                                       "frac": round(apply_bytes / (bw / 1e3) / 1e9 / HBM_PEAK_GBPS, 4)}
     if alone and wl["backward"]:
@@ -989,7 +1006,7 @@ PROFILED = {
             "norm_bwd": ("ple.hip", [r"\brms_norm_bwd", r"\bcolumn_sum_kernel"]),
             "conv_bwd": ("ple.hip", [r"\bshort_conv_bwd", r"\bcolumn_sum_kernel"])},
     "route": {"plan": ("route.hip", [r"\broute_init_kernel", r"\broute_keys_kernel", r"\bupsweep_kernel",
-                                     r"\bdownsweep_kernel", r"\broute_output_kernel"]),
+                                     r"\bdownsweep_kernel"]),
               "validate": ("route.hip", [r"\broute_validate_kernel"]),
               "pack_ids": ("route.hip", [r"\bpack_kernel<unsigned int,"]),
               "unpack_ids": ("route.hip", [r"\bunpack_kernel<unsigned int,"]),
@@ -1011,7 +1028,7 @@ WORKLOAD_TEXT = {
            "(kernel 4, dilation 3, 9-token halo), the grouped RMSNorm (groups of 2,560), the norm backward and "
            "the conv backward, each backward followed by a column sum of its weight-gradient partials",
     "route": "one request rank of a world-64 owner group: 8 x 4,096 Zipf(1.2) tokens hashed into 524,288 "
-             "full-table row IDs; per step: group by owner (route keys, one radix digit pass, route output), "
+             "full-table row IDs; per step: group by owner (route keys, then one radix digit pass that writes the grouped IDs, positions and counts), "
              "segment validation, pack of the IDs to the step's capacity, the owner's unpack, the owner's pack "
              "of 320-B bf16 value rows, the requester's unpack and the unpermute to request order",
 }

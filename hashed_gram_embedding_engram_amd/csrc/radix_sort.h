@@ -247,14 +247,26 @@ __device__ __forceinline__ uint32_t block_exclusive_scan_n(uint32_t v, uint32_t*
     return wave_off + x - v;
 }
 
+// Where the routing sort's single pass puts its result: each entry's ID
+// (ids[value]) and request position (the value) as int64 at its sorted slot,
+// and the per-owner counts (digit totals below `world`) from block 0.
+struct GroupedOut {
+    const int64_t* ids;
+    int64_t* sorted_ids;
+    int64_t* order;
+    int64_t* send_counts;
+    int world;
+};
+
 // One stable scatter pass of the LSD radix sort.  vals_in == nullptr means
-// the value of entry e is e itself.  SMALL as for load_tile_counts.
-template <bool SMALL, int ITEMS = kItems>
+// the value of entry e is e itself.  SMALL as for load_tile_counts.  With
+// GROUPED the pass writes `go`'s outputs instead of keys_out / vals_out.
+template <bool SMALL, int ITEMS = kItems, bool GROUPED = false>
 __global__ __launch_bounds__(kBlock) void downsweep_kernel(const uint32_t* __restrict__ keys_in,
                                                            const uint32_t* __restrict__ vals_in,
                                                            uint32_t* __restrict__ keys_out,
                                                            uint32_t* __restrict__ vals_out, uint32_t n, int shift,
-                                                           DigitCounts dc) {
+                                                           DigitCounts dc, GroupedOut go) {
     __shared__ uint32_t s_keys[kBlock * ITEMS];
     __shared__ uint32_t s_vals[kBlock * ITEMS];
     // per wave and digit: the wave's count, then its offset inside the tile;
@@ -334,9 +346,20 @@ __global__ __launch_bounds__(kBlock) void downsweep_kernel(const uint32_t* __res
         const uint32_t d = (k >> shift) & 0xFFu;
         const uint32_t g = s_wave_cnt[0][d] + j;  // unsigned wrap-around cancels
         if (g < n) {  // always true for a consistent histogram; keeps every store in bounds
-            keys_out[g] = k;
-            vals_out[g] = s_vals[j];
+            if (GROUPED) {
+                const uint32_t v = min(s_vals[j], n - 1);
+                go.sorted_ids[g] = go.ids[v];
+                go.order[g] = v;
+            } else {
+                keys_out[g] = k;
+                vals_out[g] = s_vals[j];
+            }
         }
+    }
+    if (GROUPED && blockIdx.x == 0 && tid < go.world) {
+        uint32_t total = 0;  // every group's count of owner tid
+        for (uint32_t gi = 0; gi < dc.num_groups; ++gi) total += dc.group[(size_t)gi * kRadix + tid];
+        go.send_counts[tid] = total;
     }
 }
 

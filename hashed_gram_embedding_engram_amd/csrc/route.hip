@@ -30,7 +30,7 @@ namespace {
 // 255 left for out-of-range IDs, and one thread per count fits a block.
 
 struct RouteLayout {
-    size_t keys_a, keys_b, vals_b, hist, count_totals, counters, total;
+    size_t keys_a, hist, count_totals, counters, total;
     int64_t num_tiles;
 };
 
@@ -40,8 +40,6 @@ RouteLayout route_layout(int64_t n) {
     size_t off = 0;
     auto take = [&](size_t bytes) { size_t at = off; off = (off + bytes + 255) & ~(size_t)255; return at; };
     L.keys_a = take(4 * (size_t)n);
-    L.keys_b = take(4 * (size_t)n);
-    L.vals_b = take(4 * (size_t)n);
     L.hist = take(4 * (size_t)kRadix * (size_t)L.num_tiles);
     L.count_totals = take(4 * count_words(L.num_tiles));
     L.counters = take(16);
@@ -96,25 +94,6 @@ __global__ __launch_bounds__(kBlock) void route_keys_kernel(const int64_t* __res
 #pragma unroll
     for (int k = 0; k < kBlock / 64; ++k) c += s_cnt[k][tid];
     publish_tile_counts(dc, blockIdx.x, tid, c);
-}
-
-// Grouped IDs, their request positions, and the per-owner send counts.
-__global__ __launch_bounds__(kBlock) void route_output_kernel(const uint32_t* __restrict__ sorted_vals,
-                                                              const int64_t* __restrict__ ids, uint32_t n, int world,
-                                                              DigitCounts dc,
-                                                              int64_t* __restrict__ sorted_ids,
-                                                              int64_t* __restrict__ order,
-                                                              int64_t* __restrict__ send_counts) {
-    const uint32_t i = blockIdx.x * kBlock + threadIdx.x;
-    if (blockIdx.x == 0 && threadIdx.x < (unsigned)world) {
-        uint32_t total = 0;  // all groups' counts of owner threadIdx.x
-        for (uint32_t g = 0; g < dc.num_groups; ++g) total += dc.group[(size_t)g * kRadix + threadIdx.x];
-        send_counts[threadIdx.x] = total;
-    }
-    if (i >= n) return;
-    const uint32_t v = min(sorted_vals[i], n - 1);
-    sorted_ids[i] = ids[v];
-    order[i] = v;
 }
 
 // Per-segment facts every block of segment w needs, from the counts (up to
@@ -341,18 +320,18 @@ hipError_t launch_route_plan(const int64_t* ids, int64_t n, int64_t local_rows, 
     }
     const uint32_t nn = (uint32_t)n, tiles = (uint32_t)L.num_tiles;
     const DigitCounts dc = make_digit_counts(ws + L.hist, count_totals, L.num_tiles);
-    uint32_t *ka = (uint32_t*)(ws + L.keys_a), *kb = (uint32_t*)(ws + L.keys_b);
-    uint32_t* vb = (uint32_t*)(ws + L.vals_b);
+    uint32_t* ka = (uint32_t*)(ws + L.keys_a);
     hipLaunchKernelGGL(route_keys_kernel, dim3(tiles), dim3(kBlock), 0, stream, ids, nn, local_rows, world, ka, dc,
                        status);
+    // One digit pass (owners fit 8 bits), writing the grouped IDs, their
+    // request positions and the send counts directly.
+    const GroupedOut go{ids, sorted_ids, order, send_counts, world};
     if (small_counts(dc))
-        hipLaunchKernelGGL(downsweep_kernel<true>, dim3(tiles), dim3(kBlock), 0, stream, ka, (const uint32_t*)nullptr,
-                           kb, vb, nn, 0, dc);
+        hipLaunchKernelGGL((downsweep_kernel<true, kItems, true>), dim3(tiles), dim3(kBlock), 0, stream, ka,
+                           (const uint32_t*)nullptr, (uint32_t*)nullptr, (uint32_t*)nullptr, nn, 0, dc, go);
     else
-        hipLaunchKernelGGL(downsweep_kernel<false>, dim3(tiles), dim3(kBlock), 0, stream, ka, (const uint32_t*)nullptr,
-                           kb, vb, nn, 0, dc);
-    hipLaunchKernelGGL(route_output_kernel, dim3((nn + kBlock - 1) / kBlock), dim3(kBlock), 0, stream, vb, ids, nn,
-                       world, dc, sorted_ids, order, send_counts);
+        hipLaunchKernelGGL((downsweep_kernel<false, kItems, true>), dim3(tiles), dim3(kBlock), 0, stream, ka,
+                           (const uint32_t*)nullptr, (uint32_t*)nullptr, (uint32_t*)nullptr, nn, 0, dc, go);
     return hipGetLastError();
 }
 

@@ -955,10 +955,10 @@ hipError_t run_sort(const Layout& L, char* ws, const int64_t* rows, const TokenR
         const uint32_t* v_in = p == 0 ? nullptr : v_cur;
         if (small_counts(dc))
             hipLaunchKernelGGL((downsweep_kernel<true, ITEMS>), dim3(tiles), dim3(kBlock), 0, stream, k_cur, v_in, k_nxt,
-                               v_nxt, nn, shift, dc);
+                               v_nxt, nn, shift, dc, GroupedOut{});
         else
             hipLaunchKernelGGL((downsweep_kernel<false, ITEMS>), dim3(tiles), dim3(kBlock), 0, stream, k_cur, v_in, k_nxt,
-                               v_nxt, nn, shift, dc);
+                               v_nxt, nn, shift, dc, GroupedOut{});
         if ((err = hipGetLastError()) != hipSuccess) return err;
         uint32_t* t = k_cur; k_cur = k_nxt; k_nxt = t;
         t = v_cur; v_cur = v_nxt; v_nxt = t;
