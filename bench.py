@@ -965,7 +965,7 @@ LOOKUP_WORKLOADS = tuple(WORKLOAD_NAMES)
 # mix and access distribution.  The backward's sums read a random permutation
 # of the gradient rows, as row_expand does; the gather's Zipf-skewed rows hit
 # in cache more often than row_gather's uniform ones, so it has no such probe.
-CEILING_OF = {"scatter_apply": "row_expand"}
+CEILING_OF = {"scatter_apply": "row_expand", "scatter_apply_dense": "row_rmw"}
 
 # Fields of the other configurations' lines kept in the default line.
 EXTRA_KEYS = ("value", "unit", "ms_per_step", "config", "phases_ms", "roofline", "phase_gbps", "gather_alone",
@@ -977,6 +977,8 @@ def add_ceiling_fracs(result, ceilings):
     if not ceilings:
         return
     dom = "scatter_apply" if "scatter_apply" in result["phase_gbps"] else "gather"
+    if dom == "scatter_apply" and result["config"].get("distinct_rows_rotation0") is None:
+        dom = "scatter_apply_dense"   # the dense gradient's read-modify-write
     c = ceilings.get(CEILING_OF.get(dom))
     if c:
         result["roofline"]["measured_ceiling"] = {"probe": CEILING_OF[dom], "gbps": c,
@@ -1257,7 +1259,9 @@ def main():
         result["ceilings_from"] = ("libengram_probe.so: streaming 16-byte reads and writes of 4 GiB; row_gather "
                                    "reads 4,194,304 uniform-random 320-B rows of a 25 M-row bf16 table and writes "
                                    "them in order; row_expand reads 3,163,052 distinct random 320-B bf16 rows and "
-                                   "writes them as 640-B fp32 rows; GB/s = bytes moved / median of 10 launches")
+                                   "writes them as 640-B fp32 rows; row_rmw adds 4 random 320-B bf16 rows into each "
+                                   "of 156,202 distinct random 640-B fp32 rows of a 5,000,024-row array (read, add, "
+                                   "write back); GB/s = bytes moved / median of 10 launches")
         add_ceiling_fracs(result, ceilings)
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(wl)

@@ -8,6 +8,10 @@
 //   expand   the backward's traffic: bf16 rows of 320 bytes read at indexed
 //            positions, written as fp32 rows of 640 bytes; each wave stages its
 //            16 output rows in LDS so that every store instruction writes 1 KiB
+//   rmw      the dense backward's traffic: each of a set of distinct fp32 rows
+//            of 640 bytes, at random places in a large array, gets the sum of
+//            kRmwReads random bf16 rows of 320 bytes added to it (read,
+//            add, write back); 16 rows per wave
 // Every kernel strides over its work with a fixed grid.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -128,11 +132,63 @@ __global__ __launch_bounds__(kBlock) void expand_kernel(const u32x4* __restrict_
     }
 }
 
+constexpr int kRmwReads = 4;  // bf16 rows added into each fp32 row
+
+// Row r of the work adds src rows idx[kRmwReads r + i] into dst row
+// idx[kRmwReads rows + r].  A lane holding bf16 chunk q of a row (8 values)
+// updates fp32 chunks 2q and 2q + 1 of the same row, so no data moves
+// between lanes.
+__global__ __launch_bounds__(kBlock) void rmw_kernel(const u32x4* __restrict__ src, const uint32_t* __restrict__ idx,
+                                                     uint64_t rows, float* __restrict__ dst) {
+    typedef float f32x4 __attribute__((ext_vector_type(4)));
+    const int lane = threadIdx.x & 63;
+    const uint64_t waves = (uint64_t)gridDim.x * (kBlock / 64);
+    const uint32_t* dst_idx = idx + (uint64_t)kRmwReads * rows;
+    for (uint64_t t = (uint64_t)blockIdx.x * (kBlock / 64) + (threadIdx.x >> 6); t * 16 < rows; t += waves) {
+        const uint64_t r0 = t * 16;
+        u32x4 x[5][kRmwReads];
+        f32x4 old[5][2];
+        f32x4* rowp[5];
+#pragma unroll
+        for (int j = 0; j < 5; ++j) {
+            const int c = lane + 64 * j, k = c / kRowChunks, q = c % kRowChunks;
+            const bool live = r0 + k < rows;
+            const uint64_t r = live ? r0 + k : 0;
+#pragma unroll
+            for (int i = 0; i < kRmwReads; ++i) {
+                const uint32_t s_row = idx[r * kRmwReads + i];
+                x[j][i] = live ? src[(uint64_t)s_row * kRowChunks + q] : u32x4{0u, 0u, 0u, 0u};
+            }
+            rowp[j] = (f32x4*)(dst + (uint64_t)dst_idx[r] * (2 * kRowChunks * 4)) + 2 * q;
+            old[j][0] = live ? rowp[j][0] : f32x4{0.f, 0.f, 0.f, 0.f};
+            old[j][1] = live ? rowp[j][1] : f32x4{0.f, 0.f, 0.f, 0.f};
+        }
+#pragma unroll
+        for (int j = 0; j < 5; ++j) {
+            const int c = lane + 64 * j, k = c / kRowChunks;
+            if (r0 + k >= rows) continue;
+            f32x4 a = old[j][0], b = old[j][1];
+#pragma unroll
+            for (int i = 0; i < kRmwReads; ++i) {
+                const u32x4 v = x[j][i];
+                a += f32x4{__uint_as_float(v[0] << 16), __uint_as_float(v[0] & 0xFFFF0000u),
+                           __uint_as_float(v[1] << 16), __uint_as_float(v[1] & 0xFFFF0000u)};
+                b += f32x4{__uint_as_float(v[2] << 16), __uint_as_float(v[2] & 0xFFFF0000u),
+                           __uint_as_float(v[3] << 16), __uint_as_float(v[3] & 0xFFFF0000u)};
+            }
+            rowp[j][0] = a;
+            rowp[j][1] = b;
+        }
+    }
+}
+
 }  // namespace
 
 // kind 0 read (src, bytes; dst: one 16-byte word per block of the grid),
 // 1 write (dst, bytes), 2 gather and 3 expand (src rows of 320 bytes, idx
-// [rows] < the rows of src, dst [rows] output rows).  Returns a hipError_t.
+// [rows] < the rows of src, dst [rows] output rows), 4 rmw (src rows of 320
+// bytes; idx: 4 * count src rows, then count distinct dst rows; dst fp32 rows
+// of 640 bytes).  Returns a hipError_t.
 extern "C" int engram_probe(int kind, const void* src, const uint32_t* idx, uint64_t count, void* dst, int grid,
                             hipStream_t stream) {
     if (grid < 1) return (int)hipErrorInvalidValue;
@@ -147,6 +203,9 @@ extern "C" int engram_probe(int kind, const void* src, const uint32_t* idx, uint
     else if (kind == 3)
         hipLaunchKernelGGL(expand_kernel, dim3(grid), dim3(kBlock), 0, stream, (const u32x4*)src, idx, count,
                            (u32x4*)dst);
+    else if (kind == 4)
+        hipLaunchKernelGGL(rmw_kernel, dim3(grid), dim3(kBlock), 0, stream, (const u32x4*)src, idx, count,
+                           (float*)dst);
     else
         return (int)hipErrorInvalidValue;
     return (int)hipGetLastError();

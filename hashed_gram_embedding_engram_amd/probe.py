@@ -48,12 +48,18 @@ def _median_ms(fn, reps):
     return sorted(ms)[len(ms) // 2]
 
 
+RMW_READS = 4  # bf16 rows the rmw probe adds into each fp32 row
+
+
 def measure_ceilings(dev, reps=10, stream_bytes=4 << 30, table_rows=25_000_000, lookups=4_194_304,
-                     distinct=3_163_052, grid=8192, seed=0):
+                     distinct=3_163_052, grid=8192, seed=0, dense_rows=5_000_024, dense_distinct=156_202,
+                     dense_lookups=562_578):
     """GB/s of each probe (bytes the kernel must move / median time).  The gather
     reads `lookups` uniform-random 320-byte rows of a `table_rows`-row bf16 table;
     the expand reads `distinct` distinct rows of a `lookups`-row bf16 array in
-    random order and writes them as fp32."""
+    random order and writes them as fp32; the rmw adds RMW_READS random rows
+    of a `dense_lookups`-row bf16 array into each of `dense_distinct` distinct
+    random fp32 rows of a `dense_rows`-row array (the owner shard's sizes)."""
     g = torch.Generator(device=dev)
     g.manual_seed(seed)
     out = {}
@@ -74,5 +80,14 @@ def measure_ceilings(dev, reps=10, stream_bytes=4 << 30, table_rows=25_000_000, 
     ms = _median_ms(lambda: run_probe(3, src, idx, distinct, dst, grid), reps)
     out["row_expand"] = distinct * (320 + 640 + 4) / ms / 1e6
     del src, idx, dst
+    src = torch.empty((dense_lookups, 160), dtype=torch.bfloat16, device=dev).fill_(1.0)
+    reads = torch.randint(0, dense_lookups, (dense_distinct * RMW_READS,), generator=g, device=dev,
+                          dtype=torch.int64)
+    rows = torch.randperm(dense_rows, generator=g, device=dev)[:dense_distinct]
+    idx = torch.cat([reads, rows]).to(torch.int32).contiguous()
+    dst = torch.zeros((dense_rows, 160), dtype=torch.float32, device=dev)
+    ms = _median_ms(lambda: run_probe(4, src, idx, dense_distinct, dst, grid), reps)
+    out["row_rmw"] = dense_distinct * (RMW_READS * (320 + 4) + 640 + 640 + 4) / ms / 1e6
+    del src, reads, rows, idx, dst
     torch.cuda.empty_cache()
     return {k: round(v, 1) for k, v in out.items()}
