@@ -643,7 +643,6 @@ def route_build(rotations, dev, world=64):
         # the owner's looked-up values, in the received (grouped) order
         t["vals"] = torch.randn((n, W.DIM), generator=g, device=dev).to(torch.bfloat16)
         t["vals_packed"] = torch.empty((world, cap, W.DIM), dtype=torch.bfloat16, device=dev)
-        t["vals_grouped"] = torch.empty((n, W.DIM), dtype=torch.bfloat16, device=dev)
         t["vals_out"] = torch.empty((n, W.DIM), dtype=torch.bfloat16, device=dev)
         rots.append(t)
     return {"rots": rots, "world": world, "num_embeddings": W.FULL_ROWS}
@@ -671,9 +670,7 @@ def route_step(wl, t, ev=None):
     mark()
     E.engram_pack_fixed_capacity(t["vals"], t["counts"], W_, t["cap"], fill=0, out=t["vals_packed"])
     mark()
-    E.engram_unpack_fixed_capacity(t["vals_packed"], t["counts"], t["n"], out=t["vals_grouped"])
-    mark()
-    E.engram_unpermute_rows(t["vals_grouped"], t["order"], out=t["vals_out"])
+    E.engram_unpack_unpermute_rows(t["vals_packed"], t["counts"], t["order"], out=t["vals_out"])
     mark()
 
 
@@ -716,7 +713,7 @@ def route_main(args, dev):
     for i in range(args.warmup):
         route_step(wl, wl["rots"][i % R])
     torch.cuda.synchronize()
-    names = ["plan", "validate", "pack_ids", "unpack_ids", "pack_values", "unpack_values", "unpermute_values"]
+    names = ["plan", "validate", "pack_ids", "unpack_ids", "pack_values", "unpack_unpermute_values"]
     elapsed, mean, pct, di = timed_phases(lambda t, ev: route_step(wl, t, ev), wl["rots"], len(names), args.steps)
     phase = dict(zip(names, mean))
     phase_pct = dict(zip(names, pct))
@@ -726,16 +723,17 @@ def route_main(args, dev):
     # Algorithmic bytes per launch: the plan reads the 8-B IDs and writes the
     # sorted IDs and their 8-B request positions; validation reads the sorted
     # IDs; a pack reads the compact rows and writes the whole padded
-    # [world][capacity] block; an unpack reads the valid rows and writes them
-    # compact; the unpermute reads and writes every row plus its 8-B position.
+    # [world][capacity] block; the IDs' unpack reads the valid rows and writes
+    # them compact; the values' unpack into request order reads every valid
+    # row and its 8-B request position and writes the row there.
     alg = {"plan": 24.0 * n, "validate": 8.0 * n, "pack_ids": 8.0 * n + 8.0 * Wd * cap,
-           "unpack_ids": 16.0 * n, "pack_values": row * n + row * Wd * cap, "unpack_values": 2 * row * n,
-           "unpermute_values": (2 * row + 8.0) * n}
+           "unpack_ids": 16.0 * n, "pack_values": row * n + row * Wd * cap,
+           "unpack_unpermute_values": (2 * row + 8.0) * n}
     dom = names[di]
     kname = {"plan": "route_keys_kernel + radix pass writing the grouped output", "validate": "route_validate_kernel",
              "pack_ids": "pack_kernel<uint32_t,uint32_t,4>", "unpack_ids": "unpack_kernel<uint32_t,uint32_t,4>",
-             "pack_values": "pack_kernel<u32x4,uint32_t,2>", "unpack_values": "unpack_kernel<u32x4,uint32_t,4>",
-             "unpermute_values": "permute_kernel<u32x4,false,1>"}
+             "pack_values": "pack_kernel<u32x4,uint32_t,2>",
+             "unpack_unpermute_values": "unpack_unpermute_kernel<u32x4,uint32_t,2>"}
     achieved = alg[dom] / (phase[dom] / 1e3) / 1e9
     result = {
         "metric": ROUTE_METRIC,
@@ -1013,15 +1011,14 @@ PROFILED = {
               "pack_ids": ("route.hip", [r"\bpack_kernel<unsigned int,"]),
               "unpack_ids": ("route.hip", [r"\bunpack_kernel<unsigned int,"]),
               "pack_values": ("route.hip", [r"\bpack_kernel<u32x4"]),
-              "unpack_values": ("route.hip", [r"\bunpack_kernel<u32x4"]),
-              "unpermute_values": ("route.hip", [r"\bpermute_kernel<u32x4"])},
+              "unpack_unpermute_values": ("route.hip", [r"\bunpack_unpermute_kernel<u32x4"])},
 }
 # Phases whose counter summaries are written (the ones a bench line can name
 # as its dominant kernel).
 COUNTED = {"long": ["gather", "scatter_plan", "scatter_apply"], "full-sft": ["gather"],
            "owner": ["gather", "scatter_plan", "scatter_apply"],
            "ple": ["conv_fwd", "norm_fwd", "norm_bwd", "conv_bwd"],
-           "route": ["pack_values", "unpack_values", "unpermute_values"]}
+           "route": ["pack_values", "unpack_unpermute_values"]}
 PROFILE_FLAGS = "--steps 5 --warmup 2 --no-cpu-baseline --no-alone --no-ceilings --no-extra-configs --calibrate-copy"
 TRACE_FILE = {"long": "kernel_trace_long_context.md", "full-sft": "kernel_trace_full_sft.md",
               "owner": "kernel_trace_owner.md", "ple": "kernel_trace_ple.md", "route": "kernel_trace_route.md"}
@@ -1032,7 +1029,7 @@ WORKLOAD_TEXT = {
     "route": "one request rank of a world-64 owner group: 8 x 4,096 Zipf(1.2) tokens hashed into 524,288 "
              "full-table row IDs; per step: group by owner (route keys, then one radix digit pass that writes the grouped IDs, positions and counts), "
              "segment validation, pack of the IDs to the step's capacity, the owner's unpack, the owner's pack "
-             "of 320-B bf16 value rows, the requester's unpack and the unpermute to request order",
+             "of 320-B bf16 value rows, and the requester's unpack straight into request order (one pass)",
 }
 
 

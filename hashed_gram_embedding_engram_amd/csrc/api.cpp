@@ -70,6 +70,13 @@ int hash_common(const int64_t* tokens, int64_t batch, int64_t seq_len, int64_t s
 
 }  // namespace
 
+namespace engram {
+// The fused unpack and move to request order (route.hip).
+hipError_t launch_unpack_unpermute(const void* src, int64_t row_bytes, const int64_t* counts, int world,
+                                  int64_t capacity, const int64_t* order, int64_t n, void* dst, int64_t* status,
+                                  hipStream_t stream);
+}  // namespace engram
+
 extern "C" {
 
 int engram_hash(const int64_t* tokens, int64_t batch, int64_t seq_len, const engram_hash_spec* spec,
@@ -283,6 +290,20 @@ int engram_unpack_fixed_capacity(const void* src, int64_t row_bytes, const int64
         return ENGRAM_EINVAL;
     return launch_result(engram::launch_unpack(src, row_bytes, split_sizes, world, capacity, dst, dst_rows, status,
                                                stream));
+}
+
+int engram_unpack_unpermute_rows(const void* src, int64_t row_bytes, const int64_t* split_sizes, int32_t world,
+                                 int64_t capacity, const int64_t* order, int64_t n, void* dst, int64_t* status,
+                                 hipStream_t stream) {
+    if (world < 1 || world > 255 || capacity < 0 || n < 0 || !row_layout_ok(row_bytes) || !split_sizes)
+        return ENGRAM_EINVAL;
+    if (capacity > 0 && n > 0 && (!dst || !src || !order)) return ENGRAM_EINVAL;
+    if (!aligned(src, 4) || !aligned(dst, 4) || !aligned(order, 8) || !aligned(split_sizes, 8) || !aligned(status, 8))
+        return ENGRAM_EINVAL;
+    if ((int64_t)world * capacity > ((int64_t)1 << 40) / row_bytes || n > ((int64_t)1 << 40) / row_bytes)
+        return ENGRAM_EINVAL;
+    return launch_result(engram::launch_unpack_unpermute(src, row_bytes, split_sizes, world, capacity, order, n, dst,
+                                                         status, stream));
 }
 
 int engram_permute_rows(const void* src, int64_t row_bytes, const int64_t* order, int64_t n, void* dst,

@@ -410,6 +410,8 @@ def _bind_route(lib):
     lib.engram_permute_rows.argtypes = [p, i64, p, i64, p, p]
     lib.engram_unpermute_rows.restype = ctypes.c_int
     lib.engram_unpermute_rows.argtypes = [p, i64, p, i64, p, p]
+    lib.engram_unpack_unpermute_rows.restype = ctypes.c_int
+    lib.engram_unpack_unpermute_rows.argtypes = [p, i64, p, i32, i64, p, i64, p, p, p]
     lib._route_bound = True
 
 
@@ -494,10 +496,29 @@ def engram_unpack_fixed_capacity(src, split_sizes, dst_rows, status=None, out=No
     return dst
 
 
+def engram_unpack_unpermute_rows(src, split_sizes, order, status=None, out=None, stream=None):
+    """[world, capacity, ...] -> [n, ...] in request order: compact row k (rank
+    order, as engram_unpack_fixed_capacity) lands in row order[k]; n = order.numel()."""
+    lib = _route_lib()
+    world, capacity = src.shape[0], src.shape[1]
+    row_shape = tuple(src.shape[2:])
+    esize = src.element_size()
+    row_bytes = esize * int(torch.Size(row_shape).numel()) if row_shape else esize
+    n = order.numel()
+    dst = torch.empty((n,) + row_shape, dtype=src.dtype, device=src.device) if out is None else out
+    _check(lib.engram_unpack_unpermute_rows(_dev_ptr(src, "src"), row_bytes,
+                                            _dev_ptr(split_sizes, "split_sizes", torch.int64, numel=world), world,
+                                            capacity, _dev_ptr(order, "order", torch.int64), n,
+                                            _dev_ptr(dst, "dst", src.dtype, min_numel=n * (row_bytes // esize)),
+                                            _status_ptr(status), _stream_handle(stream)),
+           "engram_unpack_unpermute_rows")
+    return dst
+
+
 def _permute(src, order, gather, stream, out=None):
     lib = _route_lib()
     n = order.numel()
-    row_elems = src[0].numel() if src.dim() > 1 else 1
+    row_elems = int(torch.Size(src.shape[1:]).numel()) if src.dim() > 1 else 1
     row_bytes = row_elems * src.element_size()
     dst = torch.empty_like(src) if out is None else out
     fn = lib.engram_permute_rows if gather else lib.engram_unpermute_rows

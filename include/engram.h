@@ -298,6 +298,24 @@ int engram_pack_fixed_capacity(const void* src, int64_t src_rows, int64_t row_by
 int engram_unpack_fixed_capacity(const void* src, int64_t row_bytes, const int64_t* split_sizes, int32_t world,
                                  int64_t capacity, void* dst, int64_t dst_rows, int64_t* status, hipStream_t stream);
 
+/* The requester's return path in one pass (engram API page,
+ * _fixed_capacity_all_to_all restores the compact source-ordered rows after the
+ * collective, and Qwen3_8_FlashNextOwnerShardedEmbedding.forward returns values
+ * in the original request order): compact row k, the k-th row that
+ * engram_unpack_fixed_capacity would write (block w's first
+ * min(split_sizes[w], capacity) rows, in rank order), is written to dst row
+ * order[k], as engram_unpermute_rows would move it; order is the request
+ * position of each grouped entry (engram_route_plan), dst has n rows.  Equals
+ * engram_unpack_fixed_capacity into an n-row buffer followed by
+ * engram_unpermute_rows, except that a dst row whose compact row does not exist
+ * (counts summing below n) is left as it was.  Compact rows at or past n are
+ * dropped; order entries outside [0, n) are skipped.  *status (device or NULL)
+ * = lowest rank whose split size is negative or above capacity, world if the
+ * compact rows exceed n, else -1. */
+int engram_unpack_unpermute_rows(const void* src, int64_t row_bytes, const int64_t* split_sizes, int32_t world,
+                                 int64_t capacity, const int64_t* order, int64_t n, void* dst, int64_t* status,
+                                 hipStream_t stream);
+
 /* dst[i] = src[order[i]] (into grouped order) and dst[order[i]] = src[i] (back to
  * request order), rows of row_bytes; an order entry outside [0, n) is skipped. */
 int engram_permute_rows(const void* src, int64_t row_bytes, const int64_t* order, int64_t n, void* dst,

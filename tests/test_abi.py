@@ -190,6 +190,15 @@ def test_route_entry_points_reject_bad_arguments(lib):
     assert lib.engram_unpack_fixed_capacity(f, 320, f, 8, 16, f, -1, None, None) == B.ENGRAM_EINVAL
     assert lib.engram_permute_rows(f, 6, f, 10, f, None) == B.ENGRAM_EINVAL
     assert lib.engram_unpermute_rows(None, 8, f, 10, f, None) == B.ENGRAM_EINVAL
+    # (src, row_bytes, split_sizes, world, capacity, order, n, dst, status, stream)
+    uu = lambda src=f, rb=320, cs=f, W=8, cap=16, order=f, n=100, dst=f: \
+        lib.engram_unpack_unpermute_rows(src, rb, cs, W, cap, order, n, dst, None, None)
+    assert uu(W=0) == B.ENGRAM_EINVAL and uu(W=256) == B.ENGRAM_EINVAL
+    assert uu(cap=-1) == B.ENGRAM_EINVAL and uu(n=-1) == B.ENGRAM_EINVAL
+    assert uu(rb=10) == B.ENGRAM_EINVAL                      # rows are whole 4-byte words
+    assert uu(cs=None) == B.ENGRAM_EINVAL
+    assert uu(order=None) == B.ENGRAM_EINVAL and uu(dst=None) == B.ENGRAM_EINVAL and uu(src=None) == B.ENGRAM_EINVAL
+    assert uu(order=ctypes.c_void_p(0x1004)) == B.ENGRAM_EINVAL  # int64 order, 8-byte aligned
 
 
 def test_ple_rejects_bad_arguments(lib):

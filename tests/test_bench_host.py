@@ -25,8 +25,7 @@ SUMMARIES = {
     "norm_fwd_ple_counters.txt": "ple.hip",
     "norm_bwd_ple_counters.txt": "ple.hip",
     "pack_values_route_counters.txt": "route.hip",
-    "unpack_values_route_counters.txt": "route.hip",
-    "unpermute_values_route_counters.txt": "route.hip",
+    "unpack_unpermute_values_route_counters.txt": "route.hip",
 }
 
 

@@ -143,6 +143,10 @@ def test_routing_buffers():
         E.engram_permute_rows(bf16(9, 160), i64(10))
     with pytest.raises(ValueError, match=SIZE):
         E.engram_unpermute_rows(bf16(10, 160), i64(10), out=bf16(9, 160))
+    with pytest.raises(ValueError, match=SIZE):
+        E.engram_unpack_unpermute_rows(bf16(4, 8, 160), counts, i64(20), out=bf16(19, 160))
+    with pytest.raises(ValueError, match=SIZE):
+        E.engram_unpack_unpermute_rows(bf16(4, 8, 160), i64(3), i64(20))
 
 
 @pytest.mark.gpu

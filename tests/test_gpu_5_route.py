@@ -257,3 +257,85 @@ def test_route_bench_shape():
     ref_out = np.empty_like(vals_h)
     ref_out[ro] = vals_h
     assert np.array_equal(out.cpu().view(torch.int16).numpy(), ref_out)
+    fused = E.engram_unpack_unpermute_rows(packed, c, order, status=status)   # the two calls in one pass
+    assert int(status.item()) == -1
+    assert np.array_equal(fused.cpu().view(torch.int16).numpy(), ref_out)
+
+
+def unpack_unpermute_ref(packed, counts, order, before):
+    """The oracle's unpack into n rows, then each compact row k that exists moved
+    to row order[k] of `before` (rows without a compact row keep their values)."""
+    n = order.size
+    compact, bad = RR.unpack(packed, counts, n)
+    world, capacity = packed.shape[:2]
+    total = int(sum(max(0, min(int(c), capacity)) for c in counts))
+    out = before.copy()
+    for k in range(min(total, n)):
+        if 0 <= order[k] < n:
+            out[order[k]] = compact[k]
+    return out, bad
+
+
+@pytest.mark.parametrize("dtype,row,world", [(torch.int64, (), 8), (torch.bfloat16, (160,), 64),
+                                             (torch.int32, (3,), 5), (torch.bfloat16, (160,), 1),
+                                             (torch.int16, (2, 4), 255)])
+def test_unpack_unpermute_parity(dtype, row, world):
+    """The fused return path equals the oracle's unpack followed by the move to
+    request order, and the two library calls it replaces, bit for bit (16-byte
+    and 4-byte row units, one to 255 ranks)."""
+    rng = np.random.default_rng(world)
+    capacity = 97
+    counts = rng.integers(1, capacity + 1, size=world).astype(np.int64)
+    if world > 1:
+        counts[world // 2] = 0
+    n = int(counts.sum())
+    packed = torch.from_numpy(rng.standard_normal((world, capacity) + row) * 100).to(dtype).cuda()
+    order = torch.from_numpy(rng.permutation(n).astype(np.int64)).cuda()
+    c = torch.from_numpy(counts).cuda()
+    status = torch.empty((), dtype=torch.int64, device="cuda")
+    fused = E.engram_unpack_unpermute_rows(packed, c, order, status=status)
+    assert int(status.item()) == -1
+    two = E.engram_unpermute_rows(E.engram_unpack_fixed_capacity(packed, c, n), order)
+    view = (lambda t: t.cpu().view(torch.int16).numpy()) if dtype == torch.bfloat16 else (lambda t: t.cpu().numpy())
+    assert np.array_equal(view(fused), view(two))
+    ref, bad = unpack_unpermute_ref(view(packed), counts, order.cpu().numpy(), view(fused))
+    assert bad == -1 and np.array_equal(view(fused), ref)
+
+
+def test_unpack_unpermute_bad_counts_and_orders():
+    """Counts that are negative, above the capacity, or sum past n, and order
+    entries outside [0, n): the status is the unpack's, compact rows at or past
+    n are dropped, bad order entries are skipped, and rows without a compact
+    row keep what they held."""
+    rng = np.random.default_rng(21)
+    world, capacity = 6, 40
+    packed_h = rng.integers(-1000, 1000, size=(world, capacity, 3)).astype(np.int64)
+    packed = torch.from_numpy(packed_h).cuda()
+    status = torch.empty((), dtype=torch.int64, device="cuda")
+    cases = [(np.array([12, -3, 55, 0, 40, 7]), 90),     # negative (rank 1) and above capacity (rank 2)
+             (np.array([12, 3, 30, 0, 40, 7]), 80),      # 92 compact rows for 80: dropped past n, status world
+             (np.array([12, 3, 30, 0, 20, 7]), 90)]      # 72 compact rows for 90: 18 rows keep their values
+    for counts, n in cases:
+        order_h = rng.permutation(n).astype(np.int64)
+        order_h[rng.random(n) < 0.05] = n + 3             # skipped
+        order_h[0] = -1
+        before = np.full((n, 3), -77, dtype=np.int64)
+        out = torch.from_numpy(before).cuda()
+        E.engram_unpack_unpermute_rows(packed, torch.from_numpy(counts).cuda(), torch.from_numpy(order_h).cuda(),
+                                       status=status, out=out)
+        ref, bad = unpack_unpermute_ref(packed_h, counts, order_h, before)
+        assert int(status.item()) == bad
+        assert np.array_equal(out.cpu().numpy(), ref)
+
+
+def test_unpack_unpermute_empty():
+    """No rows at all (zero capacity, or counts all zero), and the two calls it
+    replaces on empty inputs."""
+    status = torch.empty((), dtype=torch.int64, device="cuda")
+    none = torch.zeros(0, dtype=torch.int64, device="cuda")
+    zeros = torch.zeros(4, dtype=torch.int64, device="cuda")
+    for cap in (0, 5):
+        packed = torch.zeros((4, cap, 160), dtype=torch.bfloat16, device="cuda")
+        out = E.engram_unpack_unpermute_rows(packed, zeros, none, status=status)
+        assert out.shape == (0, 160) and int(status.item()) == -1
+        assert E.engram_unpermute_rows(E.engram_unpack_fixed_capacity(packed, zeros, 0), none).shape == (0, 160)
