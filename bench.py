@@ -644,6 +644,7 @@ def route_build(rotations, dev, world=64):
         t["vals"] = torch.randn((n, W.DIM), generator=g, device=dev).to(torch.bfloat16)
         t["vals_packed"] = torch.empty((world, cap, W.DIM), dtype=torch.bfloat16, device=dev)
         t["vals_out"] = torch.empty((n, W.DIM), dtype=torch.bfloat16, device=dev)
+        t["grads_grouped"] = torch.empty((n, W.DIM), dtype=torch.bfloat16, device=dev)  # two-call comparison only
         rots.append(t)
     return {"rots": rots, "world": world, "num_embeddings": W.FULL_ROWS}
 
@@ -701,6 +702,49 @@ def route_cpu_baseline(wl, target_seconds=10.0):
             "sample": "%d passes over the %d rotations in turn (%d lookups in all, world %d), plain Python loops "
                       "over segments with numpy arrays, single-threaded" % (passes, len(host), lookups, W_),
             "seconds": round(spent, 3)}
+
+
+def route_backward_send(wl, k, compare):
+    """The backward's send, timed after the steps and outside their clock: the
+    gradient rows (request order; the returned values stand in for them) taken
+    into grouped order and packed to the capacity in one pass
+    (engram_permute_pack_rows); with `compare`, also the two calls it replaces.
+    Median of k launches, HIP events on the stream they run on."""
+    import torch
+
+    import hashed_gram_embedding_engram_amd as E
+    import workloads as W
+    R, W_ = len(wl["rots"]), wl["world"]
+
+    def median_ms(fn):
+        ms = []
+        for i in range(k + 2):
+            t = wl["rots"][i % R]
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            fn(t)
+            b.record()
+            torch.cuda.synchronize()
+            ms.append(a.elapsed_time(b))
+        ms = sorted(ms[2:])
+        return ms[len(ms) // 2]
+
+    fused = median_ms(lambda t: E.engram_permute_pack_rows(t["vals_out"], t["order"], t["counts"], W_, t["cap"],
+                                                           fill=0, out=t["vals_packed"]))
+    n = sum(t["n"] for t in wl["rots"]) / R
+    cap = sum(t["cap"] for t in wl["rots"]) / R
+    row = 2.0 * W.DIM
+    alg = row * n + 8.0 * n + row * W_ * cap   # rows and positions read, the padded blocks written
+    out = {"kernel": "permute_pack_kernel<u32x4,uint32_t,2>", "ms": round(fused, 4),
+           "gbps_algorithmic": round(alg / (fused / 1e3) / 1e9, 1), "algorithmic_bytes_per_launch": alg,
+           "traffic": counter_traffic("route.hip", "backward_send_route_counters.txt"),
+           "from": "median of %d launches with HIP events, after the timed steps" % k}
+    if compare:
+        def two(t):
+            E.engram_permute_rows(t["vals_out"], t["order"], out=t["grads_grouped"])
+            E.engram_pack_fixed_capacity(t["grads_grouped"], t["counts"], W_, t["cap"], fill=0, out=t["vals_packed"])
+        out["two_calls_ms"] = round(median_ms(two), 4)
+    return out
 
 
 def route_main(args, dev):
@@ -763,6 +807,7 @@ def route_main(args, dev):
         "phase_algorithmic_bytes": alg,
         "cpu_baseline": None,
     }
+    result["backward_send"] = route_backward_send(wl, min(args.steps, 20), compare=not args.no_alone)
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = route_cpu_baseline(wl)
     print(json.dumps(result), flush=True)
@@ -1011,14 +1056,15 @@ PROFILED = {
               "pack_ids": ("route.hip", [r"\bpack_kernel<unsigned int,"]),
               "unpack_ids": ("route.hip", [r"\bunpack_kernel<unsigned int,"]),
               "pack_values": ("route.hip", [r"\bpack_kernel<u32x4"]),
-              "unpack_unpermute_values": ("route.hip", [r"\bunpack_unpermute_kernel<u32x4"])},
+              "unpack_unpermute_values": ("route.hip", [r"\bunpack_unpermute_kernel<u32x4"]),
+              "backward_send": ("route.hip", [r"\bpermute_pack_kernel<u32x4"])},
 }
 # Phases whose counter summaries are written (the ones a bench line can name
 # as its dominant kernel).
 COUNTED = {"long": ["gather", "scatter_plan", "scatter_apply"], "full-sft": ["gather"],
            "owner": ["gather", "scatter_plan", "scatter_apply"],
            "ple": ["conv_fwd", "norm_fwd", "norm_bwd", "conv_bwd"],
-           "route": ["pack_values", "unpack_unpermute_values"]}
+           "route": ["pack_values", "unpack_unpermute_values", "backward_send"]}
 PROFILE_FLAGS = "--steps 5 --warmup 2 --no-cpu-baseline --no-alone --no-ceilings --no-extra-configs --calibrate-copy"
 TRACE_FILE = {"long": "kernel_trace_long_context.md", "full-sft": "kernel_trace_full_sft.md",
               "owner": "kernel_trace_owner.md", "ple": "kernel_trace_ple.md", "route": "kernel_trace_route.md"}
@@ -1029,7 +1075,8 @@ WORKLOAD_TEXT = {
     "route": "one request rank of a world-64 owner group: 8 x 4,096 Zipf(1.2) tokens hashed into 524,288 "
              "full-table row IDs; per step: group by owner (route keys, then one radix digit pass that writes the grouped IDs, positions and counts), "
              "segment validation, pack of the IDs to the step's capacity, the owner's unpack, the owner's pack "
-             "of 320-B bf16 value rows, and the requester's unpack straight into request order (one pass)",
+             "of 320-B bf16 value rows, and the requester's unpack straight into request order (one pass); after the "
+             "steps, the backward's send (gradient rows into grouped order and packed, one pass) timed on its own",
 }
 
 
@@ -1166,6 +1213,8 @@ def summarize_profiles(name, raw):
 
     # counter summaries of the phases whose algorithmic bytes the line states
     alg = dict(line.get("phase_algorithmic_bytes") or {})
+    if "backward_send" in line:   # the routing line's extra measurement
+        alg["backward_send"] = line["backward_send"]["algorithmic_bytes_per_launch"]
     comp = dict(alg)
     if name in LOOKUP_WORKLOADS:
         cfg = line["config"]

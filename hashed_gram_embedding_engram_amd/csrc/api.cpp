@@ -71,11 +71,26 @@ int hash_common(const int64_t* tokens, int64_t batch, int64_t seq_len, int64_t s
 }  // namespace
 
 namespace engram {
-// The fused unpack and move to request order (route.hip).
+// The fused routing copies (route.hip): the unpack with the move to request
+// order, and the move to grouped order with the pack.
 hipError_t launch_unpack_unpermute(const void* src, int64_t row_bytes, const int64_t* counts, int world,
                                   int64_t capacity, const int64_t* order, int64_t n, void* dst, int64_t* status,
                                   hipStream_t stream);
+hipError_t launch_permute_pack(const void* src, int64_t row_bytes, const int64_t* order, int64_t n,
+                               const int64_t* counts, int world, int64_t capacity, const uint32_t fill16[4], void* dst,
+                               int64_t* status, hipStream_t stream);
 }  // namespace engram
+
+namespace {
+// The fill element (1, 2, 4 or 8 bytes) repeated over 16 bytes, as four words.
+void fill_words(const void* fill, int fill_bytes, uint32_t fill16[4]) {
+    unsigned char bytes[16];
+    for (int i = 0; i < 16; ++i) bytes[i] = ((const unsigned char*)fill)[i % fill_bytes];
+    for (int i = 0; i < 4; ++i)
+        fill16[i] = (uint32_t)bytes[4 * i] | ((uint32_t)bytes[4 * i + 1] << 8) | ((uint32_t)bytes[4 * i + 2] << 16) |
+                    ((uint32_t)bytes[4 * i + 3] << 24);
+}
+}  // namespace
 
 extern "C" {
 
@@ -271,13 +286,27 @@ int engram_pack_fixed_capacity(const void* src, int64_t src_rows, int64_t row_by
     if ((int64_t)world * capacity > ((int64_t)1 << 40) / row_bytes || src_rows > ((int64_t)1 << 40) / row_bytes)
         return ENGRAM_EINVAL;
     uint32_t fill16[4];
-    unsigned char bytes[16];
-    for (int i = 0; i < 16; ++i) bytes[i] = ((const unsigned char*)fill)[i % fill_bytes];
-    for (int i = 0; i < 4; ++i)
-        fill16[i] = (uint32_t)bytes[4 * i] | ((uint32_t)bytes[4 * i + 1] << 8) | ((uint32_t)bytes[4 * i + 2] << 16) |
-                    ((uint32_t)bytes[4 * i + 3] << 24);
+    fill_words(fill, fill_bytes, fill16);
     return launch_result(
         engram::launch_pack(src, src_rows, row_bytes, split_sizes, world, capacity, fill16, dst, status, stream));
+}
+
+int engram_permute_pack_rows(const void* src, int64_t row_bytes, const int64_t* order, int64_t n,
+                             const int64_t* split_sizes, int32_t world, int64_t capacity, const void* fill,
+                             int32_t fill_bytes, void* dst, int64_t* status, hipStream_t stream) {
+    if (world < 1 || world > 255 || capacity < 0 || n < 0 || !row_layout_ok(row_bytes) || !split_sizes)
+        return ENGRAM_EINVAL;
+    if (!(fill_bytes == 1 || fill_bytes == 2 || fill_bytes == 4 || fill_bytes == 8) || !fill) return ENGRAM_EINVAL;
+    if (row_bytes % fill_bytes != 0) return ENGRAM_EINVAL;
+    if (capacity > 0 && (!dst || (n > 0 && (!src || !order)))) return ENGRAM_EINVAL;
+    if (!aligned(src, 4) || !aligned(dst, 4) || !aligned(order, 8) || !aligned(split_sizes, 8) || !aligned(status, 8))
+        return ENGRAM_EINVAL;
+    if ((int64_t)world * capacity > ((int64_t)1 << 40) / row_bytes || n > ((int64_t)1 << 40) / row_bytes)
+        return ENGRAM_EINVAL;
+    uint32_t fill16[4];
+    fill_words(fill, fill_bytes, fill16);
+    return launch_result(engram::launch_permute_pack(src, row_bytes, order, n, split_sizes, world, capacity, fill16,
+                                                     dst, status, stream));
 }
 
 int engram_unpack_fixed_capacity(const void* src, int64_t row_bytes, const int64_t* split_sizes, int32_t world,

@@ -19,7 +19,8 @@
 //   pack / unpack  compact segments <-> [world][capacity] padded blocks.
 //   permute        rows into / out of the grouped order.
 //   unpack_unpermute  the requester's unpack and the move back to request
-//                  order in one pass.
+//                  order in one pass; permute_pack  the move into grouped
+//                  order and the pack in one pass (the backward's send).
 // The collective itself (RCCL all-to-all over xGMI) is outside this library.
 #include <algorithm>
 
@@ -265,6 +266,50 @@ __global__ __launch_bounds__(kBlock) void unpack_kernel(const U* __restrict__ sr
     }
 }
 
+// The move into grouped order and the pack in one pass (the requester's send
+// of gradient rows in the backward): block w's row r is grouped row
+// k = offset of w + r, read from request position order[k]; rows past the
+// kept count, past n, or whose order entry lies outside [0, n) take the fill.
+// Block rows are written in order, so the stores are non-temporal (as the
+// pack's).
+template <typename U, typename I, int K>
+__global__ __launch_bounds__(kBlock) void permute_pack_kernel(const U* __restrict__ src, int64_t row_units,
+                                                              const int64_t* __restrict__ order, int64_t n,
+                                                              const int64_t* __restrict__ counts, int world,
+                                                              int64_t capacity, u32x4 fill, U* __restrict__ dst,
+                                                              int64_t* __restrict__ status) {
+    const int w = blockIdx.y;
+    const SegmentInfo si = segment_info(counts, world, w, capacity, false);
+    const int64_t c = counts[w];
+    const int64_t kept = c < 0 ? 0 : (c > capacity ? capacity : c);
+    const int64_t avail = min(kept, max((int64_t)0, n - si.off));  // kept rows that exist in the grouped order
+    if (blockIdx.x == 0 && threadIdx.x == 0) {
+        if (c < 0 || c > capacity) report_bad(status, w);
+        if (avail < kept) report_bad(status, world);
+    }
+    const I rows = (I)avail;
+    const I units = (I)row_units, seg_units = (I)(capacity * row_units);
+    const int64_t* __restrict__ ord = order + min(si.off, n);
+    U* __restrict__ d = dst + (int64_t)w * capacity * row_units;
+    const I step = (I)gridDim.x * (I)(kBlock * K);
+    for (I e0 = (I)blockIdx.x * (I)(kBlock * K) + threadIdx.x; e0 < seg_units; e0 += step) {
+        U v[K];
+#pragma unroll
+        for (int k = 0; k < K; ++k) {
+            const I e = e0 + (I)(k * kBlock);
+            const I r = e / units;
+            const I q = e - r * units;
+            const int64_t o = (e < seg_units && r < rows) ? ord[r] : -1;
+            v[k] = (uint64_t)o < (uint64_t)n ? src[o * row_units + (int64_t)q] : fill_unit<U>(fill, (uint32_t)q);
+        }
+#pragma unroll
+        for (int k = 0; k < K; ++k) {
+            const I e = e0 + (I)(k * kBlock);
+            if (e < seg_units) __builtin_nontemporal_store(v[k], d + e);
+        }
+    }
+}
+
 // The unpack and the move back to request order in one pass: compact row k
 // (segment w's row r, k = offset of w + r, k < n) goes to dst row order[k];
 // an order entry outside [0, n) is skipped.  The block rows are read in
@@ -467,6 +512,25 @@ hipError_t launch_unpack_unpermute(const void* src, int64_t row_bytes, const int
         const int64_t units = row_bytes / 4;
         ENGRAM_SEGMENT_LAUNCH(unpack_unpermute_kernel, uint32_t, ENGRAM_UNPERMUTE_K, rows * units,
                               (const uint32_t*)src, units, counts, world, capacity, order, n, (uint32_t*)dst, status);
+    }
+    return hipGetLastError();
+}
+
+hipError_t launch_permute_pack(const void* src, int64_t row_bytes, const int64_t* order, int64_t n,
+                               const int64_t* counts, int world, int64_t capacity, const uint32_t fill16[4], void* dst,
+                               int64_t* status, hipStream_t stream) {
+    hipError_t err = launch_status_init(status, stream);
+    if (err != hipSuccess) return err;
+    const bool wide = row_bytes % 16 == 0 && ((uintptr_t)src % 16) == 0 && ((uintptr_t)dst % 16) == 0;
+    const u32x4 f = {fill16[0], fill16[1], fill16[2], fill16[3]};
+    if (wide) {
+        const int64_t units = row_bytes / 16;
+        ENGRAM_SEGMENT_LAUNCH(permute_pack_kernel, u32x4, 2, capacity * units, (const u32x4*)src, units, order, n,
+                              counts, world, capacity, f, (u32x4*)dst, status);
+    } else {
+        const int64_t units = row_bytes / 4;
+        ENGRAM_SEGMENT_LAUNCH(permute_pack_kernel, uint32_t, 4, capacity * units, (const uint32_t*)src, units, order,
+                              n, counts, world, capacity, f, (uint32_t*)dst, status);
     }
     return hipGetLastError();
 }

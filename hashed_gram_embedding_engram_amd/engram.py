@@ -412,6 +412,8 @@ def _bind_route(lib):
     lib.engram_unpermute_rows.argtypes = [p, i64, p, i64, p, p]
     lib.engram_unpack_unpermute_rows.restype = ctypes.c_int
     lib.engram_unpack_unpermute_rows.argtypes = [p, i64, p, i32, i64, p, i64, p, p, p]
+    lib.engram_permute_pack_rows.restype = ctypes.c_int
+    lib.engram_permute_pack_rows.argtypes = [p, i64, p, i64, p, i32, i64, p, i32, p, p, p]
     lib._route_bound = True
 
 
@@ -493,6 +495,28 @@ def engram_unpack_fixed_capacity(src, split_sizes, dst_rows, status=None, out=No
                                             _dev_ptr(dst, "dst", src.dtype, min_numel=dst_rows * (row_bytes // esize)),
                                             dst_rows, _status_ptr(status), _stream_handle(stream)),
            "engram_unpack_fixed_capacity")
+    return dst
+
+
+def engram_permute_pack_rows(src, order, split_sizes, world, capacity, fill=0, status=None, out=None, stream=None):
+    """Rows src [n, ...] in request order -> [world, capacity, ...]: grouped row k is
+    src[order[k]], packed as engram_pack_fixed_capacity packs; n = order.numel()."""
+    lib = _route_lib()
+    row_shape = tuple(src.shape[1:])
+    esize = src.element_size()
+    row_elems = int(torch.Size(row_shape).numel()) if row_shape else 1
+    row_bytes = esize * row_elems
+    n = order.numel()
+    dst = torch.empty((world, capacity) + row_shape, dtype=src.dtype, device=src.device) if out is None else out
+    fill_t = torch.tensor([fill], dtype=src.dtype)
+    fill_bytes = (ctypes.c_ubyte * esize).from_buffer_copy(fill_t.view(torch.uint8).numpy().tobytes())
+    _check(lib.engram_permute_pack_rows(_dev_ptr(src, "src", min_numel=n * row_elems), row_bytes,
+                                        _dev_ptr(order, "order", torch.int64), n,
+                                        _dev_ptr(split_sizes, "split_sizes", torch.int64, numel=world), world,
+                                        capacity, ctypes.cast(fill_bytes, ctypes.c_void_p), esize,
+                                        _dev_ptr(dst, "dst", src.dtype, shape=(world, capacity) + row_shape),
+                                        _status_ptr(status), _stream_handle(stream)),
+           "engram_permute_pack_rows")
     return dst
 
 

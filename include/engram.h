@@ -316,6 +316,21 @@ int engram_unpack_unpermute_rows(const void* src, int64_t row_bytes, const int64
                                  int64_t capacity, const int64_t* order, int64_t n, void* dst, int64_t* status,
                                  hipStream_t stream);
 
+/* The requester's send in the backward in one pass (engram API page,
+ * _FixedCapacityAllToAll.backward routes gradient rows back along the value
+ * route, and _fixed_capacity_all_to_all pads every segment to the agreed
+ * capacity with a fill): the gradient rows src [n][row], in request order, are
+ * taken in grouped order (grouped row k = src row order[k], as
+ * engram_permute_rows) and packed as engram_pack_fixed_capacity packs them:
+ * block w holds grouped rows offset(w) .. offset(w) + min(split_sizes[w],
+ * capacity) - 1 and the fill after them.  Equals engram_permute_rows followed
+ * by engram_pack_fixed_capacity with src_rows = n, except that a block row
+ * whose order entry lies outside [0, n) takes the fill.  *status as
+ * engram_pack_fixed_capacity with src_rows = n. */
+int engram_permute_pack_rows(const void* src, int64_t row_bytes, const int64_t* order, int64_t n,
+                             const int64_t* split_sizes, int32_t world, int64_t capacity, const void* fill,
+                             int32_t fill_bytes, void* dst, int64_t* status, hipStream_t stream);
+
 /* dst[i] = src[order[i]] (into grouped order) and dst[order[i]] = src[i] (back to
  * request order), rows of row_bytes; an order entry outside [0, n) is skipped. */
 int engram_permute_rows(const void* src, int64_t row_bytes, const int64_t* order, int64_t n, void* dst,

@@ -199,6 +199,13 @@ def test_route_entry_points_reject_bad_arguments(lib):
     assert uu(cs=None) == B.ENGRAM_EINVAL
     assert uu(order=None) == B.ENGRAM_EINVAL and uu(dst=None) == B.ENGRAM_EINVAL and uu(src=None) == B.ENGRAM_EINVAL
     assert uu(order=ctypes.c_void_p(0x1004)) == B.ENGRAM_EINVAL  # int64 order, 8-byte aligned
+    # (src, row_bytes, order, n, split_sizes, world, capacity, fill, fill_bytes, dst, status, stream)
+    pp = lambda src=f, rb=320, order=f, n=100, cs=f, W=8, cap=16, fill=ctypes.cast(one, ctypes.c_void_p), fb=2, dst=f: \
+        lib.engram_permute_pack_rows(src, rb, order, n, cs, W, cap, fill, fb, dst, None, None)
+    assert pp(W=0) == B.ENGRAM_EINVAL and pp(cap=-1) == B.ENGRAM_EINVAL and pp(n=-1) == B.ENGRAM_EINVAL
+    assert pp(rb=10) == B.ENGRAM_EINVAL and pp(fb=3) == B.ENGRAM_EINVAL and pp(fb=8, rb=12) == B.ENGRAM_EINVAL
+    assert pp(fill=None) == B.ENGRAM_EINVAL and pp(cs=None) == B.ENGRAM_EINVAL
+    assert pp(order=None) == B.ENGRAM_EINVAL and pp(src=None) == B.ENGRAM_EINVAL and pp(dst=None) == B.ENGRAM_EINVAL
 
 
 def test_ple_rejects_bad_arguments(lib):

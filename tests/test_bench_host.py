@@ -26,6 +26,7 @@ SUMMARIES = {
     "norm_bwd_ple_counters.txt": "ple.hip",
     "pack_values_route_counters.txt": "route.hip",
     "unpack_unpermute_values_route_counters.txt": "route.hip",
+    "backward_send_route_counters.txt": "route.hip",
 }
 
 

@@ -147,6 +147,10 @@ def test_routing_buffers():
         E.engram_unpack_unpermute_rows(bf16(4, 8, 160), counts, i64(20), out=bf16(19, 160))
     with pytest.raises(ValueError, match=SIZE):
         E.engram_unpack_unpermute_rows(bf16(4, 8, 160), i64(3), i64(20))
+    with pytest.raises(ValueError, match=SIZE):
+        E.engram_permute_pack_rows(bf16(19, 160), i64(20), counts, 4, 8)
+    with pytest.raises(ValueError, match=SIZE):
+        E.engram_permute_pack_rows(bf16(20, 160), i64(20), counts, 4, 8, out=bf16(4, 7, 160))
 
 
 @pytest.mark.gpu

@@ -339,3 +339,76 @@ def test_unpack_unpermute_empty():
         out = E.engram_unpack_unpermute_rows(packed, zeros, none, status=status)
         assert out.shape == (0, 160) and int(status.item()) == -1
         assert E.engram_unpermute_rows(E.engram_unpack_fixed_capacity(packed, zeros, 0), none).shape == (0, 160)
+
+
+def permute_pack_ref(src, order, counts, world, capacity, fill):
+    """The move into grouped order (grouped row k = src[order[k]], order entries
+    outside [0, n) leaving the fill), then the oracle's pack of the n grouped rows."""
+    n = order.size
+    grouped = np.empty((n,) + src.shape[1:], dtype=src.dtype)
+    grouped[...] = fill
+    ok = (order >= 0) & (order < n)
+    grouped[ok] = src[order[ok]]
+    return RR.pack(grouped, counts, world, capacity, fill)
+
+
+@pytest.mark.parametrize("dtype,row,world", [(torch.int64, (), 8), (torch.bfloat16, (160,), 64),
+                                             (torch.int32, (3,), 5), (torch.float32, (160,), 1),
+                                             (torch.int16, (2, 4), 255)])
+def test_permute_pack_parity(dtype, row, world):
+    """The backward's send in one pass equals the move into grouped order and the
+    pack (the oracle's, and the two library calls), bit for bit."""
+    rng = np.random.default_rng(100 + world)
+    capacity = 97
+    counts = rng.integers(1, capacity + 1, size=world).astype(np.int64)
+    if world > 1:
+        counts[world // 2] = 0
+    n = int(counts.sum())
+    src = torch.from_numpy(rng.standard_normal((n,) + row) * 100).to(dtype).cuda()
+    order = torch.from_numpy(rng.permutation(n).astype(np.int64)).cuda()
+    c = torch.from_numpy(counts).cuda()
+    status = torch.empty((), dtype=torch.int64, device="cuda")
+    fill = 7 if dtype != torch.float32 else -2.5
+    fused = E.engram_permute_pack_rows(src, order, c, world, capacity, fill=fill, status=status)
+    assert int(status.item()) == -1
+    two = E.engram_pack_fixed_capacity(E.engram_permute_rows(src, order), c, world, capacity, fill=fill)
+    view = (lambda t: t.cpu().view(torch.int16).numpy()) if dtype == torch.bfloat16 else (lambda t: t.cpu().numpy())
+    assert np.array_equal(view(fused), view(two))
+    fill_ref = fill if dtype != torch.bfloat16 else int(torch.tensor([fill], dtype=dtype).view(torch.int16))
+    ref, bad = permute_pack_ref(view(src), order.cpu().numpy(), counts, world, capacity, fill_ref)
+    assert bad == -1 and np.array_equal(view(fused), ref)
+
+
+def test_permute_pack_bad_counts_and_orders():
+    """Counts that are negative, above the capacity or past n, and order entries
+    outside [0, n): the status is the pack's, and those block rows take the fill."""
+    rng = np.random.default_rng(31)
+    world, capacity = 6, 40
+    status = torch.empty((), dtype=torch.int64, device="cuda")
+    for counts, n in [(np.array([12, -3, 55, 0, 40, 7]), 90), (np.array([12, 3, 30, 0, 40, 7]), 80),
+                      (np.array([12, 3, 30, 0, 20, 7]), 90)]:
+        src_h = rng.integers(-1000, 1000, size=(n, 3)).astype(np.int64)
+        order_h = rng.permutation(n).astype(np.int64)
+        order_h[rng.random(n) < 0.05] = n + 3
+        order_h[0] = -1
+        got = E.engram_permute_pack_rows(torch.from_numpy(src_h).cuda(), torch.from_numpy(order_h).cuda(),
+                                         torch.from_numpy(counts).cuda(), world, capacity, fill=-9, status=status)
+        ref, bad = permute_pack_ref(src_h, order_h, counts, world, capacity, -9)
+        assert int(status.item()) == bad
+        assert np.array_equal(got.cpu().numpy(), ref)
+
+
+def test_permute_pack_round_trip():
+    """The backward's send and the owner's unpack, then the forward's return path
+    packed by the owner: every row comes back to its request position."""
+    rng = np.random.default_rng(41)
+    world = 16
+    ids = torch.from_numpy(rng.integers(0, 16_000, size=20_000).astype(np.int64)).cuda()
+    s, order, c = E.engram_route_plan(ids, 16_000, world)
+    cap = int(c.max().item())
+    g = torch.from_numpy(rng.standard_normal((20_000, 160)).astype(np.float32)).cuda()
+    sent = E.engram_permute_pack_rows(g, order, c, world, cap)
+    grouped = E.engram_unpack_fixed_capacity(sent, c, 20_000)
+    assert torch.equal(grouped, g[order])
+    back = E.engram_unpack_unpermute_rows(E.engram_pack_fixed_capacity(grouped, c, world, cap), c, order)
+    assert torch.equal(back, g)
