@@ -1307,7 +1307,8 @@ def main():
                                    "them in order; row_expand reads 3,163,052 distinct random 320-B bf16 rows and "
                                    "writes them as 640-B fp32 rows; row_rmw adds 4 random 320-B bf16 rows into each "
                                    "of 156,202 distinct random 640-B fp32 rows of a 5,000,024-row array (read, add, "
-                                   "write back); GB/s = bytes moved / median of 10 launches")
+                                   "write back); the row probes launch one 16-row tile per wave; GB/s = bytes moved / median of 10 "
+                                   "launches")
         add_ceiling_fracs(result, ceilings)
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(wl)

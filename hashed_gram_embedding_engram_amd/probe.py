@@ -51,10 +51,18 @@ def _median_ms(fn, reps):
 RMW_READS = 4  # bf16 rows the rmw probe adds into each fp32 row
 
 
+def _tiles(rows):
+    """Blocks for one 16-row tile per wave (4 waves per block)."""
+    return max(1, (rows + 63) // 64)
+
+
 def measure_ceilings(dev, reps=10, stream_bytes=4 << 30, table_rows=25_000_000, lookups=4_194_304,
                      distinct=3_163_052, grid=8192, seed=0, dense_rows=5_000_024, dense_distinct=156_202,
                      dense_lookups=562_578):
-    """GB/s of each probe (bytes the kernel must move / median time).  The gather
+    """GB/s of each probe (bytes the kernel must move / median time).  The
+    streaming probes stride over their buffer with `grid` blocks; the row probes
+    launch one 16-row tile per wave (their fastest launch shape, as the lookup
+    kernels launch one unit of work per wave).  The gather
     reads `lookups` uniform-random 320-byte rows of a `table_rows`-row bf16 table;
     the expand reads `distinct` distinct rows of a `lookups`-row bf16 array in
     random order and writes them as fp32; the rmw adds RMW_READS random rows
@@ -71,13 +79,13 @@ def measure_ceilings(dev, reps=10, stream_bytes=4 << 30, table_rows=25_000_000, 
     table = torch.empty((table_rows, 160), dtype=torch.bfloat16, device=dev).fill_(1.0)
     idx = torch.randint(0, table_rows, (lookups,), generator=g, device=dev, dtype=torch.int64).to(torch.int32)
     dst = torch.empty((lookups, 160), dtype=torch.bfloat16, device=dev)
-    ms = _median_ms(lambda: run_probe(2, table, idx, lookups, dst, grid), reps)
+    ms = _median_ms(lambda: run_probe(2, table, idx, lookups, dst, _tiles(lookups)), reps)
     out["row_gather"] = lookups * (320 + 320 + 4) / ms / 1e6
     del table, idx, dst
     src = torch.empty((lookups, 160), dtype=torch.bfloat16, device=dev).fill_(1.0)
     idx = torch.randperm(lookups, generator=g, device=dev)[:distinct].to(torch.int32).contiguous()
     dst = torch.empty((distinct, 160), dtype=torch.float32, device=dev)
-    ms = _median_ms(lambda: run_probe(3, src, idx, distinct, dst, grid), reps)
+    ms = _median_ms(lambda: run_probe(3, src, idx, distinct, dst, _tiles(distinct)), reps)
     out["row_expand"] = distinct * (320 + 640 + 4) / ms / 1e6
     del src, idx, dst
     src = torch.empty((dense_lookups, 160), dtype=torch.bfloat16, device=dev).fill_(1.0)
@@ -86,7 +94,7 @@ def measure_ceilings(dev, reps=10, stream_bytes=4 << 30, table_rows=25_000_000, 
     rows = torch.randperm(dense_rows, generator=g, device=dev)[:dense_distinct]
     idx = torch.cat([reads, rows]).to(torch.int32).contiguous()
     dst = torch.zeros((dense_rows, 160), dtype=torch.float32, device=dev)
-    ms = _median_ms(lambda: run_probe(4, src, idx, dense_distinct, dst, grid), reps)
+    ms = _median_ms(lambda: run_probe(4, src, idx, dense_distinct, dst, _tiles(dense_distinct)), reps)
     out["row_rmw"] = dense_distinct * (RMW_READS * (320 + 4) + 640 + 640 + 4) / ms / 1e6
     del src, reads, rows, idx, dst
     torch.cuda.empty_cache()
