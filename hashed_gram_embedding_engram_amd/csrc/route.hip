@@ -332,7 +332,7 @@ __global__ __launch_bounds__(kBlock) void unpack_unpermute_kernel(const U* __res
     const int64_t fit = min(rows, max((int64_t)0, n - si.off));  // compact rows of this segment below n
     const I units = (I)row_units, seg_units = (I)(fit * row_units);
     const U* __restrict__ s = src + (int64_t)w * capacity * row_units;
-    const int64_t* __restrict__ ord = order + si.off;
+    const int64_t* __restrict__ ord = order + min(si.off, n);  // fit is 0 past n
     const I step = (I)gridDim.x * (I)(kBlock * K);
     for (I e0 = (I)blockIdx.x * (I)(kBlock * K) + threadIdx.x; e0 < seg_units; e0 += step) {
         int64_t at[K];  // destination unit, or -1
