@@ -5,7 +5,8 @@
  * (engram_hash), head rows -> table values (engram_gather), and output
  * gradients -> per-row gradient sums (engram_scatter_add).  Around them: the
  * single-GPU half of the row-owner exchange (engram_route_*, pack/unpack,
- * permute) and the PLE layer's causal short convolution and grouped RMSNorm
+ * permute, and one-pass forms of the requester's copies) and the PLE layer's
+ * causal short convolution and grouped RMSNorm
  * (engram_short_conv*, engram_grouped_rms_norm*), each declared with the
  * passage that defines it.
  *
@@ -28,7 +29,9 @@
  * Conventions for every call:
  *   - Pointers named "device" point to GPU memory owned by the caller; the
  *     library allocates nothing and keeps no mutable global state, so calls on
- *     different streams are independent and the library is thread-safe.
+ *     different streams are independent and the library is thread-safe.  The
+ *     one exception is engram_scatter_add_noalloc, whose workspace is a fixed
+ *     device array that its calls on one GPU share (see its declaration).
  *   - Work is enqueued asynchronously on `stream` (0 = the null stream); a
  *     returned ENGRAM_OK means "launched", results are ready when the stream is.
  *   - Host-checkable argument errors return a negative engram_status at once
