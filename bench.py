@@ -157,6 +157,14 @@ def build_workload(name, rotations, dev, table=None):
             all_rows = E.engram_hash(tokens, spec).reshape(-1)
             owner_rows = all_rows[all_rows < W.OWNER_ROWS].contiguous()
             tokens, rows = None, owner_rows
+            # The same rows as the exchange delivers them: each request rank's
+            # segment in its own block of the agreed capacity.
+            recv_counts = (all_rows.view(64, -1) < W.OWNER_ROWS).sum(1).to(torch.int64).contiguous()
+            cap = int(recv_counts.max().item())
+            recv = {"counts": recv_counts, "capacity": cap,
+                    "ids": E.engram_pack_fixed_capacity(owner_rows, recv_counts, 64, cap, fill=-1),
+                    "vals": torch.empty((64, cap, W.DIM), dtype=torch.bfloat16, device=dev)}
+            del all_rows
         n = rows.numel()
         g = torch.Generator(device=dev)
         g.manual_seed(1000 + r)
@@ -164,6 +172,8 @@ def build_workload(name, rotations, dev, table=None):
              "out": torch.empty((n, W.DIM), dtype=torch.bfloat16, device=dev),
              "status": torch.empty((), dtype=torch.int64, device=dev),
              "plan_status": torch.empty((), dtype=torch.int64, device=dev)}
+        if name == "owner":
+            b["recv"] = recv
         if name in ("long", "owner"):
             b["dy"] = torch.randn((n, W.DIM), generator=g, device=dev).to(torch.bfloat16)
         if name == "long":
@@ -704,6 +714,56 @@ def route_cpu_baseline(wl, target_seconds=10.0):
             "seconds": round(spent, 3)}
 
 
+def owner_response(wl, k, compare, distinct):
+    """The owner's forward response, timed after the steps and outside their
+    clock: its lookup straight from the received padded ID blocks into padded
+    value blocks (engram_gather_padded); with `compare`, also the three calls it
+    replaces (unpack of the IDs, gather, pack of the values).  Median of k
+    launches, HIP events on the stream they run on."""
+    import torch
+
+    import hashed_gram_embedding_engram_amd as E
+    import workloads as W
+    R = len(wl["batches"])
+
+    def median_ms(fn):
+        ms = []
+        for i in range(k + 2):
+            b = wl["batches"][i % R]
+            a, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            fn(b, b["recv"])
+            e.record()
+            torch.cuda.synchronize()
+            ms.append(a.elapsed_time(e))
+        ms = sorted(ms[2:])
+        return ms[len(ms) // 2]
+
+    fused = median_ms(lambda b, r: E.engram_gather_padded(wl["table"], r["ids"], r["counts"], wl["row_begin"],
+                                                          out=r["vals"], status=b["status"], validate=False))
+    n = sum(b["n"] for b in wl["batches"]) / R
+    padded = sum(64 * b["recv"]["capacity"] for b in wl["batches"]) / R
+    # the padded IDs read, a table row per ID, every padded value row written;
+    # compulsory: each distinct table row read once (rotation 0's count)
+    alg = 8.0 * padded + 320.0 * n + 320.0 * padded
+    comp = 8.0 * padded + 320.0 * distinct + 320.0 * padded
+    out = {"kernel": "gather_padded_kernel<20,16,true>", "ms": round(fused, 4),
+           "gbps_algorithmic": round(alg / (fused / 1e3) / 1e9, 1), "algorithmic_bytes_per_launch": alg,
+           "gbps_compulsory": round(comp / (fused / 1e3) / 1e9, 1), "compulsory_bytes_per_launch": comp,
+           "padded_rows": int(padded), "lookups": int(n),
+           "traffic": counter_traffic("route.hip", "owner_response_owner_counters.txt"),
+           "from": "median of %d launches with HIP events, after the timed steps" % k}
+    if compare:
+        def three(b, r):
+            ids = E.engram_unpack_fixed_capacity(r["ids"], r["counts"], b["n"], out=b["rows_recv"])
+            E.engram_gather(wl["table"], ids, wl["row_begin"], out=b["out"], status=b["status"], validate=False)
+            E.engram_pack_fixed_capacity(b["out"], r["counts"], 64, r["capacity"], fill=0, out=r["vals"])
+        for b in wl["batches"]:
+            b.setdefault("rows_recv", torch.empty_like(b["rows"]))
+        out["three_calls_ms"] = round(median_ms(three), 4)
+    return out
+
+
 def route_backward_send(wl, k, compare):
     """The backward's send, timed after the steps and outside their clock: the
     gradient rows (request order; the returned values stand in for them) taken
@@ -982,6 +1042,9 @@ def lookup_line(name, args, dev, table=None):
                                   "phases_gb": {k: round(v / 1e9, 4) for k, v in per.items()},
                                   "from": "FETCH_SIZE + WRITE_SIZE per launch in the committed rocprofv3 summaries of "
                                           "every phase of the step, over ms_per_step"}
+    if name == "owner":
+        result["owner_response"] = owner_response(wl, min(args.steps, 20), compare=not args.no_alone,
+                                                  distinct=u_fwd)
     if wl["backward"]:
         # What the step pays for the backward: the plan runs beside the
         # forward, so only what follows the forward's end counts (the wait for
@@ -1012,7 +1075,8 @@ CEILING_OF = {"scatter_apply": "row_expand", "scatter_apply_dense": "row_rmw"}
 
 # Fields of the other configurations' lines kept in the default line.
 EXTRA_KEYS = ("value", "unit", "ms_per_step", "config", "phases_ms", "roofline", "phase_gbps", "gather_alone",
-              "backward_in_step", "backward_plan_then_apply", "phases_alone_ms_p50", "distinct_rows_forward_rotation0", "step_traffic")
+              "backward_in_step", "backward_plan_then_apply", "phases_alone_ms_p50", "distinct_rows_forward_rotation0", "step_traffic",
+              "owner_response")
 
 
 def add_ceiling_fracs(result, ceilings):
@@ -1046,7 +1110,8 @@ LOOKUP_PHASES = {
 # Workloads that start from tokens run the fused hash-and-gather forward.
 FUSED_PHASES = dict(LOOKUP_PHASES, gather=("lookup.hip", [r"\bhash_gather_kernel"]))
 PROFILED = {
-    "long": FUSED_PHASES, "full-sft": FUSED_PHASES, "sft": FUSED_PHASES, "owner": LOOKUP_PHASES,
+    "long": FUSED_PHASES, "full-sft": FUSED_PHASES, "sft": FUSED_PHASES,
+    "owner": dict(LOOKUP_PHASES, owner_response=("route.hip", [r"\bgather_padded_kernel"])),
     "ple": {"conv_fwd": ("ple.hip", [r"\bshort_conv_fwd"]), "norm_fwd": ("ple.hip", [r"\brms_norm_fwd"]),
             "norm_bwd": ("ple.hip", [r"\brms_norm_bwd", r"\bcolumn_sum_kernel"]),
             "conv_bwd": ("ple.hip", [r"\bshort_conv_bwd", r"\bcolumn_sum_kernel"])},
@@ -1062,7 +1127,7 @@ PROFILED = {
 # Phases whose counter summaries are written (the ones a bench line can name
 # as its dominant kernel).
 COUNTED = {"long": ["gather", "scatter_plan", "scatter_apply"], "full-sft": ["gather"],
-           "owner": ["gather", "scatter_plan", "scatter_apply"],
+           "owner": ["gather", "scatter_plan", "scatter_apply", "owner_response"],
            "ple": ["conv_fwd", "norm_fwd", "norm_bwd", "conv_bwd"],
            "route": ["pack_values", "unpack_unpermute_values", "backward_send"]}
 PROFILE_FLAGS = "--steps 5 --warmup 2 --no-cpu-baseline --no-alone --no-ceilings --no-extra-configs --calibrate-copy"
@@ -1192,8 +1257,12 @@ def summarize_profiles(name, raw):
                "rotating input sets." % WORKLOAD_TEXT[name]
     else:
         desc = "%s; %d (token x head) lookups per step; 2 warm-up steps, 5 timed steps, then 5 steps with events " \
-               "around every phase; 4 rotating input sets.  In the step the plan (sort) runs on a second stream " \
-               "beside the gather, so the two share HBM." % (WORKLOAD_NAMES[name], line["config"]["lookups_per_step"])
+               "around every phase; 4 rotating input sets.  In the step the plan (sort) and the gather run on two " \
+               "streams side by side, so the two share HBM." % (WORKLOAD_NAMES[name],
+                                                                line["config"]["lookups_per_step"])
+        if "owner_response" in line:
+            desc += "  After the steps, the owner's lookup from the received padded ID blocks into padded value " \
+                    "blocks (owner_response) is launched on its own."
     title = WORKLOAD_NAMES.get(name) or line["config"]["workload"]
     lines = ["# Kernel trace: %s, one MI355X" % title, "",
              "Command (REPO = repository root on the MI355X machine):", "", "    " + cmds["trace"], "",
@@ -1225,6 +1294,9 @@ def summarize_profiles(name, raw):
         # compulsory bytes read each distinct table row once (rotation 0's count)
         comp = {"gather": 320.0 * line["distinct_rows_forward_rotation0"] + per_lookup - 320.0 * n,
                 "hash": alg["hash"]}
+        if "owner_response" in line:   # the owner line's extra measurement
+            alg["owner_response"] = line["owner_response"]["algorithmic_bytes_per_launch"]
+            comp["owner_response"] = line["owner_response"].get("compulsory_bytes_per_launch", alg["owner_response"])
         if "scatter_apply" in line["phase_gbps"]:
             alg["scatter_apply"] = comp["scatter_apply"] = line["roofline"]["algorithmic_bytes_per_launch"]
             alg["scatter_plan"] = comp["scatter_plan"] = sort_nominal_bytes(n, cfg["table_rows"],

@@ -79,6 +79,9 @@ hipError_t launch_unpack_unpermute(const void* src, int64_t row_bytes, const int
 hipError_t launch_permute_pack(const void* src, int64_t row_bytes, const int64_t* order, int64_t n,
                                const int64_t* counts, int world, int64_t capacity, const uint32_t fill16[4], void* dst,
                                int64_t* status, hipStream_t stream);
+hipError_t launch_gather_padded(const void* table, int elem_bytes, int64_t row_begin, int64_t num_rows, int dim,
+                                const int64_t* ids, const int64_t* counts, int world, int64_t capacity, void* out,
+                                int64_t* status, hipStream_t stream);
 }  // namespace engram
 
 namespace {
@@ -333,6 +336,23 @@ int engram_unpack_unpermute_rows(const void* src, int64_t row_bytes, const int64
         return ENGRAM_EINVAL;
     return launch_result(engram::launch_unpack_unpermute(src, row_bytes, split_sizes, world, capacity, order, n, dst,
                                                          status, stream));
+}
+
+int engram_gather_padded(const void* table, int32_t dtype, int64_t row_begin, int64_t num_rows, int32_t dim,
+                         const int64_t* ids, const int64_t* split_sizes, int32_t world, int64_t capacity, void* out,
+                         int64_t* status, hipStream_t stream) {
+    if (!dtype_ok(dtype)) return ENGRAM_EDTYPE;
+    int eb;
+    if (!row_bytes_ok(dtype, dim, &eb)) return ENGRAM_EINVAL;
+    if (world < 1 || world > 255 || capacity < 0 || num_rows < 0 || row_begin < 0 || !split_sizes)
+        return ENGRAM_EINVAL;
+    if (capacity > ((int64_t)1 << 40) / world) return ENGRAM_EINVAL;
+    if (capacity > 0 && (!ids || !out || (num_rows > 0 && !table))) return ENGRAM_EINVAL;
+    if (!aligned(table, 16) || !aligned(out, 16) || !aligned(ids, 8) || !aligned(split_sizes, 8) ||
+        !aligned(status, 8))
+        return ENGRAM_EINVAL;
+    return launch_result(engram::launch_gather_padded(table, eb, row_begin, num_rows, dim, ids, split_sizes, world,
+                                                      capacity, out, status, stream));
 }
 
 int engram_permute_rows(const void* src, int64_t row_bytes, const int64_t* order, int64_t n, void* dst,

@@ -20,11 +20,14 @@
 //   permute        rows into / out of the grouped order.
 //   unpack_unpermute  the requester's unpack and the move back to request
 //                  order in one pass; permute_pack  the move into grouped
-//                  order and the pack in one pass (the backward's send).
+//                  order and the pack in one pass (the backward's send);
+//   gather_padded  the owner's lookup from the received padded ID blocks
+//                  straight into padded value blocks.
 // The collective itself (RCCL all-to-all over xGMI) is outside this library.
 #include <algorithm>
 
 #include "radix_sort.h"
+#include "row_copy.h"
 
 // Units (16 or 4 bytes) per thread and loop step of the fused unpack: 2
 // measured best on the world-64 value rows (79 us against 87 us with 1).
@@ -356,6 +359,64 @@ __global__ __launch_bounds__(kBlock) void unpack_unpermute_kernel(const U* __res
     }
 }
 
+__device__ u32x4 kZeroRowChunk = {0u, 0u, 0u, 0u};  // never written
+
+// The owner's lookup on the exchange's padded blocks: padded entry e = (w, r)
+// holds a received ID when r < split_sizes[w] (a negative count has none),
+// otherwise padding.  Received IDs are looked up as the gather does (one
+// wave per G entries, the row copy of row_copy.h); padding and IDs outside
+// the shard give zero rows, and the lowest padded index holding an ID
+// outside the shard goes to status.  Same four-wave cap as the gather.
+template <int CPR, int G, bool ROW32>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 4))) void gather_padded_kernel(
+    const u32x4* __restrict__ table, int64_t row_begin, uint64_t num_rows, const int64_t* __restrict__ ids,
+    const int64_t* __restrict__ counts, int64_t capacity, int64_t total, u32x4* __restrict__ out,
+    int64_t* __restrict__ status) {
+    const int lane = threadIdx.x & 63;
+    const int64_t wave = (int64_t)blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6);
+    const int64_t n0 = wave * G;
+    if (n0 >= total) return;
+    uint64_t local = ~0ull;
+    if (lane < G && n0 + lane < total) {
+        const int64_t e = n0 + lane;
+        const int64_t w = e / capacity;
+        if (e - w * capacity < counts[w]) {
+            local = (uint64_t)ids[e] - (uint64_t)row_begin;
+            if (local >= num_rows) {
+                report_bad(status, e);
+                local = ~0ull;
+            }
+        }
+    }
+    copy_wave_rows<CPR, G, ROW32, false>(table, local, n0, total, out, lane, &kZeroRowChunk);
+}
+
+// Other row sizes: one 16-byte chunk per lane over the flattened output,
+// striding by the whole grid.
+__global__ __launch_bounds__(256) void gather_padded_generic_kernel(const u32x4* __restrict__ table,
+                                                                    int64_t row_begin, uint64_t num_rows,
+                                                                    const int64_t* __restrict__ ids,
+                                                                    const int64_t* __restrict__ counts,
+                                                                    int64_t capacity, int64_t total, int cpr,
+                                                                    u32x4* __restrict__ out,
+                                                                    int64_t* __restrict__ status) {
+    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+    for (int64_t f = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; f < total * cpr; f += stride) {
+        const int64_t e = f / cpr;
+        const int k = (int)(f - e * cpr);
+        const int64_t w = e / capacity;
+        u32x4 v = {0u, 0u, 0u, 0u};
+        if (e - w * capacity < counts[w]) {
+            const uint64_t local = (uint64_t)ids[e] - (uint64_t)row_begin;
+            if (local < num_rows)
+                v = table[(int64_t)local * cpr + k];
+            else if (k == 0)
+                report_bad(status, e);
+        }
+        __builtin_nontemporal_store(v, out + f);
+    }
+}
+
 // dst[i] = src[order[i]] (gather) or dst[order[i]] = src[i] (scatter); an
 // index outside [0, n) is skipped.
 template <typename U, bool GATHER, int K>
@@ -531,6 +592,41 @@ hipError_t launch_permute_pack(const void* src, int64_t row_bytes, const int64_t
         const int64_t units = row_bytes / 4;
         ENGRAM_SEGMENT_LAUNCH(permute_pack_kernel, uint32_t, 4, capacity * units, (const uint32_t*)src, units, order,
                               n, counts, world, capacity, f, (uint32_t*)dst, status);
+    }
+    return hipGetLastError();
+}
+
+hipError_t launch_gather_padded(const void* table, int elem_bytes, int64_t row_begin, int64_t num_rows, int dim,
+                                const int64_t* ids, const int64_t* counts, int world, int64_t capacity, void* out,
+                                int64_t* status, hipStream_t stream) {
+    hipError_t err = launch_status_init(status, stream);
+    const int64_t total = (int64_t)world * capacity;
+    if (err != hipSuccess || total == 0) return err;
+    const int cpr = dim * elem_bytes / 16;
+    const u32x4* t = (const u32x4*)table;
+    u32x4* o = (u32x4*)out;
+    const bool row32 = (uint64_t)num_rows < 0xFFFFFFFFull;
+    const int64_t kMaxItems = (int64_t)1 << 31;
+    const int g = cpr == 20 ? 16 : 8;
+    if ((cpr == 20 || cpr == 40) && (total + g - 1) / g * 64 <= kMaxItems) {
+        const int64_t waves = (total + g - 1) / g;
+        const dim3 grid((unsigned)((waves + 3) / 4)), block(256);
+        if (cpr == 20 && row32)
+            hipLaunchKernelGGL((gather_padded_kernel<20, 16, true>), grid, block, 0, stream, t, row_begin,
+                               (uint64_t)num_rows, ids, counts, capacity, total, o, status);
+        else if (cpr == 20)
+            hipLaunchKernelGGL((gather_padded_kernel<20, 16, false>), grid, block, 0, stream, t, row_begin,
+                               (uint64_t)num_rows, ids, counts, capacity, total, o, status);
+        else if (row32)
+            hipLaunchKernelGGL((gather_padded_kernel<40, 8, true>), grid, block, 0, stream, t, row_begin,
+                               (uint64_t)num_rows, ids, counts, capacity, total, o, status);
+        else
+            hipLaunchKernelGGL((gather_padded_kernel<40, 8, false>), grid, block, 0, stream, t, row_begin,
+                               (uint64_t)num_rows, ids, counts, capacity, total, o, status);
+    } else {
+        const int64_t grid = std::min((total * cpr + 255) / 256, kMaxItems / 256);
+        hipLaunchKernelGGL(gather_padded_generic_kernel, dim3((unsigned)grid), dim3(256), 0, stream, t, row_begin,
+                           (uint64_t)num_rows, ids, counts, capacity, total, cpr, o, status);
     }
     return hipGetLastError();
 }

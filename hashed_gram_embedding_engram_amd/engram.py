@@ -414,6 +414,8 @@ def _bind_route(lib):
     lib.engram_unpack_unpermute_rows.argtypes = [p, i64, p, i32, i64, p, i64, p, p, p]
     lib.engram_permute_pack_rows.restype = ctypes.c_int
     lib.engram_permute_pack_rows.argtypes = [p, i64, p, i64, p, i32, i64, p, i32, p, p, p]
+    lib.engram_gather_padded.restype = ctypes.c_int
+    lib.engram_gather_padded.argtypes = [p, i32, i64, i64, i32, p, p, i32, i64, p, p, p]
     lib._route_bound = True
 
 
@@ -496,6 +498,30 @@ def engram_unpack_fixed_capacity(src, split_sizes, dst_rows, status=None, out=No
                                             dst_rows, _status_ptr(status), _stream_handle(stream)),
            "engram_unpack_fixed_capacity")
     return dst
+
+
+def engram_gather_padded(table, ids, split_sizes, row_begin=0, out=None, status=None, validate=True, stream=None):
+    """The owner's lookup on received padded ID blocks ids int64 [world, capacity]
+    (block w's first split_sizes[w] entries are IDs) -> values [world, capacity, dim],
+    padding rows zero.  With ``validate`` the call synchronises and raises on an ID
+    outside the table's rows."""
+    lib = _route_lib()
+    if table.dim() != 2 or ids.dim() != 2:
+        raise ValueError("table must be [num_rows, dim] and ids [world, capacity]")
+    num_rows, dim = table.shape
+    world, capacity = ids.shape
+    if out is None:
+        out = torch.empty((world, capacity, dim), dtype=table.dtype, device=table.device)
+    if validate and status is None:
+        status = torch.empty((), dtype=torch.int64, device=table.device)
+    _check(lib.engram_gather_padded(_dev_ptr(table, "table", table.dtype), _dtype_code(table), row_begin, num_rows,
+                                    dim, _dev_ptr(ids, "ids", torch.int64),
+                                    _dev_ptr(split_sizes, "split_sizes", torch.int64, numel=world), world, capacity,
+                                    _dev_ptr(out, "out", table.dtype, shape=(world, capacity, dim)),
+                                    _status_ptr(status), _stream_handle(stream)), "engram_gather_padded")
+    if validate:
+        _raise_on_status(status, "engram_gather_padded", ids)
+    return out
 
 
 def engram_permute_pack_rows(src, order, split_sizes, world, capacity, fill=0, status=None, out=None, stream=None):

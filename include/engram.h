@@ -334,6 +334,23 @@ int engram_permute_pack_rows(const void* src, int64_t row_bytes, const int64_t* 
                              const int64_t* split_sizes, int32_t world, int64_t capacity, const void* fill,
                              int32_t fill_bytes, void* dst, int64_t* status, hipStream_t stream);
 
+/* The owner's lookup on the exchange's padded blocks in one pass (engram API
+ * page, Qwen3_8_FlashNextOwnerShardedEmbedding: owners look up the received
+ * IDs in their local rows and return the values through the same fixed-capacity
+ * exchange, _fixed_capacity_all_to_all).  ids: device int64 [world][capacity]
+ * as received; the first split_sizes[w] entries of block w are IDs (all of
+ * them for a count above capacity, none for a negative count), the rest is
+ * padding.  out: device [world][capacity][dim] of the table's dtype; an ID's
+ * row is looked up as engram_gather does (a zero row for an ID outside
+ * [row_begin, row_begin + num_rows)), padding rows are zero.  *status (device
+ * or NULL) = lowest padded index w * capacity + r holding an ID outside the
+ * shard, else -1.  Equals engram_unpack_fixed_capacity of the IDs,
+ * engram_gather and engram_pack_fixed_capacity of the values with a zero fill.
+ * Row sizes as engram_gather; 1 <= world <= 255. */
+int engram_gather_padded(const void* table, int32_t dtype, int64_t row_begin, int64_t num_rows, int32_t dim,
+                         const int64_t* ids, const int64_t* split_sizes, int32_t world, int64_t capacity, void* out,
+                         int64_t* status, hipStream_t stream);
+
 /* dst[i] = src[order[i]] (into grouped order) and dst[order[i]] = src[i] (back to
  * request order), rows of row_bytes; an order entry outside [0, n) is skipped. */
 int engram_permute_rows(const void* src, int64_t row_bytes, const int64_t* order, int64_t n, void* dst,

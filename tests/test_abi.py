@@ -206,6 +206,15 @@ def test_route_entry_points_reject_bad_arguments(lib):
     assert pp(rb=10) == B.ENGRAM_EINVAL and pp(fb=3) == B.ENGRAM_EINVAL and pp(fb=8, rb=12) == B.ENGRAM_EINVAL
     assert pp(fill=None) == B.ENGRAM_EINVAL and pp(cs=None) == B.ENGRAM_EINVAL
     assert pp(order=None) == B.ENGRAM_EINVAL and pp(src=None) == B.ENGRAM_EINVAL and pp(dst=None) == B.ENGRAM_EINVAL
+    # (table, dtype, row_begin, num_rows, dim, ids, split_sizes, world, capacity, out, status, stream)
+    gp = lambda table=f, dt=B.ENGRAM_BF16, rb=0, nr=1000, dim=160, ids=f, cs=f, W=8, cap=16, out=f: \
+        lib.engram_gather_padded(table, dt, rb, nr, dim, ids, cs, W, cap, out, None, None)
+    assert gp(dt=7) == B.ENGRAM_EDTYPE
+    assert gp(dim=0) == B.ENGRAM_EINVAL and gp(W=0) == B.ENGRAM_EINVAL and gp(W=256) == B.ENGRAM_EINVAL
+    assert gp(cap=-1) == B.ENGRAM_EINVAL and gp(nr=-1) == B.ENGRAM_EINVAL and gp(rb=-1) == B.ENGRAM_EINVAL
+    assert gp(cs=None) == B.ENGRAM_EINVAL and gp(ids=None) == B.ENGRAM_EINVAL and gp(out=None) == B.ENGRAM_EINVAL
+    assert gp(table=None) == B.ENGRAM_EINVAL
+    assert gp(out=ctypes.c_void_p(0x1008)) == B.ENGRAM_EINVAL   # rows of values are 16-byte aligned
 
 
 def test_ple_rejects_bad_arguments(lib):

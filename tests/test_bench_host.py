@@ -27,6 +27,7 @@ SUMMARIES = {
     "pack_values_route_counters.txt": "route.hip",
     "unpack_unpermute_values_route_counters.txt": "route.hip",
     "backward_send_route_counters.txt": "route.hip",
+    "owner_response_owner_counters.txt": "route.hip",
 }
 
 

@@ -412,3 +412,58 @@ def test_permute_pack_round_trip():
     assert torch.equal(grouped, g[order])
     back = E.engram_unpack_unpermute_rows(E.engram_pack_fixed_capacity(grouped, c, world, cap), c, order)
     assert torch.equal(back, g)
+
+
+@pytest.mark.parametrize("dtype,dim,world,row_begin", [(torch.bfloat16, 160, 64, 0), (torch.float32, 160, 8, 5000),
+                                                       (torch.bfloat16, 64, 5, 123), (torch.float32, 8, 1, 0)])
+def test_gather_padded_parity(dtype, dim, world, row_begin):
+    """The owner's lookup on padded ID blocks equals the unpack of the IDs, the
+    oracle's gather and the pack of the values with a zero fill, bit for bit
+    (the 16-row and 8-row wave kernels and the generic one)."""
+    rng = np.random.default_rng(world + dim)
+    num_rows, capacity = 20_000, 300
+    table = torch.from_numpy(rng.standard_normal((num_rows, dim)).astype(np.float32)).to(dtype).cuda()
+    counts = rng.integers(1, capacity + 1, size=world).astype(np.int64)
+    if world > 1:
+        counts[world // 2] = 0
+    n = int(counts.sum())
+    compact = rng.integers(row_begin, row_begin + num_rows, size=n).astype(np.int64)
+    ids_packed, _ = RR.pack(compact, counts, world, capacity, -1)
+    ids = torch.from_numpy(ids_packed).cuda()
+    c = torch.from_numpy(counts).cuda()
+    got = E.engram_gather_padded(table, ids, c, row_begin=row_begin)
+    view = (lambda t: t.cpu().view(torch.int16).numpy()) if dtype == torch.bfloat16 else (lambda t: t.cpu().numpy())
+    three = E.engram_pack_fixed_capacity(E.engram_gather(table, E.engram_unpack_fixed_capacity(ids, c, n),
+                                                         row_begin=row_begin), c, world, capacity, fill=0)
+    assert np.array_equal(view(got), view(three))
+    vals, gbad = c_oracle.gather(to_host(table), compact, row_begin)
+    ref, bad = RR.pack(vals, counts, world, capacity, 0)
+    assert gbad == -1 and bad == -1 and np.array_equal(to_host(got), ref)
+
+
+def test_gather_padded_bad_ids_and_counts():
+    """IDs outside the shard give zero rows and the lowest padded index; a
+    negative count has no IDs, a count above the capacity fills its block;
+    padding entries are never checked."""
+    rng = np.random.default_rng(5)
+    world, capacity, num_rows, row_begin = 4, 50, 1000, 300
+    table = torch.from_numpy(rng.standard_normal((num_rows, 160)).astype(np.float32)).cuda()
+    ids_h = rng.integers(row_begin, row_begin + num_rows, size=(world, capacity)).astype(np.int64)
+    counts = np.array([10, -2, 70, 25], dtype=np.int64)
+    ids_h[0, 40] = 5                      # padding of block 0: never checked
+    ids_h[2, 33] = row_begin + num_rows   # outside the shard
+    ids_h[3, 7] = -1                      # outside the shard, later block
+    status = torch.empty((), dtype=torch.int64, device="cuda")
+    got = E.engram_gather_padded(table, torch.from_numpy(ids_h).cuda(), torch.from_numpy(counts).cuda(),
+                                 row_begin=row_begin, status=status, validate=False).cpu().numpy()
+    assert int(status.item()) == 2 * capacity + 33
+    tab = table.cpu().numpy()
+    for w in range(world):
+        real = max(0, min(int(counts[w]), capacity))
+        for r in range(capacity):
+            i = ids_h[w, r] - row_begin
+            want = tab[i] if r < real and 0 <= i < num_rows else np.zeros(160, np.float32)
+            assert np.array_equal(got[w, r], want), (w, r)
+    with pytest.raises(E.EngramError):
+        E.engram_gather_padded(table, torch.from_numpy(ids_h).cuda(), torch.from_numpy(counts).cuda(),
+                               row_begin=row_begin)
