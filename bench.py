@@ -172,10 +172,12 @@ def build_workload(name, rotations, dev, table=None):
              "out": torch.empty((n, W.DIM), dtype=torch.bfloat16, device=dev),
              "status": torch.empty((), dtype=torch.int64, device=dev),
              "plan_status": torch.empty((), dtype=torch.int64, device=dev)}
-        if name == "owner":
-            b["recv"] = recv
         if name in ("long", "owner"):
             b["dy"] = torch.randn((n, W.DIM), generator=g, device=dev).to(torch.bfloat16)
+        if name == "owner":
+            # the output gradients as the exchange returns them to the owner
+            recv["dy"] = E.engram_pack_fixed_capacity(b["dy"], recv["counts"], 64, recv["capacity"], fill=0)
+            b["recv"] = recv
         if name == "long":
             b["compact"] = (torch.empty(n, dtype=torch.int64, device=dev),
                             torch.empty((n, W.DIM), dtype=torch.float32, device=dev),
@@ -764,6 +766,59 @@ def owner_response(wl, k, compare, distinct):
     return out
 
 
+def owner_backward_from_exchange(wl, k, compare):
+    """The owner's backward on what the exchange delivers, timed after the steps
+    and outside their clock: the plan over the received padded ID blocks and the
+    apply reading the received padded gradient blocks directly
+    (engram_scatter_add_plan_padded), one after the other on one stream; with
+    `compare`, the same after unpacking the IDs and the gradients first.
+    Median of k runs, HIP events."""
+    import torch
+
+    import hashed_gram_embedding_engram_amd as E
+    import workloads as W
+    R = len(wl["batches"])
+
+    def median_ms(fn):
+        ms = []
+        for i in range(k + 2):
+            b = wl["batches"][i % R]
+            a, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            fn(b, b["recv"])
+            e.record()
+            torch.cuda.synchronize()
+            ms.append(a.elapsed_time(e))
+        ms = sorted(ms[2:])
+        return ms[len(ms) // 2]
+
+    def padded(b, r):
+        m = 64 * r["capacity"]
+        E.engram_scatter_add_plan_padded(r["ids"], r["counts"], wl["table_rows"], W.DIM, wl["row_begin"],
+                                         workspace=wl["workspace_padded"], status=b["plan_status"])
+        E.engram_scatter_add_apply(r["dy"].view(m, W.DIM), m, wl["table_rows"], wl["workspace_padded"],
+                                   wl["row_begin"], grad_dense=wl["grad_dense"])
+
+    m_max = max(64 * b["recv"]["capacity"] for b in wl["batches"])
+    wl.setdefault("workspace_padded", torch.empty(E.engram_scatter_add_workspace(m_max, wl["table_rows"], W.DIM),
+                                                  dtype=torch.uint8, device=wl["table"].device))
+    out = {"plan_then_apply_ms": round(median_ms(padded), 4),
+           "from": "median of %d runs with HIP events, after the timed steps" % k}
+    if compare:
+        def unpacked(b, r):
+            E.engram_unpack_fixed_capacity(r["ids"], r["counts"], b["n"], out=b["rows_recv"])
+            E.engram_unpack_fixed_capacity(r["dy"], r["counts"], b["n"], out=b["dy_recv"])
+            E.engram_scatter_add_plan(b["rows_recv"], wl["table_rows"], W.DIM, wl["row_begin"],
+                                      workspace=wl["workspace"], status=b["plan_status"])
+            E.engram_scatter_add_apply(b["dy_recv"], b["n"], wl["table_rows"], wl["workspace"], wl["row_begin"],
+                                       grad_dense=wl["grad_dense"])
+        for b in wl["batches"]:
+            b.setdefault("rows_recv", torch.empty_like(b["rows"]))
+            b.setdefault("dy_recv", torch.empty_like(b["dy"]))
+        out["unpack_then_plan_then_apply_ms"] = round(median_ms(unpacked), 4)
+    return out
+
+
 def route_backward_send(wl, k, compare):
     """The backward's send, timed after the steps and outside their clock: the
     gradient rows (request order; the returned values stand in for them) taken
@@ -1045,6 +1100,9 @@ def lookup_line(name, args, dev, table=None):
     if name == "owner":
         result["owner_response"] = owner_response(wl, min(args.steps, 20), compare=not args.no_alone,
                                                   distinct=u_fwd)
+        if not args.no_alone:   # its plan and apply kernels would mix with the step's in a profile
+            result["owner_backward_from_exchange"] = owner_backward_from_exchange(wl, min(args.steps, 20),
+                                                                                  compare=True)
     if wl["backward"]:
         # What the step pays for the backward: the plan runs beside the
         # forward, so only what follows the forward's end counts (the wait for
@@ -1076,7 +1134,7 @@ CEILING_OF = {"scatter_apply": "row_expand", "scatter_apply_dense": "row_rmw"}
 # Fields of the other configurations' lines kept in the default line.
 EXTRA_KEYS = ("value", "unit", "ms_per_step", "config", "phases_ms", "roofline", "phase_gbps", "gather_alone",
               "backward_in_step", "backward_plan_then_apply", "phases_alone_ms_p50", "distinct_rows_forward_rotation0", "step_traffic",
-              "owner_response")
+              "owner_response", "owner_backward_from_exchange")
 
 
 def add_ceiling_fracs(result, ceilings):

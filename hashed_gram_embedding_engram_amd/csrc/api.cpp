@@ -82,6 +82,10 @@ hipError_t launch_permute_pack(const void* src, int64_t row_bytes, const int64_t
 hipError_t launch_gather_padded(const void* table, int elem_bytes, int64_t row_begin, int64_t num_rows, int dim,
                                 const int64_t* ids, const int64_t* counts, int world, int64_t capacity, void* out,
                                 int64_t* status, hipStream_t stream);
+// The backward's plan for rows as the exchange delivers them (scatter.hip).
+hipError_t launch_scatter_plan_padded(const int64_t* ids, const int64_t* counts, int world, int64_t capacity,
+                                      int64_t row_begin, int64_t num_rows, int dim, int64_t* uniq_rows,
+                                      int64_t* num_uniq, void* workspace, int64_t* status, hipStream_t stream);
 }  // namespace engram
 
 namespace {
@@ -178,6 +182,25 @@ int engram_scatter_add_plan(const int64_t* rows, int64_t n, int64_t row_begin, i
     if ((rc = workspace_check(workspace, workspace_bytes, n, num_rows, dim)) != ENGRAM_OK) return rc;
     return launch_result(engram::launch_scatter_plan(rows, n, row_begin, num_rows, dim, uniq_rows, num_uniq,
                                                      workspace, status, stream));
+}
+
+int engram_scatter_add_plan_padded(const int64_t* ids, const int64_t* split_sizes, int32_t world, int64_t capacity,
+                                   int64_t row_begin, int64_t num_rows, int32_t dim, int64_t* uniq_rows,
+                                   int64_t* num_uniq, void* workspace, size_t workspace_bytes, int64_t* status,
+                                   hipStream_t stream) {
+    if (world < 1 || world > 255 || capacity < 0 || !split_sizes) return ENGRAM_EINVAL;
+    if (capacity > ((int64_t)1 << 31) / world) return ENGRAM_EINVAL;
+    const int64_t n = (int64_t)world * capacity;
+    int eb;
+    int rc = scatter_check_common(ENGRAM_F32, dim, n, row_begin, num_rows, &eb);
+    if (rc != ENGRAM_OK) return rc;
+    if (n > 0 && !ids) return ENGRAM_EINVAL;
+    if (!aligned(ids, 8) || !aligned(split_sizes, 8) || !aligned(uniq_rows, 8) || !aligned(num_uniq, 8) ||
+        !aligned(status, 8))
+        return ENGRAM_EINVAL;
+    if ((rc = workspace_check(workspace, workspace_bytes, n, num_rows, dim)) != ENGRAM_OK) return rc;
+    return launch_result(engram::launch_scatter_plan_padded(ids, split_sizes, world, capacity, row_begin, num_rows,
+                                                            dim, uniq_rows, num_uniq, workspace, status, stream));
 }
 
 int engram_scatter_add_plan_from_tokens(const int64_t* tokens, int64_t batch, int64_t seq_len,

@@ -154,6 +154,13 @@ struct TokenRows {
     HashParams p;
 };
 constexpr int kTokenHeads = 16;
+// Rows as the exchange delivers them: [world][capacity] blocks whose first
+// counts[w] entries are rows and the rest padding (counts == nullptr: every
+// entry is a row).  Padding takes the sentinel key without a report.
+struct Padding {
+    const int64_t* counts;
+    uint32_t capacity;
+};
 
 // Step 1: keys, digit-0 tile histograms, in-range count.  A key's lookup
 // index is its position, so the first sort pass reads no value array.  With
@@ -167,7 +174,7 @@ __global__ __launch_bounds__(kBlock) void keys_kernel(const int64_t* __restrict_
                                                       int64_t row_begin, uint64_t num_rows,
                                                       uint32_t* __restrict__ keys, DigitCounts dc,
                                                       int64_t* __restrict__ status,
-                                                      uint32_t* __restrict__ counters) {
+                                                      uint32_t* __restrict__ counters, Padding pad) {
     constexpr int TILE = kBlock * ITEMS, TILE_POS = TILE / kTokenHeads;
     __shared__ uint32_t s_cnt[kBlock / 64][kRadix];
     __shared__ uint32_t s_valid;
@@ -230,11 +237,16 @@ __global__ __launch_bounds__(kBlock) void keys_kernel(const int64_t* __restrict_
         const uint32_t e = base + (uint32_t)it * 64 + (uint32_t)lane;
         if (e < n) {
             uint32_t key = sentinel;
+            bool real = true;
+            if (!TOKENS && pad.counts) {
+                const uint32_t seg = e / pad.capacity;
+                real = (int64_t)(e - seg * pad.capacity) < pad.counts[seg];
+            }
             const uint64_t local = (uint64_t)r[it] - (uint64_t)row_begin;
-            if (local < num_rows) {
+            if (real && local < num_rows) {
                 key = (uint32_t)local;
                 ++my_valid;
-            } else {
+            } else if (real) {
                 report_bad(status, e);
             }
             keys[e] = key;
@@ -921,8 +933,8 @@ hipError_t dispatch_reduce(const Layout& L, const char* ws, const void* grad_out
 
 // Steps 1-2: keys and the radix passes, ending in the sorted slots.
 template <int ITEMS>
-hipError_t run_sort(const Layout& L, char* ws, const int64_t* rows, const TokenRows* tr, int64_t n, int64_t row_begin,
-                    int64_t num_rows, int passes, int64_t* status, hipStream_t stream) {
+hipError_t run_sort(const Layout& L, char* ws, const int64_t* rows, const TokenRows* tr, Padding pad, int64_t n,
+                    int64_t row_begin, int64_t num_rows, int passes, int64_t* status, hipStream_t stream) {
     uint32_t* counters = (uint32_t*)(ws + L.counters);
     const size_t pass_words = count_words(L.num_tiles);  // chunk and group totals of one pass
     uint32_t* count_totals = (uint32_t*)(ws + L.count_totals);
@@ -940,10 +952,10 @@ hipError_t run_sort(const Layout& L, char* ws, const int64_t* rows, const TokenR
     auto pass_counts = [&](int p) { return make_digit_counts(ws + L.hist, count_totals + p * pass_words, L.num_tiles); };
     if (tr)
         hipLaunchKernelGGL((keys_kernel<ITEMS, true>), dim3(tiles), dim3(kBlock), 0, stream, nullptr, *tr, nn,
-                           row_begin, (uint64_t)num_rows, k_cur, pass_counts(0), status, counters);
+                           row_begin, (uint64_t)num_rows, k_cur, pass_counts(0), status, counters, Padding{});
     else
         hipLaunchKernelGGL((keys_kernel<ITEMS, false>), dim3(tiles), dim3(kBlock), 0, stream, rows, TokenRows{}, nn,
-                           row_begin, (uint64_t)num_rows, k_cur, pass_counts(0), status, counters);
+                           row_begin, (uint64_t)num_rows, k_cur, pass_counts(0), status, counters, pad);
     if ((err = hipGetLastError()) != hipSuccess) return err;
     for (int p = 0; p < passes; ++p) {
         const int shift = 8 * p;
@@ -975,7 +987,8 @@ size_t scatter_workspace_bytes(int64_t n, int64_t num_rows, int dim) {
 
 namespace {
 
-hipError_t scatter_plan(const int64_t* rows, const TokenRows* tr, int64_t n, int64_t row_begin, int64_t num_rows,
+hipError_t scatter_plan(const int64_t* rows, const TokenRows* tr, Padding pad, int64_t n, int64_t row_begin,
+                        int64_t num_rows,
                         int dim, int64_t* uniq_rows, int64_t* num_uniq, void* workspace, int64_t* status,
                         hipStream_t stream) {
     const Layout L = make_layout(n, dim);
@@ -993,9 +1006,9 @@ hipError_t scatter_plan(const int64_t* rows, const TokenRows* tr, int64_t n, int
     hipError_t err = hipGetLastError();
     if (err != hipSuccess || n == 0) return err;
     const int items = sort_items(n);
-    if (items == 8) err = run_sort<8>(L, ws, rows, tr, n, row_begin, num_rows, passes, status, stream);
-    else if (items == 16) err = run_sort<16>(L, ws, rows, tr, n, row_begin, num_rows, passes, status, stream);
-    else err = run_sort<24>(L, ws, rows, tr, n, row_begin, num_rows, passes, status, stream);
+    if (items == 8) err = run_sort<8>(L, ws, rows, tr, pad, n, row_begin, num_rows, passes, status, stream);
+    else if (items == 16) err = run_sort<16>(L, ws, rows, tr, pad, n, row_begin, num_rows, passes, status, stream);
+    else err = run_sort<24>(L, ws, rows, tr, pad, n, row_begin, num_rows, passes, status, stream);
     if (err != hipSuccess) return err;
 
     const uint32_t nn = (uint32_t)n;
@@ -1018,15 +1031,23 @@ hipError_t scatter_plan(const int64_t* rows, const TokenRows* tr, int64_t n, int
 hipError_t launch_scatter_plan(const int64_t* rows, int64_t n, int64_t row_begin, int64_t num_rows, int dim,
                                int64_t* uniq_rows, int64_t* num_uniq, void* workspace, int64_t* status,
                                hipStream_t stream) {
-    return scatter_plan(rows, nullptr, n, row_begin, num_rows, dim, uniq_rows, num_uniq, workspace, status, stream);
+    return scatter_plan(rows, nullptr, Padding{}, n, row_begin, num_rows, dim, uniq_rows, num_uniq, workspace, status,
+                        stream);
+}
+
+hipError_t launch_scatter_plan_padded(const int64_t* ids, const int64_t* counts, int world, int64_t capacity,
+                                      int64_t row_begin, int64_t num_rows, int dim, int64_t* uniq_rows,
+                                      int64_t* num_uniq, void* workspace, int64_t* status, hipStream_t stream) {
+    return scatter_plan(ids, nullptr, Padding{counts, (uint32_t)capacity}, (int64_t)world * capacity, row_begin,
+                        num_rows, dim, uniq_rows, num_uniq, workspace, status, stream);
 }
 
 hipError_t launch_scatter_plan_tokens(const int64_t* tokens, int64_t batch, int64_t seq_len, const HashParams& p,
                                       int64_t row_begin, int64_t num_rows, int dim, int64_t* uniq_rows,
                                       int64_t* num_uniq, void* workspace, int64_t* status, hipStream_t stream) {
     const TokenRows tr{tokens, (uint32_t)seq_len, p};
-    return scatter_plan(nullptr, &tr, batch * seq_len * kTokenHeads, row_begin, num_rows, dim, uniq_rows, num_uniq,
-                        workspace, status, stream);
+    return scatter_plan(nullptr, &tr, Padding{}, batch * seq_len * kTokenHeads, row_begin, num_rows, dim, uniq_rows,
+                        num_uniq, workspace, status, stream);
 }
 
 hipError_t launch_scatter_apply(const void* grad_out, int elem_bytes, int dim, int64_t n, int64_t num_rows,

@@ -100,6 +100,8 @@ def load_library(path=LIB_PATH):
     lib.engram_scatter_add.argtypes = [p, i64, p, i32, i32, i64, i64, p, p, p, p, p, sz, p, p]
     lib.engram_scatter_add_plan.restype = ctypes.c_int
     lib.engram_scatter_add_plan.argtypes = [p, i64, i64, i64, i32, p, p, p, sz, p, p]
+    lib.engram_scatter_add_plan_padded.restype = ctypes.c_int
+    lib.engram_scatter_add_plan_padded.argtypes = [p, p, i32, i64, i64, i64, i32, p, p, p, sz, p, p]
     lib.engram_scatter_add_plan_from_tokens.restype = ctypes.c_int
     lib.engram_scatter_add_plan_from_tokens.argtypes = [p, i64, i64, ctypes.POINTER(EngramHashSpec), i64, i64, i32, p,
                                                         p, p, sz, p, p]
@@ -342,6 +344,31 @@ def engram_scatter_add_plan(rows, num_rows, dim, row_begin=0, workspace=None, un
                                        _status_ptr(status), _stream_handle(stream)),
            "engram_scatter_add_plan")
     # What the plan in this workspace was made for; apply refuses other sizes.
+    workspace._engram_plan = (n, num_rows, dim, row_begin)
+    return workspace
+
+
+def engram_scatter_add_plan_padded(ids, split_sizes, num_rows, dim, row_begin=0, workspace=None, uniq_rows=None,
+                                   num_uniq=None, status=None, stream=None):
+    """engram_scatter_add_plan for received padded ID blocks ids int64 [world, capacity]
+    (block w's first split_sizes[w] entries are IDs, the rest padding).  Returns the
+    workspace; apply with n = world * capacity and the padded gradient blocks."""
+    lib = load_library()
+    if ids.dim() != 2:
+        raise ValueError("ids must be [world, capacity]")
+    world, capacity = ids.shape
+    n = world * capacity
+    if workspace is None:
+        workspace = torch.empty(engram_scatter_add_workspace(n, num_rows, dim), dtype=torch.uint8, device=ids.device)
+    _check(lib.engram_scatter_add_plan_padded(_dev_ptr(ids, "ids", torch.int64),
+                                              _dev_ptr(split_sizes, "split_sizes", torch.int64, numel=world), world,
+                                              capacity, row_begin, num_rows, dim,
+                                              _dev_ptr(uniq_rows, "uniq_rows", torch.int64, min_numel=n),
+                                              _dev_ptr(num_uniq, "num_uniq", torch.int64, numel=1),
+                                              _dev_ptr(workspace, "workspace"),
+                                              workspace.numel() * workspace.element_size(), _status_ptr(status),
+                                              _stream_handle(stream)),
+           "engram_scatter_add_plan_padded")
     workspace._engram_plan = (n, num_rows, dim, row_begin)
     return workspace
 

@@ -229,6 +229,24 @@ int engram_scatter_add_apply(const void* grad_out, int32_t dtype, int32_t dim, i
                              int64_t num_rows, float* grad_dense, float* uniq_grad, const void* workspace,
                              size_t workspace_bytes, hipStream_t stream);
 
+/* engram_scatter_add_plan for rows as the owner receives them from the
+ * exchange (engram API page, _FixedCapacityAllToAll.backward routes each
+ * gradient row back to the owner of its ID; Qwen3_8_FlashNextOwnerShardedEmbedding:
+ * only the owner accumulates a row's gradient): ids [world][capacity] as
+ * received (the first split_sizes[w] entries of block w are IDs, all of them
+ * for a count above capacity, none for a negative count; the rest is padding,
+ * never checked).  The plan covers n = world * capacity entries, padding as
+ * dropped lookups, so engram_scatter_add_apply then reads the gradient rows
+ * straight from the received padded gradient blocks [world][capacity][dim]
+ * with that n; no unpack of the IDs or the gradients is needed.  *status =
+ * lowest padded index holding an ID outside [row_begin, row_begin + num_rows),
+ * else -1.  Workspace: engram_scatter_add_workspace(world * capacity, ...).
+ * world * capacity < 2^31.  Returns ENGRAM_OK, ENGRAM_EINVAL or ENGRAM_EWORKSPACE. */
+int engram_scatter_add_plan_padded(const int64_t* ids, const int64_t* split_sizes, int32_t world, int64_t capacity,
+                                   int64_t row_begin, int64_t num_rows, int32_t dim, int64_t* uniq_rows,
+                                   int64_t* num_uniq, void* workspace, size_t workspace_bytes, int64_t* status,
+                                   hipStream_t stream);
+
 /* engram_scatter_add_plan for the rows engram_hash would write from `tokens`, hashed
  * inside the plan (engram API page, Qwen3_8_FlashNextNGramEmbedding: the backward of
  * _lookup_ngram_ids reaches the rows _hash_input_ids gives; the hash depends on the

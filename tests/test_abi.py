@@ -215,6 +215,14 @@ def test_route_entry_points_reject_bad_arguments(lib):
     assert gp(cs=None) == B.ENGRAM_EINVAL and gp(ids=None) == B.ENGRAM_EINVAL and gp(out=None) == B.ENGRAM_EINVAL
     assert gp(table=None) == B.ENGRAM_EINVAL
     assert gp(out=ctypes.c_void_p(0x1008)) == B.ENGRAM_EINVAL   # rows of values are 16-byte aligned
+    # (ids, split_sizes, world, capacity, row_begin, num_rows, dim, uniq_rows, num_uniq, workspace, bytes, status, stream)
+    ws = ctypes.c_void_p(0x100000)
+    spp = lambda ids=f, cs=f, W=8, cap=16, rb=0, nr=1000, dim=160, wsb=1 << 30: \
+        lib.engram_scatter_add_plan_padded(ids, cs, W, cap, rb, nr, dim, None, None, ws, wsb, None, None)
+    assert spp(W=0) == B.ENGRAM_EINVAL and spp(W=256) == B.ENGRAM_EINVAL and spp(cap=-1) == B.ENGRAM_EINVAL
+    assert spp(cs=None) == B.ENGRAM_EINVAL and spp(ids=None) == B.ENGRAM_EINVAL and spp(dim=0) == B.ENGRAM_EINVAL
+    assert spp(cap=1 << 30) == B.ENGRAM_EINVAL                  # world * capacity < 2^31
+    assert spp(wsb=16) == B.ENGRAM_EWORKSPACE
 
 
 def test_ple_rejects_bad_arguments(lib):

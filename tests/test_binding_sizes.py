@@ -154,6 +154,8 @@ def test_routing_buffers():
     with pytest.raises(ValueError, match=SIZE):
         E.engram_gather_padded(bf16(100, 160), i64(4, 8), i64(3))
     with pytest.raises(ValueError, match=SIZE):
+        E.engram_scatter_add_plan_padded(i64(4, 8), i64(3), 100, 160)
+    with pytest.raises(ValueError, match=SIZE):
         E.engram_permute_pack_rows(bf16(20, 160), i64(20), counts, 4, 8, out=bf16(4, 7, 160))
 
 

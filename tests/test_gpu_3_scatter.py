@@ -360,3 +360,78 @@ def test_sort_tile_size_boundaries(n):
     ref, rbad = c_oracle.scatter_add_dense(rows2, to_host(dy), R2)
     assert bad == rbad == -1
     assert_close_to_fp64(got, ref, "dense, n = %d" % n)
+
+
+def padded_case(rng, world, capacity, num_rows, row_begin, dim=160, bad_at=()):
+    """Received padded ID and gradient blocks: counts (one negative, one above the
+    capacity), garbage in the padding, IDs outside the shard at the given
+    (block, entry) places; returns the padded tensors and their compact forms."""
+    counts = rng.integers(0, capacity + 1, size=world).astype(np.int64)
+    if world > 2:
+        counts[1] = -3
+        counts[2] = capacity + 7
+    ids = rng.integers(-10**9, 10**9, size=(world, capacity)).astype(np.int64)   # padding: never read as IDs
+    kept = np.clip(counts, 0, capacity)
+    for w in range(world):
+        ids[w, :kept[w]] = rng.integers(row_begin, row_begin + num_rows, size=kept[w])
+    for w, r in bad_at:
+        ids[w, r] = row_begin + num_rows + 5
+    dy = grads(world * capacity, dim, seed=world).reshape(world, capacity, dim)
+    compact_ids = np.concatenate([ids[w, :kept[w]] for w in range(world)])
+    dy_h = to_host(dy)
+    compact_dy = np.concatenate([dy_h[w, :kept[w]] for w in range(world)])
+    return counts, ids, dy, compact_ids, compact_dy
+
+
+@pytest.mark.parametrize("world,capacity", [(1, 700), (8, 333), (64, 97)])
+def test_plan_padded_dense_and_compact(world, capacity):
+    """The plan over received padded blocks, applied to the padded gradient
+    blocks, equals the fp64 oracle's scatter-add of the compact IDs and
+    gradients (dense and compact outputs); padding is never read as an ID."""
+    rng = np.random.default_rng(world)
+    num_rows, row_begin = 30_000, 1_000
+    counts, ids, dy, cids, cdy = padded_case(rng, world, capacity, num_rows, row_begin)
+    c = torch.from_numpy(counts).cuda()
+    ids_g = torch.from_numpy(ids).cuda()
+    n = world * capacity
+    status = torch.empty((), dtype=torch.int64, device="cuda")
+    g = torch.zeros((num_rows, 160), dtype=torch.float32, device="cuda")
+    ws = E.engram_scatter_add_plan_padded(ids_g, c, num_rows, 160, row_begin, status=status)
+    E.engram_scatter_add_apply(dy.reshape(n, 160), n, num_rows, ws, row_begin, grad_dense=g)
+    assert int(status.item()) == -1
+    ref, rbad = c_oracle.scatter_add_dense(cids, cdy, num_rows, row_begin)
+    assert rbad == -1
+    assert_close_to_fp64(g.cpu().numpy(), ref, "dense from padded blocks")
+    ur = torch.empty(n, dtype=torch.int64, device="cuda")
+    ug = torch.empty((n, 160), dtype=torch.float32, device="cuda")
+    nu = torch.empty((), dtype=torch.int64, device="cuda")
+    ws = E.engram_scatter_add_plan_padded(ids_g, c, num_rows, 160, row_begin, workspace=ws, uniq_rows=ur,
+                                          num_uniq=nu)
+    E.engram_scatter_add_apply(dy.reshape(n, 160), n, num_rows, ws, row_begin, uniq_grad=ug)
+    u = int(nu.item())
+    rur, rug, _ = c_oracle.scatter_add_compact(cids, cdy, num_rows, row_begin)
+    assert np.array_equal(ur[:u].cpu().numpy(), rur)
+    assert_close_to_fp64(ug[:u].cpu().numpy(), rug, "compact from padded blocks")
+
+
+def test_plan_padded_bad_ids():
+    """Received IDs outside the shard: dropped, and the lowest padded index
+    reported (an ID in the padding is not one)."""
+    rng = np.random.default_rng(77)
+    world, capacity, num_rows, row_begin = 8, 120, 5_000, 0
+    counts, ids, dy, cids, cdy = padded_case(rng, world, capacity, num_rows, row_begin,
+                                             bad_at=[(4, 3), (6, 0)])
+    ids[0, capacity - 1] = -1 if counts[0] < capacity else ids[0, capacity - 1]   # padding or real, as it falls
+    kept = np.clip(counts, 0, capacity)
+    bad_real = [w * capacity + r for w in range(world) for r in range(kept[w])
+                if not (row_begin <= ids[w, r] < row_begin + num_rows)]
+    status = torch.empty((), dtype=torch.int64, device="cuda")
+    n = world * capacity
+    g = torch.zeros((num_rows, 160), dtype=torch.float32, device="cuda")
+    ws = E.engram_scatter_add_plan_padded(torch.from_numpy(ids).cuda(), torch.from_numpy(counts).cuda(), num_rows,
+                                          160, row_begin, status=status)
+    E.engram_scatter_add_apply(dy.reshape(n, 160), n, num_rows, ws, row_begin, grad_dense=g)
+    assert int(status.item()) == min(bad_real)
+    cids = np.concatenate([ids[w, :kept[w]] for w in range(world)])
+    ref, _ = c_oracle.scatter_add_dense(cids, cdy, num_rows, row_begin)
+    assert_close_to_fp64(g.cpu().numpy(), ref, "dense from padded blocks with bad IDs")
