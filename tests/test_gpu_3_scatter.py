@@ -383,7 +383,7 @@ def padded_case(rng, world, capacity, num_rows, row_begin, dim=160, bad_at=()):
     return counts, ids, dy, compact_ids, compact_dy
 
 
-@pytest.mark.parametrize("world,capacity", [(1, 700), (8, 333), (64, 97)])
+@pytest.mark.parametrize("world,capacity", [(1, 700), (8, 333), (64, 97), (255, 3), (4, 1)])
 def test_plan_padded_dense_and_compact(world, capacity):
     """The plan over received padded blocks, applied to the padded gradient
     blocks, equals the fp64 oracle's scatter-add of the compact IDs and

@@ -414,14 +414,18 @@ def test_permute_pack_round_trip():
     assert torch.equal(back, g)
 
 
-@pytest.mark.parametrize("dtype,dim,world,row_begin", [(torch.bfloat16, 160, 64, 0), (torch.float32, 160, 8, 5000),
-                                                       (torch.bfloat16, 64, 5, 123), (torch.float32, 8, 1, 0)])
-def test_gather_padded_parity(dtype, dim, world, row_begin):
+@pytest.mark.parametrize("dtype,dim,world,row_begin,capacity", [(torch.bfloat16, 160, 64, 0, 300),
+                                                                (torch.float32, 160, 8, 5000, 300),
+                                                                (torch.bfloat16, 64, 5, 123, 300),
+                                                                (torch.float32, 8, 1, 0, 300),
+                                                                (torch.bfloat16, 160, 255, 7, 1),
+                                                                (torch.bfloat16, 160, 3, 0, 17)])
+def test_gather_padded_parity(dtype, dim, world, row_begin, capacity):
     """The owner's lookup on padded ID blocks equals the unpack of the IDs, the
     oracle's gather and the pack of the values with a zero fill, bit for bit
     (the 16-row and 8-row wave kernels and the generic one)."""
-    rng = np.random.default_rng(world + dim)
-    num_rows, capacity = 20_000, 300
+    rng = np.random.default_rng(world + dim + capacity)
+    num_rows = 20_000
     table = torch.from_numpy(rng.standard_normal((num_rows, dim)).astype(np.float32)).to(dtype).cuda()
     counts = rng.integers(1, capacity + 1, size=world).astype(np.int64)
     if world > 1:
