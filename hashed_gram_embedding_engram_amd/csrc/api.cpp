@@ -123,28 +123,48 @@ int engram_gather(const void* table, int32_t dtype, int64_t row_begin, int64_t n
     return launch_result(engram::launch_gather(table, eb, row_begin, num_rows, dim, rows, n, out, status, stream));
 }
 
-int engram_hash_gather(const int64_t* tokens, int64_t batch, int64_t seq_len, const engram_hash_spec* spec,
-                       const void* table, int32_t dtype, int64_t row_begin, int64_t num_rows, int32_t dim,
-                       void* out, int64_t* rows_out, int64_t* status, hipStream_t stream) {
+namespace {
+int hash_gather_common(const int64_t* tokens, int64_t batch, int64_t seq_len, int64_t seq_begin, int64_t seq_end,
+                       const engram_hash_spec* spec, const void* table, int32_t dtype, int64_t row_begin,
+                       int64_t num_rows, int32_t dim, void* out, int64_t* rows_out, int64_t* status,
+                       hipStream_t stream) {
     if (!dtype_ok(dtype)) return ENGRAM_EDTYPE;
     int eb;
     if (!row_bytes_ok(dtype, dim, &eb)) return ENGRAM_EINVAL;
     if (batch < 0 || seq_len < 0 || num_rows < 0 || row_begin < 0) return ENGRAM_EINVAL;
+    if (seq_begin < 0 || seq_begin > seq_end || seq_end > seq_len) return ENGRAM_EINVAL;
     engram::HashParams p;
     const int rc = build_params(spec, &p);
     if (rc != ENGRAM_OK) return rc;
+    const int64_t width = seq_end - seq_begin;
     // one hash work-item per position: a launch holds fewer than 2^32
-    if (seq_len > 0 && (batch > INT64_MAX / seq_len / ENGRAM_MAX_HEADS || batch * seq_len > ((int64_t)1 << 32) - 64))
+    if (width > 0 && (batch > INT64_MAX / width / ENGRAM_MAX_HEADS || batch * width > ((int64_t)1 << 32) - 64))
         return ENGRAM_EINVAL;
-    const int64_t positions = batch * seq_len;
+    const int64_t positions = batch * width;
     if (!aligned(tokens, 8) || !aligned(table, 16) || !aligned(out, 16) || !aligned(rows_out, 16) ||
         !aligned(status, 8))
         return ENGRAM_EINVAL;
     if (positions == 0) return launch_result(engram::launch_status_init(status, stream));
     if (!tokens || !out || (num_rows > 0 && !table)) return ENGRAM_EINVAL;
     if (!rows_out && !engram::hash_gather_fused(p, eb, dim, positions)) return ENGRAM_EINVAL;
-    return launch_result(engram::launch_hash_gather(tokens, batch, seq_len, p, table, eb, row_begin, num_rows, dim,
-                                                    out, rows_out, status, stream));
+    return launch_result(engram::launch_hash_gather(tokens, batch, seq_len, seq_begin, seq_end, p, table, eb,
+                                                    row_begin, num_rows, dim, out, rows_out, status, stream));
+}
+}  // namespace
+
+int engram_hash_gather(const int64_t* tokens, int64_t batch, int64_t seq_len, const engram_hash_spec* spec,
+                       const void* table, int32_t dtype, int64_t row_begin, int64_t num_rows, int32_t dim,
+                       void* out, int64_t* rows_out, int64_t* status, hipStream_t stream) {
+    return hash_gather_common(tokens, batch, seq_len, 0, seq_len, spec, table, dtype, row_begin, num_rows, dim, out,
+                              rows_out, status, stream);
+}
+
+int engram_hash_gather_slice(const int64_t* tokens, int64_t batch, int64_t seq_len, int64_t seq_begin,
+                             int64_t seq_end, const engram_hash_spec* spec, const void* table, int32_t dtype,
+                             int64_t row_begin, int64_t num_rows, int32_t dim, void* out, int64_t* rows_out,
+                             int64_t* status, hipStream_t stream) {
+    return hash_gather_common(tokens, batch, seq_len, seq_begin, seq_end, spec, table, dtype, row_begin, num_rows,
+                              dim, out, rows_out, status, stream);
 }
 
 size_t engram_scatter_add_workspace(int64_t n, int64_t num_rows, int32_t dim) {

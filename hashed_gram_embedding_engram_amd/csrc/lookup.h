@@ -15,9 +15,12 @@ constexpr int64_t kLookupMaxPositions = (int64_t)1 << 25;
 // rows_out and then the gather.
 bool hash_gather_fused(const HashParams& p, int elem_bytes, int dim, int64_t positions);
 
-hipError_t launch_hash_gather(const int64_t* tokens, int64_t batch, int64_t seq_len, const HashParams& p,
-                              const void* table, int elem_bytes, int64_t row_begin, int64_t num_rows, int dim,
-                              void* out, int64_t* rows_out, int64_t* status, hipStream_t stream);
+// Columns [seq_begin, seq_end) of every batch row, hashed with the columns
+// before them (seq_begin = 0, seq_end = seq_len: the whole sequence).
+hipError_t launch_hash_gather(const int64_t* tokens, int64_t batch, int64_t seq_len, int64_t seq_begin,
+                              int64_t seq_end, const HashParams& p, const void* table, int elem_bytes,
+                              int64_t row_begin, int64_t num_rows, int dim, void* out, int64_t* rows_out,
+                              int64_t* status, hipStream_t stream);
 
 // Backward phase 1 from tokens: the plan of engram_scatter_add_plan for the
 // rows the released head layout hashes from `tokens` [batch][seq_len] (16

@@ -32,15 +32,19 @@ __device__ u32x4 kLookupZero = {0u, 0u, 0u, 0u};  // never written
 
 // Same occupancy cap as the gather kernel (four waves per SIMD): the copy is
 // the same, and the backward's plan runs beside it on another stream.
+// Positions [seq_begin, seq_begin + width) of every batch row (the whole row
+// when seq_begin = 0 and width = seq_len): position pos of the output is batch
+// row pos / width, column seq_begin + pos % width, hashed with the columns
+// before it (a context-parallel rank's slice of a global sequence).
 template <bool ROW32, bool ROWS_OUT>
 __global__ __launch_bounds__(kLookupBlock) __attribute__((amdgpu_waves_per_eu(1, 4))) void hash_gather_kernel(
-    const int64_t* __restrict__ tokens, int64_t seq_len, int64_t positions, HashParams p,
-    const u32x4* __restrict__ table, int64_t row_begin, uint64_t num_rows, u32x4* __restrict__ out,
+    const int64_t* __restrict__ tokens, int64_t seq_len, int64_t seq_begin, int64_t width, int64_t positions,
+    HashParams p, const u32x4* __restrict__ table, int64_t row_begin, uint64_t num_rows, u32x4* __restrict__ out,
     int64_t* __restrict__ rows_out, int64_t* __restrict__ status) {
     const int lane = threadIdx.x & 63;
     const int64_t pos = (int64_t)blockIdx.x * (kLookupBlock / 64) + (threadIdx.x >> 6);
     if (pos >= positions) return;
-    const int64_t b = pos / seq_len, t = pos - b * seq_len;
+    const int64_t b = pos / width, t = seq_begin + (pos - b * width);
     int64_t tok = 0;
     if (lane < 3 && t >= lane) tok = tokens[b * seq_len + t - lane];
     const int64_t x0 = __shfl(tok, 0, 64), x1 = __shfl(tok, 1, 64), x2 = __shfl(tok, 2, 64);
@@ -81,13 +85,15 @@ bool hash_gather_fused(const HashParams& p, int elem_bytes, int dim, int64_t pos
            positions <= kLookupMaxPositions;
 }
 
-hipError_t launch_hash_gather(const int64_t* tokens, int64_t batch, int64_t seq_len, const HashParams& p,
-                              const void* table, int elem_bytes, int64_t row_begin, int64_t num_rows, int dim,
-                              void* out, int64_t* rows_out, int64_t* status, hipStream_t stream) {
-    const int64_t positions = batch * seq_len;
+hipError_t launch_hash_gather(const int64_t* tokens, int64_t batch, int64_t seq_len, int64_t seq_begin,
+                              int64_t seq_end, const HashParams& p, const void* table, int elem_bytes,
+                              int64_t row_begin, int64_t num_rows, int dim, void* out, int64_t* rows_out,
+                              int64_t* status, hipStream_t stream) {
+    const int64_t width = seq_end - seq_begin;
+    const int64_t positions = batch * width;
     if (!hash_gather_fused(p, elem_bytes, dim, positions)) {
         // Two kernels through the caller's rows array.
-        hipError_t err = launch_hash(tokens, batch, seq_len, 0, seq_len, p, rows_out, stream);
+        hipError_t err = launch_hash(tokens, batch, seq_len, seq_begin, seq_end, p, rows_out, stream);
         if (err != hipSuccess) return err;
         const int64_t heads = (int64_t)(p.ngram_size - 1) * p.heads_per_ngram;
         return launch_gather(table, elem_bytes, row_begin, num_rows, dim, rows_out, positions * heads, out, status,
@@ -101,16 +107,16 @@ hipError_t launch_hash_gather(const int64_t* tokens, int64_t batch, int64_t seq_
     u32x4* o = (u32x4*)out;
     if (row32 && rows_out)
         hipLaunchKernelGGL((hash_gather_kernel<true, true>), grid, dim3(kLookupBlock), 0, stream, tokens, seq_len,
-                           positions, p, t, row_begin, (uint64_t)num_rows, o, rows_out, status);
+                           seq_begin, width, positions, p, t, row_begin, (uint64_t)num_rows, o, rows_out, status);
     else if (row32)
         hipLaunchKernelGGL((hash_gather_kernel<true, false>), grid, dim3(kLookupBlock), 0, stream, tokens, seq_len,
-                           positions, p, t, row_begin, (uint64_t)num_rows, o, rows_out, status);
+                           seq_begin, width, positions, p, t, row_begin, (uint64_t)num_rows, o, rows_out, status);
     else if (rows_out)
         hipLaunchKernelGGL((hash_gather_kernel<false, true>), grid, dim3(kLookupBlock), 0, stream, tokens, seq_len,
-                           positions, p, t, row_begin, (uint64_t)num_rows, o, rows_out, status);
+                           seq_begin, width, positions, p, t, row_begin, (uint64_t)num_rows, o, rows_out, status);
     else
         hipLaunchKernelGGL((hash_gather_kernel<false, false>), grid, dim3(kLookupBlock), 0, stream, tokens, seq_len,
-                           positions, p, t, row_begin, (uint64_t)num_rows, o, rows_out, status);
+                           seq_begin, width, positions, p, t, row_begin, (uint64_t)num_rows, o, rows_out, status);
     return hipGetLastError();
 }
 

@@ -94,6 +94,9 @@ def load_library(path=LIB_PATH):
     lib.engram_gather.argtypes = [p, i32, i64, i64, i32, p, i64, p, p, p]
     lib.engram_hash_gather.restype = ctypes.c_int
     lib.engram_hash_gather.argtypes = [p, i64, i64, ctypes.POINTER(EngramHashSpec), p, i32, i64, i64, i32, p, p, p, p]
+    lib.engram_hash_gather_slice.restype = ctypes.c_int
+    lib.engram_hash_gather_slice.argtypes = [p, i64, i64, i64, i64, ctypes.POINTER(EngramHashSpec), p, i32, i64, i64,
+                                             i32, p, p, p, p]
     lib.engram_scatter_add_workspace.restype = sz
     lib.engram_scatter_add_workspace.argtypes = [i64, i64, i32]
     lib.engram_scatter_add.restype = ctypes.c_int
@@ -253,6 +256,35 @@ def engram_hash_gather(tokens, spec, table, row_begin=0, out=None, rows_out=None
         if bad >= 0:
             raise EngramError("engram_hash_gather: the row of lookup %d (position %d, head %d) is outside the owned "
                               "range" % (bad, bad // heads, bad % heads))
+    return out
+
+
+def engram_hash_gather_slice(tokens, spec, table, seq_begin, seq_end, row_begin=0, out=None, rows_out=None,
+                             status=None, validate=True, stream=None):
+    """engram_hash_gather for columns [seq_begin, seq_end) of tokens int64 [batch, seq],
+    hashed with the tokens before them -> out [batch, seq_end - seq_begin, H, dim]."""
+    lib = load_library()
+    if tokens.dim() != 2 or table.dim() != 2:
+        raise ValueError("tokens must be [batch, seq] and table [num_rows, dim]")
+    batch, seq = tokens.shape
+    num_rows, dim = table.shape
+    heads = spec.num_heads
+    width = max(0, seq_end - seq_begin)
+    if out is None:
+        out = torch.empty((batch, width, heads, dim), dtype=table.dtype, device=table.device)
+    if validate and status is None:
+        status = torch.empty((), dtype=torch.int64, device=table.device)
+    _check(lib.engram_hash_gather_slice(_dev_ptr(tokens, "tokens", torch.int64), batch, seq, seq_begin, seq_end,
+                                        ctypes.byref(spec), _dev_ptr(table, "table", table.dtype), _dtype_code(table),
+                                        row_begin, num_rows, dim,
+                                        _dev_ptr(out, "out", table.dtype, numel=batch * width * heads * dim),
+                                        _dev_ptr(rows_out, "rows_out", torch.int64, numel=batch * width * heads),
+                                        _status_ptr(status), _stream_handle(stream)), "engram_hash_gather_slice")
+    if validate:
+        bad = int(status.item())
+        if bad >= 0:
+            raise EngramError("engram_hash_gather_slice: the row of lookup %d (slice position %d, head %d) is "
+                              "outside the owned range" % (bad, bad // heads, bad % heads))
     return out
 
 

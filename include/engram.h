@@ -159,6 +159,21 @@ int engram_hash_gather(const int64_t* tokens, int64_t batch, int64_t seq_len, co
                        const void* table, int32_t dtype, int64_t row_begin, int64_t num_rows, int32_t dim,
                        void* out, int64_t* rows_out, int64_t* status, hipStream_t stream);
 
+/* engram_hash_gather for columns [seq_begin, seq_end) of every batch row, each
+ * hashed with the two tokens before it even where they lie before seq_begin
+ * (engram API page, Qwen3_8_FlashNextNGramEmbedding._forward_global_slice:
+ * hash the complete sequence, look up only one local slice; a
+ * context-parallel rank's forward).  out: device [batch][seq_end -
+ * seq_begin][H][dim]; rows_out (or NULL, as for engram_hash_gather): device
+ * int64 [batch][seq_end - seq_begin][H].  Equals engram_hash_slice followed by
+ * engram_gather bit for bit.  Lookup index i = (b * width + (t - seq_begin)) *
+ * H + h in `status`.  0 <= seq_begin <= seq_end <= seq_len; batch * width <=
+ * 2^32 - 64.  Returns ENGRAM_OK, ENGRAM_EINVAL, ENGRAM_EDTYPE or ENGRAM_ESPEC. */
+int engram_hash_gather_slice(const int64_t* tokens, int64_t batch, int64_t seq_len, int64_t seq_begin,
+                             int64_t seq_end, const engram_hash_spec* spec, const void* table, int32_t dtype,
+                             int64_t row_begin, int64_t num_rows, int32_t dim, void* out, int64_t* rows_out,
+                             int64_t* status, hipStream_t stream);
+
 /* Bytes of device workspace engram_scatter_add needs for n lookups into a
  * num_rows-row shard with rows of dim values (256-byte aligned start). */
 size_t engram_scatter_add_workspace(int64_t n, int64_t num_rows, int32_t dim);

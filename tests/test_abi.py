@@ -389,6 +389,16 @@ def test_hash_gather_rejects_bad_arguments(lib):
     # launches of 2^32 work-items or more are refused; empty work succeeds
     assert call(f, 1 << 26, 64, s, f, bf, 0, 10, 160, f, f, None, None) == B.ENGRAM_EINVAL
     assert call(None, 0, 8, s, None, bf, 0, 10, 160, None, None, None, None) == B.ENGRAM_OK
+    # the slice form: 0 <= seq_begin <= seq_end <= seq_len, the rest as above
+    sl = lib.engram_hash_gather_slice
+    assert sl(f, 1, 8, 3, 2, s, f, bf, 0, 10, 160, f, f, None, None) == B.ENGRAM_EINVAL
+    assert sl(f, 1, 8, -1, 2, s, f, bf, 0, 10, 160, f, f, None, None) == B.ENGRAM_EINVAL
+    assert sl(f, 1, 8, 0, 9, s, f, bf, 0, 10, 160, f, f, None, None) == B.ENGRAM_EINVAL
+    assert sl(f, 1, 8, 2, 5, s, f, 7, 0, 10, 160, f, f, None, None) == B.ENGRAM_EDTYPE
+    assert sl(f, 1, 8, 2, 5, s, f, bf, 0, 10, 160, mis, f, None, None) == B.ENGRAM_EINVAL
+    assert sl(f, 1, 8, 2, 5, s, f, f32, 0, 10, 160, f, None, None, None) == B.ENGRAM_EINVAL
+    assert sl(f, 1 << 27, 64, 0, 32, s, f, bf, 0, 10, 160, f, f, None, None) == B.ENGRAM_EINVAL
+    assert sl(None, 1, 8, 4, 4, s, None, bf, 0, 10, 160, None, None, None, None) == B.ENGRAM_OK
 
 
 def test_plan_from_tokens_rejects_bad_arguments(lib):

@@ -286,3 +286,69 @@ def test_fused_empty_shard_and_empty_batches():
                                    validate=False)
         torch.cuda.synchronize()
         assert out.numel() == 0 and int(status.item()) == -1
+
+
+def check_slice(ids, ws, table, a, b, row_begin=0, with_rows=True, spec=None):
+    """The fused forward of columns [a, b): against the oracle's hash of the whole
+    sequence (its columns a..b-1) and the oracle's gather, and against
+    engram_hash_slice followed by engram_gather."""
+    spec = spec if spec is not None else product_spec_from(ws)
+    ids = np.ascontiguousarray(ids, dtype=np.int64)
+    batch, seq = ids.shape
+    heads = spec.num_heads
+    tokens = torch.from_numpy(ids).cuda()
+    status = torch.empty((), dtype=torch.int64, device="cuda")
+    rows_out = torch.full((batch, b - a, heads), -7, dtype=torch.int64, device="cuda") if with_rows else None
+    out = E.engram_hash_gather_slice(tokens, spec, table, a, b, row_begin, rows_out=rows_out, status=status,
+                                     validate=False)
+    torch.cuda.synchronize()
+    ref_rows = np.ascontiguousarray(oracle_hash(ids, ws)[:, a:b])
+    ref, bad = c_oracle.gather(to_host(table), ref_rows.reshape(-1), row_begin)
+    assert out.shape == (batch, b - a, heads, table.shape[1])
+    assert np.array_equal(to_host(out).reshape(ref.shape).view(np.uint8), ref.view(np.uint8))
+    assert int(status.item()) == bad
+    if with_rows:
+        assert np.array_equal(rows_out.cpu().numpy(), ref_rows)
+    two = E.engram_gather(table, E.engram_hash_slice(tokens, a, b, spec), row_begin, validate=False)
+    assert np.array_equal(to_host(two).view(np.uint8), to_host(out).view(np.uint8))
+
+
+def test_slice_forward_cuts():
+    """Slices of a sequence with EOS runs: cuts at, just after and just before
+    EOS positions, at the ends, one column, and the whole row."""
+    ws = W.tiny_spec()
+    ids = uniform_ids((3, 500), 17, ws["eos"], p_eos=1.0 / 8)
+    table = bf16_table(ws["num_rows"], 10)
+    eos_at = [int(t) for t in np.nonzero(ids[0] == ws["eos"])[0][:3]]
+    cuts = [(0, 500), (0, 1), (499, 500), (1, 2), (2, 3), (250, 251), (100, 357)]
+    for t in eos_at:
+        cuts += [(t, min(t + 40, 500)), (min(t + 1, 499), min(t + 60, 500)), (max(t - 1, 0), min(t + 7, 500))]
+    for k, (a, b) in enumerate(cuts):
+        check_slice(ids, ws, table, a, b, with_rows=k % 2 == 0)
+
+
+def test_slice_forward_released_constants():
+    """A context-parallel rank's slice of a long-context stream with the released
+    constants on owner 0's shard (most rows outside it: zero rows, status)."""
+    ws = full_oracle_spec()
+    ids, _ = W.long_context_stream(seed=5, total=20_000)
+    check_slice(ids, ws, bf16_table(W.OWNER_ROWS, 11), 7_123, 12_345, spec=E.qwen3_8_flash_next_spec())
+
+
+def test_slice_forward_empty_and_refused():
+    ws = W.tiny_spec()
+    ids = uniform_ids((2, 50), 19, ws["eos"])
+    tokens = torch.from_numpy(ids).cuda()
+    table = bf16_table(ws["num_rows"], 12)
+    spec = product_spec_from(ws)
+    assert E.engram_hash_gather_slice(tokens, spec, table, 20, 20).shape == (2, 0, 16, 160)
+    with pytest.raises(E.EngramError):
+        E.engram_hash_gather_slice(tokens, spec, table, 30, 20)      # seq_begin > seq_end
+    with pytest.raises(E.EngramError):
+        E.engram_hash_gather_slice(tokens, spec, table, 0, 51)       # past the row
+    fp32 = bf16_table(ws["num_rows"], 13, torch.float32)             # two-kernel path: rows_out required
+    with pytest.raises(E.EngramError):
+        E.engram_hash_gather_slice(tokens, spec, fp32, 5, 25)
+    rows = torch.empty((2, 20, 16), dtype=torch.int64, device="cuda")
+    out = E.engram_hash_gather_slice(tokens, spec, fp32, 5, 25, rows_out=rows)
+    assert torch.equal(out, E.engram_gather(fp32, E.engram_hash_slice(tokens, 5, 25, spec)))
