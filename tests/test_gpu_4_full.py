@@ -115,7 +115,8 @@ def test_full_table_long_context_step(full_table):
 def test_owner_shard_step():
     """Owner 0 of a world-64 table: the lookups of 64 request ranks that fall in
     rows [0, 5,000,024), gathered from the shard and scattered into a dense fp32
-    gradient."""
+    gradient, both from the compact rows and from the padded [64][capacity]
+    blocks the exchange delivers."""
     ids = W.owner_token_batches().reshape(-1, 4096)
     spec = E.qwen3_8_flash_next_spec()
     rows_all = E.engram_hash(torch.from_numpy(ids).cuda(), spec).reshape(-1)
@@ -140,3 +141,26 @@ def test_owner_shard_step():
     touched = torch.zeros(W.OWNER_ROWS, dtype=torch.bool, device="cuda")
     touched[torch.from_numpy(rur).cuda()] = True
     assert int((grad[~touched] != 0).sum().item()) == 0
+
+    # The same lookups as the exchange delivers them to the owner: request rank
+    # w's rows in block w of the agreed capacity (the largest count), padding
+    # after them; the owner's response and backward read these blocks directly.
+    counts_np = (rows_ref_all.reshape(64, -1) < W.OWNER_ROWS).sum(1).astype(np.int64)
+    cap = int(counts_np.max())
+    counts = torch.from_numpy(counts_np).cuda()
+    real = torch.from_numpy(np.arange(cap)[None, :] < counts_np[:, None]).cuda().reshape(-1)
+    ids_pad = E.engram_pack_fixed_capacity(owner, counts, 64, cap, fill=-1)
+    vals = E.engram_gather_padded(shard, ids_pad, counts).reshape(-1, W.DIM)
+    streamed_gather_check(shard, vals[real], rows_ref)         # real entries, in rank order
+    assert int((vals[~real] != 0).sum().item()) == 0             # padding rows are zero
+    del vals
+    dy_pad = E.engram_pack_fixed_capacity(dy, counts, 64, cap, fill=0)
+    m = 64 * cap
+    grad_pad = torch.zeros_like(grad)
+    ws = E.engram_scatter_add_plan_padded(ids_pad, counts, W.OWNER_ROWS, W.DIM)
+    E.engram_scatter_add_apply(dy_pad.view(m, W.DIM), m, W.OWNER_ROWS, ws, grad_dense=grad_pad)
+    assert_close_to_fp64(grad_pad[torch.from_numpy(rur).cuda()].cpu().numpy(), rug, "owner backward from blocks")
+    assert int((grad_pad[~touched] != 0).sum().item()) == 0
+    # Padding sorts after every row and the rows keep their relative order, so
+    # the sums are those of the compact form bit for bit.
+    assert torch.equal(grad_pad, grad)
