@@ -226,7 +226,8 @@ def test_loopback_world_forward_and_backward():
 def test_route_bench_shape():
     """The benchmarked exchange half: one request rank of world 64 (8 x 4,096
     Zipf tokens hashed into 524,288 full-table IDs), capacity the largest
-    count, 320-byte bf16 value rows; the same calls the benchmark times."""
+    count, 320-byte bf16 value rows; the same calls the benchmark times, the
+    backward's one-pass send included."""
     world = 64
     ids = W.owner_token_batches(seeds=[100])[0]
     gids = E.engram_hash(torch.from_numpy(ids).cuda(), E.qwen3_8_flash_next_spec()).reshape(-1).contiguous()
@@ -260,6 +261,12 @@ def test_route_bench_shape():
     fused = E.engram_unpack_unpermute_rows(packed, c, order, status=status)   # the two calls in one pass
     assert int(status.item()) == -1
     assert np.array_equal(fused.cpu().view(torch.int16).numpy(), ref_out)
+    # the backward's send: gradient rows in request order, grouped and packed in one pass
+    dy = torch.randn((n, 160), generator=g, device="cuda").to(torch.bfloat16)
+    send = E.engram_permute_pack_rows(dy, order, c, world, cap, fill=0.0, status=status)
+    assert int(status.item()) == -1
+    ref_send, _ = RR.pack(dy.cpu().view(torch.int16).numpy()[ro], rc, world, cap, 0)
+    assert np.array_equal(send.cpu().view(torch.int16).numpy(), ref_send)
 
 
 def unpack_unpermute_ref(packed, counts, order, before):
