@@ -71,6 +71,9 @@ int hash_common(const int64_t* tokens, int64_t batch, int64_t seq_len, int64_t s
 }  // namespace
 
 namespace engram {
+// Work-items of the largest launch a convolution call makes (ple.hip).
+int64_t short_conv_launch_items(int64_t batch, int64_t seq, int64_t channels, int kernel, int dilation,
+                                int elem_bytes);
 // The fused routing copies (route.hip): the unpack with the move to request
 // order, and the move to grouped order with the pack.
 hipError_t launch_unpack_unpermute(const void* src, int64_t row_bytes, const int64_t* counts, int world,
@@ -418,9 +421,10 @@ namespace {
 
 // Sizes of a PLE call over a x b rows of `channels` features: every row a
 // whole number of 16-byte chunks, at most 2^26 features per row and 2^36
-// elements in all (137 GB of bf16 per tensor), so that every convolution
-// launch holds fewer than 2^32 work-items (the smallest tile covers 16
-// positions x 4 channels per work-item).
+// elements in all (137 GB of bf16 per tensor).  A convolution call also
+// needs each of its launches below kConvLaunchItems work-items, which short
+// sequences over many batch rows can reach first.
+constexpr int64_t kConvLaunchItems = (int64_t)1 << 32;
 int ple_dims_ok(int32_t dtype, int64_t a, int64_t b, int64_t channels, int* eb) {
     if (!dtype_ok(dtype)) return ENGRAM_EDTYPE;
     *eb = dtype == ENGRAM_F32 ? 4 : 2;
@@ -458,6 +462,8 @@ int engram_short_conv(const void* x, int32_t dtype, int64_t batch, int64_t seq, 
     int rc = ple_dims_ok(dtype, batch, seq, channels, &eb);
     if (rc != ENGRAM_OK) return rc;
     if (kernel < 1 || kernel > 4 || dilation < 1 || !weight) return ENGRAM_EINVAL;
+    if (engram::short_conv_launch_items(batch, seq, channels, kernel, dilation, eb) >= kConvLaunchItems)
+        return ENGRAM_EINVAL;
     if (batch * seq > 0 && (!x || !y)) return ENGRAM_EINVAL;
     if (!ple_ptrs_ok({x, y, halo}, {weight, bias})) return ENGRAM_EINVAL;
     return launch_result(engram::launch_short_conv(x, eb, batch, seq, channels, weight, bias, kernel, dilation, halo,
@@ -472,6 +478,8 @@ int engram_short_conv_backward(const void* x, const void* dy, int32_t dtype, int
     int rc = ple_dims_ok(dtype, batch, seq, channels, &eb);
     if (rc != ENGRAM_OK) return rc;
     if (kernel < 1 || kernel > 4 || dilation < 1 || !weight || !dweight) return ENGRAM_EINVAL;
+    if (engram::short_conv_launch_items(batch, seq, channels, kernel, dilation, eb) >= kConvLaunchItems)
+        return ENGRAM_EINVAL;
     if (batch * seq > 0 && (!x || !dy || !dx)) return ENGRAM_EINVAL;
     if (!ple_ptrs_ok({x, dy, halo, dx, dhalo}, {weight, dweight, dbias})) return ENGRAM_EINVAL;
     if (((uintptr_t)workspace & 255) != 0) return ENGRAM_EWORKSPACE;

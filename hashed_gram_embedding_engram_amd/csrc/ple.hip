@@ -230,6 +230,15 @@ __global__ __launch_bounds__(kPleBlock) void short_conv_bwd_kernel(
 // loaded once per tile (plus the HIST-position overlap with the previous tile)
 // instead of once per tap.  Window indices are compile-time constants: the
 // window lives in registers.
+//
+// A block is four waves over four consecutive tiles of the same 64 quads
+// (wave w takes tile 4 * tile_group + w), and consecutive tile groups of the
+// same quads are qgroups blocks apart, which lands them on the same XCD when
+// qgroups is a multiple of 8 (40 at 10,240 channels).  Odd waves walk their
+// tile from its end down: the rows on both sides of every tile edge are then
+// read by the two neighbouring waves at about the same time (both at the end
+// of their walks, or both at the start), so the overlap rows come from L2
+// instead of being fetched twice.
 
 // Build-time tuning parameters (positions per step, positions per tile), at
 // the measured best of steps 3, 6, 9 and tiles 96, 144, 192.  The streaming
@@ -255,13 +264,15 @@ __global__ __launch_bounds__(kPleBlock) void short_conv_fwd_d3_kernel(const void
                                                                       int64_t S, int64_t C, void* __restrict__ yp) {
     using Q = Quad<BF16>;
     constexpr int HIST = (K - 1) * kConvD, P = kConvStep;
-    const Q* x = (const Q*)xp;
     const Q* halo = (const Q*)halop;
     const Q* zero = (const Q*)&kPleZero;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int64_t quads = C / 4, tiles = (S + kConvTile - 1) / kConvTile;
-    const int64_t idx = (int64_t)blockIdx.x * kPleBlock + threadIdx.x;
-    if (idx >= B * tiles * quads) return;
-    const int64_t q = idx % quads, rest = idx / quads, tt = rest % tiles, b = rest / tiles;
+    const int64_t tgroups = (tiles + kConvWavesPerBlock - 1) / kConvWavesPerBlock, qgroups = (quads + 63) / 64;
+    const int64_t qg = blockIdx.x % qgroups, rest = blockIdx.x / qgroups, tg = rest % tgroups, b = rest / tgroups;
+    const int64_t q = qg * 64 + lane, tt = tg * kConvWavesPerBlock + wave;
+    const int64_t t0 = min(S, tt * kConvTile), t1 = min(S, t0 + kConvTile);
+    if (q >= quads || t1 <= t0) return;  // no barrier or cross-lane step below
     float wv[4][K], bv[4];
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
@@ -269,21 +280,15 @@ __global__ __launch_bounds__(kPleBlock) void short_conv_fwd_d3_kernel(const void
         for (int k = 0; k < K; ++k) wv[e][k] = w[(q * 4 + e) * K + k];
         bv[e] = bias ? bias[q * 4 + e] : 0.0f;
     }
-    const Q* xb = x + b * S * quads + q;  // position t of this row and quad: xb[t * quads]
-    const int64_t t0 = tt * kConvTile, t1 = min(S, t0 + kConvTile);
-    Q win[HIST + P];  // positions t - HIST .. t + P - 1
-#pragma unroll
-    for (int i = 0; i < HIST; ++i) {
-        const int64_t ts = t0 - HIST + i;
-        const Q* src = ts >= 0 ? xb + ts * quads : (halo ? halo + ((b * HIST + HIST + ts) * quads + q) : zero);
-        win[i] = *src;
-    }
+    const Q* xb = (const Q*)xp + b * S * quads + q;
+    auto xsrc = [&](int64_t tx) -> const Q* {
+        return tx >= S ? zero : tx >= 0 ? xb + tx * quads : (halo ? halo + ((b * HIST + HIST + tx) * quads + q) : zero);
+    };
     Q* yb = (Q*)yp + b * S * quads + q;
-    for (int64_t t = t0; t < t1; t += P) {
-#pragma unroll
-        for (int j = 0; j < P; ++j) win[HIST + j] = *(t + j < S ? xb + (t + j) * quads : zero);
+    auto step = [&](int64_t t, const Q (&win)[HIST + P]) {
 #pragma unroll
         for (int j = 0; j < P; ++j) {
+            if (t + j >= t1) break;  // wave-uniform
             float acc[4];
 #pragma unroll
             for (int e = 0; e < 4; ++e) acc[e] = bv[e];
@@ -294,15 +299,38 @@ __global__ __launch_bounds__(kPleBlock) void short_conv_fwd_d3_kernel(const void
 #pragma unroll
                 for (int e = 0; e < 4; ++e) acc[e] = fmaf(wv[e][k], f[e], acc[e]);
             }
-            if (t + j < t1) yb[(t + j) * quads] = pack4<BF16>(acc);
+            yb[(t + j) * quads] = pack4<BF16>(acc);
         }
+    };
+    if ((wave & 1) == 0) {  // up from t0
+        Q win[HIST + P];  // x at t - HIST .. t + P - 1
 #pragma unroll
-        for (int i = 0; i < HIST; ++i) win[i] = win[i + P];
+        for (int i = 0; i < HIST; ++i) win[i] = *xsrc(t0 - HIST + i);
+        for (int64_t t = t0; t < t1; t += P) {
+#pragma unroll
+            for (int j = 0; j < P; ++j) win[HIST + j] = *xsrc(t + j);
+            step(t, win);
+#pragma unroll
+            for (int i = 0; i < HIST; ++i) win[i] = win[i + P];
+        }
+    } else {  // down from the last step; the step below reuses the window's lowest HIST rows as its highest
+        Q win[HIST + P];
+        int64_t t = t0 + ((t1 - t0 - 1) / P) * P;
+#pragma unroll
+        for (int i = 0; i < HIST; ++i) win[P + i] = *xsrc(t - HIST + P + i);
+        for (; t >= t0; t -= P) {
+#pragma unroll
+            for (int j = 0; j < P; ++j) win[j] = *xsrc(t - HIST + j);
+            step(t, win);
+#pragma unroll
+            for (int i = HIST - 1; i >= 0; --i) win[P + i] = win[i];
+        }
     }
 }
 
 // Backward, dilation 3.  A block is four waves over four consecutive tiles of
-// the same 64 quads; wave w takes tile 4 * tile_group + w.  Every wave keeps
+// the same 64 quads; wave w takes tile 4 * tile_group + w, odd waves walking
+// down as in the forward.  Every wave keeps
 // fp32 sums of dweight / dbias over its tile; the four are added in wave order
 // in fp64 and written as one partial per (batch row, tile group):
 // partial [B * tile_groups][C][K + 1].
@@ -334,39 +362,13 @@ __global__ __launch_bounds__(kPleBlock) void short_conv_bwd_d3_kernel(
     const Q* gb = (const Q*)dyp + b * S * quads + qc;
     const Q* halo = (const Q*)halop;
     const int64_t t0 = min(S, tt * kConvTile), t1 = min(S, t0 + kConvTile);  // empty for a tile past the end
-    Q xw[HIST + P];  // x at t - HIST .. t + P - 1
-    Q gw[HIST + P];  // dy at t .. t + HIST + P - 1
-#pragma unroll
-    for (int i = 0; i < HIST; ++i) {
-        const int64_t ts = t0 - HIST + i;
-        xw[i] = *(ts >= 0 ? xb + ts * quads : (halo ? halo + ((b * HIST + HIST + ts) * quads + qc) : zero));
-        gw[i] = *(t0 + i < S ? gb + (t0 + i) * quads : zero);
-    }
-    if (dhalop && tt == 0 && t1 > t0 && live) {
-        // halo position i (sequence position i - HIST): taps reach dy at i - HIST + (K - 1 - k) * 3
-#pragma unroll
-        for (int i = 0; i < HIST; ++i) {
-            float acc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-            for (int k = 0; k < K; ++k) {
-                const int off = i - HIST + (K - 1 - k) * kConvD;
-                if (off >= 0) {
-                    float f[4];
-                    unpack4<BF16>(gw[off], f);
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) acc[e] = fmaf(wv[e][k], f[e], acc[e]);
-                }
-            }
-            ((Q*)dhalop)[(b * HIST + i) * quads + q] = pack4<BF16>(acc);
-        }
-    }
     Q* dxb = (Q*)dxp + b * S * quads + q;
-    for (int64_t t = t0; t < t1; t += P) {
-#pragma unroll
-        for (int j = 0; j < P; ++j) {
-            xw[HIST + j] = *(t + j < S ? xb + (t + j) * quads : zero);
-            gw[HIST + j] = *(t + HIST + j < S ? gb + (t + HIST + j) * quads : zero);
-        }
+    // x at position tx (halo before 0, zero from S on)
+    auto xsrc = [&](int64_t tx) -> const Q* {
+        return tx >= S ? zero : tx >= 0 ? xb + tx * quads : (halo ? halo + ((b * HIST + HIST + tx) * quads + qc) : zero);
+    };
+    auto gsrc = [&](int64_t tg) -> const Q* { return tg < S ? gb + tg * quads : zero; };
+    auto step = [&](int64_t t, const Q (&xw)[HIST + P], const Q (&gw)[HIST + P]) {
 #pragma unroll
         for (int j = 0; j < P; ++j) {
             if (t + j >= t1) break;  // wave-uniform
@@ -390,10 +392,66 @@ __global__ __launch_bounds__(kPleBlock) void short_conv_bwd_d3_kernel(
 #pragma unroll
             for (int e = 0; e < 4; ++e) pw[e][K] += g[e];
         }
+    };
+    if ((wave & 1) == 0 || t1 <= t0) {  // up from t0
+        Q xw[HIST + P];  // x at t - HIST .. t + P - 1
+        Q gw[HIST + P];  // dy at t .. t + HIST + P - 1
 #pragma unroll
         for (int i = 0; i < HIST; ++i) {
-            xw[i] = xw[i + P];
-            gw[i] = gw[i + P];
+            xw[i] = *xsrc(t0 - HIST + i);
+            gw[i] = *gsrc(t0 + i);
+        }
+        if (dhalop && tt == 0 && t1 > t0 && live) {
+#pragma unroll
+            for (int i = 0; i < HIST; ++i) {
+                float acc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+                for (int k = 0; k < K; ++k) {
+                    const int off = i - HIST + (K - 1 - k) * kConvD;
+                    if (off >= 0) {
+                        float f[4];
+                        unpack4<BF16>(gw[off], f);
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) acc[e] = fmaf(wv[e][k], f[e], acc[e]);
+                    }
+                }
+                ((Q*)dhalop)[(b * HIST + i) * quads + q] = pack4<BF16>(acc);
+            }
+        }
+        for (int64_t t = t0; t < t1; t += P) {
+#pragma unroll
+            for (int j = 0; j < P; ++j) {
+                xw[HIST + j] = *xsrc(t + j);
+                gw[HIST + j] = *gsrc(t + HIST + j);
+            }
+            step(t, xw, gw);
+#pragma unroll
+            for (int i = 0; i < HIST; ++i) {
+                xw[i] = xw[i + P];
+                gw[i] = gw[i + P];
+            }
+        }
+    } else {  // down from the last step, the windows shifting up
+        Q xw[HIST + P];
+        Q gw[HIST + P];
+        int64_t t = t0 + ((t1 - t0 - 1) / P) * P;
+#pragma unroll
+        for (int i = 0; i < HIST; ++i) {
+            xw[P + i] = *xsrc(t - HIST + P + i);
+            gw[P + i] = *gsrc(t + P + i);
+        }
+        for (; t >= t0; t -= P) {
+#pragma unroll
+            for (int j = 0; j < P; ++j) {
+                xw[j] = *xsrc(t - HIST + j);
+                gw[j] = *gsrc(t + j);
+            }
+            step(t, xw, gw);
+#pragma unroll
+            for (int i = HIST - 1; i >= 0; --i) {
+                xw[P + i] = xw[i];
+                gw[P + i] = gw[i];
+            }
         }
     }
 #pragma unroll
@@ -641,6 +699,29 @@ unsigned blocks_for(int64_t threads) { return (unsigned)((threads + kPleBlock - 
 
 }  // namespace
 
+// Work-items of the largest launch a convolution call (forward or backward)
+// makes; saturates at INT64_MAX.  Arguments are non-negative.
+static int64_t mul_sat(int64_t a, int64_t b) {
+    int64_t r;
+    return __builtin_mul_overflow(a, b, &r) ? INT64_MAX : r;
+}
+
+int64_t short_conv_launch_items(int64_t batch, int64_t seq, int64_t channels, int kernel, int dilation,
+                                int elem_bytes) {
+    const int64_t vec = 16 / elem_bytes;
+    // the halo's gradient zeroed when there are no positions
+    const int64_t halo = mul_sat(mul_sat(batch, (int64_t)(kernel - 1) * dilation), channels / vec);
+    if (dilation == kConvD) {
+        const int64_t tiles = (seq + kConvTile - 1) / kConvTile;
+        const int64_t blocks = mul_sat(mul_sat(batch, (tiles + kConvWavesPerBlock - 1) / kConvWavesPerBlock),
+                                       (channels / 4 + 63) / 64);
+        return std::max(mul_sat(blocks, kPleBlock), halo);
+    }
+    const int64_t fwd = mul_sat(mul_sat(batch, (seq + kConvTileFwd - 1) / kConvTileFwd), channels / vec);
+    const int64_t bwd = mul_sat(mul_sat(batch, (seq + kConvTileBwd - 1) / kConvTileBwd), channels / vec);
+    return std::max({fwd, bwd, halo});
+}
+
 size_t short_conv_workspace_bytes(int64_t batch, int64_t seq, int64_t channels, int kernel) {
     const int64_t tiles = (seq + kConvTileBwd - 1) / kConvTileBwd;
     return (size_t)batch * (size_t)tiles * (size_t)channels * (size_t)(kernel + 1) * sizeof(double);
@@ -671,8 +752,9 @@ hipError_t launch_short_conv(const void* x, int elem_bytes, int64_t B, int64_t S
                              const float* bias, int K, int d, const void* halo, void* y, hipStream_t stream) {
     if (B * S == 0) return hipSuccess;
     if (d == kConvD) {
-        const int64_t threads = B * ((S + kConvTile - 1) / kConvTile) * (C / 4);
-        const dim3 grid(blocks_for(threads)), block(kPleBlock);
+        const int64_t tiles = (S + kConvTile - 1) / kConvTile;
+        const int64_t blocks = B * ((tiles + kConvWavesPerBlock - 1) / kConvWavesPerBlock) * ((C / 4 + 63) / 64);
+        const dim3 grid((unsigned)blocks), block(kPleBlock);
         ENGRAM_CONV_DISPATCH(short_conv_fwd_d3_kernel, x, halo, w, bias, B, S, C, y)
     } else {
         const int vec = 16 / elem_bytes;

@@ -409,7 +409,9 @@ int engram_unpermute_rows(const void* src, int64_t row_bytes, const int64_t* ord
  * and group_size (norm) times the element size must be a multiple of 16 bytes;
  * group_size * element size <= 10240 bytes (5120 bf16, 2560 fp32 features);
  * hidden % group_size == 0.  At most 2^36 elements per tensor, and for the
- * norm at most 2^25 (row, group) pairs, so that every launch fits.
+ * norm at most 2^25 (row, group) pairs, so that every launch fits; a
+ * convolution call whose launches would hold 2^32 work-items or more (short
+ * sequences over very many batch rows reach that first) gets ENGRAM_EINVAL.
  * 1 <= K <= 4, d >= 1.  Gradients of weight and bias are sums over every batch
  * row and position, reduced in a fixed order (deterministic), and overwrite
  * dweight / dbias.  The backward calls need a device workspace (256-byte

@@ -320,6 +320,16 @@ def test_calls_past_the_launch_limits_rejected(lib):
     assert lib.engram_hash_slice(ok, 1 << 26, 128, 0, 64, ctypes.byref(s), ok, None) == B.ENGRAM_EINVAL
     # PLE: 2^36 elements per tensor at most
     assert lib.engram_short_conv(ok, bf, 1 << 18, 1 << 10, 512, ok, None, 4, 3, None, ok, None) == B.ENGRAM_EINVAL
+    # PLE: within 2^36 elements, but one position per batch row: the dilation-3
+    # launches (a 256-lane block per batch row) and the other dilations' launches
+    # (a lane per 8 channels) would reach 2^32 work-items
+    assert lib.engram_short_conv(ok, bf, 1 << 24, 1, 8, ok, None, 4, 3, None, ok, None) == B.ENGRAM_EINVAL
+    assert lib.engram_short_conv_backward(ok, ok, bf, 1 << 24, 1, 8, ok, 4, 3, None, ok, ok, None, None, ok,
+                                          1 << 60, None) == B.ENGRAM_EINVAL
+    assert lib.engram_short_conv(ok, bf, 1 << 32, 1, 16, ok, None, 4, 2, None, ok, None) == B.ENGRAM_EINVAL
+    # no positions, but a halo gradient to clear for 2^40 batch rows
+    assert lib.engram_short_conv_backward(None, None, bf, 1 << 40, 0, 8, ok, 4, 3, None, None, ok, None, ok, None,
+                                          0, None) == B.ENGRAM_EINVAL
     # norm: 2^25 (row, group) pairs at most
     assert lib.engram_grouped_rms_norm(ok, bf, (1 << 24) + 1, 16, 8, ok, 1e-6, ok, None) == B.ENGRAM_EINVAL
     assert lib.engram_grouped_rms_norm_backward(ok, ok, bf, (1 << 24) + 1, 16, 8, ok, 1e-6, ok, ok, ok, 1 << 40,
