@@ -224,8 +224,9 @@ __global__ __launch_bounds__(kPleBlock) void short_conv_bwd_kernel(
 
 // ---- dilation 3 (the released layer): sliding register windows
 //
-// One thread owns four channels of one batch row over kConvTile positions and
-// walks them kConvStep positions at a time.  Its window holds the inputs from
+// One thread owns four channels of one batch row over a tile of positions
+// (kConvTile in the backward, kConvTileUp in the forward) and walks them
+// kConvStep positions at a time.  Its window holds the inputs from
 // HIST = (K - 1) * 3 positions back up to the current step, so every input is
 // loaded once per tile (plus the HIST-position overlap with the previous tile)
 // instead of once per tap.  Window indices are compile-time constants: the
@@ -240,8 +241,9 @@ __global__ __launch_bounds__(kPleBlock) void short_conv_bwd_kernel(
 // of their walks, or both at the start), so the overlap rows come from L2
 // instead of being fetched twice.
 
-// Build-time tuning parameters (positions per step, positions per tile), at
-// the measured best of steps 3, 6, 9 and tiles 96, 144, 192.  The streaming
+// Build-time tuning parameters (positions per step, positions per tile of the
+// backward and of the forward), at the measured best of steps 3, 6, 9, of
+// backward tiles 48, 72, 96, 144, 192, and of forward tiles 24 to 96.  The streaming
 // outputs of the norm kernels and of the convolution backward are stored
 // non-temporally (each 3-5% faster at [8, 4096, 10240]); the convolution
 // forward keeps plain stores (1.7% slower with them).
@@ -251,9 +253,13 @@ __global__ __launch_bounds__(kPleBlock) void short_conv_bwd_kernel(
 #ifndef ENGRAM_CONV_TILE
 #define ENGRAM_CONV_TILE 96
 #endif
+#ifndef ENGRAM_CONV_TILE_UP
+#define ENGRAM_CONV_TILE_UP 48
+#endif
 constexpr int kConvD = 3;
 constexpr int kConvStep = ENGRAM_CONV_STEP;
-constexpr int kConvTile = ENGRAM_CONV_TILE;  // positions per thread (multiple of kConvStep)
+constexpr int kConvTile = ENGRAM_CONV_TILE;      // backward: positions per thread (multiple of kConvStep)
+constexpr int kConvTileUp = ENGRAM_CONV_TILE_UP;  // forward: positions per thread (multiple of kConvStep)
 constexpr int kConvWavesPerBlock = kPleBlock / 64;
 
 template <bool BF16, int K>
@@ -267,11 +273,11 @@ __global__ __launch_bounds__(kPleBlock) void short_conv_fwd_d3_kernel(const void
     const Q* halo = (const Q*)halop;
     const Q* zero = (const Q*)&kPleZero;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int64_t quads = C / 4, tiles = (S + kConvTile - 1) / kConvTile;
+    const int64_t quads = C / 4, tiles = (S + kConvTileUp - 1) / kConvTileUp;
     const int64_t tgroups = (tiles + kConvWavesPerBlock - 1) / kConvWavesPerBlock, qgroups = (quads + 63) / 64;
     const int64_t qg = blockIdx.x % qgroups, rest = blockIdx.x / qgroups, tg = rest % tgroups, b = rest / tgroups;
     const int64_t q = qg * 64 + lane, tt = tg * kConvWavesPerBlock + wave;
-    const int64_t t0 = min(S, tt * kConvTile), t1 = min(S, t0 + kConvTile);
+    const int64_t t0 = min(S, tt * kConvTileUp), t1 = min(S, t0 + kConvTileUp);
     if (q >= quads || t1 <= t0) return;  // no barrier or cross-lane step below
     float wv[4][K], bv[4];
 #pragma unroll
@@ -712,7 +718,8 @@ int64_t short_conv_launch_items(int64_t batch, int64_t seq, int64_t channels, in
     // the halo's gradient zeroed when there are no positions
     const int64_t halo = mul_sat(mul_sat(batch, (int64_t)(kernel - 1) * dilation), channels / vec);
     if (dilation == kConvD) {
-        const int64_t tiles = (seq + kConvTile - 1) / kConvTile;
+        const int64_t tile = std::min(kConvTile, kConvTileUp);  // the larger grid of the two
+        const int64_t tiles = (seq + tile - 1) / tile;
         const int64_t blocks = mul_sat(mul_sat(batch, (tiles + kConvWavesPerBlock - 1) / kConvWavesPerBlock),
                                        (channels / 4 + 63) / 64);
         return std::max(mul_sat(blocks, kPleBlock), halo);
@@ -752,7 +759,7 @@ hipError_t launch_short_conv(const void* x, int elem_bytes, int64_t B, int64_t S
                              const float* bias, int K, int d, const void* halo, void* y, hipStream_t stream) {
     if (B * S == 0) return hipSuccess;
     if (d == kConvD) {
-        const int64_t tiles = (S + kConvTile - 1) / kConvTile;
+        const int64_t tiles = (S + kConvTileUp - 1) / kConvTileUp;
         const int64_t blocks = B * ((tiles + kConvWavesPerBlock - 1) / kConvWavesPerBlock) * ((C / 4 + 63) / 64);
         const dim3 grid((unsigned)blocks), block(kPleBlock);
         ENGRAM_CONV_DISPATCH(short_conv_fwd_d3_kernel, x, halo, w, bias, B, S, C, y)
