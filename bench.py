@@ -1160,7 +1160,7 @@ def add_ceiling_fracs(result, ceilings):
 LOOKUP_PHASES = {
     "hash": ("hash.hip", [r"\bhash_kernel"]),
     "gather": ("gather.hip", [r"\bgather_rows_kernel"]),
-    "scatter_plan": ("scatter.hip", [r"\bscatter_init_kernel", r"\bkeys_kernel", r"\bupsweep_kernel",
+    "scatter_plan": ("scatter.hip", [r"\bscatter_init_kernel", r"\bkeys_kernel", r"\bhead_keys_kernel", r"\bupsweep_kernel",
                                      r"\bdownsweep_kernel", r"\brun_count_kernel", r"\bblock_scan_kernel",
                                      r"\buniq_rows_kernel"]),
     "scatter_apply": ("scatter.hip", [r"\bsegment_reduce_kernel", r"\bcarry_fixup_kernel", r"\blong_run_kernel"]),
@@ -1203,17 +1203,39 @@ WORKLOAD_TEXT = {
 }
 
 
-def sort_nominal_bytes(n, num_rows, uniq=None, from_tokens=False):
+def plan_passes(num_rows, from_tokens=False, moduli=None, offsets=None, row_begin=0):
+    """Digit passes of the backward plan's sort: 8-bit digits over the bits of
+    num_rows (the out-of-range sentinel num_rows sorts last); from tokens, when
+    every head's range [offset, offset + modulus) lies in the shard and the
+    ranges are disjoint and ascending in head order, the sort runs per head over
+    the bits of the largest modulus (the last pass taking 9 bits where that
+    saves a pass), if that needs fewer passes."""
+    bits = 0
+    while bits < 32 and (num_rows >> bits) != 0:
+        bits += 1
+    passes = (bits + 7) // 8
+    if not from_tokens or moduli is None:
+        return passes
+    prev_end = 0
+    for off, mod in zip(offsets, moduli):
+        lo = off - row_begin
+        if lo < 0 or lo > num_rows or mod > num_rows - lo or lo < prev_end:
+            return passes
+        prev_end = lo + mod
+    head_bits = (max(moduli) - 1).bit_length()
+    split = 1 if head_bits <= 8 else max(2, (head_bits - 1 + 7) // 8)
+    return min(passes, split)
+
+
+def sort_nominal_bytes(n, num_rows, uniq=None, from_tokens=False, passes=None):
     """HBM bytes the backward plan's own traffic model gives for n lookups:
     keys (8 B row read, or 8 B per token when the plan hashes the rows itself,
     and 4 B key written), the first pass (4 B read, 8 B written), each later
     pass (16 B) with its histogram (4 B), the run count's read (4 B) and, in
     the compact form, the distinct rows' pass (4 B read, 8 B per distinct row
-    written)."""
-    bits = 0
-    while bits < 32 and (num_rows >> bits) != 0:   # the out-of-range sentinel num_rows sorts last
-        bits += 1
-    passes = (bits + 7) // 8
+    written).  `passes` defaults to the whole sort's (plan_passes)."""
+    if passes is None:
+        passes = plan_passes(num_rows)
     total = (n // 2 if from_tokens else 8 * n) + 16 * n + (passes - 1) * 20 * n + 4 * n
     if uniq is not None:
         total += 4 * n + 8 * uniq
@@ -1357,8 +1379,13 @@ def summarize_profiles(name, raw):
             comp["owner_response"] = line["owner_response"].get("compulsory_bytes_per_launch", alg["owner_response"])
         if "scatter_apply" in line["phase_gbps"]:
             alg["scatter_apply"] = comp["scatter_apply"] = line["roofline"]["algorithmic_bytes_per_launch"]
+            # the full table's workloads hash with the released head layout
+            released = cfg["table_rows"] == E.QWEN3_8_FLASH_NEXT_NGRAM_PADDED_ROWS
+            passes = plan_passes(cfg["table_rows"], fused, E.QWEN3_8_FLASH_NEXT_NGRAM_HEAD_VOCAB_SIZES,
+                                 E.QWEN3_8_FLASH_NEXT_NGRAM_HEAD_OFFSETS) if released else None
             alg["scatter_plan"] = comp["scatter_plan"] = sort_nominal_bytes(n, cfg["table_rows"],
-                                                                            cfg["distinct_rows_rotation0"], fused)
+                                                                            cfg["distinct_rows_rotation0"], fused,
+                                                                            passes)
     for phase in COUNTED[name]:
         if phase not in alg or phase not in fetch:
             continue

@@ -488,10 +488,12 @@ hipError_t launch_route_plan(const int64_t* ids, int64_t n, int64_t local_rows, 
     const GroupedOut go{ids, sorted_ids, order, send_counts, world};
     if (small_counts(dc))
         hipLaunchKernelGGL((downsweep_kernel<true, kItems, true>), dim3(tiles), dim3(kBlock), 0, stream, ka,
-                           (const uint32_t*)nullptr, (uint32_t*)nullptr, (uint32_t*)nullptr, nn, 0, dc, go);
+                           (const uint32_t*)nullptr, (uint32_t*)nullptr, (uint32_t*)nullptr, 0, dc,
+                           one_segment(nn, tiles), go);
     else
         hipLaunchKernelGGL((downsweep_kernel<false, kItems, true>), dim3(tiles), dim3(kBlock), 0, stream, ka,
-                           (const uint32_t*)nullptr, (uint32_t*)nullptr, (uint32_t*)nullptr, nn, 0, dc, go);
+                           (const uint32_t*)nullptr, (uint32_t*)nullptr, (uint32_t*)nullptr, 0, dc,
+                           one_segment(nn, tiles), go);
     return hipGetLastError();
 }
 

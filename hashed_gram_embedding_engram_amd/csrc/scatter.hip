@@ -20,6 +20,15 @@
 //               then a stable scatter that derives its digit offsets from
 //               those counts, ranks digits inside each wave with ballots (no
 //               atomics) and writes each tile digit-grouped through LDS.
+//               From tokens, when the heads' row ranges are disjoint,
+//               ascending and inside the shard, the sort is split by head
+//               instead: every position has exactly one lookup per head, so
+//               head h's lookups take entries [h * npos, (h + 1) * npos) with
+//               no counting pass, and each head sorts only row - offset[h]
+//               (below its modulus: 25 bits for the released table, three
+//               passes of 8, 8 and 9 bits).  Disjoint ascending ranges make
+//               the head-major order the global row order, so the result is
+//               the same as the whole sort's.
 //   3. runs     run starts per slice of S sorted entries, their prefix sum
 //               (the distinct-row index of every run) and, for the compact
 //               form, the distinct rows themselves.
@@ -90,6 +99,8 @@ struct Layout {
     int64_t num_tiles, num_slices, num_run_blocks;
 };
 constexpr int kMaxPasses = 4;  // 32-bit keys, 8-bit digits
+constexpr int kRadixWide = 512;  // the 9-bit last pass of a sort split by head
+constexpr int kTokenHeads = 16;  // rows per position of the released head layout
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
@@ -100,10 +111,22 @@ size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 // in part, and fewer blocks compete with the gather for wave slots.
 int sort_items(int64_t n) { return n <= ((int64_t)1 << 20) ? 8 : n >= ((int64_t)1 << 21) ? 24 : 16; }
 
+// Tiles per head of a sort split by head (0 when n is not 16 rows per position).
+int64_t head_tiles(int64_t n) {
+    const int64_t tile = (int64_t)kBlock * sort_items(n);
+    return n > 0 && n % kTokenHeads == 0 ? (n / kTokenHeads + tile - 1) / tile : 0;
+}
+
 Layout make_layout(int64_t n, int dim) {
     Layout L;
     const int64_t tile = (int64_t)kBlock * sort_items(n);
     L.num_tiles = (n + tile - 1) / tile;
+    const int64_t ht = head_tiles(n);
+    // room for either form of the sort: whole, or split by head with 512-digit counts
+    const size_t hist_words = std::max((size_t)kRadix * (size_t)L.num_tiles,
+                                       (size_t)kRadixWide * (size_t)(kTokenHeads * ht));
+    const size_t pass_words = std::max(count_words(L.num_tiles),
+                                       ht ? (size_t)kTokenHeads * count_words(ht, kRadixWide) : (size_t)0);
     L.num_slices = (n + kSlice - 1) / kSlice;
     L.num_run_blocks = (n + run_span(n) - 1) / run_span(n);
     size_t off = 0;
@@ -112,8 +135,8 @@ Layout make_layout(int64_t n, int dim) {
     L.spare_keys = take(4 * (size_t)n);
     L.sorted_vals = take(4 * (size_t)n);
     L.spare_vals = take(4 * (size_t)n);
-    L.hist = take(4 * (size_t)kRadix * (size_t)L.num_tiles);
-    L.count_totals = take(4 * count_words(L.num_tiles) * kMaxPasses);  // one set per pass
+    L.hist = take(4 * hist_words);
+    L.count_totals = take(4 * pass_words * kMaxPasses);  // one set per pass
     L.counters = take(16);
     L.slice_runs = take(4 * (size_t)L.num_slices);
     L.slice_base = take(4 * (size_t)L.num_slices);
@@ -153,7 +176,6 @@ struct TokenRows {
     uint32_t seq_len;
     HashParams p;
 };
-constexpr int kTokenHeads = 16;
 // Rows as the exchange delivers them: [world][capacity] blocks whose first
 // counts[w] entries are rows and the rest padding (counts == nullptr: every
 // entry is a row).  Padding takes the sentinel key without a report.
@@ -261,6 +283,74 @@ __global__ __launch_bounds__(kBlock) void keys_kernel(const int64_t* __restrict_
 #pragma unroll
     for (int k = 0; k < kBlock / 64; ++k) c += s_cnt[k][tid];
     publish_tile_counts(dc, blockIdx.x, tid, c);
+    if (tid == 0 && s_valid) atomicAdd(&counters[0], s_valid);
+}
+
+// Step 1 of the plan from tokens, split by head (see step 2 above): block
+// (h, tile) hashes head h of the tile's positions, so position pos's head-h
+// lookup (lookup index 16 pos + h) becomes entry pos of segment h, with the
+// histogram of the digit-0 of row - offset[h].  The host has checked that
+// every head's range lies in the shard, so every lookup is in range.  Lane
+// l's item it is position base + 64 it + l; the three tokens it needs are
+// loaded directly (neighbouring lanes share them in cache).
+template <int ITEMS>
+__global__ __launch_bounds__(kBlock) void head_keys_kernel(TokenRows tr, int64_t row_begin, Segments sg,
+                                                           uint32_t* __restrict__ keys, DigitCounts dc,
+                                                           uint32_t* __restrict__ counters) {
+    __shared__ uint32_t s_cnt[kBlock / 64][kRadix];
+    __shared__ uint32_t s_valid;
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const uint32_t h = blockIdx.x / sg.tiles, tile = blockIdx.x - h * sg.tiles;
+    const uint32_t npos = sg.len, sb = segment_base(sg, h);
+    dc = segment_counts(dc, sg, h);
+#pragma unroll
+    for (int k = 0; k < kBlock / 64; ++k) s_cnt[k][tid] = 0;
+    if (tid == 0) s_valid = 0;
+    __syncthreads();
+    // Head h's modulus, reciprocal and offset (block-uniform), selected with
+    // compile-time indices so the parameters stay kernel arguments.
+    uint64_t mod = tr.p.mod[0], magic = tr.p.magic[0];
+    int64_t off = tr.p.off[0];
+#pragma unroll
+    for (int j = 1; j < kTokenHeads; ++j)
+        if (h == (uint32_t)j) {
+            mod = tr.p.mod[j];
+            magic = tr.p.magic[j];
+            off = tr.p.off[j];
+        }
+    const bool trigram = h >= (uint32_t)(kTokenHeads / 2);
+    const uint32_t pos0 = tile * (uint32_t)(kBlock * ITEMS) + (uint32_t)w * (64 * ITEMS) + (uint32_t)lane;
+    uint32_t t = pos0 % tr.seq_len;  // item 0's column; advances by 64 an item
+    uint32_t my_valid = 0;
+    uint32_t* const seg_keys = keys + (size_t)h * npos;
+#pragma unroll
+    for (int it = 0; it < ITEMS; ++it) {
+        const uint32_t pos = pos0 + 64u * (uint32_t)it;
+        const uint32_t q = min(pos, npos - 1);
+        const int64_t x0 = tr.tokens[q], x1 = tr.tokens[q >= 1 ? q - 1 : 0u], x2 = tr.tokens[q >= 2 ? q - 2 : 0u];
+        const bool valid1 = t >= 1 && x1 != tr.p.eos;
+        const bool valid2 = valid1 && t >= 2 && x2 != tr.p.eos;
+        const int64_t ctx1 = valid1 ? x1 : tr.p.fill, ctx2 = valid2 ? x2 : tr.p.fill;
+        const uint64_t mix2 = (uint64_t)x0 * (uint64_t)tr.p.mult[0] ^ (uint64_t)ctx1 * (uint64_t)tr.p.mult[1];
+        const uint64_t mix = trigram ? mix2 ^ (uint64_t)ctx2 * (uint64_t)tr.p.mult[2] : mix2;
+        const int64_t row = (int64_t)floor_mod((int64_t)mix, mod, magic) + off;
+        if (pos < npos) {
+            const uint32_t key = (uint32_t)((uint64_t)row - (uint64_t)row_begin);
+            seg_keys[pos] = key;
+            atomicAdd(&s_cnt[w][(key - sb) & 0xFFu], 1u);
+            ++my_valid;
+        }
+        t += 64;
+        if (t >= tr.seq_len) t = tr.seq_len >= 64 ? t - tr.seq_len : t % tr.seq_len;
+    }
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) my_valid += __shfl_xor(my_valid, o, 64);
+    if (lane == 0 && my_valid) atomicAdd(&s_valid, my_valid);
+    __syncthreads();
+    uint32_t c = 0;
+#pragma unroll
+    for (int k = 0; k < kBlock / 64; ++k) c += s_cnt[k][tid];
+    publish_tile_counts(dc, tile, tid, c);
     if (tid == 0 && s_valid) atomicAdd(&counters[0], s_valid);
 }
 
@@ -932,13 +1022,49 @@ hipError_t dispatch_reduce(const Layout& L, const char* ws, const void* grad_out
 }
 
 // Steps 1-2: keys and the radix passes, ending in the sorted slots.
+// The shape of one sort: its segments (one for the whole sort, kTokenHeads
+// when split by head), the tiles per segment, the number of passes and the
+// digit width of the last one.
+struct SortShape {
+    Segments sg;
+    uint32_t num_segs;
+    int passes, last_bits;
+    size_t pass_words;  // chunk and group totals of one pass, all segments
+};
+
+// One digit pass: the histogram (unless the keys kernel made it), then the scatter.
+template <int ITEMS, int BITS>
+hipError_t sort_pass(const SortShape& S, char* ws, const Layout& L, uint32_t* totals, bool first, int shift,
+                     const uint32_t* k_cur, const uint32_t* v_cur, uint32_t* k_nxt, uint32_t* v_nxt,
+                     hipStream_t stream) {
+    constexpr int R = 1 << BITS;
+    Segments sg = S.sg;
+    sg.hist_words = sg.tiles * (uint32_t)R;
+    sg.total_words = (uint32_t)count_words(sg.tiles, R);
+    const DigitCounts dc = make_digit_counts(ws + L.hist, totals, sg.tiles, R);
+    const uint32_t grid = sg.tiles * S.num_segs;
+    if (!first) {
+        hipLaunchKernelGGL((upsweep_kernel<ITEMS, BITS>), dim3(grid), dim3(kBlock), 0, stream, k_cur, shift, dc, sg);
+        hipError_t err = hipGetLastError();
+        if (err != hipSuccess) return err;
+    }
+    const uint32_t* v_in = first ? nullptr : v_cur;
+    if (small_counts(dc))
+        hipLaunchKernelGGL((downsweep_kernel<true, ITEMS, false, BITS>), dim3(grid), dim3(kBlock), 0, stream, k_cur,
+                           v_in, k_nxt, v_nxt, shift, dc, sg, GroupedOut{});
+    else
+        hipLaunchKernelGGL((downsweep_kernel<false, ITEMS, false, BITS>), dim3(grid), dim3(kBlock), 0, stream, k_cur,
+                           v_in, k_nxt, v_nxt, shift, dc, sg, GroupedOut{});
+    return hipGetLastError();
+}
+
 template <int ITEMS>
 hipError_t run_sort(const Layout& L, char* ws, const int64_t* rows, const TokenRows* tr, Padding pad, int64_t n,
-                    int64_t row_begin, int64_t num_rows, int passes, int64_t* status, hipStream_t stream) {
+                    int64_t row_begin, int64_t num_rows, const SortShape& S, int64_t* status, hipStream_t stream) {
     uint32_t* counters = (uint32_t*)(ws + L.counters);
-    const size_t pass_words = count_words(L.num_tiles);  // chunk and group totals of one pass
     uint32_t* count_totals = (uint32_t*)(ws + L.count_totals);
     const uint32_t nn = (uint32_t)n, tiles = (uint32_t)L.num_tiles;
+    const int passes = S.passes;
     hipError_t err;
     // Passes ping-pong between the two buffers and must end in the sorted slots.
     uint32_t *k_cur, *k_nxt, *v_cur, *v_nxt;
@@ -949,33 +1075,59 @@ hipError_t run_sort(const Layout& L, char* ws, const int64_t* rows, const TokenR
         k_cur = (uint32_t*)(ws + L.spare_keys); k_nxt = (uint32_t*)(ws + L.sorted_keys);
         v_cur = (uint32_t*)(ws + L.spare_vals); v_nxt = (uint32_t*)(ws + L.sorted_vals);
     }
-    auto pass_counts = [&](int p) { return make_digit_counts(ws + L.hist, count_totals + p * pass_words, L.num_tiles); };
-    if (tr)
+    if (S.num_segs > 1) {
+        Segments sg = S.sg;
+        sg.hist_words = sg.tiles * (uint32_t)kRadix;
+        sg.total_words = (uint32_t)count_words(sg.tiles);
+        hipLaunchKernelGGL(head_keys_kernel<ITEMS>, dim3(sg.tiles * S.num_segs), dim3(kBlock), 0, stream, *tr,
+                           row_begin, sg, k_cur, make_digit_counts(ws + L.hist, count_totals, sg.tiles), counters);
+    } else if (tr) {
         hipLaunchKernelGGL((keys_kernel<ITEMS, true>), dim3(tiles), dim3(kBlock), 0, stream, nullptr, *tr, nn,
-                           row_begin, (uint64_t)num_rows, k_cur, pass_counts(0), status, counters, Padding{});
-    else
+                           row_begin, (uint64_t)num_rows, k_cur, make_digit_counts(ws + L.hist, count_totals, tiles),
+                           status, counters, Padding{});
+    } else {
         hipLaunchKernelGGL((keys_kernel<ITEMS, false>), dim3(tiles), dim3(kBlock), 0, stream, rows, TokenRows{}, nn,
-                           row_begin, (uint64_t)num_rows, k_cur, pass_counts(0), status, counters, pad);
+                           row_begin, (uint64_t)num_rows, k_cur, make_digit_counts(ws + L.hist, count_totals, tiles),
+                           status, counters, pad);
+    }
     if ((err = hipGetLastError()) != hipSuccess) return err;
     for (int p = 0; p < passes; ++p) {
-        const int shift = 8 * p;
-        const DigitCounts dc = pass_counts(p);
-        if (p > 0) {
-            hipLaunchKernelGGL(upsweep_kernel<ITEMS>, dim3(tiles), dim3(kBlock), 0, stream, k_cur, nn, shift, dc);
-            if ((err = hipGetLastError()) != hipSuccess) return err;
-        }
-        const uint32_t* v_in = p == 0 ? nullptr : v_cur;
-        if (small_counts(dc))
-            hipLaunchKernelGGL((downsweep_kernel<true, ITEMS>), dim3(tiles), dim3(kBlock), 0, stream, k_cur, v_in, k_nxt,
-                               v_nxt, nn, shift, dc, GroupedOut{});
+        uint32_t* totals = count_totals + p * S.pass_words;
+        if (p == passes - 1 && S.last_bits == 9)
+            err = sort_pass<ITEMS, 9>(S, ws, L, totals, p == 0, 8 * p, k_cur, v_cur, k_nxt, v_nxt, stream);
         else
-            hipLaunchKernelGGL((downsweep_kernel<false, ITEMS>), dim3(tiles), dim3(kBlock), 0, stream, k_cur, v_in, k_nxt,
-                               v_nxt, nn, shift, dc, GroupedOut{});
-        if ((err = hipGetLastError()) != hipSuccess) return err;
+            err = sort_pass<ITEMS, 8>(S, ws, L, totals, p == 0, 8 * p, k_cur, v_cur, k_nxt, v_nxt, stream);
+        if (err != hipSuccess) return err;
         uint32_t* t = k_cur; k_cur = k_nxt; k_nxt = t;
         t = v_cur; v_cur = v_nxt; v_nxt = t;
     }
     return hipSuccess;
+}
+
+// Whether the plan from tokens can split its sort by head, and with how many
+// passes: every head's range [offset, offset + modulus) inside the shard,
+// each starting at or after the previous one's end, and fewer passes over
+// the bits of the largest modulus than over those of num_rows.
+bool head_split(const TokenRows* tr, int64_t n, int64_t row_begin, int64_t num_rows, int whole_passes,
+                int* passes, int* last_bits) {
+    if (!tr || head_tiles(n) == 0) return false;
+    uint64_t prev_end = 0, max_mod = 0;
+    for (int h = 0; h < kTokenHeads; ++h) {
+        const int64_t off = tr->p.off[h];
+        const uint64_t mod = tr->p.mod[h];
+        if (off < row_begin) return false;
+        const uint64_t lo = (uint64_t)(off - row_begin);  // shard-relative start
+        if (lo > (uint64_t)num_rows || mod > (uint64_t)num_rows - lo || lo < prev_end) return false;
+        prev_end = lo + mod;
+        max_mod = std::max(max_mod, mod);
+    }
+    int bits = 0;
+    while (bits < 64 && ((max_mod - 1) >> bits) != 0) ++bits;  // keys below max_mod
+    int p = bits <= 8 ? 1 : std::max(2, (bits - 1 + 7) / 8);
+    if (p >= whole_passes) return false;
+    *passes = p;
+    *last_bits = 8 * p >= bits ? 8 : 9;
+    return true;
 }
 
 }  // namespace
@@ -996,19 +1148,35 @@ hipError_t scatter_plan(const int64_t* rows, const TokenRows* tr, Padding pad, i
     uint32_t* counters = (uint32_t*)(ws + L.counters);
     int bits = 0;
     while (bits < 32 && ((uint64_t)num_rows >> bits) != 0) ++bits;  // the sentinel num_rows sorts last
-    const int passes = (bits + 7) / 8;
-    const size_t pass_words = count_words(L.num_tiles);  // chunk and group totals of one pass
+    SortShape S;
+    S.passes = (bits + 7) / 8;
+    S.last_bits = 8;
+    S.num_segs = 1;
+    S.sg = one_segment((uint32_t)n, (uint32_t)L.num_tiles);
+    S.pass_words = count_words(L.num_tiles);
+    int seg_passes, seg_last_bits;
+    if (head_split(tr, n, row_begin, num_rows, S.passes, &seg_passes, &seg_last_bits)) {
+        const int64_t ht = head_tiles(n);
+        S.passes = seg_passes;
+        S.last_bits = seg_last_bits;
+        S.num_segs = kTokenHeads;
+        S.sg.len = (uint32_t)(n / kTokenHeads);
+        S.sg.tiles = (uint32_t)ht;
+        S.sg.val_mul = kTokenHeads;  // entry pos of head h is lookup 16 pos + h
+        for (int h = 0; h < kTokenHeads; ++h) S.sg.base[h] = (uint32_t)(tr->p.off[h] - row_begin);
+        S.pass_words = (size_t)kTokenHeads * count_words(ht, kRadixWide);
+    }
     uint32_t* count_totals = (uint32_t*)(ws + L.count_totals);
-    const uint32_t total_words = (uint32_t)(pass_words * passes);
+    const uint32_t total_words = (uint32_t)(S.pass_words * S.passes);
     const uint32_t init_grid = std::max(1u, std::min(64u, (total_words + kBlock - 1) / kBlock));
     hipLaunchKernelGGL(scatter_init_kernel, dim3(init_grid), dim3(kBlock), 0, stream, status, counters, num_uniq,
                        count_totals, total_words);
     hipError_t err = hipGetLastError();
     if (err != hipSuccess || n == 0) return err;
     const int items = sort_items(n);
-    if (items == 8) err = run_sort<8>(L, ws, rows, tr, pad, n, row_begin, num_rows, passes, status, stream);
-    else if (items == 16) err = run_sort<16>(L, ws, rows, tr, pad, n, row_begin, num_rows, passes, status, stream);
-    else err = run_sort<24>(L, ws, rows, tr, pad, n, row_begin, num_rows, passes, status, stream);
+    if (items == 8) err = run_sort<8>(L, ws, rows, tr, pad, n, row_begin, num_rows, S, status, stream);
+    else if (items == 16) err = run_sort<16>(L, ws, rows, tr, pad, n, row_begin, num_rows, S, status, stream);
+    else err = run_sort<24>(L, ws, rows, tr, pad, n, row_begin, num_rows, S, status, stream);
     if (err != hipSuccess) return err;
 
     const uint32_t nn = (uint32_t)n;

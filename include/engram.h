@@ -269,7 +269,12 @@ int engram_scatter_add_plan_padded(const int64_t* ids, const int64_t* split_size
  * released layout only (ngram_size 3, 8 heads per order: n = batch * seq_len * 16
  * lookups, lookup (b * seq_len + t) * 16 + h); the plan, its outputs and the apply
  * that follows (with this n) are exactly those of engram_scatter_add_plan on the
- * hashed rows.
+ * hashed rows.  Every position has exactly one lookup per head, so when every
+ * head's range [offset, offset + vocab size) lies in [row_begin, row_begin +
+ * num_rows) and the ranges are disjoint and ascending in head order (the released
+ * module data: the bigram heads, then the trigram heads, one after another), the
+ * sort runs per head over the bits of the largest vocab size (three passes instead
+ * of four for the released table); the result is the same.
  *   tokens    device int64 [batch][seq_len]
  *   other arguments as for engram_scatter_add_plan; the workspace is
  *   engram_scatter_add_workspace(n, num_rows, dim) bytes

@@ -9,7 +9,8 @@ import pytest
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 sys.path.insert(0, ROOT)
-import bench  # noqa: E402
+import bench
+import hashed_gram_embedding_engram_amd as E  # noqa: E402
 
 # summary file -> kernel source it was measured on
 SUMMARIES = {
@@ -115,6 +116,25 @@ def test_sort_nominal_bytes():
     assert bench.sort_nominal_bytes(n, (1 << 24) - 1) == 68 * n   # the sentinel fits 24 bits
     assert bench.sort_nominal_bytes(n, 1 << 24) == 88 * n           # it needs a 25th
     assert bench.sort_nominal_bytes(n, 320_001_536, u, from_tokens=True) == 92 * n + 8 * u - 8 * n + n // 2
+    # from tokens with the released heads the sort runs per head in three passes: one 20-B pass less
+    p = bench.plan_passes(320_001_536, True, E.QWEN3_8_FLASH_NEXT_NGRAM_HEAD_VOCAB_SIZES,
+                          E.QWEN3_8_FLASH_NEXT_NGRAM_HEAD_OFFSETS)
+    assert p == 3
+    assert bench.sort_nominal_bytes(n, 320_001_536, u, True, p) == 72 * n + 8 * u - 8 * n + n // 2
+
+
+def test_plan_passes_split_rule():
+    """Per-head passes only when the head ranges are disjoint, ascending and inside the shard."""
+    mods = [60_000] * 16
+    offs = [60_000 * h for h in range(16)]
+    assert bench.plan_passes(960_000, False, mods, offs) == 3           # rows: the whole sort
+    assert bench.plan_passes(960_000, True, mods, offs) == 2            # 16-bit heads, 20-bit table
+    assert bench.plan_passes(960_000, True, mods, offs[::-1]) == 3      # descending ranges
+    assert bench.plan_passes(959_999, True, mods, offs) == 3            # last head past the shard
+    assert bench.plan_passes(1_700_000, True, [100_000] * 16, [100_000 * h for h in range(16)]) == 2  # 8 + 9 bits
+    # the sentinel 65,536 needs a 17th bit: three passes whole, two per head
+    assert bench.plan_passes(65_536, False, [4_096] * 16, [4_096 * h for h in range(16)]) == 3
+    assert bench.plan_passes(65_536, True, [4_096] * 16, [4_096 * h for h in range(16)]) == 2
 
 
 def test_route_cpu_baseline_runs_on_tiny_inputs():

@@ -3,7 +3,8 @@ bit-exact against the oracle's hash followed by the oracle's gather; the release
 head layout (3-gram, 8 heads per order) with a 160-wide bf16 table takes the
 one-kernel path, other layouts and fp32 tables the hash-then-gather path through
 rows_out.  The backward's plan from tokens (engram_scatter_add_plan_from_tokens):
-plan + apply against the oracle's scatter-add of the oracle's rows."""
+plan + apply against the oracle's scatter-add of the oracle's rows, for the whole
+sort and for the sort split by head."""
 import ctypes
 
 import numpy as np
@@ -12,7 +13,7 @@ import torch
 
 import hashed_gram_embedding_engram_amd as E
 import workloads as W
-from oracle import c_oracle
+from oracle import c_oracle, constants as C
 from tests.gpu_common import assert_close_to_fp64, full_oracle_spec, oracle_hash, product_spec_from, requires_gpu, to_host
 
 pytestmark = [pytest.mark.gpu, requires_gpu]
@@ -230,6 +231,91 @@ def test_plan_from_tokens_equals_plan_from_rows_long_context():
     assert u == ur_a.numel()
     assert torch.equal(ur_b[:u], ur_a)
     assert torch.equal(ug_b[:u].view(torch.int32), ug_a.view(torch.int32))
+
+
+# ---- The plan from tokens split by head.  When every head's row range lies in the
+# shard and the ranges are disjoint and ascending in head order, the sort runs per
+# head over the bits of the head's modulus, in fewer passes than num_rows needs.
+# The layouts below take it with two 8-bit passes (moduli below 2^16 in a 20-bit
+# table), with an 8-bit and a 9-bit pass (moduli below 2^17 in a 21-bit table), with
+# gaps between the ranges and a shard that starts before the first one, and not at
+# all (ranges in descending head order, or one head outside the shard).  Each must
+# equal the oracle, and the plan from engram_hash's rows (never split) bit for bit.
+
+def head_layout(base, gap=0, start=0, descending=False):
+    vocab = C.consecutive_primes_above(base, 16)
+    offsets, at = [0] * 16, start
+    for h in (range(15, -1, -1) if descending else range(16)):
+        offsets[h] = at
+        at += vocab[h] + gap
+    return {"ngram_size": 3, "heads_per_ngram": 8, "eos": 999, "fill": 0, "vocab_sizes": tuple(vocab),
+            "offsets": tuple(offsets), "num_rows": at}
+
+
+def check_split_plan(ids, ws, num_rows, row_begin=0, dim=8, seed=0, dense=False):
+    check_plan_from_tokens(ids, ws, num_rows, row_begin=row_begin, dim=dim, dense=dense, seed=seed)
+    spec = product_spec_from(ws)
+    tokens = torch.from_numpy(np.ascontiguousarray(ids, dtype=np.int64)).cuda()
+    n = ids.size * 16
+    dy = grads(n, seed + 1, dim)
+    ur_a, ug_a = E.engram_scatter_add(E.engram_hash(tokens, spec), dy, num_rows, row_begin)
+    ur_b = torch.empty(n, dtype=torch.int64, device="cuda")
+    nu_b = torch.empty((), dtype=torch.int64, device="cuda")
+    ug_b = torch.empty((n, dim), dtype=torch.float32, device="cuda")
+    wsb = E.engram_scatter_add_plan_from_tokens(tokens, spec, num_rows, dim, row_begin, uniq_rows=ur_b,
+                                                num_uniq=nu_b)
+    E.engram_scatter_add_apply(dy, n, num_rows, wsb, row_begin, uniq_grad=ug_b)
+    torch.cuda.synchronize()
+    u = int(nu_b.item())
+    assert u == ur_a.numel()
+    assert torch.equal(ur_b[:u], ur_a)
+    assert torch.equal(ug_b[:u].view(torch.int32), ug_a.view(torch.int32))
+
+
+SPLIT_SHAPES = [(1, 1), (1, 2), (2, 63), (3, 5000), (1, (1 << 16) + 3), (1, (1 << 17) + 5)]
+
+
+@pytest.mark.parametrize("shape", SPLIT_SHAPES)
+def test_split_plan_two_8_bit_passes(shape):
+    ws = head_layout(60_000)
+    check_split_plan(uniform_ids(shape, sum(shape) + 3, ws["eos"]), ws, ws["num_rows"], seed=sum(shape) % 13)
+
+
+@pytest.mark.parametrize("shape", SPLIT_SHAPES)
+def test_split_plan_8_and_9_bit_passes(shape):
+    ws = head_layout(100_000)
+    check_split_plan(uniform_ids(shape, sum(shape) + 5, ws["eos"]), ws, ws["num_rows"], seed=sum(shape) % 11)
+
+
+def test_split_plan_gaps_and_shard_start():
+    ws = head_layout(100_000, gap=777, start=12_345)
+    ids = uniform_ids((4, 20_000), 41, ws["eos"], p_eos=1 / 32)
+    check_split_plan(ids, ws, ws["num_rows"] - 12_000 + 500, row_begin=12_000, seed=3)
+
+
+def test_split_plan_dense():
+    ws = head_layout(60_000)
+    check_split_plan(uniform_ids((2, 30_000), 43, ws["eos"]), ws, ws["num_rows"], seed=4, dense=True)
+
+
+def test_split_plan_released_heads_on_long_rows():
+    """The released moduli (25 bits) on the full row range: three passes, the last of 9 bits."""
+    ids = uniform_ids((2, 70_000), 47, C.EOS_TOKEN_ID, p_eos=1 / 128, vocab=5000)
+    check_split_plan(ids, full_oracle_spec(), C.padded_rows(), seed=6)
+
+
+@pytest.mark.parametrize("case", ["descending", "head_outside"])
+def test_whole_sort_when_not_split(case):
+    if case == "descending":
+        ws = head_layout(60_000, descending=True)
+        num_rows = ws["num_rows"]
+    else:
+        ws = head_layout(60_000)
+        num_rows = ws["num_rows"] - 1  # the last head's last row is outside the shard
+    ids = uniform_ids((3, 9_000), 53, ws["eos"])
+    bad = check_plan_from_tokens(ids, ws, num_rows, dim=8, seed=7)  # status checked against the oracle's
+    if case == "descending":
+        assert bad < 0
 
 
 def test_plan_from_tokens_refuses_other_layouts():
