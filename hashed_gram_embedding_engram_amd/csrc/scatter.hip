@@ -109,7 +109,13 @@ size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 // sooner); large tiles suit large ones, where the plan runs beside the
 // gather: each digit run a tile writes is longer, so fewer lines are written
 // in part, and fewer blocks compete with the gather for wave slots.
-int sort_items(int64_t n) { return n <= ((int64_t)1 << 20) ? 8 : n >= ((int64_t)1 << 21) ? 24 : 16; }
+#ifndef ENGRAM_SORT_ITEMS_LARGE
+#define ENGRAM_SORT_ITEMS_LARGE 24  // keys per thread from 2^21 lookups (16 or 24)
+#endif
+static_assert(ENGRAM_SORT_ITEMS_LARGE == 16 || ENGRAM_SORT_ITEMS_LARGE == 24, "the plan's sort takes 16 or 24");
+int sort_items(int64_t n) {
+    return n <= ((int64_t)1 << 20) ? 8 : n >= ((int64_t)1 << 21) ? ENGRAM_SORT_ITEMS_LARGE : 16;
+}
 
 // Tiles per head of a sort split by head (0 when n is not 16 rows per position).
 int64_t head_tiles(int64_t n) {
