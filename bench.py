@@ -1380,6 +1380,7 @@ def summarize_profiles(name, raw):
         if "scatter_apply" in line["phase_gbps"]:
             alg["scatter_apply"] = comp["scatter_apply"] = line["roofline"]["algorithmic_bytes_per_launch"]
             # the full table's workloads hash with the released head layout
+            import hashed_gram_embedding_engram_amd as E
             released = cfg["table_rows"] == E.QWEN3_8_FLASH_NEXT_NGRAM_PADDED_ROWS
             passes = plan_passes(cfg["table_rows"], fused, E.QWEN3_8_FLASH_NEXT_NGRAM_HEAD_VOCAB_SIZES,
                                  E.QWEN3_8_FLASH_NEXT_NGRAM_HEAD_OFFSETS) if released else None
