@@ -297,8 +297,10 @@ __global__ __launch_bounds__(kBlock) void keys_kernel(const int64_t* __restrict_
 // lookup (lookup index 16 pos + h) becomes entry pos of segment h, with the
 // histogram of the digit-0 of row - offset[h].  The host has checked that
 // every head's range lies in the shard, so every lookup is in range.  Lane
-// l's item it is position base + 64 it + l; the three tokens it needs are
-// loaded directly (neighbouring lanes share them in cache).
+// l's item it is position base + 64 it + l: each lane loads its own tokens,
+// and the two before each position come from the lanes below it (lanes 0 and
+// 1 take them from the previous item's lanes 62 and 63, or, for the first
+// item, from the two positions before the wave's span).
 template <int ITEMS>
 __global__ __launch_bounds__(kBlock) void head_keys_kernel(TokenRows tr, int64_t row_begin, Segments sg,
                                                            uint32_t* __restrict__ keys, DigitCounts dc,
@@ -325,15 +327,27 @@ __global__ __launch_bounds__(kBlock) void head_keys_kernel(TokenRows tr, int64_t
             off = tr.p.off[j];
         }
     const bool trigram = h >= (uint32_t)(kTokenHeads / 2);
-    const uint32_t pos0 = tile * (uint32_t)(kBlock * ITEMS) + (uint32_t)w * (64 * ITEMS) + (uint32_t)lane;
+    const uint32_t wbase = tile * (uint32_t)(kBlock * ITEMS) + (uint32_t)w * (64 * ITEMS);
+    const uint32_t pos0 = wbase + (uint32_t)lane;
     uint32_t t = pos0 % tr.seq_len;  // item 0's column; advances by 64 an item
     uint32_t my_valid = 0;
     uint32_t* const seg_keys = keys + (size_t)h * npos;
+    int64_t tok[ITEMS];
+#pragma unroll
+    for (int it = 0; it < ITEMS; ++it) tok[it] = tr.tokens[min(pos0 + 64u * (uint32_t)it, npos - 1)];
+    // the two positions before the span (only read where the column says they
+    // belong to the same batch row)
+    int64_t last1 = tr.tokens[min(wbase >= 1 ? wbase - 1 : 0u, npos - 1)];
+    int64_t last2 = tr.tokens[min(wbase >= 2 ? wbase - 2 : 0u, npos - 1)];
 #pragma unroll
     for (int it = 0; it < ITEMS; ++it) {
         const uint32_t pos = pos0 + 64u * (uint32_t)it;
-        const uint32_t q = min(pos, npos - 1);
-        const int64_t x0 = tr.tokens[q], x1 = tr.tokens[q >= 1 ? q - 1 : 0u], x2 = tr.tokens[q >= 2 ? q - 2 : 0u];
+        const int64_t x0 = tok[it];
+        const int64_t up1 = __shfl_up(x0, 1, 64), up2 = __shfl_up(x0, 2, 64);
+        const int64_t x1 = lane >= 1 ? up1 : last1;
+        const int64_t x2 = lane >= 2 ? up2 : lane == 1 ? last1 : last2;
+        last1 = __shfl(x0, 63, 64);  // for the next item: the positions before its lanes 0 and 1
+        last2 = __shfl(x0, 62, 64);
         const bool valid1 = t >= 1 && x1 != tr.p.eos;
         const bool valid2 = valid1 && t >= 2 && x2 != tr.p.eos;
         const int64_t ctx1 = valid1 ? x1 : tr.p.fill, ctx2 = valid2 ? x2 : tr.p.fill;
