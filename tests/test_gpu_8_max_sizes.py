@@ -1,8 +1,9 @@
 """The largest lookup count the scatter-add accepts (n = 2^31 - 1) and the same
 count through the gather, with 16-byte rows (8 bf16 values) so that everything
-fits in HBM (about 92 GB for the scatter-add, 52 GB for the gather); and
+fits in HBM (about 92 GB for the scatter-add, 52 GB for the gather);
 gathers whose work passes what one launch can hold (2^32 work-items), up to
-172 GB of output.
+172 GB of output; and the plan from tokens at its largest batch, where its sort
+runs per head.
 
 The oracle cannot run at this size, so both checks use properties that hold at
 any size.  Lookup i reads row (i * 7919) mod R with R = 1,000,003 (prime, and
@@ -97,4 +98,36 @@ def test_gather_past_one_launch_of_work_items(dim, n):
     torch.cuda.synchronize()
     gather_matches_index_select(table, rows, out)
     del rows, out, table
+    torch.cuda.empty_cache()
+
+
+def test_plan_from_tokens_split_at_max_lookups():
+    """The largest token batch the plan from tokens accepts (2^27 - 1 positions, so
+    n = 2^31 - 16 lookups) with the released heads over the full row range, where the
+    sort runs per head with a last pass of 9 bits: its dense sums equal those of the
+    whole sort from engram_hash's rows bit for bit.  Every gradient value is 1, so each
+    row's sum is its exact hit count, and the counts add up to n."""
+    dev = torch.device("cuda")
+    torch.cuda.empty_cache()
+    positions = (1 << 27) - 1
+    g = torch.Generator(device=dev)
+    g.manual_seed(37)
+    tokens = torch.randint(0, 248_320, (1, positions), generator=g, device=dev, dtype=torch.int64)
+    n = positions * 16
+    spec = E.qwen3_8_flash_next_spec()
+    rows_total = E.QWEN3_8_FLASH_NEXT_NGRAM_PADDED_ROWS
+    dy = torch.ones((n, DIM), dtype=torch.bfloat16, device=dev)
+    whole = torch.zeros((rows_total, DIM), dtype=torch.float32, device=dev)
+    rows = E.engram_hash(tokens, spec).view(-1)
+    E.engram_scatter_add(rows, dy, rows_total, grad_dense=whole)   # validates: raises on any out-of-range row
+    torch.cuda.synchronize()
+    del rows
+    torch.cuda.empty_cache()
+    split = torch.zeros_like(whole)
+    ws = E.engram_scatter_add_plan_from_tokens(tokens, spec, rows_total, DIM)
+    E.engram_scatter_add_apply(dy, n, rows_total, ws, grad_dense=split)
+    torch.cuda.synchronize()
+    assert torch.equal(split, whole)
+    assert int(split[:, 0].double().sum().item()) == n
+    del tokens, dy, whole, split, ws
     torch.cuda.empty_cache()
