@@ -330,9 +330,13 @@ __global__ __launch_bounds__(kBlock) void downsweep_kernel(const uint32_t* __res
     __shared__ uint32_t s_vals[kBlock * ITEMS];
     // per wave and digit: the wave's count, then where the wave's keys of the
     // digit start inside the tile (row 0: where the tile's digit run starts);
-    // row 0 finally holds, per digit, where the tile's digit run goes
-    // globally less where it starts in the tile
-    __shared__ uint32_t s_wave_cnt[kBlock / 64][R];
+    // both below the tile size, so 16 bits each (a 9-bit pass of 24 keys per
+    // thread then fits three blocks per compute unit).  Once the tile is
+    // ordered, the same words hold, per digit, where the tile's digit run goes
+    // globally less where it starts in the tile (s_run_off, 32 bits).
+    static_assert(kBlock * ITEMS <= 0xFFFF, "tile offsets fit 16 bits");
+    __shared__ uint16_t s_wave_cnt[kBlock / 64][R];
+    uint32_t* const s_run_off = reinterpret_cast<uint32_t*>(&s_wave_cnt[0][0]);  // R words of the 2R spare ones
     uint32_t* const s_tmp = s_keys;  // the scans' scratch: s_keys is written only after them
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const uint32_t seg = blockIdx.x / sg.tiles, tile = blockIdx.x - seg * sg.tiles;
@@ -375,7 +379,7 @@ __global__ __launch_bounds__(kBlock) void downsweep_kernel(const uint32_t* __res
         uint32_t cnt = 0;
         if (live) cnt = s_wave_cnt[w][d];
         rank[it] = cnt + before;
-        if (live && before == 0) s_wave_cnt[w][d] = cnt + (uint32_t)__popcll(peers);
+        if (live && before == 0) s_wave_cnt[w][d] = (uint16_t)(cnt + (uint32_t)__popcll(peers));
     }
     __syncthreads();
     // Per owned digit: where each wave's keys of it start inside the tile, and
@@ -390,7 +394,7 @@ __global__ __launch_bounds__(kBlock) void downsweep_kernel(const uint32_t* __res
 #pragma unroll
             for (int k = 0; k < kBlock / 64; ++k) {
                 const uint32_t c = s_wave_cnt[k][d];
-                s_wave_cnt[k][d] = sum;
+                s_wave_cnt[k][d] = (uint16_t)sum;
                 sum += c;
             }
             tile_cnt[q] = sum;
@@ -404,7 +408,7 @@ __global__ __launch_bounds__(kBlock) void downsweep_kernel(const uint32_t* __res
         for (int q = 0; q < DPT; ++q) {
             const int d = tid * DPT + q;
 #pragma unroll
-            for (int k = 0; k < kBlock / 64; ++k) s_wave_cnt[k][d] += tile_run;
+            for (int k = 0; k < kBlock / 64; ++k) s_wave_cnt[k][d] = (uint16_t)(s_wave_cnt[k][d] + tile_run);
             global_start[q] = seg_run + digit_before[q] - tile_run;
             tile_run += tile_cnt[q];
             seg_run += digit_total[q];
@@ -423,13 +427,13 @@ __global__ __launch_bounds__(kBlock) void downsweep_kernel(const uint32_t* __res
     }
     __syncthreads();
 #pragma unroll
-    for (int q = 0; q < DPT; ++q) s_wave_cnt[0][tid * DPT + q] = global_start[q];  // the wave offsets are no longer read
+    for (int q = 0; q < DPT; ++q) s_run_off[tid * DPT + q] = global_start[q];  // the wave offsets are no longer read
     __syncthreads();
     const uint32_t count = min((uint32_t)(kBlock * ITEMS), n - tile_base);
     for (uint32_t j = tid; j < count; j += kBlock) {
         const uint32_t k = s_keys[j];
         const uint32_t d = ((k - sb) >> shift) & (uint32_t)(R - 1);
-        const uint32_t g = s_wave_cnt[0][d] + j;  // unsigned wrap-around cancels
+        const uint32_t g = s_run_off[d] + j;  // unsigned wrap-around cancels
         if (g < n) {  // always true for a consistent histogram; keeps every store in its segment
             if (GROUPED) {
                 const uint32_t v = min(s_vals[j], n - 1);
