@@ -241,6 +241,25 @@ __device__ __forceinline__ void sum_tile_counts(const DigitCounts& dc, uint32_t 
     *before = b;
 }
 
+// The counts of one digit straight from the tile histograms of a short
+// segment (at most kDirectTiles tiles, so no chunk or group totals are
+// needed, nor zeroed): its total over the segment's tiles and its keys in the
+// tiles before `tile`.
+constexpr uint32_t kDirectTiles = 64;
+template <int R>
+__device__ __forceinline__ void direct_tile_counts(const DigitCounts& dc, uint32_t tiles, uint32_t tile, int d,
+                                                   uint32_t* total, uint32_t* before) {
+    uint32_t t = 0, b = 0;
+#pragma unroll 8
+    for (uint32_t k = 0; k < tiles; ++k) {
+        const uint32_t x = dc.hist[(size_t)k * R + d];
+        t += x;
+        b += k < tile ? x : 0u;
+    }
+    *total = t;
+    *before = b;
+}
+
 // Tile histograms of the BITS-bit digit at `shift` (passes after the first).
 // Thread tid owns digits tid * DPT .. tid * DPT + DPT - 1.
 template <int ITEMS = kItems, int BITS = 8>
@@ -315,10 +334,11 @@ struct GroupedOut {
 
 // One stable scatter pass of the LSD radix sort over the BITS-bit digit at
 // `shift`.  vals_in == nullptr means the value of an entry is its index (see
-// Segments).  SMALL as for load_tile_counts.  With GROUPED (one unsegmented
+// Segments).  SMALL as for load_tile_counts; DIRECT takes the counts from the
+// tile histograms alone (direct_tile_counts).  With GROUPED (one unsegmented
 // 8-bit pass) the pass writes `go`'s outputs instead of keys_out / vals_out.
 // Thread tid owns digits tid * DPT .. tid * DPT + DPT - 1.
-template <bool SMALL, int ITEMS = kItems, bool GROUPED = false, int BITS = 8>
+template <bool SMALL, int ITEMS = kItems, bool GROUPED = false, int BITS = 8, bool DIRECT = false>
 __global__ __launch_bounds__(kBlock) void downsweep_kernel(const uint32_t* __restrict__ keys_in,
                                                            const uint32_t* __restrict__ vals_in,
                                                            uint32_t* __restrict__ keys_out,
@@ -350,7 +370,7 @@ __global__ __launch_bounds__(kBlock) void downsweep_kernel(const uint32_t* __res
     const uint32_t base = tile_base + (uint32_t)w * (64 * ITEMS);
     TileCounts tc[DPT];
 #pragma unroll
-    for (int q = 0; q < DPT; ++q) load_tile_counts<SMALL, R>(dc, tile, tid * DPT + q, tc[q]);
+    for (int q = 0; q < DPT; ++q) load_tile_counts<SMALL && !DIRECT, R>(dc, tile, tid * DPT + q, tc[q]);
     uint32_t key[ITEMS], val[ITEMS], rank[ITEMS];
 #pragma unroll
     for (int it = 0; it < ITEMS; ++it) {
@@ -362,7 +382,10 @@ __global__ __launch_bounds__(kBlock) void downsweep_kernel(const uint32_t* __res
     uint32_t digit_total[DPT], digit_before[DPT];
 #pragma unroll
     for (int q = 0; q < DPT; ++q) {
-        sum_tile_counts<SMALL, R>(dc, tile, tid * DPT + q, tc[q], &digit_total[q], &digit_before[q]);
+        if (DIRECT)
+            direct_tile_counts<R>(dc, sg.tiles, tile, tid * DPT + q, &digit_total[q], &digit_before[q]);
+        else
+            sum_tile_counts<SMALL, R>(dc, tile, tid * DPT + q, tc[q], &digit_total[q], &digit_before[q]);
         // Sum here, not next to the use: the loaded counts then die before the
         // ranking needs its registers.
         asm volatile("" : "+v"(digit_total[q]), "+v"(digit_before[q]));

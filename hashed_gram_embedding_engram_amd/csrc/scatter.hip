@@ -300,11 +300,26 @@ __global__ __launch_bounds__(kBlock) void keys_kernel(const int64_t* __restrict_
 // l's item it is position base + 64 it + l: each lane loads its own tokens,
 // and the two before each position come from the lanes below it (lanes 0 and
 // 1 take them from the previous item's lanes 62 and 63, or, for the first
-// item, from the two positions before the wave's span).
-template <int ITEMS>
+// item, from the two positions before the wave's span).  With DIRECT (short
+// segments, whose first pass takes its counts from the tile histograms alone)
+// the kernel also does what the plan's init kernel would: block 0 sets the
+// status word and the in-range count (every lookup), and the grid clears the
+// later passes' chunk and group totals (`zero_words`), which are first added
+// to after this kernel.
+template <int ITEMS, bool DIRECT>
 __global__ __launch_bounds__(kBlock) void head_keys_kernel(TokenRows tr, int64_t row_begin, Segments sg,
                                                            uint32_t* __restrict__ keys, DigitCounts dc,
-                                                           uint32_t* __restrict__ counters) {
+                                                           uint32_t* __restrict__ counters,
+                                                           int64_t* __restrict__ status,
+                                                           uint32_t* __restrict__ zero_words, uint32_t zero_count) {
+    if (DIRECT) {
+        if (blockIdx.x == 0 && threadIdx.x == 0) {
+            if (status) *status = -1;
+            counters[0] = sg.len * (uint32_t)kTokenHeads;
+        }
+        for (uint32_t i = blockIdx.x * kBlock + threadIdx.x; i < zero_count; i += gridDim.x * kBlock)
+            zero_words[i] = 0;
+    }
     __shared__ uint32_t s_cnt[kBlock / 64][kRadix];
     __shared__ uint32_t s_valid;
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
@@ -370,8 +385,12 @@ __global__ __launch_bounds__(kBlock) void head_keys_kernel(TokenRows tr, int64_t
     uint32_t c = 0;
 #pragma unroll
     for (int k = 0; k < kBlock / 64; ++k) c += s_cnt[k][tid];
-    publish_tile_counts(dc, tile, tid, c);
-    if (tid == 0 && s_valid) atomicAdd(&counters[0], s_valid);
+    if (DIRECT) {
+        dc.hist[(size_t)tile * kRadix + tid] = c;
+    } else {
+        publish_tile_counts(dc, tile, tid, c);
+        if (tid == 0 && s_valid) atomicAdd(&counters[0], s_valid);
+    }
 }
 
 // Step 3a: per slice, the number of runs that start in it, the index of the
@@ -1050,6 +1069,7 @@ struct SortShape {
     uint32_t num_segs;
     int passes, last_bits;
     size_t pass_words;  // chunk and group totals of one pass, all segments
+    bool direct;        // split by head into short segments: no init kernel, first pass from tile counts
 };
 
 // One digit pass: the histogram (unless the keys kernel made it), then the scatter.
@@ -1057,6 +1077,7 @@ template <int ITEMS, int BITS>
 hipError_t sort_pass(const SortShape& S, char* ws, const Layout& L, uint32_t* totals, bool first, int shift,
                      const uint32_t* k_cur, const uint32_t* v_cur, uint32_t* k_nxt, uint32_t* v_nxt,
                      hipStream_t stream) {
+    static_assert(BITS == 8 || BITS == 9, "8- or 9-bit digits");
     constexpr int R = 1 << BITS;
     Segments sg = S.sg;
     sg.hist_words = sg.tiles * (uint32_t)R;
@@ -1069,7 +1090,10 @@ hipError_t sort_pass(const SortShape& S, char* ws, const Layout& L, uint32_t* to
         if (err != hipSuccess) return err;
     }
     const uint32_t* v_in = first ? nullptr : v_cur;
-    if (small_counts(dc))
+    if (BITS == 8 && first && S.direct)
+        hipLaunchKernelGGL((downsweep_kernel<false, ITEMS, false, 8, true>), dim3(grid), dim3(kBlock), 0, stream,
+                           k_cur, v_in, k_nxt, v_nxt, shift, dc, sg, GroupedOut{});
+    else if (small_counts(dc))
         hipLaunchKernelGGL((downsweep_kernel<true, ITEMS, false, BITS>), dim3(grid), dim3(kBlock), 0, stream, k_cur,
                            v_in, k_nxt, v_nxt, shift, dc, sg, GroupedOut{});
     else
@@ -1099,8 +1123,15 @@ hipError_t run_sort(const Layout& L, char* ws, const int64_t* rows, const TokenR
         Segments sg = S.sg;
         sg.hist_words = sg.tiles * (uint32_t)kRadix;
         sg.total_words = (uint32_t)count_words(sg.tiles);
-        hipLaunchKernelGGL(head_keys_kernel<ITEMS>, dim3(sg.tiles * S.num_segs), dim3(kBlock), 0, stream, *tr,
-                           row_begin, sg, k_cur, make_digit_counts(ws + L.hist, count_totals, sg.tiles), counters);
+        const DigitCounts dc0 = make_digit_counts(ws + L.hist, count_totals, sg.tiles);
+        const dim3 grid(sg.tiles * S.num_segs);
+        if (S.direct)
+            hipLaunchKernelGGL((head_keys_kernel<ITEMS, true>), grid, dim3(kBlock), 0, stream, *tr, row_begin, sg,
+                               k_cur, dc0, counters, status, count_totals + S.pass_words,
+                               (uint32_t)(S.pass_words * (size_t)(passes - 1)));
+        else
+            hipLaunchKernelGGL((head_keys_kernel<ITEMS, false>), grid, dim3(kBlock), 0, stream, *tr, row_begin, sg,
+                               k_cur, dc0, counters, status, (uint32_t*)nullptr, 0u);
     } else if (tr) {
         hipLaunchKernelGGL((keys_kernel<ITEMS, true>), dim3(tiles), dim3(kBlock), 0, stream, nullptr, *tr, nn,
                            row_begin, (uint64_t)num_rows, k_cur, make_digit_counts(ws + L.hist, count_totals, tiles),
@@ -1174,6 +1205,7 @@ hipError_t scatter_plan(const int64_t* rows, const TokenRows* tr, Padding pad, i
     S.num_segs = 1;
     S.sg = one_segment((uint32_t)n, (uint32_t)L.num_tiles);
     S.pass_words = count_words(L.num_tiles);
+    S.direct = false;
     int seg_passes, seg_last_bits;
     if (head_split(tr, n, row_begin, num_rows, S.passes, &seg_passes, &seg_last_bits)) {
         const int64_t ht = head_tiles(n);
@@ -1185,13 +1217,17 @@ hipError_t scatter_plan(const int64_t* rows, const TokenRows* tr, Padding pad, i
         S.sg.val_mul = kTokenHeads;  // entry pos of head h is lookup 16 pos + h
         for (int h = 0; h < kTokenHeads; ++h) S.sg.base[h] = (uint32_t)(tr->p.off[h] - row_begin);
         S.pass_words = (size_t)kTokenHeads * count_words(ht, kRadixWide);
+        S.direct = ht <= (int64_t)kDirectTiles;
     }
     uint32_t* count_totals = (uint32_t*)(ws + L.count_totals);
     const uint32_t total_words = (uint32_t)(S.pass_words * S.passes);
-    const uint32_t init_grid = std::max(1u, std::min(64u, (total_words + kBlock - 1) / kBlock));
-    hipLaunchKernelGGL(scatter_init_kernel, dim3(init_grid), dim3(kBlock), 0, stream, status, counters, num_uniq,
-                       count_totals, total_words);
-    hipError_t err = hipGetLastError();
+    hipError_t err = hipSuccess;
+    if (!S.direct) {  // the direct form's keys kernel does this itself
+        const uint32_t init_grid = std::max(1u, std::min(64u, (total_words + kBlock - 1) / kBlock));
+        hipLaunchKernelGGL(scatter_init_kernel, dim3(init_grid), dim3(kBlock), 0, stream, status, counters, num_uniq,
+                           count_totals, total_words);
+        err = hipGetLastError();
+    }
     if (err != hipSuccess || n == 0) return err;
     const int items = sort_items(n);
     if (items == 8) err = run_sort<8>(L, ws, rows, tr, pad, n, row_begin, num_rows, S, status, stream);

@@ -60,3 +60,16 @@ def assert_close_to_fp64(got, ref, what):
         i = np.argwhere(bad)[0]
         raise AssertionError("%s: %d elements out of tolerance; first at %s: got %r ref %r" %
                              (what, int(bad.sum()), tuple(i), got[tuple(i)], ref[tuple(i)]))
+
+
+def head_layout(base, gap=0, start=0, descending=False):
+    """A 3-gram, 8-heads-per-order layout of 16 consecutive primes above `base`,
+    the heads' ranges one after another from `start` (with `gap` rows between
+    them), in head order or, with descending, in reverse head order."""
+    vocab = C.consecutive_primes_above(base, 16)
+    offsets, at = [0] * 16, start
+    for h in (range(15, -1, -1) if descending else range(16)):
+        offsets[h] = at
+        at += vocab[h] + gap
+    return {"ngram_size": 3, "heads_per_ngram": 8, "eos": 999, "fill": 0, "vocab_sizes": tuple(vocab),
+            "offsets": tuple(offsets), "num_rows": at}

@@ -14,7 +14,8 @@ import torch
 import hashed_gram_embedding_engram_amd as E
 import workloads as W
 from oracle import c_oracle, constants as C
-from tests.gpu_common import assert_close_to_fp64, full_oracle_spec, oracle_hash, product_spec_from, requires_gpu, to_host
+from tests.gpu_common import (assert_close_to_fp64, full_oracle_spec, head_layout, oracle_hash, product_spec_from,
+                               requires_gpu, to_host)
 
 pytestmark = [pytest.mark.gpu, requires_gpu]
 
@@ -241,16 +242,6 @@ def test_plan_from_tokens_equals_plan_from_rows_long_context():
 # gaps between the ranges and a shard that starts before the first one, and not at
 # all (ranges in descending head order, or one head outside the shard).  Each must
 # equal the oracle, and the plan from engram_hash's rows (never split) bit for bit.
-
-def head_layout(base, gap=0, start=0, descending=False):
-    vocab = C.consecutive_primes_above(base, 16)
-    offsets, at = [0] * 16, start
-    for h in (range(15, -1, -1) if descending else range(16)):
-        offsets[h] = at
-        at += vocab[h] + gap
-    return {"ngram_size": 3, "heads_per_ngram": 8, "eos": 999, "fill": 0, "vocab_sizes": tuple(vocab),
-            "offsets": tuple(offsets), "num_rows": at}
-
 
 def check_split_plan(ids, ws, num_rows, row_begin=0, dim=8, seed=0, dense=False):
     check_plan_from_tokens(ids, ws, num_rows, row_begin=row_begin, dim=dim, dense=dense, seed=seed)

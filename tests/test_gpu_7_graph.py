@@ -6,7 +6,8 @@ replay must equal the eager calls bit for bit.
 The graph holds the step in both forms: hash and gather on the capture
 stream with the backward plan on a forked stream joined before the apply; and
 as the benchmark runs it, the fused hash-and-gather forward on the capture
-stream while the forked stream plans from the same tokens (no rows array).  Each
+stream while the forked stream plans from the same tokens (no rows array), also
+with a head layout where that plan sorts per head.  Each
 replay gets fresh inputs copied into the captured buffers and poisoned
 outputs, with eager calls and synchronisations between replays."""
 import numpy as np
@@ -15,15 +16,17 @@ import torch
 
 import hashed_gram_embedding_engram_amd as E
 import workloads as W
-from tests.gpu_common import product_spec_from, requires_gpu
+from tests.gpu_common import head_layout, product_spec_from, requires_gpu
 
 pytestmark = [pytest.mark.gpu, requires_gpu]
 
 
-@pytest.mark.parametrize("fused", [False, True])
-def test_step_graph_replays_equal_eager(fused):
+@pytest.mark.parametrize("fused,split", [(False, False), (True, False), (True, True)])
+def test_step_graph_replays_equal_eager(fused, split):
+    """split: a head layout (16-bit heads in a 20-bit table) where the plan from
+    tokens sorts per head and its keys kernel also does the plan's resets."""
     dev = torch.device("cuda")
-    ws = W.sft_spec()
+    ws = head_layout(60_000) if split else W.sft_spec()
     R, D = ws["num_rows"], 160
     table = torch.empty((R, D), dtype=torch.bfloat16, device=dev)
     W.fill_normal_(table, seed=5)
