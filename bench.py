@@ -1160,7 +1160,10 @@ def add_ceiling_fracs(result, ceilings):
 LOOKUP_PHASES = {
     "hash": ("hash.hip", [r"\bhash_kernel"]),
     "gather": ("gather.hip", [r"\bgather_rows_kernel"]),
-    "scatter_plan": ("scatter.hip", [r"\bscatter_init_kernel", r"\bkeys_kernel", r"\bhead_keys_kernel", r"\bupsweep_kernel",
+    # a plan starts with its init kernel, or, split by head into short
+    # segments, with the keys kernel that does the init's work itself
+    "scatter_plan": ("scatter.hip", [r"\bscatter_init_kernel|\bhead_keys_kernel<\d+, true>", r"\bkeys_kernel",
+                                     r"\bhead_keys_kernel", r"\bupsweep_kernel",
                                      r"\bdownsweep_kernel", r"\brun_count_kernel", r"\bblock_scan_kernel",
                                      r"\buniq_rows_kernel"]),
     "scatter_apply": ("scatter.hip", [r"\bsegment_reduce_kernel", r"\bcarry_fixup_kernel", r"\blong_run_kernel"]),
@@ -1248,10 +1251,11 @@ def profile_commands(name):
     run = "-- python3 $REPO/bench.py --workload %s %s" % (name, PROFILE_FLAGS)
     pats = []
     for _, ks in PROFILED[name].values():
-        for k in ks:
-            k = k.replace(r"\b", "").split("<")[0]
-            if k not in pats:
-                pats.append(k)
+        for alt in ks:
+            for k in alt.split("|"):
+                k = k.replace(r"\b", "").split("<")[0]
+                if k not in pats:
+                    pats.append(k)
     regex = "|".join(pats) + "|copyBuffer"
     out = "$REPO/gpurun_out/prof/%s" % name
     return {
