@@ -278,6 +278,15 @@ def test_split_plan_8_and_9_bit_passes(shape):
     check_split_plan(uniform_ids(shape, sum(shape) + 5, ws["eos"]), ws, ws["num_rows"], seed=sum(shape) % 11)
 
 
+@pytest.mark.parametrize("fill", [-1, INT64_MAX, INT64_MIN])
+def test_split_plan_fill_values_and_eos_runs(fill):
+    """Missing context takes the fill value, and EOS runs (one token in three) reset
+    the context often: the per-head sort must still see exactly the oracle's rows."""
+    ws = dict(head_layout(100_000), fill=fill)
+    ids = uniform_ids((5, 777), 59, ws["eos"], p_eos=1 / 3)
+    check_plan_from_tokens(ids, ws, ws["num_rows"], fill=fill, dim=8, seed=9)
+
+
 def test_split_plan_gaps_and_shard_start():
     ws = head_layout(100_000, gap=777, start=12_345)
     ids = uniform_ids((4, 20_000), 41, ws["eos"], p_eos=1 / 32)
