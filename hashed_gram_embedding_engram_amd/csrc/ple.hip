@@ -424,11 +424,26 @@ __global__ __launch_bounds__(kPleBlock) void short_conv_bwd_d3_kernel(
                 ((Q*)dhalop)[(b * HIST + i) * quads + q] = pack4<BF16>(acc);
             }
         }
+        // Each step's inputs are loaded one step ahead, so two steps of loads
+        // are in flight; past the tile's last step the current one is loaded
+        // again (in bounds, unused).
+        Q xn[P], gn[P];
+#pragma unroll
+        for (int j = 0; j < P; ++j) {
+            xn[j] = *xsrc(t0 + j);
+            gn[j] = *gsrc(t0 + HIST + j);
+        }
         for (int64_t t = t0; t < t1; t += P) {
 #pragma unroll
             for (int j = 0; j < P; ++j) {
-                xw[HIST + j] = *xsrc(t + j);
-                gw[HIST + j] = *gsrc(t + HIST + j);
+                xw[HIST + j] = xn[j];
+                gw[HIST + j] = gn[j];
+            }
+            const int64_t tn = t + P < t1 ? t + P : t;
+#pragma unroll
+            for (int j = 0; j < P; ++j) {
+                xn[j] = *xsrc(tn + j);
+                gn[j] = *gsrc(tn + HIST + j);
             }
             step(t, xw, gw);
 #pragma unroll
@@ -446,11 +461,23 @@ __global__ __launch_bounds__(kPleBlock) void short_conv_bwd_d3_kernel(
             xw[P + i] = *xsrc(t - HIST + P + i);
             gw[P + i] = *gsrc(t + P + i);
         }
+        Q xn[P], gn[P];  // one step ahead, as in the walk up
+#pragma unroll
+        for (int j = 0; j < P; ++j) {
+            xn[j] = *xsrc(t - HIST + j);
+            gn[j] = *gsrc(t + j);
+        }
         for (; t >= t0; t -= P) {
 #pragma unroll
             for (int j = 0; j < P; ++j) {
-                xw[j] = *xsrc(t - HIST + j);
-                gw[j] = *gsrc(t + j);
+                xw[j] = xn[j];
+                gw[j] = gn[j];
+            }
+            const int64_t tn = t - P >= t0 ? t - P : t;
+#pragma unroll
+            for (int j = 0; j < P; ++j) {
+                xn[j] = *xsrc(tn - HIST + j);
+                gn[j] = *gsrc(tn + j);
             }
             step(t, xw, gw);
 #pragma unroll
