@@ -287,6 +287,20 @@ def test_split_plan_fill_values_and_eos_runs(fill):
     check_plan_from_tokens(ids, ws, ws["num_rows"], fill=fill, dim=8, seed=9)
 
 
+def test_split_plan_one_pass():
+    """Heads below 256 rows in a 12-bit table: the per-head sort is one 8-bit pass."""
+    ws = head_layout(100)
+    check_split_plan(uniform_ids((3, 2000), 61, ws["eos"]), ws, ws["num_rows"], seed=10)
+
+
+def test_split_plan_long_segments():
+    """400,000 positions: 66 sort tiles per head, past the 64 a first pass can count
+    from the tile histograms alone, so the plan clears its counts in a kernel of its
+    own and the first pass reads chunk and group totals (8- and 9-bit passes)."""
+    ws = head_layout(100_000)
+    check_split_plan(uniform_ids((1, 400_000), 67, ws["eos"], p_eos=1 / 500), ws, ws["num_rows"], seed=11)
+
+
 def test_split_plan_gaps_and_shard_start():
     ws = head_layout(100_000, gap=777, start=12_345)
     ids = uniform_ids((4, 20_000), 41, ws["eos"], p_eos=1 / 32)
