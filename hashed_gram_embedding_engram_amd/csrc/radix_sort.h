@@ -127,7 +127,8 @@ inline DigitCounts make_digit_counts(void* hist, uint32_t* totals, int64_t num_t
                        (uint32_t)c.num_groups, c.chunk_shift, c.group_shift};
 }
 
-// A segmented sort: `count` segments of `len` keys each, segment s holding
+// A segmented sort: segments of `len` keys each (as many as the grid holds,
+// `tiles` blocks per segment), segment s holding
 // entries [s * len, (s + 1) * len) of every key and value array and sorted
 // in place, so no key leaves its segment.  Segment s owns grid blocks
 // [s * tiles, (s + 1) * tiles) and its own digit counts, `hist_words` and
@@ -356,7 +357,7 @@ __global__ __launch_bounds__(kBlock) void downsweep_kernel(const uint32_t* __res
     // globally less where it starts in the tile (s_run_off, 32 bits).
     static_assert(kBlock * ITEMS <= 0xFFFF, "tile offsets fit 16 bits");
     __shared__ uint16_t s_wave_cnt[kBlock / 64][R];
-    uint32_t* const s_run_off = reinterpret_cast<uint32_t*>(&s_wave_cnt[0][0]);  // R words of the 2R spare ones
+    uint32_t* const s_run_off = reinterpret_cast<uint32_t*>(&s_wave_cnt[0][0]);  // R of the array's 2R words
     uint32_t* const s_tmp = s_keys;  // the scans' scratch: s_keys is written only after them
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const uint32_t seg = blockIdx.x / sg.tiles, tile = blockIdx.x - seg * sg.tiles;
