@@ -226,25 +226,49 @@ int engram_scatter_add_plan_padded(const int64_t* ids, const int64_t* split_size
                                                             dim, uniq_rows, num_uniq, workspace, status, stream));
 }
 
-int engram_scatter_add_plan_from_tokens(const int64_t* tokens, int64_t batch, int64_t seq_len,
-                                        const engram_hash_spec* spec, int64_t row_begin, int64_t num_rows, int32_t dim,
-                                        int64_t* uniq_rows, int64_t* num_uniq, void* workspace,
-                                        size_t workspace_bytes, int64_t* status, hipStream_t stream) {
-    if (batch < 0 || seq_len < 0) return ENGRAM_EINVAL;
+namespace {
+
+static int plan_from_tokens_common(const int64_t* tokens, int64_t batch, int64_t seq_len, int64_t seq_begin,
+                            int64_t seq_end, const engram_hash_spec* spec, int64_t row_begin, int64_t num_rows,
+                            int32_t dim, int64_t* uniq_rows, int64_t* num_uniq, void* workspace,
+                            size_t workspace_bytes, int64_t* status, hipStream_t stream) {
+    if (batch < 0 || seq_len < 0 || seq_begin < 0 || seq_end < seq_begin || seq_end > seq_len) return ENGRAM_EINVAL;
+    if (seq_len >= ((int64_t)1 << 32)) return ENGRAM_EINVAL;
     engram::HashParams p;
     int rc = build_params(spec, &p);
     if (rc != ENGRAM_OK) return rc;
     if (p.ngram_size != 3 || p.heads_per_ngram != 8) return ENGRAM_EINVAL;  // 16 rows per position only
-    if (seq_len > 0 && batch > (((int64_t)1 << 31) - 1) / 16 / seq_len) return ENGRAM_EINVAL;
-    const int64_t n = batch * seq_len * 16;
+    const int64_t width = seq_end - seq_begin;
+    if (width > 0 && batch > (((int64_t)1 << 31) - 1) / 16 / width) return ENGRAM_EINVAL;
+    const int64_t n = batch * width * 16;
     int eb;
     if ((rc = scatter_check_common(ENGRAM_F32, dim, n, row_begin, num_rows, &eb)) != ENGRAM_OK) return rc;
     if (n > 0 && !tokens) return ENGRAM_EINVAL;
     if (!aligned(tokens, 8) || !aligned(uniq_rows, 8) || !aligned(num_uniq, 8) || !aligned(status, 8))
         return ENGRAM_EINVAL;
     if ((rc = workspace_check(workspace, workspace_bytes, n, num_rows, dim)) != ENGRAM_OK) return rc;
-    return launch_result(engram::launch_scatter_plan_tokens(tokens, batch, seq_len, p, row_begin, num_rows, dim,
-                                                            uniq_rows, num_uniq, workspace, status, stream));
+    return launch_result(engram::launch_scatter_plan_tokens(tokens, batch, seq_len, seq_begin, seq_end, p,
+                                                            row_begin, num_rows, dim, uniq_rows, num_uniq,
+                                                            workspace, status, stream));
+}
+
+}  // namespace
+
+int engram_scatter_add_plan_from_tokens(const int64_t* tokens, int64_t batch, int64_t seq_len,
+                                        const engram_hash_spec* spec, int64_t row_begin, int64_t num_rows, int32_t dim,
+                                        int64_t* uniq_rows, int64_t* num_uniq, void* workspace,
+                                        size_t workspace_bytes, int64_t* status, hipStream_t stream) {
+    return plan_from_tokens_common(tokens, batch, seq_len, 0, seq_len, spec, row_begin, num_rows, dim, uniq_rows,
+                                   num_uniq, workspace, workspace_bytes, status, stream);
+}
+
+int engram_scatter_add_plan_from_tokens_slice(const int64_t* tokens, int64_t batch, int64_t seq_len,
+                                              int64_t seq_begin, int64_t seq_end, const engram_hash_spec* spec,
+                                              int64_t row_begin, int64_t num_rows, int32_t dim, int64_t* uniq_rows,
+                                              int64_t* num_uniq, void* workspace, size_t workspace_bytes,
+                                              int64_t* status, hipStream_t stream) {
+    return plan_from_tokens_common(tokens, batch, seq_len, seq_begin, seq_end, spec, row_begin, num_rows, dim,
+                                   uniq_rows, num_uniq, workspace, workspace_bytes, status, stream);
 }
 
 int engram_scatter_add_apply(const void* grad_out, int32_t dtype, int32_t dim, int64_t n, int64_t row_begin,

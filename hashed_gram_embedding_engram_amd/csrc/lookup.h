@@ -23,10 +23,12 @@ hipError_t launch_hash_gather(const int64_t* tokens, int64_t batch, int64_t seq_
                               int64_t* status, hipStream_t stream);
 
 // Backward phase 1 from tokens: the plan of engram_scatter_add_plan for the
-// rows the released head layout hashes from `tokens` [batch][seq_len] (16
-// per position), hashed inside the plan's first kernel (scatter.hip).
-hipError_t launch_scatter_plan_tokens(const int64_t* tokens, int64_t batch, int64_t seq_len, const HashParams& p,
-                                      int64_t row_begin, int64_t num_rows, int dim, int64_t* uniq_rows,
-                                      int64_t* num_uniq, void* workspace, int64_t* status, hipStream_t stream);
+// rows the released head layout hashes from columns [seq_begin, seq_end) of
+// `tokens` [batch][seq_len] (16 per position, the columns before seq_begin
+// read as history), hashed inside the plan's first kernel (scatter.hip).
+hipError_t launch_scatter_plan_tokens(const int64_t* tokens, int64_t batch, int64_t seq_len, int64_t seq_begin,
+                                      int64_t seq_end, const HashParams& p, int64_t row_begin, int64_t num_rows,
+                                      int dim, int64_t* uniq_rows, int64_t* num_uniq, void* workspace,
+                                      int64_t* status, hipStream_t stream);
 
 }  // namespace engram

@@ -181,7 +181,29 @@ struct TokenRows {
     const int64_t* tokens;  // [batch * seq_len], flattened
     uint32_t seq_len;
     HashParams p;
+    // A context-parallel slice: positions [seq_begin, seq_begin + width) of
+    // every batch row, flattened over [batch][width]; their context is read
+    // from the columns before seq_begin (engram API page,
+    // Qwen3_8_FlashNextNGramEmbedding._forward_global_slice).  The whole
+    // sequence is seq_begin 0 and width seq_len.
+    uint32_t seq_begin, width;
 };
+
+// The three tokens of one position of a slice, read straight from the batch
+// row (the columns before the slice are its history): flattened position pos
+// is batch row b = pos / width, column t = seq_begin + pos % width.  Missing
+// context (t < s, or an EOS in [t - s, t - 1]) takes the fill value.
+__device__ __forceinline__ void slice_context(const TokenRows& tr, uint32_t b, uint32_t col, int64_t* x0,
+                                              int64_t* ctx1, int64_t* ctx2) {
+    const uint32_t t = tr.seq_begin + col;
+    const int64_t* row = tr.tokens + (size_t)b * tr.seq_len;
+    const int64_t a = row[t], b1 = row[t >= 1 ? t - 1 : t], b2 = row[t >= 2 ? t - 2 : t];
+    const bool valid1 = t >= 1 && b1 != tr.p.eos;
+    const bool valid2 = valid1 && t >= 2 && b2 != tr.p.eos;
+    *x0 = a;
+    *ctx1 = valid1 ? b1 : tr.p.fill;
+    *ctx2 = valid2 ? b2 : tr.p.fill;
+}
 // Rows as the exchange delivers them: [world][capacity] blocks whose first
 // counts[w] entries are rows and the rest padding (counts == nullptr: every
 // entry is a row).  Padding takes the sentinel key without a report.
@@ -197,7 +219,7 @@ struct Padding {
 // positions (the context of shift s is the token s back unless that lies
 // before the batch row's start or an EOS sits in [t - s, t - 1]; missing
 // context takes the fill value).
-template <int ITEMS, bool TOKENS>
+template <int ITEMS, bool TOKENS, bool SLICE = false>
 __global__ __launch_bounds__(kBlock) void keys_kernel(const int64_t* __restrict__ rows, TokenRows tr, uint32_t n,
                                                       int64_t row_begin, uint64_t num_rows,
                                                       uint32_t* __restrict__ keys, DigitCounts dc,
@@ -212,7 +234,7 @@ __global__ __launch_bounds__(kBlock) void keys_kernel(const int64_t* __restrict_
     for (int k = 0; k < kBlock / 64; ++k) s_cnt[k][tid] = 0;
     if (tid == 0) s_valid = 0;
     const uint32_t p0 = blockIdx.x * (uint32_t)TILE_POS;  // the tile's first position (TOKENS)
-    if (TOKENS) {
+    if (TOKENS && !SLICE) {
         const uint32_t npos = n / kTokenHeads;
         for (int i = tid; i < TILE_POS + 2; i += kBlock) {
             const int64_t q = (int64_t)p0 - 2 + i;
@@ -238,21 +260,34 @@ __global__ __launch_bounds__(kBlock) void keys_kernel(const int64_t* __restrict_
                 off = tr.p.off[j];
             }
         // Item it of this lane is position pos0 + 4 it; its column t advances
-        // by 4 a step, wrapping at the row length.
+        // by 4 a step, wrapping at the row length (the slice's width).
+        const uint32_t npos = n / kTokenHeads;
         const uint32_t pos0 = (base + (uint32_t)lane) / kTokenHeads;
-        uint32_t t = pos0 % tr.seq_len;
+        const uint32_t wrap = SLICE ? tr.width : tr.seq_len;
+        uint32_t t = pos0 % wrap, b = pos0 / wrap;
 #pragma unroll
         for (int it = 0; it < ITEMS; ++it) {
-            const int li = (int)(pos0 + 4u * (uint32_t)it - p0) + 2;
-            const int64_t x0 = s_tok[li], x1 = s_tok[li - 1], x2 = s_tok[li - 2];
-            const bool valid1 = t >= 1 && x1 != tr.p.eos;
-            const bool valid2 = valid1 && t >= 2 && x2 != tr.p.eos;
-            const int64_t ctx1 = valid1 ? x1 : tr.p.fill, ctx2 = valid2 ? x2 : tr.p.fill;
+            int64_t x0, ctx1, ctx2;
+            if (SLICE) {
+                const bool in = pos0 + 4u * (uint32_t)it < npos;
+                slice_context(tr, in ? b : 0u, in ? t : 0u, &x0, &ctx1, &ctx2);  // past the end: position 0, unused
+            } else {
+                const int li = (int)(pos0 + 4u * (uint32_t)it - p0) + 2;
+                const int64_t x1 = s_tok[li - 1], x2 = s_tok[li - 2];
+                x0 = s_tok[li];
+                const bool valid1 = t >= 1 && x1 != tr.p.eos;
+                const bool valid2 = valid1 && t >= 2 && x2 != tr.p.eos;
+                ctx1 = valid1 ? x1 : tr.p.fill;
+                ctx2 = valid2 ? x2 : tr.p.fill;
+            }
             const uint64_t mix2 = (uint64_t)x0 * (uint64_t)tr.p.mult[0] ^ (uint64_t)ctx1 * (uint64_t)tr.p.mult[1];
             const uint64_t mix = h < 8 ? mix2 : mix2 ^ (uint64_t)ctx2 * (uint64_t)tr.p.mult[2];
             r[it] = (int64_t)floor_mod((int64_t)mix, mod, magic) + off;
             t += 4;
-            while (t >= tr.seq_len) t -= tr.seq_len;
+            while (t >= wrap) {
+                t -= wrap;
+                ++b;
+            }
         }
     } else {
         // Loads are clamped rather than guarded, so all of a thread's loads are
@@ -306,7 +341,9 @@ __global__ __launch_bounds__(kBlock) void keys_kernel(const int64_t* __restrict_
 // status word and the in-range count (every lookup), and the grid clears the
 // later passes' chunk and group totals (`zero_words`), which are first added
 // to after this kernel.
-template <int ITEMS, bool DIRECT>
+// With SLICE (a context-parallel slice) each position reads its three tokens
+// from its batch row (slice_context): the lanes below may hold another row.
+template <int ITEMS, bool DIRECT, bool SLICE = false>
 __global__ __launch_bounds__(kBlock) void head_keys_kernel(TokenRows tr, int64_t row_begin, Segments sg,
                                                            uint32_t* __restrict__ keys, DigitCounts dc,
                                                            uint32_t* __restrict__ counters,
@@ -344,28 +381,36 @@ __global__ __launch_bounds__(kBlock) void head_keys_kernel(TokenRows tr, int64_t
     const bool trigram = h >= (uint32_t)(kTokenHeads / 2);
     const uint32_t wbase = tile * (uint32_t)(kBlock * ITEMS) + (uint32_t)w * (64 * ITEMS);
     const uint32_t pos0 = wbase + (uint32_t)lane;
-    uint32_t t = pos0 % tr.seq_len;  // item 0's column; advances by 64 an item
+    const uint32_t wrap = SLICE ? tr.width : tr.seq_len;
+    uint32_t t = pos0 % wrap, b = pos0 / wrap;  // item 0's column and row; the column advances by 64 an item
     uint32_t my_valid = 0;
     uint32_t* const seg_keys = keys + (size_t)h * npos;
     int64_t tok[ITEMS];
 #pragma unroll
-    for (int it = 0; it < ITEMS; ++it) tok[it] = tr.tokens[min(pos0 + 64u * (uint32_t)it, npos - 1)];
+    for (int it = 0; it < ITEMS; ++it) tok[it] = SLICE ? 0 : tr.tokens[min(pos0 + 64u * (uint32_t)it, npos - 1)];
     // the two positions before the span (only read where the column says they
     // belong to the same batch row)
-    int64_t last1 = tr.tokens[min(wbase >= 1 ? wbase - 1 : 0u, npos - 1)];
-    int64_t last2 = tr.tokens[min(wbase >= 2 ? wbase - 2 : 0u, npos - 1)];
+    int64_t last1 = SLICE ? 0 : tr.tokens[min(wbase >= 1 ? wbase - 1 : 0u, npos - 1)];
+    int64_t last2 = SLICE ? 0 : tr.tokens[min(wbase >= 2 ? wbase - 2 : 0u, npos - 1)];
 #pragma unroll
     for (int it = 0; it < ITEMS; ++it) {
         const uint32_t pos = pos0 + 64u * (uint32_t)it;
-        const int64_t x0 = tok[it];
-        const int64_t up1 = __shfl_up(x0, 1, 64), up2 = __shfl_up(x0, 2, 64);
-        const int64_t x1 = lane >= 1 ? up1 : last1;
-        const int64_t x2 = lane >= 2 ? up2 : lane == 1 ? last1 : last2;
-        last1 = __shfl(x0, 63, 64);  // for the next item: the positions before its lanes 0 and 1
-        last2 = __shfl(x0, 62, 64);
-        const bool valid1 = t >= 1 && x1 != tr.p.eos;
-        const bool valid2 = valid1 && t >= 2 && x2 != tr.p.eos;
-        const int64_t ctx1 = valid1 ? x1 : tr.p.fill, ctx2 = valid2 ? x2 : tr.p.fill;
+        int64_t x0, ctx1, ctx2;
+        if (SLICE) {
+            const bool in = pos < npos;
+            slice_context(tr, in ? b : 0u, in ? t : 0u, &x0, &ctx1, &ctx2);  // past the end: position 0, unused
+        } else {
+            x0 = tok[it];
+            const int64_t up1 = __shfl_up(x0, 1, 64), up2 = __shfl_up(x0, 2, 64);
+            const int64_t x1 = lane >= 1 ? up1 : last1;
+            const int64_t x2 = lane >= 2 ? up2 : lane == 1 ? last1 : last2;
+            last1 = __shfl(x0, 63, 64);  // for the next item: the positions before its lanes 0 and 1
+            last2 = __shfl(x0, 62, 64);
+            const bool valid1 = t >= 1 && x1 != tr.p.eos;
+            const bool valid2 = valid1 && t >= 2 && x2 != tr.p.eos;
+            ctx1 = valid1 ? x1 : tr.p.fill;
+            ctx2 = valid2 ? x2 : tr.p.fill;
+        }
         const uint64_t mix2 = (uint64_t)x0 * (uint64_t)tr.p.mult[0] ^ (uint64_t)ctx1 * (uint64_t)tr.p.mult[1];
         const uint64_t mix = trigram ? mix2 ^ (uint64_t)ctx2 * (uint64_t)tr.p.mult[2] : mix2;
         const int64_t row = (int64_t)floor_mod((int64_t)mix, mod, magic) + off;
@@ -376,7 +421,14 @@ __global__ __launch_bounds__(kBlock) void head_keys_kernel(TokenRows tr, int64_t
             ++my_valid;
         }
         t += 64;
-        if (t >= tr.seq_len) t = tr.seq_len >= 64 ? t - tr.seq_len : t % tr.seq_len;
+        if (SLICE) {
+            while (t >= wrap) {
+                t -= wrap;
+                ++b;
+            }
+        } else if (t >= wrap) {
+            t = wrap >= 64 ? t - wrap : t % wrap;
+        }
     }
 #pragma unroll
     for (int o = 32; o > 0; o >>= 1) my_valid += __shfl_xor(my_valid, o, 64);
@@ -1125,17 +1177,29 @@ hipError_t run_sort(const Layout& L, char* ws, const int64_t* rows, const TokenR
         sg.total_words = (uint32_t)count_words(sg.tiles);
         const DigitCounts dc0 = make_digit_counts(ws + L.hist, count_totals, sg.tiles);
         const dim3 grid(sg.tiles * S.num_segs);
-        if (S.direct)
-            hipLaunchKernelGGL((head_keys_kernel<ITEMS, true>), grid, dim3(kBlock), 0, stream, *tr, row_begin, sg,
-                               k_cur, dc0, counters, status, count_totals + S.pass_words,
-                               (uint32_t)(S.pass_words * (size_t)(passes - 1)));
+        uint32_t* const zero_words = S.direct ? count_totals + S.pass_words : nullptr;
+        const uint32_t zero_count = S.direct ? (uint32_t)(S.pass_words * (size_t)(passes - 1)) : 0u;
+        const bool slice = tr->seq_begin != 0 || tr->width != tr->seq_len;
+        if (S.direct && !slice)
+            hipLaunchKernelGGL((head_keys_kernel<ITEMS, true, false>), grid, dim3(kBlock), 0, stream, *tr, row_begin,
+                               sg, k_cur, dc0, counters, status, zero_words, zero_count);
+        else if (S.direct)
+            hipLaunchKernelGGL((head_keys_kernel<ITEMS, true, true>), grid, dim3(kBlock), 0, stream, *tr, row_begin,
+                               sg, k_cur, dc0, counters, status, zero_words, zero_count);
+        else if (!slice)
+            hipLaunchKernelGGL((head_keys_kernel<ITEMS, false, false>), grid, dim3(kBlock), 0, stream, *tr,
+                               row_begin, sg, k_cur, dc0, counters, status, zero_words, zero_count);
         else
-            hipLaunchKernelGGL((head_keys_kernel<ITEMS, false>), grid, dim3(kBlock), 0, stream, *tr, row_begin, sg,
-                               k_cur, dc0, counters, status, (uint32_t*)nullptr, 0u);
+            hipLaunchKernelGGL((head_keys_kernel<ITEMS, false, true>), grid, dim3(kBlock), 0, stream, *tr, row_begin,
+                               sg, k_cur, dc0, counters, status, zero_words, zero_count);
     } else if (tr) {
-        hipLaunchKernelGGL((keys_kernel<ITEMS, true>), dim3(tiles), dim3(kBlock), 0, stream, nullptr, *tr, nn,
-                           row_begin, (uint64_t)num_rows, k_cur, make_digit_counts(ws + L.hist, count_totals, tiles),
-                           status, counters, Padding{});
+        const DigitCounts dc0 = make_digit_counts(ws + L.hist, count_totals, tiles);
+        if (tr->seq_begin != 0 || tr->width != tr->seq_len)
+            hipLaunchKernelGGL((keys_kernel<ITEMS, true, true>), dim3(tiles), dim3(kBlock), 0, stream, nullptr, *tr,
+                               nn, row_begin, (uint64_t)num_rows, k_cur, dc0, status, counters, Padding{});
+        else
+            hipLaunchKernelGGL((keys_kernel<ITEMS, true, false>), dim3(tiles), dim3(kBlock), 0, stream, nullptr, *tr,
+                               nn, row_begin, (uint64_t)num_rows, k_cur, dc0, status, counters, Padding{});
     } else {
         hipLaunchKernelGGL((keys_kernel<ITEMS, false>), dim3(tiles), dim3(kBlock), 0, stream, rows, TokenRows{}, nn,
                            row_begin, (uint64_t)num_rows, k_cur, make_digit_counts(ws + L.hist, count_totals, tiles),
@@ -1266,11 +1330,13 @@ hipError_t launch_scatter_plan_padded(const int64_t* ids, const int64_t* counts,
                         num_rows, dim, uniq_rows, num_uniq, workspace, status, stream);
 }
 
-hipError_t launch_scatter_plan_tokens(const int64_t* tokens, int64_t batch, int64_t seq_len, const HashParams& p,
-                                      int64_t row_begin, int64_t num_rows, int dim, int64_t* uniq_rows,
-                                      int64_t* num_uniq, void* workspace, int64_t* status, hipStream_t stream) {
-    const TokenRows tr{tokens, (uint32_t)seq_len, p};
-    return scatter_plan(nullptr, &tr, Padding{}, batch * seq_len * kTokenHeads, row_begin, num_rows, dim, uniq_rows,
+hipError_t launch_scatter_plan_tokens(const int64_t* tokens, int64_t batch, int64_t seq_len, int64_t seq_begin,
+                                      int64_t seq_end, const HashParams& p, int64_t row_begin, int64_t num_rows,
+                                      int dim, int64_t* uniq_rows, int64_t* num_uniq, void* workspace,
+                                      int64_t* status, hipStream_t stream) {
+    const TokenRows tr{tokens, (uint32_t)seq_len, p, (uint32_t)seq_begin, (uint32_t)(seq_end - seq_begin)};
+    return scatter_plan(nullptr, &tr, Padding{}, batch * (seq_end - seq_begin) * kTokenHeads, row_begin, num_rows,
+                        dim, uniq_rows,
                         num_uniq, workspace, status, stream);
 }
 

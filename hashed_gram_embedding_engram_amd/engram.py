@@ -108,6 +108,9 @@ def load_library(path=LIB_PATH):
     lib.engram_scatter_add_plan_from_tokens.restype = ctypes.c_int
     lib.engram_scatter_add_plan_from_tokens.argtypes = [p, i64, i64, ctypes.POINTER(EngramHashSpec), i64, i64, i32, p,
                                                         p, p, sz, p, p]
+    lib.engram_scatter_add_plan_from_tokens_slice.restype = ctypes.c_int
+    lib.engram_scatter_add_plan_from_tokens_slice.argtypes = [p, i64, i64, i64, i64, ctypes.POINTER(EngramHashSpec),
+                                                              i64, i64, i32, p, p, p, sz, p, p]
     lib.engram_scatter_add_apply.restype = ctypes.c_int
     lib.engram_scatter_add_apply.argtypes = [p, i32, i32, i64, i64, i64, p, p, p, sz, p]
     lib.engram_scatter_add_noalloc.restype = ctypes.c_int
@@ -426,6 +429,36 @@ def engram_scatter_add_plan_from_tokens(tokens, spec, num_rows, dim, row_begin=0
                                                    workspace.numel() * workspace.element_size(), _status_ptr(status),
                                                    _stream_handle(stream)),
            "engram_scatter_add_plan_from_tokens")
+    workspace._engram_plan = (n, num_rows, dim, row_begin)
+    return workspace
+
+
+def engram_scatter_add_plan_from_tokens_slice(tokens, spec, seq_begin, seq_end, num_rows, dim, row_begin=0,
+                                              workspace=None, uniq_rows=None, num_uniq=None, status=None,
+                                              stream=None):
+    """engram_scatter_add_plan_from_tokens for columns [seq_begin, seq_end) of every
+    batch row, the columns before seq_begin read as history: the rows
+    engram_hash_slice would give.  Returns the workspace; apply with
+    n = batch * (seq_end - seq_begin) * 16."""
+    lib = load_library()
+    if tokens.dim() != 2:
+        raise ValueError("tokens must be [batch, seq]")
+    batch, seq = tokens.shape
+    if not 0 <= seq_begin <= seq_end <= seq:
+        raise ValueError("need 0 <= seq_begin <= seq_end <= seq_len")
+    n = batch * (seq_end - seq_begin) * spec.num_heads
+    if workspace is None:
+        workspace = torch.empty(engram_scatter_add_workspace(n, num_rows, dim), dtype=torch.uint8,
+                                device=tokens.device)
+    _check(lib.engram_scatter_add_plan_from_tokens_slice(_dev_ptr(tokens, "tokens", torch.int64), batch, seq,
+                                                         seq_begin, seq_end, ctypes.byref(spec), row_begin,
+                                                         num_rows, dim,
+                                                         _dev_ptr(uniq_rows, "uniq_rows", torch.int64, min_numel=n),
+                                                         _dev_ptr(num_uniq, "num_uniq", torch.int64, numel=1),
+                                                         _dev_ptr(workspace, "workspace"),
+                                                         workspace.numel() * workspace.element_size(),
+                                                         _status_ptr(status), _stream_handle(stream)),
+           "engram_scatter_add_plan_from_tokens_slice")
     workspace._engram_plan = (n, num_rows, dim, row_begin)
     return workspace
 

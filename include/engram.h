@@ -285,6 +285,29 @@ int engram_scatter_add_plan_from_tokens(const int64_t* tokens, int64_t batch, in
                                         int64_t* uniq_rows, int64_t* num_uniq, void* workspace,
                                         size_t workspace_bytes, int64_t* status, hipStream_t stream);
 
+/* engram_scatter_add_plan_from_tokens for one context-parallel slice: the rows
+ * engram_hash_slice would write for columns [seq_begin, seq_end) of every batch
+ * row, hashed inside the plan with the columns before seq_begin as history
+ * (engram API page, Qwen3_8_FlashNextNGramEmbedding._forward_global_slice: the two
+ * preceding raw tokens and the EOS resets carry across the slice boundary).  So a
+ * rank's backward re-hashes its slice without keeping a rows array.  n = batch *
+ * (seq_end - seq_begin) * 16 lookups, lookup (b * (seq_end - seq_begin) + t -
+ * seq_begin) * 16 + h, exactly as engram_hash_slice lays out rows_out; the plan,
+ * its outputs and the apply that follows (with this n) are those of
+ * engram_scatter_add_plan on those rows.  The sort splits by head under the same
+ * conditions as engram_scatter_add_plan_from_tokens.
+ *   tokens    device int64 [batch][seq_len], the whole sequence of every row
+ *   seq_begin, seq_end   0 <= seq_begin <= seq_end <= seq_len < 2^32
+ *   other arguments as for engram_scatter_add_plan_from_tokens; the workspace is
+ *   engram_scatter_add_workspace(n, num_rows, dim) bytes
+ * Requires n < 2^31.  Returns ENGRAM_OK, ENGRAM_EINVAL (also for another head
+ * layout or a bad column range), ENGRAM_ESPEC or ENGRAM_EWORKSPACE. */
+int engram_scatter_add_plan_from_tokens_slice(const int64_t* tokens, int64_t batch, int64_t seq_len,
+                                              int64_t seq_begin, int64_t seq_end, const engram_hash_spec* spec,
+                                              int64_t row_begin, int64_t num_rows, int32_t dim, int64_t* uniq_rows,
+                                              int64_t* num_uniq, void* workspace, size_t workspace_bytes,
+                                              int64_t* status, hipStream_t stream);
+
 /* ---- Owner routing: the single-GPU half of the row-owner exchange ----------
  * Engram API page, Qwen3_8_FlashNextOwnerShardedEmbedding: with `world` owners,
  * rank r owns global rows [r * local_rows, (r + 1) * local_rows), local_rows =

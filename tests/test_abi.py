@@ -411,6 +411,22 @@ def test_hash_gather_rejects_bad_arguments(lib):
     assert sl(None, 1, 8, 4, 4, s, None, bf, 0, 10, 160, None, None, None, None) == B.ENGRAM_OK
 
 
+def test_plan_from_token_slice_rejects_bad_arguments(lib):
+    f = ctypes.c_void_p(0x10000)
+    s = ctypes.byref(E.qwen3_8_flash_next_spec())
+    call = lib.engram_scatter_add_plan_from_tokens_slice
+    ws = lib.engram_scatter_add_workspace(8 * 16, 1000, 160)
+    # (tokens, batch, seq_len, seq_begin, seq_end, spec, row_begin, num_rows, dim, uniq_rows, num_uniq,
+    #  workspace, bytes, status, stream)
+    for a, b in [(-1, 4), (5, 4), (0, 9), (9, 9)]:
+        assert call(f, 1, 8, a, b, s, 0, 1000, 160, None, None, f, ws, None, None) == B.ENGRAM_EINVAL
+    assert call(f, 1, 1 << 32, 0, 8, s, 0, 1000, 160, None, None, f, ws, None, None) == B.ENGRAM_EINVAL
+    assert call(f, 1 << 20, 1 << 9, 0, 1 << 7, s, 0, 1000, 160, None, None, f, ws, None, None) == B.ENGRAM_EINVAL
+    assert call(f, 1, 64, 8, 16, s, 0, 1000, 160, None, None, f, ws - 1, None, None) == B.ENGRAM_EWORKSPACE
+    two = E.make_hash_spec(2, 8, 7, (3, 5), [101] * 8, [101 * h for h in range(8)])
+    assert call(f, 1, 8, 0, 8, ctypes.byref(two), 0, 1000, 160, None, None, f, ws, None, None) == B.ENGRAM_EINVAL
+
+
 def test_plan_from_tokens_rejects_bad_arguments(lib):
     f = ctypes.c_void_p(0x10000)
     mis = ctypes.c_void_p(0x10004)

@@ -332,6 +332,84 @@ def test_whole_sort_when_not_split(case):
         assert bad < 0
 
 
+# ---- The plan from a context-parallel slice (engram_scatter_add_plan_from_tokens_slice):
+# columns [a, b) of every batch row, the columns before a read as history.  Plan and
+# apply must equal the oracle's scatter-add of columns [a, b) of the oracle's hash of
+# the whole rows, for the whole sort and the sort split by head, at cuts inside EOS
+# runs and at the row ends.
+
+def check_slice_plan(ids, ws, a, b, num_rows, dim=8, seed=0, dense=False):
+    spec = product_spec_from(ws)
+    ids = np.ascontiguousarray(ids, dtype=np.int64)
+    tokens = torch.from_numpy(ids).cuda()
+    n = ids.shape[0] * (b - a) * 16
+    rows_ref = oracle_hash(ids, ws)[:, a:b].reshape(-1)
+    status = torch.empty((), dtype=torch.int64, device="cuda")
+    nu = torch.empty((), dtype=torch.int64, device="cuda")
+    ur = torch.full((max(n, 1),), -7, dtype=torch.int64, device="cuda")
+    wsp = E.engram_scatter_add_plan_from_tokens_slice(tokens, spec, a, b, num_rows, dim, uniq_rows=ur, num_uniq=nu,
+                                                      status=status)
+    if n == 0:
+        torch.cuda.synchronize()
+        assert int(nu.item()) == 0 and int(status.item()) == -1
+        return
+    dy = grads(n, seed, dim)
+    dy_host = to_host(dy)
+    if dense:
+        g = torch.zeros((num_rows, dim), dtype=torch.float32, device="cuda")
+        E.engram_scatter_add_apply(dy, n, num_rows, wsp, grad_dense=g)
+        ref, rbad = c_oracle.scatter_add_dense(rows_ref, dy_host, num_rows, 0)
+        torch.cuda.synchronize()
+        assert int(status.item()) == rbad
+        assert_close_to_fp64(g.cpu().numpy(), ref, "dense sums from a token slice")
+        return
+    ug = torch.empty((n, dim), dtype=torch.float32, device="cuda")
+    E.engram_scatter_add_apply(dy, n, num_rows, wsp, uniq_grad=ug)
+    torch.cuda.synchronize()
+    rur, rug, rbad = c_oracle.scatter_add_compact(rows_ref, dy_host, num_rows, 0)
+    u = int(nu.item())
+    assert int(status.item()) == rbad
+    assert u == rur.size and np.array_equal(ur[:u].cpu().numpy(), rur)
+    assert_close_to_fp64(ug[:u].cpu().numpy(), rug, "compact sums from a token slice")
+
+
+SLICE_CUTS = [(0, 300), (1, 2), (2, 301), (37, 41), (150, 300), (299, 300), (64, 192), (120, 120)]
+
+
+@pytest.mark.parametrize("layout", ["whole", "split"])
+@pytest.mark.parametrize("cut", SLICE_CUTS)
+def test_plan_from_token_slice(layout, cut):
+    ws = W.tiny_spec() if layout == "whole" else head_layout(100_000)
+    ids = uniform_ids((3, 301), 71, ws["eos"], p_eos=1 / 8)
+    ids[1, 36:40] = ws["eos"]   # a cut inside an EOS run
+    check_slice_plan(ids, ws, cut[0], cut[1], ws["num_rows"], seed=cut[0] % 7)
+
+
+@pytest.mark.parametrize("layout", ["whole", "split"])
+def test_plan_from_token_slice_every_tile_size(layout):
+    """One long row cut at 1,000 and 1,000 + 2^16 + 3 or + 2^17 + 5 positions: the
+    16- and 24-key tiles, 1 M and 2 M lookups; the dense form once."""
+    ws = W.tiny_spec() if layout == "whole" else head_layout(100_000)
+    ids = uniform_ids((1, 140_000), 73, ws["eos"], p_eos=1 / 64)
+    check_slice_plan(ids, ws, 1000, 1000 + (1 << 16) + 3, ws["num_rows"], seed=2, dense=layout == "split")
+    check_slice_plan(ids, ws, 1000, 1000 + (1 << 17) + 5, ws["num_rows"], seed=3)
+
+
+def test_plan_from_token_slice_released_heads():
+    """The released moduli over the full row range (per-head sort, 9-bit last pass):
+    an eighth of a context-parallel world's sequence, cut at 3/8 of it."""
+    ids = uniform_ids((2, 40_000), 79, C.EOS_TOKEN_ID, p_eos=1 / 256, vocab=5000)
+    check_slice_plan(ids, full_oracle_spec(), 15_000, 20_000, C.padded_rows(), seed=4)
+
+
+def test_plan_from_token_slice_refused():
+    ws = W.tiny_spec()
+    t = torch.zeros((2, 8), dtype=torch.int64, device="cuda")
+    for a, b in [(-1, 3), (4, 3), (0, 9)]:
+        with pytest.raises(ValueError):
+            E.engram_scatter_add_plan_from_tokens_slice(t, product_spec_from(ws), a, b, ws["num_rows"], 8)
+
+
 def test_plan_from_tokens_refuses_other_layouts():
     ws = W.tiny_spec()
     two = dict(ws, ngram_size=2, vocab_sizes=ws["vocab_sizes"][:8], offsets=ws["offsets"][:8])
