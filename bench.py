@@ -1162,7 +1162,7 @@ LOOKUP_PHASES = {
     "gather": ("gather.hip", [r"\bgather_rows_kernel"]),
     # a plan starts with its init kernel, or, split by head into short
     # segments, with the keys kernel that does the init's work itself
-    "scatter_plan": ("scatter.hip", [r"\bscatter_init_kernel|\bhead_keys_kernel<\d+, true>", r"\bkeys_kernel",
+    "scatter_plan": ("scatter.hip", [r"\bscatter_init_kernel|\bhead_keys_kernel<\d+, true\b", r"\bkeys_kernel",
                                      r"\bhead_keys_kernel", r"\bupsweep_kernel",
                                      r"\bdownsweep_kernel", r"\brun_count_kernel", r"\bblock_scan_kernel",
                                      r"\buniq_rows_kernel"]),
