@@ -8,7 +8,9 @@
  * permute, and one-pass forms of the requester's copies) and the PLE layer's
  * causal short convolution and grouped RMSNorm
  * (engram_short_conv*, engram_grouped_rms_norm*), each declared with the
- * passage that defines it.
+ * passage that defines it.  From raw tokens, engram_hash_gather and
+ * engram_scatter_add_plan_from_tokens (and their context-parallel slice forms)
+ * run the forward and the backward's sort without a rows array.
  *
  * Passages defining the operations ("engram API page" = the page titled
  * nemo_automodel.components.models.qwen3_8_flash_next.engram; "model-coverage
